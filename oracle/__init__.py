@@ -1,0 +1,613 @@
+"""CPU oracle for the join-agg hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP library (neither imports
+the other); the two meet only through the seeded input bytes.
+
+What it computes, and where each piece comes from (the pages: "Every Kernel
+Is a Join: Automatic Multi-GPU Parallelism for AI Computations in
+Einsummable", paperpeel full text):
+
+* dense results by their plain definitions, in float64 (``ja_oracle.c``):
+  the loop-nest contraction, textbook two-pass attention, RMSNorm, SwiGLU,
+  elementwise add;
+* tensor types, projections and tilings (section 3.1, section 3.2);
+* join-agg specs for an einsum, one function spec per combination of
+  intervals of the shardable indices (section 3.3), executed by the
+  three-phase definition Join / Aggregate / Recompose (section 3.2,
+  Definition 3.7) -- ``execute_joinagg``;
+* the degenerate relational join-agg in which every key is one cell and
+  every value a scalar (section 1) -- ``brute_force_einsum``;
+* canonical tuple lists with CSR segments -- ``tuple_records``;
+* the overlay grid whose cells are the atoms of a repartition (section 5.3),
+  and the repartition itself -- ``overlay_atoms``, ``repartition``;
+* attention as a blocked join-agg with the online-softmax aggregation
+  (m, l, acc) -- ``attention_online_blocked`` (the aggregation operator need
+  not be addition, section 5.2);
+* the LLaMA-shaped block as a chain of the above -- ``llama_block``.
+
+Readings where the pages are silent (listed again in the design notes):
+intervals are half-open [lo, hi); near-equal intervals give the first
+(n mod q) intervals one extra element; causal means key t is visible to query
+s iff t <= s, and a (s-block, t-block) tuple is dropped when t_lo >= s_hi;
+every materialised bf16 relation is rounded to nearest-even once, from the
+exact (float64) value.
+"""
+from __future__ import annotations
+
+import ctypes
+import itertools
+import os
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libja_oracle.so")
+_lib = None
+
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+
+
+def build(force: bool = False) -> str:
+    """Compile ja_oracle.c into libja_oracle.so with gcc + OpenMP."""
+    import subprocess
+
+    src = os.path.join(_HERE, "ja_oracle.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", src, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.orc_num_threads.restype = ctypes.c_int
+        lib.orc_bf16_to_f64.argtypes = [_u16p, ctypes.c_int64, _f64p]
+        lib.orc_f64_to_bf16.argtypes = [_f64p, ctypes.c_int64, _u16p]
+        lib.orc_einsum2.argtypes = [ctypes.c_char_p, _i64p, _f64p, _f64p, _f64p]
+        lib.orc_einsum2.restype = ctypes.c_int
+        lib.orc_einsum2_points.argtypes = [ctypes.c_char_p, _i64p, _f64p, _f64p, ctypes.c_int64, _i64p, _f64p]
+        lib.orc_einsum2_points.restype = ctypes.c_int
+        lib.orc_matmul.argtypes = [_f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+        lib.orc_attention_rows.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int64] * 5 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int64, _i64p, _f64p]
+        lib.orc_rmsnorm.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _f64p]
+        lib.orc_swiglu.argtypes = [_f64p, _f64p, ctypes.c_int64, _f64p]
+        lib.orc_add.argtypes = [_f64p, _f64p, ctypes.c_int64, _f64p]
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+# --------------------------------------------------------------------------
+# bfloat16
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(h) -> np.ndarray:
+    """Exact decode of bfloat16 bit patterns (uint16) to float64."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float64)
+    _load().orc_bf16_to_f64(_ptr(h, _u16p), h.size, _ptr(out, _f64p))
+    return out
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """Round float64 values to bfloat16 bit patterns, nearest-even."""
+    x = _f64(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_f64_to_bf16(_ptr(x, _f64p), x.size, _ptr(out, _u16p))
+    return out
+
+
+def round_bf16(x) -> np.ndarray:
+    """The float64 value of the bfloat16 nearest to x."""
+    return bf16_to_f64(f64_to_bf16(x))
+
+
+# --------------------------------------------------------------------------
+# dense definitions
+# --------------------------------------------------------------------------
+
+def _parse(spec: str):
+    lhs, out = spec.split("->")
+    ins = lhs.split(",")
+    return ins, out
+
+
+def _ext26(spec: str, *ops) -> np.ndarray:
+    ins, _ = _parse(spec)
+    ext = np.zeros(26, dtype=np.int64)
+    for s, a in zip(ins, ops):
+        if len(s) != a.ndim:
+            raise ValueError("operand rank does not match %r" % s)
+        for c, n in zip(s, a.shape):
+            l = ord(c) - ord("a")
+            if ext[l] and ext[l] != n:
+                raise ValueError("letter %s has two extents" % c)
+            ext[l] = n
+    return ext
+
+
+def einsum(spec: str, A, B) -> np.ndarray:
+    """Two-operand einsum by its definition: every output cell is the sum,
+    over all values of the letters that do not reach the output, of the
+    product of the two operand cells (float64 loop nest in C)."""
+    A, B = _f64(A), _f64(B)
+    ext = _ext26(spec, A, B)
+    _, out = _parse(spec)
+    shape = tuple(int(ext[ord(c) - 97]) for c in out)
+    C = np.empty(shape, dtype=np.float64)
+    rc = _load().orc_einsum2(spec.encode(), _ptr(ext, _i64p), _ptr(A, _f64p), _ptr(B, _f64p), _ptr(C, _f64p))
+    if rc:
+        raise ValueError("bad einsum spec %r" % spec)
+    return C
+
+
+def einsum_points(spec: str, A, B, points) -> np.ndarray:
+    """The einsum evaluated only at the given output multi-indices
+    (array [n, rank_out])."""
+    A, B = _f64(A), _f64(B)
+    ext = _ext26(spec, A, B)
+    _, out = _parse(spec)
+    shape = tuple(int(ext[ord(c) - 97]) for c in out)
+    pts = np.asarray(points, dtype=np.int64).reshape(-1, len(out))
+    lin = np.ascontiguousarray(np.ravel_multi_index(tuple(pts.T), shape).astype(np.int64))
+    vals = np.empty(lin.size, dtype=np.float64)
+    rc = _load().orc_einsum2_points(spec.encode(), _ptr(ext, _i64p), _ptr(A, _f64p), _ptr(B, _f64p),
+                                    lin.size, _ptr(lin, _i64p), _ptr(vals, _f64p))
+    if rc:
+        raise ValueError("bad einsum spec %r" % spec)
+    return vals
+
+
+def matmul(A, B) -> np.ndarray:
+    """C = A @ B for 2-D operands (float64, plain loops)."""
+    A, B = _f64(A), _f64(B)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner extents differ")
+    C = np.empty((M, N), dtype=np.float64)
+    _load().orc_matmul(_ptr(A, _f64p), _ptr(B, _f64p), _ptr(C, _f64p), M, K, N)
+    return C
+
+
+def attention_rows(Q, K, V, rows, scale: float, causal: bool) -> np.ndarray:
+    """Attention output rows for the listed (b, h, s) query rows.
+    Q [B,H,S,D], K/V [B,H,T,D]; two-pass softmax in float64."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    Bn, H, S, D = Q.shape
+    T = K.shape[2]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    out = np.empty((rows.shape[0], D), dtype=np.float64)
+    _load().orc_attention_rows(_ptr(Q, _f64p), _ptr(K, _f64p), _ptr(V, _f64p), Bn, H, S, T, D, float(scale),
+                               1 if causal else 0, rows.shape[0], _ptr(rows, _i64p), _ptr(out, _f64p))
+    return out
+
+
+def attention(Q, K, V, scale: float, causal: bool) -> np.ndarray:
+    Bn, H, S, D = np.shape(Q)
+    rows = np.array(list(itertools.product(range(Bn), range(H), range(S))), dtype=np.int64)
+    return attention_rows(Q, K, V, rows, scale, causal).reshape(Bn, H, S, D)
+
+
+def rmsnorm(x, g, eps: float) -> np.ndarray:
+    x, g = _f64(x), _f64(g)
+    R, D = x.shape
+    y = np.empty_like(x)
+    _load().orc_rmsnorm(_ptr(x, _f64p), _ptr(g, _f64p), R, D, float(eps), _ptr(y, _f64p))
+    return y
+
+
+def swiglu(g, u) -> np.ndarray:
+    g, u = _f64(g), _f64(u)
+    h = np.empty_like(g)
+    _load().orc_swiglu(_ptr(g, _f64p), _ptr(u, _f64p), g.size, _ptr(h, _f64p))
+    return h
+
+
+def add(a, b) -> np.ndarray:
+    a, b = _f64(a), _f64(b)
+    c = np.empty_like(a)
+    _load().orc_add(_ptr(a, _f64p), _ptr(b, _f64p), a.size, _ptr(c, _f64p))
+    return c
+
+
+# --------------------------------------------------------------------------
+# tensor types, tilings and relations (section 3.1, section 3.2)
+# --------------------------------------------------------------------------
+
+Box = Tuple[Tuple[int, ...], Tuple[int, ...]]  # (lower bounds, upper bounds), half-open
+
+
+def equal_splits(n: int, q: int) -> List[int]:
+    """Split points of [0, n) into q near-equal intervals; the first n mod q
+    intervals are one longer."""
+    if q < 1 or q > max(n, 1):
+        raise ValueError("bad interval count")
+    base, extra = divmod(n, q)
+    pts = [0]
+    for i in range(q):
+        pts.append(pts[-1] + base + (1 if i < extra else 0))
+    return pts
+
+
+def box_cells(box: Box) -> int:
+    lo, hi = box
+    n = 1
+    for a, b in zip(lo, hi):
+        n *= max(0, b - a)
+    return n
+
+
+def tiles(boxes: Sequence[Box], shape: Sequence[int]) -> bool:
+    """Section 3.1 tiling: the boxes cover the index set of the zero-bounded
+    type `shape` and are pairwise disjoint (checked cell by cell)."""
+    count = np.zeros(tuple(shape), dtype=np.int64)
+    for lo, hi in boxes:
+        if any(a < 0 or b > n or a > b for a, b, n in zip(lo, hi, shape)):
+            return False
+        count[tuple(slice(a, b) for a, b in zip(lo, hi))] += 1
+    return bool(np.all(count == 1))
+
+
+class Relation:
+    """A tensor as a set of (key, block) pairs.  The key of a block is its
+    coordinate in the per-dimension interval grid; the block is the
+    projection of the tensor onto that box (section 3.2).  Stored layout
+    (the oracle's own): blocks back to back in lexicographic key order (first
+    dimension slowest), each block dense row-major over its box."""
+
+    def __init__(self, shape: Sequence[int], splits: Sequence[Sequence[int]]):
+        self.shape = tuple(int(n) for n in shape)
+        self.splits = [list(map(int, s)) for s in splits]
+        if len(self.splits) != len(self.shape):
+            raise ValueError("one split list per dimension")
+        for n, s in zip(self.shape, self.splits):
+            if s[0] != 0 or s[-1] != n or any(b <= a for a, b in zip(s, s[1:])):
+                raise ValueError("split points must rise strictly from 0 to the extent")
+
+    @classmethod
+    def even(cls, shape: Sequence[int], nblk: Sequence[int]) -> "Relation":
+        return cls(shape, [equal_splits(n, q) for n, q in zip(shape, nblk)])
+
+    @property
+    def nblk(self) -> Tuple[int, ...]:
+        return tuple(len(s) - 1 for s in self.splits)
+
+    def keys(self):
+        return itertools.product(*[range(q) for q in self.nblk])
+
+    def box(self, key) -> Box:
+        lo = tuple(self.splits[d][k] for d, k in enumerate(key))
+        hi = tuple(self.splits[d][k + 1] for d, k in enumerate(key))
+        return lo, hi
+
+    def pack(self, dense: np.ndarray) -> np.ndarray:
+        if tuple(dense.shape) != self.shape:
+            raise ValueError("dense shape does not match the relation")
+        parts = []
+        for key in self.keys():
+            lo, hi = self.box(key)
+            parts.append(np.ascontiguousarray(dense[tuple(slice(a, b) for a, b in zip(lo, hi))]).ravel())
+        return np.concatenate(parts) if parts else np.zeros(0, dtype=dense.dtype)
+
+    def unpack(self, flat: np.ndarray) -> np.ndarray:
+        dense = np.empty(self.shape, dtype=flat.dtype)
+        off = 0
+        for key in self.keys():
+            lo, hi = self.box(key)
+            n = box_cells((lo, hi))
+            dense[tuple(slice(a, b) for a, b in zip(lo, hi))] = flat[off:off + n].reshape(
+                tuple(b - a for a, b in zip(lo, hi)))
+            off += n
+        if off != flat.size:
+            raise ValueError("flat buffer size does not match the relation")
+        return dense
+
+
+# --------------------------------------------------------------------------
+# join-agg specs and their execution (section 3.2, section 3.3)
+# --------------------------------------------------------------------------
+
+class FunctionSpec:
+    """One function specification: the projected input types and the
+    projected output type, plus the interval index of every letter (the grid
+    cell it came from)."""
+
+    def __init__(self, cell: Dict[str, int], inputs: List[Box], output: Box):
+        self.cell = cell
+        self.inputs = inputs
+        self.output = output
+
+
+def letters_of(spec: str) -> List[str]:
+    """Distinct letters in order of first appearance in the spec string."""
+    out: List[str] = []
+    for c in spec:
+        if c.isalpha() and c not in out:
+            out.append(c)
+    return out
+
+
+def joinagg_spec(spec: str, splits: Dict[str, Sequence[int]],
+                 keep: Optional[Callable[[Dict[str, Tuple[int, int]]], bool]] = None) -> List[FunctionSpec]:
+    """The join-agg spec an einsum-shaped operator returns for the given
+    intervals of its shardable letters: one function specification per
+    combination of intervals (section 3.3), each projecting every operand and
+    the output onto the intervals of its letters.  `keep` is an optional join
+    predicate over the intervals (used for dropping fully masked causal
+    tuples)."""
+    ins, out = _parse(spec)
+    letters = letters_of(spec)
+    ranges = [range(len(splits[c]) - 1) for c in letters]
+    specs = []
+    for combo in itertools.product(*ranges):
+        cell = dict(zip(letters, combo))
+        iv = {c: (splits[c][cell[c]], splits[c][cell[c] + 1]) for c in letters}
+        if keep is not None and not keep(iv):
+            continue
+        in_boxes = [(tuple(iv[c][0] for c in s), tuple(iv[c][1] for c in s)) for s in ins]
+        out_box = (tuple(iv[c][0] for c in out), tuple(iv[c][1] for c in out))
+        specs.append(FunctionSpec(cell, in_boxes, out_box))
+    return specs
+
+
+def execute_joinagg(specs: List[FunctionSpec], inputs: Sequence[np.ndarray], out_shape: Sequence[int],
+                    f: Callable[..., np.ndarray], oplus: Callable[[np.ndarray, np.ndarray], np.ndarray],
+                    finalize: Optional[Callable[[np.ndarray], np.ndarray]] = None) -> np.ndarray:
+    """Definition 3.7 in three phases:
+    (1) Join: project every input onto the spec's input types and run f;
+    (2) Aggregate: combine with oplus, in ascending spec order, all outputs
+        that share one output type;
+    (3) Recompose: check the distinct output types tile the output, then
+        stitch the aggregated blocks into the output tensor."""
+    partials: Dict[Box, np.ndarray] = {}
+    order: List[Box] = []
+    for F in specs:  # (1) join
+        blocks = [np.array(U[tuple(slice(a, b) for a, b in zip(*box))]) for U, box in zip(inputs, F.inputs)]
+        part = f(*blocks)
+        if F.output in partials:  # (2) aggregate
+            partials[F.output] = oplus(partials[F.output], part)
+        else:
+            partials[F.output] = part
+            order.append(F.output)
+    if not tiles(order, out_shape):
+        raise ValueError("output types do not tile the output (tiling condition violated)")
+    out = None
+    for box in order:  # (3) recompose
+        blk = finalize(partials[box]) if finalize else partials[box]
+        if out is None:
+            out = np.zeros(tuple(out_shape), dtype=blk.dtype)
+        out[tuple(slice(a, b) for a, b in zip(*box))] = blk
+    return out
+
+
+def contract_joinagg(spec: str, A, B, splits: Dict[str, Sequence[int]]) -> np.ndarray:
+    """An einsum contraction executed as a join-agg: f is the block einsum,
+    the aggregation is SUM (section 3.2, Examples 3.8 and 3.9)."""
+    A, B = _f64(A), _f64(B)
+    ins, out = _parse(spec)
+    ext = {c: n for s, a in zip(ins, (A, B)) for c, n in zip(s, a.shape)}
+    specs = joinagg_spec(spec, splits)
+    return execute_joinagg(specs, [A, B], [ext[c] for c in out], lambda a, b: einsum(spec, a, b), np.add)
+
+
+def brute_force_einsum(spec: str, A, B) -> np.ndarray:
+    """The degenerate relational join-agg (section 1): each relation is a set
+    of (cell index, scalar) pairs; natural join on the shared letters;
+    multiply; group by the output letters; SUM.  Pure Python: tiny inputs."""
+    ins, out = _parse(spec)
+    A, B = np.asarray(A, dtype=np.float64), np.asarray(B, dtype=np.float64)
+    relA = {idx: float(A[idx]) for idx in np.ndindex(A.shape)}
+    relB = {idx: float(B[idx]) for idx in np.ndindex(B.shape)}
+    shared = [c for c in ins[0] if c in ins[1]]
+    # hash join: index B's tuples by the values of the shared letters
+    table: Dict[tuple, list] = {}
+    for idx, v in relB.items():
+        key = tuple(idx[ins[1].index(c)] for c in shared)
+        table.setdefault(key, []).append((idx, v))
+    groups: Dict[tuple, float] = {}
+    for ia, va in relA.items():
+        key = tuple(ia[ins[0].index(c)] for c in shared)
+        for ib, vb in table.get(key, []):
+            val = {c: ia[ins[0].index(c)] for c in ins[0]}
+            val.update({c: ib[ins[1].index(c)] for c in ins[1]})
+            gk = tuple(val[c] for c in out)
+            groups[gk] = groups.get(gk, 0.0) + va * vb
+    ext = {c: n for s, a in zip(ins, (A, B)) for c, n in zip(s, a.shape)}
+    C = np.zeros(tuple(ext[c] for c in out), dtype=np.float64)
+    for k, v in groups.items():
+        C[k] = v
+    return C
+
+
+def tuple_records(letters: Sequence[str], splits: Dict[str, Sequence[int]], group_by: Sequence[str],
+                  causal: Optional[Tuple[str, str]] = None):
+    """Canonical tuple list of a decomposition: one record per kept grid
+    cell, holding the interval index of every letter (in `letters` order).
+    Records are sorted by the group-by letters' indices (in `group_by`
+    order), then by the other letters' indices (in `letters` order).  A
+    causal pair (s, t) drops every cell whose key interval starts at or
+    after the end of its query interval.  Returns (records [n, L] int32,
+    segment offsets [nseg + 1] int64)."""
+    rest = [c for c in letters if c not in group_by]
+    recs = []
+    for combo in itertools.product(*[range(len(splits[c]) - 1) for c in letters]):
+        cell = dict(zip(letters, combo))
+        if causal is not None:
+            s, t = causal
+            if splits[t][cell[t]] >= splits[s][cell[s] + 1]:
+                continue
+        recs.append(cell)
+    recs.sort(key=lambda c: (tuple(c[x] for x in group_by), tuple(c[x] for x in rest)))
+    arr = np.array([[c[x] for x in letters] for c in recs], dtype=np.int32).reshape(-1, len(letters))
+    seg = [0]
+    for i in range(1, len(recs)):
+        if any(recs[i][x] != recs[i - 1][x] for x in group_by):
+            seg.append(i)
+    if recs:
+        seg.append(len(recs))
+    return arr, np.array(seg, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# attention as a blocked join-agg with the online-softmax aggregation
+# --------------------------------------------------------------------------
+
+def attention_online_blocked(Q, K, V, s_splits, t_splits, scale: float, causal: bool,
+                             t_order: Optional[Callable[[List[int]], List[int]]] = None) -> np.ndarray:
+    """Per (b, h, s-block) segment, each kept t-block tuple yields the
+    triple (m, l, acc): m = row max of its scores, l = sum of exp(score - m),
+    acc = sum of exp(score - m) * V.  Triples combine with
+        m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m),
+        acc = acc1 e^(m1-m) + acc2 e^(m2-m),
+    which is associative and commutative with identity (-inf, 0, 0).  The
+    output block is acc / l.  `t_order` may permute the fold order."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    Bn, H, S, D = Q.shape
+    out = np.zeros_like(Q)
+    for b in range(Bn):
+        for h in range(H):
+            for si in range(len(s_splits) - 1):
+                s0, s1 = s_splits[si], s_splits[si + 1]
+                tis = [ti for ti in range(len(t_splits) - 1) if not (causal and t_splits[ti] >= s1)]
+                if t_order is not None:
+                    tis = t_order(tis)
+                m = np.full(s1 - s0, -np.inf)
+                l = np.zeros(s1 - s0)
+                acc = np.zeros((s1 - s0, D))
+                for ti in tis:
+                    t0, t1 = t_splits[ti], t_splits[ti + 1]
+                    sc = scale * (Q[b, h, s0:s1] @ K[b, h, t0:t1].T)
+                    if causal:
+                        qs = np.arange(s0, s1)[:, None]
+                        ks = np.arange(t0, t1)[None, :]
+                        sc = np.where(ks <= qs, sc, -np.inf)
+                    m2 = sc.max(axis=1)
+                    p = np.where(np.isfinite(sc), np.exp(sc - np.where(np.isfinite(m2), m2, 0.0)[:, None]), 0.0)
+                    l2 = p.sum(axis=1)
+                    acc2 = p @ V[b, h, t0:t1]
+                    mn = np.maximum(m, m2)
+                    a1 = np.where(np.isfinite(m), np.exp(m - np.where(np.isfinite(mn), mn, 0.0)), 0.0)
+                    a2 = np.where(np.isfinite(m2), np.exp(m2 - np.where(np.isfinite(mn), mn, 0.0)), 0.0)
+                    l = l * a1 + l2 * a2
+                    acc = acc * a1[:, None] + acc2 * a2[:, None]
+                    m = mn
+                out[b, h, s0:s1] = acc / l[:, None]
+    return out
+
+
+# --------------------------------------------------------------------------
+# repartition (section 4.3 item 1, section 5.3)
+# --------------------------------------------------------------------------
+
+def apply_view(dense: np.ndarray, vshape: Optional[Sequence[int]], perm: Optional[Sequence[int]],
+               out_shape: Sequence[int]) -> np.ndarray:
+    """The logical re-indexing a repartition may apply: read the source
+    row-major as `vshape`, permute axes (output axis k = view axis perm[k]),
+    then read the result row-major as `out_shape`."""
+    x = dense
+    if vshape is not None:
+        x = x.reshape(tuple(vshape))
+    if perm is not None:
+        x = np.transpose(x, tuple(perm))
+    return np.ascontiguousarray(x).reshape(tuple(out_shape))
+
+
+def repartition(src: Relation, src_flat: np.ndarray, dst: Relation, vshape=None, perm=None) -> np.ndarray:
+    """Re-block a relation: the destination holds, block by block, exactly
+    the elements of the (optionally re-indexed) source tensor."""
+    dense = src.unpack(src_flat)
+    return dst.pack(apply_view(dense, vshape, perm, dst.shape))
+
+
+def overlay_atoms(*split_families: Sequence[Sequence[int]]) -> List[List[int]]:
+    """Section 5.3 overlay: per dimension, the union of the lower and upper
+    bounds of every block of every family.  The resulting grid's cells are
+    the atoms; every block of every family is a disjoint union of atoms."""
+    rank = len(split_families[0])
+    return [sorted(set().union(*[set(fam[d]) for fam in split_families])) for d in range(rank)]
+
+
+# --------------------------------------------------------------------------
+# LLaMA-shaped block (pre-norm, causal MHA, SwiGLU FFN, two residual adds)
+# --------------------------------------------------------------------------
+
+def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
+                eps: float = 1e-6, return_intermediates: bool = False):
+    """Float64 reference of one transformer block on bf16 inputs, with every
+    materialised relation rounded to bf16.  x [batch*seq, d]; w_qkv is
+    [d, 3d] = [W_q | W_k | W_v] with head h in columns [h*hd, (h+1)*hd) of
+    each third.  Token t = b*seq + s.  No rotary embedding and no biases."""
+    T, Dm = x.shape
+    hd = Dm // heads
+    r = round_bf16
+    h1 = r(rmsnorm(x, g1, eps))
+    qkv = r(matmul(h1, w_qkv))
+    v5 = qkv.reshape(batch, seq, 3, heads, hd).transpose(2, 0, 3, 1, 4)  # [3, b, h, s, hd]
+    Q, K, V = v5[0], v5[1], v5[2]
+    O = r(attention(Q, K, V, 1.0 / np.sqrt(hd), True))
+    o = O.transpose(0, 2, 1, 3).reshape(T, Dm)
+    a = r(matmul(o, w_o))
+    x2 = r(add(x, a))
+    h2 = r(rmsnorm(x2, g2, eps))
+    gt = r(matmul(h2, w_gate))
+    up = r(matmul(h2, w_up))
+    f = r(swiglu(gt, up))
+    d = r(matmul(f, w_down))
+    y = r(add(x2, d))
+    if return_intermediates:
+        return y, dict(h1=h1, qkv=qkv, O=O, a=a, x2=x2, h2=h2, gate=gt, up=up, f=f, d=d)
+    return y
+
+
+def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
+                       tokens, eps: float = 1e-6):
+    """The same block as `llama_block`, evaluated only at the listed tokens
+    (t = b*seq + s).  Keys and values are formed for every position up to the
+    largest listed s of each batch, as causal attention needs them.  Every
+    row is computed exactly as in the full version, so the rows agree with
+    it bit for bit."""
+    x = _f64(x)
+    T, Dm = x.shape
+    hd = Dm // heads
+    r = round_bf16
+    tokens = np.asarray(tokens, dtype=np.int64)
+    y = np.empty((tokens.size, Dm))
+    for b in sorted(set((tokens // seq).tolist())):
+        sel = np.nonzero(tokens // seq == b)[0]
+        ss = tokens[sel] % seq
+        smax = int(ss.max())
+        rows = x[b * seq: b * seq + smax + 1]
+        h1 = r(rmsnorm(rows, g1, eps))
+        qkv = r(matmul(h1, w_qkv))
+        v5 = qkv.reshape(1, smax + 1, 3, heads, hd).transpose(2, 0, 3, 1, 4)
+        Q, K, V = v5[0], v5[1], v5[2]
+        q_rows = np.array([(0, h, s) for s in ss for h in range(heads)], dtype=np.int64)
+        O = r(attention_rows(Q, K, V, q_rows, 1.0 / np.sqrt(hd), True)).reshape(len(ss), heads * hd)
+        a = r(matmul(O, w_o))
+        x2 = r(add(rows[ss], a))
+        h2 = r(rmsnorm(x2, g2, eps))
+        f = r(swiglu(r(matmul(h2, w_gate)), r(matmul(h2, w_up))))
+        y[sel] = r(add(x2, r(matmul(f, w_down))))
+    return y
