@@ -1,0 +1,252 @@
+/*
+ * ja.h -- C ABI of libja, a one-GPU join-agg engine for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Model ("Every Kernel Is a Join: Automatic Multi-GPU Parallelism for AI
+ * Computations in Einsummable", paperpeel full text):
+ *   - a tensor relation is a set of (key, sub-tensor) pairs (section 1,
+ *     section 3.2); here the key of a block is its coordinate in a
+ *     per-dimension interval grid and the block is the projection of the
+ *     tensor onto that box;
+ *   - an operator is executed as a join of input blocks into n-tuples, a
+ *     per-tuple kernel f, an aggregation (the operator's sum-like operator,
+ *     which need not be addition, section 5.2) of all partial results that
+ *     share an output type, and a recompose of the aggregated blocks
+ *     (section 3.2, Definition 3.7);
+ *   - the join-agg spec for a request holds exactly one function spec per
+ *     combination of intervals of the shardable indices (section 3.3);
+ *   - between operators, data is re-blocked through the atoms of the overlay
+ *     of producer and consumer blockings (section 5.3).
+ *
+ * On one GPU the pages' "one function spec per processor" becomes "one tuple
+ * per unit of kernel work": tuples map to workgroups, and aggregation is fused
+ * into the tuple kernel (eager aggregation) unless the unfused entry points
+ * ja_kernel / ja_agg are used.
+ *
+ * Conventions for every entry point:
+ *   - No exceptions cross the ABI.  Every function returns a ja_status; on
+ *     failure ja_last_error() returns a thread-local message.
+ *   - All validation of specs, decompositions and relation descriptors runs on
+ *     the host before any HIP call, so every error except JA_ERR_HIP can be
+ *     raised without a GPU.
+ *   - The library never allocates device memory.  Device buffers (relations,
+ *     plan tables, workspaces) are owned by the caller; their sizes come from
+ *     the *_bytes queries.  Host handles (ja_spec, ja_decomp, ja_tuples,
+ *     ja_plan, ja_repart) are owned by the library until the matching
+ *     *_destroy call.
+ *   - A `stream` argument is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Run calls are asynchronous on that stream and never
+ *     synchronise the host; upload calls block until their copy is complete.
+ *   - Device pointers must be 16-byte aligned.
+ *
+ * Relation storage layout (one contiguous device buffer per relation):
+ * blocks are stored back to back in lexicographic order of their keys (first
+ * dimension slowest); every block is dense row-major over its own box.  A
+ * relation with one block per dimension is an ordinary dense row-major
+ * tensor.
+ */
+#ifndef JA_H
+#define JA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JA_MAX_RANK 8
+#define JA_ABI_VERSION 1
+
+typedef int32_t ja_status;
+#define JA_OK 0
+#define JA_ERR_ARG (-1)         /* null pointer, bad enum or count */
+#define JA_ERR_SPEC (-2)        /* malformed einsum string, op name or params */
+#define JA_ERR_DECOMP (-3)      /* bad intervals: not a tiling, wrong count, or a letter that may not be split */
+#define JA_ERR_SHAPE (-4)       /* relation shape or blocking does not match the spec / decomposition */
+#define JA_ERR_DTYPE (-5)       /* unsupported or mismatched element type */
+#define JA_ERR_WORKSPACE (-6)   /* a caller buffer is smaller than the size query returned */
+#define JA_ERR_UNSUPPORTED (-7) /* valid request that this build has no kernel for */
+#define JA_ERR_HIP (-8)         /* a HIP runtime call failed (message in ja_last_error) */
+#define JA_ERR_STATE (-9)       /* plan used before ja_plan_upload / ja_repart_upload */
+
+typedef enum { JA_F32 = 0, JA_BF16 = 1, JA_F16 = 2 } ja_dtype;
+
+/* Aggregation operators for ja_agg (section 3.2 step 2; section 5.2). */
+typedef enum { JA_AGG_SUM = 0, JA_AGG_MAX = 1 } ja_agg_op;
+
+/* A blocked tensor relation.  For dimension d, the blocks' boundaries are
+ * splits[d][0] = 0 < splits[d][1] < ... < splits[d][nblk[d]] = shape[d]
+ * (half-open intervals).  splits[d] may be NULL: then dimension d is cut into
+ * nblk[d] near-equal intervals, the first (shape[d] mod nblk[d]) of them one
+ * element longer.  The descriptor and its split arrays are read only during
+ * the call they are passed to. */
+typedef struct ja_relation_desc {
+    int32_t rank;                       /* 1 .. JA_MAX_RANK */
+    int32_t dtype;                      /* ja_dtype */
+    int64_t shape[JA_MAX_RANK];         /* logical extents, > 0 */
+    int32_t nblk[JA_MAX_RANK];          /* blocks per dimension, 1 .. shape[d] */
+    const int64_t* splits[JA_MAX_RANK]; /* nblk[d] + 1 points, or NULL */
+} ja_relation_desc;
+
+/* Logical re-indexing applied by a repartition: the source tensor is read
+ * row-major as shape[0..rank), its axes are permuted (axis k of the result is
+ * axis perm[k] of the view), and the result is read row-major as the
+ * destination's shape.  Element counts must agree. */
+typedef struct ja_view {
+    int32_t rank;
+    int64_t shape[JA_MAX_RANK];
+    int32_t perm[JA_MAX_RANK];
+} ja_view;
+
+typedef struct ja_spec ja_spec;
+typedef struct ja_decomp ja_decomp;
+typedef struct ja_tuples ja_tuples;
+typedef struct ja_plan ja_plan;
+typedef struct ja_repart ja_repart;
+
+/* ---- diagnostics ------------------------------------------------------ */
+
+int32_t ja_abi_version(void);
+/* Static string naming a status code. */
+const char* ja_status_str(ja_status status);
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* ja_last_error(void);
+
+/* ---- relations (section 3.1 tensor types and tilings; section 3.2) ----- */
+
+/* Total bytes of the relation's buffer. */
+ja_status ja_relation_bytes(const ja_relation_desc* rel, size_t* bytes);
+/* Number of blocks (the product of nblk). */
+ja_status ja_relation_nblocks(const ja_relation_desc* rel, int64_t* nblocks);
+/* Box [lo, hi) of the block with key `key` (rank entries) and its byte
+ * offset in the relation buffer. */
+ja_status ja_relation_block(const ja_relation_desc* rel, const int64_t* key, int64_t* lo, int64_t* hi,
+                            size_t* byte_off);
+
+/* ---- operators and join-agg specs (section 3.2, section 3.3) ---------- */
+
+/* An abstract operator over named indices, written as an einsum string whose
+ * letters ('a'..'z') are the named indices; the letters' order of first
+ * appearance is the "letter order" used by every per-letter array below.
+ *
+ *   op "contract":  "A,B->C", two operands (e.g. "ij,jk->ik").  f is the
+ *                   block contraction; letters absent from the output are
+ *                   aggregated with SUM (section 3.2, Examples 3.8, 3.9).
+ *                   Every letter must appear in at least two of A, B, C.
+ *   op "attention": "Q,K,V->O" with Q = O = [batch..., s, d] and
+ *                   K = V = [batch..., t, d] (e.g. "bhsd,bhtd,bhtd->bhsd").
+ *                   Scores Q K^T * scale joined on d; aggregation over t with
+ *                   the online-softmax triple (max, sum of exponentials,
+ *                   weighted sum of values); then O = weighted sum / sum.
+ *                   params: "scale=<float>" (default 1/sqrt(|d|)),
+ *                   "causal=<s>,<t>" (key t visible to query s iff t <= s;
+ *                   fully masked tuples are dropped at join).
+ *   op "rmsnorm":   "rd,d->rd": y = x / sqrt(mean_d x^2 + eps) * gain; the
+ *                   per-row sum of squares is SUM-aggregated over d blocks,
+ *                   then joined 1:1 with x and gain.  params "eps=<float>"
+ *                   (default 1e-6).
+ *   op "swiglu":    "rf,rf->rf": h = g / (1 + exp(-g)) * u, a 1:1 key join.
+ *   op "add":       "rd,rd->rd": c = a + b, a 1:1 key join.
+ */
+ja_status ja_spec_create(const char* einsum, const char* op, const char* params, ja_spec** out);
+void ja_spec_destroy(ja_spec* spec);
+/* Letters in letter order, NUL-terminated, into buf (cap >= 27 suffices). */
+ja_status ja_spec_letters(const ja_spec* spec, char* buf, size_t cap);
+
+/* A decomposition: the intervals requested for every letter (section 3.3).
+ * extents[i] is the extent of letter i (letter order).  For letter i either
+ * splits[i] (intervals[i] + 1 points from 0 to extents[i]) is given, or
+ * splits == NULL / splits[i] == NULL and the letter is cut into intervals[i]
+ * near-equal intervals.  Letters an operator cannot split (attention: the
+ * head dimension d) must have one interval (JA_ERR_DECOMP otherwise). */
+ja_status ja_decomp_create(const ja_spec* spec, const int64_t* extents, const int32_t* intervals,
+                           const int64_t* const* splits, ja_decomp** out);
+void ja_decomp_destroy(ja_decomp* decomp);
+
+/* ---- join: the tuple list (section 3.2 step 1) ------------------------- */
+
+/* Enumerate the join-agg spec's function specs: one tuple per cell of the
+ * interval grid (product of the interval counts), minus cells removed by
+ * the operator's join predicate (causal attention drops a cell when its key
+ * interval starts at or after the end of its query interval).  Tuples are
+ * sorted by their group-by key (contract and attention: the output letters;
+ * rmsnorm: the row letter; swiglu and add: all letters), then by the other
+ * letters' interval indices in letter order.  Equal group-by keys form one
+ * aggregation segment.  Host only, deterministic. */
+ja_status ja_join(const ja_spec* spec, const ja_decomp* decomp, ja_tuples** out);
+ja_status ja_tuples_count(const ja_tuples* tuples, int64_t* n_tuples, int64_t* n_segs, int32_t* n_letters);
+/* rec: n_tuples * n_letters int32 (each record = the interval index of every
+ * letter, letter order); seg_off: n_segs + 1 int64 CSR offsets. */
+ja_status ja_tuples_export(const ja_tuples* tuples, int32_t* rec, int64_t rec_cap, int64_t* seg_off,
+                           int64_t seg_cap);
+void ja_tuples_destroy(ja_tuples* tuples);
+
+/* ---- plans: join + fused kernel + aggregation + recompose -------------- */
+
+/* Validate the relations against the spec and decomposition (each input and
+ * the output must be blocked exactly as the decomposition cuts their letters;
+ * dtypes: contract f32 x f32 -> f32 or bf16 x bf16 -> bf16 / f32; attention,
+ * rmsnorm, swiglu, add: bf16), run the join, and build the device tables. */
+ja_status ja_plan_create(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
+                         int32_t n_in, const ja_relation_desc* out, ja_plan** plan);
+/* table_bytes: device buffer size for ja_plan_upload; workspace_bytes: the
+ * workspace ja_plan_run needs (may be 0). */
+ja_status ja_plan_device_bytes(const ja_plan* plan, size_t* table_bytes, size_t* workspace_bytes);
+/* Copy the plan's tables to dev_buf (at least table_bytes) on `stream` and
+ * wait for the copy.  The buffer must stay alive while the plan is run. */
+ja_status ja_plan_upload(ja_plan* plan, void* dev_buf, size_t bytes, void* stream);
+/* Run the whole join-agg: every tuple's kernel with the aggregation fused
+ * into it, writing each output block exactly once (recompose in place).
+ * in_ptrs[i] / out_ptr: device buffers of the relations given at create. */
+ja_status ja_plan_run(const ja_plan* plan, const void* const* in_ptrs, void* out_ptr, void* workspace,
+                      void* stream);
+/* Unfused path (contract only): ja_kernel writes every tuple's partial
+ * output block in float32 to `partials` (ja_plan_partial_bytes bytes; tuple
+ * i's block starts after the blocks of tuples 0..i-1, dense row-major);
+ * ja_agg folds each segment's partials in ascending tuple order with `op`
+ * and writes the output relation. */
+ja_status ja_plan_partial_bytes(const ja_plan* plan, size_t* bytes);
+ja_status ja_kernel(const ja_plan* plan, const void* const* in_ptrs, void* partials, void* stream);
+ja_status ja_agg(const ja_plan* plan, ja_agg_op op, const void* partials, void* out_ptr, void* stream);
+void ja_plan_destroy(ja_plan* plan);
+
+/* One-shot convenience: create a plan, upload its tables into dev_ws, run,
+ * and destroy the plan.  Blocks until the table upload is done; the run
+ * itself stays asynchronous.  ws_bytes must be at least the value returned
+ * by ja_einsum_workspace_bytes. */
+ja_status ja_einsum_workspace_bytes(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
+                                    int32_t n_in, const ja_relation_desc* out, size_t* bytes);
+ja_status ja_einsum(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
+                    const void* const* in_ptrs, int32_t n_in, const ja_relation_desc* out, void* out_ptr,
+                    void* dev_ws, size_t ws_bytes, void* stream);
+
+/* ---- repartition (section 4.3 repartition cost; section 5.3 atoms) ----- */
+
+/* Plan the re-blocking of `src` into `dst`, optionally through `view` (NULL:
+ * identity; then the shapes must be equal).  Both relations must have the
+ * same dtype.  The plan's atoms are the cells of the overlay of both
+ * blockings, refined so that every atom is a box in both; every destination
+ * element is written exactly once, by a copy of its source bytes.  The
+ * reshapes of the view must factor into common sub-dimensions
+ * (JA_ERR_UNSUPPORTED otherwise). */
+ja_status ja_repart_create(const ja_relation_desc* src, const ja_relation_desc* dst, const ja_view* view,
+                           ja_repart** out);
+/* n_atoms: overlay cells; n_tasks: device copy tasks (atoms, possibly cut
+ * into chunks). */
+ja_status ja_repart_count(const ja_repart* rp, int64_t* n_atoms, int64_t* n_tasks);
+ja_status ja_repart_device_bytes(const ja_repart* rp, size_t* table_bytes);
+ja_status ja_repart_upload(ja_repart* rp, void* dev_buf, size_t bytes, void* stream);
+ja_status ja_repart_run(const ja_repart* rp, const void* src_ptr, void* dst_ptr, void* stream);
+void ja_repart_destroy(ja_repart* rp);
+/* One-shot convenience (create, upload into dev_ws, run, destroy). */
+ja_status ja_repartition_workspace_bytes(const ja_relation_desc* src, const ja_relation_desc* dst,
+                                         const ja_view* view, size_t* bytes);
+ja_status ja_repartition(const ja_relation_desc* src, const void* src_ptr, const ja_relation_desc* dst,
+                         void* dst_ptr, const ja_view* view, void* dev_ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JA_H */

@@ -1,0 +1,372 @@
+"""ctypes binding of libja's C ABI (include/ja.h).
+
+Argument marshalling only: every function here forwards to the entry point of
+the same name in libja.so, which runs the whole join-agg path in its HIP
+kernels.  Device pointers and streams are plain integers (for example
+``tensor.data_ptr()`` and ``torch.cuda.current_stream().cuda_stream``).
+Failures raise JaError with the library's status and message.
+
+If libja.so has not been built the import fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libja.so")
+
+JA_MAX_RANK = 8
+JA_F32, JA_BF16, JA_F16 = 0, 1, 2
+JA_AGG_SUM, JA_AGG_MAX = 0, 1
+STATUS = {0: "JA_OK", -1: "JA_ERR_ARG", -2: "JA_ERR_SPEC", -3: "JA_ERR_DECOMP", -4: "JA_ERR_SHAPE",
+          -5: "JA_ERR_DTYPE", -6: "JA_ERR_WORKSPACE", -7: "JA_ERR_UNSUPPORTED", -8: "JA_ERR_HIP",
+          -9: "JA_ERR_STATE"}
+DTYPE_SIZE = {JA_F32: 4, JA_BF16: 2, JA_F16: 2}
+
+
+class JaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.name = STATUS.get(status, "JA_ERR_UNKNOWN")
+        super().__init__("%s: %s" % (self.name, message))
+
+
+class ja_relation_desc(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * JA_MAX_RANK), ("nblk", ctypes.c_int32 * JA_MAX_RANK),
+                ("splits", ctypes.POINTER(ctypes.c_int64) * JA_MAX_RANK)]
+
+
+class ja_view(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("shape", ctypes.c_int64 * JA_MAX_RANK),
+                ("perm", ctypes.c_int32 * JA_MAX_RANK)]
+
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_st = ctypes.c_int32
+_descp = ctypes.POINTER(ja_relation_desc)
+_descpp = ctypes.POINTER(_descp)
+_viewp = ctypes.POINTER(ja_view)
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "ja_abi_version": (_i32, []),
+    "ja_status_str": (ctypes.c_char_p, [_st]),
+    "ja_last_error": (ctypes.c_char_p, []),
+    "ja_relation_bytes": (_st, [_descp, ctypes.POINTER(_sz)]),
+    "ja_relation_nblocks": (_st, [_descp, ctypes.POINTER(_i64)]),
+    "ja_relation_block": (_st, [_descp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                ctypes.POINTER(_sz)]),
+    "ja_spec_create": (_st, [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, ctypes.POINTER(_vp)]),
+    "ja_spec_destroy": (None, [_vp]),
+    "ja_spec_letters": (_st, [_vp, ctypes.c_char_p, _sz]),
+    "ja_decomp_create": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32),
+                               ctypes.POINTER(ctypes.POINTER(_i64)), ctypes.POINTER(_vp)]),
+    "ja_decomp_destroy": (None, [_vp]),
+    "ja_join": (_st, [_vp, _vp, ctypes.POINTER(_vp)]),
+    "ja_tuples_count": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
+    "ja_tuples_export": (_st, [_vp, ctypes.POINTER(_i32), _i64, ctypes.POINTER(_i64), _i64]),
+    "ja_tuples_destroy": (None, [_vp]),
+    "ja_plan_create": (_st, [_vp, _vp, _descpp, _i32, _descp, ctypes.POINTER(_vp)]),
+    "ja_plan_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "ja_plan_upload": (_st, [_vp, _vp, _sz, _vp]),
+    "ja_plan_run": (_st, [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp]),
+    "ja_plan_partial_bytes": (_st, [_vp, ctypes.POINTER(_sz)]),
+    "ja_kernel": (_st, [_vp, ctypes.POINTER(_vp), _vp, _vp]),
+    "ja_agg": (_st, [_vp, _i32, _vp, _vp, _vp]),
+    "ja_plan_destroy": (None, [_vp]),
+    "ja_einsum_workspace_bytes": (_st, [_vp, _vp, _descpp, _i32, _descp, ctypes.POINTER(_sz)]),
+    "ja_einsum": (_st, [_vp, _vp, _descpp, ctypes.POINTER(_vp), _i32, _descp, _vp, _vp, _sz, _vp]),
+    "ja_repart_create": (_st, [_descp, _descp, _viewp, ctypes.POINTER(_vp)]),
+    "ja_repart_count": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "ja_repart_device_bytes": (_st, [_vp, ctypes.POINTER(_sz)]),
+    "ja_repart_upload": (_st, [_vp, _vp, _sz, _vp]),
+    "ja_repart_run": (_st, [_vp, _vp, _vp, _vp]),
+    "ja_repart_destroy": (None, [_vp]),
+    "ja_repartition_workspace_bytes": (_st, [_descp, _descp, _viewp, ctypes.POINTER(_sz)]),
+    "ja_repartition": (_st, [_descp, _vp, _descp, _vp, _viewp, _vp, _sz, _vp]),
+}
+
+EXPORTED = sorted(_SIGS)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libja.so is not built (%s); run `python -m tensor_relational_join_amd.build`" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def _check(st: int):
+    if st != 0:
+        raise JaError(st, _lib.ja_last_error().decode())
+
+
+def raw():
+    """The loaded ctypes library."""
+    return _lib
+
+
+# --------------------------------------------------------------------------- descriptors
+
+class Relation:
+    """Owner of a ja_relation_desc and its split arrays."""
+
+    def __init__(self, shape: Sequence[int], nblk: Optional[Sequence[int]] = None,
+                 splits: Optional[Sequence[Optional[Sequence[int]]]] = None, dtype: int = JA_BF16):
+        rank = len(shape)
+        if not 1 <= rank <= JA_MAX_RANK:
+            raise ValueError("rank must be 1..8")
+        self.shape = tuple(int(x) for x in shape)
+        self.dtype = dtype
+        d = ja_relation_desc()
+        d.rank = rank
+        d.dtype = dtype
+        self._keep = []
+        for i in range(rank):
+            d.shape[i] = self.shape[i]
+            sp = splits[i] if splits is not None else None
+            if sp is not None:
+                arr = (ctypes.c_int64 * len(sp))(*[int(x) for x in sp])
+                self._keep.append(arr)
+                d.splits[i] = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64))
+                d.nblk[i] = len(sp) - 1
+            else:
+                d.nblk[i] = int(nblk[i]) if nblk is not None else 1
+        self.desc = d
+        self.nblk = tuple(int(d.nblk[i]) for i in range(rank))
+
+    @property
+    def ptr(self):
+        return ctypes.pointer(self.desc)
+
+    @property
+    def nbytes(self) -> int:
+        return ja_relation_bytes(self)
+
+
+def _desc_array(rels):
+    arr = (_descp * len(rels))()
+    for i, r in enumerate(rels):
+        arr[i] = r.ptr
+    return arr
+
+
+def _ptr_array(ptrs):
+    arr = (_vp * len(ptrs))()
+    for i, p in enumerate(ptrs):
+        arr[i] = _vp(int(p))
+    return arr
+
+
+def make_view(shape: Sequence[int], perm: Sequence[int]) -> ja_view:
+    v = ja_view()
+    v.rank = len(shape)
+    for i, (s, p) in enumerate(zip(shape, perm)):
+        v.shape[i] = int(s)
+        v.perm[i] = int(p)
+    return v
+
+
+# --------------------------------------------------------------------------- entry points
+
+def ja_abi_version() -> int:
+    return int(_lib.ja_abi_version())
+
+
+def ja_status_str(status: int) -> str:
+    return _lib.ja_status_str(status).decode()
+
+
+def ja_last_error() -> str:
+    return _lib.ja_last_error().decode()
+
+
+def ja_relation_bytes(rel: Relation) -> int:
+    n = _sz()
+    _check(_lib.ja_relation_bytes(rel.ptr, ctypes.byref(n)))
+    return n.value
+
+
+def ja_relation_nblocks(rel: Relation) -> int:
+    n = _i64()
+    _check(_lib.ja_relation_nblocks(rel.ptr, ctypes.byref(n)))
+    return n.value
+
+
+def ja_relation_block(rel: Relation, key: Sequence[int]):
+    r = len(rel.shape)
+    k = (_i64 * r)(*key)
+    lo, hi, off = (_i64 * r)(), (_i64 * r)(), _sz()
+    _check(_lib.ja_relation_block(rel.ptr, k, lo, hi, ctypes.byref(off)))
+    return tuple(lo), tuple(hi), off.value
+
+
+def ja_spec_create(einsum: str, op: str, params: str = "") -> int:
+    h = _vp()
+    _check(_lib.ja_spec_create(einsum.encode(), op.encode(), params.encode(), ctypes.byref(h)))
+    return h.value
+
+
+def ja_spec_destroy(spec: int):
+    _lib.ja_spec_destroy(_vp(spec))
+
+
+def ja_spec_letters(spec: int) -> str:
+    buf = ctypes.create_string_buffer(32)
+    _check(_lib.ja_spec_letters(_vp(spec), buf, 32))
+    return buf.value.decode()
+
+
+def ja_decomp_create(spec: int, extents: Sequence[int], intervals: Sequence[int],
+                     splits: Optional[Sequence[Optional[Sequence[int]]]] = None) -> int:
+    n = len(extents)
+    ext = (_i64 * n)(*extents)
+    iv = (_i32 * n)(*intervals)
+    sp = None
+    keep = []
+    if splits is not None:
+        sp = (ctypes.POINTER(_i64) * n)()
+        for i, s in enumerate(splits):
+            if s is not None:
+                arr = (_i64 * len(s))(*s)
+                keep.append(arr)
+                sp[i] = ctypes.cast(arr, ctypes.POINTER(_i64))
+    h = _vp()
+    _check(_lib.ja_decomp_create(_vp(spec), ext, iv, sp, ctypes.byref(h)))
+    return h.value
+
+
+def ja_decomp_destroy(decomp: int):
+    _lib.ja_decomp_destroy(_vp(decomp))
+
+
+def ja_join(spec: int, decomp: int) -> int:
+    h = _vp()
+    _check(_lib.ja_join(_vp(spec), _vp(decomp), ctypes.byref(h)))
+    return h.value
+
+
+def ja_tuples_count(tuples: int):
+    nt, ns, nl = _i64(), _i64(), _i32()
+    _check(_lib.ja_tuples_count(_vp(tuples), ctypes.byref(nt), ctypes.byref(ns), ctypes.byref(nl)))
+    return nt.value, ns.value, nl.value
+
+
+def ja_tuples_export(tuples: int):
+    """(records as a list of per-letter interval indices, segment offsets)."""
+    import numpy as np
+
+    nt, ns, nl = ja_tuples_count(tuples)
+    rec = np.zeros(max(nt * nl, 1), dtype=np.int32)
+    seg = np.zeros(ns + 1, dtype=np.int64)
+    _check(_lib.ja_tuples_export(_vp(tuples), rec.ctypes.data_as(ctypes.POINTER(_i32)), rec.size,
+                                 seg.ctypes.data_as(ctypes.POINTER(_i64)), seg.size))
+    return rec[: nt * nl].reshape(nt, nl), seg
+
+
+def ja_tuples_destroy(tuples: int):
+    _lib.ja_tuples_destroy(_vp(tuples))
+
+
+def ja_plan_create(spec: int, decomp: int, ins: Sequence[Relation], out: Relation) -> int:
+    h = _vp()
+    _check(_lib.ja_plan_create(_vp(spec), _vp(decomp), _desc_array(ins), len(ins), out.ptr, ctypes.byref(h)))
+    return h.value
+
+
+def ja_plan_device_bytes(plan: int):
+    tb, wb = _sz(), _sz()
+    _check(_lib.ja_plan_device_bytes(_vp(plan), ctypes.byref(tb), ctypes.byref(wb)))
+    return tb.value, wb.value
+
+
+def ja_plan_upload(plan: int, dev_buf: int, nbytes: int, stream: int = 0):
+    _check(_lib.ja_plan_upload(_vp(plan), _vp(dev_buf), nbytes, _vp(stream)))
+
+
+def ja_plan_run(plan: int, in_ptrs: Sequence[int], out_ptr: int, workspace: int = 0, stream: int = 0):
+    _check(_lib.ja_plan_run(_vp(plan), _ptr_array(in_ptrs), _vp(out_ptr), _vp(workspace), _vp(stream)))
+
+
+def ja_plan_partial_bytes(plan: int) -> int:
+    n = _sz()
+    _check(_lib.ja_plan_partial_bytes(_vp(plan), ctypes.byref(n)))
+    return n.value
+
+
+def ja_kernel(plan: int, in_ptrs: Sequence[int], partials: int, stream: int = 0):
+    _check(_lib.ja_kernel(_vp(plan), _ptr_array(in_ptrs), _vp(partials), _vp(stream)))
+
+
+def ja_agg(plan: int, op: int, partials: int, out_ptr: int, stream: int = 0):
+    _check(_lib.ja_agg(_vp(plan), op, _vp(partials), _vp(out_ptr), _vp(stream)))
+
+
+def ja_plan_destroy(plan: int):
+    _lib.ja_plan_destroy(_vp(plan))
+
+
+def ja_einsum_workspace_bytes(spec: int, decomp: int, ins: Sequence[Relation], out: Relation) -> int:
+    n = _sz()
+    _check(_lib.ja_einsum_workspace_bytes(_vp(spec), _vp(decomp), _desc_array(ins), len(ins), out.ptr,
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def ja_einsum(spec: int, decomp: int, ins: Sequence[Relation], in_ptrs: Sequence[int], out: Relation,
+              out_ptr: int, dev_ws: int, ws_bytes: int, stream: int = 0):
+    _check(_lib.ja_einsum(_vp(spec), _vp(decomp), _desc_array(ins), _ptr_array(in_ptrs), len(ins), out.ptr,
+                          _vp(out_ptr), _vp(dev_ws), ws_bytes, _vp(stream)))
+
+
+def _view_ptr(view: Optional[ja_view]):
+    return ctypes.pointer(view) if view is not None else None
+
+
+def ja_repart_create(src: Relation, dst: Relation, view: Optional[ja_view] = None) -> int:
+    h = _vp()
+    _check(_lib.ja_repart_create(src.ptr, dst.ptr, _view_ptr(view), ctypes.byref(h)))
+    return h.value
+
+
+def ja_repart_count(rp: int):
+    na, nt = _i64(), _i64()
+    _check(_lib.ja_repart_count(_vp(rp), ctypes.byref(na), ctypes.byref(nt)))
+    return na.value, nt.value
+
+
+def ja_repart_device_bytes(rp: int) -> int:
+    n = _sz()
+    _check(_lib.ja_repart_device_bytes(_vp(rp), ctypes.byref(n)))
+    return n.value
+
+
+def ja_repart_upload(rp: int, dev_buf: int, nbytes: int, stream: int = 0):
+    _check(_lib.ja_repart_upload(_vp(rp), _vp(dev_buf), nbytes, _vp(stream)))
+
+
+def ja_repart_run(rp: int, src_ptr: int, dst_ptr: int, stream: int = 0):
+    _check(_lib.ja_repart_run(_vp(rp), _vp(src_ptr), _vp(dst_ptr), _vp(stream)))
+
+
+def ja_repart_destroy(rp: int):
+    _lib.ja_repart_destroy(_vp(rp))
+
+
+def ja_repartition_workspace_bytes(src: Relation, dst: Relation, view: Optional[ja_view] = None) -> int:
+    n = _sz()
+    _check(_lib.ja_repartition_workspace_bytes(src.ptr, dst.ptr, _view_ptr(view), ctypes.byref(n)))
+    return n.value
+
+
+def ja_repartition(src: Relation, src_ptr: int, dst: Relation, dst_ptr: int, view: Optional[ja_view],
+                   dev_ws: int, ws_bytes: int, stream: int = 0):
+    _check(_lib.ja_repartition(src.ptr, _vp(src_ptr), dst.ptr, _vp(dst_ptr), _view_ptr(view), _vp(dev_ws),
+                               ws_bytes, _vp(stream)))

@@ -1,0 +1,284 @@
+// stream_ops.hip -- the HBM-bound kernels of libja: repartition copies,
+// the 1:1 key joins (SwiGLU, residual add), RMSNorm, and the standalone
+// segmented aggregation.
+//
+// All of them stream: coalesced 16-byte loads issued back to back before any
+// use, arithmetic in fp32, one pass over the data.
+#include "dev_common.h"
+
+namespace ja {
+
+// ---------------------------------------------------------------- repartition
+// One workgroup per copy task (at most REP_CHUNK elements).  Each thread
+// first loads all of its 16-byte vectors, then stores them.
+constexpr int REP_THREADS = 256;
+constexpr int REP_MAXV = 8;  // vectors per thread per pass
+
+__global__ __launch_bounds__(REP_THREADS) void repart_kernel(const RepTask* __restrict__ tasks,
+                                                             const uint8_t* __restrict__ src,
+                                                             uint8_t* __restrict__ dst, int32_t esize) {
+    const RepTask t = tasks[blockIdx.x];
+    const uint32_t n1 = t.n[1], n2 = t.n[2], n3 = t.n[3];
+    const uint32_t rows = (uint32_t)t.n[0] * n1 * n2;
+    if (t.flags & REP_VEC) {
+        const uint32_t vpe = 16 / esize;  // elements per vector
+        const uint32_t vpr = n3 / vpe;    // vectors per row
+        const uint32_t total = rows * vpr;
+        for (uint32_t base = 0; base < total; base += REP_THREADS * REP_MAXV) {
+            uint4 v[REP_MAXV];
+            int64_t doff[REP_MAXV];
+#pragma unroll
+            for (int j = 0; j < REP_MAXV; ++j) {
+                uint32_t i = base + threadIdx.x + j * REP_THREADS;
+                doff[j] = -1;
+                if (i < total) {
+                    uint32_t r = i / vpr, c = i - r * vpr;
+                    uint32_t i2 = r % n2, r1 = r / n2;
+                    uint32_t i1 = r1 % n1, i0 = r1 / n1;
+                    int64_t so = t.src_off + i0 * t.ss[0] + i1 * t.ss[1] + i2 * t.ss[2] + (int64_t)c * vpe;
+                    doff[j] = t.dst_off + i0 * t.ds[0] + i1 * t.ds[1] + i2 * t.ds[2] + (int64_t)c * vpe;
+                    v[j] = *reinterpret_cast<const uint4*>(src + so * esize);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < REP_MAXV; ++j)
+                if (doff[j] >= 0) *reinterpret_cast<uint4*>(dst + doff[j] * esize) = v[j];
+        }
+    } else {
+        const uint32_t total = rows * n3;
+        for (uint32_t i = threadIdx.x; i < total; i += REP_THREADS) {
+            uint32_t r = i / n3, c = i - r * n3;
+            uint32_t i2 = r % n2, r1 = r / n2;
+            uint32_t i1 = r1 % n1, i0 = r1 / n1;
+            int64_t so = t.src_off + i0 * t.ss[0] + i1 * t.ss[1] + i2 * t.ss[2] + (int64_t)c * t.ss[3];
+            int64_t dof = t.dst_off + i0 * t.ds[0] + i1 * t.ds[1] + i2 * t.ds[2] + (int64_t)c * t.ds[3];
+            if (esize == 2)
+                *reinterpret_cast<uint16_t*>(dst + dof * 2) = *reinterpret_cast<const uint16_t*>(src + so * 2);
+            else
+                *reinterpret_cast<uint32_t*>(dst + dof * 4) = *reinterpret_cast<const uint32_t*>(src + so * 4);
+        }
+    }
+}
+
+hipError_t launch_repart(const void* table, int64_t ntasks, const void* src, void* dst, int32_t esize,
+                         int32_t vec_ok, hipStream_t stream) {
+    (void)vec_ok;
+    const RepTask* tasks = (const RepTask*)table;
+    for (int64_t first = 0; first < ntasks; first += 0x7fffffff) {
+        int64_t n = ntasks - first < 0x7fffffff ? ntasks - first : 0x7fffffff;
+        hipLaunchKernelGGL(repart_kernel, dim3((unsigned)n), dim3(REP_THREADS), 0, stream, tasks + first,
+                           (const uint8_t*)src, (uint8_t*)dst, esize);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- 1:1 joins
+// The three relations are identically blocked, so the join is a zip of the
+// flat buffers.  Each thread handles ZIP_V vectors of 8 bf16.
+constexpr int ZIP_THREADS = 256;
+constexpr int ZIP_V = 4;
+
+template <int OP>  // 0: swiglu, 1: add
+__global__ __launch_bounds__(ZIP_THREADS) void zip_kernel(const uint4* __restrict__ a, const uint4* __restrict__ b,
+                                                          uint4* __restrict__ c, int64_t nvec) {
+    const int64_t base = (int64_t)blockIdx.x * ZIP_THREADS * ZIP_V + threadIdx.x;
+    uint4 va[ZIP_V], vb[ZIP_V];
+#pragma unroll
+    for (int j = 0; j < ZIP_V; ++j) {
+        int64_t i = base + j * ZIP_THREADS;
+        if (i < nvec) {
+            va[j] = a[i];
+            vb[j] = b[i];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < ZIP_V; ++j) {
+        int64_t i = base + j * ZIP_THREADS;
+        if (i >= nvec) continue;
+        uint32_t x[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+        uint32_t y[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float x0 = bf16lo_to_f32(x[k]), x1 = bf16hi_to_f32(x[k]);
+            float y0 = bf16lo_to_f32(y[k]), y1 = bf16hi_to_f32(y[k]);
+            float r0, r1;
+            if (OP == 0) {
+                r0 = x0 / (1.0f + __expf(-x0)) * y0;
+                r1 = x1 / (1.0f + __expf(-x1)) * y1;
+            } else {
+                r0 = x0 + y0;
+                r1 = x1 + y1;
+            }
+            o[k] = pack_bf16x2(r0, r1);
+        }
+        c[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+template <int OP>
+__global__ void zip_tail_kernel(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t first, int64_t n) {
+    int64_t i = first + threadIdx.x;
+    if (i >= n) return;
+    float x = bf16_to_f32(a[i]), y = bf16_to_f32(b[i]);
+    float r = OP == 0 ? x / (1.0f + __expf(-x)) * y : x + y;
+    c[i] = (uint16_t)f32_to_bf16(r);
+}
+
+template <int OP>
+static hipError_t launch_zip(const void* a, const void* b, void* c, int64_t n, hipStream_t stream) {
+    int64_t nvec = n / 8;
+    if (nvec > 0) {
+        int64_t per = (int64_t)ZIP_THREADS * ZIP_V;
+        int64_t grid = (nvec + per - 1) / per;
+        hipLaunchKernelGGL(zip_kernel<OP>, dim3((unsigned)grid), dim3(ZIP_THREADS), 0, stream, (const uint4*)a,
+                           (const uint4*)b, (uint4*)c, nvec);
+    }
+    if (n % 8)
+        hipLaunchKernelGGL(zip_tail_kernel<OP>, dim3(1), dim3(8), 0, stream, (const uint16_t*)a, (const uint16_t*)b,
+                           (uint16_t*)c, nvec * 8, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const void* g, const void* u, void* h, int64_t n, hipStream_t stream) {
+    return launch_zip<0>(g, u, h, n, stream);
+}
+hipError_t launch_add(const void* a, const void* b, void* c, int64_t n, hipStream_t stream) {
+    return launch_zip<1>(a, b, c, n, stream);
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// One wavefront per row.  Pass 1 walks the row's pieces in every column block
+// (the join of the row's tuples), stages them in LDS and SUM-aggregates the
+// squares; pass 2 joins each piece 1:1 with the row statistic and the gain.
+constexpr int NORM_WAVES = 4;
+
+__global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t* __restrict__ rsplit, int32_t nrb,
+                                                                  const NormBlock* __restrict__ blocks, int32_t ndb,
+                                                                  int64_t rows, int32_t D,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ gain,
+                                                                  uint16_t* __restrict__ y, float eps, int32_t vec) {
+    extern __shared__ uint16_t lds_row[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * NORM_WAVES + wave;
+    if (r >= rows) return;
+    uint16_t* row = lds_row + (size_t)wave * D;
+    int rb = 0;
+    while (rb + 1 < nrb && rsplit[rb + 1] <= r) ++rb;
+    const int64_t rr = r - rsplit[rb];
+    const NormBlock* bl = blocks + (int64_t)rb * ndb;
+    float ss = 0.f;
+    for (int db = 0; db < ndb; ++db) {
+        const NormBlock b = bl[db];
+        const uint16_t* src = x + b.off + rr * b.width;
+        if (vec) {
+            for (int e = lane * 8; e < b.width; e += 512) {
+                uint4 v = *reinterpret_cast<const uint4*>(src + e);
+                *reinterpret_cast<uint4*>(row + b.d_lo + e) = v;
+                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    float a0 = bf16lo_to_f32(w[k]), a1 = bf16hi_to_f32(w[k]);
+                    ss += a0 * a0 + a1 * a1;
+                }
+            }
+        } else {
+            for (int e = lane; e < b.width; e += 64) {
+                uint16_t h = src[e];
+                row[b.d_lo + e] = h;
+                float a = bf16_to_f32(h);
+                ss += a * a;
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = rsqrtf(ss / (float)D + eps);
+    for (int db = 0; db < ndb; ++db) {
+        const NormBlock b = bl[db];
+        uint16_t* dstp = y + b.off + rr * b.width;
+        if (vec) {
+            for (int e = lane * 8; e < b.width; e += 512) {
+                uint4 v = *reinterpret_cast<const uint4*>(row + b.d_lo + e);
+                uint4 g = *reinterpret_cast<const uint4*>(gain + b.d_lo + e);
+                uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w}, o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    o[k] = pack_bf16x2(bf16lo_to_f32(w[k]) * inv * bf16lo_to_f32(gw[k]),
+                                       bf16hi_to_f32(w[k]) * inv * bf16hi_to_f32(gw[k]));
+                *reinterpret_cast<uint4*>(dstp + e) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        } else {
+            for (int e = lane; e < b.width; e += 64)
+                dstp[e] = (uint16_t)f32_to_bf16(bf16_to_f32(row[b.d_lo + e]) * inv * bf16_to_f32(gain[b.d_lo + e]));
+        }
+    }
+}
+
+hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
+                          int64_t rows, int32_t D, const void* x, const void* gain, void* y, float eps, int32_t vec,
+                          hipStream_t stream) {
+    const uint8_t* t = (const uint8_t*)table;
+    int64_t grid = (rows + NORM_WAVES - 1) / NORM_WAVES;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)grid), dim3(NORM_WAVES * 64),
+                       (unsigned)((size_t)NORM_WAVES * D * 2), stream, (const int64_t*)(t + rsplit_off), nrb,
+                       (const NormBlock*)(t + blocks_off), ndb, rows, D, (const uint16_t*)x, (const uint16_t*)gain,
+                       (uint16_t*)y, eps, vec);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- aggregation
+// One workgroup per (segment, chunk of AGG_CHUNK output elements); each
+// thread folds its elements over the segment's tuples in ascending order and
+// writes them once.  No atomics: every output element has one owner.
+constexpr int AGG_THREADS = 256;
+
+template <int OUT_BF16>
+__global__ __launch_bounds__(AGG_THREADS) void agg_kernel(const AggTile* __restrict__ tiles,
+                                                          const AggSeg* __restrict__ segs,
+                                                          const int64_t* __restrict__ poff,
+                                                          const float* __restrict__ part, void* __restrict__ out,
+                                                          int32_t op) {
+    const AggTile tl = tiles[blockIdx.x];
+    const AggSeg sg = segs[tl.seg];
+    constexpr int PER = AGG_CHUNK / AGG_THREADS;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = op == JA_AGG_MAX ? -INFINITY : 0.f;
+    for (int t = sg.t_begin; t < sg.t_end; ++t) {
+        const float* p = part + poff[t];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            int e = tl.e0 + threadIdx.x + j * AGG_THREADS;
+            if (e < sg.nelem) {
+                float v = p[e];
+                acc[j] = op == JA_AGG_MAX ? fmaxf(acc[j], v) : acc[j] + v;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        int e = tl.e0 + threadIdx.x + j * AGG_THREADS;
+        if (e < sg.nelem) {
+            if (OUT_BF16)
+                ((uint16_t*)out)[sg.out_off + e] = (uint16_t)f32_to_bf16(acc[j]);
+            else
+                ((float*)out)[sg.out_off + e] = acc[j];
+        }
+    }
+}
+
+hipError_t launch_agg(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t poff_off,
+                      const float* partials, void* out, int32_t out_dtype, int32_t op, hipStream_t stream) {
+    const uint8_t* t = (const uint8_t*)table;
+    if (out_dtype == JA_BF16)
+        hipLaunchKernelGGL(agg_kernel<1>, dim3(ntiles), dim3(AGG_THREADS), 0, stream, (const AggTile*)(t + tiles_off),
+                           (const AggSeg*)(t + segs_off), (const int64_t*)(t + poff_off), partials, out, op);
+    else
+        hipLaunchKernelGGL(agg_kernel<0>, dim3(ntiles), dim3(AGG_THREADS), 0, stream, (const AggTile*)(t + tiles_off),
+                           (const AggSeg*)(t + segs_off), (const int64_t*)(t + poff_off), partials, out, op);
+    return hipGetLastError();
+}
+
+}  // namespace ja

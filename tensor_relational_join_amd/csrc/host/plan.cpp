@@ -1,0 +1,526 @@
+// plan.cpp -- join-agg plans: validate relations against a spec and a
+// decomposition, run the join, lay out the device tables that drive the fused
+// per-tuple kernels, and dispatch them.
+//
+// The execution follows the three phases of Definition 3.7 ("Every Kernel Is
+// a Join", paperpeel full text, section 3.2): every tuple of the join is one
+// unit of kernel work; the aggregation of tuples that share an output type is
+// fused into the kernel (one workgroup owns each output tile of a segment and
+// folds the segment's tuples in ascending order, so no atomics are needed);
+// the recompose is in place, since every aggregated block is written straight
+// into its slot of the output relation.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "ja_host.h"
+
+using namespace ja;
+
+struct ja_plan {
+    ja_op_kind kind;
+    std::vector<uint8_t> table;
+    void* dev = nullptr;
+    int32_t n_in = 0;
+    // contract
+    int64_t tiles_off = 0, segs_off = 0, tuples_off = 0;
+    int32_t ntiles = 0;
+    int64_t utiles_off = 0, usegs_off = 0;
+    int32_t nutiles = 0;
+    int64_t atiles_off = 0, asegs_off = 0, apoff_off = 0;
+    int32_t natiles = 0;
+    int32_t in_dtype = 0, out_dtype = 0, a_layout = 0, b_layout = 0;
+    int64_t partial_elems = 0;
+    // attention
+    float scale = 0.f;
+    int32_t causal = 0;
+    // rmsnorm
+    int64_t rsplit_off = 0, nblk_off = 0;
+    int32_t nrb = 0, ndb = 0, D = 0, norm_vec = 0;
+    int64_t rows = 0;
+    float eps = 0.f;
+    // 1:1 joins
+    int64_t n = 0;
+};
+
+namespace {
+
+// Append a POD array to the table at a 16-byte aligned offset.
+template <class T>
+int64_t put(std::vector<uint8_t>& tab, const std::vector<T>& v) {
+    size_t off = (tab.size() + 15) & ~(size_t)15;
+    tab.resize(off + v.size() * sizeof(T));
+    if (!v.empty()) std::memcpy(tab.data() + off, v.data(), v.size() * sizeof(T));
+    return (int64_t)off;
+}
+
+// Check that relation `r` is the projection grid the decomposition asks for:
+// one dimension per letter of `s`, extents and split points equal to the
+// decomposition's for those letters.
+ja_status match_rel(const Rel& r, const std::string& s, const ja_spec* sp, const ja_decomp* d, const char* what) {
+    if (r.rank != (int)s.size())
+        return fail(JA_ERR_SHAPE, std::string(what) + ": rank differs from its letters '" + s + "'");
+    for (int k = 0; k < r.rank; ++k) {
+        int l = sp->letter_index(s[k]);
+        if (r.shape[k] != d->ext[l])
+            return fail(JA_ERR_SHAPE, std::string(what) + ": extent of letter " + s[k] + " differs from the decomposition");
+        if (r.sp[k] != d->sp[l])
+            return fail(JA_ERR_SHAPE, std::string(what) + ": blocking of letter " + s[k] +
+                                          " differs from the decomposition (repartition it first)");
+    }
+    return JA_OK;
+}
+
+// Interval index of letter c in tuple record `rec`.
+inline int64_t coord(const ja_spec* s, const int32_t* rec, char c) { return rec[s->letter_index(c)]; }
+
+int64_t block_of(const Rel& r, const std::string& letters, const ja_spec* s, const int32_t* rec) {
+    int64_t key[JA_MAX_RANK];
+    for (size_t k = 0; k < letters.size(); ++k) key[k] = coord(s, rec, letters[k]);
+    return r.block_index(key);
+}
+
+int64_t extent_of(const ja_decomp* d, const ja_spec* s, const int32_t* rec, const std::string& letters) {
+    int64_t n = 1;
+    for (char c : letters) {
+        int l = s->letter_index(c);
+        n *= d->sp[l][rec[l] + 1] - d->sp[l][rec[l]];
+    }
+    return n;
+}
+
+// Split an operand's letters into role runs.  Returns false unless the
+// operand is [batch run][first run][second run] with the two named roles in
+// either order; `first_is` reports which role came first.
+bool runs(const std::string& op, const std::string& batch, const std::string& r1, const std::string& r2,
+          bool& r1_first) {
+    size_t nb = batch.size();
+    if (op.substr(0, nb) != batch) return false;
+    std::string rest = op.substr(nb);
+    if (rest == r1 + r2) {
+        r1_first = true;
+        return true;
+    }
+    if (rest == r2 + r1) {
+        r1_first = false;
+        return true;
+    }
+    return false;
+}
+
+ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_tuples& t,
+                        const ja_relation_desc* const* in, const ja_relation_desc* out) {
+    Rel A, B, C;
+    ja_status st;
+    if ((st = rel_from_desc(in[0], A)) || (st = rel_from_desc(in[1], B)) || (st = rel_from_desc(out, C))) return st;
+    const std::string &sa = s->ins[0], &sb = s->ins[1], &sc = s->out;
+    if ((st = match_rel(A, sa, s, d, "operand A")) || (st = match_rel(B, sb, s, d, "operand B")) ||
+        (st = match_rel(C, sc, s, d, "output")))
+        return st;
+    if (A.dtype != B.dtype) return fail(JA_ERR_DTYPE, "contract operands must share a dtype");
+    if (A.dtype == JA_F32) {
+        if (C.dtype != JA_F32) return fail(JA_ERR_DTYPE, "f32 contraction writes f32");
+    } else if (A.dtype == JA_BF16) {
+        if (C.dtype != JA_BF16 && C.dtype != JA_F32) return fail(JA_ERR_DTYPE, "bf16 contraction writes bf16 or f32");
+    } else {
+        return fail(JA_ERR_DTYPE, "contract supports f32 and bf16 operands");
+    }
+    // roles of the letters: batch (A, B, C), M (A, C), N (B, C), K (A, B)
+    std::string batch, M, N, K;
+    for (char c : sc) {
+        bool ia = sa.find(c) != std::string::npos, ib = sb.find(c) != std::string::npos;
+        if (ia && ib) batch.push_back(c);
+    }
+    for (char c : sc)
+        if (batch.find(c) == std::string::npos) (sa.find(c) != std::string::npos ? M : N).push_back(c);
+    for (char c : sa)
+        if (sc.find(c) == std::string::npos) K.push_back(c);
+    // M and N in the output's order; K in A's order
+    std::string Mo, No;
+    for (char c : sc) {
+        if (M.find(c) != std::string::npos) Mo.push_back(c);
+        if (N.find(c) != std::string::npos) No.push_back(c);
+    }
+    bool a_m_first = true, b_k_first = true;
+    if (sc != batch + Mo + No || !runs(sa, batch, Mo, K, a_m_first) || !runs(sb, batch, K, No, b_k_first))
+        return fail(JA_ERR_UNSUPPORTED,
+                    "contract needs operands laid out as [batch][rows][cols] runs with matching letter orders");
+    p->a_layout = a_m_first ? JA_A_MK : JA_A_KM;
+    p->b_layout = b_k_first ? JA_B_KN : JA_B_NK;
+    p->in_dtype = A.dtype;
+    p->out_dtype = C.dtype;
+    const int TM = A.dtype == JA_BF16 ? GEMM_BF16_TM : GEMM_F32_TM;
+    const int TN = A.dtype == JA_BF16 ? GEMM_BF16_TN : GEMM_F32_TN;
+
+    const int64_t nt = t.count(), nseg = (int64_t)t.seg.size() - 1;
+    std::vector<GemmTuple> tuples(nt);
+    std::vector<GemmSeg> segs(nseg), usegs(nt);
+    std::vector<GemmTile> tiles, utiles;
+    std::vector<AggTile> atiles;
+    std::vector<AggSeg> asegs(nseg);
+    std::vector<int64_t> poff(nt);
+    int64_t part = 0;
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    for (int64_t i = 0; i < nt; ++i) {
+        const int32_t* rec = &t.rec[i * t.nl];
+        int64_t nb = extent_of(d, s, rec, batch), m = extent_of(d, s, rec, Mo), n = extent_of(d, s, rec, No),
+                k = extent_of(d, s, rec, K);
+        if (m > lim || n > lim || k > lim) return fail(JA_ERR_UNSUPPORTED, "block extent beyond 2^31");
+        GemmTuple& g = tuples[i];
+        g.a_off = A.blk_off[block_of(A, sa, s, rec)];
+        g.b_off = B.blk_off[block_of(B, sb, s, rec)];
+        g.a_bstride = m * k;
+        g.b_bstride = k * n;
+        g.K = (int32_t)k;
+        g.lda = (int32_t)(a_m_first ? k : m);
+        g.ldb = (int32_t)(b_k_first ? n : k);
+        g.pad = 0;
+        // unfused: every tuple is its own segment writing an f32 partial block
+        GemmSeg& u = usegs[i];
+        u.c_off = part;
+        u.c_bstride = m * n;
+        u.M = (int32_t)m;
+        u.N = (int32_t)n;
+        u.ldc = (int32_t)n;
+        u.t_begin = (int32_t)i;
+        u.t_end = (int32_t)i + 1;
+        u.pad = 0;
+        poff[i] = part;
+        part += nb * m * n;
+        for (int32_t b = 0; b < nb; ++b)
+            for (int32_t m0 = 0; m0 < m; m0 += TM)
+                for (int32_t n0 = 0; n0 < n; n0 += TN) utiles.push_back({(int32_t)i, m0, n0, b});
+    }
+    for (int64_t sg = 0; sg < nseg; ++sg) {
+        const int32_t* rec = &t.rec[t.seg[sg] * t.nl];
+        int64_t nb = extent_of(d, s, rec, batch), m = extent_of(d, s, rec, Mo), n = extent_of(d, s, rec, No);
+        GemmSeg& g = segs[sg];
+        g.c_off = C.blk_off[block_of(C, sc, s, rec)];
+        g.c_bstride = m * n;
+        g.M = (int32_t)m;
+        g.N = (int32_t)n;
+        g.ldc = (int32_t)n;
+        g.t_begin = (int32_t)t.seg[sg];
+        g.t_end = (int32_t)t.seg[sg + 1];
+        g.pad = 0;
+        for (int32_t b = 0; b < nb; ++b)
+            for (int32_t m0 = 0; m0 < m; m0 += TM)
+                for (int32_t n0 = 0; n0 < n; n0 += TN) tiles.push_back({(int32_t)sg, m0, n0, b});
+        AggSeg& a = asegs[sg];
+        a.out_off = g.c_off;
+        if (nb * m * n > lim) return fail(JA_ERR_UNSUPPORTED, "output block beyond 2^31 elements");
+        a.nelem = (int32_t)(nb * m * n);
+        a.t_begin = g.t_begin;
+        a.t_end = g.t_end;
+        a.pad = 0;
+        for (int32_t e0 = 0; e0 < a.nelem; e0 += AGG_CHUNK) atiles.push_back({(int32_t)sg, e0});
+    }
+    if ((int64_t)tiles.size() > lim || (int64_t)utiles.size() > lim) return fail(JA_ERR_UNSUPPORTED, "too many tiles");
+    if (A.dtype == JA_BF16) {
+        // the MFMA kernel moves 8 bf16 (16 bytes) at a time along every contiguous axis
+        for (const GemmTuple& g : tuples) {
+            bool ok = g.K % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_off % 8 == 0 && g.b_off % 8 == 0 &&
+                      g.a_bstride % 8 == 0 && g.b_bstride % 8 == 0;
+            if (!ok) return fail(JA_ERR_UNSUPPORTED, "bf16 contraction needs block extents that are multiples of 8");
+        }
+        for (const GemmSeg& g : segs)
+            if ((!a_m_first && g.M % 8) || (b_k_first && g.N % 8))
+                return fail(JA_ERR_UNSUPPORTED, "bf16 contraction needs block extents that are multiples of 8");
+    }
+    p->partial_elems = part;
+    p->tiles_off = put(p->table, tiles);
+    p->ntiles = (int32_t)tiles.size();
+    p->segs_off = put(p->table, segs);
+    p->tuples_off = put(p->table, tuples);
+    p->utiles_off = put(p->table, utiles);
+    p->nutiles = (int32_t)utiles.size();
+    p->usegs_off = put(p->table, usegs);
+    p->atiles_off = put(p->table, atiles);
+    p->natiles = (int32_t)atiles.size();
+    p->asegs_off = put(p->table, asegs);
+    p->apoff_off = put(p->table, poff);
+    return JA_OK;
+}
+
+ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_tuples& t,
+                         const ja_relation_desc* const* in, const ja_relation_desc* out) {
+    Rel Q, K, V, O;
+    ja_status st;
+    if ((st = rel_from_desc(in[0], Q)) || (st = rel_from_desc(in[1], K)) || (st = rel_from_desc(in[2], V)) ||
+        (st = rel_from_desc(out, O)))
+        return st;
+    if ((st = match_rel(Q, s->ins[0], s, d, "Q")) || (st = match_rel(K, s->ins[1], s, d, "K")) ||
+        (st = match_rel(V, s->ins[2], s, d, "V")) || (st = match_rel(O, s->out, s, d, "O")))
+        return st;
+    if (Q.dtype != JA_BF16 || K.dtype != JA_BF16 || V.dtype != JA_BF16 || O.dtype != JA_BF16)
+        return fail(JA_ERR_DTYPE, "attention takes and writes bf16");
+    const std::string& q = s->ins[0];
+    const size_t r = q.size();
+    const std::string batch = q.substr(0, r - 2);
+    const char cs = q[r - 2], ct = s->ins[1][r - 2], cd = q[r - 1];
+    const int64_t D = d->ext[s->letter_index(cd)];
+    if (D != ATTN_D) return fail(JA_ERR_UNSUPPORTED, "attention kernel is built for head dimension 128");
+    p->scale = (float)(s->has_scale ? s->scale : 1.0 / std::sqrt((double)D));
+    p->causal = s->causal ? 1 : 0;
+    const int ls = s->letter_index(cs), lt = s->letter_index(ct);
+    const int64_t nt = t.count(), nseg = (int64_t)t.seg.size() - 1;
+    std::vector<AttnTuple> tuples(nt);
+    std::vector<AttnSeg> segs(nseg);
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    for (int64_t i = 0; i < nt; ++i) {
+        const int32_t* rec = &t.rec[i * t.nl];
+        int64_t T = d->sp[lt][rec[lt] + 1] - d->sp[lt][rec[lt]];
+        if (T > lim) return fail(JA_ERR_UNSUPPORTED, "key block beyond 2^31");
+        AttnTuple& a = tuples[i];
+        a.k_off = K.blk_off[block_of(K, s->ins[1], s, rec)];
+        a.v_off = V.blk_off[block_of(V, s->ins[2], s, rec)];
+        a.kv_bhstride = T * D;
+        a.T = (int32_t)T;
+        a.t_lo = (int32_t)d->sp[lt][rec[lt]];
+    }
+    struct W {
+        AttnTile tile;
+        int64_t work;
+    };
+    std::vector<W> work;
+    for (int64_t sg = 0; sg < nseg; ++sg) {
+        const int32_t* rec = &t.rec[t.seg[sg] * t.nl];
+        int64_t S = d->sp[ls][rec[ls] + 1] - d->sp[ls][rec[ls]];
+        int64_t nbh = extent_of(d, s, rec, batch);
+        if (S > lim || nbh > lim) return fail(JA_ERR_UNSUPPORTED, "query block beyond 2^31");
+        AttnSeg& g = segs[sg];
+        g.q_off = Q.blk_off[block_of(Q, q, s, rec)];
+        g.o_off = O.blk_off[block_of(O, s->out, s, rec)];
+        g.q_bhstride = S * D;
+        g.S = (int32_t)S;
+        g.s_lo = (int32_t)d->sp[ls][rec[ls]];
+        g.t_begin = (int32_t)t.seg[sg];
+        g.t_end = (int32_t)t.seg[sg + 1];
+        for (int32_t bh = 0; bh < nbh; ++bh)
+            for (int32_t s0 = 0; s0 < S; s0 += ATTN_TQ) {
+                // work estimate: keys visible to the tile's last query row
+                int64_t last = g.s_lo + std::min<int64_t>(S, s0 + ATTN_TQ) - 1, w = 0;
+                for (int32_t k = g.t_begin; k < g.t_end; ++k) {
+                    int64_t vis = p->causal ? std::min<int64_t>(tuples[k].T, last - tuples[k].t_lo + 1) : tuples[k].T;
+                    w += std::max<int64_t>(vis, 0);
+                }
+                work.push_back({{(int32_t)sg, bh, s0, 0}, w});
+            }
+    }
+    // longest tiles first, so the tail of the launch is short ones
+    std::stable_sort(work.begin(), work.end(), [](const W& a, const W& b) { return a.work > b.work; });
+    std::vector<AttnTile> tiles;
+    tiles.reserve(work.size());
+    for (auto& w : work) tiles.push_back(w.tile);
+    if ((int64_t)tiles.size() > lim) return fail(JA_ERR_UNSUPPORTED, "too many tiles");
+    p->tiles_off = put(p->table, tiles);
+    p->ntiles = (int32_t)tiles.size();
+    p->segs_off = put(p->table, segs);
+    p->tuples_off = put(p->table, tuples);
+    return JA_OK;
+}
+
+ja_status plan_rmsnorm(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_relation_desc* const* in,
+                       const ja_relation_desc* out) {
+    Rel X, G, Y;
+    ja_status st;
+    if ((st = rel_from_desc(in[0], X)) || (st = rel_from_desc(in[1], G)) || (st = rel_from_desc(out, Y))) return st;
+    if ((st = match_rel(X, s->ins[0], s, d, "x")) || (st = match_rel(G, s->ins[1], s, d, "gain")) ||
+        (st = match_rel(Y, s->out, s, d, "y")))
+        return st;
+    if (X.dtype != JA_BF16 || G.dtype != JA_BF16 || Y.dtype != JA_BF16)
+        return fail(JA_ERR_DTYPE, "rmsnorm takes and writes bf16");
+    const int64_t D = X.shape[1];
+    if (D > 16384) return fail(JA_ERR_UNSUPPORTED, "rmsnorm rows longer than 16384");
+    p->nrb = X.nblk(0);
+    p->ndb = X.nblk(1);
+    p->D = (int32_t)D;
+    p->rows = X.shape[0];
+    p->eps = (float)s->eps;
+    std::vector<int64_t> rsp(X.sp[0]);
+    std::vector<NormBlock> blk;
+    bool vec = true;  // every row piece 16-byte aligned
+    for (int rb = 0; rb < p->nrb; ++rb)
+        for (int db = 0; db < p->ndb; ++db) {
+            int64_t key[2] = {rb, db};
+            NormBlock b{X.blk_off[X.block_index(key)], (int32_t)X.ext(1, db), (int32_t)X.sp[1][db]};
+            vec = vec && b.off % 8 == 0 && b.width % 8 == 0;
+            blk.push_back(b);
+        }
+    p->norm_vec = vec ? 1 : 0;
+    p->rsplit_off = put(p->table, rsp);
+    p->nblk_off = put(p->table, blk);
+    return JA_OK;
+}
+
+ja_status plan_zip(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_relation_desc* const* in,
+                   const ja_relation_desc* out) {
+    Rel A, B, C;
+    ja_status st;
+    if ((st = rel_from_desc(in[0], A)) || (st = rel_from_desc(in[1], B)) || (st = rel_from_desc(out, C))) return st;
+    if ((st = match_rel(A, s->ins[0], s, d, "operand 1")) || (st = match_rel(B, s->ins[1], s, d, "operand 2")) ||
+        (st = match_rel(C, s->out, s, d, "output")))
+        return st;
+    if (A.dtype != JA_BF16 || B.dtype != JA_BF16 || C.dtype != JA_BF16)
+        return fail(JA_ERR_DTYPE, "elementwise joins take and write bf16");
+    // The three relations are blocked identically, so the 1:1 key join pairs
+    // block i of each buffer with block i of the others at identical offsets:
+    // the whole join is a zip of the three flat buffers.
+    p->n = A.elems;
+    return JA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ja_status ja_plan_create(const ja_spec* s, const ja_decomp* d, const ja_relation_desc* const* in, int32_t n_in,
+                         const ja_relation_desc* out, ja_plan** plan) {
+    if (!plan) return fail(JA_ERR_ARG, "plan is NULL");
+    *plan = nullptr;
+    if (!s || !d || !in || !out) return fail(JA_ERR_ARG, "NULL argument");
+    if (d->letters != s->letters) return fail(JA_ERR_DECOMP, "decomposition was made for another spec");
+    if (n_in != (int32_t)s->ins.size()) return fail(JA_ERR_ARG, "number of input relations differs from the spec");
+    for (int i = 0; i < n_in; ++i)
+        if (!in[i]) return fail(JA_ERR_ARG, "input relation descriptor is NULL");
+    ja_tuples t;
+    ja_status st = build_tuples(s, d, t);
+    if (st) return st;
+    ja_plan* p = new ja_plan();
+    p->kind = s->kind;
+    p->n_in = n_in;
+    switch (s->kind) {
+        case JA_OP_CONTRACT: st = plan_contract(p, s, d, t, in, out); break;
+        case JA_OP_ATTENTION: st = plan_attention(p, s, d, t, in, out); break;
+        case JA_OP_RMSNORM: st = plan_rmsnorm(p, s, d, in, out); break;
+        default: st = plan_zip(p, s, d, in, out); break;
+    }
+    if (st) {
+        delete p;
+        return st;
+    }
+    if (p->table.empty()) p->table.resize(16, 0);
+    *plan = p;
+    return JA_OK;
+}
+
+ja_status ja_plan_device_bytes(const ja_plan* p, size_t* table_bytes, size_t* workspace_bytes) {
+    if (!p) return fail(JA_ERR_ARG, "plan is NULL");
+    if (table_bytes) *table_bytes = p->table.size();
+    if (workspace_bytes) *workspace_bytes = 0;
+    return JA_OK;
+}
+
+ja_status ja_plan_upload(ja_plan* p, void* dev_buf, size_t bytes, void* stream) {
+    if (!p || !dev_buf) return fail(JA_ERR_ARG, "NULL argument");
+    if (bytes < p->table.size()) return fail(JA_ERR_WORKSPACE, "table buffer smaller than ja_plan_device_bytes");
+    if ((uintptr_t)dev_buf & 15) return fail(JA_ERR_ARG, "table buffer must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    JA_TRY_HIP(hipMemcpyAsync(dev_buf, p->table.data(), p->table.size(), hipMemcpyHostToDevice, st));
+    JA_TRY_HIP(hipStreamSynchronize(st));
+    p->dev = dev_buf;
+    return JA_OK;
+}
+
+static ja_status check_ptrs(const ja_plan* p, const void* const* in_ptrs, const void* out_ptr) {
+    if (!p) return fail(JA_ERR_ARG, "plan is NULL");
+    if (!p->dev) return fail(JA_ERR_STATE, "plan tables are not uploaded");
+    if (!in_ptrs || !out_ptr) return fail(JA_ERR_ARG, "NULL buffer");
+    for (int i = 0; i < p->n_in; ++i) {
+        if (!in_ptrs[i]) return fail(JA_ERR_ARG, "NULL input buffer");
+        if ((uintptr_t)in_ptrs[i] & 15) return fail(JA_ERR_ARG, "input buffers must be 16-byte aligned");
+    }
+    if ((uintptr_t)out_ptr & 15) return fail(JA_ERR_ARG, "output buffer must be 16-byte aligned");
+    return JA_OK;
+}
+
+ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_ptr, void* workspace, void* stream) {
+    (void)workspace;
+    ja_status st = check_ptrs(p, in_ptrs, out_ptr);
+    if (st) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    switch (p->kind) {
+        case JA_OP_CONTRACT:
+            if (p->ntiles == 0) return JA_OK;
+            JA_TRY_HIP(launch_gemm(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
+                                   out_ptr, p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, hs));
+            break;
+        case JA_OP_ATTENTION:
+            if (p->ntiles == 0) return JA_OK;
+            JA_TRY_HIP(launch_attention(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, in_ptrs[0],
+                                        in_ptrs[1], in_ptrs[2], out_ptr, p->scale, p->causal, hs));
+            break;
+        case JA_OP_RMSNORM:
+            JA_TRY_HIP(launch_rmsnorm(p->dev, p->rsplit_off, p->nrb, p->nblk_off, p->ndb, p->rows, p->D, in_ptrs[0],
+                                      in_ptrs[1], out_ptr, p->eps, p->norm_vec, hs));
+            break;
+        case JA_OP_SWIGLU: JA_TRY_HIP(launch_swiglu(in_ptrs[0], in_ptrs[1], out_ptr, p->n, hs)); break;
+        case JA_OP_ADD: JA_TRY_HIP(launch_add(in_ptrs[0], in_ptrs[1], out_ptr, p->n, hs)); break;
+    }
+    return JA_OK;
+}
+
+ja_status ja_plan_partial_bytes(const ja_plan* p, size_t* bytes) {
+    if (!p || !bytes) return fail(JA_ERR_ARG, "NULL argument");
+    if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    *bytes = (size_t)p->partial_elems * 4;
+    return JA_OK;
+}
+
+ja_status ja_kernel(const ja_plan* p, const void* const* in_ptrs, void* partials, void* stream) {
+    ja_status st = check_ptrs(p, in_ptrs, partials);
+    if (st) return st;
+    if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (p->nutiles == 0) return JA_OK;
+    JA_TRY_HIP(launch_gemm(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
+                           partials, p->in_dtype, JA_F32, p->a_layout, p->b_layout, (hipStream_t)stream));
+    return JA_OK;
+}
+
+ja_status ja_agg(const ja_plan* p, ja_agg_op op, const void* partials, void* out_ptr, void* stream) {
+    if (!p || !partials || !out_ptr) return fail(JA_ERR_ARG, "NULL argument");
+    if (!p->dev) return fail(JA_ERR_STATE, "plan tables are not uploaded");
+    if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (op != JA_AGG_SUM && op != JA_AGG_MAX) return fail(JA_ERR_ARG, "unknown aggregation operator");
+    if (((uintptr_t)partials & 15) || ((uintptr_t)out_ptr & 15)) return fail(JA_ERR_ARG, "buffers must be 16-byte aligned");
+    if (p->natiles == 0) return JA_OK;
+    JA_TRY_HIP(launch_agg(p->dev, p->atiles_off, p->natiles, p->asegs_off, p->apoff_off, (const float*)partials,
+                          out_ptr, p->out_dtype, (int32_t)op, (hipStream_t)stream));
+    return JA_OK;
+}
+
+void ja_plan_destroy(ja_plan* p) { delete p; }
+
+ja_status ja_einsum_workspace_bytes(const ja_spec* s, const ja_decomp* d, const ja_relation_desc* const* in,
+                                    int32_t n_in, const ja_relation_desc* out, size_t* bytes) {
+    if (!bytes) return fail(JA_ERR_ARG, "bytes is NULL");
+    ja_plan* p = nullptr;
+    ja_status st = ja_plan_create(s, d, in, n_in, out, &p);
+    if (st) return st;
+    size_t tb = 0, wb = 0;
+    ja_plan_device_bytes(p, &tb, &wb);
+    *bytes = ((tb + 255) & ~(size_t)255) + wb;
+    ja_plan_destroy(p);
+    return JA_OK;
+}
+
+ja_status ja_einsum(const ja_spec* s, const ja_decomp* d, const ja_relation_desc* const* in,
+                    const void* const* in_ptrs, int32_t n_in, const ja_relation_desc* out, void* out_ptr,
+                    void* dev_ws, size_t ws_bytes, void* stream) {
+    ja_plan* p = nullptr;
+    ja_status st = ja_plan_create(s, d, in, n_in, out, &p);
+    if (st) return st;
+    size_t tb = 0, wb = 0;
+    ja_plan_device_bytes(p, &tb, &wb);
+    size_t tb_al = (tb + 255) & ~(size_t)255;
+    if (!dev_ws || ws_bytes < tb_al + wb) {
+        ja_plan_destroy(p);
+        return fail(JA_ERR_WORKSPACE, "workspace smaller than ja_einsum_workspace_bytes");
+    }
+    st = ja_plan_upload(p, dev_ws, tb, stream);
+    if (!st) st = ja_plan_run(p, in_ptrs, out_ptr, wb ? (char*)dev_ws + tb_al : nullptr, stream);
+    ja_plan_destroy(p);
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+"""Device-side conveniences over the C ABI: torch provides device memory and
+streams; every computation goes through libja's entry points.
+
+* ``Op``      -- an operator with a decomposition and its uploaded plan
+                 (ja_spec_create / ja_decomp_create / ja_plan_create /
+                 ja_plan_upload / ja_plan_run).
+* ``Repart``  -- an uploaded repartition plan (ja_repart_*).
+* ``alloc``   -- a device buffer for a relation.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import binding as B
+from .binding import JA_BF16, JA_F16, JA_F32, Relation  # noqa: F401
+
+TORCH_DTYPE = {JA_F32: torch.float32, JA_BF16: torch.bfloat16, JA_F16: torch.float16}
+
+
+def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def alloc(rel: Relation, device="cuda") -> torch.Tensor:
+    """A flat device buffer holding one relation (torch allocations are
+    256-byte aligned)."""
+    n = rel.nbytes // B.DTYPE_SIZE[rel.dtype]
+    return torch.empty(n, dtype=TORCH_DTYPE[rel.dtype], device=device)
+
+
+def _table(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(16, (nbytes + 15) // 16 * 16), dtype=torch.uint8, device=device)
+
+
+def relation_for(letters: str, splits: Dict[str, Sequence[int]], dtype: int) -> Relation:
+    """The relation blocked exactly as the decomposition cuts its letters."""
+    return Relation([splits[c][-1] for c in letters], splits=[list(splits[c]) for c in letters], dtype=dtype)
+
+
+def equal_splits(n: int, q: int):
+    base, extra = divmod(n, q)
+    pts = [0]
+    for i in range(q):
+        pts.append(pts[-1] + base + (1 if i < extra else 0))
+    return pts
+
+
+class Op:
+    """One operator, one decomposition, one plan uploaded to the device.
+
+    einsum/op/params as in ja_spec_create; `splits` maps every letter to its
+    interval boundaries (0 ... extent).  Relations default to the blocking
+    the decomposition asks for; dtypes default to bf16."""
+
+    def __init__(self, einsum: str, op: str, splits: Dict[str, Sequence[int]], params: str = "",
+                 in_dtypes: Optional[Sequence[int]] = None, out_dtype: int = JA_BF16, device="cuda",
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.einsum, self.op = einsum, op
+        self.spec = B.ja_spec_create(einsum, op, params)
+        self.decomp = None
+        self.plan = None
+        try:
+            self.letters = B.ja_spec_letters(self.spec)
+            ext = [splits[c][-1] for c in self.letters]
+            iv = [len(splits[c]) - 1 for c in self.letters]
+            self.decomp = B.ja_decomp_create(self.spec, ext, iv, [list(splits[c]) for c in self.letters])
+            lhs, out = einsum.split("->")
+            ins = lhs.split(",")
+            in_dtypes = in_dtypes or [JA_BF16] * len(ins)
+            self.in_rels = [relation_for(s, splits, dt) for s, dt in zip(ins, in_dtypes)]
+            self.out_rel = relation_for(out, splits, out_dtype)
+            self.plan = B.ja_plan_create(self.spec, self.decomp, self.in_rels, self.out_rel)
+            tb, wb = B.ja_plan_device_bytes(self.plan)
+            self.table = _table(tb, device)
+            self.workspace = _table(wb, device) if wb else None
+            B.ja_plan_upload(self.plan, self.table.data_ptr(), self.table.numel(), stream_handle(stream))
+        except Exception:
+            self.close()
+            raise
+
+    def tuples(self):
+        t = B.ja_join(self.spec, self.decomp)
+        try:
+            return B.ja_tuples_export(t)
+        finally:
+            B.ja_tuples_destroy(t)
+
+    def run(self, ins: Sequence[torch.Tensor], out: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+        ws = self.workspace.data_ptr() if self.workspace is not None else 0
+        B.ja_plan_run(self.plan, [t.data_ptr() for t in ins], out.data_ptr(), ws, stream_handle(stream))
+
+    def partial_buffer(self) -> torch.Tensor:
+        return torch.empty(B.ja_plan_partial_bytes(self.plan) // 4, dtype=torch.float32, device=self.table.device)
+
+    def kernel(self, ins: Sequence[torch.Tensor], partials: torch.Tensor, stream=None):
+        B.ja_kernel(self.plan, [t.data_ptr() for t in ins], partials.data_ptr(), stream_handle(stream))
+
+    def agg(self, partials: torch.Tensor, out: torch.Tensor, op: int = B.JA_AGG_SUM, stream=None):
+        B.ja_agg(self.plan, op, partials.data_ptr(), out.data_ptr(), stream_handle(stream))
+
+    def close(self):
+        if self.plan:
+            B.ja_plan_destroy(self.plan)
+            self.plan = None
+        if self.decomp:
+            B.ja_decomp_destroy(self.decomp)
+            self.decomp = None
+        if self.spec:
+            B.ja_spec_destroy(self.spec)
+            self.spec = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Repart:
+    """An uploaded re-blocking plan from `src` to `dst` (optional view)."""
+
+    def __init__(self, src: Relation, dst: Relation, view: Optional[B.ja_view] = None, device="cuda",
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.src, self.dst, self.view = src, dst, view
+        self.rp = B.ja_repart_create(src, dst, view)
+        try:
+            self.n_atoms, self.n_tasks = B.ja_repart_count(self.rp)
+            self.table = _table(B.ja_repart_device_bytes(self.rp), device)
+            B.ja_repart_upload(self.rp, self.table.data_ptr(), self.table.numel(), stream_handle(stream))
+        except Exception:
+            self.close()
+            raise
+
+    def run(self, src: torch.Tensor, dst: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+        B.ja_repart_run(self.rp, src.data_ptr(), dst.data_ptr(), stream_handle(stream))
+
+    def close(self):
+        if self.rp:
+            B.ja_repart_destroy(self.rp)
+            self.rp = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

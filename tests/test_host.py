@@ -1,0 +1,246 @@
+"""Host logic of libja checked without a GPU: tuple lists (bit-exact against
+the oracle's independent enumeration), relation layout, spec and
+decomposition validation, error codes, repartition atom counts, and plan
+construction for every configuration."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from tensor_relational_join_amd import binding
+
+    return binding
+
+
+def _tuples(B, einsum, op, splits, params=""):
+    s = B.ja_spec_create(einsum, op, params)
+    try:
+        letters = B.ja_spec_letters(s)
+        d = B.ja_decomp_create(s, [splits[c][-1] for c in letters], [len(splits[c]) - 1 for c in letters],
+                               [splits[c] for c in letters])
+        try:
+            t = B.ja_join(s, d)
+            try:
+                rec, seg = B.ja_tuples_export(t)
+            finally:
+                B.ja_tuples_destroy(t)
+        finally:
+            B.ja_decomp_destroy(d)
+    finally:
+        B.ja_spec_destroy(s)
+    return letters, rec, seg
+
+
+def _eq(n, q):
+    base, extra = divmod(n, q)
+    p = [0]
+    for i in range(q):
+        p.append(p[-1] + base + (i < extra))
+    return p
+
+
+CASES = [
+    ("ij,jk->ik", "contract", {"i": _eq(64, 2), "j": _eq(64, 2), "k": _eq(64, 2)}, "", "ik", None),
+    ("bd,df->bf", "contract", {"b": _eq(2048, 2), "d": _eq(4096, 4), "f": _eq(11008, 4)}, "", "bf", None),
+    ("bhsd,bhtd,bhtd->bhsd", "attention",
+     {"b": _eq(4, 4), "h": _eq(32, 32), "s": _eq(2048, 16), "t": _eq(2048, 16), "d": [0, 128]},
+     "causal=s,t", "bhsd", ("s", "t")),
+    ("rd,d->rd", "rmsnorm", {"r": _eq(8192, 1), "d": _eq(4096, 8)}, "eps=1e-6", "r", None),
+    ("rf,rf->rf", "swiglu", {"r": _eq(8192, 1), "f": _eq(11008, 8)}, "", "rf", None),
+    ("td,dn->tn", "contract", {"t": _eq(8192, 2), "d": _eq(4096, 2), "n": _eq(12288, 2)}, "", "tn", None),
+    ("ij,kj->ik", "contract", {"i": [0, 3, 10], "j": [0, 1, 5, 7], "k": [0, 4, 9]}, "", "ik", None),
+    ("bhsd,bhtd,bhtd->bhsd", "attention",
+     {"b": [0, 2], "h": [0, 1, 3], "s": [0, 50, 130, 300], "t": [0, 100, 128, 300], "d": [0, 128]},
+     "causal=s,t", "bhsd", ("s", "t")),
+]
+
+
+@pytest.mark.parametrize("einsum,op,splits,params,group,causal", CASES)
+def test_tuple_lists_match_oracle(B, orc, einsum, op, splits, params, group, causal):
+    letters, rec, seg = _tuples(B, einsum, op, splits, params)
+    o_rec, o_seg = orc.tuple_records(list(letters), splits, group_by=list(group), causal=causal)
+    assert rec.dtype == np.int32
+    assert np.array_equal(rec, o_rec)
+    assert np.array_equal(seg, o_seg)
+
+
+def test_config_counts(B):
+    _, rec, seg = _tuples(B, *CASES[0][:4])
+    assert (len(rec), len(seg) - 1) == (8, 4)
+    _, rec, seg = _tuples(B, *CASES[1][:4])
+    assert (len(rec), len(seg) - 1) == (32, 8)
+    _, rec, seg = _tuples(B, *CASES[2][:4])
+    assert (len(rec), len(seg) - 1) == (17408, 2048)
+    _, rec, seg = _tuples(B, *CASES[5][:4])
+    assert (len(rec), len(seg) - 1) == (8, 4)
+
+
+def test_examples_3_8_3_9_through_the_join(B):
+    g = json.load(open(os.path.join(GOLDEN, "example_3_8_3_9_matmul_specs.json")))
+    for case in g["cases"]:
+        letters, rec, seg = _tuples(B, "ij,jk->ik", "contract", case["splits"])
+        assert len(rec) == case["n_specs"]
+        assert list(np.diff(seg)) == case["segment_sizes"]
+        # boxes of each tuple's projections
+        sp = case["splits"]
+        for r, want in zip(rec.tolist(), case["specs"]):
+            iv = {c: (sp[c][r[letters.index(c)]], sp[c][r[letters.index(c)] + 1]) for c in "ijk"}
+            assert [[iv["i"][0], iv["j"][0]], [iv["i"][1], iv["j"][1]]] == want["A"]
+            assert [[iv["j"][0], iv["k"][0]], [iv["j"][1], iv["k"][1]]] == want["B"]
+            assert [[iv["i"][0], iv["k"][0]], [iv["i"][1], iv["k"][1]]] == want["C"]
+
+
+def test_relation_layout_matches_oracle(B, orc):
+    shape, splits = (7, 10, 3), [[0, 2, 7], [0, 4, 5, 10], [0, 3]]
+    rel = B.Relation(shape, splits=splits, dtype=B.JA_F32)
+    assert B.ja_relation_bytes(rel) == 7 * 10 * 3 * 4
+    assert B.ja_relation_nblocks(rel) == 6
+    o = orc.Relation(shape, splits)
+    flat = o.pack(np.arange(np.prod(shape)).reshape(shape))
+    off = 0
+    for key in itertools.product(range(2), range(3), range(1)):
+        lo, hi, boff = B.ja_relation_block(rel, key)
+        assert (lo, hi) == o.box(key)
+        assert boff == off * 4
+        # the first element of the block in the oracle's packing is the cell at lo
+        assert flat[off] == np.ravel_multi_index(lo, shape)
+        off += orc.box_cells((lo, hi))
+    # near-equal default splits
+    r2 = B.Relation((10,), nblk=(3,), dtype=B.JA_BF16)
+    assert [B.ja_relation_block(r2, (k,))[0][0] for k in range(3)] == [0, 4, 7]
+
+
+@pytest.mark.parametrize("einsum,op,params,code", [
+    ("ij,jk", "contract", "", "JA_ERR_SPEC"),
+    ("ij,jk->ik", "conv", "", "JA_ERR_SPEC"),
+    ("ii,jk->ik", "contract", "", "JA_ERR_SPEC"),
+    ("ij,jk->iz", "contract", "", "JA_ERR_SPEC"),
+    ("ij,kl->ik", "contract", "", "JA_ERR_SPEC"),          # j and l appear once
+    ("bhsd,bhtd,bhtd->bhsd", "attention", "causal=t,s", "JA_ERR_SPEC"),
+    ("bhsd,bhtd->bhsd", "attention", "", "JA_ERR_SPEC"),
+    ("rd,d->rd", "rmsnorm", "eps=-1", "JA_ERR_SPEC"),
+    ("rd,d->rd", "rmsnorm", "bogus=1", "JA_ERR_SPEC"),
+    ("ij,jk->ik", "contract", "causal=i,k", "JA_ERR_SPEC"),
+])
+def test_spec_errors(B, einsum, op, params, code):
+    with pytest.raises(B.JaError) as e:
+        B.ja_spec_create(einsum, op, params)
+    assert e.value.name == code
+    assert B.ja_last_error()
+
+
+def test_decomposition_errors(B):
+    s = B.ja_spec_create("ij,jk->ik", "contract")
+    try:
+        for ext, iv, sp, code in [
+            ([4, 4, 4], [5, 1, 1], None, "JA_ERR_DECOMP"),        # more intervals than cells
+            ([4, 4, 4], [0, 1, 1], None, "JA_ERR_DECOMP"),
+            ([4, 0, 4], [1, 1, 1], None, "JA_ERR_DECOMP"),
+            ([4, 4, 4], [2, 1, 1], [[0, 3, 3], None, None], "JA_ERR_DECOMP"),   # not rising
+            ([4, 4, 4], [2, 1, 1], [[0, 2, 5], None, None], "JA_ERR_DECOMP"),   # past the extent
+        ]:
+            with pytest.raises(B.JaError) as e:
+                B.ja_decomp_create(s, ext, iv, sp)
+            assert e.value.name == code
+    finally:
+        B.ja_spec_destroy(s)
+    a = B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", "causal=s,t")
+    try:
+        with pytest.raises(B.JaError) as e:
+            B.ja_decomp_create(a, [1, 1, 256, 128, 256], [1, 1, 2, 2, 2])  # letters b h s d t: d split
+        assert e.value.name == "JA_ERR_DECOMP"
+    finally:
+        B.ja_spec_destroy(a)
+
+
+def test_plan_validation_errors(B):
+    from tensor_relational_join_amd.device import relation_for
+
+    s = B.ja_spec_create("ij,jk->ik", "contract")
+    sp = {"i": [0, 32, 64], "j": [0, 32, 64], "k": [0, 32, 64]}
+    d = B.ja_decomp_create(s, [64, 64, 64], [2, 2, 2], [sp["i"], sp["j"], sp["k"]])
+    try:
+        A = relation_for("ij", sp, B.JA_F32)
+        Bm = relation_for("jk", sp, B.JA_F32)
+        C = relation_for("ik", sp, B.JA_F32)
+        p = B.ja_plan_create(s, d, [A, Bm], C)
+        assert B.ja_plan_device_bytes(p)[0] > 0
+        with pytest.raises(B.JaError) as e:       # running before upload
+            B.ja_plan_run(p, [16, 32], 48)
+        assert e.value.name == "JA_ERR_STATE"
+        B.ja_plan_destroy(p)
+        bad = B.Relation((64, 64), nblk=(1, 2), dtype=B.JA_F32)   # A not blocked as the decomposition asks
+        with pytest.raises(B.JaError) as e:
+            B.ja_plan_create(s, d, [bad, Bm], C)
+        assert e.value.name == "JA_ERR_SHAPE"
+        C16 = relation_for("ik", sp, B.JA_BF16)
+        with pytest.raises(B.JaError) as e:
+            B.ja_plan_create(s, d, [A, Bm], C16)
+        assert e.value.name == "JA_ERR_DTYPE"
+        with pytest.raises(B.JaError) as e:
+            B.ja_plan_create(s, d, [A], C)
+        assert e.value.name == "JA_ERR_ARG"
+        A16, B16 = relation_for("ij", sp, B.JA_BF16), relation_for("jk", {**sp, "k": [0, 30, 64]}, B.JA_BF16)
+        with pytest.raises(B.JaError):
+            B.ja_plan_create(s, d, [A16, B16], C16)
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
+
+
+def test_bf16_alignment_is_refused_not_miscomputed(B):
+    from tensor_relational_join_amd.device import relation_for
+
+    s = B.ja_spec_create("ij,jk->ik", "contract")
+    sp = {"i": [0, 16], "j": [0, 12], "k": [0, 16]}   # K = 12: not a multiple of 8
+    d = B.ja_decomp_create(s, [16, 12, 16], [1, 1, 1], [sp["i"], sp["j"], sp["k"]])
+    try:
+        with pytest.raises(B.JaError) as e:
+            B.ja_plan_create(s, d, [relation_for("ij", sp, B.JA_BF16), relation_for("jk", sp, B.JA_BF16)],
+                             relation_for("ik", sp, B.JA_BF16))
+        assert e.value.name == "JA_ERR_UNSUPPORTED"
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
+
+
+def test_section_5_3_overlay_atom_count(B):
+    g = json.load(open(os.path.join(GOLDEN, "section_5_3_overlay_atoms.json")))
+    src = B.Relation(g["shape"], splits=[g["producer_row_splits"], g["col_splits"]], dtype=B.JA_BF16)
+    dst = B.Relation(g["shape"], splits=[g["consumer_row_splits"], g["col_splits"]], dtype=B.JA_BF16)
+    rp = B.ja_repart_create(src, dst)
+    try:
+        n_atoms, n_tasks = B.ja_repart_count(rp)
+        assert n_atoms == g["n_atoms"]
+        assert n_tasks >= n_atoms
+    finally:
+        B.ja_repart_destroy(rp)
+
+
+def test_repartition_atoms_for_head_views(B):
+    # token-major [8192, 12288] blocked 2x2 -> head-major [3,4,32,2048,128] blocks [1,1,1,128,128]
+    src = B.Relation((8192, 12288), nblk=(2, 2), dtype=B.JA_BF16)
+    dst = B.Relation((3, 4, 32, 2048, 128), nblk=(3, 4, 32, 16, 1), dtype=B.JA_BF16)
+    view = B.make_view((4, 2048, 3, 32, 128), (2, 0, 3, 1, 4))
+    rp = B.ja_repart_create(src, dst, view)
+    try:
+        assert B.ja_repart_count(rp) == (6144, 6144)
+    finally:
+        B.ja_repart_destroy(rp)
+    # views that do not factor are refused
+    bad = B.make_view((6, 4), (1, 0))
+    with pytest.raises(B.JaError) as e:
+        B.ja_repart_create(B.Relation((4, 6), nblk=(1, 1), dtype=B.JA_F32),
+                           B.Relation((4, 6), nblk=(1, 1), dtype=B.JA_F32), bad)
+    assert e.value.name == "JA_ERR_UNSUPPORTED"
+    with pytest.raises(B.JaError) as e:
+        B.ja_repart_create(B.Relation((4, 6), nblk=(1, 1), dtype=B.JA_F32),
+                           B.Relation((4, 6), nblk=(1, 1), dtype=B.JA_BF16))
+    assert e.value.name == "JA_ERR_DTYPE"
