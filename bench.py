@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the one-GPU join-agg path on MI355X.
+
+A step is one pass of the LLaMA-shaped block (batch 4, seq 2048, d 4096, 32
+heads of 128, ffn 11008, bf16) through libja: RMSNorm, the 2x2x2 QKV
+contraction join-agg, the tokens->heads repartition, causal attention with
+the online-softmax aggregation, heads->tokens, the output projection,
+residual add, RMSNorm, gate/up contractions, SwiGLU, down contraction and the
+second residual add.  Inputs are seeded synthetic tensors already resident
+in HBM in the blockings the operators need.
+
+Prints one JSON line.  `value` is the block's join-agg throughput (all
+contraction and attention flops of a step / step time).  `roofline` is for
+the dominant kernel (the bf16 MFMA contraction), timed with HIP events on
+the stream the steps run on.  `cpu_baseline` times the CPU oracle on a
+bounded token sample of the same block.
+
+    python bench.py [--steps K] [--warmup W] [--workload block|ffn|attention|norm_swiglu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "join-agg TFLOP/s & % MFMA peak; LLaMA-7B-shape block ms, 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def _eq(n, q):
+    base, extra = divmod(n, q)
+    p = [0]
+    for i in range(q):
+        p.append(p[-1] + base + (i < extra))
+    return p
+
+
+def _bits_to_dev(bits):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).ravel()).view(torch.bfloat16).cuda()
+
+
+def _mean_ms(pairs):
+    return sum(s.elapsed_time(e) for s, e in pairs) / max(1, len(pairs))
+
+
+def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0):
+    """Time the oracle (as it stands) on the first n tokens of batch 0 of the
+    same block; n is grown until one run takes a few seconds."""
+    import numpy as np
+
+    import oracle
+
+    f = {k: oracle.bf16_to_f64(v) for k, v in inp.items()}
+    hd = dm // heads
+
+    def flops(n):
+        per_tok = 2.0 * (dm * 3 * dm + dm * dm + 3 * dm * ffn)
+        att = sum(2 * 2.0 * (s + 1) * hd * heads for s in range(n))
+        return n * per_tok + att
+
+    n, dt = 8, 0.0
+    while True:
+        toks = list(range(n))
+        t0 = time.perf_counter()
+        oracle.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
+                                  f["w_down"], batch, seq, heads, toks)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or n >= seq:
+            break
+        n = min(seq, max(n * 2, int(n * target_s / 4 / max(dt, 1e-3))))
+    return {"value": flops(n) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "float64 oracle block forward on tokens 0..%d of batch 0 (%.1f GFLOP, %.2f s)" %
+                      (n - 1, flops(n) / 1e9, dt)}
+
+
+def bench_block(args):
+    import torch
+
+    from tensor_relational_join_amd import synth
+    from tensor_relational_join_amd.block import GEMMS, LlamaBlock
+    from tensor_relational_join_amd.device import alloc
+
+    batch, seq, dm, heads, ffn = 4, 2048, 4096, 32, 11008
+    blk = LlamaBlock(batch, seq, dm, heads, ffn)
+    inp = synth.llama_block_inputs(5, batch, seq, dm, ffn)
+    x = blk.materialize(_bits_to_dev(inp["x"]), blk.x_rel)
+    w = {k: blk.materialize(_bits_to_dev(inp[k]), rel) for k, rel in blk.w_rel.items()}
+    w["g1"] = blk.materialize(_bits_to_dev(inp["g1"]), blk.g_rel)
+    w["g2"] = blk.materialize(_bits_to_dev(inp["g2"]), blk.ops["norm2"].in_rels[1])
+    y = alloc(blk.ops["add2"].out_rel)
+    flops = blk.flops()
+    total_flops = sum(flops.values())
+
+    for _ in range(args.warmup):
+        blk.forward(x, w, y)
+    torch.cuda.synchronize()
+    # timed region 1: K steps back to back, one event pair around all of them
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s0.record()
+    for _ in range(args.steps):
+        blk.forward(x, w, y)
+    s1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = s0.elapsed_time(s1) / args.steps
+    # timed region 2: the same K steps with an event pair around every step of the path
+    ev = {}
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        blk.forward(x, w, y, events=ev)
+    torch.cuda.synchronize()
+    step_ms = {k: _mean_ms(v) for k, v in ev.items()}
+    gemm_ms = sum(step_ms[k] for k in GEMMS)
+    gemm_flops = sum(flops[k] for k in GEMMS)
+    achieved = gemm_flops / len(GEMMS) / (gemm_ms / len(GEMMS) / 1e3) / 1e12
+    nbytes = blk.step_bytes()
+    parts = {}
+    for k in step_ms:
+        d = {"ms": round(step_ms[k], 4)}
+        if k in flops:
+            d["tflops"] = round(flops[k] / (step_ms[k] / 1e3) / 1e12, 1)
+            d["frac_mfma_peak"] = round(d["tflops"] / PEAK_BF16_TFLOPS, 3)
+        if k in nbytes:
+            d["gbs"] = round(nbytes[k] / (step_ms[k] / 1e3) / 1e9, 1)
+            d["frac_hbm_peak"] = round(d["gbs"] / PEAK_HBM_GBS, 3)
+        parts[k] = d
+    value = total_flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b_shaped_block", "batch": batch, "seq_len": seq, "d_model": dm,
+                   "heads": heads, "head_dim": 128, "ffn": ffn, "parallelism": "single GPU"},
+        "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "block_gflop": round(total_flops / 1e9, 1),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "roofline": {"kernel": "gemm_bf16_kernel (contraction join-agg, fused SUM)", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "launches_per_step": len(GEMMS), "gflop_per_launch": round(gemm_flops / len(GEMMS) / 1e9, 1),
+                     "avg_launch_ms": round(gemm_ms / len(GEMMS), 4)},
+        "parts": parts,
+    }
+    blk.close()
+    return out, inp
+
+
+def bench_kernel(args):
+    """Single-operator workloads at the configs' sizes (diagnostics and
+    profiling): ffn = bd,df->bf 2048x4096x11008 (2x4x4); attention =
+    [4,32,2048,128] causal, 128-blocks; norm_swiglu = RMSNorm [8192,4096]
+    (d by 8) + SwiGLU [8192,11008] (f by 8)."""
+    import torch
+
+    from tensor_relational_join_amd import synth
+    from tensor_relational_join_amd.device import Op, alloc
+
+    runs = []
+    if args.workload == "ffn":
+        sp = {"b": _eq(2048, 2), "d": _eq(4096, 4), "f": _eq(11008, 4)}
+        op = Op("bd,df->bf", "contract", sp)
+        ins = [alloc(r) for r in op.in_rels]
+        for t in ins:
+            t.normal_()
+        out = alloc(op.out_rel)
+        runs.append(("ffn_contract", op, ins, out, 2.0 * 2048 * 4096 * 11008, None))
+    elif args.workload == "attention":
+        sp = {"b": _eq(4, 4), "h": _eq(32, 32), "s": _eq(2048, 16), "t": _eq(2048, 16), "d": [0, 128]}
+        op = Op("bhsd,bhtd,bhtd->bhsd", "attention", sp, "causal=s,t")
+        ins = [alloc(r) for r in op.in_rels]
+        for t in ins:
+            t.normal_()
+        out = alloc(op.out_rel)
+        runs.append(("attention", op, ins, out, 2 * 2.0 * 128 * 128 * 128 * 136 * 128, None))
+    else:
+        op = Op("rd,d->rd", "rmsnorm", {"r": [0, 8192], "d": _eq(4096, 8)}, "eps=1e-6")
+        ins = [alloc(r) for r in op.in_rels]
+        ins[0].normal_()
+        ins[1].fill_(1.0)
+        out = alloc(op.out_rel)
+        runs.append(("rmsnorm", op, ins, out, None, 2.0 * (2 * 8192 * 4096 + 4096)))
+        op2 = Op("rf,rf->rf", "swiglu", {"r": [0, 8192], "f": _eq(11008, 8)})
+        ins2 = [alloc(r) for r in op2.in_rels]
+        for t in ins2:
+            t.normal_()
+        out2 = alloc(op2.out_rel)
+        runs.append(("swiglu", op2, ins2, out2, None, 2.0 * 3 * 8192 * 11008))
+    res = {}
+    for name, op, ins, out, fl, by in runs:
+        for _ in range(args.warmup):
+            op.run(ins, out)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            op.run(ins, out)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / args.steps
+        d = {"ms": round(ms, 4)}
+        if fl:
+            d["tflops"] = round(fl / (ms / 1e3) / 1e12, 1)
+            d["frac_mfma_peak"] = round(d["tflops"] / PEAK_BF16_TFLOPS, 3)
+        if by:
+            d["gbs"] = round(by / (ms / 1e3) / 1e9, 1)
+            d["frac_hbm_peak"] = round(d["gbs"] / PEAK_HBM_GBS, 3)
+        res[name] = d
+        op.close()
+    return {"workload": args.workload, "steps": args.steps, "warmup": args.warmup, "results": res}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="block", choices=["block", "ffn", "attention", "norm_swiglu"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (every kernel runs on one "
+              "GPU's share); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.workload != "block":
+        print(json.dumps(bench_kernel(args)))
+        return
+    out, inp = bench_block(args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(inp, 4, 2048, 4096, 32, 11008)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -141,6 +141,17 @@ class Relation:
                 d.nblk[i] = int(nblk[i]) if nblk is not None else 1
         self.desc = d
         self.nblk = tuple(int(d.nblk[i]) for i in range(rank))
+        # split points per dimension (near-equal reading where none were given)
+        self.splits = []
+        for i in range(rank):
+            sp = splits[i] if splits is not None else None
+            if sp is None:
+                n, q = self.shape[i], self.nblk[i]
+                base, extra = divmod(n, q)
+                sp = [0]
+                for j in range(q):
+                    sp.append(sp[-1] + base + (1 if j < extra else 0))
+            self.splits.append([int(x) for x in sp])
 
     @property
     def ptr(self):

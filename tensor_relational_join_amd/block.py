@@ -1,0 +1,175 @@
+"""A LLaMA-shaped transformer block as a graph of join-agg operators.
+
+Pre-norm block, causal multi-head attention, SwiGLU feed-forward, two
+residual adds, no rotary embedding and no biases:
+
+    h1 = rmsnorm(x, g1)               rd,d->rd      r: 2  d: 2
+    qkv = h1 @ W_qkv                  td,dn->tn     t: 2  d: 2  n: 2   (3-D matmul decomposition, 8 tuples)
+    Q, K, V = heads(qkv)              repartition [t, 3*dm] -> [3, b, h, s, hd], blocks [1,1,1,128,128]
+    O = attention(Q, K, V)            bhsd,bhtd,bhtd->bhsd   b, h unit intervals, s and t 128-blocks, causal
+    o = tokens(O)                     repartition [b, h, s, hd] -> [t, dm], blocks [t/2, dm/2]
+    a = o @ W_o                       tm,mn->tn     t: 2  m: 2  n: 2
+    x2 = x + a                        1:1 join on [t/2, dm/2] blocks
+    h2 = rmsnorm(x2, g2)
+    gt = h2 @ W_gate, up = h2 @ W_up  td,df->tf     t: 2  d: 2  f: 4
+    f = silu(gt) * up                 1:1 join on [t/2, ffn/4] blocks
+    dn = f @ W_down                   tf,fn->tn     t: 2  f: 4  n: 2
+    y = x2 + dn
+
+Only the QKV decomposition is fixed by the workload; the others are chosen
+so that every producer's output blocking is its consumer's input blocking
+(the repartition sub-cost of the pages' cost model, section 4.3, is then
+zero for them), which leaves exactly the two re-indexing repartitions around
+attention (tokens <-> heads).
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import torch
+
+from . import binding as B
+from .device import Op, Repart, alloc, equal_splits
+
+# (name, kind) of every step, in execution order
+STEPS = ["norm1", "qkv", "to_heads", "attn", "to_tokens", "oproj", "add1", "norm2", "gate", "up", "swiglu",
+         "down", "add2"]
+GEMMS = ["qkv", "oproj", "gate", "up", "down"]
+
+
+class LlamaBlock:
+    def __init__(self, batch: int = 4, seq: int = 2048, dm: int = 4096, heads: int = 32, ffn: int = 11008,
+                 eps: float = 1e-6, device="cuda"):
+        if dm % heads or dm // heads != 128 or seq % 128:
+            raise ValueError("the attention kernel needs head_dim 128 and 128-multiples of seq")
+        self.batch, self.seq, self.dm, self.heads, self.ffn, self.eps = batch, seq, dm, heads, ffn, eps
+        self.hd = dm // heads
+        T = batch * seq
+        self.T = T
+        t2, d2 = equal_splits(T, 2), equal_splits(dm, 2)
+        f4 = equal_splits(ffn, 4)
+        ep = "eps=%r" % eps
+        self.ops: Dict[str, Op] = {}
+        self.ops["norm1"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
+        self.ops["qkv"] = Op("td,dn->tn", "contract", {"t": t2, "d": d2, "n": equal_splits(3 * dm, 2)}, device=device)
+        nb = seq // 128
+        att_sp = {"b": equal_splits(batch, batch), "h": equal_splits(heads, heads), "s": equal_splits(seq, nb),
+                  "t": equal_splits(seq, nb), "d": [0, self.hd]}
+        self.ops["attn"] = Op("bhsd,bhtd,bhtd->bhsd", "attention", att_sp, "causal=s,t", device=device)
+        self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": d2, "n": d2}, device=device)
+        self.ops["add1"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
+        self.ops["norm2"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
+        self.ops["gate"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
+        self.ops["up"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
+        self.ops["swiglu"] = Op("tf,tf->tf", "swiglu", {"t": t2, "f": f4}, device=device)
+        self.ops["down"] = Op("tf,fn->tn", "contract", {"t": t2, "f": f4, "n": d2}, device=device)
+        self.ops["add2"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
+        # token-major <-> head-major re-blockings around attention
+        heads_rel = B.Relation((3, batch, heads, seq, self.hd), nblk=(3, batch, heads, nb, 1), dtype=B.JA_BF16)
+        self.rp: Dict[str, Repart] = {}
+        self.rp["to_heads"] = Repart(self.ops["qkv"].out_rel, heads_rel,
+                                     B.make_view((batch, seq, 3, heads, self.hd), (2, 0, 3, 1, 4)), device=device)
+        self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, self.ops["oproj"].in_rels[0],
+                                      B.make_view((batch, heads, seq, self.hd), (0, 2, 1, 3)), device=device)
+        self.heads_rel = heads_rel
+        # relations of the block's inputs (materialised straight into the blockings the ops need)
+        self.x_rel = self.ops["norm1"].in_rels[0]
+        self.g_rel = self.ops["norm1"].in_rels[1]
+        self.w_rel = {"w_qkv": self.ops["qkv"].in_rels[1], "w_o": self.ops["oproj"].in_rels[1],
+                      "w_gate": self.ops["gate"].in_rels[1], "w_up": self.ops["up"].in_rels[1],
+                      "w_down": self.ops["down"].in_rels[1]}
+        # intermediates
+        o = self.ops
+        self.buf = {
+            "h1": alloc(o["norm1"].out_rel, device), "qkv": alloc(o["qkv"].out_rel, device),
+            "heads": alloc(heads_rel, device), "O": alloc(o["attn"].out_rel, device),
+            "o": alloc(o["oproj"].in_rels[0], device), "a": alloc(o["oproj"].out_rel, device),
+            "x2": alloc(o["add1"].out_rel, device), "h2": alloc(o["norm2"].out_rel, device),
+            "gt": alloc(o["gate"].out_rel, device), "up": alloc(o["up"].out_rel, device),
+            "f": alloc(o["swiglu"].out_rel, device), "dn": alloc(o["down"].out_rel, device),
+        }
+
+    # ---------------------------------------------------------------- flops / bytes
+    def flops(self) -> Dict[str, float]:
+        T, dm, ffn = self.T, self.dm, self.ffn
+        f = {"qkv": 2.0 * T * dm * 3 * dm, "oproj": 2.0 * T * dm * dm, "gate": 2.0 * T * dm * ffn,
+             "up": 2.0 * T * dm * ffn, "down": 2.0 * T * ffn * dm}
+        nb = self.seq // 128
+        kept = nb * (nb + 1) // 2  # kept (s-block, t-block) tuples per (b, h)
+        f["attn"] = 2 * 2.0 * 128 * 128 * self.hd * kept * self.batch * self.heads
+        return f
+
+    def step_bytes(self) -> Dict[str, float]:
+        """Algorithmic HBM bytes of the memory-bound steps (inputs read once,
+        outputs written once)."""
+        T, dm, ffn = self.T, self.dm, self.ffn
+        e = 2.0
+        return {"norm1": e * (2 * T * dm + dm), "norm2": e * (2 * T * dm + dm), "add1": e * 3 * T * dm,
+                "add2": e * 3 * T * dm, "swiglu": e * 3 * T * ffn, "to_heads": e * 2 * T * 3 * dm,
+                "to_tokens": e * 2 * T * dm}
+
+    # ---------------------------------------------------------------- execution
+    def forward(self, x: torch.Tensor, w: Dict[str, torch.Tensor], y: torch.Tensor,
+                events: Optional[Dict[str, List]] = None, stream=None):
+        """One pass of the block.  x, y and the weights are device buffers in
+        the relations' layouts (x_rel, w_rel, g_rel).  If `events` is given,
+        a (start, end) torch event pair is recorded around every step."""
+        o, b = self.ops, self.buf
+        n = self.T * self.heads * self.hd  # elements of each of Q, K, V
+        q, k, v = b["heads"][:n], b["heads"][n:2 * n], b["heads"][2 * n:]
+        plan = [
+            ("norm1", lambda: o["norm1"].run([x, w["g1"]], b["h1"], stream)),
+            ("qkv", lambda: o["qkv"].run([b["h1"], w["w_qkv"]], b["qkv"], stream)),
+            ("to_heads", lambda: self.rp["to_heads"].run(b["qkv"], b["heads"], stream)),
+            ("attn", lambda: o["attn"].run([q, k, v], b["O"], stream)),
+            ("to_tokens", lambda: self.rp["to_tokens"].run(b["O"], b["o"], stream)),
+            ("oproj", lambda: o["oproj"].run([b["o"], w["w_o"]], b["a"], stream)),
+            ("add1", lambda: o["add1"].run([x, b["a"]], b["x2"], stream)),
+            ("norm2", lambda: o["norm2"].run([b["x2"], w["g2"]], b["h2"], stream)),
+            ("gate", lambda: o["gate"].run([b["h2"], w["w_gate"]], b["gt"], stream)),
+            ("up", lambda: o["up"].run([b["h2"], w["w_up"]], b["up"], stream)),
+            ("swiglu", lambda: o["swiglu"].run([b["gt"], b["up"]], b["f"], stream)),
+            ("down", lambda: o["down"].run([b["f"], w["w_down"]], b["dn"], stream)),
+            ("add2", lambda: o["add2"].run([b["x2"], b["dn"]], y, stream)),
+        ]
+        for name, fn in plan:
+            if events is not None:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                fn()
+                e.record()
+                events.setdefault(name, []).append((s, e))
+            else:
+                fn()
+
+    # ---------------------------------------------------------------- inputs
+    def materialize(self, dense: torch.Tensor, rel: B.Relation) -> torch.Tensor:
+        """Copy a dense row-major bf16 device tensor into `rel`'s blocking
+        with ja_repartition (a dense tensor is the relation with one block)."""
+        src = B.Relation(rel.shape, nblk=[1] * len(rel.shape), dtype=rel.dtype)
+        out = alloc(rel, dense.device)
+        rp = Repart(src, rel, device=dense.device)
+        try:
+            rp.run(dense.reshape(-1), out)
+        finally:
+            torch.cuda.synchronize()
+            rp.close()
+        return out
+
+    def dense(self, t: torch.Tensor, rel: B.Relation) -> torch.Tensor:
+        """The inverse of `materialize`: a relation back to a dense tensor."""
+        dst = B.Relation(rel.shape, nblk=[1] * len(rel.shape), dtype=rel.dtype)
+        out = alloc(dst, t.device)
+        rp = Repart(rel, dst, device=t.device)
+        try:
+            rp.run(t, out)
+        finally:
+            torch.cuda.synchronize()
+            rp.close()
+        return out.reshape(rel.shape)
+
+    def close(self):
+        for op in self.ops.values():
+            op.close()
+        for rp in self.rp.values():
+            rp.close()

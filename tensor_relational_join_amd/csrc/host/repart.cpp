@@ -49,13 +49,13 @@ std::vector<int64_t> strides_of(const std::vector<int64_t>& shape) {
 // value u meaning "the inner part has extent u").  Returns the sub-extents
 // from outer to inner, or an empty vector if the cuts do not nest.
 std::vector<int64_t> refine(int64_t n, const std::set<int64_t>& cuts) {
+    if (n == 1) return {1};  // a unit dimension is its own (single) sub-dimension
     std::vector<int64_t> c(cuts.begin(), cuts.end());  // ascending, includes 1 and n
     std::vector<int64_t> sub;
     for (size_t i = c.size() - 1; i > 0; --i) {
         if (c[i] % c[i - 1]) return {};
         sub.push_back(c[i] / c[i - 1]);
     }
-    (void)n;
     return sub;
 }
 
@@ -135,6 +135,7 @@ static ja_status build_repart(const Rel& S, const Rel& Dr, const ja_view* view, 
         int64_t inner = vshape[v];
         for (auto e : ext) {
             inner /= e;
+            if (e == 1) continue;  // unit sub-dimensions index nothing
             Sub s{};
             s.ext = e;
             s.vdim = v;

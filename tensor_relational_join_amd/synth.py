@@ -123,3 +123,26 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns to float32 (for convenience in
     harness code; not used by either implementation's arithmetic)."""
     return (np.ascontiguousarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+LLAMA_BLOCK_STREAMS = ["x", "g1", "w_qkv", "w_o", "g2", "w_gate", "w_up", "w_down"]
+
+
+def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int) -> dict:
+    """bf16 bit patterns of one block's inputs: x ~ N(0,1) [batch*seq, dm];
+    gains ~ N(1, 0.1) [dm]; weights ~ N(0, 0.02): w_qkv [dm, 3dm] (= [W_q |
+    W_k | W_v]), w_o [dm, dm], w_gate and w_up [dm, ffn], w_down [ffn, dm].
+    Stream i of `seed` feeds the i-th tensor of LLAMA_BLOCK_STREAMS."""
+    T = batch * seq
+    shapes = {"x": (T, dm), "g1": (dm,), "w_qkv": (dm, 3 * dm), "w_o": (dm, dm), "g2": (dm,),
+              "w_gate": (dm, ffn), "w_up": (dm, ffn), "w_down": (ffn, dm)}
+    out = {}
+    for i, name in enumerate(LLAMA_BLOCK_STREAMS):
+        if name == "x":
+            mean, std = 0.0, 1.0
+        elif name in ("g1", "g2"):
+            mean, std = 1.0, 0.1
+        else:
+            mean, std = 0.0, 0.02
+        out[name] = normal_bf16(seed, i, shapes[name], mean=mean, std=std)
+    return out

@@ -1,0 +1,152 @@
+"""The LLaMA-shaped block as a graph of join-agg operators on the GPU,
+against the oracle.
+
+Per-step parity (the bar): every step's GPU output is compared with the
+oracle applied to that step's GPU inputs -- full tensors for the
+memory-bound steps and at reduced shapes, sampled outputs for the full-size
+contractions and attention, bit-exact for the two repartitions -- at the
+bf16 tolerance (relative Frobenius <= 2e-3).
+
+End-to-end chain: the block output is also compared with the oracle's own
+chain from the block inputs.  Both sides round every one of the eleven
+materialised bf16 relations, so once an upstream value differs by a fraction
+of an ulp the downstream roundings decorrelate; each decorrelated rounding
+adds up to ~2^-8/sqrt(6) ~ 1.6e-3 relative noise, and with up to ~20
+such stages feeding forward the bound is sqrt(20) * 1.6e-3 ~ 7e-3, so the
+chain is held to CHAIN_TOL = 1e-2.  A wrong index, head mapping or dropped
+tuple gives errors of order 1."""
+import itertools
+
+import numpy as np
+import pytest
+
+from gpu_helpers import bf16_bits, rel_frobenius, to_dev_bf16
+from tensor_relational_join_amd import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+CHAIN_TOL = 1e-2
+
+
+def _pack(orc, rel, bits):
+    return to_dev_bf16(orc.Relation(rel.shape, rel.splits).pack(bits))
+
+
+def _unpack(orc, rel, t, as_bits=False):
+    bits = orc.Relation(rel.shape, rel.splits).unpack(bf16_bits(t))
+    return bits if as_bits else orc.bf16_to_f64(bits)
+
+
+def _run_block(orc, batch, seq, dm, heads, ffn, seed):
+    import torch
+
+    from tensor_relational_join_amd.block import LlamaBlock
+    from tensor_relational_join_amd.device import alloc
+
+    blk = LlamaBlock(batch, seq, dm, heads, ffn)
+    inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn)
+    x = _pack(orc, blk.x_rel, inp["x"])
+    w = {k: _pack(orc, rel, inp[k]) for k, rel in blk.w_rel.items()}
+    w["g1"] = _pack(orc, blk.g_rel, inp["g1"])
+    w["g2"] = _pack(orc, blk.ops["norm2"].in_rels[1], inp["g2"])
+    y = alloc(blk.ops["add2"].out_rel)
+    blk.forward(x, w, y)
+    torch.cuda.synchronize()
+    return blk, inp, x, y
+
+
+def _check_steps(orc, blk, inp, y, sampled: bool):
+    """Each step against the oracle on the GPU's inputs to that step.
+    Returns {step: error}; repartitions report 0.0 when bit-exact."""
+    o, b = blk.ops, blk.buf
+    batch, seq, dm, heads, ffn, T = blk.batch, blk.seq, blk.dm, blk.heads, blk.ffn, blk.T
+    f64 = orc.bf16_to_f64
+    rng = np.random.default_rng(2)
+    errs = {}
+
+    def contract(name, a_rel, a_buf, w_name, out_rel, out_buf, N, blockN):
+        A = _unpack(orc, a_rel, a_buf)
+        W = f64(inp[w_name])
+        got = _unpack(orc, out_rel, out_buf)
+        if sampled:
+            rows = sorted(set([0, 1, T // 2 - 1, T // 2, T - 1] + list(rng.integers(0, T, 24))))
+            cols = sorted(set([0, 1, 127, 128, blockN - 1, blockN, N - 1] + list(rng.integers(0, N, 24))))
+            pts = np.array(list(itertools.product(rows, cols)))
+            want = orc.round_bf16(orc.einsum_points("ij,jk->ik", A, W, pts))
+            errs[name] = rel_frobenius(got[pts[:, 0], pts[:, 1]], want)
+        else:
+            errs[name] = rel_frobenius(got, orc.round_bf16(orc.matmul(A, W)))
+
+    xd = f64(inp["x"])
+    h1 = _unpack(orc, o["norm1"].out_rel, b["h1"])
+    errs["norm1"] = rel_frobenius(h1, orc.round_bf16(orc.rmsnorm(xd, f64(inp["g1"]), blk.eps)))
+    contract("qkv", o["norm1"].out_rel, b["h1"], "w_qkv", o["qkv"].out_rel, b["qkv"], 3 * dm, 3 * dm // 2)
+    qr, hr = o["qkv"].out_rel, blk.heads_rel
+    want_heads = orc.repartition(orc.Relation(qr.shape, qr.splits), bf16_bits(b["qkv"]),
+                                 orc.Relation(hr.shape, hr.splits), (batch, seq, 3, heads, 128), (2, 0, 3, 1, 4))
+    heads_bits = bf16_bits(b["heads"])
+    errs["to_heads"] = 0.0 if np.array_equal(heads_bits, want_heads) else 1.0
+    hd = f64(orc.Relation(hr.shape, hr.splits).unpack(heads_bits))
+    Od = _unpack(orc, o["attn"].out_rel, b["O"])
+    if sampled:
+        ss = [0, 1, 127, 128, 1000, seq - 1]
+        rows = np.array([(bb, hh, s) for bb, hh in [(0, 0), (batch // 2, heads // 2), (batch - 1, heads - 1)]
+                         for s in ss])
+    else:
+        rows = np.array(list(itertools.product(range(batch), range(heads), range(seq))))
+    want = orc.round_bf16(orc.attention_rows(hd[0], hd[1], hd[2], rows, 1.0 / np.sqrt(128.0), True))
+    errs["attn"] = rel_frobenius(Od[rows[:, 0], rows[:, 1], rows[:, 2]], want)
+    ar, orl = o["attn"].out_rel, o["oproj"].in_rels[0]
+    want_o = orc.repartition(orc.Relation(ar.shape, ar.splits), bf16_bits(b["O"]),
+                             orc.Relation(orl.shape, orl.splits), (batch, heads, seq, 128), (0, 2, 1, 3))
+    errs["to_tokens"] = 0.0 if np.array_equal(bf16_bits(b["o"]), want_o) else 1.0
+    contract("oproj", orl, b["o"], "w_o", o["oproj"].out_rel, b["a"], dm, dm // 2)
+    x2 = _unpack(orc, o["add1"].out_rel, b["x2"])
+    errs["add1"] = rel_frobenius(x2, orc.round_bf16(xd + _unpack(orc, o["oproj"].out_rel, b["a"])))
+    h2 = _unpack(orc, o["norm2"].out_rel, b["h2"])
+    errs["norm2"] = rel_frobenius(h2, orc.round_bf16(orc.rmsnorm(x2, f64(inp["g2"]), blk.eps)))
+    contract("gate", o["norm2"].out_rel, b["h2"], "w_gate", o["gate"].out_rel, b["gt"], ffn, ffn // 4)
+    contract("up", o["norm2"].out_rel, b["h2"], "w_up", o["up"].out_rel, b["up"], ffn, ffn // 4)
+    fa = _unpack(orc, o["swiglu"].out_rel, b["f"])
+    errs["swiglu"] = rel_frobenius(fa, orc.round_bf16(orc.swiglu(_unpack(orc, o["gate"].out_rel, b["gt"]),
+                                                                 _unpack(orc, o["up"].out_rel, b["up"]))))
+    contract("down", o["swiglu"].out_rel, b["f"], "w_down", o["down"].out_rel, b["dn"], dm, dm // 2)
+    yd = _unpack(orc, o["add2"].out_rel, y)
+    errs["add2"] = rel_frobenius(yd, orc.round_bf16(x2 + _unpack(orc, o["down"].out_rel, b["dn"])))
+    assert np.isfinite(yd).all()
+    return errs, yd
+
+
+def test_block_reduced_shapes(orc):
+    batch, seq, dm, heads, ffn = 2, 256, 256, 2, 704
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=11)
+    try:
+        errs, yd = _check_steps(orc, blk, inp, y, sampled=False)
+        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
+        want = orc.llama_block(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"],
+                               batch, seq, heads)
+        chain = rel_frobenius(yd, want)
+        print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        for k, v in errs.items():
+            assert v <= TOL, (k, v)
+        assert chain <= CHAIN_TOL
+    finally:
+        blk.close()
+
+
+def test_block_full_size(orc):
+    batch, seq, dm, heads, ffn = 4, 2048, 4096, 32, 11008
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=5)
+    try:
+        errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
+        toks = [bb * seq + s for bb in range(batch) for s in (0, 1, 63, 100)]
+        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
+        want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
+                                        f["w_down"], batch, seq, heads, toks)
+        chain = rel_frobenius(yd[toks], want_y)
+        print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        for k, v in errs.items():
+            assert v <= TOL, (k, v)
+        assert chain <= CHAIN_TOL
+    finally:
+        blk.close()

@@ -357,3 +357,10 @@ def test_repartition_llama_views_full_size(dev, orc):
                  [_eq(8192, 2), _eq(4096, 2)], vshape=(4, 32, 2048, 128), perm=(0, 2, 1, 3), seed=6)
     _repart_case(dev, orc, (8192, 4096), [_eq(8192, 2), _eq(4096, 8)], (8192, 4096),
                  [_eq(8192, 2), _eq(4096, 2)], seed=7)
+
+
+def test_repartition_unit_dimensions(dev, orc):
+    _repart_case(dev, orc, (256, 768), [_eq(256, 2), _eq(768, 2)], (3, 1, 2, 256, 128),
+                 [_eq(3, 3), [0, 1], _eq(2, 2), _eq(256, 2), [0, 128]], vshape=(1, 256, 3, 2, 128),
+                 perm=(2, 0, 3, 1, 4), seed=8)
+    _repart_case(dev, orc, (1, 1), [[0, 1], [0, 1]], (1,), [[0, 1]], vshape=(1,), perm=(0,), dtype="f32", seed=9)

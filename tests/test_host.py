@@ -244,3 +244,16 @@ def test_repartition_atoms_for_head_views(B):
         B.ja_repart_create(B.Relation((4, 6), nblk=(1, 1), dtype=B.JA_F32),
                            B.Relation((4, 6), nblk=(1, 1), dtype=B.JA_BF16))
     assert e.value.name == "JA_ERR_DTYPE"
+
+
+def test_repartition_views_with_unit_dimensions(B):
+    # batch of one: the view's leading extent-1 axis indexes nothing
+    src = B.Relation((256, 768), nblk=(2, 2), dtype=B.JA_BF16)
+    dst = B.Relation((3, 1, 2, 256, 128), nblk=(3, 1, 2, 2, 1), dtype=B.JA_BF16)
+    rp = B.ja_repart_create(src, dst, B.make_view((1, 256, 3, 2, 128), (2, 0, 3, 1, 4)))
+    assert B.ja_repart_count(rp) == (12, 12)
+    B.ja_repart_destroy(rp)
+    rp = B.ja_repart_create(B.Relation((1, 1), nblk=(1, 1), dtype=B.JA_F32), B.Relation((1,), nblk=(1,), dtype=B.JA_F32),
+                            B.make_view((1,), (0,)))
+    assert B.ja_repart_count(rp) == (1, 1)
+    B.ja_repart_destroy(rp)
