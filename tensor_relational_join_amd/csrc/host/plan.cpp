@@ -203,9 +203,14 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         g.t_begin = (int32_t)t.seg[sg];
         g.t_end = (int32_t)t.seg[sg + 1];
         g.pad = 0;
+        // grouped order: GEMM_GROUP_M row tiles, then every column tile, so a
+        // contiguous run of the list forms a compact block of output tiles
+        const int32_t mt = (int32_t)((m + TM - 1) / TM), ntl = (int32_t)((n + TN - 1) / TN);
         for (int32_t b = 0; b < nb; ++b)
-            for (int32_t m0 = 0; m0 < m; m0 += TM)
-                for (int32_t n0 = 0; n0 < n; n0 += TN) tiles.push_back({(int32_t)sg, m0, n0, b});
+            for (int32_t mg = 0; mg < mt; mg += GEMM_GROUP_M)
+                for (int32_t nj = 0; nj < ntl; ++nj)
+                    for (int32_t mi = mg; mi < std::min(mt, mg + GEMM_GROUP_M); ++mi)
+                        tiles.push_back({(int32_t)sg, mi * TM, nj * TN, b});
         AggSeg& a = asegs[sg];
         a.out_off = g.c_off;
         if (nb * m * n > lim) return fail(JA_ERR_UNSUPPORTED, "output block beyond 2^31 elements");
