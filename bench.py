@@ -15,7 +15,10 @@ the dominant kernel (the bf16 MFMA contraction), timed with HIP events on
 the stream the steps run on.  `cpu_baseline` times the CPU oracle on a
 bounded token sample of the same block.
 
-    python bench.py [--steps K] [--warmup W] [--workload block|ffn|attention|norm_swiglu]
+    python bench.py [--steps K] [--warmup W] [--workload block|ffn|attention|norm_swiglu|copy]
+
+The non-block workloads print per-operator diagnostics (and `copy` the HBM
+copy ceiling); only `block` prints the contract line.
 """
 from __future__ import annotations
 
@@ -80,6 +83,25 @@ def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0):
     return {"value": flops(n) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "float64 oracle block forward on tokens 0..%d of batch 0 (%.1f GFLOP, %.2f s)" %
                       (n - 1, flops(n) / 1e9, dt)}
+
+
+def _gemm_traffic():
+    """HBM-side bytes per contraction launch from the committed counter record
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or None
+    when the kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "gemm_bf16_block_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except (OSError, ValueError, KeyError):
+        return None
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
 def bench_block(args):
@@ -147,7 +169,8 @@ def bench_block(args):
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "roofline": {"kernel": "gemm_bf16_kernel (contraction join-agg, fused SUM)", "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": _gemm_traffic(),
+                     "traffic_unit": "bytes per launch (L2 memory side, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "launches_per_step": len(GEMMS), "gflop_per_launch": round(gemm_flops / len(GEMMS) / 1e9, 1),
                      "avg_launch_ms": round(gemm_ms / len(GEMMS), 4)},
         "parts": parts,
@@ -166,6 +189,25 @@ def bench_kernel(args):
     from tensor_relational_join_amd import synth
     from tensor_relational_join_amd.device import Op, alloc
 
+    if args.workload == "copy":
+        # a plain device copy of known size: the HBM ceiling, and the
+        # calibration point of the FETCH_SIZE / WRITE_SIZE counters
+        n = 1 << 29  # 1 GiB of bf16
+        src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / args.steps
+        gbs = 2.0 * n * 2 / (ms / 1e3) / 1e9
+        return {"workload": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "steps": args.steps,
+                "ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
     runs = []
     if args.workload == "ffn":
         sp = {"b": _eq(2048, 2), "d": _eq(4096, 4), "f": _eq(11008, 4)}
@@ -225,7 +267,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="block", choices=["block", "ffn", "attention", "norm_swiglu"])
+    ap.add_argument("--workload", default="block", choices=["block", "ffn", "attention", "norm_swiglu", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
