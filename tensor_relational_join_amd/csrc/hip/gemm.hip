@@ -240,6 +240,302 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* 
     }
 }
 
+// ---------------------------------------------------------------- bf16 MFMA, direct-to-LDS pipeline
+// The same tile and wavefront shape, but operand tiles travel from global
+// memory straight into LDS (buffer_load ... lds, 16 bytes per lane) and NS
+// stages of BK = 32 contracted elements are in flight at once, so a stage's
+// loads have NS - 1 stages of MFMA work to arrive in.  No operand passes
+// through registers on its way in; an operand whose rows are contiguous in
+// memory (k strided) is stored as [k][rows] and read back transposed with
+// ds_read_b64_tr_b16.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_p;
+typedef __attribute__((address_space(3))) bf16x8_t* lds_bf16x8_p;
+
+constexpr uint32_t DMA_OOB = 0x80000000u;  // a buffer offset past any valid extent: reads as zero
+
+// Raw buffer descriptor over [base, base + bytes).
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4_t r;
+    r.x = (int32_t)(uint32_t)a;
+    r.y = (int32_t)(uint32_t)(a >> 32);  // stride 0
+    r.z = (int32_t)bytes;
+    r.w = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from global memory into LDS: lane l's bytes land at
+// lds_byte + 16 l (lds_byte is wave-uniform); the global byte offset is
+// voff + soff (soff is wave-uniform).  The compiler does not see the LDS
+// write; the pipeline below waits on vmcnt itself before each barrier.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds_byte, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_byte), "v"(voff),
+                 "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// LDS layouts of a 32-wide stage (element offsets).  K-contiguous tile
+// [rows][32]: 16-byte chunk c of row r at c ^ ksw(r).  Row-contiguous tile
+// [32][R]: chunk c (8 rows of the operand) of k-row k at c ^ msw(k).  Both
+// were chosen against bank-conflict counts measured on gfx950 (64 banks of
+// 4 bytes; a ds_read_b128 serves 16 lanes per cycle, not 16 consecutive
+// lanes): an MFMA fragment read of either tile takes the minimum 4 (b128)
+// or 2 (b64 transposed) LDS cycles.
+__device__ __forceinline__ int ksw(int r) { return ((r >> 2) & 1) << 1; }
+__device__ __forceinline__ int msw(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+__device__ __forceinline__ int koff(int r, int c) { return r * 32 + ((c ^ ksw(r)) << 3); }
+template <int R>
+__device__ __forceinline__ int moff(int k, int n) {
+    return k * R + (((n >> 3) ^ msw(k)) << 3) + (n & 7);
+}
+
+// One operand tile of a stage: rows [r0, r0 + R) x k [k0, k0 + 32).  Each
+// lane's byte offsets for k0 = 0 are computed once per tuple (rows past the
+// block already folded into an out-of-range offset); a full stage then only
+// adds the uniform k0 term as the instruction's scalar offset.
+template <int R, int NT, bool MN>
+struct DmaTile {
+    static constexpr int SLOTS = R * 32 / 8;
+    static constexpr int WAVES = NT / 64;
+    static constexpr int PER_WAVE = SLOTS / 64 / WAVES;  // load instructions per wavefront per stage
+    static_assert(SLOTS % (64 * WAVES) == 0, "tile must split evenly over the wavefronts");
+    uint32_t off[PER_WAVE];  // byte offset of this lane's slot at k0 = 0
+    int kin[PER_WAVE];       // k of the slot's first element inside the stage
+
+    // the slot's logical (row, k) inside the tile
+    __device__ static void slot(int s, int& r, int& k) {
+        if (MN) {
+            k = s / (R / 8);
+            r = ((s % (R / 8)) ^ msw(k)) * 8;
+        } else {
+            r = s / 4;
+            k = ((s % 4) ^ ksw(r)) * 8;
+        }
+    }
+    __device__ void setup(int ld, int r0, int rext, int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            int r, k;
+            slot((wave * PER_WAVE + j) * 64 + lane, r, k);
+            const int gr = r0 + r;
+            kin[j] = k;
+            off[j] = gr < rext ? (uint32_t)((MN ? (int64_t)k * ld + gr : (int64_t)gr * ld + k) * 2) : DMA_OOB;
+        }
+    }
+    // uniform byte offset of contracted position k0
+    __device__ static uint32_t koffset(int ld, int k0) { return (uint32_t)((MN ? (int64_t)k0 * ld : (int64_t)k0) * 2); }
+
+    __device__ void issue(uint32_t lds_byte, i32x4_t rsrc, int ld, int k0, int kext, int wave) const {
+        const uint32_t soff = koffset(ld, k0);
+        if (k0 + 32 <= kext) {
+#pragma unroll
+            for (int j = 0; j < PER_WAVE; ++j) dma16(rsrc, lds_byte + (wave * PER_WAVE + j) * 1024, off[j], soff);
+        } else {  // ragged last stage: slots past the contracted extent read zeros
+#pragma unroll
+            for (int j = 0; j < PER_WAVE; ++j)
+                dma16(rsrc, lds_byte + (wave * PER_WAVE + j) * 1024,
+                      (k0 + kin[j] < kext && off[j] != DMA_OOB) ? off[j] + soff : DMA_OOB, 0u);
+        }
+    }
+
+    // The MFMA operand for fragment rows [rb, rb + 16): lane l gets row
+    // rb + l % 16, k = 8 (l / 16) .. +7.
+    __device__ static bf16x8_t frag(const uint16_t* tile, int rb, int lane) {
+        if (MN) {
+            const int g = lane >> 4, j = lane & 15;
+            const int k = 8 * g + (j >> 2), n = rb + 4 * (j & 3);
+            const uint16_t* p0 = tile + moff<R>(k, n);
+            const uint16_t* p1 = tile + moff<R>(k + 4, n);
+            i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)p0);
+            i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)p1);
+            typedef short i16x8_t __attribute__((ext_vector_type(8)));
+            i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8_t, v);
+        } else {
+            const int r = rb + (lane & 15);
+            return *reinterpret_cast<const bf16x8_t*>(tile + koff(r, lane >> 4));
+        }
+    }
+};
+
+// Wait until at most `left` of this wavefront's loads are in flight, then
+// barrier.  `left` is a compile-time count.
+template <int LEFT>
+__device__ __forceinline__ void wait_loads_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(LEFT) : "memory");
+}
+
+template <int BM, int BN, int NS, int WM, int WN, int AL, int BL, int OUT_BF16>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTile* __restrict__ tiles, int ntiles,
+                                                                    const GemmSeg* __restrict__ segs,
+                                                                    const GemmTuple* __restrict__ tuples,
+                                                                    const uint16_t* __restrict__ A,
+                                                                    const uint16_t* __restrict__ B,
+                                                                    void* __restrict__ C) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int BK = 32;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    using TA = DmaTile<BM, NT, AL == JA_A_KM>;
+    using TB = DmaTile<BN, NT, BL == JA_B_KN>;
+    constexpr int PER_STAGE = TA::PER_WAVE + TB::PER_WAVE;
+    constexpr int STAGE = (BM + BN) * BK;  // elements per stage
+    static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+    static_assert((NS - 1) * PER_STAGE <= 63, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) uint16_t gemm_lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const GemmTile tl = tiles[xcd_remap(blockIdx.x, ntiles)];
+    const GemmSeg sg = segs[tl.seg];
+    const int m0 = tl.m0, n0 = tl.n0;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)gemm_lds;
+
+    int nst = 0;
+    for (int t = sg.t_begin; t < sg.t_end; ++t) nst += (tuples[t].K + BK - 1) / BK;
+
+    f32x4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // load cursor: tuple lt, contracted offset lk inside it; the per-lane
+    // offsets and buffer descriptors of tuple lt are cached
+    int lt = sg.t_begin, lk = 0, cached = -1;
+    TA ta;
+    TB tb;
+    i32x4_t rsa, rsb;
+    int lda = 0, ldb = 0, kext = 0;
+    auto issue = [&](int buf) {
+        if (cached != lt) {
+            const GemmTuple tp = tuples[lt];
+            const uint16_t* pa = A + tp.a_off + (int64_t)tl.batch * tp.a_bstride;
+            const uint16_t* pb = B + tp.b_off + (int64_t)tl.batch * tp.b_bstride;
+            rsa = buffer_rsrc(pa, (uint32_t)(tp.a_bstride * 2));
+            rsb = buffer_rsrc(pb, (uint32_t)(tp.b_bstride * 2));
+            lda = tp.lda;
+            ldb = tp.ldb;
+            kext = tp.K;
+            ta.setup(lda, m0, sg.M, wave, lane);
+            tb.setup(ldb, n0, sg.N, wave, lane);
+            cached = lt;
+        }
+        const uint32_t st = lds0 + (uint32_t)(buf * STAGE * 2);
+        ta.issue(st, rsa, lda, lk, kext, wave);
+        tb.issue(st + BM * BK * 2, rsb, ldb, lk, kext, wave);
+        lk += BK;
+        if (lk >= kext) {
+            lk = 0;
+            ++lt;
+        }
+    };
+    // Stage s lives in LDS buffer s % NS.  The fragments of stage it + 1 are
+    // read into registers while the MFMAs of stage it run, so once a
+    // wavefront passes the barrier of iteration it, nobody reads buffer
+    // it % NS any more and it is refilled with stage it + NS.
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < nst) issue(s);
+
+    const int arow = wm * WTM, brow = wn * WTN;
+    bf16x8_t fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, bf16x8_t* a, bf16x8_t* b) {
+        const uint16_t* as = gemm_lds + buf * STAGE;
+        const uint16_t* bs = as + BM * BK;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = TA::frag(as, arow + i * 16, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = TB::frag(bs, brow + j * 16, lane);
+    };
+    // wait until stage `need` has landed: the stages issued after it may stay in flight
+    auto wait_stage = [&](int need) {
+        // issued so far: stages 0 .. NS - 1 up front, then one per step
+        const int ahead = need == 0 ? min(NS - 1, nst - 1) : min(need + NS - 2, nst - 1) - need;
+        if (ahead >= 3)
+            wait_loads_barrier<(NS >= 4 ? 3 : 0) * PER_STAGE>();
+        else if (ahead == 2)
+            wait_loads_barrier<(NS >= 3 ? 2 : 0) * PER_STAGE>();
+        else if (ahead == 1)
+            wait_loads_barrier<PER_STAGE>();
+        else
+            wait_loads_barrier<0>();
+    };
+    // After the barrier a wavefront starts its MFMAs at once (their operands
+    // were read one step earlier) and issues the refill of buffer it % NS
+    // halfway through them, so the load issue hides behind matrix work.
+    // Per step: barrier; the first quarter of the MFMAs (their operands were
+    // read one step earlier and are complete, so any wait the compiler puts
+    // before them is free); the fragment reads of the next stage; a quarter;
+    // the refill of buffer it % NS; the last half.  The reads and the load
+    // issue thus run in the shadow of matrix work.  The wait and the reads
+    // also run on the last step (reading a buffer nobody refills any more)
+    // so that every path has the same LDS reads in flight.
+    auto mfma_rows = [&](int i0, int i1, const bf16x8_t* ca, const bf16x8_t* cb) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            if (i >= i0 && i < i1)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb[j], ca[i], acc[i][j], 0, 0, 0);
+    };
+    auto step = [&](int it, bf16x8_t* ca, bf16x8_t* cb, bf16x8_t* na, bf16x8_t* nb) {
+        wait_stage(it + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(0, FM / 4, ca, cb);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags((it + 1) % NS, na, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(FM / 4, FM / 2, ca, cb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + NS < nst) issue(it % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(FM / 2, FM, ca, cb);
+    };
+    if (nst > 0) {
+        wait_stage(0);
+        read_frags(0, fa[0], fb[0]);
+    }
+    for (int it = 0; it < nst; it += 2) {
+        step(it, fa[0], fb[0], fa[1], fb[1]);
+        if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
+    }
+
+    // epilogue: lane owns C[row][col .. col+3] of every fragment
+    const int kc = lane >> 4;
+    const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = m0 + arow + i * 16 + (lane & 15);
+        if (row >= sg.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + brow + j * 16 + 4 * kc;
+            const int64_t off = cbase + (int64_t)row * sg.ldc + col;
+            const f32x4_t a = acc[i][j];
+            if (col + 4 <= sg.N && (off & 3) == 0) {
+                if (OUT_BF16)
+                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_bf16x2(a[0], a[1]),
+                                                                               pack_bf16x2(a[2], a[3]));
+                else
+                    *reinterpret_cast<float4*>((float*)C + off) = make_float4(a[0], a[1], a[2], a[3]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (col + r < sg.N) {
+                        if (OUT_BF16)
+                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_bf16(a[r]);
+                        else
+                            ((float*)C)[off + r] = a[r];
+                    }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- fp32 path
 // Plain LDS-tiled fp32 FMA kernel (64x64 tile, 4x4 outputs per thread) for
 // fp32 relations.  Same segment / tuple walk as the bf16 kernel.
@@ -303,18 +599,34 @@ static void launch_bf16(const GemmTile* tiles, int ntiles, const GemmSeg* segs, 
                        tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C);
 }
 
+template <int AL, int BL, int OB>
+static void launch_bf16_dma(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples,
+                            const void* A, const void* B, void* C, hipStream_t s) {
+    constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, NS = GEMM_DMA_STAGES, WM = 2, WN = 4;
+    constexpr unsigned lds = (unsigned)NS * (BM + BN) * 32 * sizeof(uint16_t);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, OB>), dim3(ntiles), dim3(WM * WN * 64), lds,
+                       s, tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C);
+}
+
 template <int AL, int BL>
-static void launch_bf16_out(int out_bf16, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
+static void launch_bf16_out(int out_bf16, int dma, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
                             const GemmTuple* tuples, const void* A, const void* B, void* C, hipStream_t s) {
-    if (out_bf16)
-        launch_bf16<AL, BL, 1>(tiles, ntiles, segs, tuples, A, B, C, s);
-    else
-        launch_bf16<AL, BL, 0>(tiles, ntiles, segs, tuples, A, B, C, s);
+    if (dma) {
+        if (out_bf16)
+            launch_bf16_dma<AL, BL, 1>(tiles, ntiles, segs, tuples, A, B, C, s);
+        else
+            launch_bf16_dma<AL, BL, 0>(tiles, ntiles, segs, tuples, A, B, C, s);
+    } else {
+        if (out_bf16)
+            launch_bf16<AL, BL, 1>(tiles, ntiles, segs, tuples, A, B, C, s);
+        else
+            launch_bf16<AL, BL, 0>(tiles, ntiles, segs, tuples, A, B, C, s);
+    }
 }
 
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
                        const void* A, const void* B, void* C, int32_t in_dtype, int32_t out_dtype, int32_t a_layout,
-                       int32_t b_layout, hipStream_t s) {
+                       int32_t b_layout, int32_t dma, hipStream_t s) {
     const uint8_t* t = (const uint8_t*)table;
     const GemmTile* tiles = (const GemmTile*)(t + tiles_off);
     const GemmSeg* segs = (const GemmSeg*)(t + segs_off);
@@ -322,13 +634,13 @@ hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int
     if (in_dtype == JA_BF16) {
         const int ob = out_dtype == JA_BF16;
         if (a_layout == JA_A_MK && b_layout == JA_B_KN)
-            launch_bf16_out<JA_A_MK, JA_B_KN>(ob, tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16_out<JA_A_MK, JA_B_KN>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
         else if (a_layout == JA_A_MK && b_layout == JA_B_NK)
-            launch_bf16_out<JA_A_MK, JA_B_NK>(ob, tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16_out<JA_A_MK, JA_B_NK>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
         else if (a_layout == JA_A_KM && b_layout == JA_B_KN)
-            launch_bf16_out<JA_A_KM, JA_B_KN>(ob, tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16_out<JA_A_KM, JA_B_KN>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
         else
-            launch_bf16_out<JA_A_KM, JA_B_NK>(ob, tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16_out<JA_A_KM, JA_B_NK>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
     } else {
 #define JA_F32_CASE(al, bl)                                                                                       \
     hipLaunchKernelGGL((gemm_f32_kernel<al, bl>), dim3(ntiles), dim3(256), 0, s, tiles, ntiles, segs, tuples,     \

@@ -30,6 +30,7 @@ struct ja_plan {
     int64_t atiles_off = 0, asegs_off = 0, apoff_off = 0;
     int32_t natiles = 0;
     int32_t in_dtype = 0, out_dtype = 0, a_layout = 0, b_layout = 0;
+    int32_t gemm_dma = 0;  // bf16 operands reachable through 32-bit buffer offsets
     int64_t partial_elems = 0;
     // attention
     float scale = 0.f;
@@ -231,6 +232,10 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         for (const GemmSeg& g : segs)
             if ((!a_m_first && g.M % 8) || (b_k_first && g.N % 8))
                 return fail(JA_ERR_UNSUPPORTED, "bf16 contraction needs block extents that are multiples of 8");
+        // the direct-to-LDS kernel addresses each operand matrix with 32-bit byte offsets
+        bool dma = true;
+        for (const GemmTuple& g : tuples) dma = dma && g.a_bstride * 2 < lim && g.b_bstride * 2 < lim;
+        p->gemm_dma = dma ? 1 : 0;
     }
     p->partial_elems = part;
     p->tiles_off = put(p->table, tiles);
@@ -448,7 +453,7 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
         case JA_OP_CONTRACT:
             if (p->ntiles == 0) return JA_OK;
             JA_TRY_HIP(launch_gemm(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
-                                   out_ptr, p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, hs));
+                                   out_ptr, p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, p->gemm_dma, hs));
             break;
         case JA_OP_ATTENTION:
             if (p->ntiles == 0) return JA_OK;
@@ -478,7 +483,7 @@ ja_status ja_kernel(const ja_plan* p, const void* const* in_ptrs, void* partials
     if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
     if (p->nutiles == 0) return JA_OK;
     JA_TRY_HIP(launch_gemm(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
-                           partials, p->in_dtype, JA_F32, p->a_layout, p->b_layout, (hipStream_t)stream));
+                           partials, p->in_dtype, JA_F32, p->a_layout, p->b_layout, p->gemm_dma, (hipStream_t)stream));
     return JA_OK;
 }
 

@@ -139,6 +139,12 @@ BF16_CASES = [
     ("ji,jk->ik", {"i": [0, 64, 200], "j": [0, 160, 320], "k": [0, 72, 144]}),
     ("ji,kj->ik", {"i": [0, 136], "j": [0, 64, 128], "k": [0, 40, 96]}),
     ("bij,bjk->bik", {"b": [0, 2, 3], "i": [0, 70, 130], "j": [0, 64, 192], "k": [0, 80, 160]}),
+    # a segment shorter than the load pipeline: one 32-wide stage, then two
+    ("ij,jk->ik", {"i": [0, 64], "j": [0, 24], "k": [0, 40, 80]}),
+    ("ij,kj->ik", {"i": [0, 300], "j": [0, 40], "k": [0, 264]}),
+    # several tiles with ragged tails and uneven tuples inside a segment
+    ("ij,jk->ik", {"i": [0, 520], "j": [0, 200, 336, 432], "k": [0, 776]}),
+    ("ji,jk->ik", {"i": [0, 264, 520], "j": [0, 96, 328], "k": [0, 256, 264]}),
 ]
 
 
