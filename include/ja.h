@@ -139,7 +139,8 @@ ja_status ja_relation_block(const ja_relation_desc* rel, const int64_t* key, int
  *                   Scores Q K^T * scale joined on d; aggregation over t with
  *                   the online-softmax triple (max, sum of exponentials,
  *                   weighted sum of values); then O = weighted sum / sum.
- *                   params: "scale=<float>" (default 1/sqrt(|d|)),
+ *                   params: "scale=<float>" (default 1/sqrt(|d|); must be
+ *                   positive, JA_ERR_SPEC otherwise),
  *                   "causal=<s>,<t>" (key t visible to query s iff t <= s;
  *                   fully masked tuples are dropped at join).
  *   op "rmsnorm":   "rd,d->rd": y = x / sqrt(mean_d x^2 + eps) * gain; the

@@ -9,53 +9,93 @@
 // join followed by an aggregation, section 1; the aggregation operator need
 // not be addition, section 5.2).  Fully masked (query block, key block) pairs
 // never reach the kernel: the join drops them.
-//
-// One workgroup = 4 wavefronts = 128 query rows of one segment.  A segment's
-// tuples are folded in ascending key order, 64 keys per step:
-//   S^T[key][query] = K Q^T  with v_mfma_f32_32x32x16_bf16 (Q fragments stay
-//                            in registers for the whole segment);
-//   P = exp2(S * scale * log2(e) - m), fp32, then fp16;
-//   O^T[d][query] += V^T P^T with v_mfma_f32_32x32x16_f16.
-// Computing S transposed puts each lane on one query, so P leaves the first
-// MFMA's accumulators already in the second MFMA's B-operand layout.  V is
-// transposed (and converted to fp16) on its way to LDS, with the key order
-// inside each 16-key group arranged to match those accumulators.
+
 #include "dev_common.h"
 
 namespace ja {
 
-constexpr int AT_KT = 64;          // keys per step
-constexpr int AT_KPITCH = 128 + 8; // K tile row pitch in LDS (elements)
-constexpr int AT_VPITCH = AT_KT + 8;
+constexpr int AT_KT = 64;         // keys per step
+constexpr int AT_THREADS = 256;   // 4 wavefronts x 32 queries
+constexpr int AT_STAGE = AT_KT * ATTN_D * 2;  // elements per stage: K [64][128] bf16 + V^T [128][64] fp16
 
-__global__ __launch_bounds__(256) void attention_kernel(const AttnTile* __restrict__ tiles, int ntiles,
-                                                        const AttnSeg* __restrict__ segs,
-                                                        const AttnTuple* __restrict__ tuples,
-                                                        const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                        const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                                                        float scale_log2, int causal) {
+typedef int32_t at_i32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
+// LDS layouts (element offsets), chosen against bank-conflict counts measured
+// on gfx950 so that every MFMA fragment read takes the minimum 4 LDS cycles:
+// K tile [key][d] bf16, 16-byte chunk c of row `key` at c ^ kswz(key);
+// V^T tile [d][key'] fp16 (key' = key with the middle quads of every 16 keys
+// swapped, see below), chunk c of row d at c ^ vswz(d).
+__device__ __forceinline__ int kswz(int r) { return ((r & 1) << 1) ^ ((r >> 1) & 1) ^ (r & 4) ^ ((r >> 1) & 8); }
+__device__ __forceinline__ int vswz(int d) { return (d & 6) ^ (((d >> 3) & 1) * 3) ^ (((d >> 4) & 1) * 7); }
+__device__ __forceinline__ int at_koff(int key, int c) { return key * ATTN_D + ((c ^ kswz(key)) << 3); }
+__device__ __forceinline__ int at_voff(int d, int c) { return d * AT_KT + ((c ^ vswz(d)) << 3); }
+
+__device__ __forceinline__ at_i32x4_t at_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    at_i32x4_t r;
+    r.x = (int32_t)(uint32_t)a;
+    r.y = (int32_t)(uint32_t)(a >> 32);
+    r.z = (int32_t)bytes;
+    r.w = 0x00020000;
+    return r;
+}
+// Buffer load of 16 bytes; offsets past the descriptor's extent read as zero,
+// so masked loads need no branch (a branch around a load makes the compiler
+// wait for it on the spot).
+extern "C" __device__ at_i32x4_t at_buffer_load_x4(at_i32x4_t rsrc, int32_t voffset, int32_t soffset, int32_t aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+
+// 16 bytes per lane, global -> LDS (lane l's bytes at lds_byte + 16 l); the
+// compiler does not see the LDS write, the step loop waits on vmcnt itself.
+__device__ __forceinline__ void at_dma16(at_i32x4_t rsrc, uint32_t lds_byte, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_byte), "v"(voff),
+                 "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// One workgroup = 4 wavefronts = 128 query rows of one segment.  The
+// segment's tuples are folded in ascending key order, 64 keys per step:
+//   S^T[key][query] = K Q^T with v_mfma_f32_32x32x16_bf16 (Q fragments stay
+//                     in registers; each lane then holds one query);
+//   P = exp2(S * scale log2(e) - m), in fp32, rounded to fp16;
+//   O^T[d][query] += V^T P^T with v_mfma_f32_32x32x16_f16.
+// K and V are double buffered: while step i multiplies, K of step i + 1
+// streams into LDS directly and V of step i + 1 waits in registers, to be
+// converted to fp16 and transposed into LDS after the step's MFMAs; one
+// barrier per step.  Masks are only evaluated on steps that cross the
+// causal diagonal or the end of a key block, and O is rescaled only when
+// some query's running maximum moved.
+__global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile* __restrict__ tiles, int ntiles,
+                                                               const AttnSeg* __restrict__ segs,
+                                                               const AttnTuple* __restrict__ tuples,
+                                                               const uint16_t* __restrict__ Q,
+                                                               const uint16_t* __restrict__ K,
+                                                               const uint16_t* __restrict__ V,
+                                                               uint16_t* __restrict__ O, float scale_log2, int causal) {
     constexpr int D = ATTN_D;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[AT_KT * AT_KPITCH];
-    __shared__ __attribute__((aligned(16))) _Float16 Vt[D * AT_VPITCH];
+    extern __shared__ __attribute__((aligned(16))) uint16_t at_lds[];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)at_lds;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lq = lane & 31;
     const AttnTile tl = tiles[blockIdx.x];
     const AttnSeg sg = segs[tl.seg];
     const int qrow = tl.s0 + wave * 32 + lq;  // query row inside the block
     const int qglob = sg.s_lo + qrow;         // global query index (causal mask)
+    const int wave_qmin = sg.s_lo + tl.s0 + wave * 32;
     const int wave_qmax = sg.s_lo + min(tl.s0 + wave * 32 + 31, sg.S - 1);
+    const int tile_qmax = sg.s_lo + min(tl.s0 + 127, sg.S - 1);
 
-    // Q^T fragments (B operand): lane holds Q[query lq][d = 16*step + 8*g .. +7]
+    // Q^T fragments (B operand): lane holds Q[query lq][d = 16 st + 8 g .. +7]
     bf16x8_t qf[D / 16];
     {
-        const uint16_t* qp = Q + sg.q_off + (int64_t)tl.bh * sg.q_bhstride + (int64_t)qrow * D + 8 * g;
+        const at_i32x4_t rq = at_rsrc(Q + sg.q_off + (int64_t)tl.bh * sg.q_bhstride, (uint32_t)(sg.q_bhstride * 2));
+        const int32_t qo = qrow < sg.S ? (qrow * D + 8 * g) * 2 : (int32_t)0x80000000;
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (qrow < sg.S) v = *reinterpret_cast<const uint4*>(qp + 16 * st);
-            qf[st] = *reinterpret_cast<bf16x8_t*>(&v);
-        }
+        for (int st = 0; st < D / 16; ++st)
+            qf[st] = __builtin_bit_cast(bf16x8_t, at_buffer_load_x4(rq, qo + (qrow < sg.S ? 32 * st : 0), 0, 0));
     }
     f32x16_t oacc[D / 32];
 #pragma unroll
@@ -64,123 +104,179 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnTile* __restri
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
+    // steps: (tuple, 64-key offset) pairs some query of the tile can see
+    int nsteps = 0;
     for (int t = sg.t_begin; t < sg.t_end; ++t) {
         const AttnTuple tp = tuples[t];
+        int n = (tp.T + AT_KT - 1) / AT_KT;
+        if (causal) n = tile_qmax < tp.t_lo ? 0 : min(n, (tile_qmax - tp.t_lo) / AT_KT + 1);
+        nsteps += n;
+    }
+
+    // per-lane DMA slots of the K tile (4 per wavefront): key and chunk
+    int kkey[4];
+    uint32_t koffb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int s = (wave * 4 + j) * 64 + lane;  // 16-byte slot of the 16 KiB tile
+        const int key = s >> 4, c = (s & 15) ^ kswz(key);
+        kkey[j] = key;
+        koffb[j] = (uint32_t)((key * D + c * 8) * 2);
+    }
+    // V staging: keys 4 kg .. 4 kg + 3 of the step, d = 8 dj .. 8 dj + 7
+    const int kg = tid >> 4, dj = tid & 15;
+    at_i32x4_t vr[4];
+
+    // load cursor
+    int lt = sg.t_begin, lkt = 0;
+    auto load_step = [&](int buf) {
+        const AttnTuple tp = tuples[lt];
         const uint16_t* kb = K + tp.k_off + (int64_t)tl.bh * tp.kv_bhstride;
-        const uint16_t* vb = V + tp.v_off + (int64_t)tl.bh * tp.kv_bhstride;
-        for (int kt0 = 0; kt0 < tp.T; kt0 += AT_KT) {
-            const int key0 = tp.t_lo + kt0;  // global index of the step's first key
-            // whole workgroup skips steps no query of the tile can see
-            const int tile_qmax = sg.s_lo + min(tl.s0 + 127, sg.S - 1);
-            if (causal && key0 > tile_qmax) break;
-            // ---- stage K (direct) and V (transposed to [d][key], fp16) through registers
-            uint4 kr[4], vr[4];
+        const at_i32x4_t rs = at_rsrc(kb, (uint32_t)(tp.kv_bhstride * 2));
+        const uint32_t st = lds0 + (uint32_t)(buf * AT_STAGE * 2);
+        const uint32_t soff = (uint32_t)(lkt * D * 2);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int vi = tid + j * 256;
-                int r = vi >> 4, c = (vi & 15) * 8;
-                kr[j] = make_uint4(0, 0, 0, 0);
-                if (kt0 + r < tp.T) kr[j] = *reinterpret_cast<const uint4*>(kb + (int64_t)(kt0 + r) * D + c);
+        for (int j = 0; j < 4; ++j) {
+            // keys past the block read as zero: 0x80000000 stays past the
+            // descriptor's extent with or without the scalar offset added
+            const bool ok = lkt + kkey[j] < tp.T;
+            at_dma16(rs, st + (wave * 4 + j) * 1024, ok ? koffb[j] : 0x80000000u, soff);
+        }
+        const at_i32x4_t rv = at_rsrc(V + tp.v_off + (int64_t)tl.bh * tp.kv_bhstride, (uint32_t)(tp.kv_bhstride * 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = lkt + kg * 4 + i;
+            vr[i] = at_buffer_load_x4(rv, key < tp.T ? (key * D + dj * 8) * 2 : (int32_t)0x80000000, 0, 0);
+        }
+        // advance the cursor to the next visible step
+        lkt += AT_KT;
+        if (lkt >= tp.T || (causal && tp.t_lo + lkt > tile_qmax)) {
+            lkt = 0;
+            ++lt;
+        }
+    };
+    // V^T[d][key'] <- vr, converted to fp16; key' swaps the middle quads of
+    // each 16 keys, matching the order P^T takes from the S^T accumulators
+    auto store_v = [&](int buf) {
+        _Float16* vt = reinterpret_cast<_Float16*>(at_lds + buf * AT_STAGE + AT_KT * D);
+        const int hgrp = kg >> 2, q = kg & 3;
+        const int qpos = q == 1 ? 2 : (q == 2 ? 1 : q);
+        const int c = 2 * hgrp + (qpos >> 1), half = qpos & 1;
+        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vr[0]);
+        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vr[1]);
+        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vr[2]);
+        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vr[3]);  // words of the 4 keys' 8 d values
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                h4 hv = {(_Float16)(e ? bf16hi_to_f32(r0[w]) : bf16lo_to_f32(r0[w])),
+                         (_Float16)(e ? bf16hi_to_f32(r1[w]) : bf16lo_to_f32(r1[w])),
+                         (_Float16)(e ? bf16hi_to_f32(r2[w]) : bf16lo_to_f32(r2[w])),
+                         (_Float16)(e ? bf16hi_to_f32(r3[w]) : bf16lo_to_f32(r3[w]))};
+                const int d = dj * 8 + 2 * w + e;
+                *reinterpret_cast<h4*>(vt + at_voff(d, c) + half * 4) = hv;
             }
-            // V: one sub-block of 4 keys x 8 d per thread (16 key quads x 16 d octets)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int key = kt0 + (tid >> 4) * 4 + i;
-                vr[i] = make_uint4(0, 0, 0, 0);
-                if (key < tp.T) vr[i] = *reinterpret_cast<const uint4*>(vb + (int64_t)key * D + (tid & 15) * 8);
-            }
-            __syncthreads();  // previous step's readers are done
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int vi = tid + j * 256;
-                int r = vi >> 4, c = (vi & 15) * 8;
-                *reinterpret_cast<uint4*>(Ks + r * AT_KPITCH + c) = kr[j];
-            }
-            {
-                // thread: keys kg*4..+3, d = 8*(tid&15) .. +7
-                int kg = tid >> 4, d0 = (tid & 15) * 8;
-                int hgrp = kg >> 2, q = kg & 3;
-                int qpos = q == 1 ? 2 : (q == 2 ? 1 : q);  // swap the middle quads of each 16-key group
-                int col = hgrp * 16 + qpos * 4;
-                const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vr[0]);
-                const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vr[1]);
-                const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vr[2]);
-                const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vr[3]);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        float a0 = e ? bf16hi_to_f32(r0[w]) : bf16lo_to_f32(r0[w]);
-                        float a1 = e ? bf16hi_to_f32(r1[w]) : bf16lo_to_f32(r1[w]);
-                        float a2 = e ? bf16hi_to_f32(r2[w]) : bf16lo_to_f32(r2[w]);
-                        float a3 = e ? bf16hi_to_f32(r3[w]) : bf16lo_to_f32(r3[w]);
-                        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-                        h4 hv = {(_Float16)a0, (_Float16)a1, (_Float16)a2, (_Float16)a3};
-                        *reinterpret_cast<h4*>(Vt + (d0 + 2 * w + e) * AT_VPITCH + col) = hv;
-                    }
-                }
-            }
-            __syncthreads();
-            if (causal && key0 > wave_qmax) continue;  // nothing visible to this wave
-            // ---- S^T = K Q^T : two 32-key tiles
+    };
+    auto sync_step = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    // compute cursor (same walk as the load cursor)
+    int ct = sg.t_begin, ckt = 0;
+    if (nsteps > 0) {
+        load_step(0);
+        store_v(0);
+        sync_step();
+    }
+    for (int i = 0; i < nsteps; ++i) {
+        const int buf = i & 1;
+        const bool more = i + 1 < nsteps;
+        if (more) load_step(buf ^ 1);
+        const AttnTuple tp = tuples[ct];
+        const int key0 = tp.t_lo + ckt;  // global index of the step's first key
+        if (!causal || key0 <= wave_qmax) {
+            const uint16_t* ks = at_lds + buf * AT_STAGE;
+            const _Float16* vt = reinterpret_cast<const _Float16*>(ks + AT_KT * D);
+            // ---- S^T = K Q^T: two 32-key tiles
             f32x16_t s[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
+                // all eight fragments of the 32-key tile first, so LDS latency
+                // overlaps the MFMA chain
+                bf16x8_t kf[D / 16];
+#pragma unroll
+                for (int st = 0; st < D / 16; ++st)
+                    kf[st] = *reinterpret_cast<const bf16x8_t*>(ks + at_koff(kt * 32 + lq, 2 * st + g));
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
-                for (int st = 0; st < D / 16; ++st) {
-                    bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Ks + (kt * 32 + lq) * AT_KPITCH + 16 * st + 8 * g);
-                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[kt], 0, 0, 0);
-                }
+                for (int st = 0; st < D / 16; ++st)
+                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s[kt], 0, 0, 0);
             }
-            // ---- online softmax for query lq (this lane holds 32 of the 64 keys)
+            // ---- masks: only where the step crosses the diagonal or the key block's end
+            const bool ragged = ckt + AT_KT > tp.T;
+            if (ragged || (causal && key0 + AT_KT - 1 > wave_qmin)) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        // acc index r -> key 8 (r / 4) + 4 g + r % 4 inside the 32-key tile
+                        const int kk = kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        const bool ok = ckt + kk < tp.T && (!causal || key0 + kk <= qglob);
+                        s[kt][r] = ok ? s[kt][r] : -INFINITY;
+                    }
+            }
+            // ---- online softmax for query lq (this lane holds 32 of the 64 keys);
+            // the maximum is taken on raw scores, which the positive scale preserves
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    // acc index r -> key 8*(r/4) + 4*g + r%4 inside the 32-key tile
-                    int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    float v = s[kt][r] * scale_log2;
-                    bool ok = (kt0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) < tp.T && (!causal || key <= qglob);
-                    v = ok ? v : -INFINITY;
-                    s[kt][r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            const float mc = m_new == -INFINITY ? 0.f : m_new * scale_log2;
+            const float alpha = __builtin_amdgcn_exp2f(m_run * scale_log2 - mc);
             m_run = m_new;
             float lsum = 0.f;
-            typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-            h8 pf[4];
+            h8_t pf[4];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = __builtin_amdgcn_exp2f(s[kt][r] - m_use);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], scale_log2, -mc));
                     lsum += p;
                     pf[kt * 2 + (r >> 3)][r & 7] = (_Float16)p;
                 }
             l_run = l_run * alpha + lsum;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-            for (int i = 0; i < D / 32; ++i)
+                for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            }
             // ---- O^T += V^T P^T : 4 k-steps of 16 keys
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int kq = 0; kq < 4; ++kq) {
+                h8_t vf[D / 32];
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    h8 vf = *reinterpret_cast<const h8*>(Vt + (dt * 32 + lq) * AT_VPITCH + ks * 16 + 8 * g);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], oacc[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < D / 32; ++dt)
+                    vf[dt] = *reinterpret_cast<const h8_t*>(vt + at_voff(dt * 32 + lq, 2 * kq + g));
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt], pf[kq], oacc[dt], 0, 0, 0);
             }
         }
+        if (more) store_v(buf ^ 1);
+        // advance the compute cursor
+        ckt += AT_KT;
+        if (ckt >= tp.T || (causal && tp.t_lo + ckt > tile_qmax)) {
+            ckt = 0;
+            ++ct;
+        }
+        sync_step();
     }
-    // ---- finalize: O = acc / l ; lane holds O^T[d = 32*dt + 8j + 4g + r][query lq]
+    // ---- finalize: O = acc / l ; lane holds O^T[d = 32 dt + 8 j + 4 g + r][query lq]
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.0f / l_tot;
     if (qrow < sg.S) {
@@ -189,7 +285,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnTile* __restri
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                int d = dt * 32 + 8 * j + 4 * g;
+                const int d = dt * 32 + 8 * j + 4 * g;
                 uint2 w;
                 w.x = pack_bf16x2(oacc[dt][4 * j + 0] * inv, oacc[dt][4 * j + 1] * inv);
                 w.y = pack_bf16x2(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
@@ -203,9 +299,11 @@ hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles
                             int32_t causal, hipStream_t stream) {
     const uint8_t* t = (const uint8_t*)table;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(attention_kernel, dim3(ntiles), dim3(256), 0, stream, (const AttnTile*)(t + tiles_off), ntiles,
-                       (const AttnSeg*)(t + segs_off), (const AttnTuple*)(t + tuples_off), (const uint16_t*)Q,
-                       (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)O, scale_log2, causal);
+    const unsigned lds = 2u * AT_STAGE * sizeof(uint16_t);
+    hipLaunchKernelGGL(attention_kernel, dim3(ntiles), dim3(AT_THREADS), lds, stream,
+                       (const AttnTile*)(t + tiles_off), ntiles, (const AttnSeg*)(t + segs_off),
+                       (const AttnTuple*)(t + tuples_off), (const uint16_t*)Q, (const uint16_t*)K,
+                       (const uint16_t*)V, (uint16_t*)O, scale_log2, causal);
     return hipGetLastError();
 }
 

@@ -133,6 +133,7 @@ static ja_status parse_params(const char* params, ja_spec* s) {
             double x = std::strtod(v.c_str(), &e);
             if (!e || *e || v.empty() || !std::isfinite(x)) return fail(JA_ERR_SPEC, "bad number for " + k);
             if (k == "scale") {
+                if (!(x > 0)) return fail(JA_ERR_SPEC, "scale must be > 0");
                 s->scale = x;
                 s->has_scale = true;
             } else {
