@@ -10,9 +10,49 @@ namespace ja {
 
 // ---------------------------------------------------------------- repartition
 // One workgroup per copy task (at most REP_CHUNK elements).  Each thread
-// first loads all of its 16-byte vectors, then stores them.
+// issues all of its loads before its first store (lanes past the task's end
+// copy the task's first vector, which the planner has checked to be in
+// bounds, onto itself), so a pass keeps REP_MAXV loads in flight per
+// thread.  A task whose outer loops are trivial is a plain rows x vectors
+// copy and needs no index division; a power-of-two row length needs none at
+// all.
 constexpr int REP_THREADS = 256;
 constexpr int REP_MAXV = 8;  // vectors per thread per pass
+
+template <bool FLAT, bool POW2>
+__device__ __forceinline__ void rep_vec_pass(const RepTask& t, const uint8_t* __restrict__ src,
+                                             uint8_t* __restrict__ dst, int32_t esize, uint32_t vpe, uint32_t vpr,
+                                             uint32_t lg, uint32_t total, uint32_t base) {
+    const uint32_t n1 = t.n[1], n2 = t.n[2];
+    uint4 v[REP_MAXV];
+    int64_t doff[REP_MAXV];
+#pragma unroll
+    for (int j = 0; j < REP_MAXV; ++j) {
+        const uint32_t i = base + threadIdx.x + j * REP_THREADS;
+        const uint32_t ii = i < total ? i : 0u;
+        const uint32_t r = POW2 ? ii >> lg : ii / vpr;
+        const uint32_t c = ii - r * vpr;
+        int64_t so, dof;
+        if (FLAT) {
+            so = t.src_off + (int64_t)r * t.ss[2] + (int64_t)c * vpe;
+            dof = t.dst_off + (int64_t)r * t.ds[2] + (int64_t)c * vpe;
+        } else {
+            const uint32_t i2 = r % n2, r1 = r / n2;
+            const uint32_t i1 = r1 % n1, i0 = r1 / n1;
+            so = t.src_off + i0 * t.ss[0] + i1 * t.ss[1] + i2 * t.ss[2] + (int64_t)c * vpe;
+            dof = t.dst_off + i0 * t.ds[0] + i1 * t.ds[1] + i2 * t.ds[2] + (int64_t)c * vpe;
+        }
+        // issued as asm so the compiler cannot sink each load to its store
+        // and wait for it there; one explicit wait covers them all
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v[j]) : "v"(src + so * esize) : "memory");
+        doff[j] = dof;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // stores are unconditional (a lane past the end rewrites the task's first
+    // vector with the bytes lane 0 writes there)
+#pragma unroll
+    for (int j = 0; j < REP_MAXV; ++j) *reinterpret_cast<uint4*>(dst + doff[j] * esize) = v[j];
+}
 
 __global__ __launch_bounds__(REP_THREADS) void repart_kernel(const RepTask* __restrict__ tasks,
                                                              const uint8_t* __restrict__ src,
@@ -24,25 +64,16 @@ __global__ __launch_bounds__(REP_THREADS) void repart_kernel(const RepTask* __re
         const uint32_t vpe = 16 / esize;  // elements per vector
         const uint32_t vpr = n3 / vpe;    // vectors per row
         const uint32_t total = rows * vpr;
+        const bool flat = t.n[0] == 1 && n1 == 1;
+        const bool pow2 = (vpr & (vpr - 1)) == 0;
+        const uint32_t lg = __builtin_ctz(vpr);
         for (uint32_t base = 0; base < total; base += REP_THREADS * REP_MAXV) {
-            uint4 v[REP_MAXV];
-            int64_t doff[REP_MAXV];
-#pragma unroll
-            for (int j = 0; j < REP_MAXV; ++j) {
-                uint32_t i = base + threadIdx.x + j * REP_THREADS;
-                doff[j] = -1;
-                if (i < total) {
-                    uint32_t r = i / vpr, c = i - r * vpr;
-                    uint32_t i2 = r % n2, r1 = r / n2;
-                    uint32_t i1 = r1 % n1, i0 = r1 / n1;
-                    int64_t so = t.src_off + i0 * t.ss[0] + i1 * t.ss[1] + i2 * t.ss[2] + (int64_t)c * vpe;
-                    doff[j] = t.dst_off + i0 * t.ds[0] + i1 * t.ds[1] + i2 * t.ds[2] + (int64_t)c * vpe;
-                    v[j] = *reinterpret_cast<const uint4*>(src + so * esize);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < REP_MAXV; ++j)
-                if (doff[j] >= 0) *reinterpret_cast<uint4*>(dst + doff[j] * esize) = v[j];
+            if (flat && pow2)
+                rep_vec_pass<true, true>(t, src, dst, esize, vpe, vpr, lg, total, base);
+            else if (flat)
+                rep_vec_pass<true, false>(t, src, dst, esize, vpe, vpr, lg, total, base);
+            else
+                rep_vec_pass<false, false>(t, src, dst, esize, vpe, vpr, lg, total, base);
         }
     } else {
         const uint32_t total = rows * n3;
@@ -216,11 +247,94 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t*
     }
 }
 
+// The same join with the whole row held in registers: one wavefront per
+// row, lane l holding the 16-byte vectors at columns 512 k + 8 l.  Used when
+// every column block is W wide with W a multiple of 512, so each vector lies
+// in one block and its block index k * 512 / W is uniform; all NV loads of a
+// row are in flight together, then one wavefront reduction, then the stores.
+template <int NV>
+__global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_rows_kernel(const int64_t* __restrict__ rsplit,
+                                                                       int32_t nrb,
+                                                                       const NormBlock* __restrict__ blocks,
+                                                                       int32_t ndb, int64_t rows, int32_t W,
+                                                                       const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ gain,
+                                                                       uint16_t* __restrict__ y, float eps) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * NORM_WAVES + wave;
+    if (r >= rows) return;
+    int rb = 0;
+    while (rb + 1 < nrb && rsplit[rb + 1] <= r) ++rb;
+    const int64_t rr = r - rsplit[rb];
+    const NormBlock* bl = blocks + (int64_t)rb * ndb;
+    uint4 v[NV];
+    int64_t off[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int db = (k * 512) / W;
+        off[k] = bl[db].off + rr * W + (k * 512 - db * W) + lane * 8;
+        v[k] = *reinterpret_cast<const uint4*>(x + off[k]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a0 = bf16lo_to_f32(w[q]), a1 = bf16hi_to_f32(w[q]);
+            ss += a0 * a0 + a1 * a1;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = rsqrtf(ss / (float)(NV * 512) + eps);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const uint4 g = *reinterpret_cast<const uint4*>(gain + k * 512 + lane * 8);
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w}, gw[4] = {g.x, g.y, g.z, g.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = pack_bf16x2(bf16lo_to_f32(w[q]) * inv * bf16lo_to_f32(gw[q]),
+                               bf16hi_to_f32(w[q]) * inv * bf16hi_to_f32(gw[q]));
+        *reinterpret_cast<uint4*>(y + off[k]) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// vec: 0 scalar pieces, 1 16-byte pieces (both staged through LDS), 2 rows
+// held in registers (D a multiple of 512 up to 8192, every block W wide with
+// W a multiple of 512; the planner checks this)
 hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
-                          int64_t rows, int32_t D, const void* x, const void* gain, void* y, float eps, int32_t vec,
-                          hipStream_t stream) {
+                          int64_t rows, int32_t D, int32_t W, const void* x, const void* gain, void* y, float eps,
+                          int32_t vec, hipStream_t stream) {
     const uint8_t* t = (const uint8_t*)table;
     int64_t grid = (rows + NORM_WAVES - 1) / NORM_WAVES;
+    if (vec == 2) {
+        const int nv = D / 512;
+#define JA_ROWS_CASE(N)                                                                                           \
+    case N:                                                                                                       \
+        hipLaunchKernelGGL(rmsnorm_rows_kernel<N>, dim3((unsigned)grid), dim3(NORM_WAVES * 64), 0, stream,        \
+                           (const int64_t*)(t + rsplit_off), nrb, (const NormBlock*)(t + blocks_off), ndb, rows, W, \
+                           (const uint16_t*)x, (const uint16_t*)gain, (uint16_t*)y, eps);                        \
+        break;
+        switch (nv) {
+            JA_ROWS_CASE(1)
+            JA_ROWS_CASE(2)
+            JA_ROWS_CASE(3)
+            JA_ROWS_CASE(4)
+            JA_ROWS_CASE(5)
+            JA_ROWS_CASE(6)
+            JA_ROWS_CASE(7)
+            JA_ROWS_CASE(8)
+            JA_ROWS_CASE(10)
+            JA_ROWS_CASE(12)
+            JA_ROWS_CASE(14)
+            JA_ROWS_CASE(16)
+            default: return hipErrorInvalidValue;
+        }
+#undef JA_ROWS_CASE
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)grid), dim3(NORM_WAVES * 64),
                        (unsigned)((size_t)NORM_WAVES * D * 2), stream, (const int64_t*)(t + rsplit_off), nrb,
                        (const NormBlock*)(t + blocks_off), ndb, rows, D, (const uint16_t*)x, (const uint16_t*)gain,

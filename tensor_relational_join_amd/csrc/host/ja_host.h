@@ -97,7 +97,7 @@ hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles
                             int64_t tuples_off, const void* Q, const void* K, const void* V, void* O,
                             float scale, int32_t causal, hipStream_t stream);
 hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
-                          int64_t rows, int32_t D, const void* x, const void* gain, void* y, float eps,
+                          int64_t rows, int32_t D, int32_t W, const void* x, const void* gain, void* y, float eps,
                           int32_t vec, hipStream_t stream);
 hipError_t launch_swiglu(const void* g, const void* u, void* h, int64_t n, hipStream_t stream);
 hipError_t launch_add(const void* a, const void* b, void* c, int64_t n, hipStream_t stream);

@@ -37,7 +37,7 @@ struct ja_plan {
     int32_t causal = 0;
     // rmsnorm
     int64_t rsplit_off = 0, nblk_off = 0;
-    int32_t nrb = 0, ndb = 0, D = 0, norm_vec = 0;
+    int32_t nrb = 0, ndb = 0, D = 0, norm_vec = 0, norm_w = 0;
     int64_t rows = 0;
     float eps = 0.f;
     // 1:1 joins
@@ -358,6 +358,17 @@ ja_status plan_rmsnorm(ja_plan* p, const ja_spec* s, const ja_decomp* d, const j
             blk.push_back(b);
         }
     p->norm_vec = vec ? 1 : 0;
+    // rows in registers: equal block widths that are multiples of 512, and a
+    // row length the register kernel is instantiated for
+    const int64_t W = X.ext(1, 0);
+    bool rows_ok = vec && W % 512 == 0 && D % 512 == 0;
+    for (int db = 0; db < p->ndb; ++db) rows_ok = rows_ok && X.ext(1, db) == W;
+    const int64_t nv = D / 512;
+    rows_ok = rows_ok && (nv <= 8 || nv == 10 || nv == 12 || nv == 14 || nv == 16);
+    if (rows_ok) {
+        p->norm_vec = 2;
+        p->norm_w = (int32_t)W;
+    }
     p->rsplit_off = put(p->table, rsp);
     p->nblk_off = put(p->table, blk);
     return JA_OK;
@@ -461,8 +472,8 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
                                         in_ptrs[1], in_ptrs[2], out_ptr, p->scale, p->causal, hs));
             break;
         case JA_OP_RMSNORM:
-            JA_TRY_HIP(launch_rmsnorm(p->dev, p->rsplit_off, p->nrb, p->nblk_off, p->ndb, p->rows, p->D, in_ptrs[0],
-                                      in_ptrs[1], out_ptr, p->eps, p->norm_vec, hs));
+            JA_TRY_HIP(launch_rmsnorm(p->dev, p->rsplit_off, p->nrb, p->nblk_off, p->ndb, p->rows, p->D, p->norm_w,
+                                      in_ptrs[0], in_ptrs[1], out_ptr, p->eps, p->norm_vec, hs));
             break;
         case JA_OP_SWIGLU: JA_TRY_HIP(launch_swiglu(in_ptrs[0], in_ptrs[1], out_ptr, p->n, hs)); break;
         case JA_OP_ADD: JA_TRY_HIP(launch_add(in_ptrs[0], in_ptrs[1], out_ptr, p->n, hs)); break;

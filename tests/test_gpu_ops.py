@@ -258,6 +258,10 @@ def test_attention_full_size_sampled_rows(dev, orc):
     (64, 512, [0, 64], _eq(512, 4)),
     (70, 200, [0, 5, 70], [0, 7, 100, 200]),      # unaligned widths: element path
     (8192, 4096, [0, 8192], _eq(4096, 8)),         # x [8192, 4096], d split into 8 blocks
+    # rows held in registers: several row blocks, 6 and 2 vectors per lane
+    (300, 2048, [0, 100, 300], _eq(2048, 2)),
+    (10, 3072, [0, 3, 10], _eq(3072, 3)),
+    (5, 1024, [0, 5], [0, 1024]),
 ])
 def test_rmsnorm(dev, orc, R, D, rsp, dsp):
     x = synth.normal_bf16(4, 0, (R, D))
