@@ -15,7 +15,7 @@ the dominant kernel (the bf16 MFMA contraction), timed with HIP events on
 the stream the steps run on.  `cpu_baseline` times the CPU oracle on a
 bounded token sample of the same block.
 
-    python bench.py [--steps K] [--warmup W] [--workload block|ffn|attention|norm_swiglu|copy]
+    python bench.py [--steps K] [--warmup W] [--workload block|configs|ffn|attention|norm_swiglu|copy]
 
 The non-block workloads print per-operator diagnostics (and `copy` the HBM
 copy ceiling); only `block` prints the contract line.
@@ -181,9 +181,11 @@ def bench_block(args):
 
 def bench_kernel(args):
     """Single-operator workloads at the configs' sizes (diagnostics and
-    profiling): ffn = bd,df->bf 2048x4096x11008 (2x4x4); attention =
-    [4,32,2048,128] causal, 128-blocks; norm_swiglu = RMSNorm [8192,4096]
-    (d by 8) + SwiGLU [8192,11008] (f by 8)."""
+    profiling): tiny = ij,jk->ik 64^3 fp32 (2x2x2); ffn = bd,df->bf
+    2048x4096x11008 (2x4x4), fused and unfused (ja_kernel then ja_agg);
+    attention = [4,32,2048,128] causal, 128-blocks; norm_swiglu = RMSNorm
+    [8192,4096] (d by 8) + SwiGLU [8192,11008] (f by 8); configs = all of
+    them.  Inputs are seeded torch draws with the configs' distributions."""
     import torch
 
     from tensor_relational_join_amd import synth
@@ -208,57 +210,82 @@ def bench_kernel(args):
         gbs = 2.0 * n * 2 / (ms / 1e3) / 1e9
         return {"workload": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "steps": args.steps,
                 "ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
-    runs = []
-    if args.workload == "ffn":
+    runs = []  # (name, launch, flops, bytes, ops to close)
+    want = ["tiny", "ffn", "ffn_unfused", "attention", "rmsnorm", "swiglu"] if args.workload == "configs" else \
+        {"ffn": ["ffn"], "attention": ["attention"], "norm_swiglu": ["rmsnorm", "swiglu"]}[args.workload]
+
+    def tensors(op, seed, stds):
+        torch.manual_seed(seed)
+        ins = [alloc(r) for r in op.in_rels]
+        for t, (mean, std) in zip(ins, stds):
+            t.normal_(mean, std)
+        return ins, alloc(op.out_rel)
+
+    from tensor_relational_join_amd.binding import JA_F32
+
+    if "tiny" in want:  # ij,jk->ik 64^3 fp32 U[-1, 1], every letter split in 2: 8 tuples, 4 segments
+        sp = {c: _eq(64, 2) for c in "ijk"}
+        op = Op("ij,jk->ik", "contract", sp, in_dtypes=[JA_F32, JA_F32], out_dtype=JA_F32)
+        torch.manual_seed(1)
+        ins = [alloc(r).uniform_(-1, 1) for r in op.in_rels]
+        out = alloc(op.out_rel)
+        runs.append(("tiny_fp32_2x2x2", lambda op=op, ins=ins, out=out: op.run(ins, out), 2.0 * 64 ** 3,
+                     4.0 * 3 * 64 * 64, [op]))
+    if "ffn" in want or "ffn_unfused" in want:  # bd,df->bf 2048x4096x11008, b by 2, d by 4, f by 4
         sp = {"b": _eq(2048, 2), "d": _eq(4096, 4), "f": _eq(11008, 4)}
         op = Op("bd,df->bf", "contract", sp)
-        ins = [alloc(r) for r in op.in_rels]
-        for t in ins:
-            t.normal_()
-        out = alloc(op.out_rel)
-        runs.append(("ffn_contract", op, ins, out, 2.0 * 2048 * 4096 * 11008, None))
-    elif args.workload == "attention":
+        ins, out = tensors(op, 2, [(0.0, 1.0), (0.0, 0.02)])
+        fl = 2.0 * 2048 * 4096 * 11008
+        by = 2.0 * (2048 * 4096 + 4096 * 11008 + 2048 * 11008)
+        if "ffn" in want:  # the op is closed after its last use
+            runs.append(("ffn_contract", lambda op=op, ins=ins, out=out: op.run(ins, out), fl, by,
+                         [] if "ffn_unfused" in want else [op]))
+        if "ffn_unfused" in want:
+            part = op.partial_buffer()
+
+            def unfused(op=op, ins=ins, out=out, part=part):
+                op.kernel(ins, part)
+                op.agg(part, out)
+            # the unfused path also writes and reads every fp32 partial (32 blocks of 1024 x 2752)
+            runs.append(("ffn_unfused_kernel_then_agg", unfused, fl, by + 2 * 4.0 * part.numel(), [op]))
+    if "attention" in want:  # [4, 32, 2048, 128] causal, 128-blocks: 17,408 tuples
         sp = {"b": _eq(4, 4), "h": _eq(32, 32), "s": _eq(2048, 16), "t": _eq(2048, 16), "d": [0, 128]}
         op = Op("bhsd,bhtd,bhtd->bhsd", "attention", sp, "causal=s,t")
-        ins = [alloc(r) for r in op.in_rels]
-        for t in ins:
-            t.normal_()
-        out = alloc(op.out_rel)
-        runs.append(("attention", op, ins, out, 2 * 2.0 * 128 * 128 * 128 * 136 * 128, None))
-    else:
+        ins, out = tensors(op, 3, [(0.0, 1.0)] * 3)
+        runs.append(("attention", lambda op=op, ins=ins, out=out: op.run(ins, out),
+                     2 * 2.0 * 128 * 128 * 128 * 136 * 128, 2.0 * 4 * 4 * 32 * 2048 * 128, [op]))
+    if "rmsnorm" in want:  # x [8192, 4096], d by 8, eps 1e-6, gain N(1, 0.1)
         op = Op("rd,d->rd", "rmsnorm", {"r": [0, 8192], "d": _eq(4096, 8)}, "eps=1e-6")
-        ins = [alloc(r) for r in op.in_rels]
-        ins[0].normal_()
-        ins[1].fill_(1.0)
-        out = alloc(op.out_rel)
-        runs.append(("rmsnorm", op, ins, out, None, 2.0 * (2 * 8192 * 4096 + 4096)))
-        op2 = Op("rf,rf->rf", "swiglu", {"r": [0, 8192], "f": _eq(11008, 8)})
-        ins2 = [alloc(r) for r in op2.in_rels]
-        for t in ins2:
-            t.normal_()
-        out2 = alloc(op2.out_rel)
-        runs.append(("swiglu", op2, ins2, out2, None, 2.0 * 3 * 8192 * 11008))
+        ins, out = tensors(op, 4, [(0.0, 1.0), (1.0, 0.1)])
+        runs.append(("rmsnorm", lambda op=op, ins=ins, out=out: op.run(ins, out), None,
+                     2.0 * (2 * 8192 * 4096 + 4096), [op]))
+    if "swiglu" in want:  # g, u [8192, 11008], f by 8, 1:1 join
+        op = Op("rf,rf->rf", "swiglu", {"r": [0, 8192], "f": _eq(11008, 8)})
+        ins, out = tensors(op, 4, [(0.0, 1.0)] * 2)
+        runs.append(("swiglu", lambda op=op, ins=ins, out=out: op.run(ins, out), None, 2.0 * 3 * 8192 * 11008,
+                     [op]))
     res = {}
-    for name, op, ins, out, fl, by in runs:
+    for name, launch, fl, by, ops in runs:
         for _ in range(args.warmup):
-            op.run(ins, out)
+            launch()
         torch.cuda.synchronize()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record()
         for _ in range(args.steps):
-            op.run(ins, out)
+            launch()
         s1.record()
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / args.steps
         d = {"ms": round(ms, 4)}
         if fl:
-            d["tflops"] = round(fl / (ms / 1e3) / 1e12, 1)
+            d["tflops"] = round(fl / (ms / 1e3) / 1e12, 2)
             d["frac_mfma_peak"] = round(d["tflops"] / PEAK_BF16_TFLOPS, 3)
         if by:
             d["gbs"] = round(by / (ms / 1e3) / 1e9, 1)
             d["frac_hbm_peak"] = round(d["gbs"] / PEAK_HBM_GBS, 3)
         res[name] = d
-        op.close()
+        for op in ops:
+            op.close()
     return {"workload": args.workload, "steps": args.steps, "warmup": args.warmup, "results": res}
 
 
@@ -267,7 +294,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="block", choices=["block", "ffn", "attention", "norm_swiglu", "copy"])
+    ap.add_argument("--workload", default="block", choices=["block", "configs", "ffn", "attention", "norm_swiglu", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

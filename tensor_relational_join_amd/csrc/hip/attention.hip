@@ -215,7 +215,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
             }
             // ---- masks: only where the step crosses the diagonal or the key block's end
             const bool ragged = ckt + AT_KT > tp.T;
-            if (ragged || (causal && key0 + AT_KT - 1 > wave_qmin)) {
+            if (ragged) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -225,36 +225,56 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                         const bool ok = ckt + kk < tp.T && (!causal || key0 + kk <= qglob);
                         s[kt][r] = ok ? s[kt][r] : -INFINITY;
                     }
+            } else if (causal && key0 + AT_KT - 1 > wave_qmin) {
+                const int lim = qglob - key0 - 4 * g;  // key kk visible iff kk - 4 g <= lim
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        s[kt][r] = kt * 32 + 8 * (r >> 2) + (r & 3) <= lim ? s[kt][r] : -INFINITY;
             }
-            // ---- online softmax for query lq (this lane holds 32 of the 64 keys);
-            // the maximum is taken on raw scores, which the positive scale preserves
+            // ---- online softmax for query lq (this lane holds 32 of the 64 keys).
+            // The maximum is taken on raw scores, which the positive scale
+            // preserves.  The reference maximum m_run only moves when a new
+            // score exceeds it by more than 2^8 after scaling, so P stays in
+            // (0, 256] (exact in the fp16 range) and O and l are rescaled
+            // rarely; the result O = acc / l does not depend on the reference.
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);
-            const float mc = m_new == -INFINITY ? 0.f : m_new * scale_log2;
-            const float alpha = __builtin_amdgcn_exp2f(m_run * scale_log2 - mc);
-            m_run = m_new;
-            float lsum = 0.f;
-            h8_t pf[4];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], scale_log2, -mc));
-                    lsum += p;
-                    pf[kt * 2 + (r >> 3)][r & 7] = (_Float16)p;
-                }
-            l_run = l_run * alpha + lsum;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+            const bool move = mx * scale_log2 > m_run * scale_log2 + 8.0f || (m_run == -INFINITY && mx != -INFINITY);
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                const float m_new = move ? mx : m_run;
+                const float alpha = move ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.0f;
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
             }
+            const float mc = m_run == -INFINITY ? 0.f : m_run * scale_log2;
+            // P in fp16, two scores per conversion; the row sum is taken over
+            // the rounded values the MFMA consumes (fp16 pairs dotted with 1)
+            typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+            h8_t pf[4];
+            float lsum = 0.f;
+            const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], scale_log2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r + 1], scale_log2, -mc));
+                    const h2_t ph = {(_Float16)p0, (_Float16)p1};  // round to nearest even
+                    lsum = __builtin_amdgcn_fdot2(ph, one2, lsum, false);
+                    pf[kt * 2 + (r >> 3)][r & 7] = ph[0];
+                    pf[kt * 2 + (r >> 3)][(r & 7) + 1] = ph[1];
+                }
+            l_run += lsum;
             // ---- O^T += V^T P^T : 4 k-steps of 16 keys
 #pragma unroll
             for (int kq = 0; kq < 4; ++kq) {
