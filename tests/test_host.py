@@ -128,6 +128,9 @@ def test_relation_layout_matches_oracle(B, orc):
     ("rd,d->rd", "rmsnorm", "eps=-1", "JA_ERR_SPEC"),
     ("rd,d->rd", "rmsnorm", "bogus=1", "JA_ERR_SPEC"),
     ("ij,jk->ik", "contract", "causal=i,k", "JA_ERR_SPEC"),
+    # the attention kernel takes the running maximum on raw scores: the scale must be positive
+    ("bhsd,bhtd,bhtd->bhsd", "attention", "scale=0", "JA_ERR_SPEC"),
+    ("bhsd,bhtd,bhtd->bhsd", "attention", "scale=-0.5;causal=s,t", "JA_ERR_SPEC"),
 ])
 def test_spec_errors(B, einsum, op, params, code):
     with pytest.raises(B.JaError) as e:
