@@ -374,3 +374,109 @@ def test_repartition_unit_dimensions(dev, orc):
                  [_eq(3, 3), [0, 1], _eq(2, 2), _eq(256, 2), [0, 128]], vshape=(1, 256, 3, 2, 128),
                  perm=(2, 0, 3, 1, 4), seed=8)
     _repart_case(dev, orc, (1, 1), [[0, 1], [0, 1]], (1,), [[0, 1]], vshape=(1,), perm=(0,), dtype="f32", seed=9)
+
+
+# ------------------------------------------------------------------ one-shot entry points
+
+def _one_shot(dev, orc, einsum, op, splits, dense_inputs, params="", in_dtypes=None, out_dtype=None):
+    """Run an operator through ja_einsum (plan, upload and run in one call, with
+    a caller-owned workspace of the queried size) and unpack its output."""
+    import torch
+
+    from tensor_relational_join_amd import binding as B
+
+    lhs, out = einsum.split("->")
+    ins = lhs.split(",")
+    in_dtypes = in_dtypes or [B.JA_BF16] * len(ins)
+    out_dtype = B.JA_BF16 if out_dtype is None else out_dtype
+    spec = B.ja_spec_create(einsum, op, params)
+    decomp = None
+    try:
+        letters = B.ja_spec_letters(spec)
+        decomp = B.ja_decomp_create(spec, [splits[c][-1] for c in letters], [len(splits[c]) - 1 for c in letters],
+                                    [list(splits[c]) for c in letters])
+        in_rels = [dev.relation_for(s, splits, dt) for s, dt in zip(ins, in_dtypes)]
+        out_rel = dev.relation_for(out, splits, out_dtype)
+        dev_ins = []
+        for s, x, dt in zip(ins, dense_inputs, in_dtypes):
+            flat = orc.Relation([splits[c][-1] for c in s], [splits[c] for c in s]).pack(x)
+            dev_ins.append(to_dev_bf16(flat) if dt == B.JA_BF16 else to_dev_f32(flat))
+        out_t = dev.alloc(out_rel)
+        need = B.ja_einsum_workspace_bytes(spec, decomp, in_rels, out_rel)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        B.ja_einsum(spec, decomp, in_rels, [t.data_ptr() for t in dev_ins], out_rel, out_t.data_ptr(),
+                    ws.data_ptr(), need)
+        torch.cuda.synchronize()
+        orel = orc.Relation([splits[c][-1] for c in out], [splits[c] for c in out])
+        host = bf16_bits(out_t) if out_dtype == B.JA_BF16 else f32_host(out_t)
+        res = orel.unpack(host)
+        if out_dtype == B.JA_BF16:
+            res = orc.bf16_to_f64(res)
+        return res.astype(np.float64), dev_ins
+    finally:
+        if decomp is not None:
+            B.ja_decomp_destroy(decomp)
+        B.ja_spec_destroy(spec)
+
+
+def test_one_shot_einsum_fp32(dev, orc):
+    from tensor_relational_join_amd.binding import JA_F32
+
+    A = synth.uniform(21, 0, (64, 64))
+    Bm = synth.uniform(21, 1, (64, 64))
+    sp = {c: _eq(64, 2) for c in "ijk"}
+    got, _ = _one_shot(dev, orc, "ij,jk->ik", "contract", sp, [A, Bm], in_dtypes=[JA_F32, JA_F32],
+                       out_dtype=JA_F32)
+    assert rel_inf(got, orc.einsum("ij,jk->ik", A, Bm)) <= FP32_TOL
+
+
+def test_one_shot_einsum_bf16_matches_plan_path(dev, orc):
+    """The one-shot call and the plan API run the same kernels on the same
+    tuple list, so their outputs agree bit for bit; both meet the oracle bar."""
+    sp = {"i": [0, 144, 300], "j": [0, 104, 520], "k": [0, 128, 256, 328]}
+    X = synth.normal_bf16(22, 0, (300, 520))
+    W = synth.normal_bf16(22, 1, (520, 328), std=0.02)
+    got, _ = _one_shot(dev, orc, "ij,jk->ik", "contract", sp, [X, W])
+    want = orc.round_bf16(orc.einsum("ij,jk->ik", orc.bf16_to_f64(X), orc.bf16_to_f64(W)))
+    assert rel_frobenius(got, want) <= BF16_TOL
+    got2, o, _ = _run(dev, orc, "ij,jk->ik", "contract", sp, [X, W])
+    o.close()
+    assert np.array_equal(got, got2)
+
+
+def test_one_shot_attention(dev, orc):
+    Bn, H, S = 1, 2, 384
+    sp = {"b": [0, 1], "h": _eq(H, H), "s": _eq(S, 3), "t": _eq(S, 2), "d": [0, 128]}
+    Q = synth.normal_bf16(23, 0, (Bn, H, S, 128))
+    K = synth.normal_bf16(23, 1, (Bn, H, S, 128))
+    V = synth.normal_bf16(23, 2, (Bn, H, S, 128))
+    got, _ = _one_shot(dev, orc, "bhsd,bhtd,bhtd->bhsd", "attention", sp, [Q, K, V], params="causal=s,t")
+    want = orc.round_bf16(orc.attention(orc.bf16_to_f64(Q), orc.bf16_to_f64(K), orc.bf16_to_f64(V),
+                                        1.0 / np.sqrt(128.0), True))
+    assert rel_frobenius(got, want) <= BF16_TOL
+
+
+def test_one_shot_repartition(dev, orc):
+    """ja_repartition (tables built, uploaded and run in one call) gives the
+    same bytes as the oracle's repartition, with and without a view."""
+    import torch
+
+    from tensor_relational_join_amd import binding as B
+
+    cases = [((256, 256), [[0, 128, 256], [0, 256]], (256, 256), [[0, 64, 128, 192, 256], [0, 256]], None, None),
+             ((24, 40), [[0, 10, 24], [0, 16, 40]], (40, 24), [[0, 8, 40], [0, 24]], (24, 40), (1, 0))]
+    for n, (ss, ssp, ds, dsp, vshape, perm) in enumerate(cases):
+        s_rel = B.Relation(ss, splits=ssp, dtype=B.JA_BF16)
+        d_rel = B.Relation(ds, splits=dsp, dtype=B.JA_BF16)
+        view = B.make_view(vshape, perm) if vshape is not None else None
+        dense = np.random.default_rng(40 + n).integers(0, 65536, size=ss, dtype=np.uint32).astype(np.uint16)
+        os_rel, od_rel = orc.Relation(ss, ssp), orc.Relation(ds, dsp)
+        flat = os_rel.pack(dense)
+        src_t = torch.from_numpy(flat.view(np.int16)).cuda()
+        dst_t = torch.zeros(int(np.prod(ds)), dtype=torch.int16, device="cuda")
+        need = B.ja_repartition_workspace_bytes(s_rel, d_rel, view)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        B.ja_repartition(s_rel, src_t.data_ptr(), d_rel, dst_t.data_ptr(), view, ws.data_ptr(), need)
+        torch.cuda.synchronize()
+        got = dst_t.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, orc.repartition(os_rel, flat, od_rel, vshape, perm))

@@ -260,3 +260,30 @@ def test_repartition_views_with_unit_dimensions(B):
                             B.make_view((1,), (0,)))
     assert B.ja_repart_count(rp) == (1, 1)
     B.ja_repart_destroy(rp)
+
+
+def test_one_shot_entry_points_refuse_a_small_workspace(B):
+    """ja_einsum and ja_repartition check the caller's workspace against the
+    size query before any HIP call, so an undersized (or absent) workspace is
+    refused on the host."""
+    s = B.ja_spec_create("ij,jk->ik", "contract")
+    d = B.ja_decomp_create(s, [64, 64, 64], [2, 2, 2])
+    try:
+        ins = [B.Relation((64, 64), nblk=(2, 2), dtype=B.JA_F32)] * 2
+        out = B.Relation((64, 64), nblk=(2, 2), dtype=B.JA_F32)
+        need = B.ja_einsum_workspace_bytes(s, d, ins, out)
+        assert need > 0 and need % 256 == 0
+        for ws, nbytes in ((0, need), (1 << 20, need - 1)):
+            with pytest.raises(B.JaError) as e:
+                B.ja_einsum(s, d, ins, [16, 16], out, 16, ws, nbytes)
+            assert e.value.name == "JA_ERR_WORKSPACE"
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
+    src = B.Relation((256, 256), splits=[[0, 128, 256], [0, 256]], dtype=B.JA_BF16)
+    dst = B.Relation((256, 256), splits=[[0, 64, 128, 192, 256], [0, 256]], dtype=B.JA_BF16)
+    need = B.ja_repartition_workspace_bytes(src, dst)
+    assert need > 0
+    with pytest.raises(B.JaError) as e:
+        B.ja_repartition(src, 16, dst, 16, None, 1 << 20, need - 1)
+    assert e.value.name == "JA_ERR_WORKSPACE"
