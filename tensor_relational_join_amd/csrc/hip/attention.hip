@@ -125,6 +125,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     }
     // V staging: keys 4 kg .. 4 kg + 3 of the step, d = 8 dj .. 8 dj + 7
     const int kg = tid >> 4, dj = tid & 15;
+    const int32_t vlane = ((kg * 4) * D + dj * 8) * 2;  // byte offset of this lane's first V row at key 0
     at_i32x4_t vr[4];
 
     // load cursor
@@ -135,18 +136,25 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
         const at_i32x4_t rs = at_rsrc(kb, (uint32_t)(tp.kv_bhstride * 2));
         const uint32_t st = lds0 + (uint32_t)(buf * AT_STAGE * 2);
         const uint32_t soff = (uint32_t)(lkt * D * 2);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // keys past the block read as zero: 0x80000000 stays past the
-            // descriptor's extent with or without the scalar offset added
-            const bool ok = lkt + kkey[j] < tp.T;
-            at_dma16(rs, st + (wave * 4 + j) * 1024, ok ? koffb[j] : 0x80000000u, soff);
-        }
         const at_i32x4_t rv = at_rsrc(V + tp.v_off + (int64_t)tl.bh * tp.kv_bhstride, (uint32_t)(tp.kv_bhstride * 2));
+        if (lkt + AT_KT <= tp.T) {  // every key of the step is in the block
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = lkt + kg * 4 + i;
-            vr[i] = at_buffer_load_x4(rv, key < tp.T ? (key * D + dj * 8) * 2 : (int32_t)0x80000000, 0, 0);
+            for (int j = 0; j < 4; ++j) at_dma16(rs, st + (wave * 4 + j) * 1024, koffb[j], soff);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vr[i] = at_buffer_load_x4(rv, vlane + i * D * 2, (int32_t)soff, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // keys past the block read as zero: 0x80000000 stays past the
+                // descriptor's extent with or without the scalar offset added
+                const bool ok = lkt + kkey[j] < tp.T;
+                at_dma16(rs, st + (wave * 4 + j) * 1024, ok ? koffb[j] : 0x80000000u, soff);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = lkt + kg * 4 + i;
+                vr[i] = at_buffer_load_x4(rv, key < tp.T ? (key * D + dj * 8) * 2 : (int32_t)0x80000000, 0, 0);
+            }
         }
         // advance the cursor to the next visible step
         lkt += AT_KT;
@@ -233,18 +241,23 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                     for (int r = 0; r < 16; ++r)
                         s[kt][r] = kt * 32 + 8 * (r >> 2) + (r & 3) <= lim ? s[kt][r] : -INFINITY;
             }
-            // ---- online softmax for query lq (this lane holds 32 of the 64 keys).
-            // The maximum is taken on raw scores, which the positive scale
-            // preserves.  The reference maximum m_run only moves when a new
-            // score exceeds it by more than 2^8 after scaling, so P stays in
-            // (0, 256] (exact in the fp16 range) and O and l are rescaled
-            // rarely; the result O = acc / l does not depend on the reference.
+            // ---- online softmax for query lq (this lane holds 32 of the 64
+            // keys, the lane 32 away the other 32).  The maximum is taken on
+            // raw scores, which the positive scale preserves.  The reference
+            // maximum m_run only moves when a new score exceeds it by more
+            // than 2^8 after scaling, so P stays in (0, 256] (exact in the
+            // fp16 range) and O and l are rescaled rarely; the result
+            // O = acc / l does not depend on the reference.
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            {
+                const auto sw =
+                    __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
             const bool move = mx * scale_log2 > m_run * scale_log2 + 8.0f || (m_run == -INFINITY && mx != -INFINITY);
             if (__builtin_amdgcn_ballot_w64(move) != 0) {
                 const float m_new = move ? mx : m_run;
@@ -297,7 +310,11 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
         sync_step();
     }
     // ---- finalize: O = acc / l ; lane holds O^T[d = 32 dt + 8 j + 4 g + r][query lq]
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    float l_tot;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     const float inv = 1.0f / l_tot;
     if (qrow < sg.S) {
         uint16_t* op = O + sg.o_off + (int64_t)tl.bh * sg.q_bhstride + (int64_t)qrow * D;
