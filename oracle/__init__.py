@@ -23,7 +23,9 @@ Einsummable", paperpeel full text):
   and the repartition itself -- ``overlay_atoms``, ``repartition``;
 * attention as a blocked join-agg with the online-softmax aggregation
   (m, l, acc) -- ``attention_online_blocked`` (the aggregation operator need
-  not be addition, section 5.2);
+  not be addition, section 5.2); both attention forms take fewer key-value
+  heads than query heads (grouped-query attention, section 3.3: query heads
+  g*R .. g*R+R-1 share key-value head g);
 * the LLaMA-shaped block as a chain of the above -- ``llama_block``.
 
 Readings where the pages are silent (listed again in the design notes):
@@ -77,7 +79,7 @@ def _load():
         lib.orc_einsum2_points.argtypes = [ctypes.c_char_p, _i64p, _f64p, _f64p, ctypes.c_int64, _i64p, _f64p]
         lib.orc_einsum2_points.restype = ctypes.c_int
         lib.orc_matmul.argtypes = [_f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
-        lib.orc_attention_rows.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int64] * 5 + [
+        lib.orc_attention_rows.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int64] * 6 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_int64, _i64p, _f64p]
         lib.orc_rmsnorm.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _f64p]
         lib.orc_swiglu.argtypes = [_f64p, _f64p, ctypes.c_int64, _f64p]
@@ -193,13 +195,18 @@ def matmul(A, B) -> np.ndarray:
 
 def attention_rows(Q, K, V, rows, scale: float, causal: bool) -> np.ndarray:
     """Attention output rows for the listed (b, h, s) query rows.
-    Q [B,H,S,D], K/V [B,H,T,D]; two-pass softmax in float64."""
+    Q [B,H,S,D], K/V [B,HK,T,D] with HK dividing H: query head h reads
+    key-value head h // (H // HK) (grouped-query attention when HK < H,
+    section 3.3; ordinary multi-head attention when HK = H).  Two-pass
+    softmax in float64."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     Bn, H, S, D = Q.shape
-    T = K.shape[2]
+    HK, T = K.shape[1], K.shape[2]
+    if K.shape != V.shape or K.shape[0] != Bn or K.shape[3] != D or H % HK:
+        raise ValueError("attention: K and V must be [B, HK, T, D] with HK dividing Q's H")
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
     out = np.empty((rows.shape[0], D), dtype=np.float64)
-    _load().orc_attention_rows(_ptr(Q, _f64p), _ptr(K, _f64p), _ptr(V, _f64p), Bn, H, S, T, D, float(scale),
+    _load().orc_attention_rows(_ptr(Q, _f64p), _ptr(K, _f64p), _ptr(V, _f64p), Bn, H, HK, S, T, D, float(scale),
                                1 if causal else 0, rows.shape[0], _ptr(rows, _i64p), _ptr(out, _f64p))
     return out
 
@@ -485,9 +492,11 @@ def attention_online_blocked(Q, K, V, s_splits, t_splits, scale: float, causal: 
     output block is acc / l.  `t_order` may permute the fold order."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     Bn, H, S, D = Q.shape
+    rep = H // K.shape[1]  # query heads per key-value head (grouped-query attention when > 1)
     out = np.zeros_like(Q)
     for b in range(Bn):
         for h in range(H):
+            kh = h // rep
             for si in range(len(s_splits) - 1):
                 s0, s1 = s_splits[si], s_splits[si + 1]
                 tis = [ti for ti in range(len(t_splits) - 1) if not (causal and t_splits[ti] >= s1)]
@@ -498,7 +507,7 @@ def attention_online_blocked(Q, K, V, s_splits, t_splits, scale: float, causal: 
                 acc = np.zeros((s1 - s0, D))
                 for ti in tis:
                     t0, t1 = t_splits[ti], t_splits[ti + 1]
-                    sc = scale * (Q[b, h, s0:s1] @ K[b, h, t0:t1].T)
+                    sc = scale * (Q[b, h, s0:s1] @ K[b, kh, t0:t1].T)
                     if causal:
                         qs = np.arange(s0, s1)[:, None]
                         ks = np.arange(t0, t1)[None, :]
@@ -506,7 +515,7 @@ def attention_online_blocked(Q, K, V, s_splits, t_splits, scale: float, causal: 
                     m2 = sc.max(axis=1)
                     p = np.where(np.isfinite(sc), np.exp(sc - np.where(np.isfinite(m2), m2, 0.0)[:, None]), 0.0)
                     l2 = p.sum(axis=1)
-                    acc2 = p @ V[b, h, t0:t1]
+                    acc2 = p @ V[b, kh, t0:t1]
                     mn = np.maximum(m, m2)
                     a1 = np.where(np.isfinite(m), np.exp(m - np.where(np.isfinite(mn), mn, 0.0)), 0.0)
                     a2 = np.where(np.isfinite(m2), np.exp(m2 - np.where(np.isfinite(mn), mn, 0.0)), 0.0)

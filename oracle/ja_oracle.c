@@ -202,14 +202,19 @@ void orc_matmul(const double* A, const double* B, double* C, int64_t M, int64_t 
 /* Scaled dot-product attention, textbook two-pass softmax per query row     */
 /* ------------------------------------------------------------------------ */
 
-/* Q [B,H,S,D], K and V [B,H,T,D], dense row-major doubles.  For each listed
- * row (b,h,s): score_t = scale * <Q[b,h,s,:], K[b,h,t,:]>, keys t > s are
- * excluded when causal; p_t = exp(score_t - max_t score_t);
- * out = sum_t p_t V[b,h,t,:] / sum_t p_t.  rows holds 3 int64 per row. */
-void orc_attention_rows(const double* Q, const double* K, const double* V, int64_t B, int64_t H,
+/* Q [B,H,S,D], K and V [B,HK,T,D] with HK dividing H, dense row-major
+ * doubles.  Query head h reads key-value head h / (H / HK): with HK < H this
+ * is grouped-query attention, query heads g*(H/HK) .. (g+1)*(H/HK)-1 sharing
+ * key-value head g (the pages' section 3.3, Shardable Indices); HK = H is
+ * ordinary multi-head attention.  For each listed row (b,h,s):
+ * score_t = scale * <Q[b,h,s,:], K[b,kv(h),t,:]>, keys t > s are excluded
+ * when causal; p_t = exp(score_t - max_t score_t);
+ * out = sum_t p_t V[b,kv(h),t,:] / sum_t p_t.  rows holds 3 int64 per row. */
+void orc_attention_rows(const double* Q, const double* K, const double* V, int64_t B, int64_t H, int64_t HK,
                         int64_t S, int64_t T, int64_t D, double scale, int causal, int64_t nrows,
                         const int64_t* rows, double* out) {
     (void)B;
+    const int64_t rep = H / HK;
 #pragma omp parallel
     {
         double* sc = (double*)malloc(sizeof(double) * (size_t)T);
@@ -217,8 +222,8 @@ void orc_attention_rows(const double* Q, const double* K, const double* V, int64
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t b = rows[3 * r], h = rows[3 * r + 1], s = rows[3 * r + 2];
             const double* q = Q + ((b * H + h) * S + s) * D;
-            const double* kb = K + (b * H + h) * T * D;
-            const double* vb = V + (b * H + h) * T * D;
+            const double* kb = K + (b * HK + h / rep) * T * D;
+            const double* vb = V + (b * HK + h / rep) * T * D;
             int64_t tmax = causal ? (s + 1 < T ? s + 1 : T) : T;
             double m = -INFINITY;
             for (int64_t t = 0; t < tmax; ++t) {

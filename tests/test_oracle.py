@@ -285,6 +285,51 @@ def test_attention_dominant_key(orc):
     np.testing.assert_allclose(out[0, 0, 2], [0.0, 20.0], atol=1e-12)
 
 
+def test_gqa_hand_example(orc):
+    """Grouped-query attention (the pages' section 3.3): two query heads share
+    one key-value head.  One query per head, two keys, scale 1: head 0's
+    query (1, 0) scores the keys (1, 0); head 1's query (0, 1) scores them
+    (0, 1).  Both read the same V."""
+    Q = np.array([[1.0, 0.0], [0.0, 1.0]]).reshape(1, 2, 1, 2)
+    K = np.array([[1.0, 0.0], [0.0, 1.0]]).reshape(1, 1, 2, 2)
+    V = np.array([[1.0, 2.0], [3.0, 4.0]]).reshape(1, 1, 2, 2)
+    e = math.e
+    want = np.array([[(e + 3) / (e + 1), (2 * e + 4) / (e + 1)],
+                     [(1 + 3 * e) / (1 + e), (2 + 4 * e) / (1 + e)]])
+    got = orc.attention(Q, K, V, 1.0, False).reshape(2, 2)
+    np.testing.assert_allclose(got, want, rtol=1e-15)
+
+
+def test_gqa_equals_mha_on_repeated_kv(orc):
+    """Query heads g*4 .. g*4+3 use key-value head g: the same as multi-head
+    attention with every key-value head repeated four times (a wrong head
+    map, such as h mod HK, fails this)."""
+    rng = np.random.default_rng(31)
+    B, HK, R, S, D = 2, 3, 4, 17, 8
+    Q = rng.standard_normal((B, HK * R, S, D))
+    K, V = (rng.standard_normal((B, HK, S, D)) for _ in range(2))
+    Kr, Vr = np.repeat(K, R, axis=1), np.repeat(V, R, axis=1)
+    for causal in (True, False):
+        got = orc.attention(Q, K, V, 0.4, causal)
+        want = orc.attention(Q, Kr, Vr, 0.4, causal)
+        np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-15)
+        blocked = orc.attention_online_blocked(Q, K, V, [0, 5, 17], [0, 8, 11, 17], 0.4, causal)
+        np.testing.assert_allclose(blocked, want, rtol=1e-12, atol=1e-13)
+    with pytest.raises(ValueError):
+        orc.attention(Q[:, :10], K, V, 0.4, True)  # 3 key-value heads do not divide 10 query heads
+
+
+def test_gqa_tuple_count(orc):
+    """Q [b, g, r, s, d] against K, V [b, g, t, d]: one tuple per (b, g, r,
+    s, t) interval cell with t_lo < s_hi, so 16 query and key blocks give
+    n (n + 1) / 2 = 136 tuples per (b, g, r) block and one segment per
+    (b, g, r, s) block."""
+    sp = {"b": [0, 1], "g": orc.equal_splits(8, 8), "r": [0, 4], "s": orc.equal_splits(2048, 16),
+          "t": orc.equal_splits(2048, 16), "d": [0, 128]}
+    rec, seg = orc.tuple_records("bgrsdt", sp, "bgrs", causal=("s", "t"))
+    assert rec.shape == (8 * 136, 6) and len(seg) - 1 == 8 * 16
+
+
 def test_attention_online_blocked_equals_two_pass(orc):
     rng = np.random.default_rng(12)
     S, D = 20, 4
