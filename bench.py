@@ -185,7 +185,9 @@ def bench_kernel(args):
     2048x4096x11008 (2x4x4), fused and unfused (ja_kernel then ja_agg);
     attention = [4,32,2048,128] causal, 128-blocks; norm_swiglu = RMSNorm
     [8192,4096] (d by 8) + SwiGLU [8192,11008] (f by 8); configs = all of
-    them.  Inputs are seeded torch draws with the configs' distributions."""
+    them; gqa = grouped-query causal attention, 32 query heads over 8
+    key-value heads, head_dim 128, one 8,192-token sequence and 8 x 1,024
+    tokens.  Inputs are seeded torch draws with the configs' distributions."""
     import torch
 
     from tensor_relational_join_amd import synth
@@ -212,7 +214,8 @@ def bench_kernel(args):
                 "ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
     runs = []  # (name, launch, flops, bytes, ops to close)
     want = ["tiny", "ffn", "ffn_unfused", "attention", "rmsnorm", "swiglu"] if args.workload == "configs" else \
-        {"ffn": ["ffn"], "attention": ["attention"], "norm_swiglu": ["rmsnorm", "swiglu"]}[args.workload]
+        {"ffn": ["ffn"], "attention": ["attention"], "norm_swiglu": ["rmsnorm", "swiglu"],
+         "gqa": ["gqa_8k", "gqa_8x1k"]}[args.workload]
 
     def tensors(op, seed, stds):
         torch.manual_seed(seed)
@@ -254,6 +257,18 @@ def bench_kernel(args):
         ins, out = tensors(op, 3, [(0.0, 1.0)] * 3)
         runs.append(("attention", lambda op=op, ins=ins, out=out: op.run(ins, out),
                      2 * 2.0 * 128 * 128 * 128 * 136 * 128, 2.0 * 4 * 4 * 32 * 2048 * 128, [op]))
+    for name, nb, seq in (("gqa_8k", 1, 8192), ("gqa_8x1k", 8, 1024)):
+        if name not in want:
+            continue
+        # grouped-query causal attention, 32 query heads over 8 key-value heads (4 per group),
+        # head_dim 128, 128-blocks on s and t: Q, O [nb, 8, 4, seq, 128], K, V [nb, 8, seq, 128]
+        nblk = seq // 128
+        sp = {"b": _eq(nb, nb), "g": _eq(8, 8), "r": [0, 4], "s": _eq(seq, nblk), "t": _eq(seq, nblk), "d": [0, 128]}
+        op = Op("bgrsd,bgtd,bgtd->bgrsd", "attention", sp, "causal=s,t")
+        ins, out = tensors(op, 5, [(0.0, 1.0)] * 3)
+        fl = 2 * 2.0 * 128 ** 3 * (nblk * (nblk + 1) // 2) * 32 * nb
+        by = 2.0 * (2 * nb * 32 * seq * 128 + 2 * nb * 8 * seq * 128)
+        runs.append((name, lambda op=op, ins=ins, out=out: op.run(ins, out), fl, by, [op]))
     if "rmsnorm" in want:  # x [8192, 4096], d by 8, eps 1e-6, gain N(1, 0.1)
         op = Op("rd,d->rd", "rmsnorm", {"r": [0, 8192], "d": _eq(4096, 8)}, "eps=1e-6")
         ins, out = tensors(op, 4, [(0.0, 1.0), (1.0, 0.1)])
@@ -294,7 +309,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="block", choices=["block", "configs", "ffn", "attention", "norm_swiglu", "copy"])
+    ap.add_argument("--workload", default="block",
+                    choices=["block", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -134,8 +134,14 @@ ja_status ja_relation_block(const ja_relation_desc* rel, const int64_t* key, int
  *                   block contraction; letters absent from the output are
  *                   aggregated with SUM (section 3.2, Examples 3.8, 3.9).
  *                   Every letter must appear in at least two of A, B, C.
- *   op "attention": "Q,K,V->O" with Q = O = [batch..., s, d] and
+ *   op "attention": "Q,K,V->O" with Q = O = [batch..., group..., s, d] and
  *                   K = V = [batch..., t, d] (e.g. "bhsd,bhtd,bhtd->bhsd").
+ *                   The optional group letters, which must not index K and
+ *                   V, number the query heads that share one key-value head
+ *                   (grouped-query attention, section 3.3: with
+ *                   "bgrsd,bgtd,bgtd->bgrsd", query head 4g + r of a
+ *                   4-per-group layout reads key-value head g, and splitting
+ *                   g splits the query heads with it).
  *                   Scores Q K^T * scale joined on d; aggregation over t with
  *                   the online-softmax triple (max, sum of exponentials,
  *                   weighted sum of values); then O = weighted sum / sum.

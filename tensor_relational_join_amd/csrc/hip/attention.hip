@@ -82,6 +82,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     const int g = lane >> 5, lq = lane & 31;
     const AttnTile tl = tiles[blockIdx.x];
     const AttnSeg sg = segs[tl.seg];
+    const int kvbh = tl.bh / sg.rep;  // key-value batch-head (query heads of a group share it)
     const int qrow = tl.s0 + wave * 32 + lq;  // query row inside the block
     const int qglob = sg.s_lo + qrow;         // global query index (causal mask)
     const int wave_qmin = sg.s_lo + tl.s0 + wave * 32;
@@ -132,11 +133,11 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     int lt = sg.t_begin, lkt = 0;
     auto load_step = [&](int buf) {
         const AttnTuple tp = tuples[lt];
-        const uint16_t* kb = K + tp.k_off + (int64_t)tl.bh * tp.kv_bhstride;
+        const uint16_t* kb = K + tp.k_off + (int64_t)kvbh * tp.kv_bhstride;
         const at_i32x4_t rs = at_rsrc(kb, (uint32_t)(tp.kv_bhstride * 2));
         const uint32_t st = lds0 + (uint32_t)(buf * AT_STAGE * 2);
         const uint32_t soff = (uint32_t)(lkt * D * 2);
-        const at_i32x4_t rv = at_rsrc(V + tp.v_off + (int64_t)tl.bh * tp.kv_bhstride, (uint32_t)(tp.kv_bhstride * 2));
+        const at_i32x4_t rv = at_rsrc(V + tp.v_off + (int64_t)kvbh * tp.kv_bhstride, (uint32_t)(tp.kv_bhstride * 2));
         if (lkt + AT_KT <= tp.T) {  // every key of the step is in the block
 #pragma unroll
             for (int j = 0; j < 4; ++j) at_dma16(rs, st + (wave * 4 + j) * 1024, koffb[j], soff);

@@ -194,13 +194,21 @@ static ja_status parse_spec(const char* einsum, const char* op, const char* para
     } else if (o == "attention") {
         s->kind = JA_OP_ATTENTION;
         if (s->ins.size() != 3) return fail(JA_ERR_SPEC, "attention takes Q, K, V");
+        // Q = O = [batch..., group..., s, d], K = V = [batch..., t, d]: the
+        // optional group letters index the query heads that share one
+        // key-value head (grouped-query attention)
         const std::string &q = s->ins[0], &k = s->ins[1], &v = s->ins[2];
-        if (q != s->out || k != v || q.size() != k.size() || q.size() < 2)
-            return fail(JA_ERR_SPEC, "attention needs Q = O = [batch..., s, d] and K = V = [batch..., t, d]");
-        size_t r = q.size();
-        if (q[r - 1] != k[r - 1] || q[r - 2] == k[r - 2] || q.substr(0, r - 2) != k.substr(0, r - 2))
-            return fail(JA_ERR_SPEC, "attention letters must be [batch..., s, d] and [batch..., t, d]");
-        if (s->causal && (s->causal_s != q[r - 2] || s->causal_t != k[r - 2]))
+        if (q != s->out || k != v || k.size() < 2 || q.size() < k.size())
+            return fail(JA_ERR_SPEC,
+                        "attention needs Q = O = [batch..., group..., s, d] and K = V = [batch..., t, d]");
+        const size_t r = q.size(), rk = k.size();
+        if (q[r - 1] != k[rk - 1] || q[r - 2] == k[rk - 2] || q.substr(0, rk - 2) != k.substr(0, rk - 2) ||
+            q.find(k[rk - 2]) != std::string::npos)
+            return fail(JA_ERR_SPEC, "attention letters must be [batch..., group..., s, d] and [batch..., t, d]");
+        for (size_t i = rk - 2; i < r - 2; ++i)
+            if (k.find(q[i]) != std::string::npos)
+                return fail(JA_ERR_SPEC, "attention group letters must not index K and V");
+        if (s->causal && (s->causal_s != q[r - 2] || s->causal_t != k[rk - 2]))
             return fail(JA_ERR_SPEC, "causal pair must name the query and key position letters");
         s->group_by = s->out;
     } else if (o == "rmsnorm") {

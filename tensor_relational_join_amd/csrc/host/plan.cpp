@@ -357,9 +357,9 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
     if (Q.dtype != JA_BF16 || K.dtype != JA_BF16 || V.dtype != JA_BF16 || O.dtype != JA_BF16)
         return fail(JA_ERR_DTYPE, "attention takes and writes bf16");
     const std::string& q = s->ins[0];
-    const size_t r = q.size();
-    const std::string batch = q.substr(0, r - 2);
-    const char cs = q[r - 2], ct = s->ins[1][r - 2], cd = q[r - 1];
+    const size_t r = q.size(), rk = s->ins[1].size();
+    const std::string batch = q.substr(0, r - 2), kbatch = s->ins[1].substr(0, rk - 2);
+    const char cs = q[r - 2], ct = s->ins[1][rk - 2], cd = q[r - 1];
     const int64_t D = d->ext[s->letter_index(cd)];
     if (D != ATTN_D) return fail(JA_ERR_UNSUPPORTED, "attention kernel is built for head dimension 128");
     p->scale = (float)(s->has_scale ? s->scale : 1.0 / std::sqrt((double)D));
@@ -388,9 +388,13 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
     for (int64_t sg = 0; sg < nseg; ++sg) {
         const int32_t* rec = &t.rec[t.seg[sg] * t.nl];
         int64_t S = d->sp[ls][rec[ls] + 1] - d->sp[ls][rec[ls]];
-        int64_t nbh = extent_of(d, s, rec, batch);
+        int64_t nbh = extent_of(d, s, rec, batch), nkv = extent_of(d, s, rec, kbatch);
         if (S > lim || nbh > lim) return fail(JA_ERR_UNSUPPORTED, "query block beyond 2^31");
         AttnSeg& g = segs[sg];
+        // the group letters trail the batch letters, so query batch-head bh
+        // of the block reads key-value batch-head bh / rep
+        g.rep = (int32_t)(nbh / nkv);
+        g.pad = 0;
         g.q_off = Q.blk_off[block_of(Q, q, s, rec)];
         g.o_off = O.blk_off[block_of(O, s->out, s, rec)];
         g.q_bhstride = S * D;

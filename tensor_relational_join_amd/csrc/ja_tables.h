@@ -87,6 +87,8 @@ struct AttnSeg {
     int32_t S;             // query rows in the block
     int32_t s_lo;          // global query index of the block's first row
     int32_t t_begin, t_end;
+    int32_t rep;           // query batch-heads per key-value batch-head: K/V index = bh / rep
+    int32_t pad;
 };
 
 struct AttnTuple {

@@ -285,6 +285,56 @@ def test_attention_full_size_sampled_rows(dev, orc):
     assert np.isfinite(got).all()
 
 
+# ------------------------------------------------------------------ grouped-query attention
+
+GQA_CASES = [
+    # (B, G, R, S, T, splits of g, r, s, t, causal): Q [B, G, R, S, 128], K and V [B, G, T, 128]
+    ((1, 2, 4, 384, 384), {"g": [0, 1, 2], "r": [0, 4], "s": _eq(384, 3), "t": _eq(384, 3)}, True),
+    ((2, 3, 2, 200, 200), {"g": [0, 2, 3], "r": [0, 1, 2], "s": [0, 72, 200], "t": [0, 130, 200]}, True),
+    ((1, 2, 3, 256, 384), {"g": [0, 2], "r": [0, 3], "s": [0, 128, 256], "t": [0, 64, 384]}, False),
+]
+
+
+@pytest.mark.parametrize("shape,sp,causal", GQA_CASES)
+def test_gqa_attention_small(dev, orc, shape, sp, causal):
+    """Query head g R + r reads key-value head g; splitting g splits the
+    query heads with it (the pages' section 3.3)."""
+    Bn, G, R, S, T = shape
+    sp = dict(sp, b=_eq(Bn, Bn), d=[0, 128])
+    Q = synth.normal_bf16(11, 0, (Bn, G, R, S, 128))
+    K = synth.normal_bf16(11, 1, (Bn, G, T, 128))
+    V = synth.normal_bf16(11, 2, (Bn, G, T, 128))
+    got, o, _ = _run(dev, orc, "bgrsd,bgtd,bgtd->bgrsd", "attention", sp, [Q, K, V],
+                     params="causal=s,t" if causal else "")
+    o.close()
+    want = orc.attention(orc.bf16_to_f64(Q).reshape(Bn, G * R, S, 128), orc.bf16_to_f64(K), orc.bf16_to_f64(V),
+                         1.0 / np.sqrt(128.0), causal)
+    assert rel_frobenius(got, orc.round_bf16(want).reshape(Bn, G, R, S, 128)) <= BF16_TOL
+
+
+def test_gqa_attention_8k_sampled_rows(dev, orc):
+    """The pages' grouped-query shape: 32 query heads over 8 key-value heads,
+    one 8,192-token sequence, 128-blocks on s and t, causal: 8 x 2,080
+    tuples, 512 segments of 4 query heads each."""
+    G, R, S = 8, 4, 8192
+    sp = {"b": [0, 1], "g": _eq(G, G), "r": [0, R], "s": _eq(S, 64), "t": _eq(S, 64), "d": [0, 128]}
+    Q = synth.normal_bf16(12, 0, (1, G, R, S, 128))
+    K = synth.normal_bf16(12, 1, (1, G, S, 128))
+    V = synth.normal_bf16(12, 2, (1, G, S, 128))
+    got, o, _ = _run(dev, orc, "bgrsd,bgtd,bgtd->bgrsd", "attention", sp, [Q, K, V], params="causal=s,t")
+    rec, seg = o.tuples()
+    o.close()
+    assert rec.shape[0] == 8 * 2080 and len(seg) - 1 == 512
+    rng = np.random.default_rng(4)
+    ss = sorted(set([0, 1, 127, 128, 4095, 8191] + list(rng.integers(0, S, 6))))
+    rows = np.array([(0, h, s) for h in (0, 3, 4, 17, 31) for s in ss])
+    want = orc.attention_rows(orc.bf16_to_f64(Q).reshape(1, G * R, S, 128), orc.bf16_to_f64(K),
+                              orc.bf16_to_f64(V), rows, 1.0 / np.sqrt(128.0), True)
+    g = got.reshape(1, G * R, S, 128)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert rel_frobenius(g, orc.round_bf16(want)) <= BF16_TOL
+    assert np.isfinite(got).all()
+
+
 # ------------------------------------------------------------------ RMSNorm, SwiGLU, add
 
 @pytest.mark.parametrize("R,D,rsp,dsp", [

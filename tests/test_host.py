@@ -59,6 +59,13 @@ CASES = [
     ("bhsd,bhtd,bhtd->bhsd", "attention",
      {"b": [0, 2], "h": [0, 1, 3], "s": [0, 50, 130, 300], "t": [0, 100, 128, 300], "d": [0, 128]},
      "causal=s,t", "bhsd", ("s", "t")),
+    # grouped-query attention (section 3.3): 8 key-value heads of 4 query heads each, 8K tokens
+    ("bgrsd,bgtd,bgtd->bgrsd", "attention",
+     {"b": [0, 1], "g": _eq(8, 8), "r": [0, 4], "s": _eq(8192, 64), "t": _eq(8192, 64), "d": [0, 128]},
+     "causal=s,t", "bgrs", ("s", "t")),
+    ("bgrsd,bgtd,bgtd->bgrsd", "attention",
+     {"b": [0, 2], "g": [0, 1, 3], "r": [0, 1, 2], "s": [0, 70, 200], "t": [0, 130, 200], "d": [0, 128]},
+     "", "bgrs", None),
 ]
 
 
@@ -131,6 +138,10 @@ def test_relation_layout_matches_oracle(B, orc):
     # the attention kernel takes the running maximum on raw scores: the scale must be positive
     ("bhsd,bhtd,bhtd->bhsd", "attention", "scale=0", "JA_ERR_SPEC"),
     ("bhsd,bhtd,bhtd->bhsd", "attention", "scale=-0.5;causal=s,t", "JA_ERR_SPEC"),
+    # grouped-query attention: the group letters trail Q's batch letters and do not index K, V
+    ("rbgsd,bgtd,bgtd->rbgsd", "attention", "", "JA_ERR_SPEC"),
+    ("bgsd,bgrtd,bgrtd->bgsd", "attention", "", "JA_ERR_SPEC"),
+    ("bgrsd,bgsd,bgsd->bgrsd", "attention", "", "JA_ERR_SPEC"),
 ])
 def test_spec_errors(B, einsum, op, params, code):
     with pytest.raises(B.JaError) as e:
