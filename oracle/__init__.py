@@ -562,19 +562,33 @@ def overlay_atoms(*split_families: Sequence[Sequence[int]]) -> List[List[int]]:
 # LLaMA-shaped block (pre-norm, causal MHA, SwiGLU FFN, two residual adds)
 # --------------------------------------------------------------------------
 
+def _qkv_heads(qkv, batch: int, seq: int, heads: int, kv_heads: int, hd: int):
+    """Q [b, heads, s, hd], K and V [b, kv_heads, s, hd] from the fused
+    projection's columns [Q heads | K heads | V heads], head h of each part in
+    columns [h*hd, (h+1)*hd) of that part; token t = b*seq + s."""
+    qd, kd = heads * hd, kv_heads * hd
+    Q = qkv[:, :qd].reshape(batch, seq, heads, hd).transpose(0, 2, 1, 3)
+    K = qkv[:, qd:qd + kd].reshape(batch, seq, kv_heads, hd).transpose(0, 2, 1, 3)
+    V = qkv[:, qd + kd:qd + 2 * kd].reshape(batch, seq, kv_heads, hd).transpose(0, 2, 1, 3)
+    return Q, K, V
+
+
 def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
-                eps: float = 1e-6, return_intermediates: bool = False):
+                eps: float = 1e-6, return_intermediates: bool = False, kv_heads: Optional[int] = None):
     """Float64 reference of one transformer block on bf16 inputs, with every
     materialised relation rounded to bf16.  x [batch*seq, d]; w_qkv is
-    [d, 3d] = [W_q | W_k | W_v] with head h in columns [h*hd, (h+1)*hd) of
-    each third.  Token t = b*seq + s.  No rotary embedding and no biases."""
+    [d, (heads + 2 kv_heads) hd] = [W_q | W_k | W_v] with head h in columns
+    [h*hd, (h+1)*hd) of each part; kv_heads < heads is grouped-query
+    attention (query head h reads key-value head h // (heads // kv_heads),
+    section 3.3), kv_heads = heads (the default) multi-head attention.
+    Token t = b*seq + s.  No rotary embedding and no biases."""
     T, Dm = x.shape
     hd = Dm // heads
+    kv_heads = heads if kv_heads is None else kv_heads
     r = round_bf16
     h1 = r(rmsnorm(x, g1, eps))
     qkv = r(matmul(h1, w_qkv))
-    v5 = qkv.reshape(batch, seq, 3, heads, hd).transpose(2, 0, 3, 1, 4)  # [3, b, h, s, hd]
-    Q, K, V = v5[0], v5[1], v5[2]
+    Q, K, V = _qkv_heads(qkv, batch, seq, heads, kv_heads, hd)
     O = r(attention(Q, K, V, 1.0 / np.sqrt(hd), True))
     o = O.transpose(0, 2, 1, 3).reshape(T, Dm)
     a = r(matmul(o, w_o))
@@ -591,7 +605,7 @@ def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: in
 
 
 def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
-                       tokens, eps: float = 1e-6):
+                       tokens, eps: float = 1e-6, kv_heads: Optional[int] = None):
     """The same block as `llama_block`, evaluated only at the listed tokens
     (t = b*seq + s).  Keys and values are formed for every position up to the
     largest listed s of each batch, as causal attention needs them.  Every
@@ -600,6 +614,7 @@ def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, 
     x = _f64(x)
     T, Dm = x.shape
     hd = Dm // heads
+    kv_heads = heads if kv_heads is None else kv_heads
     r = round_bf16
     tokens = np.asarray(tokens, dtype=np.int64)
     y = np.empty((tokens.size, Dm))
@@ -610,8 +625,7 @@ def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, 
         rows = x[b * seq: b * seq + smax + 1]
         h1 = r(rmsnorm(rows, g1, eps))
         qkv = r(matmul(h1, w_qkv))
-        v5 = qkv.reshape(1, smax + 1, 3, heads, hd).transpose(2, 0, 3, 1, 4)
-        Q, K, V = v5[0], v5[1], v5[2]
+        Q, K, V = _qkv_heads(qkv, 1, smax + 1, heads, kv_heads, hd)
         q_rows = np.array([(0, h, s) for s in ss for h in range(heads)], dtype=np.int64)
         O = r(attention_rows(Q, K, V, q_rows, 1.0 / np.sqrt(hd), True)).reshape(len(ss), heads * hd)
         a = r(matmul(O, w_o))

@@ -465,3 +465,26 @@ def test_block_tokens_match_full(orc):
     toks = [0, 3, seq - 1, seq, seq + 2]
     yt = orc.llama_block_tokens(**w, batch=batch, seq=seq, heads=heads, tokens=toks)
     assert np.array_equal(yt, y[toks])
+
+
+def test_gqa_block_equals_mha_block_on_expanded_weights(orc):
+    """Grouped-query block (4 query heads over 2 key-value heads, section
+    3.3): the same as the multi-head block whose W_k and W_v repeat each
+    key-value head's columns for the query heads of its group -- bit for
+    bit, since every output element is computed from the same values in the
+    same order.  The token-sampled form agrees with the full form."""
+    rng = np.random.default_rng(6)
+    T, Dm, heads, kv, F, batch = 12, 16, 4, 2, 6, 2
+    hd = Dm // heads
+    r = lambda a: rng.standard_normal(a) * 0.5
+    w = dict(x=orc.round_bf16(r((T, Dm))), g1=1 + 0.1 * r(Dm), w_qkv=r((Dm, Dm + 2 * kv * hd)), w_o=r((Dm, Dm)),
+             g2=1 + 0.1 * r(Dm), w_gate=r((Dm, F)), w_up=r((Dm, F)), w_down=r((F, Dm)))
+    y = orc.llama_block(**w, batch=batch, seq=T // batch, heads=heads, kv_heads=kv)
+    wq, wk, wv = w["w_qkv"][:, :Dm], w["w_qkv"][:, Dm:Dm + kv * hd], w["w_qkv"][:, Dm + kv * hd:]
+    grp = [h // (heads // kv) for h in range(heads)]
+    expand = lambda m: np.concatenate([m[:, g * hd:(g + 1) * hd] for g in grp], axis=1)
+    w_mha = dict(w, w_qkv=np.concatenate([wq, expand(wk), expand(wv)], axis=1))
+    assert np.array_equal(y, orc.llama_block(**w_mha, batch=batch, seq=T // batch, heads=heads))
+    toks = [0, 4, 5, 6, 11]
+    yt = orc.llama_block_tokens(**w, batch=batch, seq=T // batch, heads=heads, tokens=toks, kv_heads=kv)
+    assert np.array_equal(yt, y[toks])
