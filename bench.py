@@ -104,6 +104,16 @@ def _gemm_traffic():
     return rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
+# the measured block (LLaMA-7B-shaped, multi-head attention) and the pages'
+# own LLaMA-3-8B-like block (grouped-query attention, 32 query over 8
+# key-value heads, FFN 14,336) at 8 sequences of 1,024 tokens
+BLOCKS = {
+    "block": dict(name="llama7b_shaped_block", batch=4, seq=2048, dm=4096, heads=32, kv_heads=32, ffn=11008),
+    "block_gqa": dict(name="llama3_8b_shaped_block_gqa", batch=8, seq=1024, dm=4096, heads=32, kv_heads=8,
+                      ffn=14336),
+}
+
+
 def bench_block(args):
     import torch
 
@@ -111,9 +121,10 @@ def bench_block(args):
     from tensor_relational_join_amd.block import GEMMS, LlamaBlock
     from tensor_relational_join_amd.device import alloc
 
-    batch, seq, dm, heads, ffn = 4, 2048, 4096, 32, 11008
-    blk = LlamaBlock(batch, seq, dm, heads, ffn)
-    inp = synth.llama_block_inputs(5, batch, seq, dm, ffn)
+    cfg = BLOCKS[args.workload]
+    batch, seq, dm, heads, kv, ffn = (cfg[k] for k in ("batch", "seq", "dm", "heads", "kv_heads", "ffn"))
+    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv)
+    inp = synth.llama_block_inputs(5, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols)
     x = blk.materialize(_bits_to_dev(inp["x"]), blk.x_rel)
     w = {k: blk.materialize(_bits_to_dev(inp[k]), rel) for k, rel in blk.w_rel.items()}
     w["g1"] = blk.materialize(_bits_to_dev(inp["g1"]), blk.g_rel)
@@ -162,8 +173,8 @@ def bench_block(args):
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "llama7b_shaped_block", "batch": batch, "seq_len": seq, "d_model": dm,
-                   "heads": heads, "head_dim": 128, "ffn": ffn, "parallelism": "single GPU"},
+        "config": {"workload": cfg["name"], "batch": batch, "seq_len": seq, "d_model": dm,
+                   "heads": heads, "kv_heads": kv, "head_dim": 128, "ffn": ffn, "parallelism": "single GPU"},
         "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "block_gflop": round(total_flops / 1e9, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
@@ -310,7 +321,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block",
-                    choices=["block", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy"])
+                    choices=["block", "block_gqa", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -322,11 +333,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    if args.workload != "block":
+    if args.workload not in BLOCKS:
         print(json.dumps(bench_kernel(args)))
         return
     out, inp = bench_block(args)
-    if not args.no_cpu_baseline:
+    if args.workload == "block" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_block(inp, 4, 2048, 4096, 32, 11008)
     print(json.dumps(out))
 

@@ -21,6 +21,20 @@ so that every producer's output blocking is its consumer's input blocking
 (the repartition sub-cost of the pages' cost model, section 4.3, is then
 zero for them), which leaves exactly the two re-indexing repartitions around
 attention (tokens <-> heads).
+
+With kv_heads < heads the block uses grouped-query attention (the pages'
+section 3.3: query heads g*R .. g*R+R-1 read key-value head g, R = heads /
+kv_heads), the shape of the pages' own LLaMA-3-8B-like blocks:
+
+    qkv = h1 @ W_qkv                  td,dn->tn     t: 1  d: 2  n: cut at the Q | K | V column boundaries
+    (every other op as above, with the tokens in one block)
+    Q = q_heads(qkv[Q part])          repartition [t, heads*hd] -> [b, g, r, s, hd], blocks [1,1,R,128,128]
+    K, V = kv_heads(qkv[K, V parts])  repartition [t, kv*hd] -> [b, g, s, hd], blocks [1,1,128,128]
+    O = attention(Q, K, V)            bgrsd,bgtd,bgtd->bgrsd   b, g unit intervals, s and t 128-blocks
+    o = tokens(O)                     repartition [b, g, r, s, hd] -> [t, dm]
+
+With t unsplit, the three column blocks of the projection's output are
+three contiguous [t, *] arrays, each re-blocked on its own.
 """
 from __future__ import annotations
 
@@ -39,23 +53,39 @@ GEMMS = ["qkv", "oproj", "gate", "up", "down"]
 
 class LlamaBlock:
     def __init__(self, batch: int = 4, seq: int = 2048, dm: int = 4096, heads: int = 32, ffn: int = 11008,
-                 eps: float = 1e-6, device="cuda"):
+                 eps: float = 1e-6, device="cuda", kv_heads: Optional[int] = None):
         if dm % heads or dm // heads != 128 or seq % 128:
             raise ValueError("the attention kernel needs head_dim 128 and 128-multiples of seq")
+        kv = heads if kv_heads is None else kv_heads
+        if kv <= 0 or heads % kv:
+            raise ValueError("kv_heads must divide heads")
         self.batch, self.seq, self.dm, self.heads, self.ffn, self.eps = batch, seq, dm, heads, ffn, eps
+        self.kv_heads, self.gqa = kv, kv != heads
         self.hd = dm // heads
         T = batch * seq
         self.T = T
-        t2, d2 = equal_splits(T, 2), equal_splits(dm, 2)
+        kvd = kv * self.hd
+        self.qkv_cols = dm + 2 * kvd
+        # tokens in two blocks; one block with grouped key-value heads, where the
+        # projection's output must keep its Q, K, V parts contiguous
+        t2, d2 = (equal_splits(T, 2) if not self.gqa else [0, T]), equal_splits(dm, 2)
         f4 = equal_splits(ffn, 4)
         ep = "eps=%r" % eps
+        nb = seq // 128
         self.ops: Dict[str, Op] = {}
         self.ops["norm1"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
-        self.ops["qkv"] = Op("td,dn->tn", "contract", {"t": t2, "d": d2, "n": equal_splits(3 * dm, 2)}, device=device)
-        nb = seq // 128
-        att_sp = {"b": equal_splits(batch, batch), "h": equal_splits(heads, heads), "s": equal_splits(seq, nb),
-                  "t": equal_splits(seq, nb), "d": [0, self.hd]}
-        self.ops["attn"] = Op("bhsd,bhtd,bhtd->bhsd", "attention", att_sp, "causal=s,t", device=device)
+        if not self.gqa:
+            self.ops["qkv"] = Op("td,dn->tn", "contract", {"t": t2, "d": d2, "n": equal_splits(3 * dm, 2)},
+                                 device=device)
+            att_sp = {"b": equal_splits(batch, batch), "h": equal_splits(heads, heads), "s": equal_splits(seq, nb),
+                      "t": equal_splits(seq, nb), "d": [0, self.hd]}
+            self.ops["attn"] = Op("bhsd,bhtd,bhtd->bhsd", "attention", att_sp, "causal=s,t", device=device)
+        else:
+            self.ops["qkv"] = Op("td,dn->tn", "contract",
+                                 {"t": t2, "d": d2, "n": [0, dm, dm + kvd, dm + 2 * kvd]}, device=device)
+            att_sp = {"b": equal_splits(batch, batch), "g": equal_splits(kv, kv), "r": [0, heads // kv],
+                      "s": equal_splits(seq, nb), "t": equal_splits(seq, nb), "d": [0, self.hd]}
+            self.ops["attn"] = Op("bgrsd,bgtd,bgtd->bgrsd", "attention", att_sp, "causal=s,t", device=device)
         self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": d2, "n": d2}, device=device)
         self.ops["add1"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
         self.ops["norm2"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
@@ -65,13 +95,29 @@ class LlamaBlock:
         self.ops["down"] = Op("tf,fn->tn", "contract", {"t": t2, "f": f4, "n": d2}, device=device)
         self.ops["add2"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
         # token-major <-> head-major re-blockings around attention
-        heads_rel = B.Relation((3, batch, heads, seq, self.hd), nblk=(3, batch, heads, nb, 1), dtype=B.JA_BF16)
         self.rp: Dict[str, Repart] = {}
-        self.rp["to_heads"] = Repart(self.ops["qkv"].out_rel, heads_rel,
-                                     B.make_view((batch, seq, 3, heads, self.hd), (2, 0, 3, 1, 4)), device=device)
-        self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, self.ops["oproj"].in_rels[0],
-                                      B.make_view((batch, heads, seq, self.hd), (0, 2, 1, 3)), device=device)
-        self.heads_rel = heads_rel
+        if not self.gqa:
+            heads_rel = B.Relation((3, batch, heads, seq, self.hd), nblk=(3, batch, heads, nb, 1), dtype=B.JA_BF16)
+            self.rp["to_heads"] = Repart(self.ops["qkv"].out_rel, heads_rel,
+                                         B.make_view((batch, seq, 3, heads, self.hd), (2, 0, 3, 1, 4)),
+                                         device=device)
+            self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, self.ops["oproj"].in_rels[0],
+                                          B.make_view((batch, heads, seq, self.hd), (0, 2, 1, 3)), device=device)
+            self.heads_rel = heads_rel
+        else:
+            rep = heads // kv
+            q_rel, k_rel, v_rel = self.ops["attn"].in_rels
+            self.part_rel = {"q": B.Relation((T, dm), nblk=(1, 1), dtype=B.JA_BF16),
+                             "k": B.Relation((T, kvd), nblk=(1, 1), dtype=B.JA_BF16),
+                             "v": B.Relation((T, kvd), nblk=(1, 1), dtype=B.JA_BF16)}
+            self.rp["to_q"] = Repart(self.part_rel["q"], q_rel,
+                                     B.make_view((batch, seq, kv, rep, self.hd), (0, 2, 3, 1, 4)), device=device)
+            for name, rel in (("k", k_rel), ("v", v_rel)):
+                self.rp["to_" + name] = Repart(self.part_rel[name], rel,
+                                               B.make_view((batch, seq, kv, self.hd), (0, 2, 1, 3)), device=device)
+            self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, self.ops["oproj"].in_rels[0],
+                                          B.make_view((batch, kv, rep, seq, self.hd), (0, 3, 1, 2, 4)),
+                                          device=device)
         # relations of the block's inputs (materialised straight into the blockings the ops need)
         self.x_rel = self.ops["norm1"].in_rels[0]
         self.g_rel = self.ops["norm1"].in_rels[1]
@@ -80,9 +126,13 @@ class LlamaBlock:
                       "w_down": self.ops["down"].in_rels[1]}
         # intermediates
         o = self.ops
+        if not self.gqa:
+            heads = {"heads": alloc(self.heads_rel, device)}
+        else:
+            heads = {n: alloc(r, device) for n, r in zip("qkv", o["attn"].in_rels)}
         self.buf = {
             "h1": alloc(o["norm1"].out_rel, device), "qkv": alloc(o["qkv"].out_rel, device),
-            "heads": alloc(heads_rel, device), "O": alloc(o["attn"].out_rel, device),
+            **heads, "O": alloc(o["attn"].out_rel, device),
             "o": alloc(o["oproj"].in_rels[0], device), "a": alloc(o["oproj"].out_rel, device),
             "x2": alloc(o["add1"].out_rel, device), "h2": alloc(o["norm2"].out_rel, device),
             "gt": alloc(o["gate"].out_rel, device), "up": alloc(o["up"].out_rel, device),
@@ -92,7 +142,7 @@ class LlamaBlock:
     # ---------------------------------------------------------------- flops / bytes
     def flops(self) -> Dict[str, float]:
         T, dm, ffn = self.T, self.dm, self.ffn
-        f = {"qkv": 2.0 * T * dm * 3 * dm, "oproj": 2.0 * T * dm * dm, "gate": 2.0 * T * dm * ffn,
+        f = {"qkv": 2.0 * T * dm * self.qkv_cols, "oproj": 2.0 * T * dm * dm, "gate": 2.0 * T * dm * ffn,
              "up": 2.0 * T * dm * ffn, "down": 2.0 * T * ffn * dm}
         nb = self.seq // 128
         kept = nb * (nb + 1) // 2  # kept (s-block, t-block) tuples per (b, h)
@@ -105,7 +155,7 @@ class LlamaBlock:
         T, dm, ffn = self.T, self.dm, self.ffn
         e = 2.0
         return {"norm1": e * (2 * T * dm + dm), "norm2": e * (2 * T * dm + dm), "add1": e * 3 * T * dm,
-                "add2": e * 3 * T * dm, "swiglu": e * 3 * T * ffn, "to_heads": e * 2 * T * 3 * dm,
+                "add2": e * 3 * T * dm, "swiglu": e * 3 * T * ffn, "to_heads": e * 2 * T * self.qkv_cols,
                 "to_tokens": e * 2 * T * dm}
 
     # ---------------------------------------------------------------- execution
@@ -115,12 +165,24 @@ class LlamaBlock:
         the relations' layouts (x_rel, w_rel, g_rel).  If `events` is given,
         a (start, end) torch event pair is recorded around every step."""
         o, b = self.ops, self.buf
-        n = self.T * self.heads * self.hd  # elements of each of Q, K, V
-        q, k, v = b["heads"][:n], b["heads"][n:2 * n], b["heads"][2 * n:]
+        if not self.gqa:
+            n = self.T * self.heads * self.hd  # elements of each of Q, K, V
+            q, k, v = b["heads"][:n], b["heads"][n:2 * n], b["heads"][2 * n:]
+
+            def to_heads():
+                self.rp["to_heads"].run(b["qkv"], b["heads"], stream)
+        else:
+            q, k, v = b["q"], b["k"], b["v"]
+            nq, nk = self.T * self.dm, self.T * self.kv_heads * self.hd  # the projection's Q and K, V parts
+
+            def to_heads():
+                self.rp["to_q"].run(b["qkv"][:nq], q, stream)
+                self.rp["to_k"].run(b["qkv"][nq:nq + nk], k, stream)
+                self.rp["to_v"].run(b["qkv"][nq + nk:], v, stream)
         plan = [
             ("norm1", lambda: o["norm1"].run([x, w["g1"]], b["h1"], stream)),
             ("qkv", lambda: o["qkv"].run([b["h1"], w["w_qkv"]], b["qkv"], stream)),
-            ("to_heads", lambda: self.rp["to_heads"].run(b["qkv"], b["heads"], stream)),
+            ("to_heads", to_heads),
             ("attn", lambda: o["attn"].run([q, k, v], b["O"], stream)),
             ("to_tokens", lambda: self.rp["to_tokens"].run(b["O"], b["o"], stream)),
             ("oproj", lambda: o["oproj"].run([b["o"], w["w_o"]], b["a"], stream)),

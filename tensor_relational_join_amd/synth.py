@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import os
 from concurrent.futures import ThreadPoolExecutor
-from typing import Sequence
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -128,13 +128,14 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
 LLAMA_BLOCK_STREAMS = ["x", "g1", "w_qkv", "w_o", "g2", "w_gate", "w_up", "w_down"]
 
 
-def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int) -> dict:
+def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int, qkv_cols: Optional[int] = None) -> dict:
     """bf16 bit patterns of one block's inputs: x ~ N(0,1) [batch*seq, dm];
-    gains ~ N(1, 0.1) [dm]; weights ~ N(0, 0.02): w_qkv [dm, 3dm] (= [W_q |
-    W_k | W_v]), w_o [dm, dm], w_gate and w_up [dm, ffn], w_down [ffn, dm].
+    gains ~ N(1, 0.1) [dm]; weights ~ N(0, 0.02): w_qkv [dm, qkv_cols] (= [W_q
+    | W_k | W_v]; 3 dm columns unless given, fewer with grouped key-value
+    heads), w_o [dm, dm], w_gate and w_up [dm, ffn], w_down [ffn, dm].
     Stream i of `seed` feeds the i-th tensor of LLAMA_BLOCK_STREAMS."""
     T = batch * seq
-    shapes = {"x": (T, dm), "g1": (dm,), "w_qkv": (dm, 3 * dm), "w_o": (dm, dm), "g2": (dm,),
+    shapes = {"x": (T, dm), "g1": (dm,), "w_qkv": (dm, qkv_cols or 3 * dm), "w_o": (dm, dm), "g2": (dm,),
               "w_gate": (dm, ffn), "w_up": (dm, ffn), "w_down": (ffn, dm)}
     out = {}
     for i, name in enumerate(LLAMA_BLOCK_STREAMS):

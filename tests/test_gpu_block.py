@@ -37,14 +37,14 @@ def _unpack(orc, rel, t, as_bits=False):
     return bits if as_bits else orc.bf16_to_f64(bits)
 
 
-def _run_block(orc, batch, seq, dm, heads, ffn, seed):
+def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None):
     import torch
 
     from tensor_relational_join_amd.block import LlamaBlock
     from tensor_relational_join_amd.device import alloc
 
-    blk = LlamaBlock(batch, seq, dm, heads, ffn)
-    inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn)
+    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv_heads)
+    inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols)
     x = _pack(orc, blk.x_rel, inp["x"])
     w = {k: _pack(orc, rel, inp[k]) for k, rel in blk.w_rel.items()}
     w["g1"] = _pack(orc, blk.g_rel, inp["g1"])
@@ -80,25 +80,48 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
     xd = f64(inp["x"])
     h1 = _unpack(orc, o["norm1"].out_rel, b["h1"])
     errs["norm1"] = rel_frobenius(h1, orc.round_bf16(orc.rmsnorm(xd, f64(inp["g1"]), blk.eps)))
-    contract("qkv", o["norm1"].out_rel, b["h1"], "w_qkv", o["qkv"].out_rel, b["qkv"], 3 * dm, 3 * dm // 2)
-    qr, hr = o["qkv"].out_rel, blk.heads_rel
-    want_heads = orc.repartition(orc.Relation(qr.shape, qr.splits), bf16_bits(b["qkv"]),
-                                 orc.Relation(hr.shape, hr.splits), (batch, seq, 3, heads, 128), (2, 0, 3, 1, 4))
-    heads_bits = bf16_bits(b["heads"])
-    errs["to_heads"] = 0.0 if np.array_equal(heads_bits, want_heads) else 1.0
-    hd = f64(orc.Relation(hr.shape, hr.splits).unpack(heads_bits))
-    Od = _unpack(orc, o["attn"].out_rel, b["O"])
+    N = blk.qkv_cols
+    contract("qkv", o["norm1"].out_rel, b["h1"], "w_qkv", o["qkv"].out_rel, b["qkv"], N,
+             dm if blk.gqa else N // 2)
+    qr = o["qkv"].out_rel
+    kv, rep = blk.kv_heads, heads // blk.kv_heads
+    if not blk.gqa:
+        hr = blk.heads_rel
+        want_heads = orc.repartition(orc.Relation(qr.shape, qr.splits), bf16_bits(b["qkv"]),
+                                     orc.Relation(hr.shape, hr.splits), (batch, seq, 3, heads, 128), (2, 0, 3, 1, 4))
+        heads_bits = bf16_bits(b["heads"])
+        errs["to_heads"] = 0.0 if np.array_equal(heads_bits, want_heads) else 1.0
+        Qd, Kd, Vd = f64(orc.Relation(hr.shape, hr.splits).unpack(heads_bits))
+    else:
+        # the projection's output is three contiguous [T, *] parts: Q heads, K heads, V heads
+        flat = bf16_bits(b["qkv"])
+        nq, nk = T * dm, T * kv * 128
+        parts = {"q": flat[:nq], "k": flat[nq:nq + nk], "v": flat[nq + nk:]}
+        views = {"q": ((batch, seq, kv, rep, 128), (0, 2, 3, 1, 4)), "k": ((batch, seq, kv, 128), (0, 2, 1, 3)),
+                 "v": ((batch, seq, kv, 128), (0, 2, 1, 3))}
+        ok, dense = True, {}
+        for name, rel in zip("qkv", o["attn"].in_rels):
+            pr = blk.part_rel[name]
+            want_p = orc.repartition(orc.Relation(pr.shape, pr.splits), parts[name],
+                                     orc.Relation(rel.shape, rel.splits), *views[name])
+            got_p = bf16_bits(b[name])
+            ok = ok and np.array_equal(got_p, want_p)
+            dense[name] = f64(orc.Relation(rel.shape, rel.splits).unpack(got_p))
+        errs["to_heads"] = 0.0 if ok else 1.0
+        Qd, Kd, Vd = dense["q"].reshape(batch, heads, seq, 128), dense["k"], dense["v"]
+    Od = _unpack(orc, o["attn"].out_rel, b["O"]).reshape(batch, heads, seq, 128)
     if sampled:
         ss = [0, 1, 127, 128, 1000, seq - 1]
         rows = np.array([(bb, hh, s) for bb, hh in [(0, 0), (batch // 2, heads // 2), (batch - 1, heads - 1)]
                          for s in ss])
     else:
         rows = np.array(list(itertools.product(range(batch), range(heads), range(seq))))
-    want = orc.round_bf16(orc.attention_rows(hd[0], hd[1], hd[2], rows, 1.0 / np.sqrt(128.0), True))
+    want = orc.round_bf16(orc.attention_rows(Qd, Kd, Vd, rows, 1.0 / np.sqrt(128.0), True))
     errs["attn"] = rel_frobenius(Od[rows[:, 0], rows[:, 1], rows[:, 2]], want)
     ar, orl = o["attn"].out_rel, o["oproj"].in_rels[0]
+    view = ((batch, kv, rep, seq, 128), (0, 3, 1, 2, 4)) if blk.gqa else ((batch, heads, seq, 128), (0, 2, 1, 3))
     want_o = orc.repartition(orc.Relation(ar.shape, ar.splits), bf16_bits(b["O"]),
-                             orc.Relation(orl.shape, orl.splits), (batch, heads, seq, 128), (0, 2, 1, 3))
+                             orc.Relation(orl.shape, orl.splits), *view)
     errs["to_tokens"] = 0.0 if np.array_equal(bf16_bits(b["o"]), want_o) else 1.0
     contract("oproj", orl, b["o"], "w_o", o["oproj"].out_rel, b["a"], dm, dm // 2)
     x2 = _unpack(orc, o["add1"].out_rel, b["x2"])
@@ -143,6 +166,44 @@ def test_block_full_size(orc):
         f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
         want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
                                         f["w_down"], batch, seq, heads, toks)
+        chain = rel_frobenius(yd[toks], want_y)
+        print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        for k, v in errs.items():
+            assert v <= TOL, (k, v)
+        assert chain <= CHAIN_TOL
+    finally:
+        blk.close()
+
+
+def test_gqa_block_reduced_shapes(orc):
+    """Grouped-query block: 8 query heads over 2 key-value heads."""
+    batch, seq, dm, heads, kv, ffn = 2, 256, 1024, 8, 2, 768
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=13, kv_heads=kv)
+    try:
+        errs, yd = _check_steps(orc, blk, inp, y, sampled=False)
+        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
+        want = orc.llama_block(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"],
+                               batch, seq, heads, kv_heads=kv)
+        chain = rel_frobenius(yd, want)
+        print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        for k, v in errs.items():
+            assert v <= TOL, (k, v)
+        assert chain <= CHAIN_TOL
+    finally:
+        blk.close()
+
+
+def test_gqa_block_llama3_8b_shape(orc):
+    """The pages' LLaMA-3-8B-like block: d 4096, 32 query heads over 8
+    key-value heads, FFN 14,336, 8 sequences of 1,024 tokens."""
+    batch, seq, dm, heads, kv, ffn = 8, 1024, 4096, 32, 8, 14336
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=14, kv_heads=kv)
+    try:
+        errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
+        toks = [bb * seq + s for bb in (0, 5) for s in (0, 1, 63, 100)]
+        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
+        want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
+                                        f["w_down"], batch, seq, heads, toks, kv_heads=kv)
         chain = rel_frobenius(yd[toks], want_y)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
         for k, v in errs.items():
