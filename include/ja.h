@@ -198,23 +198,14 @@ void ja_tuples_destroy(ja_tuples* tuples);
 ja_status ja_plan_create(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
                          int32_t n_in, const ja_relation_desc* out, ja_plan** plan);
 /* table_bytes: device buffer size for ja_plan_upload; workspace_bytes: the
- * workspace ja_plan_run needs, 0 for most plans.  A bf16 contraction whose
- * output tiles leave the last wave of workgroups partly idle splits the
- * tiles of that wave along the contracted extent; it then needs one arrival
- * counter per split tile and one fp32 output tile (256 x 256) of partial sums
- * per piece. */
+ * workspace ja_plan_run needs (may be 0). */
 ja_status ja_plan_device_bytes(const ja_plan* plan, size_t* table_bytes, size_t* workspace_bytes);
 /* Copy the plan's tables to dev_buf (at least table_bytes) on `stream` and
  * wait for the copy.  The buffer must stay alive while the plan is run. */
 ja_status ja_plan_upload(ja_plan* plan, void* dev_buf, size_t bytes, void* stream);
 /* Run the whole join-agg: every tuple's kernel with the aggregation fused
  * into it, writing each output block exactly once (recompose in place).
- * in_ptrs[i] / out_ptr: device buffers of the relations given at create.
- * workspace: caller-owned device buffer of workspace_bytes, 256-byte
- * aligned, or NULL when workspace_bytes is 0 (JA_ERR_WORKSPACE otherwise).
- * The run clears what it uses of it first; runs that share one workspace
- * must be ordered (same stream).  Results do not depend on the order in
- * which split pieces finish: their partial sums are added in a fixed order. */
+ * in_ptrs[i] / out_ptr: device buffers of the relations given at create. */
 ja_status ja_plan_run(const ja_plan* plan, const void* const* in_ptrs, void* out_ptr, void* workspace,
                       void* stream);
 /* Unfused path (contract only): ja_kernel writes every tuple's partial
@@ -229,9 +220,8 @@ void ja_plan_destroy(ja_plan* plan);
 
 /* One-shot convenience: create a plan, upload its tables into dev_ws, run,
  * and destroy the plan.  Blocks until the table upload is done; the run
- * itself stays asynchronous.  dev_ws must be 256-byte aligned and ws_bytes at
- * least the value returned by ja_einsum_workspace_bytes (the tables, rounded
- * up to 256 bytes, followed by the plan's run workspace). */
+ * itself stays asynchronous.  ws_bytes must be at least the value returned
+ * by ja_einsum_workspace_bytes. */
 ja_status ja_einsum_workspace_bytes(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
                                     int32_t n_in, const ja_relation_desc* out, size_t* bytes);
 ja_status ja_einsum(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,

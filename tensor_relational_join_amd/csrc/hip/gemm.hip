@@ -368,10 +368,12 @@ __device__ __forceinline__ void wait_loads_barrier() {
 }
 
 template <int BM, int BN, int NS, int WM, int WN, int AL, int BL, int OUT_BF16>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
-    const GemmTile* __restrict__ tiles, const GemmPiece* __restrict__ pieces, int ndp, int ngrid,
-    const GemmSeg* __restrict__ segs, const GemmTuple* __restrict__ tuples, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ B, void* __restrict__ C, float* __restrict__ slots, uint32_t* __restrict__ counters) {
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTile* __restrict__ tiles, int ntiles,
+                                                                    const GemmSeg* __restrict__ segs,
+                                                                    const GemmTuple* __restrict__ tuples,
+                                                                    const uint16_t* __restrict__ A,
+                                                                    const uint16_t* __restrict__ B,
+                                                                    void* __restrict__ C) {
     constexpr int NT = WM * WN * 64;
     constexpr int BK = 32;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -383,202 +385,155 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
     static_assert((NS - 1) * PER_STAGE <= 63, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) uint16_t gemm_lds[];
-    int& last_flag = *reinterpret_cast<int*>(gemm_lds + NS * STAGE);  // after the stages
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
+    const GemmTile tl = tiles[xcd_remap(blockIdx.x, ntiles)];
+    const GemmSeg sg = segs[tl.seg];
+    const int m0 = tl.m0, n0 = tl.n0;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)gemm_lds;
+
+    int nst = 0;
+    for (int t = sg.t_begin; t < sg.t_end; ++t) nst += (tuples[t].K + BK - 1) / BK;
+
+    f32x4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // load cursor: tuple lt, contracted offset lk inside it; the per-lane
+    // offsets and buffer descriptors of tuple lt are cached
+    int lt = sg.t_begin, lk = 0, cached = -1;
+    TA ta;
+    TB tb;
+    i32x4_t rsa, rsb;
+    int lda = 0, ldb = 0, kext = 0;
+    auto issue = [&](int buf) {
+        if (cached != lt) {
+            const GemmTuple tp = tuples[lt];
+            const uint16_t* pa = A + tp.a_off + (int64_t)tl.batch * tp.a_bstride;
+            const uint16_t* pb = B + tp.b_off + (int64_t)tl.batch * tp.b_bstride;
+            rsa = buffer_rsrc(pa, (uint32_t)(tp.a_bstride * 2));
+            rsb = buffer_rsrc(pb, (uint32_t)(tp.b_bstride * 2));
+            lda = tp.lda;
+            ldb = tp.ldb;
+            kext = tp.K;
+            ta.setup(lda, m0, sg.M, wave, lane);
+            tb.setup(ldb, n0, sg.N, wave, lane);
+            cached = lt;
+        }
+        const uint32_t st = lds0 + (uint32_t)(buf * STAGE * 2);
+        ta.issue(st, rsa, lda, lk, kext, wave);
+        tb.issue(st + BM * BK * 2, rsb, ldb, lk, kext, wave);
+        lk += BK;
+        if (lk >= kext) {
+            lk = 0;
+            ++lt;
+        }
+    };
+    // Stage s lives in LDS buffer s % NS.  The fragments of stage it + 1 are
+    // read into registers while the MFMAs of stage it run, so once a
+    // wavefront passes the barrier of iteration it, nobody reads buffer
+    // it % NS any more and it is refilled with stage it + NS.
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < nst) issue(s);
+
     const int arow = wm * WTM, brow = wn * WTN;
-
-    // One piece per workgroup.  Whole tiles come first in the grid, then the
-    // pieces of split tiles; each range is spread over the XCDs on its own,
-    // so both stay balanced and the pieces of one tile share an XCD.
-    const int bid = blockIdx.x;
-    const int v = bid < ndp ? xcd_remap(bid, ndp) : ndp + xcd_remap(bid - ndp, ngrid - ndp);
-    {
-        const GemmPiece pz = pieces[v];
-        const GemmTile tl = tiles[pz.tile];
-        const GemmSeg sg = segs[tl.seg];
-        const int m0 = tl.m0, n0 = tl.n0;
-        const int nst = pz.nst;
-
-        f32x4_t acc[FM][FN];
+    bf16x8_t fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, bf16x8_t* a, bf16x8_t* b) {
+        const uint16_t* as = gemm_lds + buf * STAGE;
+        const uint16_t* bs = as + BM * BK;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = TA::frag(as, arow + i * 16, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = TB::frag(bs, brow + j * 16, lane);
+    };
+    // wait until stage `need` has landed: the stages issued after it may stay in flight
+    auto wait_stage = [&](int need) {
+        // issued so far: stages 0 .. NS - 1 up front, then one per step
+        const int ahead = need == 0 ? min(NS - 1, nst - 1) : min(need + NS - 2, nst - 1) - need;
+        if (ahead >= 3)
+            wait_loads_barrier<(NS >= 4 ? 3 : 0) * PER_STAGE>();
+        else if (ahead == 2)
+            wait_loads_barrier<(NS >= 3 ? 2 : 0) * PER_STAGE>();
+        else if (ahead == 1)
+            wait_loads_barrier<PER_STAGE>();
+        else
+            wait_loads_barrier<0>();
+    };
+    // After the barrier a wavefront starts its MFMAs at once (their operands
+    // were read one step earlier) and issues the refill of buffer it % NS
+    // halfway through them, so the load issue hides behind matrix work.
+    // Per step: barrier; the first quarter of the MFMAs (their operands were
+    // read one step earlier and are complete, so any wait the compiler puts
+    // before them is free); the fragment reads of the next stage; a quarter;
+    // the refill of buffer it % NS; the last half.  The reads and the load
+    // issue thus run in the shadow of matrix work.  The wait and the reads
+    // also run on the last step (reading a buffer nobody refills any more)
+    // so that every path has the same LDS reads in flight.
+    auto mfma_rows = [&](int i0, int i1, const bf16x8_t* ca, const bf16x8_t* cb) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        // load cursor: tuple lt, contracted offset lk inside it; the per-lane
-        // offsets and buffer descriptors of tuple lt are cached
-        int lt = pz.t0, lk = pz.k0, cached = -1;
-        TA ta;
-        TB tb;
-        i32x4_t rsa, rsb;
-        int lda = 0, ldb = 0, kext = 0;
-        auto issue = [&](int buf) {
-            if (cached != lt) {
-                const GemmTuple tp = tuples[lt];
-                const uint16_t* pa = A + tp.a_off + (int64_t)tl.batch * tp.a_bstride;
-                const uint16_t* pb = B + tp.b_off + (int64_t)tl.batch * tp.b_bstride;
-                rsa = buffer_rsrc(pa, (uint32_t)(tp.a_bstride * 2));
-                rsb = buffer_rsrc(pb, (uint32_t)(tp.b_bstride * 2));
-                lda = tp.lda;
-                ldb = tp.ldb;
-                kext = tp.K;
-                ta.setup(lda, m0, sg.M, wave, lane);
-                tb.setup(ldb, n0, sg.N, wave, lane);
-                cached = lt;
-            }
-            const uint32_t st = lds0 + (uint32_t)(buf * STAGE * 2);
-            ta.issue(st, rsa, lda, lk, kext, wave);
-            tb.issue(st + BM * BK * 2, rsb, ldb, lk, kext, wave);
-            lk += BK;
-            if (lk >= kext) {
-                lk = 0;
-                ++lt;
-            }
-        };
-        // Stage s lives in LDS buffer s % NS.  The fragments of stage it + 1
-        // are read into registers while the MFMAs of stage it run, so once a
-        // wavefront passes the barrier of iteration it, nobody reads buffer
-        // it % NS any more and it is refilled with stage it + NS.
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-            if (s < nst) issue(s);
-
-        bf16x8_t fa[2][FM], fb[2][FN];
-        auto read_frags = [&](int buf, bf16x8_t* a, bf16x8_t* b) {
-            const uint16_t* as = gemm_lds + buf * STAGE;
-            const uint16_t* bs = as + BM * BK;
-#pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = TA::frag(as, arow + i * 16, lane);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = TB::frag(bs, brow + j * 16, lane);
-        };
-        // wait until stage `need` has landed: the stages issued after it may stay in flight
-        auto wait_stage = [&](int need) {
-            // issued so far: stages 0 .. NS - 1 up front, then one per step
-            const int ahead = need == 0 ? min(NS - 1, nst - 1) : min(need + NS - 2, nst - 1) - need;
-            if (ahead >= 3)
-                wait_loads_barrier<(NS >= 4 ? 3 : 0) * PER_STAGE>();
-            else if (ahead == 2)
-                wait_loads_barrier<(NS >= 3 ? 2 : 0) * PER_STAGE>();
-            else if (ahead == 1)
-                wait_loads_barrier<PER_STAGE>();
-            else
-                wait_loads_barrier<0>();
-        };
-        // Per step: barrier; the first quarter of the MFMAs (their operands
-        // were read one step earlier and are complete, so any wait the
-        // compiler puts before them is free); the fragment reads of the next
-        // stage; a quarter; the refill of buffer it % NS; the last half.  The
-        // reads and the load issue thus run in the shadow of matrix work.  The
-        // wait and the reads also run on the last step (reading a buffer
-        // nobody refills any more) so that every path has the same LDS reads
-        // in flight.
-        auto mfma_rows = [&](int i0, int i1, const bf16x8_t* ca, const bf16x8_t* cb) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                if (i >= i0 && i < i1)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb[j], ca[i], acc[i][j], 0, 0, 0);
-        };
-        auto step = [&](int it, bf16x8_t* ca, bf16x8_t* cb, bf16x8_t* na, bf16x8_t* nb) {
-            wait_stage(it + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_rows(0, FM / 4, ca, cb);
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags((it + 1) % NS, na, nb);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_rows(FM / 4, FM / 2, ca, cb);
-            __builtin_amdgcn_sched_barrier(0);
-            if (it + NS < nst) issue(it % NS);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_rows(FM / 2, FM, ca, cb);
-        };
-        if (nst > 0) {
-            wait_stage(0);
-            read_frags(0, fa[0], fb[0]);
-        }
-        for (int it = 0; it < nst; it += 2) {
-            step(it, fa[0], fb[0], fa[1], fb[1]);
-            if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
-        }
-
-        if (pz.nparts > 1) {
-            // A piece of a split tile: its partial sum goes to the tile's
-            // workspace slot for this part; the last part to arrive adds all
-            // parts in part order (so the sum does not depend on the order of
-            // arrival) and writes the output.  One device-scope acquire-release
-            // increment publishes the workgroup's slot (the barrier orders
-            // every wavefront's stores before it) and, for the last arrival,
-            // makes the other parts' slots visible to the whole workgroup
-            // (the barrier after it orders every wavefront's loads after it).
-            float* const slot = slots + (int64_t)pz.slot0 * (BM * BN);
-            float* const mine = slot + (int64_t)pz.part * (BM * BN);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
+            if (i >= i0 && i < i1)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    *reinterpret_cast<f32x4_t*>(mine + ((i * FN + j) * NT + tid) * 4) = acc[i][j];
-            __syncthreads();
-            if (tid == 0)
-                last_flag = __hip_atomic_fetch_add(counters + pz.cnt, 1u, __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(pz.nparts - 1);
-            __syncthreads();
-            if (!last_flag) return;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int e = ((i * FN + j) * NT + tid) * 4;
-                    f32x4_t s = pz.part == 0 ? acc[i][j] : *reinterpret_cast<const f32x4_t*>(slot + e);
-                    for (int c = 1; c < pz.nparts; ++c)
-                        s += c == pz.part ? acc[i][j]
-                                          : *reinterpret_cast<const f32x4_t*>(slot + (int64_t)c * (BM * BN) + e);
-                    acc[i][j] = s;
-                }
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb[j], ca[i], acc[i][j], 0, 0, 0);
+    };
+    auto step = [&](int it, bf16x8_t* ca, bf16x8_t* cb, bf16x8_t* na, bf16x8_t* nb) {
+        wait_stage(it + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(0, FM / 4, ca, cb);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags((it + 1) % NS, na, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(FM / 4, FM / 2, ca, cb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + NS < nst) issue(it % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(FM / 2, FM, ca, cb);
+    };
+    if (nst > 0) {
+        wait_stage(0);
+        read_frags(0, fa[0], fb[0]);
+    }
+    for (int it = 0; it < nst; it += 2) {
+        step(it, fa[0], fb[0], fa[1], fb[1]);
+        if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
+    }
 
-        // epilogue: lane owns C[row][col .. col+3] of every fragment
-        const int kc = lane >> 4;
-        const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
+    // epilogue: lane owns C[row][col .. col+3] of every fragment
+    const int kc = lane >> 4;
+    const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = m0 + arow + i * 16 + (lane & 15);
-            if (row >= sg.M) continue;
+    for (int i = 0; i < FM; ++i) {
+        const int row = m0 + arow + i * 16 + (lane & 15);
+        if (row >= sg.M) continue;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + brow + j * 16 + 4 * kc;
-                const int64_t off = cbase + (int64_t)row * sg.ldc + col;
-                const f32x4_t a = acc[i][j];
-                if (col + 4 <= sg.N && (off & 3) == 0) {
-                    if (OUT_BF16)
-                        *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_bf16x2(a[0], a[1]),
-                                                                                   pack_bf16x2(a[2], a[3]));
-                    else
-                        *reinterpret_cast<float4*>((float*)C + off) = make_float4(a[0], a[1], a[2], a[3]);
-                } else {
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + brow + j * 16 + 4 * kc;
+            const int64_t off = cbase + (int64_t)row * sg.ldc + col;
+            const f32x4_t a = acc[i][j];
+            if (col + 4 <= sg.N && (off & 3) == 0) {
+                if (OUT_BF16)
+                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_bf16x2(a[0], a[1]),
+                                                                               pack_bf16x2(a[2], a[3]));
+                else
+                    *reinterpret_cast<float4*>((float*)C + off) = make_float4(a[0], a[1], a[2], a[3]);
+            } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (col + r < sg.N) {
-                            if (OUT_BF16)
-                                ((uint16_t*)C)[off + r] = (uint16_t)f32_to_bf16(a[r]);
-                            else
-                                ((float*)C)[off + r] = a[r];
-                        }
-                }
+                for (int r = 0; r < 4; ++r)
+                    if (col + r < sg.N) {
+                        if (OUT_BF16)
+                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_bf16(a[r]);
+                        else
+                            ((float*)C)[off + r] = a[r];
+                    }
             }
         }
     }
-}
-
-// Arrival counters of split tiles start every run at zero.
-__global__ void gemm_zero_counters(uint32_t* __restrict__ c, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) c[i] = 0u;
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -645,29 +600,22 @@ static void launch_bf16(const GemmTile* tiles, int ntiles, const GemmSeg* segs, 
 }
 
 template <int AL, int BL, int OB>
-static void launch_bf16_dma(const GemmTile* tiles, const GemmGrid& g, const uint8_t* t, const GemmSeg* segs,
-                            const GemmTuple* tuples, const void* A, const void* B, void* C, void* ws, hipStream_t s) {
+static void launch_bf16_dma(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples,
+                            const void* A, const void* B, void* C, hipStream_t s) {
     constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, NS = GEMM_DMA_STAGES, WM = 2, WN = 4;
-    constexpr unsigned lds = (unsigned)NS * (BM + BN) * 32 * sizeof(uint16_t) + 16;  // stages + arrival flag
-    const GemmPiece* pieces = (const GemmPiece*)(t + g.pieces_off);
-    uint32_t* counters = (uint32_t*)ws;
-    float* slots = ws ? (float*)((uint8_t*)ws + g.slots_off) : nullptr;
-    if (g.ncnt > 0)
-        hipLaunchKernelGGL(gemm_zero_counters, dim3((g.ncnt + 255) / 256), dim3(256), 0, s, counters, g.ncnt);
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, OB>), dim3(g.ngrid), dim3(WM * WN * 64), lds,
-                       s, tiles, pieces, g.ndp, g.ngrid, segs, tuples, (const uint16_t*)A,
-                       (const uint16_t*)B, C, slots, counters);
+    constexpr unsigned lds = (unsigned)NS * (BM + BN) * 32 * sizeof(uint16_t);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, OB>), dim3(ntiles), dim3(WM * WN * 64), lds,
+                       s, tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C);
 }
 
 template <int AL, int BL>
-static void launch_bf16_out(int out_bf16, const GemmGrid* grid, const uint8_t* t, const GemmTile* tiles, int ntiles,
-                            const GemmSeg* segs, const GemmTuple* tuples, const void* A, const void* B, void* C,
-                            void* ws, hipStream_t s) {
-    if (grid) {
+static void launch_bf16_out(int out_bf16, int dma, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
+                            const GemmTuple* tuples, const void* A, const void* B, void* C, hipStream_t s) {
+    if (dma) {
         if (out_bf16)
-            launch_bf16_dma<AL, BL, 1>(tiles, *grid, t, segs, tuples, A, B, C, ws, s);
+            launch_bf16_dma<AL, BL, 1>(tiles, ntiles, segs, tuples, A, B, C, s);
         else
-            launch_bf16_dma<AL, BL, 0>(tiles, *grid, t, segs, tuples, A, B, C, ws, s);
+            launch_bf16_dma<AL, BL, 0>(tiles, ntiles, segs, tuples, A, B, C, s);
     } else {
         if (out_bf16)
             launch_bf16<AL, BL, 1>(tiles, ntiles, segs, tuples, A, B, C, s);
@@ -677,8 +625,8 @@ static void launch_bf16_out(int out_bf16, const GemmGrid* grid, const uint8_t* t
 }
 
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
-                       const GemmGrid* grid, const void* A, const void* B, void* C, int32_t in_dtype,
-                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, void* ws, hipStream_t s) {
+                       const void* A, const void* B, void* C, int32_t in_dtype, int32_t out_dtype, int32_t a_layout,
+                       int32_t b_layout, int32_t dma, hipStream_t s) {
     const uint8_t* t = (const uint8_t*)table;
     const GemmTile* tiles = (const GemmTile*)(t + tiles_off);
     const GemmSeg* segs = (const GemmSeg*)(t + segs_off);
@@ -686,13 +634,13 @@ hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int
     if (in_dtype == JA_BF16) {
         const int ob = out_dtype == JA_BF16;
         if (a_layout == JA_A_MK && b_layout == JA_B_KN)
-            launch_bf16_out<JA_A_MK, JA_B_KN>(ob, grid, t, tiles, ntiles, segs, tuples, A, B, C, ws, s);
+            launch_bf16_out<JA_A_MK, JA_B_KN>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
         else if (a_layout == JA_A_MK && b_layout == JA_B_NK)
-            launch_bf16_out<JA_A_MK, JA_B_NK>(ob, grid, t, tiles, ntiles, segs, tuples, A, B, C, ws, s);
+            launch_bf16_out<JA_A_MK, JA_B_NK>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
         else if (a_layout == JA_A_KM && b_layout == JA_B_KN)
-            launch_bf16_out<JA_A_KM, JA_B_KN>(ob, grid, t, tiles, ntiles, segs, tuples, A, B, C, ws, s);
+            launch_bf16_out<JA_A_KM, JA_B_KN>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
         else
-            launch_bf16_out<JA_A_KM, JA_B_NK>(ob, grid, t, tiles, ntiles, segs, tuples, A, B, C, ws, s);
+            launch_bf16_out<JA_A_KM, JA_B_NK>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
     } else {
 #define JA_F32_CASE(al, bl)                                                                                       \
     hipLaunchKernelGGL((gemm_f32_kernel<al, bl>), dim3(ntiles), dim3(256), 0, s, tiles, ntiles, segs, tuples,     \

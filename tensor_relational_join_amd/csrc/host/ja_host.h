@@ -90,12 +90,9 @@ ja_status build_tuples(const ja_spec* spec, const ja_decomp* d, ja_tuples& t);
 
 // ---- kernel launchers (implemented in the .hip sources) --------------------
 namespace ja {
-// grid: the piece list of the direct-to-LDS bf16 kernel, or NULL for the
-// one-tile-per-workgroup kernels; ws: the plan workspace (split-tile
-// counters and partial sums) when grid has split tiles.
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
-                       const GemmGrid* grid, const void* A, const void* B, void* C, int32_t in_dtype,
-                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, void* ws, hipStream_t stream);
+                       const void* A, const void* B, void* C, int32_t in_dtype, int32_t out_dtype,
+                       int32_t a_layout, int32_t b_layout, int32_t dma, hipStream_t stream);
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
                             int64_t tuples_off, const void* Q, const void* K, const void* V, void* O,
                             float scale, int32_t causal, hipStream_t stream);

@@ -10,7 +10,6 @@
 // the recompose is in place, since every aggregated block is written straight
 // into its slot of the output relation.
 #include <algorithm>
-#include <climits>
 #include <cmath>
 #include <cstring>
 
@@ -32,8 +31,6 @@ struct ja_plan {
     int32_t natiles = 0;
     int32_t in_dtype = 0, out_dtype = 0, a_layout = 0, b_layout = 0;
     int32_t gemm_dma = 0;  // bf16 operands reachable through 32-bit buffer offsets
-    GemmGrid grid{}, ugrid{};  // piece lists of the fused and unfused launches (direct-to-LDS kernel)
-    size_t ws_bytes = 0;
     int64_t partial_elems = 0;
     // attention
     float scale = 0.f;
@@ -56,85 +53,6 @@ int64_t put(std::vector<uint8_t>& tab, const std::vector<T>& v) {
     tab.resize(off + v.size() * sizeof(T));
     if (!v.empty()) std::memcpy(tab.data() + off, v.data(), v.size() * sizeof(T));
     return (int64_t)off;
-}
-
-// Lay out the pieces of a contraction launch (one workgroup each).  Stages
-// are the kernel's 32-wide steps along the contracted extent; a tile's
-// stages run through its segment's tuples in order.  With `split` false, or
-// when it would not shorten the launch, every tile is one piece.  Otherwise
-// the tiles of the machine's last, partly filled wave (or of the last two
-// waves) are each cut into s pieces of near-equal stage counts, with s and
-// the number of cut tiles chosen to minimise the launch length counted in
-// tile-times at GEMM_WAVE_WGS workgroups per wave; a split has to shorten
-// it by 10% to pay for the partial-sum traffic.
-void build_pieces(const std::vector<GemmTile>& tiles, const std::vector<GemmSeg>& segs,
-                  const std::vector<GemmTuple>& tuples, bool split, std::vector<GemmPiece>& pieces, GemmGrid& g) {
-    const int BK = 32;
-    const int64_t T = (int64_t)tiles.size(), G = GEMM_WAVE_WGS;
-    std::vector<int64_t> seg_st(segs.size(), 0);
-    for (size_t i = 0; i < segs.size(); ++i)
-        for (int32_t t = segs[i].t_begin; t < segs[i].t_end; ++t) seg_st[i] += (tuples[t].K + BK - 1) / BK;
-    // first stage of a piece: tuple index and contracted offset inside it
-    auto stage_at = [&](const GemmSeg& sg, int64_t st, int32_t& t0, int32_t& k0) {
-        for (int32_t t = sg.t_begin; t < sg.t_end; ++t) {
-            const int64_t n = (tuples[t].K + BK - 1) / BK;
-            if (st < n) {
-                t0 = t;
-                k0 = (int32_t)(st * BK);
-                return;
-            }
-            st -= n;
-        }
-        t0 = sg.t_end;
-        k0 = 0;
-    };
-    int64_t ndp = T, parts = 1;
-    if (split && T % G != 0) {
-        int64_t min_st = INT64_MAX;
-        for (const GemmTile& t : tiles) min_st = std::min(min_st, seg_st[t.seg]);
-        const double whole = (double)((T + G - 1) / G);
-        double best = whole * 0.9;  // splitting has to win by a margin (the partial sums cost traffic)
-        for (int64_t keep : {T / G * G, std::max<int64_t>(0, T / G - 1) * G})
-            for (int64_t s = 2; s <= 4; ++s) {
-                const int64_t r = T - keep;
-                if (r <= 0 || min_st < 8 * s) continue;  // pieces of at least 8 stages
-                const double len = (double)(keep / G) + (double)((r * s + G - 1) / G) / (double)s;
-                if (len < best - 1e-9) {
-                    best = len;
-                    ndp = keep;
-                    parts = s;
-                }
-            }
-    }
-    pieces.clear();
-    g = GemmGrid{};
-    int32_t nslot = 0, ncnt = 0;
-    for (int64_t i = 0; i < T; ++i) {
-        const GemmSeg& sg = segs[tiles[i].seg];
-        const int64_t n = seg_st[tiles[i].seg];
-        const int64_t np = i < ndp ? 1 : parts;
-        for (int64_t k = 0; k < np; ++k) {
-            GemmPiece pc{};
-            pc.tile = (int32_t)i;
-            const int64_t lo = n * k / np, hi = n * (k + 1) / np;
-            stage_at(sg, lo, pc.t0, pc.k0);
-            pc.nst = (int32_t)(hi - lo);
-            pc.part = (int32_t)k;
-            pc.nparts = (int32_t)np;
-            pc.slot0 = np > 1 ? nslot : -1;
-            pc.cnt = np > 1 ? ncnt : -1;
-            pieces.push_back(pc);
-        }
-        if (np > 1) {
-            nslot += (int32_t)np;
-            ++ncnt;
-        }
-    }
-    g.ndp = (int32_t)ndp;
-    g.ngrid = (int32_t)pieces.size();
-    g.ncnt = ncnt;
-    g.nslot = nslot;
-    g.slots_off = (int64_t)(((size_t)ncnt * 4 + 255) & ~(size_t)255);
 }
 
 // Check that relation `r` is the projection grid the decomposition asks for:
@@ -327,16 +245,6 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
     p->utiles_off = put(p->table, utiles);
     p->nutiles = (int32_t)utiles.size();
     p->usegs_off = put(p->table, usegs);
-    if (p->gemm_dma) {
-        std::vector<GemmPiece> pieces;
-        build_pieces(tiles, segs, tuples, true, pieces, p->grid);
-        p->grid.pieces_off = put(p->table, pieces);
-        if (p->grid.ncnt > 0)
-            p->ws_bytes = (size_t)p->grid.slots_off + (size_t)p->grid.nslot * GEMM_BF16_TM * GEMM_BF16_TN * 4;
-        // the unfused kernel writes each tuple's own partial block: whole tiles only
-        build_pieces(utiles, usegs, tuples, false, pieces, p->ugrid);
-        p->ugrid.pieces_off = put(p->table, pieces);
-    }
     p->atiles_off = put(p->table, atiles);
     p->natiles = (int32_t)atiles.size();
     p->asegs_off = put(p->table, asegs);
@@ -524,7 +432,7 @@ ja_status ja_plan_create(const ja_spec* s, const ja_decomp* d, const ja_relation
 ja_status ja_plan_device_bytes(const ja_plan* p, size_t* table_bytes, size_t* workspace_bytes) {
     if (!p) return fail(JA_ERR_ARG, "plan is NULL");
     if (table_bytes) *table_bytes = p->table.size();
-    if (workspace_bytes) *workspace_bytes = p->ws_bytes;
+    if (workspace_bytes) *workspace_bytes = 0;
     return JA_OK;
 }
 
@@ -552,17 +460,15 @@ static ja_status check_ptrs(const ja_plan* p, const void* const* in_ptrs, const 
 }
 
 ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_ptr, void* workspace, void* stream) {
+    (void)workspace;
     ja_status st = check_ptrs(p, in_ptrs, out_ptr);
     if (st) return st;
-    if (p->ws_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255)))
-        return fail(JA_ERR_WORKSPACE, "this plan needs a 256-byte aligned workspace of ja_plan_device_bytes bytes");
     hipStream_t hs = (hipStream_t)stream;
     switch (p->kind) {
         case JA_OP_CONTRACT:
             if (p->ntiles == 0) return JA_OK;
-            JA_TRY_HIP(launch_gemm(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off,
-                                   p->gemm_dma ? &p->grid : nullptr, in_ptrs[0], in_ptrs[1], out_ptr, p->in_dtype,
-                                   p->out_dtype, p->a_layout, p->b_layout, workspace, hs));
+            JA_TRY_HIP(launch_gemm(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
+                                   out_ptr, p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, p->gemm_dma, hs));
             break;
         case JA_OP_ATTENTION:
             if (p->ntiles == 0) return JA_OK;
@@ -591,9 +497,8 @@ ja_status ja_kernel(const ja_plan* p, const void* const* in_ptrs, void* partials
     if (st) return st;
     if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
     if (p->nutiles == 0) return JA_OK;
-    JA_TRY_HIP(launch_gemm(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off,
-                           p->gemm_dma ? &p->ugrid : nullptr, in_ptrs[0], in_ptrs[1], partials, p->in_dtype, JA_F32,
-                           p->a_layout, p->b_layout, nullptr, (hipStream_t)stream));
+    JA_TRY_HIP(launch_gemm(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
+                           partials, p->in_dtype, JA_F32, p->a_layout, p->b_layout, p->gemm_dma, (hipStream_t)stream));
     return JA_OK;
 }
 

@@ -37,34 +37,6 @@ struct GemmTuple {
     int32_t pad;
 };
 
-// A contiguous run of one output tile's 32-wide contracted stages, taken by
-// one workgroup.  A tile taken whole is one piece (nparts = 1) and writes the
-// output block directly.  When the tiles leave the machine's last wave
-// partly idle, the tiles of that wave are split along the contracted extent
-// into nparts pieces of near-equal stage counts; each piece leaves a partial
-// sum in the workspace and whichever piece finishes last adds them in part
-// order, so the result does not depend on the arrival order.
-struct GemmPiece {
-    int32_t tile;    // index into the tile list
-    int32_t t0, k0;  // first stage: tuple index and contracted offset inside it
-    int32_t nst;     // stages in the piece
-    int32_t part;    // position among the tile's pieces (stage order)
-    int32_t nparts;  // pieces of the tile
-    int32_t slot0;   // workspace slot of the tile's part 0 (parts are consecutive)
-    int32_t cnt;     // arrival counter of the tile in the workspace
-};
-
-// How the direct-to-LDS contraction kernel is launched over a piece list
-// (host-side record; the offsets point into the plan table and workspace).
-struct GemmGrid {
-    int64_t pieces_off;  // byte offset of the GemmPiece array (one per workgroup) in the table
-    int32_t ndp;         // workgroups that take whole tiles (the first ndp of the grid)
-    int32_t ngrid;       // workgroups in the grid
-    int32_t ncnt;        // arrival counters at the start of the workspace
-    int32_t nslot;       // partial-sum slots (one output tile of fp32 each) after them
-    int64_t slots_off;   // byte offset of the partial-sum slots in the workspace
-};
-
 // Layout of an operand matrix inside its block.
 enum : int32_t {
     JA_A_MK = 0,  // A[m][k] at m*lda + k (k contiguous)
@@ -138,7 +110,6 @@ constexpr int GEMM_BF16_TN = 256;  // output columns per workgroup tile
 constexpr int GEMM_BF16_TK = 64;   // contracted elements per LDS stage
 constexpr int GEMM_GROUP_M = 4;    // row tiles per group in the tile order (L2 reuse)
 constexpr int GEMM_DMA_STAGES = 4; // 32-wide stages in flight in the direct-to-LDS kernel
-constexpr int GEMM_WAVE_WGS = 256; // contraction workgroups resident at once (one per CU)
 constexpr int GEMM_F32_TM = 64;    // fp32 kernel tile
 constexpr int GEMM_F32_TN = 64;
 constexpr int ATTN_TQ = 128;       // query rows per attention workgroup

@@ -185,39 +185,6 @@ def test_contract_bf16_f32_output_and_determinism(dev, orc):
     assert JA_BF16 != JA_F32
 
 
-def test_contract_bf16_split_tiles(dev, orc):
-    """Two output tiles on a machine that holds far more workgroups: each tile
-    is cut along the contracted extent into three pieces (stages 0-7, 8-15,
-    16-24 of 25), so the second piece starts on the ragged last stage of the
-    first tuple (K = 264) and the third inside the second tuple.  The pieces
-    leave partial sums in the workspace and the last to finish adds them."""
-    import torch
-
-    from tensor_relational_join_amd.binding import JA_F32
-
-    sp = {"i": [0, 256, 512], "j": [0, 264, 520, 776], "k": [0, 256]}
-    X = synth.normal_bf16(9, 0, (512, 776))
-    W = synth.normal_bf16(9, 1, (776, 256), std=0.02)
-    want = orc.einsum("ij,jk->ik", orc.bf16_to_f64(X), orc.bf16_to_f64(W))
-    got, o, _ = _run(dev, orc, "ij,jk->ik", "contract", sp, [X, W])
-    try:
-        assert o.workspace is not None  # the split pieces need counters and partial-sum slots
-    finally:
-        o.close()
-    assert rel_frobenius(got, orc.round_bf16(want)) <= BF16_TOL
-    got32, o, ins = _run(dev, orc, "ij,jk->ik", "contract", sp, [X, W], out_dtype=JA_F32)
-    try:
-        assert rel_inf(got32, want) <= 1e-5
-        # the same workspace serves the next run: counters are cleared per run
-        again = dev.alloc(o.out_rel)
-        o.run(ins, again)
-        torch.cuda.synchronize()
-        orel = orc.Relation((512, 256), [sp["i"], sp["k"]])
-        assert np.array_equal(orel.unpack(f32_host(again)).astype(np.float64), got32)
-    finally:
-        o.close()
-
-
 def test_ffn_contraction_full_size_sampled(dev, orc):
     """b=2048, d=4096, f=11008 split 2 x 4 x 4: 32 tuples, 8 segments of 4."""
     sp = {"b": _eq(2048, 2), "d": _eq(4096, 4), "f": _eq(11008, 4)}

@@ -298,43 +298,3 @@ def test_one_shot_entry_points_refuse_a_small_workspace(B):
     with pytest.raises(B.JaError) as e:
         B.ja_repartition(src, 16, dst, 16, None, 1 << 20, need - 1)
     assert e.value.name == "JA_ERR_WORKSPACE"
-
-
-def test_split_tile_workspace_sizes(B):
-    """Output tiles that leave the last wave of 256 workgroups partly idle are
-    split along the contracted extent; the plan then asks for one 4-byte
-    counter per split tile (rounded up to 256 bytes) and one fp32 256 x 256
-    partial-sum tile per piece.  Tile counts that fill whole waves, and the
-    fp32 kernel, need no workspace."""
-    from tensor_relational_join_amd.device import equal_splits as eq, relation_for
-
-    def ws(einsum, sp, dt=None):
-        dt = B.JA_BF16 if dt is None else dt
-        s = B.ja_spec_create(einsum, "contract")
-        L = B.ja_spec_letters(s)
-        d = B.ja_decomp_create(s, [sp[c][-1] for c in L], [len(sp[c]) - 1 for c in L], [sp[c] for c in L])
-        p = None
-        try:
-            lhs, o = einsum.split("->")
-            p = B.ja_plan_create(s, d, [relation_for(x, sp, dt) for x in lhs.split(",")], relation_for(o, sp, dt))
-            return B.ja_plan_device_bytes(p)[1]
-        finally:
-            if p is not None:
-                B.ja_plan_destroy(p)
-            B.ja_decomp_destroy(d)
-            B.ja_spec_destroy(s)
-
-    tile = 256 * 256 * 4
-    # FFN 2048 x 4096 x 11008 cut 2 x 4 x 4: 8 blocks of 4 x 11 tiles = 352 tiles; the 96 past the
-    # first wave are cut in two (1 + 192 / 256 / 2 = 1.5 tile-times instead of 2)
-    assert ws("bd,df->bf", {"b": eq(2048, 2), "d": eq(4096, 4), "f": eq(11008, 4)}) == 512 + 192 * tile
-    # gate projection 8192 x 4096 x 11008 cut 2 x 2 x 4: 1408 tiles = 5.5 waves; cutting the last
-    # wave's tiles in two would save under 10%, less than it costs, so they stay whole
-    assert ws("td,df->tf", {"t": eq(8192, 2), "d": eq(4096, 2), "f": eq(11008, 4)}) == 0
-    # QKV 8192 x 4096 x 12288: 1536 tiles = 6 full waves
-    assert ws("td,dn->tn", {"t": eq(8192, 2), "d": eq(4096, 2), "n": eq(12288, 2)}) == 0
-    # too few stages to cut (K = 24 is one stage)
-    assert ws("ij,jk->ik", {"i": [0, 64], "j": [0, 24], "k": [0, 40, 80]}) == 0
-    # two tiles of 25 stages: three pieces each
-    assert ws("ij,jk->ik", {"i": [0, 256, 512], "j": [0, 264, 520, 776], "k": [0, 256]}) == 256 + 6 * tile
-    assert ws("ij,jk->ik", {"i": [0, 256, 512], "j": [0, 264, 520, 776], "k": [0, 256]}, B.JA_F32) == 0
