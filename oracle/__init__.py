@@ -25,7 +25,9 @@ Einsummable", paperpeel full text):
   (m, l, acc) -- ``attention_online_blocked`` (the aggregation operator need
   not be addition, section 5.2); both attention forms take fewer key-value
   heads than query heads (grouped-query attention, section 3.3: query heads
-  g*R .. g*R+R-1 share key-value head g);
+  g*R .. g*R+R-1 share key-value head g), and ``attention`` /
+  ``tuple_records`` take sequences packed end to end along the sequence index
+  (section 3.3: attention never crosses a sequence boundary);
 * the LLaMA-shaped block as a chain of the above -- ``llama_block``.
 
 Readings where the pages are silent (listed again in the design notes):
@@ -80,7 +82,7 @@ def _load():
         lib.orc_einsum2_points.restype = ctypes.c_int
         lib.orc_matmul.argtypes = [_f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
         lib.orc_attention_rows.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int64] * 6 + [
-            ctypes.c_double, ctypes.c_int, ctypes.c_int64, _i64p, _f64p]
+            ctypes.c_double, ctypes.c_int, ctypes.c_int64, _i64p, ctypes.c_int64, _i64p, _f64p]
         lib.orc_rmsnorm.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _f64p]
         lib.orc_swiglu.argtypes = [_f64p, _f64p, ctypes.c_int64, _f64p]
         lib.orc_add.argtypes = [_f64p, _f64p, ctypes.c_int64, _f64p]
@@ -193,28 +195,34 @@ def matmul(A, B) -> np.ndarray:
     return C
 
 
-def attention_rows(Q, K, V, rows, scale: float, causal: bool) -> np.ndarray:
+def attention_rows(Q, K, V, rows, scale: float, causal: bool, seq_ends: Optional[Sequence[int]] = None) -> np.ndarray:
     """Attention output rows for the listed (b, h, s) query rows.
     Q [B,H,S,D], K/V [B,HK,T,D] with HK dividing H: query head h reads
     key-value head h // (H // HK) (grouped-query attention when HK < H,
-    section 3.3; ordinary multi-head attention when HK = H).  Two-pass
-    softmax in float64."""
+    section 3.3; ordinary multi-head attention when HK = H).  With seq_ends
+    (ascending, the last = S = T) the sequence index holds independent
+    sequences packed end to end (section 3.3) and a key is visible to a query
+    only inside the query's own sequence.  Two-pass softmax in float64."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     Bn, H, S, D = Q.shape
     HK, T = K.shape[1], K.shape[2]
     if K.shape != V.shape or K.shape[0] != Bn or K.shape[3] != D or H % HK:
         raise ValueError("attention: K and V must be [B, HK, T, D] with HK dividing Q's H")
+    ends = np.ascontiguousarray(np.asarray(seq_ends if seq_ends is not None else [], dtype=np.int64))
+    if ends.size and (S != T or ends[-1] != S or np.any(np.diff(ends) <= 0) or ends[0] <= 0):
+        raise ValueError("attention: sequence ends must ascend to S = T")
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
     out = np.empty((rows.shape[0], D), dtype=np.float64)
     _load().orc_attention_rows(_ptr(Q, _f64p), _ptr(K, _f64p), _ptr(V, _f64p), Bn, H, HK, S, T, D, float(scale),
-                               1 if causal else 0, rows.shape[0], _ptr(rows, _i64p), _ptr(out, _f64p))
+                               1 if causal else 0, ends.size, _ptr(ends, _i64p) if ends.size else None,
+                               rows.shape[0], _ptr(rows, _i64p), _ptr(out, _f64p))
     return out
 
 
-def attention(Q, K, V, scale: float, causal: bool) -> np.ndarray:
+def attention(Q, K, V, scale: float, causal: bool, seq_ends: Optional[Sequence[int]] = None) -> np.ndarray:
     Bn, H, S, D = np.shape(Q)
     rows = np.array(list(itertools.product(range(Bn), range(H), range(S))), dtype=np.int64)
-    return attention_rows(Q, K, V, rows, scale, causal).reshape(Bn, H, S, D)
+    return attention_rows(Q, K, V, rows, scale, causal, seq_ends).reshape(Bn, H, S, D)
 
 
 def rmsnorm(x, g, eps: float) -> np.ndarray:
@@ -449,14 +457,16 @@ def brute_force_einsum(spec: str, A, B) -> np.ndarray:
 
 
 def tuple_records(letters: Sequence[str], splits: Dict[str, Sequence[int]], group_by: Sequence[str],
-                  causal: Optional[Tuple[str, str]] = None):
+                  causal: Optional[Tuple[str, str]] = None, packed: Optional[Tuple[str, str, Sequence[int]]] = None):
     """Canonical tuple list of a decomposition: one record per kept grid
     cell, holding the interval index of every letter (in `letters` order).
     Records are sorted by the group-by letters' indices (in `group_by`
     order), then by the other letters' indices (in `letters` order).  A
     causal pair (s, t) drops every cell whose key interval starts at or
-    after the end of its query interval.  Returns (records [n, L] int32,
-    segment offsets [nseg + 1] int64)."""
+    after the end of its query interval.  packed = (s, t, sequence ends)
+    drops every cell whose query and key intervals share no sequence
+    (section 3.3: attention never crosses a sequence boundary).  Returns
+    (records [n, L] int32, segment offsets [nseg + 1] int64)."""
     rest = [c for c in letters if c not in group_by]
     recs = []
     for combo in itertools.product(*[range(len(splits[c]) - 1) for c in letters]):
@@ -464,6 +474,13 @@ def tuple_records(letters: Sequence[str], splits: Dict[str, Sequence[int]], grou
         if causal is not None:
             s, t = causal
             if splits[t][cell[t]] >= splits[s][cell[s] + 1]:
+                continue
+        if packed is not None:
+            s, t, ends = packed
+            slo, shi = splits[s][cell[s]], splits[s][cell[s] + 1]
+            tlo, thi = splits[t][cell[t]], splits[t][cell[t] + 1]
+            starts = [0] + list(ends[:-1])
+            if not any(a < shi and b > slo and a < thi and b > tlo for a, b in zip(starts, ends)):
                 continue
         recs.append(cell)
     recs.sort(key=lambda c: (tuple(c[x] for x in group_by), tuple(c[x] for x in rest)))

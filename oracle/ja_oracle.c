@@ -209,10 +209,15 @@ void orc_matmul(const double* A, const double* B, double* C, int64_t M, int64_t 
  * ordinary multi-head attention.  For each listed row (b,h,s):
  * score_t = scale * <Q[b,h,s,:], K[b,kv(h),t,:]>, keys t > s are excluded
  * when causal; p_t = exp(score_t - max_t score_t);
- * out = sum_t p_t V[b,kv(h),t,:] / sum_t p_t.  rows holds 3 int64 per row. */
+ * out = sum_t p_t V[b,kv(h),t,:] / sum_t p_t.  rows holds 3 int64 per row.
+ * Packed sequences (the pages' section 3.3: independent sequences packed end
+ * to end along the sequence index; attention never crosses a sequence
+ * boundary): with nseq > 0, seq_ends holds the ascending end positions of the
+ * sequences (the last equal to S = T), and key t is visible to query s only
+ * if both lie in the same sequence [start, end). */
 void orc_attention_rows(const double* Q, const double* K, const double* V, int64_t B, int64_t H, int64_t HK,
-                        int64_t S, int64_t T, int64_t D, double scale, int causal, int64_t nrows,
-                        const int64_t* rows, double* out) {
+                        int64_t S, int64_t T, int64_t D, double scale, int causal, int64_t nseq,
+                        const int64_t* seq_ends, int64_t nrows, const int64_t* rows, double* out) {
     (void)B;
     const int64_t rep = H / HK;
 #pragma omp parallel
@@ -224,19 +229,26 @@ void orc_attention_rows(const double* Q, const double* K, const double* V, int64
             const double* q = Q + ((b * H + h) * S + s) * D;
             const double* kb = K + (b * HK + h / rep) * T * D;
             const double* vb = V + (b * HK + h / rep) * T * D;
-            int64_t tmax = causal ? (s + 1 < T ? s + 1 : T) : T;
+            int64_t tmin = 0, tmax = causal ? (s + 1 < T ? s + 1 : T) : T;
+            for (int64_t k = 0; k < nseq; ++k)
+                if (s < seq_ends[k]) {  /* the query's sequence is [tmin, seq_ends[k]) */
+                    if (seq_ends[k] < tmax) tmax = seq_ends[k];
+                    break;
+                } else {
+                    tmin = seq_ends[k];
+                }
             double m = -INFINITY;
-            for (int64_t t = 0; t < tmax; ++t) {
+            for (int64_t t = tmin; t < tmax; ++t) {
                 double acc = 0.0;
                 for (int64_t d = 0; d < D; ++d) acc += q[d] * kb[t * D + d];
                 sc[t] = scale * acc;
                 if (sc[t] > m) m = sc[t];
             }
             double l = 0.0;
-            for (int64_t t = 0; t < tmax; ++t) { sc[t] = exp(sc[t] - m); l += sc[t]; }
+            for (int64_t t = tmin; t < tmax; ++t) { sc[t] = exp(sc[t] - m); l += sc[t]; }
             double* o = out + r * D;
             for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-            for (int64_t t = 0; t < tmax; ++t)
+            for (int64_t t = tmin; t < tmax; ++t)
                 for (int64_t d = 0; d < D; ++d) o[d] += sc[t] * vb[t * D + d];
             for (int64_t d = 0; d < D; ++d) o[d] /= l;
         }

@@ -488,3 +488,43 @@ def test_gqa_block_equals_mha_block_on_expanded_weights(orc):
     toks = [0, 4, 5, 6, 11]
     yt = orc.llama_block_tokens(**w, batch=batch, seq=T // batch, heads=heads, tokens=toks, kv_heads=kv)
     assert np.array_equal(yt, y[toks])
+
+
+def test_packed_attention_is_per_sequence_attention(orc):
+    """Packed sequences (the pages' section 3.3): three sequences ending at 5,
+    13 and 20 along one index.  Each query sees only its own sequence, so the
+    packed result equals attention run on every sequence by itself -- causal
+    and not, multi-head and grouped-query; one sequence is plain attention."""
+    rng = np.random.default_rng(41)
+    S, D, ends = 20, 8, [5, 13, 20]
+    for H, HK in ((2, 2), (4, 2)):
+        Q = rng.standard_normal((2, H, S, D))
+        K, V = (rng.standard_normal((2, HK, S, D)) for _ in range(2))
+        for causal in (True, False):
+            got = orc.attention(Q, K, V, 0.6, causal, seq_ends=ends)
+            for a, b in zip([0] + ends[:-1], ends):
+                want = orc.attention(Q[:, :, a:b], K[:, :, a:b], V[:, :, a:b], 0.6, causal)
+                np.testing.assert_allclose(got[:, :, a:b], want, rtol=1e-14, atol=1e-15)
+            np.testing.assert_array_equal(orc.attention(Q, K, V, 0.6, causal, seq_ends=[S]),
+                                          orc.attention(Q, K, V, 0.6, causal))
+    with pytest.raises(ValueError):
+        orc.attention(Q, K, V, 0.6, True, seq_ends=[5, 13])  # must end at S
+
+
+def test_packed_tuple_counts(orc):
+    """The pages' example: 4,096 positions holding sequences that end at
+    1,024, 2,560 and 4,096.  Cut at every sequence end, only the three
+    diagonal (query block, key block) cells share a sequence; cut at 1,024
+    only, the two blocks hold no common sequence, so the off-diagonal cells
+    drop too."""
+    ends = [1024, 2560, 4096]
+    sp = {"s": [0, 1024, 2560, 4096], "t": [0, 1024, 2560, 4096], "d": [0, 128]}
+    for causal in (("s", "t"), None):
+        rec, seg = orc.tuple_records("sdt", sp, "s", causal=causal, packed=("s", "t", ends))
+        assert rec[:, [0, 2]].tolist() == [[0, 0], [1, 1], [2, 2]] and len(seg) - 1 == 3
+    sp2 = {"s": [0, 1024, 4096], "t": [0, 1024, 4096], "d": [0, 128]}
+    rec, _ = orc.tuple_records("sdt", sp2, "s", causal=None, packed=("s", "t", ends))
+    assert rec[:, [0, 2]].tolist() == [[0, 0], [1, 1]]
+    # without the packing predicate a causal cut keeps the lower triangle
+    rec, _ = orc.tuple_records("sdt", sp, "s", causal=("s", "t"))
+    assert rec.shape[0] == 6
