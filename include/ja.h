@@ -148,7 +148,15 @@ ja_status ja_relation_block(const ja_relation_desc* rel, const int64_t* key, int
  *                   params: "scale=<float>" (default 1/sqrt(|d|); must be
  *                   positive, JA_ERR_SPEC otherwise),
  *                   "causal=<s>,<t>" (key t visible to query s iff t <= s;
- *                   fully masked tuples are dropped at join).
+ *                   fully masked tuples are dropped at join),
+ *                   "packed=<e1>,<e2>,...": independent sequences packed end
+ *                   to end along s and t, ending at the ascending positions
+ *                   e1 < e2 < ...; a key is visible to a query only inside
+ *                   the query's sequence, the join drops (query block, key
+ *                   block) pairs that share no sequence, and a decomposition
+ *                   may split s and t only at sequence ends and must span
+ *                   every sequence (section 3.3, Shardable Indices;
+ *                   JA_ERR_DECOMP otherwise).
  *   op "rmsnorm":   "rd,d->rd": y = x / sqrt(mean_d x^2 + eps) * gain; the
  *                   per-row sum of squares is SUM-aggregated over d blocks,
  *                   then joined 1:1 with x and gain.  params "eps=<float>"

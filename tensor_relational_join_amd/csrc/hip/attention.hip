@@ -66,9 +66,11 @@ __device__ __forceinline__ void at_dma16(at_i32x4_t rsrc, uint32_t lds_byte, uin
 // barrier per step.  Masks are only evaluated on steps that cross the
 // causal diagonal or the end of a key block, and O is rescaled only when
 // some query's running maximum moved.
+template <bool PACKED>
 __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile* __restrict__ tiles, int ntiles,
                                                                const AttnSeg* __restrict__ segs,
                                                                const AttnTuple* __restrict__ tuples,
+                                                               const int32_t* __restrict__ seq_ends, int nseq,
                                                                const uint16_t* __restrict__ Q,
                                                                const uint16_t* __restrict__ K,
                                                                const uint16_t* __restrict__ V,
@@ -88,6 +90,45 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     const int wave_qmin = sg.s_lo + tl.s0 + wave * 32;
     const int wave_qmax = sg.s_lo + min(tl.s0 + wave * 32 + 31, sg.S - 1);
     const int tile_qmax = sg.s_lo + min(tl.s0 + 127, sg.S - 1);
+    // Packed sequences: [seq_lo, seq_hi) of a position's sequence.  A key is
+    // visible to a query only inside the query's sequence; the bounds are
+    // nondecreasing in the position, so the first and last rows of a
+    // wavefront or tile bound its rows'.
+    constexpr bool packed = PACKED;
+    auto seq_of = [&](int pos, int& lo, int& hi) {
+        int a = 0, b = nseq - 1;  // first sequence whose end lies past pos
+        while (a < b) {
+            const int m = (a + b) >> 1;
+            if (seq_ends[m] > pos)
+                b = m;
+            else
+                a = m + 1;
+        }
+        hi = seq_ends[a];
+        lo = a > 0 ? seq_ends[a - 1] : 0;
+    };
+    int qs_lo = 0, qs_hi = 0x7fffffff, w_lo_min = 0, w_lo_max = 0, w_hi_min = 0x7fffffff, w_hi_max = 0x7fffffff;
+    int t_lo_min = 0, t_hi_max = 0x7fffffff;
+    if constexpr (PACKED) {
+        int dummy;
+        seq_of(min(qglob, sg.s_lo + sg.S - 1), qs_lo, qs_hi);
+        seq_of(min(wave_qmin, wave_qmax), w_lo_min, w_hi_min);
+        seq_of(wave_qmax, w_lo_max, w_hi_max);
+        seq_of(sg.s_lo + tl.s0, t_lo_min, dummy);
+        seq_of(tile_qmax, dummy, t_hi_max);
+    }
+    // a tuple's keys [first_key, end_key) that some query row of the tile can see
+    auto first_key = [&](const AttnTuple& tp) { return packed ? max(0, (t_lo_min - tp.t_lo) / AT_KT * AT_KT) : 0; };
+    auto end_key = [&](const AttnTuple& tp) {
+        int e = tp.T;
+        if (causal) e = min(e, tile_qmax - tp.t_lo + 1);
+        if (packed) e = min(e, t_hi_max - tp.t_lo);
+        return e;
+    };
+    auto tuple_steps = [&](const AttnTuple& tp) {
+        const int f = first_key(tp), e = end_key(tp);
+        return e > f ? (e - f + AT_KT - 1) / AT_KT : 0;
+    };
 
     // Q^T fragments (B operand): lane holds Q[query lq][d = 16 st + 8 g .. +7]
     bf16x8_t qf[D / 16];
@@ -107,12 +148,24 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
 
     // steps: (tuple, 64-key offset) pairs some query of the tile can see
     int nsteps = 0;
-    for (int t = sg.t_begin; t < sg.t_end; ++t) {
-        const AttnTuple tp = tuples[t];
-        int n = (tp.T + AT_KT - 1) / AT_KT;
-        if (causal) n = tile_qmax < tp.t_lo ? 0 : min(n, (tile_qmax - tp.t_lo) / AT_KT + 1);
-        nsteps += n;
-    }
+    for (int t = sg.t_begin; t < sg.t_end; ++t) nsteps += tuple_steps(tuples[t]);
+    // a cursor over the steps: enter the first tuple with steps at or after t
+    // (without packing every tuple the walk reaches has steps)
+    auto enter = [&](int& t, int& k) {
+        if constexpr (PACKED) {
+            while (t < sg.t_end && tuple_steps(tuples[t]) == 0) ++t;
+            k = t < sg.t_end ? first_key(tuples[t]) : 0;
+        } else {
+            k = 0;
+        }
+    };
+    auto advance = [&](int& t, int& k, const AttnTuple& tp) {  // tp = tuples[t]
+        k += AT_KT;
+        if (k >= end_key(tp)) {
+            ++t;
+            enter(t, k);
+        }
+    };
 
     // per-lane DMA slots of the K tile (4 per wavefront): key and chunk
     int kkey[4];
@@ -131,6 +184,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
 
     // load cursor
     int lt = sg.t_begin, lkt = 0;
+    enter(lt, lkt);
     auto load_step = [&](int buf) {
         const AttnTuple tp = tuples[lt];
         const uint16_t* kb = K + tp.k_off + (int64_t)kvbh * tp.kv_bhstride;
@@ -157,12 +211,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                 vr[i] = at_buffer_load_x4(rv, key < tp.T ? (key * D + dj * 8) * 2 : (int32_t)0x80000000, 0, 0);
             }
         }
-        // advance the cursor to the next visible step
-        lkt += AT_KT;
-        if (lkt >= tp.T || (causal && tp.t_lo + lkt > tile_qmax)) {
-            lkt = 0;
-            ++lt;
-        }
+        advance(lt, lkt, tp);  // to the next visible step
     };
     // V^T[d][key'] <- vr, converted to fp16; key' swaps the middle quads of
     // each 16 keys, matching the order P^T takes from the S^T accumulators
@@ -192,6 +241,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
 
     // compute cursor (same walk as the load cursor)
     int ct = sg.t_begin, ckt = 0;
+    enter(ct, ckt);
     if (nsteps > 0) {
         load_step(0);
         store_v(0);
@@ -203,7 +253,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
         if (more) load_step(buf ^ 1);
         const AttnTuple tp = tuples[ct];
         const int key0 = tp.t_lo + ckt;  // global index of the step's first key
-        if (!causal || key0 <= wave_qmax) {
+        if ((!causal || key0 <= wave_qmax) && (!packed || (key0 + AT_KT > w_lo_min && key0 < w_hi_max))) {
             const uint16_t* ks = at_lds + buf * AT_STAGE;
             const _Float16* vt = reinterpret_cast<const _Float16*>(ks + AT_KT * D);
             // ---- S^T = K Q^T: two 32-key tiles
@@ -224,14 +274,17 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
             }
             // ---- masks: only where the step crosses the diagonal or the key block's end
             const bool ragged = ckt + AT_KT > tp.T;
-            if (ragged) {
+            const bool seqmask = packed && (key0 < w_lo_max || key0 + AT_KT > w_hi_min);
+            if (ragged || seqmask) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         // acc index r -> key 8 (r / 4) + 4 g + r % 4 inside the 32-key tile
                         const int kk = kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        const bool ok = ckt + kk < tp.T && (!causal || key0 + kk <= qglob);
+                        const int key = key0 + kk;
+                        const bool ok = ckt + kk < tp.T && (!causal || key <= qglob) &&
+                                        (!packed || (key >= qs_lo && key < qs_hi));
                         s[kt][r] = ok ? s[kt][r] : -INFINITY;
                     }
             } else if (causal && key0 + AT_KT - 1 > wave_qmin) {
@@ -302,12 +355,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
             }
         }
         if (more) store_v(buf ^ 1);
-        // advance the compute cursor
-        ckt += AT_KT;
-        if (ckt >= tp.T || (causal && tp.t_lo + ckt > tile_qmax)) {
-            ckt = 0;
-            ++ct;
-        }
+        advance(ct, ckt, tp);  // the compute cursor
         sync_step();
     }
     // ---- finalize: O = acc / l ; lane holds O^T[d = 32 dt + 8 j + 4 g + r][query lq]
@@ -333,14 +381,16 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
 }
 
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
-                            int64_t tuples_off, const void* Q, const void* K, const void* V, void* O, float scale,
-                            int32_t causal, hipStream_t stream) {
+                            int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,
+                            const void* V, void* O, float scale, int32_t causal, hipStream_t stream) {
     const uint8_t* t = (const uint8_t*)table;
     const float scale_log2 = scale * 1.4426950408889634f;
     const unsigned lds = 2u * AT_STAGE * sizeof(uint16_t);
-    hipLaunchKernelGGL(attention_kernel, dim3(ntiles), dim3(AT_THREADS), lds, stream,
+    auto kernel = nseq ? attention_kernel<true> : attention_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(AT_THREADS), lds, stream,
                        (const AttnTile*)(t + tiles_off), ntiles, (const AttnSeg*)(t + segs_off),
-                       (const AttnTuple*)(t + tuples_off), (const uint16_t*)Q, (const uint16_t*)K,
+                       (const AttnTuple*)(t + tuples_off), nseq ? (const int32_t*)(t + seq_off) : nullptr, nseq,
+                       (const uint16_t*)Q, (const uint16_t*)K,
                        (const uint16_t*)V, (uint16_t*)O, scale_log2, causal);
     return hipGetLastError();
 }

@@ -140,6 +140,22 @@ static ja_status parse_params(const char* params, ja_spec* s) {
                 if (x < 0) return fail(JA_ERR_SPEC, "eps must be >= 0");
                 s->eps = x;
             }
+        } else if (k == "packed") {
+            // ascending positive sequence ends, comma separated
+            s->packed.clear();
+            size_t q = 0;
+            while (q <= v.size()) {
+                size_t c = v.find(',', q);
+                if (c == std::string::npos) c = v.size();
+                const std::string num = v.substr(q, c - q);
+                char* e = nullptr;
+                const long long x = std::strtoll(num.c_str(), &e, 10);
+                if (num.empty() || !e || *e || x <= 0 || (!s->packed.empty() && x <= s->packed.back()) ||
+                    x > ((int64_t)1 << 31) - 1)
+                    return fail(JA_ERR_SPEC, "packed expects ascending positive sequence ends");
+                s->packed.push_back(x);
+                q = c + 1;
+            }
         } else if (k == "causal") {
             if (v.size() != 3 || v[1] != ',') return fail(JA_ERR_SPEC, "causal expects '<s>,<t>'");
             s->causal = true;
@@ -225,6 +241,7 @@ static ja_status parse_spec(const char* einsum, const char* op, const char* para
     } else {
         return fail(JA_ERR_SPEC, "unknown op " + o);
     }
+    if (s->kind != JA_OP_ATTENTION && !s->packed.empty()) return fail(JA_ERR_SPEC, "packed applies to attention only");
     if (!s->causal || s->kind == JA_OP_ATTENTION) return JA_OK;
     return fail(JA_ERR_SPEC, "causal applies to attention only");
 }
@@ -251,6 +268,12 @@ ja_status build_tuples(const ja_spec* s, const ja_decomp* d, ja_tuples& t) {
         is = s->letter_index(s->causal_s);
         it = s->letter_index(s->causal_t);
     }
+    int ps = -1, pt = -1;  // packed sequences: the query and key position letters
+    if (!s->packed.empty()) {
+        const std::string &q = s->ins[0], &k = s->ins[1];
+        ps = s->letter_index(q[q.size() - 2]);
+        pt = s->letter_index(k[k.size() - 2]);
+    }
     t.nl = nl;
     t.rec.clear();
     t.seg.assign(1, 0);
@@ -262,6 +285,13 @@ ja_status build_tuples(const ja_spec* s, const ja_decomp* d, ja_tuples& t) {
         if (s->causal) {
             // drop the tuple when its first key comes after its last query
             if (d->sp[it][idx[it]] >= d->sp[is][idx[is] + 1]) keep = false;
+        }
+        if (keep && ps >= 0) {
+            // drop the tuple when its query and key intervals share no sequence
+            // (both are unions of whole sequences, so: when they do not overlap)
+            const int64_t slo = d->sp[ps][idx[ps]], shi = d->sp[ps][idx[ps] + 1];
+            const int64_t tlo = d->sp[pt][idx[pt]], thi = d->sp[pt][idx[pt] + 1];
+            if (std::max(slo, tlo) >= std::min(shi, thi)) keep = false;
         }
         if (keep) {
             bool newseg = n > 0;
@@ -393,6 +423,22 @@ ja_status ja_decomp_create(const ja_spec* s, const int64_t* extents, const int32
         if (d->sp[id].size() != 2) {
             delete d;
             return fail(JA_ERR_DECOMP, "attention: the head-dimension letter cannot be split");
+        }
+        if (!s->packed.empty()) {
+            // packed sequences: the sequence letters span every sequence and may be
+            // split only at sequence ends (section 3.3)
+            const std::string &q = s->ins[0], &k = s->ins[1];
+            for (char c : {q[q.size() - 2], k[k.size() - 2]}) {
+                const std::vector<int64_t>& sp = d->sp[s->letter_index(c)];
+                bool ok = sp.back() == s->packed.back();
+                for (size_t i = 1; ok && i + 1 < sp.size(); ++i)
+                    ok = std::binary_search(s->packed.begin(), s->packed.end(), sp[i]);
+                if (!ok) {
+                    delete d;
+                    return fail(JA_ERR_DECOMP, std::string("attention: letter ") + c +
+                                                   " must end at the last sequence end and be split only at sequence ends");
+                }
+            }
         }
     }
     *out = d;

@@ -64,6 +64,7 @@ struct ja_spec {
     bool has_scale = false;
     bool causal = false;
     char causal_s = 0, causal_t = 0;
+    std::vector<int64_t> packed;  // attention: ascending ends of sequences packed along the s and t letters
     double eps = 1e-6;
     int letter_index(char c) const {
         auto p = letters.find(c);
@@ -93,9 +94,10 @@ namespace ja {
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
                        const void* A, const void* B, void* C, int32_t in_dtype, int32_t out_dtype,
                        int32_t a_layout, int32_t b_layout, int32_t dma, hipStream_t stream);
+// seq_off / nseq: the packed sequences' int32 end positions in the table (nseq = 0: not packed)
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
-                            int64_t tuples_off, const void* Q, const void* K, const void* V, void* O,
-                            float scale, int32_t causal, hipStream_t stream);
+                            int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,
+                            const void* V, void* O, float scale, int32_t causal, hipStream_t stream);
 hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
                           int64_t rows, int32_t D, int32_t W, const void* x, const void* gain, void* y, float eps,
                           int32_t vec, hipStream_t stream);

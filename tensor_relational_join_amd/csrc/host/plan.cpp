@@ -10,6 +10,7 @@
 // the recompose is in place, since every aggregated block is written straight
 // into its slot of the output relation.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 
@@ -35,6 +36,8 @@ struct ja_plan {
     // attention
     float scale = 0.f;
     int32_t causal = 0;
+    int64_t seq_off = 0;  // packed sequences: int32 sequence ends in the table
+    int32_t nseq = 0;
     // rmsnorm
     int64_t rsplit_off = 0, nblk_off = 0;
     int32_t nrb = 0, ndb = 0, D = 0, norm_vec = 0, norm_w = 0;
@@ -312,11 +315,21 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
         g.t_end = (int32_t)t.seg[sg + 1];
         for (int32_t bh = 0; bh < nbh; ++bh)
             for (int32_t s0 = 0; s0 < S; s0 += ATTN_TQ) {
-                // work estimate: keys visible to the tile's last query row
+                // work estimate: keys visible to the tile's last query row (inside
+                // the sequences of the tile's rows when sequences are packed)
                 int64_t last = g.s_lo + std::min<int64_t>(S, s0 + ATTN_TQ) - 1, w = 0;
+                int64_t klo = 0, khi = INT64_MAX;
+                if (!s->packed.empty()) {
+                    auto e1 = std::upper_bound(s->packed.begin(), s->packed.end(), (int64_t)g.s_lo + s0);
+                    klo = e1 == s->packed.begin() ? 0 : *(e1 - 1);
+                    auto e2 = std::upper_bound(s->packed.begin(), s->packed.end(), last);
+                    khi = e2 == s->packed.end() ? s->packed.back() : *e2;
+                }
                 for (int32_t k = g.t_begin; k < g.t_end; ++k) {
-                    int64_t vis = p->causal ? std::min<int64_t>(tuples[k].T, last - tuples[k].t_lo + 1) : tuples[k].T;
-                    w += std::max<int64_t>(vis, 0);
+                    int64_t a = std::max<int64_t>(tuples[k].t_lo, klo);
+                    int64_t b = std::min<int64_t>((int64_t)tuples[k].t_lo + tuples[k].T, khi);
+                    if (p->causal) b = std::min<int64_t>(b, last + 1);
+                    w += std::max<int64_t>(b - a, 0);
                 }
                 work.push_back({{(int32_t)sg, bh, s0, 0}, w});
             }
@@ -331,6 +344,11 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
     p->ntiles = (int32_t)tiles.size();
     p->segs_off = put(p->table, segs);
     p->tuples_off = put(p->table, tuples);
+    if (!s->packed.empty()) {
+        std::vector<int32_t> ends(s->packed.begin(), s->packed.end());
+        p->seq_off = put(p->table, ends);
+        p->nseq = (int32_t)ends.size();
+    }
     return JA_OK;
 }
 
@@ -472,8 +490,9 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
             break;
         case JA_OP_ATTENTION:
             if (p->ntiles == 0) return JA_OK;
-            JA_TRY_HIP(launch_attention(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, in_ptrs[0],
-                                        in_ptrs[1], in_ptrs[2], out_ptr, p->scale, p->causal, hs));
+            JA_TRY_HIP(launch_attention(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, p->seq_off,
+                                        p->nseq, in_ptrs[0], in_ptrs[1], in_ptrs[2], out_ptr, p->scale, p->causal,
+                                        hs));
             break;
         case JA_OP_RMSNORM:
             JA_TRY_HIP(launch_rmsnorm(p->dev, p->rsplit_off, p->nrb, p->nblk_off, p->ndb, p->rows, p->D, p->norm_w,

@@ -302,6 +302,36 @@ def test_gqa_attention_8k_sampled_rows(dev, orc):
     assert np.isfinite(got).all()
 
 
+# ------------------------------------------------------------------ packed sequences
+
+PACKED_CASES = [
+    # (heads q, heads kv, S, sequence ends, s and t cuts, causal)
+    (2, 2, 4096, [1024, 2560, 4096], [0, 1024, 2560, 4096], True),   # the pages' section 3.3 example
+    (2, 2, 3000, [700, 1900, 3000], [0, 700, 3000], True),          # a block of two sequences; ends mid-tile
+    (1, 1, 3000, [700, 1900, 3000], [0, 3000], False),              # one block of three, bidirectional
+    (4, 2, 2000, [300, 301, 1250, 2000], [0, 301, 2000], True),     # grouped-query; a one-token sequence
+]
+
+
+@pytest.mark.parametrize("H,HK,S,ends,cuts,causal", PACKED_CASES)
+def test_packed_attention(dev, orc, H, HK, S, ends, cuts, causal):
+    """Sequences packed end to end along s and t (the pages' section 3.3):
+    no query sees a key of another sequence, whichever sequence ends the
+    decomposition cuts at."""
+    R = H // HK
+    sp = {"b": [0, 1], "g": _eq(HK, HK), "r": [0, R], "s": cuts, "t": cuts, "d": [0, 128]}
+    Q = synth.normal_bf16(15, 0, (1, HK, R, S, 128))
+    K = synth.normal_bf16(15, 1, (1, HK, S, 128))
+    V = synth.normal_bf16(15, 2, (1, HK, S, 128))
+    params = "packed=" + ",".join(map(str, ends)) + (";causal=s,t" if causal else "")
+    got, o, _ = _run(dev, orc, "bgrsd,bgtd,bgtd->bgrsd", "attention", sp, [Q, K, V], params=params)
+    o.close()
+    want = orc.attention(orc.bf16_to_f64(Q).reshape(1, H, S, 128), orc.bf16_to_f64(K), orc.bf16_to_f64(V),
+                         1.0 / np.sqrt(128.0), causal, seq_ends=ends)
+    assert rel_frobenius(got.reshape(1, H, S, 128), orc.round_bf16(want)) <= BF16_TOL
+    assert np.isfinite(got).all()
+
+
 # ------------------------------------------------------------------ RMSNorm, SwiGLU, add
 
 @pytest.mark.parametrize("R,D,rsp,dsp", [

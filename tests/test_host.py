@@ -69,6 +69,51 @@ CASES = [
 ]
 
 
+PACKED_CASES = [
+    # the pages' section 3.3 example: sequences ending at 1,024, 2,560 and 4,096, cut at every end
+    ({"b": [0, 2], "h": [0, 1, 2], "s": [0, 1024, 2560, 4096], "t": [0, 1024, 2560, 4096], "d": [0, 128]},
+     [1024, 2560, 4096], True),
+    # cut at one end only: the second block holds two sequences
+    ({"b": [0, 1], "h": [0, 2], "s": [0, 1024, 4096], "t": [0, 1024, 4096], "d": [0, 128]},
+     [1024, 2560, 4096], True),
+    # different cuts on the query and key letters, not causal
+    ({"b": [0, 1], "h": [0, 1], "s": [0, 700, 3000], "t": [0, 700, 1900, 3000], "d": [0, 128]},
+     [700, 1900, 3000], False),
+]
+
+
+@pytest.mark.parametrize("splits,ends,causal", PACKED_CASES)
+def test_packed_tuple_lists_match_oracle(B, orc, splits, ends, causal):
+    params = "packed=" + ",".join(map(str, ends)) + (";causal=s,t" if causal else "")
+    letters, rec, seg = _tuples(B, "bhsd,bhtd,bhtd->bhsd", "attention", splits, params)
+    o_rec, o_seg = orc.tuple_records(list(letters), splits, group_by=list("bhsd"),
+                                     causal=("s", "t") if causal else None, packed=("s", "t", ends))
+    assert np.array_equal(rec, o_rec) and np.array_equal(seg, o_seg)
+
+
+def test_packed_sequence_split_points(B):
+    """A sequence letter may be split only at sequence ends, and must span
+    every sequence (the pages' section 3.3)."""
+    s = B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", "packed=1024,2560,4096;causal=s,t")
+    try:
+        ok = B.ja_decomp_create(s, [1, 1, 4096, 128, 4096], [1, 1, 2, 1, 3],
+                                [[0, 1], [0, 1], [0, 2560, 4096], [0, 128], [0, 1024, 2560, 4096]])
+        B.ja_decomp_destroy(ok)
+        for sp, ext in (([0, 2048, 4096], 4096), ([0, 1024, 3000], 3000)):
+            with pytest.raises(B.JaError) as e:
+                B.ja_decomp_create(s, [1, 1, ext, 128, ext], [1, 1, len(sp) - 1, 1, len(sp) - 1],
+                                   [[0, 1], [0, 1], sp, [0, 128], sp])
+            assert e.value.name == "JA_ERR_DECOMP"
+    finally:
+        B.ja_spec_destroy(s)
+    for bad in ("packed=0,10", "packed=10,5", "packed=", "packed=4,x"):
+        with pytest.raises(B.JaError) as e:
+            B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", bad)
+        assert e.value.name == "JA_ERR_SPEC"
+    with pytest.raises(B.JaError):
+        B.ja_spec_create("ij,jk->ik", "contract", "packed=4")
+
+
 @pytest.mark.parametrize("einsum,op,splits,params,group,causal", CASES)
 def test_tuple_lists_match_oracle(B, orc, einsum, op, splits, params, group, causal):
     letters, rec, seg = _tuples(B, einsum, op, splits, params)
