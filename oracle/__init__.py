@@ -76,6 +76,8 @@ def _load():
         lib.orc_num_threads.restype = ctypes.c_int
         lib.orc_bf16_to_f64.argtypes = [_u16p, ctypes.c_int64, _f64p]
         lib.orc_f64_to_bf16.argtypes = [_f64p, ctypes.c_int64, _u16p]
+        lib.orc_f16_to_f64.argtypes = [_u16p, ctypes.c_int64, _f64p]
+        lib.orc_f64_to_f16.argtypes = [_f64p, ctypes.c_int64, _u16p]
         lib.orc_einsum2.argtypes = [ctypes.c_char_p, _i64p, _f64p, _f64p, _f64p]
         lib.orc_einsum2.restype = ctypes.c_int
         lib.orc_einsum2_points.argtypes = [ctypes.c_char_p, _i64p, _f64p, _f64p, ctypes.c_int64, _i64p, _f64p]
@@ -125,6 +127,27 @@ def f64_to_bf16(x) -> np.ndarray:
 def round_bf16(x) -> np.ndarray:
     """The float64 value of the bfloat16 nearest to x."""
     return bf16_to_f64(f64_to_bf16(x))
+
+
+def f16_to_f64(h) -> np.ndarray:
+    """Exact decode of IEEE half bit patterns (uint16) to float64."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float64)
+    _load().orc_f16_to_f64(_ptr(h, _u16p), h.size, _ptr(out, _f64p))
+    return out
+
+
+def f64_to_f16(x) -> np.ndarray:
+    """Round float64 values to IEEE half bit patterns, nearest-even."""
+    x = _f64(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_f64_to_f16(_ptr(x, _f64p), x.size, _ptr(out, _u16p))
+    return out
+
+
+def round_f16(x) -> np.ndarray:
+    """The float64 value of the IEEE half nearest to x."""
+    return f16_to_f64(f64_to_f16(x))
 
 
 # --------------------------------------------------------------------------

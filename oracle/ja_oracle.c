@@ -5,7 +5,8 @@
  * It shares no code, header or constant with the HIP path.
  *
  * Everything here computes in IEEE double precision.  Rounding to bfloat16
- * happens only where a relation is materialised, via orc_f64_to_bf16().
+ * (or IEEE half) happens only where a relation is materialised, via
+ * orc_f64_to_bf16() (orc_f64_to_f16()).
  *
  * Sources (the pages: "Every Kernel Is a Join: Automatic Multi-GPU Parallelism
  * for AI Computations in Einsummable", paperpeel full text):
@@ -79,6 +80,55 @@ static uint16_t bf16_encode(double x) {
     double q = nearbyint(ldexp(a, 133));
     if (q >= 128.0) return sign | (uint16_t)(1 << 7); /* rounds up to min normal */
     return sign | (uint16_t)q;
+}
+
+/* IEEE binary16 (half): 1 sign bit, 5 exponent bits (bias 15), 10 stored
+ * mantissa bits.  Decoding is exact. */
+static double f16_decode(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (e == 0x1F) {
+        v = (m == 0) ? INFINITY : NAN;
+    } else if (e == 0) {
+        v = ldexp((double)m, -14 - 10); /* subnormal: m * 2^-24 */
+    } else {
+        v = ldexp((double)(1024 + m), e - 15 - 10);
+    }
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16, ties to even mantissa, once,
+ * directly from double; magnitudes that round past 65504 become infinity. */
+static uint16_t f16_encode(double x) {
+    if (isnan(x)) return 0x7E00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a)) return sign | 0x7C00;
+    if (a == 0.0) return sign;
+    int E;
+    double f = frexp(a, &E); /* a = f * 2^E, f in [0.5, 1) */
+    if (E - 1 >= -14) {        /* normal: a = (1.m) * 2^(E-1) */
+        double r = nearbyint(ldexp(f, 11)); /* 11 significant bits, RNE */
+        if (r == 2048.0) { r = 1024.0; E += 1; }
+        int he = (E - 1) + 15;
+        if (he >= 31) return sign | 0x7C00;
+        return sign | (uint16_t)(he << 10) | (uint16_t)((int)r - 1024);
+    }
+    double q = nearbyint(ldexp(a, 24)); /* subnormal range: multiples of 2^-24 */
+    if (q >= 1024.0) return sign | (uint16_t)(1 << 10);
+    return sign | (uint16_t)q;
+}
+
+void orc_f16_to_f64(const uint16_t* in, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_decode(in[i]);
+}
+
+void orc_f64_to_f16(const double* in, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_encode(in[i]);
 }
 
 void orc_bf16_to_f64(const uint16_t* in, int64_t n, double* out) {

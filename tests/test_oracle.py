@@ -528,3 +528,33 @@ def test_packed_tuple_counts(orc):
     # without the packing predicate a causal cut keeps the lower triangle
     rec, _ = orc.tuple_records("sdt", sp, "s", causal=("s", "t"))
     assert rec.shape[0] == 6
+
+
+# ---------------------------------------------------------------- IEEE half (fp16 relations)
+
+def test_f16_known_encodings(orc):
+    cases = {
+        1.0: 0x3C00, -2.0: 0xC000, 65504.0: 0x7BFF,         # largest finite half
+        65519.0: 0x7BFF, 65520.0: 0x7C00,                   # the tie at the top rounds to even: infinity
+        2.0 ** -14: 0x0400, 2.0 ** -24: 0x0001,             # smallest normal, smallest subnormal
+        2.0 ** -25: 0x0000, 3 * 2.0 ** -25: 0x0002,         # ties to even in the subnormal range
+        1.0 + 2.0 ** -11: 0x3C00, 1.0 + 3 * 2.0 ** -11: 0x3C02,  # ties to even at 1
+        0.1: 0x2E66, -0.0: 0x8000,
+    }
+    xs = np.array(list(cases.keys()))
+    got = orc.f64_to_f16(xs)
+    assert [int(v) for v in got] == list(cases.values())
+    assert orc.f64_to_f16(np.array([np.inf]))[0] == 0x7C00
+    assert orc.f64_to_f16(np.array([np.nan]))[0] & 0x7FFF > 0x7C00
+
+
+def test_f16_all_patterns_and_independent_route(orc):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = orc.f16_to_f64(h)
+    fin = np.isfinite(v)
+    assert np.array_equal(orc.f64_to_f16(v[fin]), h[fin])          # every finite pattern round trips
+    assert np.array_equal(v[fin], h[fin].view(np.float16).astype(np.float64))  # numpy's decode
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(200000) * s for s in (1e-6, 1e-3, 1.0, 1e3, 6e4)])
+    with np.errstate(over="ignore"):  # the widest scale overflows to infinity on both routes
+        assert np.array_equal(orc.f64_to_f16(x), x.astype(np.float16).view(np.uint16))  # numpy's RNE encode
