@@ -201,8 +201,11 @@ void ja_tuples_destroy(ja_tuples* tuples);
 
 /* Validate the relations against the spec and decomposition (each input and
  * the output must be blocked exactly as the decomposition cuts their letters;
- * dtypes: contract f32 x f32 -> f32 or bf16 x bf16 -> bf16 / f32; attention,
- * rmsnorm, swiglu, add: bf16), run the join, and build the device tables. */
+ * dtypes: contract f32 x f32 -> f32, bf16 x bf16 -> bf16 / f32 or
+ * f16 x f16 -> f16 / f32, accumulating in f32; attention, rmsnorm, swiglu,
+ * add: every relation bf16, or every relation f16 -- JA_ERR_DTYPE
+ * otherwise), run the join, and build the device tables.  16-bit outputs are
+ * rounded to nearest even once from f32. */
 ja_status ja_plan_create(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
                          int32_t n_in, const ja_relation_desc* out, ja_plan** plan);
 /* table_bytes: device buffer size for ja_plan_upload; workspace_bytes: the

@@ -66,7 +66,7 @@ __device__ __forceinline__ void at_dma16(at_i32x4_t rsrc, uint32_t lds_byte, uin
 // barrier per step.  Masks are only evaluated on steps that cross the
 // causal diagonal or the end of a key block, and O is rescaled only when
 // some query's running maximum moved.
-template <bool PACKED>
+template <bool PACKED, bool F16>
 __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile* __restrict__ tiles, int ntiles,
                                                                const AttnSeg* __restrict__ segs,
                                                                const AttnTuple* __restrict__ tuples,
@@ -213,8 +213,9 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
         }
         advance(lt, lkt, tp);  // to the next visible step
     };
-    // V^T[d][key'] <- vr, converted to fp16; key' swaps the middle quads of
-    // each 16 keys, matching the order P^T takes from the S^T accumulators
+    // V^T[d][key'] <- vr, in fp16 (converted from bf16, moved as is from
+    // fp16); key' swaps the middle quads of each 16 keys, matching the order
+    // P^T takes from the S^T accumulators
     auto store_v = [&](int buf) {
         _Float16* vt = reinterpret_cast<_Float16*>(at_lds + buf * AT_STAGE + AT_KT * D);
         const int hgrp = kg >> 2, q = kg & 3;
@@ -228,13 +229,21 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
         for (int w = 0; w < 4; ++w)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-                h4 hv = {(_Float16)(e ? bf16hi_to_f32(r0[w]) : bf16lo_to_f32(r0[w])),
-                         (_Float16)(e ? bf16hi_to_f32(r1[w]) : bf16lo_to_f32(r1[w])),
-                         (_Float16)(e ? bf16hi_to_f32(r2[w]) : bf16lo_to_f32(r2[w])),
-                         (_Float16)(e ? bf16hi_to_f32(r3[w]) : bf16lo_to_f32(r3[w]))};
                 const int d = dj * 8 + 2 * w + e;
-                *reinterpret_cast<h4*>(vt + at_voff(d, c) + half * 4) = hv;
+                if constexpr (F16) {
+                    // already fp16: move the e-th half of word w of the 4 keys
+                    const uint32_t sh = 16 * e, mk = 0xffffu;
+                    *reinterpret_cast<uint2*>(vt + at_voff(d, c) + half * 4) =
+                        make_uint2(((r0[w] >> sh) & mk) | (((r1[w] >> sh) & mk) << 16),
+                                   ((r2[w] >> sh) & mk) | (((r3[w] >> sh) & mk) << 16));
+                } else {
+                    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                    h4 hv = {(_Float16)(e ? bf16hi_to_f32(r0[w]) : bf16lo_to_f32(r0[w])),
+                             (_Float16)(e ? bf16hi_to_f32(r1[w]) : bf16lo_to_f32(r1[w])),
+                             (_Float16)(e ? bf16hi_to_f32(r2[w]) : bf16lo_to_f32(r2[w])),
+                             (_Float16)(e ? bf16hi_to_f32(r3[w]) : bf16lo_to_f32(r3[w]))};
+                    *reinterpret_cast<h4*>(vt + at_voff(d, c) + half * 4) = hv;
+                }
             }
     };
     auto sync_step = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
@@ -270,7 +279,11 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                 for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
                 for (int st = 0; st < D / 16; ++st)
-                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s[kt], 0, 0, 0);
+                    if constexpr (F16)
+                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, kf[st]),
+                                                                       __builtin_bit_cast(h8_t, qf[st]), s[kt], 0, 0, 0);
+                    else
+                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s[kt], 0, 0, 0);
             }
             // ---- masks: only where the step crosses the diagonal or the key block's end
             const bool ragged = ckt + AT_KT > tp.T;
@@ -373,8 +386,8 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
             for (int j = 0; j < 4; ++j) {
                 const int d = dt * 32 + 8 * j + 4 * g;
                 uint2 w;
-                w.x = pack_bf16x2(oacc[dt][4 * j + 0] * inv, oacc[dt][4 * j + 1] * inv);
-                w.y = pack_bf16x2(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
+                w.x = pack_h16x2<F16>(oacc[dt][4 * j + 0] * inv, oacc[dt][4 * j + 1] * inv);
+                w.y = pack_h16x2<F16>(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
                 *reinterpret_cast<uint2*>(op + d) = w;
             }
     }
@@ -382,11 +395,12 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
 
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
                             int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,
-                            const void* V, void* O, float scale, int32_t causal, hipStream_t stream) {
+                            const void* V, void* O, float scale, int32_t causal, int32_t f16, hipStream_t stream) {
     const uint8_t* t = (const uint8_t*)table;
     const float scale_log2 = scale * 1.4426950408889634f;
     const unsigned lds = 2u * AT_STAGE * sizeof(uint16_t);
-    auto kernel = nseq ? attention_kernel<true> : attention_kernel<false>;
+    auto kernel = nseq ? (f16 ? attention_kernel<true, true> : attention_kernel<true, false>)
+                       : (f16 ? attention_kernel<false, true> : attention_kernel<false, false>);
     hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(AT_THREADS), lds, stream,
                        (const AttnTile*)(t + tiles_off), ntiles, (const AttnSeg*)(t + segs_off),
                        (const AttnTuple*)(t + tuples_off), nseq ? (const int32_t*)(t + seq_off) : nullptr, nseq,

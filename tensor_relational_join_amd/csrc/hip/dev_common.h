@@ -29,6 +29,54 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 // Two floats -> two bfloat16 packed in one dword (lo = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
 
+// IEEE half bits <-> float: exact widening; narrowing rounds to nearest even
+// (the default rounding mode of v_cvt_f16_f32).
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) { return f32_to_f16(a) | (f32_to_f16(b) << 16); }
+
+// The 16-bit element formats the kernels read and write: F16 selects IEEE
+// half, otherwise bfloat16.
+template <bool F16>
+__device__ __forceinline__ float h16_to_f32(uint32_t h) {
+    if constexpr (F16)
+        return f16_to_f32(h);
+    else
+        return bf16_to_f32(h);
+}
+template <bool F16>
+__device__ __forceinline__ uint32_t f32_to_h16(float f) {
+    if constexpr (F16)
+        return f32_to_f16(f);
+    else
+        return f32_to_bf16(f);
+}
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_h16x2(float a, float b) {
+    return f32_to_h16<F16>(a) | (f32_to_h16<F16>(b) << 16);
+}
+// low / high 16-bit element of a dword, widened to float
+template <bool F16>
+__device__ __forceinline__ float h16lo_to_f32(uint32_t w) {
+    return F16 ? f16_to_f32(w & 0xffffu) : bf16lo_to_f32(w);
+}
+template <bool F16>
+__device__ __forceinline__ float h16hi_to_f32(uint32_t w) {
+    return F16 ? f16_to_f32(w >> 16) : bf16hi_to_f32(w);
+}
+
+// 16x16x32 MFMA on 16-byte fragments of 8 elements in either format.
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Workgroup index -> work-item index such that each XCD (workgroups are
 // dealt to the 8 XCDs round-robin) receives a contiguous range of the work
 // list, keeping neighbouring tiles in one L2.

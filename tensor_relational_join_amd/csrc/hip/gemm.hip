@@ -126,7 +126,7 @@ using Stage = typename std::conditional<TRANS, TransStage<R, BK, NT>, DirectStag
 // with the B fragment as its first operand, so each accumulator holds C^T:
 // lane l owns C[m = l % 16][n = 4 (l / 16) .. +3], four adjacent columns that
 // leave in one store.
-template <int BM, int BN, int BK, int WM, int WN, int AL, int BL, int OUT_BF16>
+template <int BM, int BN, int BK, int WM, int WN, int AL, int BL, bool IN_F16, bool OUT16>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* __restrict__ tiles, int ntiles,
                                                                 const GemmSeg* __restrict__ segs,
                                                                 const GemmTuple* __restrict__ tuples,
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* 
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma16x16x32<IN_F16>(bfr[j], af[i], acc[i][j]);
         }
         if (!more) break;
         sa.store(As(buf ^ 1), tid);
@@ -221,17 +221,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* 
             const int64_t off = cbase + (int64_t)row * sg.ldc + col;
             const f32x4_t a = acc[i][j];
             if (col + 4 <= sg.N && (off & 3) == 0) {
-                if (OUT_BF16)
-                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_bf16x2(a[0], a[1]),
-                                                                               pack_bf16x2(a[2], a[3]));
+                if (OUT16)
+                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_h16x2<IN_F16>(a[0], a[1]),
+                                                                               pack_h16x2<IN_F16>(a[2], a[3]));
                 else
                     *reinterpret_cast<float4*>((float*)C + off) = make_float4(a[0], a[1], a[2], a[3]);
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (col + r < sg.N) {
-                        if (OUT_BF16)
-                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_bf16(a[r]);
+                        if (OUT16)
+                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_h16<IN_F16>(a[r]);
                         else
                             ((float*)C)[off + r] = a[r];
                     }
@@ -367,7 +367,7 @@ __device__ __forceinline__ void wait_loads_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(LEFT) : "memory");
 }
 
-template <int BM, int BN, int NS, int WM, int WN, int AL, int BL, int OUT_BF16>
+template <int BM, int BN, int NS, int WM, int WN, int AL, int BL, bool IN_F16, bool OUT16>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTile* __restrict__ tiles, int ntiles,
                                                                     const GemmSeg* __restrict__ segs,
                                                                     const GemmTuple* __restrict__ tuples,
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
             if (i >= i0 && i < i1)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb[j], ca[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma16x16x32<IN_F16>(cb[j], ca[i], acc[i][j]);
     };
     auto step = [&](int it, bf16x8_t* ca, bf16x8_t* cb, bf16x8_t* na, bf16x8_t* nb) {
         wait_stage(it + 1);
@@ -517,17 +517,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
             const int64_t off = cbase + (int64_t)row * sg.ldc + col;
             const f32x4_t a = acc[i][j];
             if (col + 4 <= sg.N && (off & 3) == 0) {
-                if (OUT_BF16)
-                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_bf16x2(a[0], a[1]),
-                                                                               pack_bf16x2(a[2], a[3]));
+                if (OUT16)
+                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_h16x2<IN_F16>(a[0], a[1]),
+                                                                               pack_h16x2<IN_F16>(a[2], a[3]));
                 else
                     *reinterpret_cast<float4*>((float*)C + off) = make_float4(a[0], a[1], a[2], a[3]);
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (col + r < sg.N) {
-                        if (OUT_BF16)
-                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_bf16(a[r]);
+                        if (OUT16)
+                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_h16<IN_F16>(a[r]);
                         else
                             ((float*)C)[off + r] = a[r];
                     }
@@ -590,38 +590,55 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmTile* __restric
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int AL, int BL, int OB>
+template <int AL, int BL, bool F16, bool OUT16>
 static void launch_bf16(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples, const void* A,
                         const void* B, void* C, hipStream_t s) {
     constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, BK = GEMM_BF16_TK, WM = 2, WN = 4;
     constexpr unsigned lds = 2u * (BM + BN) * BK * sizeof(uint16_t);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, AL, BL, OB>), dim3(ntiles), dim3(WM * WN * 64), lds, s,
-                       tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, AL, BL, F16, OUT16>), dim3(ntiles), dim3(WM * WN * 64),
+                       lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C);
 }
 
-template <int AL, int BL, int OB>
+template <int AL, int BL, bool F16, bool OUT16>
 static void launch_bf16_dma(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples,
                             const void* A, const void* B, void* C, hipStream_t s) {
     constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, NS = GEMM_DMA_STAGES, WM = 2, WN = 4;
     constexpr unsigned lds = (unsigned)NS * (BM + BN) * 32 * sizeof(uint16_t);
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, OB>), dim3(ntiles), dim3(WM * WN * 64), lds,
-                       s, tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, F16, OUT16>), dim3(ntiles),
+                       dim3(WM * WN * 64), lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A,
+                       (const uint16_t*)B, C);
 }
 
-template <int AL, int BL>
-static void launch_bf16_out(int out_bf16, int dma, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
+// 16-bit inputs (bf16 or, with F16, IEEE half) into fp32 accumulators;
+// out16 writes the output in the input's format, otherwise fp32.
+template <int AL, int BL, bool F16>
+static void launch_bf16_out(int out16, int dma, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
                             const GemmTuple* tuples, const void* A, const void* B, void* C, hipStream_t s) {
     if (dma) {
-        if (out_bf16)
-            launch_bf16_dma<AL, BL, 1>(tiles, ntiles, segs, tuples, A, B, C, s);
+        if (out16)
+            launch_bf16_dma<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, s);
         else
-            launch_bf16_dma<AL, BL, 0>(tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16_dma<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, s);
     } else {
-        if (out_bf16)
-            launch_bf16<AL, BL, 1>(tiles, ntiles, segs, tuples, A, B, C, s);
+        if (out16)
+            launch_bf16<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, s);
         else
-            launch_bf16<AL, BL, 0>(tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, s);
     }
+}
+
+template <bool F16>
+static void launch_h16(int a_layout, int b_layout, int out16, int dma, const GemmTile* tiles, int ntiles,
+                       const GemmSeg* segs, const GemmTuple* tuples, const void* A, const void* B, void* C,
+                       hipStream_t s) {
+    if (a_layout == JA_A_MK && b_layout == JA_B_KN)
+        launch_bf16_out<JA_A_MK, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+    else if (a_layout == JA_A_MK && b_layout == JA_B_NK)
+        launch_bf16_out<JA_A_MK, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+    else if (a_layout == JA_A_KM && b_layout == JA_B_KN)
+        launch_bf16_out<JA_A_KM, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+    else
+        launch_bf16_out<JA_A_KM, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
 }
 
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
@@ -631,16 +648,12 @@ hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int
     const GemmTile* tiles = (const GemmTile*)(t + tiles_off);
     const GemmSeg* segs = (const GemmSeg*)(t + segs_off);
     const GemmTuple* tuples = (const GemmTuple*)(t + tuples_off);
-    if (in_dtype == JA_BF16) {
-        const int ob = out_dtype == JA_BF16;
-        if (a_layout == JA_A_MK && b_layout == JA_B_KN)
-            launch_bf16_out<JA_A_MK, JA_B_KN>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
-        else if (a_layout == JA_A_MK && b_layout == JA_B_NK)
-            launch_bf16_out<JA_A_MK, JA_B_NK>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
-        else if (a_layout == JA_A_KM && b_layout == JA_B_KN)
-            launch_bf16_out<JA_A_KM, JA_B_KN>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+    if (in_dtype == JA_BF16 || in_dtype == JA_F16) {
+        const int out16 = out_dtype != JA_F32;
+        if (in_dtype == JA_F16)
+            launch_h16<true>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
         else
-            launch_bf16_out<JA_A_KM, JA_B_NK>(ob, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_h16<false>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
     } else {
 #define JA_F32_CASE(al, bl)                                                                                       \
     hipLaunchKernelGGL((gemm_f32_kernel<al, bl>), dim3(ntiles), dim3(256), 0, s, tiles, ntiles, segs, tuples,     \

@@ -105,11 +105,12 @@ hipError_t launch_repart(const void* table, int64_t ntasks, const void* src, voi
 
 // ---------------------------------------------------------------- 1:1 joins
 // The three relations are identically blocked, so the join is a zip of the
-// flat buffers.  Each thread handles ZIP_V vectors of 8 bf16.
+// flat buffers.  Each thread handles ZIP_V vectors of 8 16-bit elements
+// (bf16, or IEEE half with F16).
 constexpr int ZIP_THREADS = 256;
 constexpr int ZIP_V = 4;
 
-template <int OP>  // 0: swiglu, 1: add
+template <int OP, bool F16>  // OP 0: swiglu, 1: add
 __global__ __launch_bounds__(ZIP_THREADS) void zip_kernel(const uint4* __restrict__ a, const uint4* __restrict__ b,
                                                           uint4* __restrict__ c, int64_t nvec) {
     const int64_t base = (int64_t)blockIdx.x * ZIP_THREADS * ZIP_V + threadIdx.x;
@@ -131,8 +132,8 @@ __global__ __launch_bounds__(ZIP_THREADS) void zip_kernel(const uint4* __restric
         uint32_t o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            float x0 = bf16lo_to_f32(x[k]), x1 = bf16hi_to_f32(x[k]);
-            float y0 = bf16lo_to_f32(y[k]), y1 = bf16hi_to_f32(y[k]);
+            float x0 = h16lo_to_f32<F16>(x[k]), x1 = h16hi_to_f32<F16>(x[k]);
+            float y0 = h16lo_to_f32<F16>(y[k]), y1 = h16hi_to_f32<F16>(y[k]);
             float r0, r1;
             if (OP == 0) {
                 r0 = x0 / (1.0f + __expf(-x0)) * y0;
@@ -141,41 +142,41 @@ __global__ __launch_bounds__(ZIP_THREADS) void zip_kernel(const uint4* __restric
                 r0 = x0 + y0;
                 r1 = x1 + y1;
             }
-            o[k] = pack_bf16x2(r0, r1);
+            o[k] = pack_h16x2<F16>(r0, r1);
         }
         c[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
-template <int OP>
+template <int OP, bool F16>
 __global__ void zip_tail_kernel(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t first, int64_t n) {
     int64_t i = first + threadIdx.x;
     if (i >= n) return;
-    float x = bf16_to_f32(a[i]), y = bf16_to_f32(b[i]);
+    float x = h16_to_f32<F16>(a[i]), y = h16_to_f32<F16>(b[i]);
     float r = OP == 0 ? x / (1.0f + __expf(-x)) * y : x + y;
-    c[i] = (uint16_t)f32_to_bf16(r);
+    c[i] = (uint16_t)f32_to_h16<F16>(r);
 }
 
-template <int OP>
+template <int OP, bool F16>
 static hipError_t launch_zip(const void* a, const void* b, void* c, int64_t n, hipStream_t stream) {
     int64_t nvec = n / 8;
     if (nvec > 0) {
         int64_t per = (int64_t)ZIP_THREADS * ZIP_V;
         int64_t grid = (nvec + per - 1) / per;
-        hipLaunchKernelGGL(zip_kernel<OP>, dim3((unsigned)grid), dim3(ZIP_THREADS), 0, stream, (const uint4*)a,
+        hipLaunchKernelGGL((zip_kernel<OP, F16>), dim3((unsigned)grid), dim3(ZIP_THREADS), 0, stream, (const uint4*)a,
                            (const uint4*)b, (uint4*)c, nvec);
     }
     if (n % 8)
-        hipLaunchKernelGGL(zip_tail_kernel<OP>, dim3(1), dim3(8), 0, stream, (const uint16_t*)a, (const uint16_t*)b,
+        hipLaunchKernelGGL((zip_tail_kernel<OP, F16>), dim3(1), dim3(8), 0, stream, (const uint16_t*)a, (const uint16_t*)b,
                            (uint16_t*)c, nvec * 8, n);
     return hipGetLastError();
 }
 
-hipError_t launch_swiglu(const void* g, const void* u, void* h, int64_t n, hipStream_t stream) {
-    return launch_zip<0>(g, u, h, n, stream);
+hipError_t launch_swiglu(const void* g, const void* u, void* h, int64_t n, int32_t f16, hipStream_t stream) {
+    return f16 ? launch_zip<0, true>(g, u, h, n, stream) : launch_zip<0, false>(g, u, h, n, stream);
 }
-hipError_t launch_add(const void* a, const void* b, void* c, int64_t n, hipStream_t stream) {
-    return launch_zip<1>(a, b, c, n, stream);
+hipError_t launch_add(const void* a, const void* b, void* c, int64_t n, int32_t f16, hipStream_t stream) {
+    return f16 ? launch_zip<1, true>(a, b, c, n, stream) : launch_zip<1, false>(a, b, c, n, stream);
 }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -184,6 +185,7 @@ hipError_t launch_add(const void* a, const void* b, void* c, int64_t n, hipStrea
 // squares; pass 2 joins each piece 1:1 with the row statistic and the gain.
 constexpr int NORM_WAVES = 4;
 
+template <bool F16>
 __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t* __restrict__ rsplit, int32_t nrb,
                                                                   const NormBlock* __restrict__ blocks, int32_t ndb,
                                                                   int64_t rows, int32_t D,
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t*
                 uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    float a0 = bf16lo_to_f32(w[k]), a1 = bf16hi_to_f32(w[k]);
+                    float a0 = h16lo_to_f32<F16>(w[k]), a1 = h16hi_to_f32<F16>(w[k]);
                     ss += a0 * a0 + a1 * a1;
                 }
             }
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t*
             for (int e = lane; e < b.width; e += 64) {
                 uint16_t h = src[e];
                 row[b.d_lo + e] = h;
-                float a = bf16_to_f32(h);
+                float a = h16_to_f32<F16>(h);
                 ss += a * a;
             }
         }
@@ -236,13 +238,13 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t*
                 uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w}, o[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    o[k] = pack_bf16x2(bf16lo_to_f32(w[k]) * inv * bf16lo_to_f32(gw[k]),
-                                       bf16hi_to_f32(w[k]) * inv * bf16hi_to_f32(gw[k]));
+                    o[k] = pack_h16x2<F16>(h16lo_to_f32<F16>(w[k]) * inv * h16lo_to_f32<F16>(gw[k]),
+                                       h16hi_to_f32<F16>(w[k]) * inv * h16hi_to_f32<F16>(gw[k]));
                 *reinterpret_cast<uint4*>(dstp + e) = make_uint4(o[0], o[1], o[2], o[3]);
             }
         } else {
             for (int e = lane; e < b.width; e += 64)
-                dstp[e] = (uint16_t)f32_to_bf16(bf16_to_f32(row[b.d_lo + e]) * inv * bf16_to_f32(gain[b.d_lo + e]));
+                dstp[e] = (uint16_t)f32_to_h16<F16>(h16_to_f32<F16>(row[b.d_lo + e]) * inv * h16_to_f32<F16>(gain[b.d_lo + e]));
         }
     }
 }
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t*
 // every column block is W wide with W a multiple of 512, so each vector lies
 // in one block and its block index k * 512 / W is uniform; all NV loads of a
 // row are in flight together, then one wavefront reduction, then the stores.
-template <int NV>
+template <int NV, bool F16>
 __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_rows_kernel(const int64_t* __restrict__ rsplit,
                                                                        int32_t nrb,
                                                                        const NormBlock* __restrict__ blocks,
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_rows_kernel(const int
         const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float a0 = bf16lo_to_f32(w[q]), a1 = bf16hi_to_f32(w[q]);
+            const float a0 = h16lo_to_f32<F16>(w[q]), a1 = h16hi_to_f32<F16>(w[q]);
             ss += a0 * a0 + a1 * a1;
         }
     }
@@ -295,8 +297,8 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_rows_kernel(const int
         uint32_t o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            o[q] = pack_bf16x2(bf16lo_to_f32(w[q]) * inv * bf16lo_to_f32(gw[q]),
-                               bf16hi_to_f32(w[q]) * inv * bf16hi_to_f32(gw[q]));
+            o[q] = pack_h16x2<F16>(h16lo_to_f32<F16>(w[q]) * inv * h16lo_to_f32<F16>(gw[q]),
+                               h16hi_to_f32<F16>(w[q]) * inv * h16hi_to_f32<F16>(gw[q]));
         *reinterpret_cast<uint4*>(y + off[k]) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
@@ -304,16 +306,17 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_rows_kernel(const int
 // vec: 0 scalar pieces, 1 16-byte pieces (both staged through LDS), 2 rows
 // held in registers (D a multiple of 512 up to 8192, every block W wide with
 // W a multiple of 512; the planner checks this)
-hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
-                          int64_t rows, int32_t D, int32_t W, const void* x, const void* gain, void* y, float eps,
-                          int32_t vec, hipStream_t stream) {
+template <bool F16>
+static hipError_t launch_rmsnorm_t(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off,
+                                   int32_t ndb, int64_t rows, int32_t D, int32_t W, const void* x, const void* gain,
+                                   void* y, float eps, int32_t vec, hipStream_t stream) {
     const uint8_t* t = (const uint8_t*)table;
     int64_t grid = (rows + NORM_WAVES - 1) / NORM_WAVES;
     if (vec == 2) {
         const int nv = D / 512;
 #define JA_ROWS_CASE(N)                                                                                           \
     case N:                                                                                                       \
-        hipLaunchKernelGGL(rmsnorm_rows_kernel<N>, dim3((unsigned)grid), dim3(NORM_WAVES * 64), 0, stream,        \
+        hipLaunchKernelGGL((rmsnorm_rows_kernel<N, F16>), dim3((unsigned)grid), dim3(NORM_WAVES * 64), 0, stream,        \
                            (const int64_t*)(t + rsplit_off), nrb, (const NormBlock*)(t + blocks_off), ndb, rows, W, \
                            (const uint16_t*)x, (const uint16_t*)gain, (uint16_t*)y, eps);                        \
         break;
@@ -335,11 +338,19 @@ hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, in
 #undef JA_ROWS_CASE
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)grid), dim3(NORM_WAVES * 64),
+    hipLaunchKernelGGL(rmsnorm_kernel<F16>, dim3((unsigned)grid), dim3(NORM_WAVES * 64),
                        (unsigned)((size_t)NORM_WAVES * D * 2), stream, (const int64_t*)(t + rsplit_off), nrb,
                        (const NormBlock*)(t + blocks_off), ndb, rows, D, (const uint16_t*)x, (const uint16_t*)gain,
                        (uint16_t*)y, eps, vec);
     return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
+                          int64_t rows, int32_t D, int32_t W, const void* x, const void* gain, void* y, float eps,
+                          int32_t vec, int32_t f16, hipStream_t stream) {
+    return f16 ? launch_rmsnorm_t<true>(table, rsplit_off, nrb, blocks_off, ndb, rows, D, W, x, gain, y, eps, vec, stream)
+               : launch_rmsnorm_t<false>(table, rsplit_off, nrb, blocks_off, ndb, rows, D, W, x, gain, y, eps, vec,
+                                         stream);
 }
 
 // ---------------------------------------------------------------- aggregation
@@ -348,7 +359,7 @@ hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, in
 // writes them once.  No atomics: every output element has one owner.
 constexpr int AGG_THREADS = 256;
 
-template <int OUT_BF16>
+template <int OUT>  // 0: f32, 1: bf16, 2: IEEE half
 __global__ __launch_bounds__(AGG_THREADS) void agg_kernel(const AggTile* __restrict__ tiles,
                                                           const AggSeg* __restrict__ segs,
                                                           const int64_t* __restrict__ poff,
@@ -375,8 +386,10 @@ __global__ __launch_bounds__(AGG_THREADS) void agg_kernel(const AggTile* __restr
     for (int j = 0; j < PER; ++j) {
         int e = tl.e0 + threadIdx.x + j * AGG_THREADS;
         if (e < sg.nelem) {
-            if (OUT_BF16)
+            if (OUT == 1)
                 ((uint16_t*)out)[sg.out_off + e] = (uint16_t)f32_to_bf16(acc[j]);
+            else if (OUT == 2)
+                ((uint16_t*)out)[sg.out_off + e] = (uint16_t)f32_to_f16(acc[j]);
             else
                 ((float*)out)[sg.out_off + e] = acc[j];
         }
@@ -388,6 +401,9 @@ hipError_t launch_agg(const void* table, int64_t tiles_off, int32_t ntiles, int6
     const uint8_t* t = (const uint8_t*)table;
     if (out_dtype == JA_BF16)
         hipLaunchKernelGGL(agg_kernel<1>, dim3(ntiles), dim3(AGG_THREADS), 0, stream, (const AggTile*)(t + tiles_off),
+                           (const AggSeg*)(t + segs_off), (const int64_t*)(t + poff_off), partials, out, op);
+    else if (out_dtype == JA_F16)
+        hipLaunchKernelGGL(agg_kernel<2>, dim3(ntiles), dim3(AGG_THREADS), 0, stream, (const AggTile*)(t + tiles_off),
                            (const AggSeg*)(t + segs_off), (const int64_t*)(t + poff_off), partials, out, op);
     else
         hipLaunchKernelGGL(agg_kernel<0>, dim3(ntiles), dim3(AGG_THREADS), 0, stream, (const AggTile*)(t + tiles_off),

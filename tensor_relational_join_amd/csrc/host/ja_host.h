@@ -97,12 +97,12 @@ hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int
 // seq_off / nseq: the packed sequences' int32 end positions in the table (nseq = 0: not packed)
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
                             int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,
-                            const void* V, void* O, float scale, int32_t causal, hipStream_t stream);
+                            const void* V, void* O, float scale, int32_t causal, int32_t f16, hipStream_t stream);
 hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
                           int64_t rows, int32_t D, int32_t W, const void* x, const void* gain, void* y, float eps,
-                          int32_t vec, hipStream_t stream);
-hipError_t launch_swiglu(const void* g, const void* u, void* h, int64_t n, hipStream_t stream);
-hipError_t launch_add(const void* a, const void* b, void* c, int64_t n, hipStream_t stream);
+                          int32_t vec, int32_t f16, hipStream_t stream);
+hipError_t launch_swiglu(const void* g, const void* u, void* h, int64_t n, int32_t f16, hipStream_t stream);
+hipError_t launch_add(const void* a, const void* b, void* c, int64_t n, int32_t f16, hipStream_t stream);
 hipError_t launch_agg(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t poff_off,
                       const float* partials, void* out, int32_t out_dtype, int32_t op, hipStream_t stream);
 hipError_t launch_repart(const void* table, int64_t ntasks, const void* src, void* dst, int32_t esize,

@@ -124,11 +124,13 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
     if (A.dtype != B.dtype) return fail(JA_ERR_DTYPE, "contract operands must share a dtype");
     if (A.dtype == JA_F32) {
         if (C.dtype != JA_F32) return fail(JA_ERR_DTYPE, "f32 contraction writes f32");
-    } else if (A.dtype == JA_BF16) {
-        if (C.dtype != JA_BF16 && C.dtype != JA_F32) return fail(JA_ERR_DTYPE, "bf16 contraction writes bf16 or f32");
+    } else if (A.dtype == JA_BF16 || A.dtype == JA_F16) {
+        if (C.dtype != A.dtype && C.dtype != JA_F32)
+            return fail(JA_ERR_DTYPE, "a 16-bit contraction writes its input format or f32");
     } else {
-        return fail(JA_ERR_DTYPE, "contract supports f32 and bf16 operands");
+        return fail(JA_ERR_DTYPE, "contract supports f32, bf16 and f16 operands");
     }
+    const bool h16 = A.dtype != JA_F32;  // bf16 or f16: the MFMA kernels
     // roles of the letters: batch (A, B, C), M (A, C), N (B, C), K (A, B)
     std::string batch, M, N, K;
     for (char c : sc) {
@@ -153,8 +155,8 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
     p->b_layout = b_k_first ? JA_B_KN : JA_B_NK;
     p->in_dtype = A.dtype;
     p->out_dtype = C.dtype;
-    const int TM = A.dtype == JA_BF16 ? GEMM_BF16_TM : GEMM_F32_TM;
-    const int TN = A.dtype == JA_BF16 ? GEMM_BF16_TN : GEMM_F32_TN;
+    const int TM = h16 ? GEMM_BF16_TM : GEMM_F32_TM;
+    const int TN = h16 ? GEMM_BF16_TN : GEMM_F32_TN;
 
     const int64_t nt = t.count(), nseg = (int64_t)t.seg.size() - 1;
     std::vector<GemmTuple> tuples(nt);
@@ -225,16 +227,16 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         for (int32_t e0 = 0; e0 < a.nelem; e0 += AGG_CHUNK) atiles.push_back({(int32_t)sg, e0});
     }
     if ((int64_t)tiles.size() > lim || (int64_t)utiles.size() > lim) return fail(JA_ERR_UNSUPPORTED, "too many tiles");
-    if (A.dtype == JA_BF16) {
+    if (h16) {
         // the MFMA kernel moves 8 bf16 (16 bytes) at a time along every contiguous axis
         for (const GemmTuple& g : tuples) {
             bool ok = g.K % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_off % 8 == 0 && g.b_off % 8 == 0 &&
                       g.a_bstride % 8 == 0 && g.b_bstride % 8 == 0;
-            if (!ok) return fail(JA_ERR_UNSUPPORTED, "bf16 contraction needs block extents that are multiples of 8");
+            if (!ok) return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction needs block extents that are multiples of 8");
         }
         for (const GemmSeg& g : segs)
             if ((!a_m_first && g.M % 8) || (b_k_first && g.N % 8))
-                return fail(JA_ERR_UNSUPPORTED, "bf16 contraction needs block extents that are multiples of 8");
+                return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction needs block extents that are multiples of 8");
         // the direct-to-LDS kernel addresses each operand matrix with 32-bit byte offsets
         bool dma = true;
         for (const GemmTuple& g : tuples) dma = dma && g.a_bstride * 2 < lim && g.b_bstride * 2 < lim;
@@ -265,8 +267,9 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
     if ((st = match_rel(Q, s->ins[0], s, d, "Q")) || (st = match_rel(K, s->ins[1], s, d, "K")) ||
         (st = match_rel(V, s->ins[2], s, d, "V")) || (st = match_rel(O, s->out, s, d, "O")))
         return st;
-    if (Q.dtype != JA_BF16 || K.dtype != JA_BF16 || V.dtype != JA_BF16 || O.dtype != JA_BF16)
-        return fail(JA_ERR_DTYPE, "attention takes and writes bf16");
+    if ((Q.dtype != JA_BF16 && Q.dtype != JA_F16) || K.dtype != Q.dtype || V.dtype != Q.dtype || O.dtype != Q.dtype)
+        return fail(JA_ERR_DTYPE, "attention takes and writes bf16 or f16 (one format for Q, K, V and O)");
+    p->in_dtype = Q.dtype;
     const std::string& q = s->ins[0];
     const size_t r = q.size(), rk = s->ins[1].size();
     const std::string batch = q.substr(0, r - 2), kbatch = s->ins[1].substr(0, rk - 2);
@@ -360,8 +363,9 @@ ja_status plan_rmsnorm(ja_plan* p, const ja_spec* s, const ja_decomp* d, const j
     if ((st = match_rel(X, s->ins[0], s, d, "x")) || (st = match_rel(G, s->ins[1], s, d, "gain")) ||
         (st = match_rel(Y, s->out, s, d, "y")))
         return st;
-    if (X.dtype != JA_BF16 || G.dtype != JA_BF16 || Y.dtype != JA_BF16)
-        return fail(JA_ERR_DTYPE, "rmsnorm takes and writes bf16");
+    if ((X.dtype != JA_BF16 && X.dtype != JA_F16) || G.dtype != X.dtype || Y.dtype != X.dtype)
+        return fail(JA_ERR_DTYPE, "rmsnorm takes and writes bf16 or f16 (one format for x, gain and y)");
+    p->in_dtype = X.dtype;
     const int64_t D = X.shape[1];
     if (D > 16384) return fail(JA_ERR_UNSUPPORTED, "rmsnorm rows longer than 16384");
     p->nrb = X.nblk(0);
@@ -404,8 +408,9 @@ ja_status plan_zip(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_re
     if ((st = match_rel(A, s->ins[0], s, d, "operand 1")) || (st = match_rel(B, s->ins[1], s, d, "operand 2")) ||
         (st = match_rel(C, s->out, s, d, "output")))
         return st;
-    if (A.dtype != JA_BF16 || B.dtype != JA_BF16 || C.dtype != JA_BF16)
-        return fail(JA_ERR_DTYPE, "elementwise joins take and write bf16");
+    if ((A.dtype != JA_BF16 && A.dtype != JA_F16) || B.dtype != A.dtype || C.dtype != A.dtype)
+        return fail(JA_ERR_DTYPE, "elementwise joins take and write bf16 or f16 (one format throughout)");
+    p->in_dtype = A.dtype;
     // The three relations are blocked identically, so the 1:1 key join pairs
     // block i of each buffer with block i of the others at identical offsets:
     // the whole join is a zip of the three flat buffers.
@@ -492,14 +497,17 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
             if (p->ntiles == 0) return JA_OK;
             JA_TRY_HIP(launch_attention(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, p->seq_off,
                                         p->nseq, in_ptrs[0], in_ptrs[1], in_ptrs[2], out_ptr, p->scale, p->causal,
-                                        hs));
+                                        p->in_dtype == JA_F16, hs));
             break;
         case JA_OP_RMSNORM:
             JA_TRY_HIP(launch_rmsnorm(p->dev, p->rsplit_off, p->nrb, p->nblk_off, p->ndb, p->rows, p->D, p->norm_w,
-                                      in_ptrs[0], in_ptrs[1], out_ptr, p->eps, p->norm_vec, hs));
+                                      in_ptrs[0], in_ptrs[1], out_ptr, p->eps, p->norm_vec, p->in_dtype == JA_F16,
+                                      hs));
             break;
-        case JA_OP_SWIGLU: JA_TRY_HIP(launch_swiglu(in_ptrs[0], in_ptrs[1], out_ptr, p->n, hs)); break;
-        case JA_OP_ADD: JA_TRY_HIP(launch_add(in_ptrs[0], in_ptrs[1], out_ptr, p->n, hs)); break;
+        case JA_OP_SWIGLU:
+            JA_TRY_HIP(launch_swiglu(in_ptrs[0], in_ptrs[1], out_ptr, p->n, p->in_dtype == JA_F16, hs));
+            break;
+        case JA_OP_ADD: JA_TRY_HIP(launch_add(in_ptrs[0], in_ptrs[1], out_ptr, p->n, p->in_dtype == JA_F16, hs)); break;
     }
     return JA_OK;
 }

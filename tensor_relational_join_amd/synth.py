@@ -119,6 +119,12 @@ def normal_bf16(seed: int, stream: int, shape: Sequence[int], mean: float = 0.0,
     return f32_to_bf16_bits(normal(seed, stream, shape, mean, std))
 
 
+def normal_f16(seed: int, stream: int, shape: Sequence[int], mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+    """IEEE half bit patterns (uint16) of N(mean, std^2) draws, rounded once
+    from float64 to nearest even (numpy's float16 conversion)."""
+    return np.asarray(normal(seed, stream, shape, mean, std), dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns to float32 (for convenience in
     harness code; not used by either implementation's arithmetic)."""

@@ -38,3 +38,10 @@ def bf16_bits(t) -> np.ndarray:
 
 def f32_host(t) -> np.ndarray:
     return t.detach().cpu().numpy().astype(np.float32)
+
+
+def to_dev_f16(bits):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16).ravel()).view(
+        torch.float16).cuda()

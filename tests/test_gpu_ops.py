@@ -11,7 +11,7 @@ import itertools
 import numpy as np
 import pytest
 
-from gpu_helpers import bf16_bits, f32_host, rel_frobenius, rel_inf, to_dev_bf16, to_dev_f32
+from gpu_helpers import bf16_bits, f32_host, rel_frobenius, rel_inf, to_dev_bf16, to_dev_f16, to_dev_f32
 from tensor_relational_join_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -43,7 +43,7 @@ def _run(dev, orc, einsum, op, splits, dense_inputs, params="", in_dtypes=None, 
     unpack the output relation with the oracle's layout code."""
     import torch
 
-    from tensor_relational_join_amd.binding import JA_BF16, JA_F32
+    from tensor_relational_join_amd.binding import JA_BF16, JA_F16, JA_F32
 
     lhs, out = einsum.split("->")
     ins = lhs.split(",")
@@ -55,15 +55,18 @@ def _run(dev, orc, einsum, op, splits, dense_inputs, params="", in_dtypes=None, 
         for s, x, dt in zip(ins, dense_inputs, in_dtypes):
             rel = orc.Relation([splits[c][-1] for c in s], [splits[c] for c in s])
             flat = rel.pack(x)
-            dev_ins.append(to_dev_bf16(flat) if dt == JA_BF16 else to_dev_f32(flat))
+            dev_ins.append(to_dev_bf16(flat) if dt == JA_BF16 else to_dev_f16(flat) if dt == JA_F16 else
+                           to_dev_f32(flat))
         out_t = dev.alloc(o.out_rel)
         o.run(dev_ins, out_t)
         torch.cuda.synchronize()
         orel = orc.Relation([splits[c][-1] for c in out], [splits[c] for c in out])
-        host = bf16_bits(out_t) if out_dtype == JA_BF16 else f32_host(out_t)
+        host = bf16_bits(out_t) if out_dtype in (JA_BF16, JA_F16) else f32_host(out_t)
         res = orel.unpack(host)
         if out_dtype == JA_BF16:
             res = orc.bf16_to_f64(res)
+        elif out_dtype == JA_F16:
+            res = orc.f16_to_f64(res)
         return res.astype(np.float64), o, dev_ins
     except Exception:
         o.close()
@@ -330,6 +333,93 @@ def test_packed_attention(dev, orc, H, HK, S, ends, cuts, causal):
                          1.0 / np.sqrt(128.0), causal, seq_ends=ends)
     assert rel_frobenius(got.reshape(1, H, S, 128), orc.round_bf16(want)) <= BF16_TOL
     assert np.isfinite(got).all()
+
+
+# ------------------------------------------------------------------ fp16 relations
+
+F16_CONTRACT_CASES = [
+    ("ij,jk->ik", {"i": [0, 77, 200], "j": [0, 96, 320], "k": [0, 64, 136]}),
+    ("ij,kj->ik", {"i": [0, 300], "j": [0, 128, 256], "k": [0, 264]}),
+    ("ji,jk->ik", {"i": [0, 136], "j": [0, 64, 128], "k": [0, 40, 96]}),
+    ("bd,df->bf", {"b": [0, 256, 512], "d": [0, 512, 1024], "f": [0, 384, 776]}),
+]
+
+
+@pytest.mark.parametrize("einsum,sp", F16_CONTRACT_CASES)
+def test_contract_f16(dev, orc, einsum, sp):
+    """IEEE half relations (the pages' blocks run in fp16): fp16 in, fp32
+    accumulate, fp16 or fp32 out, fused and unfused (partials, then SUM)."""
+    import torch
+
+    from tensor_relational_join_amd.binding import JA_F16, JA_F32
+
+    lhs, out = einsum.split("->")
+    shapes = [tuple(sp[c][-1] for c in s) for s in lhs.split(",")]
+    X = synth.normal_f16(21, 0, shapes[0])
+    W = synth.normal_f16(21, 1, shapes[1], std=0.02)
+    exact = orc.einsum(einsum, orc.f16_to_f64(X), orc.f16_to_f64(W))
+    got, o, ins = _run(dev, orc, einsum, "contract", sp, [X, W], in_dtypes=[JA_F16, JA_F16], out_dtype=JA_F16)
+    try:
+        want = orc.round_f16(exact)
+        assert rel_frobenius(got, want) <= BF16_TOL
+        assert np.mean(got == want) > 0.9  # nearly every element is the correctly rounded fp32 sum
+        part = o.partial_buffer()
+        o.kernel(ins, part)
+        out2 = dev.alloc(o.out_rel)
+        o.agg(part, out2)
+        torch.cuda.synchronize()
+        orel = orc.Relation([sp[c][-1] for c in out], [sp[c] for c in out])
+        assert rel_frobenius(orc.f16_to_f64(orel.unpack(bf16_bits(out2))), want) <= BF16_TOL
+    finally:
+        o.close()
+    got32, o, _ = _run(dev, orc, einsum, "contract", sp, [X, W], in_dtypes=[JA_F16, JA_F16], out_dtype=JA_F32)
+    o.close()
+    assert rel_inf(got32, exact) <= 1e-5  # fp32 accumulation of exact fp16 products
+
+
+@pytest.mark.parametrize("causal,packed", [(True, None), (False, None), (True, [200, 512])])
+def test_attention_f16(dev, orc, causal, packed):
+    """fp16 Q, K, V, O: the scores multiply in fp16 and V needs no conversion."""
+    from tensor_relational_join_amd.binding import JA_F16
+
+    G, R, S = 2, 2, 512
+    cuts = [0, 200, 512] if packed else _eq(S, 4)
+    sp = {"b": [0, 1], "g": _eq(G, G), "r": [0, R], "s": cuts, "t": cuts, "d": [0, 128]}
+    Q = synth.normal_f16(22, 0, (1, G, R, S, 128))
+    K = synth.normal_f16(22, 1, (1, G, S, 128))
+    V = synth.normal_f16(22, 2, (1, G, S, 128))
+    params = ";".join(p for p in ("causal=s,t" if causal else "",
+                                  "packed=" + ",".join(map(str, packed)) if packed else "") if p)
+    got, o, _ = _run(dev, orc, "bgrsd,bgtd,bgtd->bgrsd", "attention", sp, [Q, K, V], params=params,
+                     in_dtypes=[JA_F16] * 3, out_dtype=JA_F16)
+    o.close()
+    want = orc.attention(orc.f16_to_f64(Q).reshape(1, G * R, S, 128), orc.f16_to_f64(K), orc.f16_to_f64(V),
+                         1.0 / np.sqrt(128.0), causal, seq_ends=packed)
+    assert rel_frobenius(got.reshape(1, G * R, S, 128), orc.round_f16(want)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "swiglu", "add"])
+def test_norm_and_elementwise_f16(dev, orc, op):
+    from tensor_relational_join_amd.binding import JA_F16
+
+    if op == "rmsnorm":
+        R, D = 300, 4096
+        x = synth.normal_f16(23, 0, (R, D))
+        gn = synth.normal_f16(23, 1, (D,), mean=1.0, std=0.1)
+        got, o, _ = _run(dev, orc, "rd,d->rd", "rmsnorm", {"r": [0, 100, 300], "d": _eq(D, 8)}, [x, gn],
+                         params="eps=1e-6", in_dtypes=[JA_F16] * 2, out_dtype=JA_F16)
+        want = orc.round_f16(orc.rmsnorm(orc.f16_to_f64(x), orc.f16_to_f64(gn), 1e-6))
+    else:
+        R, F = 64, 1000
+        a = synth.normal_f16(24, 0, (R, F))
+        b = synth.normal_f16(24, 1, (R, F))
+        got, o, _ = _run(dev, orc, "rf,rf->rf", op, {"r": [0, R], "f": [0, 504, 1000]}, [a, b],
+                         in_dtypes=[JA_F16] * 2, out_dtype=JA_F16)
+        af, bf = orc.f16_to_f64(a), orc.f16_to_f64(b)
+        want = orc.round_f16(orc.swiglu(af, bf) if op == "swiglu" else orc.add(af, bf))
+    o.close()
+    assert rel_frobenius(got, want) <= BF16_TOL
+    assert np.mean(got == want) > 0.99
 
 
 # ------------------------------------------------------------------ RMSNorm, SwiGLU, add
