@@ -57,7 +57,8 @@ def _mean_ms(pairs):
 
 def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0):
     """Time the oracle (as it stands) on the first n tokens of batch 0 of the
-    same block; n is grown until one run takes a few seconds."""
+    same block; n is grown (at most 16x per probe) until one run takes about
+    target_s seconds."""
     import numpy as np
 
     import oracle
@@ -77,9 +78,9 @@ def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0):
         oracle.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
                                   f["w_down"], batch, seq, heads, toks)
         dt = time.perf_counter() - t0
-        if dt >= target_s / 4 or n >= seq:
+        if dt >= target_s * 0.7 or n >= seq:
             break
-        n = min(seq, max(n * 2, int(n * target_s / 4 / max(dt, 1e-3))))
+        n = min(seq, 16 * n, max(n * 2, int(n * target_s / max(dt, 1e-3))))
     return {"value": flops(n) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "float64 oracle block forward on tokens 0..%d of batch 0 (%.1f GFLOP, %.2f s)" %
                       (n - 1, flops(n) / 1e9, dt)}
