@@ -316,13 +316,76 @@ def bench_kernel(args):
     return {"workload": args.workload, "steps": args.steps, "warmup": args.warmup, "results": res}
 
 
+def bench_join(args):
+    """The join step on the device (ja_djoin_run: grid enumeration, join
+    predicate, group-by order, CSR segments) against the host join
+    (ja_join, timed on the host) on the same decompositions: the
+    [4, 32, 2048, 128] causal attention grid (128-blocks), a 131,072-token
+    causal grid over 8 heads (1,024 query and key blocks), and the pages'
+    packed example (4,096 positions, sequences ending at 1,024, 2,560 and
+    4,096) over 32 heads.  Algorithmic bytes: records and segment offsets
+    written once, split points read once."""
+    import torch
+
+    from tensor_relational_join_amd import binding as B
+    from tensor_relational_join_amd.device import DeviceJoin
+
+    cases = [
+        ("attention_4x32x2048_causal", "bhsd,bhtd,bhtd->bhsd", "causal=s,t",
+         {"b": _eq(4, 4), "h": _eq(32, 32), "s": _eq(2048, 16), "t": _eq(2048, 16), "d": [0, 128]}),
+        ("causal_131072_tokens_8_heads", "bhsd,bhtd,bhtd->bhsd", "causal=s,t",
+         {"b": [0, 1], "h": _eq(8, 8), "s": _eq(131072, 1024), "t": _eq(131072, 1024), "d": [0, 128]}),
+        ("packed_4096_32_heads", "bhsd,bhtd,bhtd->bhsd", "packed=1024,2560,4096;causal=s,t",
+         {"b": [0, 1], "h": _eq(32, 32), "s": [0, 1024, 2560, 4096], "t": [0, 1024, 2560, 4096], "d": [0, 128]}),
+    ]
+    res = {}
+    for name, einsum, params, sp in cases:
+        dj = DeviceJoin(einsum, "attention", {c: len(v) - 1 for c, v in sp.items()},
+                        {c: v[-1] for c, v in sp.items()}, params)
+        splits = torch.tensor([x for c in dj.letters for x in sp[c]], dtype=torch.int64, device="cuda")
+        for _ in range(args.warmup):
+            dj.run(splits)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            dj.run(splits)
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / args.steps
+        nt, ns, status = (int(v) for v in dj.counts.cpu())
+        nl = len(dj.letters)
+        by = 4.0 * nt * nl + 8.0 * (ns + 1) + 8.0 * splits.numel()
+        # the host join of the same decomposition
+        spec = B.ja_spec_create(einsum, "attention", params)
+        dec = B.ja_decomp_create(spec, [sp[c][-1] for c in dj.letters], [len(sp[c]) - 1 for c in dj.letters],
+                                 [sp[c] for c in dj.letters])
+        reps, t0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < 0.5:
+            B.ja_tuples_destroy(B.ja_join(spec, dec))
+            reps += 1
+        host_ms = (time.perf_counter() - t0) / reps * 1e3
+        B.ja_decomp_destroy(dec)
+        B.ja_spec_destroy(spec)
+        cells = 1
+        for v in sp.values():
+            cells *= len(v) - 1
+        res[name] = {"cells": cells, "tuples": nt, "segments": ns, "status": status, "ms": round(ms, 4),
+                     "mtuples_per_s": round(nt / (ms / 1e3) / 1e6, 1), "gbs": round(by / (ms / 1e3) / 1e9, 1),
+                     "frac_hbm_peak": round(by / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "host_join_ms": round(host_ms, 3), "speedup_vs_host": round(host_ms / ms, 1)}
+        dj.close()
+    return {"workload": "join", "steps": args.steps, "warmup": args.warmup, "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block",
-                    choices=["block", "block_gqa", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy"])
+                    choices=["block", "block_gqa", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy",
+                             "join"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -334,6 +397,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "join":
+        print(json.dumps(bench_join(args)))
+        return
     if args.workload not in BLOCKS:
         print(json.dumps(bench_kernel(args)))
         return

@@ -197,6 +197,54 @@ ja_status ja_tuples_export(const ja_tuples* tuples, int32_t* rec, int64_t rec_ca
                            int64_t seg_cap);
 void ja_tuples_destroy(ja_tuples* tuples);
 
+/* ---- device-side join (section 3.2 step 1 on the GPU; section 3.3) ------ */
+
+/* The same join as ja_join, run by kernels on a stream into caller-owned
+ * device memory, with the split POSITIONS read from device memory at run
+ * time: a decomposition whose cuts depend on device data (for example the
+ * ends of packed sequences computed on the GPU, section 3.3) is joined with
+ * no host round trip.  Only the extents and the interval COUNTS are fixed
+ * when the join is created.  The result, for given split points, equals
+ * ja_join's records and segment offsets for the decomposition with those
+ * split points, bit for bit.
+ *
+ * ja_djoin_create: host only; extents[i] and intervals[i] per letter (letter
+ * order).  JA_ERR_DECOMP for a count outside [1, extent], a split attention
+ * head dimension, or (packed sequences) a sequence letter that does not span
+ * every sequence or has more intervals than there are sequences;
+ * JA_ERR_UNSUPPORTED beyond 2^28 grid cells.  The handle keeps no reference
+ * to spec. */
+typedef struct ja_djoin ja_djoin;
+ja_status ja_djoin_create(const ja_spec* spec, const int64_t* extents, const int32_t* intervals, ja_djoin** out);
+/* table_bytes: device table to upload once (the packed sequence ends);
+ * workspace_bytes: device scratch of one run (256-byte aligned);
+ * max_tuples / max_segs: capacities the outputs need (the full grid, the
+ * number of group-by keys); n_splits: int64 entries of the split array. */
+ja_status ja_djoin_device_bytes(const ja_djoin* join, size_t* table_bytes, size_t* workspace_bytes,
+                                int64_t* max_tuples, int64_t* max_segs, int64_t* n_splits);
+/* Copies the table into dev_buf (16-byte aligned, caller-owned, kept until
+ * destroy) and waits for the copy. */
+ja_status ja_djoin_upload(ja_djoin* join, void* dev_buf, size_t bytes, void* stream);
+/* Enqueue the join on `stream` (asynchronous; no host synchronisation).
+ *   splits_dev: device int64, n_splits entries: letter after letter (letter
+ *               order), the intervals + 1 split points of the letter;
+ *   rec:        device int32, max_tuples * n_letters: record i = the
+ *               interval index of every letter (letter order), sorted as
+ *               ja_join sorts; the first n_tuples records are written;
+ *   seg_off:    device int64, max_segs + 1: CSR offsets, the first
+ *               n_segs + 1 written;
+ *   counts:     device int64[3]: n_tuples, n_segs, status.  status 0: valid;
+ *               bit 0: some letter's split points do not start at 0, end at
+ *               its extent and rise strictly; bit 1: a packed sequence
+ *               letter is cut away from a sequence end.  A nonzero status
+ *               leaves n_tuples = n_segs = 0 and seg_off[0] = 0.
+ *   workspace:  device, workspace_bytes.
+ * Host-side argument errors return before anything is enqueued; device
+ * buffers too small for the stated sizes are undefined behaviour. */
+ja_status ja_djoin_run(const ja_djoin* join, const int64_t* splits_dev, int32_t* rec, int64_t* seg_off,
+                       int64_t* counts, void* workspace, void* stream);
+void ja_djoin_destroy(ja_djoin* join);
+
 /* ---- plans: join + fused kernel + aggregation + recompose -------------- */
 
 /* Validate the relations against the spec and decomposition (each input and

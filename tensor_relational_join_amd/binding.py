@@ -72,6 +72,12 @@ _SIGS = {
     "ja_tuples_count": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
     "ja_tuples_export": (_st, [_vp, ctypes.POINTER(_i32), _i64, ctypes.POINTER(_i64), _i64]),
     "ja_tuples_destroy": (None, [_vp]),
+    "ja_djoin_create": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_vp)]),
+    "ja_djoin_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_i64),
+                                    ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "ja_djoin_upload": (_st, [_vp, _vp, _sz, _vp]),
+    "ja_djoin_run": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ja_djoin_destroy": (None, [_vp]),
     "ja_plan_create": (_st, [_vp, _vp, _descpp, _i32, _descp, ctypes.POINTER(_vp)]),
     "ja_plan_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "ja_plan_upload": (_st, [_vp, _vp, _sz, _vp]),
@@ -284,6 +290,34 @@ def ja_tuples_export(tuples: int):
 
 def ja_tuples_destroy(tuples: int):
     _lib.ja_tuples_destroy(_vp(tuples))
+
+
+def ja_djoin_create(spec: int, extents: Sequence[int], intervals: Sequence[int]) -> int:
+    n = len(extents)
+    h = _vp()
+    _check(_lib.ja_djoin_create(_vp(spec), (_i64 * n)(*extents), (_i32 * n)(*intervals), ctypes.byref(h)))
+    return h.value
+
+
+def ja_djoin_device_bytes(join: int):
+    """(table_bytes, workspace_bytes, max_tuples, max_segs, n_splits)."""
+    tb, wb, mt, ms, ns = _sz(), _sz(), _i64(), _i64(), _i64()
+    _check(_lib.ja_djoin_device_bytes(_vp(join), ctypes.byref(tb), ctypes.byref(wb), ctypes.byref(mt),
+                                      ctypes.byref(ms), ctypes.byref(ns)))
+    return tb.value, wb.value, mt.value, ms.value, ns.value
+
+
+def ja_djoin_upload(join: int, dev_buf: int, nbytes: int, stream: int = 0):
+    _check(_lib.ja_djoin_upload(_vp(join), _vp(dev_buf), nbytes, _vp(stream)))
+
+
+def ja_djoin_run(join: int, splits_dev: int, rec: int, seg_off: int, counts: int, workspace: int, stream: int = 0):
+    _check(_lib.ja_djoin_run(_vp(join), _vp(splits_dev), _vp(rec), _vp(seg_off), _vp(counts), _vp(workspace),
+                             _vp(stream)))
+
+
+def ja_djoin_destroy(join: int):
+    _lib.ja_djoin_destroy(_vp(join))
 
 
 def ja_plan_create(spec: int, decomp: int, ins: Sequence[Relation], out: Relation) -> int:

@@ -147,3 +147,63 @@ class Repart:
             self.close()
         except Exception:
             pass
+
+
+class DeviceJoin:
+    """The join of one spec over a grid of fixed interval counts, run on the
+    device from split points in device memory (ja_djoin_*).
+
+    `counts` maps every letter to its number of intervals and `extents` to
+    its extent.  ``run(splits)`` enqueues the join; ``splits`` is a device
+    int64 tensor holding, letter after letter (letter order), each letter's
+    intervals + 1 split points.  The records, segment offsets and
+    [n_tuples, n_segs, status] stay in device memory (``rec``, ``seg_off``,
+    ``counts``)."""
+
+    def __init__(self, einsum: str, op: str, counts: Dict[str, int], extents: Dict[str, int], params: str = "",
+                 device="cuda", stream: Optional[torch.cuda.Stream] = None):
+        self.spec = B.ja_spec_create(einsum, op, params)
+        self.dj = None
+        try:
+            self.letters = B.ja_spec_letters(self.spec)
+            self.dj = B.ja_djoin_create(self.spec, [extents[c] for c in self.letters],
+                                        [counts[c] for c in self.letters])
+            tb, wb, self.max_tuples, self.max_segs, self.n_splits = B.ja_djoin_device_bytes(self.dj)
+            self.table = _table(tb, device)
+            B.ja_djoin_upload(self.dj, self.table.data_ptr(), self.table.numel(), stream_handle(stream))
+            self.workspace = torch.empty(max(wb, 256), dtype=torch.uint8, device=device)
+            nl = len(self.letters)
+            self.rec = torch.empty(max(self.max_tuples * nl, 1), dtype=torch.int32, device=device)
+            self.seg_off = torch.empty(self.max_segs + 1, dtype=torch.int64, device=device)
+            self.counts = torch.empty(3, dtype=torch.int64, device=device)
+        except Exception:
+            self.close()
+            raise
+
+    def run(self, splits: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+        if splits.dtype != torch.int64 or not splits.is_cuda or splits.numel() != self.n_splits:
+            raise ValueError("splits: a device int64 tensor of %d split points" % self.n_splits)
+        B.ja_djoin_run(self.dj, splits.data_ptr(), self.rec.data_ptr(), self.seg_off.data_ptr(),
+                       self.counts.data_ptr(), self.workspace.data_ptr(), stream_handle(stream))
+
+    def result(self):
+        """(records [n, letters] int32, segment offsets [nseg + 1] int64,
+        status) copied to the host (synchronises)."""
+        nt, ns, status = (int(v) for v in self.counts.cpu())
+        nl = len(self.letters)
+        rec = self.rec[: nt * nl].cpu().numpy().reshape(nt, nl)
+        return rec, self.seg_off[: ns + 1].cpu().numpy(), status
+
+    def close(self):
+        if self.dj:
+            B.ja_djoin_destroy(self.dj)
+            self.dj = None
+        if self.spec:
+            B.ja_spec_destroy(self.spec)
+            self.spec = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

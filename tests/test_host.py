@@ -343,3 +343,42 @@ def test_one_shot_entry_points_refuse_a_small_workspace(B):
     with pytest.raises(B.JaError) as e:
         B.ja_repartition(src, 16, dst, 16, None, 1 << 20, need - 1)
     assert e.value.name == "JA_ERR_WORKSPACE"
+
+
+# ------------------------------------------------------------------ device-side join (host checks)
+
+def test_device_join_sizes_and_errors(B):
+    """ja_djoin_* host side: capacities from the interval counts, argument
+    checks before anything reaches the GPU, decomposition rules."""
+    s = B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", "causal=s,t")
+    try:
+        dj = B.ja_djoin_create(s, [2, 4, 2048, 128, 2048], [1, 4, 16, 1, 16])
+        try:
+            tb, wb, mt, ms, ns = B.ja_djoin_device_bytes(dj)
+            assert (mt, ms, ns) == (4 * 16 * 16, 4 * 16, 2 + 5 + 17 + 2 + 17)
+            assert tb >= 8 and wb >= 4 * (ms + 1)
+            with pytest.raises(B.JaError) as e:  # table not uploaded
+                B.ja_djoin_run(dj, 256, 256, 256, 256, 256)
+            assert e.value.name == "JA_ERR_STATE"
+        finally:
+            B.ja_djoin_destroy(dj)
+        ext = [2, 4, 2048, 128, 2048]
+        for iv in ([1, 4, 16, 2, 16], [1, 5, 16, 1, 16], [0, 4, 16, 1, 16]):  # split d; 5 > 4 heads; no interval
+            with pytest.raises(B.JaError) as e:
+                B.ja_djoin_create(s, ext, iv)
+            assert e.value.name == "JA_ERR_DECOMP"
+        with pytest.raises(B.JaError) as e:  # 2^30 grid cells
+            B.ja_djoin_create(s, [1 << 10, 1 << 10, 1 << 10, 128, 1 << 10], [1 << 10, 1 << 10, 1 << 5, 1, 1 << 5])
+        assert e.value.name == "JA_ERR_UNSUPPORTED"
+    finally:
+        B.ja_spec_destroy(s)
+    s = B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", "packed=1024,2560,4096")
+    try:
+        B.ja_djoin_destroy(B.ja_djoin_create(s, [1, 1, 4096, 128, 4096], [1, 1, 3, 1, 2]))
+        for ext, iv in (([1, 1, 4096, 128, 4096], [1, 1, 4, 1, 2]),   # more intervals than sequences
+                        ([1, 1, 4000, 128, 4000], [1, 1, 2, 1, 2])):  # does not span every sequence
+            with pytest.raises(B.JaError) as e:
+                B.ja_djoin_create(s, ext, iv)
+            assert e.value.name == "JA_ERR_DECOMP"
+    finally:
+        B.ja_spec_destroy(s)
