@@ -378,6 +378,110 @@ def bench_join(args):
     return {"workload": "join", "steps": args.steps, "warmup": args.warmup, "results": res}
 
 
+def _pearson(xs, ys):
+    import numpy as np
+
+    x, y = np.asarray(xs, dtype=np.float64), np.asarray(ys, dtype=np.float64)
+    if len(x) < 3 or x.std() == 0 or y.std() == 0:
+        return None
+    return float(np.corrcoef(x, y)[0, 1])
+
+
+def bench_plans(args):
+    """The logical optimizer's plans run on one GPU (an analogue of the
+    pages' section 6 Experiments 3 and 5): for each graph, the optimizer's
+    plan, the greedy plan and 20 random plans on p = 8, each timed (every
+    operator plus every repartition between operators; computation inputs
+    already in the blockings their consumers ask for), with the Pearson
+    correlation between the communication-cost proxy and the measured time.
+    Graphs: the pages' matrix chains B, (M1 M2)((M3 M4) M5) with dimensions
+    9,216 / 20,480 / 5,120 / 20,480 / 5,120 / 9,216, and C, M1 (M2 M3) with
+    10,240 x 12,288 x 32,768 x 2,048; and the LLaMA-7B-shaped pre-norm FFN
+    with its residual (8,192 tokens, d 4,096, FFN 11,008).  bf16, N(0, 1)
+    inputs scaled by 1/sqrt(fan-in)."""
+    import torch
+
+    from tensor_relational_join_amd.binding import JA_PLAN_GREEDY, JA_PLAN_OPTIMAL, JA_PLAN_RANDOM
+    from tensor_relational_join_amd.graph import Graph, PlannedRun
+
+    def chain_b():
+        g = Graph()
+        d = [9216, 20480, 5120, 20480, 5120, 9216]
+        m = [g.input((d[i], d[i + 1])) for i in range(5)]
+        p_ = g.op("ab,bc->ac", "contract", [m[0], m[1]])
+        q = g.op("cd,de->ce", "contract", [m[2], m[3]])
+        r = g.op("ce,ef->cf", "contract", [q, m[4]])
+        g.op("ac,cf->af", "contract", [p_, r])
+        return g
+
+    def chain_c():
+        g = Graph()
+        m = [g.input(s) for s in ((10240, 12288), (12288, 32768), (32768, 2048))]
+        x = g.op("bc,cd->bd", "contract", [m[1], m[2]])
+        g.op("ab,bd->ad", "contract", [m[0], x])
+        return g
+
+    def ffn():
+        g = Graph()
+        T, D, F = 8192, 4096, 11008
+        x, gn, wg, wu, wd = g.input((T, D)), g.input((D,)), g.input((D, F)), g.input((D, F)), g.input((F, D))
+        h = g.op("rd,d->rd", "rmsnorm", [x, gn], "eps=1e-6")
+        a = g.op("td,df->tf", "contract", [h, wg])
+        b = g.op("td,df->tf", "contract", [h, wu])
+        s_ = g.op("rf,rf->rf", "swiglu", [a, b])
+        dn = g.op("tf,fd->td", "contract", [s_, wd])
+        g.op("rd,rd->rd", "add", [dn, x])
+        return g
+
+    p, nrand = 8, 20
+    res = {}
+    for name, make in (("chain_b", chain_b), ("chain_c", chain_c), ("ffn_llama7b", ffn)):
+        g = make()
+        torch.manual_seed(11)
+        dense = {}
+        for t, shape in enumerate(g.shapes):
+            if g.producer[t] is not None:
+                continue
+            x = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+            if len(shape) == 1:  # the RMSNorm gain
+                x.normal_(1.0, 0.1)
+            elif name == "ffn_llama7b" and t == 0:  # the FFN's activations
+                x.normal_()
+            else:  # a matrix of a chain or a weight: N(0, 1 / fan-in)
+                x.normal_(0.0, float(shape[0]) ** -0.5)
+            dense[t] = x
+        plans = [("optimal", JA_PLAN_OPTIMAL, 0), ("greedy", JA_PLAN_GREEDY, 0)] + \
+                [("random", JA_PLAN_RANDOM, s) for s in range(nrand)]
+        rows = []
+        for label, mode, seed in plans:
+            cost, plan = g.plan(p, mode, seed)
+            run = PlannedRun(g, plan)
+            try:
+                run.load(dense)
+                for _ in range(args.warmup):
+                    run.run()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    run.run()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / args.steps
+                rows.append({"plan": label, "seed": seed, "cost": cost, "ms": round(ms, 4),
+                             "repartitions": len(run.reparts),
+                             "intervals": ["".join("%s%d" % (c, v) for c, v in sp.items()) for sp in plan]})
+            finally:
+                run.close()
+        rnd = [r for r in rows if r["plan"] == "random"]
+        res[name] = {"p": p, "optimal": rows[0], "greedy": rows[1],
+                     "random_ms_median": float(sorted(r["ms"] for r in rnd)[len(rnd) // 2]),
+                     "random_ms_best": min(r["ms"] for r in rnd),
+                     "pearson_cost_vs_ms": _pearson([r["cost"] for r in rows], [r["ms"] for r in rows]),
+                     "plans": rows[2:]}
+    return {"workload": "plans", "steps": args.steps, "warmup": args.warmup, "results": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -385,7 +489,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block",
                     choices=["block", "block_gqa", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy",
-                             "join"])
+                             "join", "plans"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -399,6 +503,9 @@ def main():
         sys.exit(2)
     if args.workload == "join":
         print(json.dumps(bench_join(args)))
+        return
+    if args.workload == "plans":
+        print(json.dumps(bench_plans(args)))
         return
     if args.workload not in BLOCKS:
         print(json.dumps(bench_kernel(args)))

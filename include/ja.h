@@ -245,6 +245,72 @@ ja_status ja_djoin_run(const ja_djoin* join, const int64_t* splits_dev, int32_t*
                        int64_t* counts, void* workspace, void* stream);
 void ja_djoin_destroy(ja_djoin* join);
 
+/* ---- logical optimization (section 4) ------------------------------------ */
+
+/* A computation graph of abstract operators (section 4.2: vertices are
+ * operators, an edge runs from the producer of a tensor to each consumer)
+ * and the choice of one join-agg spec per operator.
+ *
+ * Candidate specs of an operator cut its shardable indices (section 3.3:
+ * every index of a contraction or an elementwise join; for attention the
+ * key-value batch / head letters and both sequence letters, not the query
+ * group letters nor the head dimension; for RMSNorm the row and the feature
+ * letter) into near-equal intervals whose counts multiply to the processor
+ * count p.  A tiling of a tensor is given by its interval count per
+ * dimension.
+ *
+ * Cost proxy (section 4.3), in elements: repartition -- every element of an
+ * operator-produced input whose tiling differs from the one the consumer's
+ * spec asks for (computation inputs are materialised directly in the blocks
+ * asked for: zero); join -- the elements of every input block of every
+ * function specification the join keeps; aggregation -- (copies - 1) times
+ * the elements of every distinct aggregated type (contraction and
+ * attention: the output blocks; RMSNorm: the per-row sums of squares).
+ *
+ * Modes of ja_graph_plan:
+ *   JA_PLAN_OPTIMAL: the dynamic program over output tilings (section 4.2):
+ *       Opt(Op, T) = min over specs J with out(J) = T of join(J) + agg(J) +
+ *       sum over inputs k of min over the producer's tilings T_k of
+ *       [repartition(J, k, T_k) + Opt(producer_k, T_k)], then a trace back
+ *       from the cheapest tiling of the output.  Graphs that are not trees
+ *       are cut at every edge out of a tensor with several consumers and the
+ *       pieces planned one at a time, larger first (section 4.5); an edge
+ *       between pieces is charged when the second of its two pieces is
+ *       planned.  Optimal within each piece.
+ *   JA_PLAN_GREEDY: the same program with the repartition sub-cost removed,
+ *       so each operator takes its cheapest join + aggregation (section 6,
+ *       Experiment 3).
+ *   JA_PLAN_RANDOM: one spec per operator, uniformly from `seed`.
+ * Ties go to the first candidate in lexicographic order of the interval
+ * counts (letter order).  Host only. */
+#define JA_PLAN_OPTIMAL 0
+#define JA_PLAN_GREEDY 1
+#define JA_PLAN_RANDOM 2
+typedef struct ja_graph ja_graph;
+ja_status ja_graph_create(ja_graph** out);
+void ja_graph_destroy(ja_graph* graph);
+/* A computation input of the given shape; writes its tensor id. */
+ja_status ja_graph_add_input(ja_graph* graph, int32_t rank, const int64_t* shape, int32_t* tensor);
+/* Operator `spec` (copied) on tensors inputs[0..n_inputs), whose dimensions
+ * bind the spec's input letters in order; writes the output tensor's id.
+ * JA_ERR_SHAPE when a letter gets two extents or a rank differs;
+ * JA_ERR_UNSUPPORTED for packed-sequence attention. */
+ja_status ja_graph_add_op(ja_graph* graph, const ja_spec* spec, const int32_t* inputs, int32_t n_inputs,
+                          int32_t* tensor);
+ja_status ja_graph_count(const ja_graph* graph, int32_t* n_ops, int32_t* n_tensors);
+/* Choose a spec for every operator (mode above); *cost (may be NULL) gets
+ * the chosen plan's total proxy cost.  JA_ERR_UNSUPPORTED when an operator
+ * has no candidate with p function specifications. */
+ja_status ja_graph_plan(ja_graph* graph, int32_t p, int32_t mode, uint64_t seed, double* cost);
+/* The chosen interval counts of operator `op` in its spec's letter order
+ * (cap >= number of letters).  JA_ERR_STATE before ja_graph_plan. */
+ja_status ja_graph_plan_intervals(const ja_graph* graph, int32_t op, int32_t* intervals, int32_t cap);
+/* The proxy's three sub-costs for a full assignment: intervals[op] holds the
+ * interval counts of operator op (letter order); intervals == NULL costs the
+ * planned assignment. */
+ja_status ja_graph_cost(const ja_graph* graph, const int32_t* const* intervals, double* repart, double* join,
+                        double* agg);
+
 /* ---- plans: join + fused kernel + aggregation + recompose -------------- */
 
 /* Validate the relations against the spec and decomposition (each input and

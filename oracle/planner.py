@@ -1,0 +1,253 @@
+"""Logical optimization by exhaustive search -- TEST INFRASTRUCTURE ONLY
+(part of the CPU oracle; the same import rules hold).
+
+Source: "Every Kernel Is a Join: Automatic Multi-GPU Parallelism for AI
+Computations in Einsummable" (paperpeel full text), section 3.3 (shardable
+indices, one function spec per combination of intervals), section 4.2 (a
+computation graph; choosing one join-agg spec per operator), section 4.3 (the
+communication-cost proxy and its three sub-costs), section 4.4 (the 3D matrix
+multiply the optimizer recovers), section 4.5 (graphs that are not trees are
+cut at the edges out of multiply-consumed tensors and the pieces planned one
+at a time, larger first).
+
+Every function here enumerates: the candidate specs of an operator, the cells
+of its interval grid, and every joint choice of specs.  Nothing is shared with
+the library's planner.
+
+Readings (also in the design notes): candidate specs cut the shardable
+indices into near-equal intervals whose counts multiply to p; a tiling is the
+interval count per dimension; the join sub-cost counts only cells that the
+causal predicate keeps; the aggregated types are the output blocks of a
+contraction or attention and the per-row sums of squares of RMSNorm; edges
+between pieces are charged when the second of their two pieces is planned;
+pieces of equal size go in the order of their root operators.
+"""
+from __future__ import annotations
+
+import itertools
+from typing import Dict, List, Optional, Sequence, Tuple
+
+from . import equal_splits
+
+
+class Graph:
+    """Tensors (computation inputs or operator outputs) and operators, each
+    operator an einsum over named indices with an op kind and params."""
+
+    def __init__(self):
+        self.shapes: List[Tuple[int, ...]] = []
+        self.producer: List[Optional[int]] = []
+        self.ops: List[dict] = []
+
+    def input(self, shape) -> int:
+        self.shapes.append(tuple(shape))
+        self.producer.append(None)
+        return len(self.shapes) - 1
+
+    def op(self, einsum: str, kind: str, inputs: Sequence[int], params: str = "") -> int:
+        lhs, out = einsum.split("->")
+        ins = lhs.split(",")
+        letters: List[str] = []
+        for s in ins + [out]:
+            for c in s:
+                if c not in letters:
+                    letters.append(c)
+        ext: Dict[str, int] = {}
+        for s, t in zip(ins, inputs):
+            for c, e in zip(s, self.shapes[t]):
+                assert ext.setdefault(c, e) == e
+        causal = None
+        for kv in params.split(";"):
+            if kv.startswith("causal="):
+                causal = tuple(kv[len("causal="):].split(","))
+        self.ops.append(dict(ins=ins, out=out, kind=kind, inputs=list(inputs), letters=letters, ext=ext,
+                             causal=causal))
+        self.shapes.append(tuple(ext[c] for c in out))
+        self.producer.append(len(self.ops) - 1)
+        return len(self.shapes) - 1
+
+    def consumers(self, t: int) -> List[Tuple[int, int]]:
+        return [(i, k) for i, o in enumerate(self.ops) for k, x in enumerate(o["inputs"]) if x == t]
+
+    def numel(self, t: int) -> int:
+        n = 1
+        for e in self.shapes[t]:
+            n *= e
+        return n
+
+
+def shardable(op: dict) -> List[str]:
+    """Section 3.3: contraction and elementwise indices are all shardable
+    ("any"); attention shards the key-value batch / head indices and the
+    sequence (the query-head group and the head dimension are not directly
+    shardable); RMSNorm shards rows and features."""
+    if op["kind"] == "attention":
+        q, k = op["ins"][0], op["ins"][1]
+        return [c for c in op["letters"] if (c in k or c == q[-2]) and c != q[-1]]
+    return list(op["letters"])
+
+
+def candidate_specs(op: dict, p: int) -> List[Dict[str, int]]:
+    """Every choice of interval counts, one per shardable index (1 for the
+    others), whose product is p."""
+    sh = shardable(op)
+    ranges = [range(1, min(op["ext"][c], p) + 1) if c in sh else range(1, 2) for c in op["letters"]]
+    out = []
+    for combo in itertools.product(*ranges):
+        prod = 1
+        for v in combo:
+            prod *= v
+        if prod == p:
+            out.append(dict(zip(op["letters"], combo)))
+    return out
+
+
+def spec_subcosts(op: dict, counts: Dict[str, int]) -> Tuple[float, float]:
+    """(join, aggregation) of section 4.3 for the join-agg spec with these
+    interval counts: its function specifications are the cells of the
+    interval grid that the join keeps."""
+    sp = {c: equal_splits(op["ext"][c], counts[c]) for c in op["letters"]}
+    join = 0.0
+    copies: Dict[tuple, List[float]] = {}
+    for cell in itertools.product(*[range(counts[c]) for c in op["letters"]]):
+        at = dict(zip(op["letters"], cell))
+        if op["causal"] is not None:
+            s, t = op["causal"]
+            if sp[t][at[t]] >= sp[s][at[s] + 1]:
+                continue
+        size = lambda c: sp[c][at[c] + 1] - sp[c][at[c]]  # noqa: E731
+        for s in op["ins"]:
+            n = 1
+            for c in s:
+                n *= size(c)
+            join += n
+        if op["kind"] in ("contract", "attention", "rmsnorm"):
+            agg_letters = op["out"][:1] if op["kind"] == "rmsnorm" else op["out"]
+            n = 1
+            for c in agg_letters:
+                n *= size(c)
+            key = tuple(at[c] for c in agg_letters)
+            copies.setdefault(key, []).append(n)
+    agg = sum((len(v) - 1) * v[0] for v in copies.values())
+    return join, agg
+
+
+def tiling(letters: str, counts: Dict[str, int]) -> Tuple[int, ...]:
+    return tuple(counts[c] for c in letters)
+
+
+def plan_cost(g: Graph, plan: Sequence[Dict[str, int]]) -> Tuple[float, float, float]:
+    """(repartition, join, aggregation) of a full assignment (section 4.3):
+    an operator-produced input whose tiling under the consumer's spec differs
+    from its tiling under the producer's spec costs all its elements."""
+    rep = join = agg = 0.0
+    for i, op in enumerate(g.ops):
+        j, a = spec_subcosts(op, plan[i])
+        join += j
+        agg += a
+        for s, t in zip(op["ins"], op["inputs"]):
+            q = g.producer[t]
+            if q is not None and tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q]):
+                rep += g.numel(t)
+    return rep, join, agg
+
+
+def brute_force(g: Graph, p: int) -> Tuple[float, List[Dict[str, int]]]:
+    """The cheapest full assignment by trying every joint choice of specs."""
+    cands = [candidate_specs(op, p) for op in g.ops]
+    best = None
+    for plan in itertools.product(*cands):
+        c = sum(plan_cost(g, plan))
+        if best is None or c < best[0]:
+            best = (c, list(plan))
+    return best
+
+
+def output_tensor(g: Graph, i: int) -> int:
+    return g.producer.index(i)
+
+
+def pieces(g: Graph) -> List[Tuple[int, List[int]]]:
+    """Section 4.5: cut every edge out of a tensor with several consumers;
+    the pieces (connected by the remaining edges) as (root, operators), larger
+    first, equal sizes by root.  The root is the operator whose output is not
+    consumed inside its piece."""
+    n = len(g.ops)
+    cut = {t for t in range(len(g.shapes)) if len(g.consumers(t)) > 1}
+    comp = list(range(n))
+
+    def find(x):
+        while comp[x] != x:
+            x = comp[x]
+        return x
+
+    for i, op in enumerate(g.ops):
+        for t in op["inputs"]:
+            q = g.producer[t]
+            if q is not None and t not in cut:
+                comp[find(i)] = find(q)
+    groups: Dict[int, List[int]] = {}
+    for i in range(n):
+        groups.setdefault(find(i), []).append(i)
+    out = []
+    for ops in groups.values():
+        root = [i for i in ops if len(g.consumers(output_tensor(g, i))) != 1]
+        out.append((root[0], sorted(ops)))
+    out.sort(key=lambda r: (-len(r[1]), r[0]))
+    return out
+
+
+def piece_cost(g: Graph, plan: Sequence[Optional[Dict[str, int]]], root: int, ops: Sequence[int],
+               with_repartition: bool = True) -> float:
+    """What planning one piece minimizes, given `plan` (its own operators'
+    specs, and those of the pieces planned before it; None elsewhere): the
+    join and aggregation of its operators, and the repartitions on every edge
+    whose two ends are both planned and of which at least one end is in the
+    piece."""
+    cost = 0.0
+    for i in ops:
+        op = g.ops[i]
+        j, a = spec_subcosts(op, plan[i])
+        cost += j + a
+        if not with_repartition:
+            continue
+        for s, t in zip(op["ins"], op["inputs"]):
+            q = g.producer[t]
+            if q is None or plan[q] is None:
+                continue  # a computation input, or charged when the producer's piece is planned
+            if tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q]):
+                cost += g.numel(t)
+    if with_repartition:
+        t_out = output_tensor(g, root)
+        for (c, k) in g.consumers(t_out):
+            if c not in ops and plan[c] is not None and \
+                    tiling(g.ops[c]["ins"][k], plan[c]) != tiling(g.ops[root]["out"], plan[root]):
+                cost += g.numel(t_out)
+    return cost
+
+
+def best_piece(g: Graph, p: int, plan: Sequence[Optional[Dict[str, int]]], root: int, ops: Sequence[int],
+               with_repartition: bool = True) -> Tuple[float, List[Dict[str, int]]]:
+    """The cheapest choice of specs for one piece by trying every one."""
+    best = None
+    for choice in itertools.product(*[candidate_specs(g.ops[i], p) for i in ops]):
+        trial = list(plan)
+        for i, c in zip(ops, choice):
+            trial[i] = c
+        cost = piece_cost(g, trial, root, ops, with_repartition)
+        if best is None or cost < best[0]:
+            best = (cost, list(choice))
+    return best
+
+
+def piecewise_plan(g: Graph, p: int, with_repartition: bool = True) -> Tuple[float, List[Dict[str, int]]]:
+    """Plan the pieces one at a time (section 4.5), each by exhaustive search
+    given the specs already fixed; with_repartition False charges no
+    repartition while choosing (the greedy selector of section 6, Experiment
+    3).  Returns the plan's full proxy cost and the plan."""
+    plan: List[Optional[Dict[str, int]]] = [None] * len(g.ops)
+    for root, ops in pieces(g):
+        _, choice = best_piece(g, p, plan, root, ops, with_repartition)
+        for i, c in zip(ops, choice):
+            plan[i] = c
+    return sum(plan_cost(g, plan)), plan

@@ -78,6 +78,15 @@ _SIGS = {
     "ja_djoin_upload": (_st, [_vp, _vp, _sz, _vp]),
     "ja_djoin_run": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ja_djoin_destroy": (None, [_vp]),
+    "ja_graph_create": (_st, [ctypes.POINTER(_vp)]),
+    "ja_graph_destroy": (None, [_vp]),
+    "ja_graph_add_input": (_st, [_vp, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
+    "ja_graph_add_op": (_st, [_vp, _vp, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
+    "ja_graph_count": (_st, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "ja_graph_plan": (_st, [_vp, _i32, _i32, ctypes.c_uint64, ctypes.POINTER(ctypes.c_double)]),
+    "ja_graph_plan_intervals": (_st, [_vp, _i32, ctypes.POINTER(_i32), _i32]),
+    "ja_graph_cost": (_st, [_vp, ctypes.POINTER(ctypes.POINTER(_i32)), ctypes.POINTER(ctypes.c_double),
+                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "ja_plan_create": (_st, [_vp, _vp, _descpp, _i32, _descp, ctypes.POINTER(_vp)]),
     "ja_plan_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "ja_plan_upload": (_st, [_vp, _vp, _sz, _vp]),
@@ -318,6 +327,61 @@ def ja_djoin_run(join: int, splits_dev: int, rec: int, seg_off: int, counts: int
 
 def ja_djoin_destroy(join: int):
     _lib.ja_djoin_destroy(_vp(join))
+
+
+JA_PLAN_OPTIMAL, JA_PLAN_GREEDY, JA_PLAN_RANDOM = 0, 1, 2
+
+
+def ja_graph_create() -> int:
+    h = _vp()
+    _check(_lib.ja_graph_create(ctypes.byref(h)))
+    return h.value
+
+
+def ja_graph_destroy(graph: int):
+    _lib.ja_graph_destroy(_vp(graph))
+
+
+def ja_graph_add_input(graph: int, shape: Sequence[int]) -> int:
+    t = _i32()
+    _check(_lib.ja_graph_add_input(_vp(graph), len(shape), (_i64 * len(shape))(*shape), ctypes.byref(t)))
+    return t.value
+
+
+def ja_graph_add_op(graph: int, spec: int, inputs: Sequence[int]) -> int:
+    t = _i32()
+    _check(_lib.ja_graph_add_op(_vp(graph), _vp(spec), (_i32 * len(inputs))(*inputs), len(inputs), ctypes.byref(t)))
+    return t.value
+
+
+def ja_graph_count(graph: int):
+    n_ops, n_t = _i32(), _i32()
+    _check(_lib.ja_graph_count(_vp(graph), ctypes.byref(n_ops), ctypes.byref(n_t)))
+    return n_ops.value, n_t.value
+
+
+def ja_graph_plan(graph: int, p: int, mode: int = 0, seed: int = 0) -> float:
+    c = ctypes.c_double()
+    _check(_lib.ja_graph_plan(_vp(graph), p, mode, seed, ctypes.byref(c)))
+    return c.value
+
+
+def ja_graph_plan_intervals(graph: int, op: int, n_letters: int):
+    buf = (_i32 * n_letters)()
+    _check(_lib.ja_graph_plan_intervals(_vp(graph), op, buf, n_letters))
+    return list(buf)
+
+
+def ja_graph_cost(graph: int, intervals=None):
+    """(repartition, join, aggregation) of the planned assignment, or of
+    `intervals` (one list of interval counts per operator, letter order)."""
+    r, j, a = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    arg = None
+    if intervals is not None:
+        rows = [(_i32 * len(v))(*v) for v in intervals]
+        arg = (ctypes.POINTER(_i32) * len(rows))(*[ctypes.cast(x, ctypes.POINTER(_i32)) for x in rows])
+    _check(_lib.ja_graph_cost(_vp(graph), arg, ctypes.byref(r), ctypes.byref(j), ctypes.byref(a)))
+    return r.value, j.value, a.value
 
 
 def ja_plan_create(spec: int, decomp: int, ins: Sequence[Relation], out: Relation) -> int:

@@ -1,0 +1,285 @@
+"""Logical optimization (the pages' section 4): the oracle's exhaustive
+search pinned against the pages' worked cases and hand-computed costs, then
+the library's dynamic program (ja_graph_*) checked against it.  CPU only."""
+import numpy as np
+import pytest
+
+from oracle import planner as P
+
+
+@pytest.fixture(scope="module")
+def B():
+    from tensor_relational_join_amd import binding
+
+    return binding
+
+
+# ------------------------------------------------------------------ oracle pins
+
+def test_3d_matmul_is_optimal():
+    """Section 4.4: one N x N x N matrix multiply with computation inputs on
+    p = q^3 processors.  A spec with a, b, c intervals on i, j, k joins the
+    first input c times over and the second a times over (N^2 (a + c)) and
+    aggregates b copies of every output block ((b - 1) N^2), so the cost is
+    N^2 (a + b + c - 1), least at a = b = c = q (the classical 3D algorithm)."""
+    N = 48
+    for q in (1, 2, 3, 4):
+        g = P.Graph()
+        x, y = g.input((N, N)), g.input((N, N))
+        g.op("ij,jk->ik", "contract", [x, y])
+        for spec in P.candidate_specs(g.ops[0], q ** 3):
+            assert sum(P.plan_cost(g, [spec])) == N * N * (spec["i"] + spec["j"] + spec["k"] - 1)
+        cost, plan = P.brute_force(g, q ** 3)
+        assert cost == N * N * (3 * q - 1) and plan == [{"i": q, "j": q, "k": q}]
+
+
+def test_example_3_8_cost_by_hand():
+    """Section 3.3 / Example 3.8: i = k = 256, j = 512, i and j cut in two, k
+    whole.  Four function specs, each joining a 128 x 256 block of the first
+    input with a 256 x 256 block of the second: join = 4 (32,768 + 65,536) =
+    393,216.  Two output types ([0,128) x [0,256) and [128,256) x [0,256)),
+    each made twice: aggregation = 2 (2 - 1) 32,768 = 65,536."""
+    g = P.Graph()
+    a, b = g.input((256, 512)), g.input((512, 256))
+    g.op("ij,jk->ik", "contract", [a, b])
+    assert P.plan_cost(g, [{"i": 2, "j": 2, "k": 1}]) == (0.0, 393216.0, 65536.0)
+
+
+def test_repartition_by_hand():
+    """Two chained products on p = 2: the first cuts i (its output leaves
+    tiling (2, 1)), the second cuts l, reading that output whole (tiling
+    (1, 1)), so the 64 x 32 intermediate is repartitioned: 2,048 elements.
+    The second product's own join: its (64 x 32) first input twice over and
+    two 32 x 8 halves of its second input: 2 x 2,048 + 512 = 4,608."""
+    g = P.Graph()
+    a, b, c = g.input((64, 16)), g.input((16, 32)), g.input((32, 16))
+    t = g.op("ij,jk->ik", "contract", [a, b])
+    g.op("ik,kl->il", "contract", [t, c])
+    rep, join, agg = P.plan_cost(g, [{"i": 2, "j": 1, "k": 1}, {"i": 1, "k": 1, "l": 2}])
+    assert rep == 64 * 32
+    assert join == (2 * (32 * 16 + 16 * 32)) + (2 * 64 * 32 + 2 * 32 * 8)
+    assert agg == 0.0
+    # the same tiling on both sides costs no repartition
+    assert P.plan_cost(g, [{"i": 2, "j": 1, "k": 1}, {"i": 2, "k": 1, "l": 1}])[0] == 0.0
+
+
+def test_causal_attention_joins_only_kept_tuples():
+    """Causal attention with s and t cut in two keeps 3 of the 4 cells (the
+    key block after the query block is dropped), so the join counts three
+    (Q, K, V) block triples; each of the two output blocks of the first query
+    half is made once and the second twice: aggregation = one O block."""
+    g = P.Graph()
+    q, k, v = g.input((1, 2, 64, 128)), g.input((1, 2, 64, 128)), g.input((1, 2, 64, 128))
+    g.op("bhsd,bhtd,bhtd->bhsd", "attention", [q, k, v], "causal=s,t")
+    spec = {"b": 1, "h": 1, "s": 2, "d": 1, "t": 2}
+    blk = 2 * 32 * 128
+    assert P.plan_cost(g, [spec]) == (0.0, 3 * 3 * blk, blk)
+    assert [c for c in P.shardable(g.ops[0])] == ["b", "h", "s", "t"]
+
+
+def test_pieces_of_a_residual_ffn():
+    """Section 4.5 on a pre-norm FFN with a residual: the norm's output feeds
+    both projections, so both edges out of it are cut (x, a computation
+    input, costs nothing to share).  Pieces: the tree {gate, up, SwiGLU, down,
+    add} rooted at the add, then the norm by itself."""
+    g = _ffn_graph_oracle()
+    ps = P.pieces(g)
+    assert ps == [(5, [1, 2, 3, 4, 5]), (0, [0])]
+
+
+# ------------------------------------------------------------------ graphs in both worlds
+
+def _ffn_desc(T=64, D=32, F=48):
+    """A pre-norm FFN block with its residual: norm, gate, up, SwiGLU, down,
+    add.  Returns (inputs, ops) where ops are (einsum, kind, params, inputs)
+    and tensor ids count inputs first, then operator outputs in order."""
+    inputs = [(T, D), (D,), (D, F), (D, F), (F, D)]  # x, gain, W_gate, W_up, W_down
+    x, gn, wg, wu, wd = range(5)
+    n = len(inputs)
+    ops = [("rd,d->rd", "rmsnorm", "eps=1e-6", [x, gn]),          # n+0
+           ("td,df->tf", "contract", "", [n + 0, wg]),           # n+1
+           ("td,df->tf", "contract", "", [n + 0, wu]),           # n+2
+           ("rf,rf->rf", "swiglu", "", [n + 1, n + 2]),          # n+3
+           ("tf,fd->td", "contract", "", [n + 3, wd]),           # n+4
+           ("rd,rd->rd", "add", "", [n + 4, x])]                 # n+5
+    return inputs, ops
+
+
+def _ffn_graph_oracle():
+    inputs, ops = _ffn_desc()
+    return _oracle_graph(inputs, ops)
+
+
+def _oracle_graph(inputs, ops):
+    g = P.Graph()
+    for s in inputs:
+        g.input(s)
+    for einsum, kind, params, ins in ops:
+        g.op(einsum, kind, ins, params)
+    return g
+
+
+def _lib_graph(B, inputs, ops):
+    g = B.ja_graph_create()
+    specs = []
+    for s in inputs:
+        B.ja_graph_add_input(g, list(s))
+    letters = []
+    for einsum, kind, params, ins in ops:
+        sp = B.ja_spec_create(einsum, kind, params)
+        specs.append(sp)
+        letters.append(B.ja_spec_letters(sp))
+        B.ja_graph_add_op(g, sp, ins)
+    for sp in specs:
+        B.ja_spec_destroy(sp)  # the graph keeps its own copies
+    return g, letters
+
+
+def _lib_plan(B, g, letters):
+    return [dict(zip(L, B.ja_graph_plan_intervals(g, i, len(L)))) for i, L in enumerate(letters)]
+
+
+def _chain(dims):
+    """M1 (M2 (... Mn)) right-associated: ops multiply from the right end."""
+    inputs = [(dims[i], dims[i + 1]) for i in range(len(dims) - 1)]
+    n = len(inputs)
+    ops, cur = [], n - 1
+    names = "abcdefgh"
+    for m in range(n - 2, -1, -1):
+        i, j, k = names[m], names[m + 1], names[n]
+        ops.append(("%s%s,%s%s->%s%s" % (i, j, j, k, i, k), "contract", "", [m, cur]))
+        cur = n + len(ops) - 1
+    return inputs, ops
+
+
+CHAINS = [([24, 16, 40, 8], 4), ([24, 16, 40, 8], 8), ([30, 12, 20, 18, 10], 6), ([64, 8, 64, 8], 8),
+          ([16, 48, 16, 48, 16], 4)]
+
+
+@pytest.mark.parametrize("dims,p", CHAINS)
+def test_dynamic_program_is_optimal_on_trees(B, dims, p):
+    """A matrix chain is a tree: the library's dynamic program reaches the
+    exhaustive minimum, and its reported cost is the oracle's cost of the
+    plan it returns."""
+    inputs, ops = _chain(dims)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        cost = B.ja_graph_plan(g, p, B.JA_PLAN_OPTIMAL)
+        plan = _lib_plan(B, g, letters)
+        og = _oracle_graph(inputs, ops)
+        assert cost == pytest.approx(sum(P.plan_cost(og, plan)), rel=1e-12)
+        assert cost == pytest.approx(P.brute_force(og, p)[0], rel=1e-12)
+        assert B.ja_graph_cost(g) == pytest.approx(P.plan_cost(og, plan), rel=1e-12)
+    finally:
+        B.ja_graph_destroy(g)
+
+
+@pytest.mark.parametrize("dims,p", CHAINS[:3])
+def test_greedy_and_random_selectors(B, dims, p):
+    """Greedy (section 6, Experiment 3): the same program without the
+    repartition sub-cost, so every operator takes its cheapest join +
+    aggregation and the plan costs at least the optimum.  Random: a valid spec
+    per operator, costed like any plan."""
+    inputs, ops = _chain(dims)
+    og = _oracle_graph(inputs, ops)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        opt = B.ja_graph_plan(g, p, B.JA_PLAN_OPTIMAL)
+        greedy = B.ja_graph_plan(g, p, B.JA_PLAN_GREEDY)
+        plan = _lib_plan(B, g, letters)
+        _, j, a = P.plan_cost(og, plan)
+        assert j + a == pytest.approx(sum(min(sum(P.spec_subcosts(op, c)) for c in P.candidate_specs(op, p))
+                                          for op in og.ops), rel=1e-12)
+        assert greedy >= opt - 1e-9
+        for seed in range(5):
+            c = B.ja_graph_plan(g, p, B.JA_PLAN_RANDOM, seed)
+            plan = _lib_plan(B, g, letters)
+            for spec in plan:
+                assert int(np.prod(list(spec.values()))) == p
+            assert c == pytest.approx(sum(P.plan_cost(og, plan)), rel=1e-12)
+            assert c >= opt - 1e-9
+    finally:
+        B.ja_graph_destroy(g)
+
+
+@pytest.mark.parametrize("p", [2, 4, 8])
+def test_pieces_are_planned_optimally(B, p):
+    """A graph that is not a tree (the residual FFN): every piece of the
+    library's plan is the exhaustive optimum given the pieces planned before
+    it (section 4.5's guarantee), and the reported cost is the plan's cost."""
+    inputs, ops = _ffn_desc()
+    og = _oracle_graph(inputs, ops)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        cost = B.ja_graph_plan(g, p, B.JA_PLAN_OPTIMAL)
+        plan = _lib_plan(B, g, letters)
+        assert cost == pytest.approx(sum(P.plan_cost(og, plan)), rel=1e-12)
+        fixed = [None] * len(og.ops)
+        for root, piece in P.pieces(og):
+            for i in piece:
+                fixed[i] = plan[i]
+            best, _ = P.best_piece(og, p, [f if (k not in piece) else None for k, f in enumerate(fixed)],
+                                   root, piece)
+            assert P.piece_cost(og, fixed, root, piece) == pytest.approx(best, rel=1e-12)
+    finally:
+        B.ja_graph_destroy(g)
+
+
+def test_library_recovers_the_3d_algorithm(B):
+    g, letters = _lib_graph(B, [(96, 96), (96, 96)], [("ij,jk->ik", "contract", "", [0, 1])])
+    try:
+        for q in (2, 3, 4):
+            cost = B.ja_graph_plan(g, q ** 3)
+            assert cost == 96 * 96 * (3 * q - 1)
+            assert B.ja_graph_plan_intervals(g, 0, 3) == [q, q, q]
+    finally:
+        B.ja_graph_destroy(g)
+
+
+def test_attention_and_norm_costs_match_oracle(B):
+    """Causal attention (only kept tuples join) and RMSNorm (per-row sums
+    aggregated over feature intervals) cost the same in both worlds for every
+    candidate the planner would consider."""
+    inputs = [(2, 4, 96, 128)] * 3 + [(96, 64), (64,)]
+    ops = [("bhsd,bhtd,bhtd->bhsd", "attention", "causal=s,t", [0, 1, 2]),
+           ("rd,d->rd", "rmsnorm", "eps=1e-6", [3, 4])]
+    og = _oracle_graph(inputs, ops)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        for p in (4, 6, 8):
+            for sa in P.candidate_specs(og.ops[0], p):
+                for sn in P.candidate_specs(og.ops[1], p):
+                    iv = [[sa[c] for c in letters[0]], [sn[c] for c in letters[1]]]
+                    assert B.ja_graph_cost(g, iv) == pytest.approx(P.plan_cost(og, [sa, sn]), rel=1e-12)
+            cost = B.ja_graph_plan(g, p)
+            assert cost == pytest.approx(P.brute_force(og, p)[0], rel=1e-12)
+    finally:
+        B.ja_graph_destroy(g)
+
+
+def test_planner_errors(B):
+    g = B.ja_graph_create()
+    try:
+        x = B.ja_graph_add_input(g, [4, 3])
+        y = B.ja_graph_add_input(g, [5, 2])
+        s = B.ja_spec_create("ij,jk->ik", "contract", "")
+        with pytest.raises(B.JaError) as e:  # j would be both 3 and 5
+            B.ja_graph_add_op(g, s, [x, y])
+        assert e.value.name == "JA_ERR_SHAPE"
+        y = B.ja_graph_add_input(g, [3, 2])
+        B.ja_graph_add_op(g, s, [x, y])
+        B.ja_spec_destroy(s)
+        with pytest.raises(B.JaError) as e:  # 4 * 3 * 2 = 24 cells at most
+            B.ja_graph_plan(g, 25)
+        assert e.value.name == "JA_ERR_UNSUPPORTED"
+        with pytest.raises(B.JaError) as e:
+            B.ja_graph_plan_intervals(g, 0, 3)
+        assert e.value.name == "JA_ERR_STATE"
+        sp = B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", "packed=8,16")
+        q = B.ja_graph_add_input(g, [1, 1, 16, 128])
+        with pytest.raises(B.JaError) as e:
+            B.ja_graph_add_op(g, sp, [q, q, q])
+        assert e.value.name == "JA_ERR_UNSUPPORTED"
+        B.ja_spec_destroy(sp)
+    finally:
+        B.ja_graph_destroy(g)
