@@ -390,10 +390,11 @@ def _pearson(xs, ys):
 def bench_plans(args):
     """The logical optimizer's plans run on one GPU (an analogue of the
     pages' section 6 Experiments 3 and 5): for each graph, the optimizer's
-    plan, the greedy plan and 20 random plans on p = 8, each timed (every
-    operator plus every repartition between operators; computation inputs
-    already in the blockings their consumers ask for), with the Pearson
-    correlation between the communication-cost proxy and the measured time.
+    plan, the greedy plan, the plan chosen with the device-time model and 20
+    random plans on p = 8, each timed (every operator plus every repartition
+    between operators; computation inputs already in the blockings their
+    consumers ask for), with the Pearson correlations of the measured time
+    with the communication-cost proxy and with the device-time model.
     Graphs: the pages' matrix chains B, (M1 M2)((M3 M4) M5) with dimensions
     9,216 / 20,480 / 5,120 / 20,480 / 5,120 / 9,216, and C, M1 (M2 M3) with
     10,240 x 12,288 x 32,768 x 2,048; and the LLaMA-7B-shaped pre-norm FFN
@@ -401,7 +402,7 @@ def bench_plans(args):
     inputs scaled by 1/sqrt(fan-in)."""
     import torch
 
-    from tensor_relational_join_amd.binding import JA_PLAN_GREEDY, JA_PLAN_OPTIMAL, JA_PLAN_RANDOM
+    from tensor_relational_join_amd.binding import JA_PLAN_DEVICE, JA_PLAN_GREEDY, JA_PLAN_OPTIMAL, JA_PLAN_RANDOM
     from tensor_relational_join_amd.graph import Graph, PlannedRun
 
     def chain_b():
@@ -450,11 +451,13 @@ def bench_plans(args):
             else:  # a matrix of a chain or a weight: N(0, 1 / fan-in)
                 x.normal_(0.0, float(shape[0]) ** -0.5)
             dense[t] = x
-        plans = [("optimal", JA_PLAN_OPTIMAL, 0), ("greedy", JA_PLAN_GREEDY, 0)] + \
+        plans = [("optimal", JA_PLAN_OPTIMAL, 0), ("greedy", JA_PLAN_GREEDY, 0), ("device", JA_PLAN_DEVICE, 0)] + \
                 [("random", JA_PLAN_RANDOM, s) for s in range(nrand)]
         rows = []
         for label, mode, seed in plans:
-            cost, plan = g.plan(p, mode, seed)
+            _, plan = g.plan(p, mode, seed)
+            cost = sum(g.cost(plan))
+            model_us = g.device_time(plan)
             run = PlannedRun(g, plan)
             try:
                 run.load(dense)
@@ -468,17 +471,19 @@ def bench_plans(args):
                 e1.record()
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / args.steps
-                rows.append({"plan": label, "seed": seed, "cost": cost, "ms": round(ms, 4),
+                rows.append({"plan": label, "seed": seed, "cost": cost, "model_ms": round(model_us / 1e3, 4),
+                             "ms": round(ms, 4),
                              "repartitions": len(run.reparts),
                              "intervals": ["".join("%s%d" % (c, v) for c, v in sp.items()) for sp in plan]})
             finally:
                 run.close()
         rnd = [r for r in rows if r["plan"] == "random"]
-        res[name] = {"p": p, "optimal": rows[0], "greedy": rows[1],
+        res[name] = {"p": p, "optimal": rows[0], "greedy": rows[1], "device": rows[2],
                      "random_ms_median": float(sorted(r["ms"] for r in rnd)[len(rnd) // 2]),
                      "random_ms_best": min(r["ms"] for r in rnd),
                      "pearson_cost_vs_ms": _pearson([r["cost"] for r in rows], [r["ms"] for r in rows]),
-                     "plans": rows[2:]}
+                     "pearson_model_vs_ms": _pearson([r["model_ms"] for r in rows], [r["ms"] for r in rows]),
+                     "plans": rows[3:]}
     return {"workload": "plans", "steps": args.steps, "warmup": args.warmup, "results": res}
 
 

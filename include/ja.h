@@ -281,11 +281,22 @@ void ja_djoin_destroy(ja_djoin* join);
  *       so each operator takes its cheapest join + aggregation (section 6,
  *       Experiment 3).
  *   JA_PLAN_RANDOM: one spec per operator, uniformly from `seed`.
+ *   JA_PLAN_DEVICE: the same program and cuts with a compute-aware cost in
+ *       place of the communication proxy (the computation awareness the
+ *       pages leave as future work, section 8): a model, in microseconds, of
+ *       this library's kernels on one MI355X -- a contraction as 256 x 256
+ *       output tiles, each costing its segment's contracted extent at the
+ *       measured per-CU rate of the fused bf16 contraction, placed longest
+ *       first on the least loaded of 256 CUs; attention as 128-query-row
+ *       tiles costed by the keys they see at the measured attention rate;
+ *       RMSNorm, SwiGLU, add and every repartition as their bytes at the
+ *       measured copy rate; 4 us per launch.  See ja_graph_device_time.
  * Ties go to the first candidate in lexicographic order of the interval
  * counts (letter order).  Host only. */
 #define JA_PLAN_OPTIMAL 0
 #define JA_PLAN_GREEDY 1
 #define JA_PLAN_RANDOM 2
+#define JA_PLAN_DEVICE 3
 typedef struct ja_graph ja_graph;
 ja_status ja_graph_create(ja_graph** out);
 void ja_graph_destroy(ja_graph* graph);
@@ -299,8 +310,9 @@ ja_status ja_graph_add_op(ja_graph* graph, const ja_spec* spec, const int32_t* i
                           int32_t* tensor);
 ja_status ja_graph_count(const ja_graph* graph, int32_t* n_ops, int32_t* n_tensors);
 /* Choose a spec for every operator (mode above); *cost (may be NULL) gets
- * the chosen plan's total proxy cost.  JA_ERR_UNSUPPORTED when an operator
- * has no candidate with p function specifications. */
+ * the chosen plan's total proxy cost (JA_PLAN_DEVICE: its modelled time in
+ * microseconds).  JA_ERR_UNSUPPORTED when an operator has no candidate with
+ * p function specifications. */
 ja_status ja_graph_plan(ja_graph* graph, int32_t p, int32_t mode, uint64_t seed, double* cost);
 /* The chosen interval counts of operator `op` in its spec's letter order
  * (cap >= number of letters).  JA_ERR_STATE before ja_graph_plan. */
@@ -310,6 +322,11 @@ ja_status ja_graph_plan_intervals(const ja_graph* graph, int32_t op, int32_t* in
  * planned assignment. */
 ja_status ja_graph_cost(const ja_graph* graph, const int32_t* const* intervals, double* repart, double* join,
                         double* agg);
+/* The device-time model (JA_PLAN_DEVICE) of a full assignment, in
+ * microseconds: every operator's modelled kernel time plus, on every edge
+ * whose tilings differ, one repartition launch copying the tensor once
+ * (computation inputs are free).  intervals as for ja_graph_cost. */
+ja_status ja_graph_device_time(const ja_graph* graph, const int32_t* const* intervals, double* us);
 
 /* ---- plans: join + fused kernel + aggregation + recompose -------------- */
 

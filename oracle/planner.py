@@ -251,3 +251,105 @@ def piecewise_plan(g: Graph, p: int, with_repartition: bool = True) -> Tuple[flo
         for i, c in zip(ops, choice):
             plan[i] = c
     return sum(plan_cost(g, plan)), plan
+
+
+# --------------------------------------------------------------------------
+# the device-time model of one MI355X running this library's kernels (the
+# computation awareness the pages leave as future work, section 8)
+# --------------------------------------------------------------------------
+
+CUS = 256
+GEMM_CU_FLOPS = 1213e12 / CUS   # measured fused bf16 contraction, per CU
+ATTN_CU_FLOPS = 775e12 / CUS    # measured causal attention, per CU
+COPY_BPS = 5.0e12               # measured plain device copy
+LAUNCH_US = 4.0
+
+
+def makespan(times: Sequence[float], cus: int = CUS) -> float:
+    """Longest job first, each onto the CU that frees up first; the time the
+    last CU finishes."""
+    loads = [0.0] * cus
+    for t in sorted(times, reverse=True):
+        k = min(range(cus), key=lambda c: loads[c])
+        loads[k] += t
+    return max(loads) if times else 0.0
+
+
+def op_device_time(op: dict, counts: Dict[str, int]) -> float:
+    """Microseconds of one operator's kernel under a spec: a contraction as
+    256 x 256 output tiles per segment (output block), each doing its
+    segment's whole contracted extent; attention as 128-query-row tiles, each
+    seeing the keys of its segment's kept key blocks up to its last row; the
+    memory-bound operators as their bytes at the copy rate."""
+    numel_out = 1
+    for c in op["out"]:
+        numel_out *= op["ext"][c]
+    if op["kind"] in ("rmsnorm", "swiglu", "add"):
+        nbytes = 2 * (2 * numel_out + op["ext"][op["ins"][1][0]]) if op["kind"] == "rmsnorm" else 2 * 3 * numel_out
+        return LAUNCH_US + nbytes / COPY_BPS * 1e6
+    sp = {c: equal_splits(op["ext"][c], counts[c]) for c in op["letters"]}
+    segs: Dict[tuple, list] = {}
+    for cell in itertools.product(*[range(counts[c]) for c in op["letters"]]):
+        at = dict(zip(op["letters"], cell))
+        if op["causal"] is not None:
+            s, t = op["causal"]
+            if sp[t][at[t]] >= sp[s][at[s] + 1]:
+                continue
+        segs.setdefault(tuple(at[c] for c in op["out"]), []).append(at)
+    size = lambda at, c: sp[c][at[c] + 1] - sp[c][at[c]]  # noqa: E731
+    tiles: List[float] = []
+    if op["kind"] == "contract":
+        A, B_ = op["ins"]
+        for cells in segs.values():
+            nb = M = N = 1
+            for c in op["out"]:
+                if c in A and c in B_:
+                    nb *= size(cells[0], c)
+                elif c in A:
+                    M *= size(cells[0], c)
+                else:
+                    N *= size(cells[0], c)
+            K = 0
+            for at in cells:
+                k = 1
+                for c in op["letters"]:
+                    if c not in op["out"]:
+                        k *= size(at, c)
+                K += k
+            n = nb * -(-M // 256) * -(-N // 256)
+            tiles += [2.0 * 256 * 256 * K / GEMM_CU_FLOPS * 1e6] * n
+    else:
+        q, k = op["ins"][0], op["ins"][1]
+        s, t, d = q[-2], k[-2], q[-1]
+        for cells in segs.values():
+            nbh = 1
+            for c in q[:-2]:
+                nbh *= size(cells[0], c)
+            s_lo, S = sp[s][cells[0][s]], size(cells[0], s)
+            for s0 in range(0, S, 128):
+                last = s_lo + min(S, s0 + 128) - 1
+                keys = 0
+                for at in cells:
+                    t_lo, t_hi = sp[t][at[t]], sp[t][at[t] + 1]
+                    hi = min(t_hi, last + 1) if op["causal"] is not None else t_hi
+                    keys += max(0, hi - t_lo)
+                tiles += [4.0 * 128 * op["ext"][d] * keys / ATTN_CU_FLOPS * 1e6] * nbh
+    return LAUNCH_US + makespan(tiles)
+
+
+def plan_device_time(g: Graph, plan: Sequence[Dict[str, int]]) -> float:
+    """Every operator's modelled time, plus one copy launch per edge whose
+    tilings differ (each element read and written once, 2 bytes each)."""
+    total = 0.0
+    for i, op in enumerate(g.ops):
+        total += op_device_time(op, plan[i])
+        for s, t in zip(op["ins"], op["inputs"]):
+            q = g.producer[t]
+            if q is not None and tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q]):
+                total += LAUNCH_US + 2 * 2 * g.numel(t) / COPY_BPS * 1e6
+    return total
+
+
+def brute_force_device(g: Graph, p: int) -> float:
+    """The least modelled time over every joint choice of specs."""
+    return min(plan_device_time(g, plan) for plan in itertools.product(*[candidate_specs(op, p) for op in g.ops]))

@@ -87,6 +87,7 @@ _SIGS = {
     "ja_graph_plan_intervals": (_st, [_vp, _i32, ctypes.POINTER(_i32), _i32]),
     "ja_graph_cost": (_st, [_vp, ctypes.POINTER(ctypes.POINTER(_i32)), ctypes.POINTER(ctypes.c_double),
                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
+    "ja_graph_device_time": (_st, [_vp, ctypes.POINTER(ctypes.POINTER(_i32)), ctypes.POINTER(ctypes.c_double)]),
     "ja_plan_create": (_st, [_vp, _vp, _descpp, _i32, _descp, ctypes.POINTER(_vp)]),
     "ja_plan_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "ja_plan_upload": (_st, [_vp, _vp, _sz, _vp]),
@@ -329,7 +330,7 @@ def ja_djoin_destroy(join: int):
     _lib.ja_djoin_destroy(_vp(join))
 
 
-JA_PLAN_OPTIMAL, JA_PLAN_GREEDY, JA_PLAN_RANDOM = 0, 1, 2
+JA_PLAN_OPTIMAL, JA_PLAN_GREEDY, JA_PLAN_RANDOM, JA_PLAN_DEVICE = 0, 1, 2, 3
 
 
 def ja_graph_create() -> int:
@@ -382,6 +383,18 @@ def ja_graph_cost(graph: int, intervals=None):
         arg = (ctypes.POINTER(_i32) * len(rows))(*[ctypes.cast(x, ctypes.POINTER(_i32)) for x in rows])
     _check(_lib.ja_graph_cost(_vp(graph), arg, ctypes.byref(r), ctypes.byref(j), ctypes.byref(a)))
     return r.value, j.value, a.value
+
+
+def ja_graph_device_time(graph: int, intervals=None) -> float:
+    """The device-time model (microseconds) of the planned assignment, or of
+    `intervals` (one list of interval counts per operator, letter order)."""
+    us = ctypes.c_double()
+    arg = None
+    if intervals is not None:
+        rows = [(_i32 * len(v))(*v) for v in intervals]
+        arg = (ctypes.POINTER(_i32) * len(rows))(*[ctypes.cast(x, ctypes.POINTER(_i32)) for x in rows])
+    _check(_lib.ja_graph_device_time(_vp(graph), arg, ctypes.byref(us)))
+    return us.value
 
 
 def ja_plan_create(spec: int, decomp: int, ins: Sequence[Relation], out: Relation) -> int:

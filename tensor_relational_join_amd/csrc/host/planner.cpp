@@ -9,9 +9,11 @@
 // near-equal intervals).  A tiling of a tensor is then fixed by its interval
 // count per dimension.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <functional>
 #include <map>
+#include <queue>
 
 #include "ja_host.h"
 
@@ -34,6 +36,7 @@ struct Cand {
     std::vector<std::vector<int32_t>> in;  // tiling of each input: counts per dimension
     std::vector<int32_t> out;               // tiling of the output
     double join = 0, agg = 0;
+    double dev_us = 0;                      // device-time model of the operator under this spec
 };
 
 struct GOp {
@@ -142,6 +145,122 @@ void sub_costs(const GOp& op, Cand& c) {
     for (auto& kv : groups) c.agg += (double)(kv.second.first - 1) * kv.second.second;
 }
 
+// ---- device-time model of this library's kernels on one MI355X -----------
+// The pages' proxy ignores computation (section 4.3) and name computation
+// awareness as future work (section 8).  On one GPU the join and the
+// aggregation are fused into the kernels, so the time of a plan is its
+// kernels' time plus its repartitions' copies.  Model: a contraction is
+// 256 x 256 output tiles, each taking its segment's contracted extent at the
+// measured per-CU rate of the fused bf16 contraction, placed longest first on
+// the least loaded of 256 CUs; attention is 128-query-row tiles costed by the
+// keys they see, at the measured attention rate; RMSNorm, SwiGLU, add and
+// repartitions move their bytes at the measured copy rate; every launch adds
+// a fixed latency.
+constexpr int DEV_CUS = 256;
+constexpr double DEV_GEMM_CU_FLOPS = 1213e12 / DEV_CUS;  // measured fused bf16 contraction, per CU
+constexpr double DEV_ATTN_CU_FLOPS = 775e12 / DEV_CUS;   // measured causal attention, per CU
+constexpr double DEV_COPY_BPS = 5.0e12;                  // measured plain device copy, bytes/s
+constexpr double DEV_LAUNCH_US = 4.0;                    // per kernel launch
+constexpr int DEV_GEMM_TILE = 256, DEV_ATTN_ROWS = 128;
+
+// Longest-processing-time-first placement of tile times on DEV_CUS CUs: the
+// finishing time of the last CU.
+double makespan(std::vector<double> t) {
+    std::sort(t.begin(), t.end(), std::greater<double>());
+    std::priority_queue<double, std::vector<double>, std::greater<double>> load;
+    for (int i = 0; i < DEV_CUS; ++i) load.push(0.0);
+    double end = 0;
+    for (double x : t) {
+        const double l = load.top() + x;
+        load.pop();
+        load.push(l);
+        end = std::max(end, l);
+    }
+    return end;
+}
+
+void device_time(const GOp& op, Cand& c) {
+    const ja_spec& s = op.spec;
+    const int nl = (int)s.letters.size();
+    double numel_out = 1;
+    for (char ch : s.out) numel_out *= (double)op.ext[s.letter_index(ch)];
+    if (s.kind == JA_OP_RMSNORM || s.kind == JA_OP_SWIGLU || s.kind == JA_OP_ADD) {
+        const double bytes = s.kind == JA_OP_RMSNORM ? 2.0 * (2.0 * numel_out + (double)op.ext[s.letter_index(s.ins[1][0])])
+                                                     : 2.0 * 3.0 * numel_out;
+        c.dev_us = DEV_LAUNCH_US + bytes / DEV_COPY_BPS * 1e6;
+        return;
+    }
+    std::vector<std::vector<int64_t>> sp(nl);
+    for (int i = 0; i < nl; ++i) sp[i] = equal_splits(op.ext[i], c.cnt[i]);
+    const int is = s.causal ? s.letter_index(s.causal_s) : -1, it = s.causal ? s.letter_index(s.causal_t) : -1;
+    // segments: kept cells grouped by output key
+    std::map<std::vector<int64_t>, std::vector<std::vector<int64_t>>> seg;
+    std::vector<int64_t> idx(nl, 0);
+    int64_t ncell = 1;
+    for (int i = 0; i < nl; ++i) ncell *= c.cnt[i];
+    for (int64_t cell = 0; cell < ncell; ++cell) {
+        int64_t r = cell;
+        for (int i = nl - 1; i >= 0; --i) {
+            idx[i] = r % c.cnt[i];
+            r /= c.cnt[i];
+        }
+        if (is >= 0 && sp[it][idx[it]] >= sp[is][idx[is] + 1]) continue;
+        std::vector<int64_t> key;
+        for (char ch : s.out) key.push_back(idx[s.letter_index(ch)]);
+        seg[key].push_back(idx);
+    }
+    auto len = [&](int l, int64_t k) { return sp[l][k + 1] - sp[l][k]; };
+    std::vector<double> tiles;
+    if (s.kind == JA_OP_CONTRACT) {
+        const std::string &A = s.ins[0], &B = s.ins[1];
+        for (auto& kv : seg) {
+            const std::vector<int64_t>& first = kv.second[0];
+            double nb = 1, M = 1, N = 1;
+            for (char ch : s.out) {
+                const int l = s.letter_index(ch);
+                const bool inA = A.find(ch) != std::string::npos, inB = B.find(ch) != std::string::npos;
+                (inA && inB ? nb : inA ? M : N) *= (double)len(l, first[l]);
+            }
+            double K = 0;
+            for (auto& cell : kv.second) {
+                double k = 1;
+                for (int l = 0; l < nl; ++l)
+                    if (s.out.find(s.letters[l]) == std::string::npos) k *= (double)len(l, cell[l]);
+                K += k;
+            }
+            const double t = 2.0 * DEV_GEMM_TILE * DEV_GEMM_TILE * K / DEV_GEMM_CU_FLOPS * 1e6;
+            const int64_t n = (int64_t)nb * (int64_t)std::ceil(M / DEV_GEMM_TILE) * (int64_t)std::ceil(N / DEV_GEMM_TILE);
+            tiles.insert(tiles.end(), (size_t)n, t);
+        }
+    } else {  // attention
+        const std::string& q = s.ins[0];
+        const int ls = s.letter_index(q[q.size() - 2]), ld = s.letter_index(q.back());
+        const int lt = s.letter_index(s.ins[1][s.ins[1].size() - 2]);
+        const double D = (double)op.ext[ld];
+        for (auto& kv : seg) {
+            const std::vector<int64_t>& first = kv.second[0];
+            double nbh = 1;
+            for (size_t i = 0; i + 2 < q.size(); ++i) nbh *= (double)len(s.letter_index(q[i]), first[s.letter_index(q[i])]);
+            const int64_t s_lo = sp[ls][first[ls]], S = len(ls, first[ls]);
+            for (int64_t s0 = 0; s0 < S; s0 += DEV_ATTN_ROWS) {
+                const int64_t last = s_lo + std::min<int64_t>(S, s0 + DEV_ATTN_ROWS) - 1;
+                double keys = 0;
+                for (auto& cell : kv.second) {
+                    const int64_t t_lo = sp[lt][cell[lt]], t_hi = sp[lt][cell[lt] + 1];
+                    keys += (double)std::max<int64_t>(0, (is >= 0 ? std::min(t_hi, last + 1) : t_hi) - t_lo);
+                }
+                const double t = 4.0 * DEV_ATTN_ROWS * D * keys / DEV_ATTN_CU_FLOPS * 1e6;
+                tiles.insert(tiles.end(), (size_t)nbh, t);
+            }
+        }
+    }
+    c.dev_us = DEV_LAUNCH_US + makespan(tiles);
+}
+
+// A repartition in the device-time model: one launch copying the tensor once.
+double rep_time(const ja_graph* g, int op, int slot, const std::vector<int32_t>& cons_tiling,
+                const std::vector<int32_t>& prod_tiling);
+
 uint64_t splitmix64(uint64_t x) {
     x += 0x9E3779B97F4A7C15ull;
     x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -155,6 +274,12 @@ uint64_t splitmix64(uint64_t x) {
 double rep_cost(const ja_graph* g, int op, int slot, const std::vector<int32_t>& cons_tiling,
                 const std::vector<int32_t>& prod_tiling) {
     return cons_tiling == prod_tiling ? 0.0 : g->t[g->ops[op].inputs[slot]].numel();
+}
+
+double rep_time(const ja_graph* g, int op, int slot, const std::vector<int32_t>& cons_tiling,
+                const std::vector<int32_t>& prod_tiling) {
+    if (cons_tiling == prod_tiling) return 0.0;
+    return DEV_LAUNCH_US + 2.0 * 2.0 * g->t[g->ops[op].inputs[slot]].numel() / DEV_COPY_BPS * 1e6;
 }
 
 }  // namespace
@@ -228,7 +353,7 @@ ja_status ja_graph_count(const ja_graph* g, int32_t* n_ops, int32_t* n_tensors) 
 ja_status ja_graph_plan(ja_graph* g, int32_t p, int32_t mode, uint64_t seed, double* cost) {
     if (!g) return fail(JA_ERR_ARG, "graph is NULL");
     if (p < 1) return fail(JA_ERR_ARG, "processor count must be positive");
-    if (mode < JA_PLAN_OPTIMAL || mode > JA_PLAN_RANDOM) return fail(JA_ERR_ARG, "unknown plan mode");
+    if (mode < JA_PLAN_OPTIMAL || mode > JA_PLAN_DEVICE) return fail(JA_ERR_ARG, "unknown plan mode");
     if (g->ops.empty()) return fail(JA_ERR_ARG, "graph has no operator");
     const int nop = (int)g->ops.size();
     // candidate specs and their join / aggregation sub-costs
@@ -247,6 +372,7 @@ ja_status ja_graph_plan(ja_graph* g, int32_t p, int32_t mode, uint64_t seed, dou
             for (const std::string& in : op.spec.ins) c.in.push_back(tiling_of(op.spec, in, cnt));
             c.out = tiling_of(op.spec, op.spec.out, cnt);
             sub_costs(op, c);
+            device_time(op, c);
             op.cands.push_back(c);
         }
         op.chosen = -1;
@@ -255,7 +381,11 @@ ja_status ja_graph_plan(ja_graph* g, int32_t p, int32_t mode, uint64_t seed, dou
         for (int i = 0; i < nop; ++i)
             g->ops[i].chosen = (int)(splitmix64(seed * 0x100000001B3ull + (uint64_t)i) % g->ops[i].cands.size());
     } else {
-        const bool with_rep = mode == JA_PLAN_OPTIMAL;
+        const bool with_rep = mode != JA_PLAN_GREEDY;
+        const bool dev = mode == JA_PLAN_DEVICE;
+        auto edge = [&](int op, int slot, const std::vector<int32_t>& cons, const std::vector<int32_t>& prod) {
+            return dev ? rep_time(g, op, slot, cons, prod) : rep_cost(g, op, slot, cons, prod);
+        };
         // pieces (section 4.5): cut every edge out of a tensor with several consumers
         auto cut = [&](int tensor) { return g->t[tensor].consumers.size() > 1; };
         std::vector<int> piece(nop);
@@ -294,20 +424,20 @@ ja_status ja_graph_plan(ja_graph* g, int32_t p, int32_t mode, uint64_t seed, dou
                 pk.assign(op.cands.size(), {});
                 for (size_t ci = 0; ci < op.cands.size(); ++ci) {
                     const Cand& c = op.cands[ci];
-                    double b = c.join + c.agg;
+                    double b = dev ? c.dev_us : c.join + c.agg;
                     pk[ci].assign(op.inputs.size(), {});
                     for (size_t k = 0; k < op.inputs.size(); ++k) {
                         const int tin = op.inputs[k], q = g->t[tin].producer;
                         if (q < 0) continue;  // a computation input: materialised in the blocks asked for
                         if (cut(tin)) {
                             // charged here if its producer is already fixed, else when it is planned
-                            if (fixed[q] && with_rep) b += rep_cost(g, i, (int)k, c.in[k], g->ops[q].cands[g->ops[q].chosen].out);
+                            if (fixed[q] && with_rep) b += edge(i, (int)k, c.in[k], g->ops[q].cands[g->ops[q].chosen].out);
                             continue;
                         }
                         double best = 0;
                         bool first = true;
                         for (auto& kv : opt[q]) {
-                            const double v = kv.second.first + (with_rep ? rep_cost(g, i, (int)k, c.in[k], kv.first) : 0.0);
+                            const double v = kv.second.first + (with_rep ? edge(i, (int)k, c.in[k], kv.first) : 0.0);
                             if (first || v < best) {
                                 best = v;
                                 pk[ci][k] = kv.first;
@@ -320,7 +450,7 @@ ja_status ja_graph_plan(ja_graph* g, int32_t p, int32_t mode, uint64_t seed, dou
                         // consumers of the root's output in pieces planned earlier
                         for (auto& cs : g->t[op.out].consumers)
                             if (fixed[cs.first])
-                                b += rep_cost(g, cs.first, cs.second,
+                                b += edge(cs.first, cs.second,
                                               g->ops[cs.first].cands[g->ops[cs.first].chosen].in[cs.second], c.out);
                     }
                     auto it = tab.find(c.out);
@@ -351,6 +481,7 @@ ja_status ja_graph_plan(ja_graph* g, int32_t p, int32_t mode, uint64_t seed, dou
         }
     }
     if (cost) {
+        if (mode == JA_PLAN_DEVICE) return ja_graph_device_time(g, nullptr, cost);
         double r, j, a;
         const ja_status st = ja_graph_cost(g, nullptr, &r, &j, &a);
         if (st) return st;
@@ -369,11 +500,13 @@ ja_status ja_graph_plan_intervals(const ja_graph* g, int32_t op, int32_t* interv
     return JA_OK;
 }
 
-ja_status ja_graph_cost(const ja_graph* g, const int32_t* const* intervals, double* repart, double* join,
-                        double* agg) {
-    if (!g) return fail(JA_ERR_ARG, "graph is NULL");
+}  // extern "C"
+
+namespace {
+// The candidate of every operator: from `intervals`, or the planned one.
+ja_status assignment(const ja_graph* g, const int32_t* const* intervals, std::vector<Cand>& pl) {
     const int nop = (int)g->ops.size();
-    std::vector<Cand> pl(nop);
+    pl.assign(nop, Cand());
     for (int i = 0; i < nop; ++i) {
         const GOp& op = g->ops[i];
         if (intervals) {
@@ -387,12 +520,26 @@ ja_status ja_graph_cost(const ja_graph* g, const int32_t* const* intervals, doub
             for (const std::string& in : op.spec.ins) c.in.push_back(tiling_of(op.spec, in, c.cnt));
             c.out = tiling_of(op.spec, op.spec.out, c.cnt);
             sub_costs(op, c);
+            device_time(op, c);
             pl[i] = c;
         } else {
             if (op.chosen < 0) return fail(JA_ERR_STATE, "graph has not been planned");
             pl[i] = op.cands[op.chosen];
         }
     }
+    return JA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+ja_status ja_graph_cost(const ja_graph* g, const int32_t* const* intervals, double* repart, double* join,
+                        double* agg) {
+    if (!g) return fail(JA_ERR_ARG, "graph is NULL");
+    const int nop = (int)g->ops.size();
+    std::vector<Cand> pl;
+    ja_status st = assignment(g, intervals, pl);
+    if (st) return st;
     double r = 0, j = 0, a = 0;
     for (int i = 0; i < nop; ++i) {
         const GOp& op = g->ops[i];
@@ -406,6 +553,24 @@ ja_status ja_graph_cost(const ja_graph* g, const int32_t* const* intervals, doub
     if (repart) *repart = r;
     if (join) *join = j;
     if (agg) *agg = a;
+    return JA_OK;
+}
+
+ja_status ja_graph_device_time(const ja_graph* g, const int32_t* const* intervals, double* us) {
+    if (!g || !us) return fail(JA_ERR_ARG, "NULL argument");
+    std::vector<Cand> pl;
+    ja_status st = assignment(g, intervals, pl);
+    if (st) return st;
+    double t = 0;
+    for (size_t i = 0; i < g->ops.size(); ++i) {
+        const GOp& op = g->ops[i];
+        t += pl[i].dev_us;
+        for (size_t k = 0; k < op.inputs.size(); ++k) {
+            const int q = g->t[op.inputs[k]].producer;
+            if (q >= 0) t += rep_time(g, (int)i, (int)k, pl[i].in[k], pl[q].out);
+        }
+    }
+    *us = t;
     return JA_OK;
 }
 

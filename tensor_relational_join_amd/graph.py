@@ -89,6 +89,14 @@ class Graph:
         finally:
             B.ja_graph_destroy(g)
 
+    def device_time(self, plan: Sequence[Dict[str, int]]) -> float:
+        """The device-time model of a plan, in microseconds."""
+        g = self._lib()
+        try:
+            return B.ja_graph_device_time(g, [[spec[c] for c in op["letters"]] for spec, op in zip(plan, self.ops)])
+        finally:
+            B.ja_graph_destroy(g)
+
 
 class PlannedRun:
     """One plan of a Graph, built on the current device (bf16 relations)."""

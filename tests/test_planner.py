@@ -1,6 +1,8 @@
 """Logical optimization (the pages' section 4): the oracle's exhaustive
 search pinned against the pages' worked cases and hand-computed costs, then
 the library's dynamic program (ja_graph_*) checked against it.  CPU only."""
+import itertools
+
 import numpy as np
 import pytest
 
@@ -281,5 +283,75 @@ def test_planner_errors(B):
             B.ja_graph_add_op(g, sp, [q, q, q])
         assert e.value.name == "JA_ERR_UNSUPPORTED"
         B.ja_spec_destroy(sp)
+    finally:
+        B.ja_graph_destroy(g)
+
+
+# ------------------------------------------------------------------ device-time model
+
+def test_device_model_closed_forms():
+    """The model's arithmetic on cases whose answer is known: 256 equal tiles
+    fill the 256 CUs once, one tile more takes a second round; a 4,096^3
+    product as one block is 16 x 16 tiles of K = 4,096; a copy-bound
+    operator is its bytes over the copy rate."""
+    assert P.makespan([1.0] * 256) == 1.0 and P.makespan([1.0] * 257) == 2.0
+    assert P.makespan([3.0, 2.0, 2.0, 1.0], cus=2) == 4.0  # 3+1 and 2+2
+    g = P.Graph()
+    a, b = g.input((4096, 4096)), g.input((4096, 4096))
+    g.op("ij,jk->ik", "contract", [a, b])
+    tile = 2.0 * 256 * 256 * 4096 / P.GEMM_CU_FLOPS * 1e6
+    assert P.op_device_time(g.ops[0], {"i": 1, "j": 1, "k": 1}) == pytest.approx(P.LAUNCH_US + tile)
+    # j cut in two: each output tile still does all 4,096 contracted elements (the SUM is fused)
+    assert P.op_device_time(g.ops[0], {"i": 1, "j": 2, "k": 1}) == pytest.approx(P.LAUNCH_US + tile)
+    # i cut in 8 x 512-row blocks: 2 x 16 tiles per block, 256 tiles in all, one round
+    assert P.op_device_time(g.ops[0], {"i": 8, "j": 1, "k": 1}) == pytest.approx(P.LAUNCH_US + tile)
+    # i cut in 3: 1,366 / 1,365-row blocks give 6 x 16 tiles each (288 > 256): two rounds
+    assert P.op_device_time(g.ops[0], {"i": 3, "j": 1, "k": 1}) == pytest.approx(P.LAUNCH_US + 2 * tile)
+    g2 = P.Graph()
+    x, y = g2.input((1024, 4096)), g2.input((1024, 4096))
+    g2.op("rd,rd->rd", "add", [x, y])
+    assert P.op_device_time(g2.ops[0], {"r": 2, "d": 4}) == pytest.approx(
+        P.LAUNCH_US + 6.0 * 1024 * 4096 / P.COPY_BPS * 1e6)
+
+
+@pytest.mark.parametrize("dims,p", CHAINS[:3])
+def test_device_model_matches_oracle(B, dims, p):
+    """Library and oracle compute the same modelled time for every plan of a
+    chain, and the library's JA_PLAN_DEVICE reaches the exhaustive minimum."""
+    inputs, ops = _chain([d * 64 for d in dims])
+    og = _oracle_graph(inputs, ops)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        cands = [P.candidate_specs(op, p) for op in og.ops]
+        for plan in list(itertools.product(*cands))[::7]:
+            iv = [[sp[c] for c in L] for sp, L in zip(plan, letters)]
+            assert B.ja_graph_device_time(g, iv) == pytest.approx(P.plan_device_time(og, plan), rel=1e-9)
+        t = B.ja_graph_plan(g, p, B.JA_PLAN_DEVICE)
+        assert t == pytest.approx(P.brute_force_device(og, p), rel=1e-9)
+        assert t == pytest.approx(P.plan_device_time(og, _lib_plan(B, g, letters)), rel=1e-9)
+    finally:
+        B.ja_graph_destroy(g)
+
+
+def test_device_model_attention_and_ffn(B):
+    """Causal attention tiles see only the keys up to their last row; the
+    residual FFN (not a tree) is planned piece by piece like the proxy."""
+    inputs = [(2, 8, 1024, 128)] * 3
+    ops = [("bhsd,bhtd,bhtd->bhsd", "attention", "causal=s,t", [0, 1, 2])]
+    og = _oracle_graph(inputs, ops)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        for spec in P.candidate_specs(og.ops[0], 8):
+            iv = [[spec[c] for c in letters[0]]]
+            assert B.ja_graph_device_time(g, iv) == pytest.approx(P.plan_device_time(og, [spec]), rel=1e-9)
+    finally:
+        B.ja_graph_destroy(g)
+    inputs, ops = _ffn_desc(T=2048, D=1024, F=2816)
+    og = _oracle_graph(inputs, ops)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        t = B.ja_graph_plan(g, 8, B.JA_PLAN_DEVICE)
+        assert t == pytest.approx(P.plan_device_time(og, _lib_plan(B, g, letters)), rel=1e-9)
+        assert t == pytest.approx(B.ja_graph_device_time(g), rel=1e-12)
     finally:
         B.ja_graph_destroy(g)
