@@ -198,8 +198,8 @@ def bench_kernel(args):
     attention = [4,32,2048,128] causal, 128-blocks; norm_swiglu = RMSNorm
     [8192,4096] (d by 8) + SwiGLU [8192,11008] (f by 8); configs = all of
     them; gqa = grouped-query causal attention, 32 query heads over 8
-    key-value heads, head_dim 128, one 8,192-token sequence and 8 x 1,024
-    tokens.  Inputs are seeded torch draws with the configs' distributions."""
+    key-value heads, head_dim 128, one 8,192-token sequence, 8 x 1,024
+    tokens and one 131,072-token sequence.  Inputs are seeded torch draws with the configs' distributions."""
     import torch
 
     from tensor_relational_join_amd import synth
@@ -227,7 +227,7 @@ def bench_kernel(args):
     runs = []  # (name, launch, flops, bytes, ops to close)
     want = ["tiny", "ffn", "ffn_unfused", "attention", "rmsnorm", "swiglu"] if args.workload == "configs" else \
         {"ffn": ["ffn"], "attention": ["attention"], "norm_swiglu": ["rmsnorm", "swiglu"],
-         "gqa": ["gqa_8k", "gqa_8x1k"]}[args.workload]
+         "gqa": ["gqa_8k", "gqa_8x1k", "gqa_128k"]}[args.workload]
 
     def tensors(op, seed, stds):
         torch.manual_seed(seed)
@@ -269,7 +269,7 @@ def bench_kernel(args):
         ins, out = tensors(op, 3, [(0.0, 1.0)] * 3)
         runs.append(("attention", lambda op=op, ins=ins, out=out: op.run(ins, out),
                      2 * 2.0 * 128 * 128 * 128 * 136 * 128, 2.0 * 4 * 4 * 32 * 2048 * 128, [op]))
-    for name, nb, seq in (("gqa_8k", 1, 8192), ("gqa_8x1k", 8, 1024)):
+    for name, nb, seq in (("gqa_8k", 1, 8192), ("gqa_8x1k", 8, 1024), ("gqa_128k", 1, 131072)):
         if name not in want:
             continue
         # grouped-query causal attention, 32 query heads over 8 key-value heads (4 per group),

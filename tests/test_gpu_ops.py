@@ -305,6 +305,40 @@ def test_gqa_attention_8k_sampled_rows(dev, orc):
     assert np.isfinite(got).all()
 
 
+def test_gqa_attention_128k_single_sequence(dev, orc):
+    """The pages' longest workload: one 131,072-token sequence, 32 query heads
+    over 8 key-value heads, 128-blocks on s and t, causal: 8 x 524,800 tuples
+    (4.2 M) in 8,192 segments.  Inputs are drawn on the device (seeded N(0, 1)
+    bf16, directly in the relation layout) and copied to the host for the
+    oracle, which computes sampled rows against all of their keys."""
+    import torch
+
+    G, R, S = 8, 4, 131072
+    n = S // 128
+    sp = {"b": [0, 1], "g": _eq(G, G), "r": [0, R], "s": _eq(S, n), "t": _eq(S, n), "d": [0, 128]}
+    op = dev.Op("bgrsd,bgtd,bgtd->bgrsd", "attention", sp, "causal=s,t")
+    try:
+        gen = torch.Generator(device="cuda").manual_seed(13)
+        ins = [dev.alloc(r).normal_(generator=gen) for r in op.in_rels]
+        out = dev.alloc(op.out_rel)
+        op.run(ins, out)
+        torch.cuda.synchronize()
+        rec, seg = op.tuples()
+        assert rec.shape[0] == G * n * (n + 1) // 2 and len(seg) - 1 == G * n
+        host = [orc.Relation(r.shape, r.splits).unpack(bf16_bits(t)) for r, t in zip(op.in_rels, ins)]
+        got = orc.bf16_to_f64(orc.Relation(op.out_rel.shape, op.out_rel.splits).unpack(bf16_bits(out)))
+    finally:
+        op.close()
+    rng = np.random.default_rng(5)
+    ss = sorted(set([0, 127, 128, 65535, 65536, S - 1] + list(rng.integers(0, S, 4))))
+    rows = np.array([(0, h, s) for h in (0, 5, 18, 31) for s in ss])
+    Q = orc.bf16_to_f64(host[0]).reshape(1, G * R, S, 128)
+    want = orc.attention_rows(Q, orc.bf16_to_f64(host[1]), orc.bf16_to_f64(host[2]), rows, 1.0 / np.sqrt(128.0), True)
+    g = got.reshape(1, G * R, S, 128)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert rel_frobenius(g, orc.round_bf16(want)) <= BF16_TOL
+    assert np.isfinite(got[0, :, :, ::4096]).all()
+
+
 # ------------------------------------------------------------------ packed sequences
 
 PACKED_CASES = [
