@@ -227,7 +227,7 @@ def bench_kernel(args):
     runs = []  # (name, launch, flops, bytes, ops to close)
     want = ["tiny", "ffn", "ffn_unfused", "attention", "rmsnorm", "swiglu"] if args.workload == "configs" else \
         {"ffn": ["ffn"], "attention": ["attention"], "norm_swiglu": ["rmsnorm", "swiglu"],
-         "gqa": ["gqa_8k", "gqa_8x1k", "gqa_128k"]}[args.workload]
+         "gqa": ["gqa_8k", "gqa_8x1k", "gqa_128k"], "f16": ["ffn_f16", "attention_f16"]}[args.workload]
 
     def tensors(op, seed, stds):
         torch.manual_seed(seed)
@@ -263,6 +263,22 @@ def bench_kernel(args):
                 op.agg(part, out)
             # the unfused path also writes and reads every fp32 partial (32 blocks of 1024 x 2752)
             runs.append(("ffn_unfused_kernel_then_agg", unfused, fl, by + 2 * 4.0 * part.numel(), [op]))
+    if "ffn_f16" in want:  # the FFN contraction with IEEE half relations (fp32 accumulation)
+        from tensor_relational_join_amd.binding import JA_F16
+
+        sp = {"b": _eq(2048, 2), "d": _eq(4096, 4), "f": _eq(11008, 4)}
+        op = Op("bd,df->bf", "contract", sp, in_dtypes=[JA_F16, JA_F16], out_dtype=JA_F16)
+        ins, out = tensors(op, 2, [(0.0, 1.0), (0.0, 0.02)])
+        runs.append(("ffn_contract_f16", lambda op=op, ins=ins, out=out: op.run(ins, out),
+                     2.0 * 2048 * 4096 * 11008, 2.0 * (2048 * 4096 + 4096 * 11008 + 2048 * 11008), [op]))
+    if "attention_f16" in want:  # [4, 32, 2048, 128] causal, 128-blocks, IEEE half Q, K, V, O
+        from tensor_relational_join_amd.binding import JA_F16
+
+        sp = {"b": _eq(4, 4), "h": _eq(32, 32), "s": _eq(2048, 16), "t": _eq(2048, 16), "d": [0, 128]}
+        op = Op("bhsd,bhtd,bhtd->bhsd", "attention", sp, "causal=s,t", in_dtypes=[JA_F16] * 3, out_dtype=JA_F16)
+        ins, out = tensors(op, 3, [(0.0, 1.0)] * 3)
+        runs.append(("attention_f16", lambda op=op, ins=ins, out=out: op.run(ins, out),
+                     2 * 2.0 * 128 * 128 * 128 * 136 * 128, 2.0 * 4 * 4 * 32 * 2048 * 128, [op]))
     if "attention" in want:  # [4, 32, 2048, 128] causal, 128-blocks: 17,408 tuples
         sp = {"b": _eq(4, 4), "h": _eq(32, 32), "s": _eq(2048, 16), "t": _eq(2048, 16), "d": [0, 128]}
         op = Op("bhsd,bhtd,bhtd->bhsd", "attention", sp, "causal=s,t")
@@ -487,6 +503,70 @@ def bench_plans(args):
     return {"workload": "plans", "steps": args.steps, "warmup": args.warmup, "results": res}
 
 
+def bench_varlen(args):
+    """Causal grouped-query attention over a packed batch whose sequence
+    ends are device data (32 query heads over 8 key-value heads, head_dim
+    128, 16 sequences summing to 16,384 tokens, lengths drawn on the GPU from
+    a fixed seed): one step is ja_dattn_run -- the device-side join, the
+    table-building kernels and the attention kernel, no host round trip.
+    Beside it, the same cuts planned on the host (join and tables built by the
+    CPU, uploaded, then the attention kernel), timed as host planning plus
+    the kernel."""
+    import torch
+
+    from tensor_relational_join_amd.device import DeviceAttention, Op
+
+    G, R, S, nseq = 8, 4, 16384, 16
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    cuts = torch.randperm(S - 1, generator=gen, device="cuda")[: nseq - 1] + 1
+    ends = torch.cat([torch.zeros(1, dtype=torch.int64, device="cuda"), cuts.sort().values,
+                      torch.full((1,), S, dtype=torch.int64, device="cuda")])
+    t = lambda lo, hi: torch.tensor([lo, hi], dtype=torch.int64, device="cuda")  # noqa: E731
+    gsp = torch.tensor(_eq(G, G), dtype=torch.int64, device="cuda")
+    splits = torch.cat([t(0, 1), gsp, t(0, R), ends, t(0, 128), ends])  # letters b g r s d t
+    da = DeviceAttention("bgrsd,bgtd,bgtd->bgrsd", {"b": 1, "g": G, "r": 1, "s": nseq, "d": 1, "t": nseq},
+                         {"b": 1, "g": G, "r": R, "s": S, "d": 128, "t": S})
+    Q = torch.empty(G * R * S * 128, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+    K = torch.empty(G * S * 128, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+    V = torch.empty_like(K).normal_(generator=gen)
+    O = torch.empty_like(Q)
+    for _ in range(args.warmup):
+        da.run(splits, Q, K, V, O)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        da.run(splits, Q, K, V, O)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    e = ends.cpu().tolist()
+    lens = [b - a for a, b in zip(e[:-1], e[1:])]
+    flops = sum(2 * 2.0 * 128 * L * (L + 1) / 2 for L in lens) * G * R
+    da.close()
+    # the same cuts planned on the host, per step
+    sp = {"b": [0, 1], "g": _eq(G, G), "r": [0, R], "s": e, "d": [0, 128], "t": e}
+    t0 = time.perf_counter()
+    op = Op("bgrsd,bgtd,bgtd->bgrsd", "attention", sp, "packed=device;causal=s,t")
+    host_plan_ms = (time.perf_counter() - t0) * 1e3
+    ins = [torch.empty(r.nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_(generator=gen) for r in op.in_rels]
+    out = torch.empty(op.out_rel.nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        op.run(ins, out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        op.run(ins, out)
+    e1.record()
+    torch.cuda.synchronize()
+    kernel_ms = e0.elapsed_time(e1) / args.steps
+    op.close()
+    return {"workload": "varlen", "steps": args.steps, "warmup": args.warmup,
+            "results": {"device_planned_ms": round(ms, 4), "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+                        "host_planned_kernel_ms": round(kernel_ms, 4), "host_plan_ms": round(host_plan_ms, 3),
+                        "sequence_lengths": lens}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -494,7 +574,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block",
                     choices=["block", "block_gqa", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy",
-                             "join", "plans"])
+                             "join", "plans", "f16", "varlen"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -511,6 +591,9 @@ def main():
         return
     if args.workload == "plans":
         print(json.dumps(bench_plans(args)))
+        return
+    if args.workload == "varlen":
+        print(json.dumps(bench_varlen(args)))
         return
     if args.workload not in BLOCKS:
         print(json.dumps(bench_kernel(args)))

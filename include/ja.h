@@ -157,6 +157,11 @@ ja_status ja_relation_block(const ja_relation_desc* rel, const int64_t* key, int
  *                   may split s and t only at sequence ends and must span
  *                   every sequence (section 3.3, Shardable Indices;
  *                   JA_ERR_DECOMP otherwise).
+ *                   "packed=device": the sequences end exactly at the cuts
+ *                   of s (and t, which must be cut alike, JA_ERR_DECOMP
+ *                   otherwise), so the ends can be data computed on the GPU
+ *                   and handed to the device-side join and planner
+ *                   (ja_djoin_*, ja_dattn_*) as split points.
  *   op "rmsnorm":   "rd,d->rd": y = x / sqrt(mean_d x^2 + eps) * gain; the
  *                   per-row sum of squares is SUM-aggregated over d blocks,
  *                   then joined 1:1 with x and gain.  params "eps=<float>"
@@ -236,14 +241,52 @@ ja_status ja_djoin_upload(ja_djoin* join, void* dev_buf, size_t bytes, void* str
  *   counts:     device int64[3]: n_tuples, n_segs, status.  status 0: valid;
  *               bit 0: some letter's split points do not start at 0, end at
  *               its extent and rise strictly; bit 1: a packed sequence
- *               letter is cut away from a sequence end.  A nonzero status
- *               leaves n_tuples = n_segs = 0 and seg_off[0] = 0.
+ *               letter is cut away from a sequence end; bit 2 (spec with
+ *               "packed=device"): the two sequence letters are cut
+ *               differently.  A nonzero status leaves n_tuples = n_segs = 0
+ *               and seg_off[0] = 0.
  *   workspace:  device, workspace_bytes.
  * Host-side argument errors return before anything is enqueued; device
  * buffers too small for the stated sizes are undefined behaviour. */
 ja_status ja_djoin_run(const ja_djoin* join, const int64_t* splits_dev, int32_t* rec, int64_t* seg_off,
                        int64_t* counts, void* workspace, void* stream);
 void ja_djoin_destroy(ja_djoin* join);
+
+/* ---- attention planned on the device (section 3.3; section 3.2 on the GPU) */
+
+/* Packed sequences whose ends are device data: attention with
+ * "packed=device" (the sequences end at the cuts of s and t), joined by the
+ * device-side join, turned into the attention kernel's tables by kernels,
+ * and computed, all enqueued on one stream with no host round trip.
+ *
+ * ja_dattn_create: host only.  extents / intervals per letter as for
+ * ja_djoin_create; s and t have one interval per sequence (the same count),
+ * the head dimension (128) one; every other letter is cut into near-equal
+ * intervals.  dtype JA_BF16 or JA_F16 (Q, K, V, O alike).  JA_ERR_SPEC for
+ * any other spec.
+ *
+ * Layouts (caller-owned, 16-byte aligned): Q and O are the relation
+ * [batch..., group..., S, D] blocked by the intervals of its batch and group
+ * letters only (s and d whole): blocks back to back in key order, each dense
+ * row-major; K and V likewise over [batch..., S, D] with their batch
+ * letters.  These layouts do not depend on where the sequences end. */
+typedef struct ja_dattn ja_dattn;
+ja_status ja_dattn_create(const ja_spec* spec, const int64_t* extents, const int32_t* intervals, int32_t dtype,
+                          ja_dattn** out);
+/* table_bytes: device table, uploaded once (256-byte aligned buffer);
+ * workspace_bytes: scratch of one run (256-byte aligned); n_splits: int64
+ * entries of the split array. */
+ja_status ja_dattn_device_bytes(const ja_dattn* attn, size_t* table_bytes, size_t* workspace_bytes,
+                                int64_t* n_splits);
+ja_status ja_dattn_upload(ja_dattn* attn, void* dev_buf, size_t bytes, void* stream);
+/* Enqueue join, table building and attention on `stream`.  splits_dev:
+ * every letter's split points in letter order (device int64), those of s and
+ * t being the sequence ends 0 < e1 < ... < S.  counts: device int64[3], the
+ * join's tuple and segment counts and status (ja_djoin_run); with a nonzero
+ * status nothing is computed and O is not written. */
+ja_status ja_dattn_run(const ja_dattn* attn, const int64_t* splits_dev, const void* Q, const void* K, const void* V,
+                       void* O, int64_t* counts, void* workspace, void* stream);
+void ja_dattn_destroy(ja_dattn* attn);
 
 /* ---- logical optimization (section 4) ------------------------------------ */
 

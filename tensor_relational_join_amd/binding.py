@@ -78,6 +78,11 @@ _SIGS = {
     "ja_djoin_upload": (_st, [_vp, _vp, _sz, _vp]),
     "ja_djoin_run": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ja_djoin_destroy": (None, [_vp]),
+    "ja_dattn_create": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, ctypes.POINTER(_vp)]),
+    "ja_dattn_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_i64)]),
+    "ja_dattn_upload": (_st, [_vp, _vp, _sz, _vp]),
+    "ja_dattn_run": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ja_dattn_destroy": (None, [_vp]),
     "ja_graph_create": (_st, [ctypes.POINTER(_vp)]),
     "ja_graph_destroy": (None, [_vp]),
     "ja_graph_add_input": (_st, [_vp, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
@@ -328,6 +333,34 @@ def ja_djoin_run(join: int, splits_dev: int, rec: int, seg_off: int, counts: int
 
 def ja_djoin_destroy(join: int):
     _lib.ja_djoin_destroy(_vp(join))
+
+
+def ja_dattn_create(spec: int, extents: Sequence[int], intervals: Sequence[int], dtype: int = JA_BF16) -> int:
+    n = len(extents)
+    h = _vp()
+    _check(_lib.ja_dattn_create(_vp(spec), (_i64 * n)(*extents), (_i32 * n)(*intervals), dtype, ctypes.byref(h)))
+    return h.value
+
+
+def ja_dattn_device_bytes(attn: int):
+    """(table_bytes, workspace_bytes, n_splits)."""
+    tb, wb, ns = _sz(), _sz(), _i64()
+    _check(_lib.ja_dattn_device_bytes(_vp(attn), ctypes.byref(tb), ctypes.byref(wb), ctypes.byref(ns)))
+    return tb.value, wb.value, ns.value
+
+
+def ja_dattn_upload(attn: int, dev_buf: int, nbytes: int, stream: int = 0):
+    _check(_lib.ja_dattn_upload(_vp(attn), _vp(dev_buf), nbytes, _vp(stream)))
+
+
+def ja_dattn_run(attn: int, splits_dev: int, q: int, k: int, v: int, o: int, counts: int, workspace: int,
+                 stream: int = 0):
+    _check(_lib.ja_dattn_run(_vp(attn), _vp(splits_dev), _vp(q), _vp(k), _vp(v), _vp(o), _vp(counts),
+                             _vp(workspace), _vp(stream)))
+
+
+def ja_dattn_destroy(attn: int):
+    _lib.ja_dattn_destroy(_vp(attn))
 
 
 JA_PLAN_OPTIMAL, JA_PLAN_GREEDY, JA_PLAN_RANDOM, JA_PLAN_DEVICE = 0, 1, 2, 3

@@ -66,8 +66,11 @@ __device__ __forceinline__ void at_dma16(at_i32x4_t rsrc, uint32_t lds_byte, uin
 // barrier per step.  Masks are only evaluated on steps that cross the
 // causal diagonal or the end of a key block, and O is rescaled only when
 // some query's running maximum moved.
+// With tables built on the device, the grid covers an upper bound of tiles and
+// the count is read from ntiles_dev (NULL: the grid is exact).
 template <bool PACKED, bool F16>
-__global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile* __restrict__ tiles, int ntiles,
+__global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile* __restrict__ tiles,
+                                                               const int32_t* __restrict__ ntiles_dev,
                                                                const AttnSeg* __restrict__ segs,
                                                                const AttnTuple* __restrict__ tuples,
                                                                const int32_t* __restrict__ seq_ends, int nseq,
@@ -76,6 +79,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                                                                const uint16_t* __restrict__ V,
                                                                uint16_t* __restrict__ O, float scale_log2, int causal) {
     constexpr int D = ATTN_D;
+    if (ntiles_dev && (int)blockIdx.x >= *ntiles_dev) return;
     extern __shared__ __attribute__((aligned(16))) uint16_t at_lds[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)at_lds;
 
@@ -402,10 +406,23 @@ hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles
     auto kernel = nseq ? (f16 ? attention_kernel<true, true> : attention_kernel<true, false>)
                        : (f16 ? attention_kernel<false, true> : attention_kernel<false, false>);
     hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(AT_THREADS), lds, stream,
-                       (const AttnTile*)(t + tiles_off), ntiles, (const AttnSeg*)(t + segs_off),
+                       (const AttnTile*)(t + tiles_off), (const int32_t*)nullptr, (const AttnSeg*)(t + segs_off),
                        (const AttnTuple*)(t + tuples_off), nseq ? (const int32_t*)(t + seq_off) : nullptr, nseq,
                        (const uint16_t*)Q, (const uint16_t*)K,
                        (const uint16_t*)V, (uint16_t*)O, scale_log2, causal);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_dev(const AttnTile* tiles, const int32_t* ntiles_dev, uint32_t max_tiles,
+                                const AttnSeg* segs, const AttnTuple* tuples, const int32_t* seq_ends, int32_t nseq,
+                                const void* Q, const void* K, const void* V, void* O, float scale, int32_t causal,
+                                int32_t f16, hipStream_t stream) {
+    const float scale_log2 = scale * 1.4426950408889634f;
+    const unsigned lds = 2u * AT_STAGE * sizeof(uint16_t);
+    auto kernel = f16 ? attention_kernel<true, true> : attention_kernel<true, false>;
+    hipLaunchKernelGGL(kernel, dim3(max_tiles), dim3(AT_THREADS), lds, stream, tiles, ntiles_dev, segs, tuples,
+                       seq_ends, nseq, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)O,
+                       scale_log2, causal);
     return hipGetLastError();
 }
 

@@ -112,7 +112,8 @@ __device__ int32_t dj_validate_block(const DJoinArgs& a, const int64_t* __restri
         const int64_t x = sp[e];
         if (j == 0 ? x != 0 : x <= sp[e - 1]) bad |= DJ_BAD_SPLITS;
         if (j == n && x != ext) bad |= DJ_BAD_SPLITS;
-        if ((l == a.ps || l == a.pt) && j > 0 && j < n) {
+        if (l == a.ps && a.nends < 0 && x != sp[a.sp_off[a.pt] + j]) bad |= DJ_BAD_SEQS;
+        if ((l == a.ps || l == a.pt) && a.nends >= 0 && j > 0 && j < n) {
             // an interior cut must be a sequence end (binary search)
             int32_t lo = 0, hi = a.nends;
             while (lo < hi) {

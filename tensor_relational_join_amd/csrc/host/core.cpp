@@ -140,9 +140,14 @@ static ja_status parse_params(const char* params, ja_spec* s) {
                 if (x < 0) return fail(JA_ERR_SPEC, "eps must be >= 0");
                 s->eps = x;
             }
+        } else if (k == "packed" && v == "device") {
+            // the sequence ends are the split points of the sequence letters
+            s->packed.clear();
+            s->packed_device = true;
         } else if (k == "packed") {
             // ascending positive sequence ends, comma separated
             s->packed.clear();
+            s->packed_device = false;
             size_t q = 0;
             while (q <= v.size()) {
                 size_t c = v.find(',', q);
@@ -241,7 +246,8 @@ static ja_status parse_spec(const char* einsum, const char* op, const char* para
     } else {
         return fail(JA_ERR_SPEC, "unknown op " + o);
     }
-    if (s->kind != JA_OP_ATTENTION && !s->packed.empty()) return fail(JA_ERR_SPEC, "packed applies to attention only");
+    if (s->kind != JA_OP_ATTENTION && (!s->packed.empty() || s->packed_device))
+        return fail(JA_ERR_SPEC, "packed applies to attention only");
     if (!s->causal || s->kind == JA_OP_ATTENTION) return JA_OK;
     return fail(JA_ERR_SPEC, "causal applies to attention only");
 }
@@ -269,7 +275,7 @@ ja_status build_tuples(const ja_spec* s, const ja_decomp* d, ja_tuples& t) {
         it = s->letter_index(s->causal_t);
     }
     int ps = -1, pt = -1;  // packed sequences: the query and key position letters
-    if (!s->packed.empty()) {
+    if (!s->packed.empty() || s->packed_device) {
         const std::string &q = s->ins[0], &k = s->ins[1];
         ps = s->letter_index(q[q.size() - 2]);
         pt = s->letter_index(k[k.size() - 2]);
@@ -423,6 +429,14 @@ ja_status ja_decomp_create(const ja_spec* s, const int64_t* extents, const int32
         if (d->sp[id].size() != 2) {
             delete d;
             return fail(JA_ERR_DECOMP, "attention: the head-dimension letter cannot be split");
+        }
+        if (s->packed_device) {
+            // sequence ends given by the cuts themselves: both sequence letters cut alike
+            const std::string &q = s->ins[0], &k = s->ins[1];
+            if (d->sp[s->letter_index(q[q.size() - 2])] != d->sp[s->letter_index(k[k.size() - 2])]) {
+                delete d;
+                return fail(JA_ERR_DECOMP, "attention: packed=device needs the same cuts on both sequence letters");
+            }
         }
         if (!s->packed.empty()) {
             // packed sequences: the sequence letters span every sequence and may be

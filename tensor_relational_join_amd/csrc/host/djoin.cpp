@@ -54,6 +54,11 @@ ja_status ja_djoin_create(const ja_spec* s, const int64_t* extents, const int32_
         const std::string &q = s->ins[0], &k = s->ins[1];
         if (intervals[s->letter_index(q.back())] != 1)
             return fail(JA_ERR_DECOMP, "attention: the head-dimension letter cannot be split");
+        if (s->packed_device) {
+            const int ls = s->letter_index(q[q.size() - 2]), lt = s->letter_index(k[k.size() - 2]);
+            if (extents[ls] != extents[lt] || intervals[ls] != intervals[lt])
+                return fail(JA_ERR_DECOMP, "attention: packed=device needs the same cuts on both sequence letters");
+        }
         if (!s->packed.empty())
             for (char c : {q[q.size() - 2], k[k.size() - 2]}) {
                 const int l = s->letter_index(c);
@@ -102,12 +107,12 @@ ja_status ja_djoin_create(const ja_spec* s, const int64_t* extents, const int32_
         a.is = s->letter_index(s->causal_s);
         a.it = s->letter_index(s->causal_t);
     }
-    if (!s->packed.empty()) {
+    if (!s->packed.empty() || s->packed_device) {
         const std::string &q = s->ins[0], &k = s->ins[1];
         a.ps = s->letter_index(q[q.size() - 2]);
         a.pt = s->letter_index(k[k.size() - 2]);
         j->ends = s->packed;
-        a.nends = (int32_t)s->packed.size();
+        a.nends = s->packed_device ? -1 : (int32_t)s->packed.size();
     }
     if (j->ends.empty()) j->ends.assign(2, 0);  // a non-empty table
     size_t o = 0;

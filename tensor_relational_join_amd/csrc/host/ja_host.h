@@ -65,6 +65,7 @@ struct ja_spec {
     bool causal = false;
     char causal_s = 0, causal_t = 0;
     std::vector<int64_t> packed;  // attention: ascending ends of sequences packed along the s and t letters
+    bool packed_device = false;   // attention: the sequences end exactly at the cuts of the s and t letters
     double eps = 1e-6;
     int letter_index(char c) const {
         auto p = letters.find(c);

@@ -280,6 +280,9 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
     p->causal = s->causal ? 1 : 0;
     const int ls = s->letter_index(cs), lt = s->letter_index(ct);
     const int64_t nt = t.count(), nseg = (int64_t)t.seg.size() - 1;
+    // packed sequence ends: given, or the cuts of the sequence letter
+    const std::vector<int64_t> ends = s->packed_device ? std::vector<int64_t>(d->sp[ls].begin() + 1, d->sp[ls].end())
+                                                       : s->packed;
     std::vector<AttnTuple> tuples(nt);
     std::vector<AttnSeg> segs(nseg);
     const int64_t lim = ((int64_t)1 << 31) - 1;
@@ -322,11 +325,11 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
                 // the sequences of the tile's rows when sequences are packed)
                 int64_t last = g.s_lo + std::min<int64_t>(S, s0 + ATTN_TQ) - 1, w = 0;
                 int64_t klo = 0, khi = INT64_MAX;
-                if (!s->packed.empty()) {
-                    auto e1 = std::upper_bound(s->packed.begin(), s->packed.end(), (int64_t)g.s_lo + s0);
-                    klo = e1 == s->packed.begin() ? 0 : *(e1 - 1);
-                    auto e2 = std::upper_bound(s->packed.begin(), s->packed.end(), last);
-                    khi = e2 == s->packed.end() ? s->packed.back() : *e2;
+                if (!ends.empty()) {
+                    auto e1 = std::upper_bound(ends.begin(), ends.end(), (int64_t)g.s_lo + s0);
+                    klo = e1 == ends.begin() ? 0 : *(e1 - 1);
+                    auto e2 = std::upper_bound(ends.begin(), ends.end(), last);
+                    khi = e2 == ends.end() ? ends.back() : *e2;
                 }
                 for (int32_t k = g.t_begin; k < g.t_end; ++k) {
                     int64_t a = std::max<int64_t>(tuples[k].t_lo, klo);
@@ -347,10 +350,10 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
     p->ntiles = (int32_t)tiles.size();
     p->segs_off = put(p->table, segs);
     p->tuples_off = put(p->table, tuples);
-    if (!s->packed.empty()) {
-        std::vector<int32_t> ends(s->packed.begin(), s->packed.end());
-        p->seq_off = put(p->table, ends);
-        p->nseq = (int32_t)ends.size();
+    if (!ends.empty()) {
+        std::vector<int32_t> e32(ends.begin(), ends.end());
+        p->seq_off = put(p->table, e32);
+        p->nseq = (int32_t)e32.size();
     }
     return JA_OK;
 }

@@ -35,13 +35,14 @@ struct DJDiv {
 enum : int32_t {
     DJ_BAD_SPLITS = 1,  // split points do not start at 0, end at the extent and rise strictly
     DJ_BAD_PACKED = 2,  // a packed sequence letter cut away from a sequence end
+    DJ_BAD_SEQS = 4,    // sequences given by the cuts: the two sequence letters cut differently
 };
 
 struct DJoinArgs {
     int32_t nl;           // letters
     int32_t is, it;       // causal query / key letters (-1: no causal predicate)
     int32_t ps, pt;       // packed-sequence query / key letters (-1: not packed)
-    int32_t nends;        // packed sequence ends in the table
+    int32_t nends;        // packed sequence ends in the table (-1: the cuts are the ends)
     uint32_t ncell;       // grid cells (product of the interval counts)
     uint32_t ngroup;      // group-by keys (product of the group-by letters' counts)
     uint32_t nchunk;      // workgroups over cells

@@ -207,3 +207,51 @@ class DeviceJoin:
             self.close()
         except Exception:
             pass
+
+
+class DeviceAttention:
+    """Attention over packed sequences whose ends are device data
+    (ja_dattn_*, spec params with "packed=device"): ``run(splits, Q, K, V,
+    O)`` enqueues the device-side join, the kernels that build the attention
+    tables and the attention kernel on one stream.  ``splits`` holds every
+    letter's split points (letter order), those of s and t being the sequence
+    ends.  ``counts`` keeps the join's [n_tuples, n_segs, status]."""
+
+    def __init__(self, einsum: str, counts: Dict[str, int], extents: Dict[str, int],
+                 params: str = "packed=device;causal=s,t", dtype: int = JA_BF16, device="cuda",
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.spec = B.ja_spec_create(einsum, "attention", params)
+        self.da = None
+        try:
+            self.letters = B.ja_spec_letters(self.spec)
+            self.da = B.ja_dattn_create(self.spec, [extents[c] for c in self.letters],
+                                        [counts[c] for c in self.letters], dtype)
+            tb, wb, self.n_splits = B.ja_dattn_device_bytes(self.da)
+            self.table = torch.empty(max(tb, 256), dtype=torch.uint8, device=device)
+            B.ja_dattn_upload(self.da, self.table.data_ptr(), self.table.numel(), stream_handle(stream))
+            self.workspace = torch.empty(max(wb, 256), dtype=torch.uint8, device=device)
+            self.counts = torch.zeros(3, dtype=torch.int64, device=device)
+        except Exception:
+            self.close()
+            raise
+
+    def run(self, splits: torch.Tensor, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor,
+            stream: Optional[torch.cuda.Stream] = None):
+        if splits.dtype != torch.int64 or not splits.is_cuda or splits.numel() != self.n_splits:
+            raise ValueError("splits: a device int64 tensor of %d split points" % self.n_splits)
+        B.ja_dattn_run(self.da, splits.data_ptr(), Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                       self.counts.data_ptr(), self.workspace.data_ptr(), stream_handle(stream))
+
+    def close(self):
+        if self.da:
+            B.ja_dattn_destroy(self.da)
+            self.da = None
+        if self.spec:
+            B.ja_spec_destroy(self.spec)
+            self.spec = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

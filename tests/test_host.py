@@ -382,3 +382,48 @@ def test_device_join_sizes_and_errors(B):
             assert e.value.name == "JA_ERR_DECOMP"
     finally:
         B.ja_spec_destroy(s)
+
+
+def test_packed_device_spec_and_planner_checks(B, orc):
+    """"packed=device": the sequences end at the cuts of s (and t, cut
+    alike).  The host join keeps the block-diagonal pairs; the device planner
+    takes only such specs, head dimension 128, bf16 or fp16."""
+    with pytest.raises(B.JaError) as e:
+        B.ja_spec_create("ij,jk->ik", "contract", "packed=device")
+    assert e.value.name == "JA_ERR_SPEC"
+    cuts = [0, 300, 1000, 1024]
+    splits = {"b": [0, 1], "h": [0, 2, 4], "s": cuts, "d": [0, 128], "t": cuts}
+    letters, rec, seg = _tuples(B, "bhsd,bhtd,bhtd->bhsd", "attention", splits, "packed=device;causal=s,t")
+    o_rec, o_seg = orc.tuple_records(list(letters), splits, group_by=list("bhsd"), causal=("s", "t"),
+                                     packed=("s", "t", cuts[1:]))
+    assert np.array_equal(rec, o_rec) and np.array_equal(seg, o_seg) and rec.shape[0] == 2 * 3
+    s = B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", "packed=device;causal=s,t")
+    try:
+        with pytest.raises(B.JaError) as e:  # s and t cut differently
+            B.ja_decomp_create(s, [1, 4, 1024, 128, 1024], [1, 1, 2, 1, 2],
+                               [[0, 1], [0, 4], [0, 500, 1024], [0, 128], [0, 600, 1024]])
+        assert e.value.name == "JA_ERR_DECOMP"
+        da = B.ja_dattn_create(s, [1, 4, 1024, 128, 1024], [1, 2, 3, 1, 3])
+        try:
+            tb, wb, ns = B.ja_dattn_device_bytes(da)
+            assert tb > 0 and wb > 0 and ns == 2 + 3 + 4 + 2 + 4
+            with pytest.raises(B.JaError) as e:
+                B.ja_dattn_run(da, 256, 256, 256, 256, 256, 256, 256)
+            assert e.value.name == "JA_ERR_STATE"
+        finally:
+            B.ja_dattn_destroy(da)
+        for ext, iv, dt, name in (([1, 4, 1024, 64, 1024], [1, 2, 3, 1, 3], B.JA_BF16, "JA_ERR_UNSUPPORTED"),
+                                  ([1, 4, 1024, 128, 1024], [1, 2, 3, 1, 2], B.JA_BF16, "JA_ERR_DECOMP"),
+                                  ([1, 4, 1024, 128, 1024], [1, 2, 3, 1, 3], B.JA_F32, "JA_ERR_DTYPE")):
+            with pytest.raises(B.JaError) as e:
+                B.ja_dattn_create(s, ext, iv, dt)
+            assert e.value.name == name
+    finally:
+        B.ja_spec_destroy(s)
+    s = B.ja_spec_create("bhsd,bhtd,bhtd->bhsd", "attention", "causal=s,t")
+    try:
+        with pytest.raises(B.JaError) as e:
+            B.ja_dattn_create(s, [1, 4, 1024, 128, 1024], [1, 2, 3, 1, 3])
+        assert e.value.name == "JA_ERR_SPEC"
+    finally:
+        B.ja_spec_destroy(s)
