@@ -14,248 +14,11 @@
 #include <cmath>
 #include <cstring>
 
-#include "ja_host.h"
+#include "plan_internal.h"
 
 using namespace ja;
 
-struct ja_plan {
-    ja_op_kind kind;
-    std::vector<uint8_t> table;
-    void* dev = nullptr;
-    int32_t n_in = 0;
-    // contract
-    int64_t tiles_off = 0, segs_off = 0, tuples_off = 0;
-    int32_t ntiles = 0;
-    int64_t utiles_off = 0, usegs_off = 0;
-    int32_t nutiles = 0;
-    int64_t atiles_off = 0, asegs_off = 0, apoff_off = 0;
-    int32_t natiles = 0;
-    int32_t in_dtype = 0, out_dtype = 0, a_layout = 0, b_layout = 0;
-    int32_t gemm_dma = 0;  // bf16 operands reachable through 32-bit buffer offsets
-    int64_t partial_elems = 0;
-    // attention
-    float scale = 0.f;
-    int32_t causal = 0;
-    int64_t seq_off = 0;  // packed sequences: int32 sequence ends in the table
-    int32_t nseq = 0;
-    // rmsnorm
-    int64_t rsplit_off = 0, nblk_off = 0;
-    int32_t nrb = 0, ndb = 0, D = 0, norm_vec = 0, norm_w = 0;
-    int64_t rows = 0;
-    float eps = 0.f;
-    // 1:1 joins
-    int64_t n = 0;
-};
-
 namespace {
-
-// Append a POD array to the table at a 16-byte aligned offset.
-template <class T>
-int64_t put(std::vector<uint8_t>& tab, const std::vector<T>& v) {
-    size_t off = (tab.size() + 15) & ~(size_t)15;
-    tab.resize(off + v.size() * sizeof(T));
-    if (!v.empty()) std::memcpy(tab.data() + off, v.data(), v.size() * sizeof(T));
-    return (int64_t)off;
-}
-
-// Check that relation `r` is the projection grid the decomposition asks for:
-// one dimension per letter of `s`, extents and split points equal to the
-// decomposition's for those letters.
-ja_status match_rel(const Rel& r, const std::string& s, const ja_spec* sp, const ja_decomp* d, const char* what) {
-    if (r.rank != (int)s.size())
-        return fail(JA_ERR_SHAPE, std::string(what) + ": rank differs from its letters '" + s + "'");
-    for (int k = 0; k < r.rank; ++k) {
-        int l = sp->letter_index(s[k]);
-        if (r.shape[k] != d->ext[l])
-            return fail(JA_ERR_SHAPE, std::string(what) + ": extent of letter " + s[k] + " differs from the decomposition");
-        if (r.sp[k] != d->sp[l])
-            return fail(JA_ERR_SHAPE, std::string(what) + ": blocking of letter " + s[k] +
-                                          " differs from the decomposition (repartition it first)");
-    }
-    return JA_OK;
-}
-
-// Interval index of letter c in tuple record `rec`.
-inline int64_t coord(const ja_spec* s, const int32_t* rec, char c) { return rec[s->letter_index(c)]; }
-
-int64_t block_of(const Rel& r, const std::string& letters, const ja_spec* s, const int32_t* rec) {
-    int64_t key[JA_MAX_RANK];
-    for (size_t k = 0; k < letters.size(); ++k) key[k] = coord(s, rec, letters[k]);
-    return r.block_index(key);
-}
-
-int64_t extent_of(const ja_decomp* d, const ja_spec* s, const int32_t* rec, const std::string& letters) {
-    int64_t n = 1;
-    for (char c : letters) {
-        int l = s->letter_index(c);
-        n *= d->sp[l][rec[l] + 1] - d->sp[l][rec[l]];
-    }
-    return n;
-}
-
-// Split an operand's letters into role runs.  Returns false unless the
-// operand is [batch run][first run][second run] with the two named roles in
-// either order; `first_is` reports which role came first.
-bool runs(const std::string& op, const std::string& batch, const std::string& r1, const std::string& r2,
-          bool& r1_first) {
-    size_t nb = batch.size();
-    if (op.substr(0, nb) != batch) return false;
-    std::string rest = op.substr(nb);
-    if (rest == r1 + r2) {
-        r1_first = true;
-        return true;
-    }
-    if (rest == r2 + r1) {
-        r1_first = false;
-        return true;
-    }
-    return false;
-}
-
-ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_tuples& t,
-                        const ja_relation_desc* const* in, const ja_relation_desc* out) {
-    Rel A, B, C;
-    ja_status st;
-    if ((st = rel_from_desc(in[0], A)) || (st = rel_from_desc(in[1], B)) || (st = rel_from_desc(out, C))) return st;
-    const std::string &sa = s->ins[0], &sb = s->ins[1], &sc = s->out;
-    if ((st = match_rel(A, sa, s, d, "operand A")) || (st = match_rel(B, sb, s, d, "operand B")) ||
-        (st = match_rel(C, sc, s, d, "output")))
-        return st;
-    if (A.dtype != B.dtype) return fail(JA_ERR_DTYPE, "contract operands must share a dtype");
-    if (A.dtype == JA_F32) {
-        if (C.dtype != JA_F32) return fail(JA_ERR_DTYPE, "f32 contraction writes f32");
-    } else if (A.dtype == JA_BF16 || A.dtype == JA_F16) {
-        if (C.dtype != A.dtype && C.dtype != JA_F32)
-            return fail(JA_ERR_DTYPE, "a 16-bit contraction writes its input format or f32");
-    } else {
-        return fail(JA_ERR_DTYPE, "contract supports f32, bf16 and f16 operands");
-    }
-    const bool h16 = A.dtype != JA_F32;  // bf16 or f16: the MFMA kernels
-    // roles of the letters: batch (A, B, C), M (A, C), N (B, C), K (A, B)
-    std::string batch, M, N, K;
-    for (char c : sc) {
-        bool ia = sa.find(c) != std::string::npos, ib = sb.find(c) != std::string::npos;
-        if (ia && ib) batch.push_back(c);
-    }
-    for (char c : sc)
-        if (batch.find(c) == std::string::npos) (sa.find(c) != std::string::npos ? M : N).push_back(c);
-    for (char c : sa)
-        if (sc.find(c) == std::string::npos) K.push_back(c);
-    // M and N in the output's order; K in A's order
-    std::string Mo, No;
-    for (char c : sc) {
-        if (M.find(c) != std::string::npos) Mo.push_back(c);
-        if (N.find(c) != std::string::npos) No.push_back(c);
-    }
-    bool a_m_first = true, b_k_first = true;
-    if (sc != batch + Mo + No || !runs(sa, batch, Mo, K, a_m_first) || !runs(sb, batch, K, No, b_k_first))
-        return fail(JA_ERR_UNSUPPORTED,
-                    "contract needs operands laid out as [batch][rows][cols] runs with matching letter orders");
-    p->a_layout = a_m_first ? JA_A_MK : JA_A_KM;
-    p->b_layout = b_k_first ? JA_B_KN : JA_B_NK;
-    p->in_dtype = A.dtype;
-    p->out_dtype = C.dtype;
-    const int TM = h16 ? GEMM_BF16_TM : GEMM_F32_TM;
-    const int TN = h16 ? GEMM_BF16_TN : GEMM_F32_TN;
-
-    const int64_t nt = t.count(), nseg = (int64_t)t.seg.size() - 1;
-    std::vector<GemmTuple> tuples(nt);
-    std::vector<GemmSeg> segs(nseg), usegs(nt);
-    std::vector<GemmTile> tiles, utiles;
-    std::vector<AggTile> atiles;
-    std::vector<AggSeg> asegs(nseg);
-    std::vector<int64_t> poff(nt);
-    int64_t part = 0;
-    const int64_t lim = ((int64_t)1 << 31) - 1;
-    for (int64_t i = 0; i < nt; ++i) {
-        const int32_t* rec = &t.rec[i * t.nl];
-        int64_t nb = extent_of(d, s, rec, batch), m = extent_of(d, s, rec, Mo), n = extent_of(d, s, rec, No),
-                k = extent_of(d, s, rec, K);
-        if (m > lim || n > lim || k > lim) return fail(JA_ERR_UNSUPPORTED, "block extent beyond 2^31");
-        GemmTuple& g = tuples[i];
-        g.a_off = A.blk_off[block_of(A, sa, s, rec)];
-        g.b_off = B.blk_off[block_of(B, sb, s, rec)];
-        g.a_bstride = m * k;
-        g.b_bstride = k * n;
-        g.K = (int32_t)k;
-        g.lda = (int32_t)(a_m_first ? k : m);
-        g.ldb = (int32_t)(b_k_first ? n : k);
-        g.pad = 0;
-        // unfused: every tuple is its own segment writing an f32 partial block
-        GemmSeg& u = usegs[i];
-        u.c_off = part;
-        u.c_bstride = m * n;
-        u.M = (int32_t)m;
-        u.N = (int32_t)n;
-        u.ldc = (int32_t)n;
-        u.t_begin = (int32_t)i;
-        u.t_end = (int32_t)i + 1;
-        u.pad = 0;
-        poff[i] = part;
-        part += nb * m * n;
-        for (int32_t b = 0; b < nb; ++b)
-            for (int32_t m0 = 0; m0 < m; m0 += TM)
-                for (int32_t n0 = 0; n0 < n; n0 += TN) utiles.push_back({(int32_t)i, m0, n0, b});
-    }
-    for (int64_t sg = 0; sg < nseg; ++sg) {
-        const int32_t* rec = &t.rec[t.seg[sg] * t.nl];
-        int64_t nb = extent_of(d, s, rec, batch), m = extent_of(d, s, rec, Mo), n = extent_of(d, s, rec, No);
-        GemmSeg& g = segs[sg];
-        g.c_off = C.blk_off[block_of(C, sc, s, rec)];
-        g.c_bstride = m * n;
-        g.M = (int32_t)m;
-        g.N = (int32_t)n;
-        g.ldc = (int32_t)n;
-        g.t_begin = (int32_t)t.seg[sg];
-        g.t_end = (int32_t)t.seg[sg + 1];
-        g.pad = 0;
-        // grouped order: GEMM_GROUP_M row tiles, then every column tile, so a
-        // contiguous run of the list forms a compact block of output tiles
-        const int32_t mt = (int32_t)((m + TM - 1) / TM), ntl = (int32_t)((n + TN - 1) / TN);
-        for (int32_t b = 0; b < nb; ++b)
-            for (int32_t mg = 0; mg < mt; mg += GEMM_GROUP_M)
-                for (int32_t nj = 0; nj < ntl; ++nj)
-                    for (int32_t mi = mg; mi < std::min(mt, mg + GEMM_GROUP_M); ++mi)
-                        tiles.push_back({(int32_t)sg, mi * TM, nj * TN, b});
-        AggSeg& a = asegs[sg];
-        a.out_off = g.c_off;
-        if (nb * m * n > lim) return fail(JA_ERR_UNSUPPORTED, "output block beyond 2^31 elements");
-        a.nelem = (int32_t)(nb * m * n);
-        a.t_begin = g.t_begin;
-        a.t_end = g.t_end;
-        a.pad = 0;
-        for (int32_t e0 = 0; e0 < a.nelem; e0 += AGG_CHUNK) atiles.push_back({(int32_t)sg, e0});
-    }
-    if ((int64_t)tiles.size() > lim || (int64_t)utiles.size() > lim) return fail(JA_ERR_UNSUPPORTED, "too many tiles");
-    if (h16) {
-        // the MFMA kernel moves 8 bf16 (16 bytes) at a time along every contiguous axis
-        for (const GemmTuple& g : tuples) {
-            bool ok = g.K % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_off % 8 == 0 && g.b_off % 8 == 0 &&
-                      g.a_bstride % 8 == 0 && g.b_bstride % 8 == 0;
-            if (!ok) return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction needs block extents that are multiples of 8");
-        }
-        for (const GemmSeg& g : segs)
-            if ((!a_m_first && g.M % 8) || (b_k_first && g.N % 8))
-                return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction needs block extents that are multiples of 8");
-        // the direct-to-LDS kernel addresses each operand matrix with 32-bit byte offsets
-        bool dma = true;
-        for (const GemmTuple& g : tuples) dma = dma && g.a_bstride * 2 < lim && g.b_bstride * 2 < lim;
-        p->gemm_dma = dma ? 1 : 0;
-    }
-    p->partial_elems = part;
-    p->tiles_off = put(p->table, tiles);
-    p->ntiles = (int32_t)tiles.size();
-    p->segs_off = put(p->table, segs);
-    p->tuples_off = put(p->table, tuples);
-    p->utiles_off = put(p->table, utiles);
-    p->nutiles = (int32_t)utiles.size();
-    p->usegs_off = put(p->table, usegs);
-    p->atiles_off = put(p->table, atiles);
-    p->natiles = (int32_t)atiles.size();
-    p->asegs_off = put(p->table, asegs);
-    p->apoff_off = put(p->table, poff);
-    return JA_OK;
-}
 
 ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_tuples& t,
                          const ja_relation_desc* const* in, const ja_relation_desc* out) {

@@ -1,0 +1,181 @@
+// plan_contract.cpp -- the contraction planner: the fused GEMM-shaped tables
+// (output tiles of every segment, segments, tuples) of a contraction's
+// join-agg spec ("Every Kernel Is a Join", paperpeel full text, section 3.2,
+// Examples 3.8 and 3.9: block products whose partial results are SUM-aggregated
+// per output block).
+#include <algorithm>
+#include <climits>
+#include <cmath>
+
+#include "plan_internal.h"
+
+namespace ja {
+namespace {
+
+// Split an operand's letters into role runs.  Returns false unless the
+// operand is [batch run][first run][second run] with the two named roles in
+// either order; `first_is` reports which role came first.
+bool runs(const std::string& op, const std::string& batch, const std::string& r1, const std::string& r2,
+          bool& r1_first) {
+    size_t nb = batch.size();
+    if (op.substr(0, nb) != batch) return false;
+    std::string rest = op.substr(nb);
+    if (rest == r1 + r2) {
+        r1_first = true;
+        return true;
+    }
+    if (rest == r2 + r1) {
+        r1_first = false;
+        return true;
+    }
+    return false;
+}
+
+}  // namespace
+
+ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_tuples& t,
+                        const ja_relation_desc* const* in, const ja_relation_desc* out) {
+    Rel A, B, C;
+    ja_status st;
+    if ((st = rel_from_desc(in[0], A)) || (st = rel_from_desc(in[1], B)) || (st = rel_from_desc(out, C))) return st;
+    const std::string &sa = s->ins[0], &sb = s->ins[1], &sc = s->out;
+    if ((st = match_rel(A, sa, s, d, "operand A")) || (st = match_rel(B, sb, s, d, "operand B")) ||
+        (st = match_rel(C, sc, s, d, "output")))
+        return st;
+    if (A.dtype != B.dtype) return fail(JA_ERR_DTYPE, "contract operands must share a dtype");
+    if (A.dtype == JA_F32) {
+        if (C.dtype != JA_F32) return fail(JA_ERR_DTYPE, "f32 contraction writes f32");
+    } else if (A.dtype == JA_BF16 || A.dtype == JA_F16) {
+        if (C.dtype != A.dtype && C.dtype != JA_F32)
+            return fail(JA_ERR_DTYPE, "a 16-bit contraction writes its input format or f32");
+    } else {
+        return fail(JA_ERR_DTYPE, "contract supports f32, bf16 and f16 operands");
+    }
+    const bool h16 = A.dtype != JA_F32;  // bf16 or f16: the MFMA kernels
+    // roles of the letters: batch (A, B, C), M (A, C), N (B, C), K (A, B)
+    std::string batch, M, N, K;
+    for (char c : sc) {
+        bool ia = sa.find(c) != std::string::npos, ib = sb.find(c) != std::string::npos;
+        if (ia && ib) batch.push_back(c);
+    }
+    for (char c : sc)
+        if (batch.find(c) == std::string::npos) (sa.find(c) != std::string::npos ? M : N).push_back(c);
+    for (char c : sa)
+        if (sc.find(c) == std::string::npos) K.push_back(c);
+    // M and N in the output's order; K in A's order
+    std::string Mo, No;
+    for (char c : sc) {
+        if (M.find(c) != std::string::npos) Mo.push_back(c);
+        if (N.find(c) != std::string::npos) No.push_back(c);
+    }
+    bool a_m_first = true, b_k_first = true;
+    if (sc != batch + Mo + No || !runs(sa, batch, Mo, K, a_m_first) || !runs(sb, batch, K, No, b_k_first))
+        return fail(JA_ERR_UNSUPPORTED,
+                    "contract needs operands laid out as [batch][rows][cols] runs with matching letter orders");
+    p->a_layout = a_m_first ? JA_A_MK : JA_A_KM;
+    p->b_layout = b_k_first ? JA_B_KN : JA_B_NK;
+    p->in_dtype = A.dtype;
+    p->out_dtype = C.dtype;
+    const int TM = h16 ? GEMM_BF16_TM : GEMM_F32_TM;
+    const int TN = h16 ? GEMM_BF16_TN : GEMM_F32_TN;
+
+    const int64_t nt = t.count(), nseg = (int64_t)t.seg.size() - 1;
+    std::vector<GemmTuple> tuples(nt);
+    std::vector<GemmSeg> segs(nseg), usegs(nt);
+    std::vector<GemmTile> tiles, utiles;
+    std::vector<AggTile> atiles;
+    std::vector<AggSeg> asegs(nseg);
+    std::vector<int64_t> poff(nt);
+    int64_t part = 0;
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    for (int64_t i = 0; i < nt; ++i) {
+        const int32_t* rec = &t.rec[i * t.nl];
+        int64_t nb = extent_of(d, s, rec, batch), m = extent_of(d, s, rec, Mo), n = extent_of(d, s, rec, No),
+                k = extent_of(d, s, rec, K);
+        if (m > lim || n > lim || k > lim) return fail(JA_ERR_UNSUPPORTED, "block extent beyond 2^31");
+        GemmTuple& g = tuples[i];
+        g.a_off = A.blk_off[block_of(A, sa, s, rec)];
+        g.b_off = B.blk_off[block_of(B, sb, s, rec)];
+        g.a_bstride = m * k;
+        g.b_bstride = k * n;
+        g.K = (int32_t)k;
+        g.lda = (int32_t)(a_m_first ? k : m);
+        g.ldb = (int32_t)(b_k_first ? n : k);
+        g.pad = 0;
+        // unfused: every tuple is its own segment writing an f32 partial block
+        GemmSeg& u = usegs[i];
+        u.c_off = part;
+        u.c_bstride = m * n;
+        u.M = (int32_t)m;
+        u.N = (int32_t)n;
+        u.ldc = (int32_t)n;
+        u.t_begin = (int32_t)i;
+        u.t_end = (int32_t)i + 1;
+        u.pad = 0;
+        poff[i] = part;
+        part += nb * m * n;
+        for (int32_t b = 0; b < nb; ++b)
+            for (int32_t m0 = 0; m0 < m; m0 += TM)
+                for (int32_t n0 = 0; n0 < n; n0 += TN) utiles.push_back({(int32_t)i, m0, n0, b});
+    }
+    for (int64_t sg = 0; sg < nseg; ++sg) {
+        const int32_t* rec = &t.rec[t.seg[sg] * t.nl];
+        int64_t nb = extent_of(d, s, rec, batch), m = extent_of(d, s, rec, Mo), n = extent_of(d, s, rec, No);
+        GemmSeg& g = segs[sg];
+        g.c_off = C.blk_off[block_of(C, sc, s, rec)];
+        g.c_bstride = m * n;
+        g.M = (int32_t)m;
+        g.N = (int32_t)n;
+        g.ldc = (int32_t)n;
+        g.t_begin = (int32_t)t.seg[sg];
+        g.t_end = (int32_t)t.seg[sg + 1];
+        g.pad = 0;
+        // grouped order: GEMM_GROUP_M row tiles, then every column tile, so a
+        // contiguous run of the list forms a compact block of output tiles
+        const int32_t mt = (int32_t)((m + TM - 1) / TM), ntl = (int32_t)((n + TN - 1) / TN);
+        for (int32_t b = 0; b < nb; ++b)
+            for (int32_t mg = 0; mg < mt; mg += GEMM_GROUP_M)
+                for (int32_t nj = 0; nj < ntl; ++nj)
+                    for (int32_t mi = mg; mi < std::min(mt, mg + GEMM_GROUP_M); ++mi)
+                        tiles.push_back({(int32_t)sg, mi * TM, nj * TN, b});
+        AggSeg& a = asegs[sg];
+        a.out_off = g.c_off;
+        if (nb * m * n > lim) return fail(JA_ERR_UNSUPPORTED, "output block beyond 2^31 elements");
+        a.nelem = (int32_t)(nb * m * n);
+        a.t_begin = g.t_begin;
+        a.t_end = g.t_end;
+        a.pad = 0;
+        for (int32_t e0 = 0; e0 < a.nelem; e0 += AGG_CHUNK) atiles.push_back({(int32_t)sg, e0});
+    }
+    if ((int64_t)tiles.size() > lim || (int64_t)utiles.size() > lim) return fail(JA_ERR_UNSUPPORTED, "too many tiles");
+    if (h16) {
+        // the MFMA kernel moves 8 bf16 (16 bytes) at a time along every contiguous axis
+        for (const GemmTuple& g : tuples) {
+            bool ok = g.K % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_off % 8 == 0 && g.b_off % 8 == 0 &&
+                      g.a_bstride % 8 == 0 && g.b_bstride % 8 == 0;
+            if (!ok) return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction needs block extents that are multiples of 8");
+        }
+        for (const GemmSeg& g : segs)
+            if ((!a_m_first && g.M % 8) || (b_k_first && g.N % 8))
+                return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction needs block extents that are multiples of 8");
+        // the direct-to-LDS kernel addresses each operand matrix with 32-bit byte offsets
+        bool dma = true;
+        for (const GemmTuple& g : tuples) dma = dma && g.a_bstride * 2 < lim && g.b_bstride * 2 < lim;
+        p->gemm_dma = dma ? 1 : 0;
+    }
+    p->partial_elems = part;
+    p->tiles_off = put(p->table, tiles);
+    p->ntiles = (int32_t)tiles.size();
+    p->segs_off = put(p->table, segs);
+    p->tuples_off = put(p->table, tuples);
+    p->utiles_off = put(p->table, utiles);
+    p->nutiles = (int32_t)utiles.size();
+    p->usegs_off = put(p->table, usegs);
+    p->atiles_off = put(p->table, atiles);
+    p->natiles = (int32_t)atiles.size();
+    p->asegs_off = put(p->table, asegs);
+    p->apoff_off = put(p->table, poff);
+    return JA_OK;
+}
+
+}  // namespace ja
