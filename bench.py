@@ -51,6 +51,55 @@ def _bits_to_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).ravel()).view(torch.bfloat16).cuda()
 
 
+def _stats(ms_list):
+    """mean, median, min, max and the half-width of a 95% confidence interval
+    of the mean (normal approximation) of per-iteration times."""
+    import numpy as np
+
+    a = np.asarray(ms_list, dtype=np.float64)
+    half = 1.96 * a.std(ddof=1) / np.sqrt(len(a)) if len(a) > 1 else 0.0
+    return {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
+            "min": round(float(a.min()), 4), "max": round(float(a.max()), 4), "ci95": round(float(half), 4),
+            "n": int(len(a))}
+
+
+def _timed(launch, steps, flush=None):
+    """Per-iteration times (ms) of `launch`, each between its own event pair
+    on the current stream; `flush` (not timed) runs before every iteration."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record()
+        launch()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+_SNAPSHOT = None
+
+
+def _device_snapshot():
+    """Clock and power lines of rocm-smi, read once by a child process before
+    this process touches the GPU."""
+    global _SNAPSHOT
+    if _SNAPSHOT is not None:
+        return _SNAPSHOT or None
+    import subprocess
+
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower"], capture_output=True, text=True,
+                             timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    keep = [ln.strip() for ln in out.splitlines() if "sclk" in ln or "mclk" in ln or "Power" in ln]
+    _SNAPSHOT = keep[:8]
+    return _SNAPSHOT or None
+
+
 def _mean_ms(pairs):
     return sum(s.elapsed_time(e) for s, e in pairs) / max(1, len(pairs))
 
@@ -148,6 +197,8 @@ def bench_block(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = s0.elapsed_time(s1) / args.steps
+    # per-step distribution: the same K steps, an event pair around each
+    step_stats = _stats(_timed(lambda: blk.forward(x, w, y), args.steps))
     # timed region 2: the same K steps with an event pair around every step of the path
     ev = {}
     torch.cuda.synchronize()
@@ -179,6 +230,7 @@ def bench_block(args):
         "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "block_gflop": round(total_flops / 1e9, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "step_ms": step_stats,
         "roofline": {"kernel": "gemm_bf16_kernel (contraction join-agg, fused SUM)", "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": _gemm_traffic(),
@@ -308,6 +360,9 @@ def bench_kernel(args):
         runs.append(("swiglu", lambda op=op, ins=ins, out=out: op.run(ins, out), None, 2.0 * 3 * 8192 * 11008,
                      [op]))
     res = {}
+    # cold runs: reading 512 MiB between iterations evicts the 256 MB Infinity
+    # Cache (a read leaves clean lines, so the timed kernel writes nothing back)
+    scratch = torch.ones(1 << 28, dtype=torch.int16, device="cuda")
     for name, launch, fl, by, ops in runs:
         for _ in range(args.warmup):
             launch()
@@ -319,17 +374,93 @@ def bench_kernel(args):
         s1.record()
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / args.steps
-        d = {"ms": round(ms, 4)}
+        # at least 100 timed iterations where a kernel is short, about 2 s of timing otherwise
+        nstep = max(args.steps, min(100, int(2000.0 / max(ms, 1e-3))))
+        d = {"ms": round(ms, 4), "warm": _stats(_timed(launch, nstep)),
+             "cold": _stats(_timed(launch, min(nstep, 30), flush=lambda: scratch.max()))}
         if fl:
             d["tflops"] = round(fl / (ms / 1e3) / 1e12, 2)
             d["frac_mfma_peak"] = round(d["tflops"] / PEAK_BF16_TFLOPS, 3)
         if by:
             d["gbs"] = round(by / (ms / 1e3) / 1e9, 1)
             d["frac_hbm_peak"] = round(d["gbs"] / PEAK_HBM_GBS, 3)
+            d["cold_gbs"] = round(by / (d["cold"]["median"] / 1e3) / 1e9, 1)
+        if fl:
+            d["cold_tflops"] = round(fl / (d["cold"]["median"] / 1e3) / 1e12, 2)
         res[name] = d
         for op in ops:
             op.close()
-    return {"workload": args.workload, "steps": args.steps, "warmup": args.warmup, "results": res}
+    if args.workload == "configs" and not args.no_cpu_baseline:
+        for name, cpu in _cpu_configs().items():
+            if name in res:
+                res[name]["cpu_oracle"] = cpu
+    del scratch
+    return {"workload": args.workload, "steps": args.steps, "warmup": args.warmup, "device": _device_snapshot(),
+            "results": res}
+
+
+def _cpu_configs():
+    """The float64 oracle (as it stands) on the configs' own inputs, timed on
+    the host cores beside the GPU runs: cfg1 median of 5 runs, cfg2 one run
+    of the full contraction, cfg3 the full causal attention, cfg4 one run
+    each."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(0)
+    out = {}
+
+    def timed(fn, reps=1):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)) * 1e3
+
+    a, b = rng.uniform(-1, 1, (64, 64)), rng.uniform(-1, 1, (64, 64))
+    out["tiny_fp32_2x2x2"] = timed(lambda: oracle.matmul(a, b), 5)
+    x, wt = rng.standard_normal((2048, 4096)), rng.standard_normal((4096, 11008)) * 0.02
+    out["ffn_contract"] = timed(lambda: oracle.matmul(x, wt))
+    q = [rng.standard_normal((4, 32, 2048, 128)) for _ in range(3)]
+    out["attention"] = timed(lambda: oracle.attention(q[0], q[1], q[2], 1.0 / np.sqrt(128.0), True))
+    xr, gn = rng.standard_normal((8192, 4096)), rng.normal(1.0, 0.1, 4096)
+    out["rmsnorm"] = timed(lambda: oracle.rmsnorm(xr, gn, 1e-6))
+    g, u = rng.standard_normal((8192, 11008)), rng.standard_normal((8192, 11008))
+    out["swiglu"] = timed(lambda: oracle.swiglu(g, u))
+    threads = oracle.num_threads()
+    return {k: {"ms": round(v, 2), "cores": threads, "kind": "oracle"} for k, v in out.items()}
+
+
+def bench_ceilings(args):
+    """The two ceilings the kernels are compared against beside the published
+    peaks: a plain 1 GiB device copy (HBM) and a loop of nothing but bf16
+    MFMAs (matrix cores, no memory traffic), each timed per launch."""
+    import torch
+
+    from tensor_relational_join_amd import binding as B
+
+    n = 1 << 29
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    copy = _stats(_timed(lambda: dst.copy_(src), args.steps))
+    wgs, iters = 256 * 8, 4096
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    fl = B.ja_calibrate_mfma(wgs, iters, sink.data_ptr(), stream)
+    for _ in range(args.warmup):
+        B.ja_calibrate_mfma(wgs, iters, sink.data_ptr(), stream)
+    mf = _stats(_timed(lambda: B.ja_calibrate_mfma(wgs, iters, sink.data_ptr(), stream), args.steps))
+    mfma_tflops = fl / (mf["median"] / 1e3) / 1e12
+    return {"workload": "ceilings", "steps": args.steps, "warmup": args.warmup, "device": _device_snapshot(),
+            "copy": {"bytes_moved": 4 * n, "ms": copy, "gbs": round(4 * n / (copy["median"] / 1e3) / 1e9, 1),
+                     "frac_hbm_peak": round(4 * n / (copy["median"] / 1e3) / 1e9 / PEAK_HBM_GBS, 3)},
+            "mfma_loop": {"flops": fl, "ms": mf, "tflops": round(mfma_tflops, 1),
+                          "frac_mfma_peak": round(mfma_tflops / PEAK_BF16_TFLOPS, 3),
+                          "implied_clock_ghz": round(mfma_tflops / PEAK_BF16_TFLOPS * 2.4, 3)}}
 
 
 def bench_join(args):
@@ -574,13 +705,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block",
                     choices=["block", "block_gqa", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy",
-                             "join", "plans", "f16", "varlen"])
+                             "join", "plans", "f16", "varlen", "ceilings"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (every kernel runs on one "
               "GPU's share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    _device_snapshot()  # before anything initialises the GPU in this process
     import torch
 
     if not torch.cuda.is_available():
@@ -595,10 +727,14 @@ def main():
     if args.workload == "varlen":
         print(json.dumps(bench_varlen(args)))
         return
+    if args.workload == "ceilings":
+        print(json.dumps(bench_ceilings(args)))
+        return
     if args.workload not in BLOCKS:
         print(json.dumps(bench_kernel(args)))
         return
     out, inp = bench_block(args)
+    out["device"] = _device_snapshot()
     if args.workload == "block" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_block(inp, 4, 2048, 4096, 32, 11008)
     print(json.dumps(out))

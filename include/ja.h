@@ -252,6 +252,15 @@ ja_status ja_djoin_run(const ja_djoin* join, const int64_t* splits_dev, int32_t*
                        int64_t* counts, void* workspace, void* stream);
 void ja_djoin_destroy(ja_djoin* join);
 
+/* ---- measurement aid ------------------------------------------------------ */
+
+/* The matrix-core ceiling this GPU sustains: `workgroups` workgroups of 4
+ * wavefronts, each wavefront issuing `iters` rounds of 4 independent bf16
+ * 32x32x16 MFMAs with no memory traffic, LDS or barriers.  sink: device,
+ * workgroups * 256 floats, written with the accumulators' sums.  *flops
+ * (may be NULL) gets the flops enqueued; time the launch on `stream`. */
+ja_status ja_calibrate_mfma(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream);
+
 /* ---- attention planned on the device (section 3.3; section 3.2 on the GPU) */
 
 /* Packed sequences whose ends are device data: attention with

@@ -78,6 +78,7 @@ _SIGS = {
     "ja_djoin_upload": (_st, [_vp, _vp, _sz, _vp]),
     "ja_djoin_run": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ja_djoin_destroy": (None, [_vp]),
+    "ja_calibrate_mfma": (_st, [_i32, _i32, _vp, ctypes.POINTER(ctypes.c_double), _vp]),
     "ja_dattn_create": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, ctypes.POINTER(_vp)]),
     "ja_dattn_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_i64)]),
     "ja_dattn_upload": (_st, [_vp, _vp, _sz, _vp]),
@@ -333,6 +334,13 @@ def ja_djoin_run(join: int, splits_dev: int, rec: int, seg_off: int, counts: int
 
 def ja_djoin_destroy(join: int):
     _lib.ja_djoin_destroy(_vp(join))
+
+
+def ja_calibrate_mfma(workgroups: int, iters: int, sink: int, stream: int = 0) -> float:
+    """Enqueue the MFMA-loop ceiling kernel; returns the flops it performs."""
+    f = ctypes.c_double()
+    _check(_lib.ja_calibrate_mfma(workgroups, iters, _vp(sink), ctypes.byref(f), _vp(stream)))
+    return f.value
 
 
 def ja_dattn_create(spec: int, extents: Sequence[int], intervals: Sequence[int], dtype: int = JA_BF16) -> int:
