@@ -427,3 +427,10 @@ def test_packed_device_spec_and_planner_checks(B, orc):
         assert e.value.name == "JA_ERR_SPEC"
     finally:
         B.ja_spec_destroy(s)
+
+
+def test_calibration_argument_checks(B):
+    for wgs, iters, sink in ((0, 1, 256), (1, 0, 256), (1, 1, 0), (1, 1, 258)):
+        with pytest.raises(B.JaError) as e:
+            B.ja_calibrate_mfma(wgs, iters, sink)
+        assert e.value.name == "JA_ERR_ARG"
