@@ -2,13 +2,16 @@
 // device-side join's records ("Every Kernel Is a Join", section 3.2 step 1
 // on the device; section 3.3 packed sequences whose ends are the cuts).
 //
-//   zero    clears the tile histogram and cursors
+//   zero    clears the histogram and cursors
 //   seg     per segment (one output block: a query batch-head block and one
-//           sequence): its AttnSeg and its 128-row tile count, added to the
-//           histogram of tiles by position inside the sequence; the int32
-//           sequence ends the kernel masks with
-//   scan    one workgroup: the first slot of every position, later positions
-//           (tiles that see more keys) first, and the tile count
+//           sequence): its AttnSeg and its 128-row tile count; its batch-heads
+//           are added to a histogram indexed by the segment's tiles per
+//           batch-head (one atomic per segment); the int32 sequence ends the
+//           kernel masks with
+//   scan    one workgroup: tiles at position q = batch-heads of segments with
+//           more than q tiles (a suffix sum of that histogram), then the first
+//           slot of every position, later positions (tiles that see more keys)
+//           first, and the tile count
 //   tiles   per segment: its tiles (batch-head, first row), each in a slot of
 //           its position taken with an atomic cursor, so the longest tiles
 //           are launched first as the host planner orders them (the order
@@ -74,21 +77,13 @@ __global__ __launch_bounds__(DA_THREADS) void da_seg_kernel(DAttnArgs a, const i
     segs[k] = g;
     const int32_t ntq = (g.S + ATTN_TQ - 1) / ATTN_TQ;
     tcnt[k] = (uint32_t)qn[qi] * (uint32_t)ntq;
-    for (int32_t q = 0; q < ntq; ++q) atomicAdd(&hist[q], (uint32_t)qn[qi]);
+    atomicAdd(&hist[ntq - 1], (uint32_t)qn[qi]);  // segments with ntq tiles per batch-head
 }
 
-// One workgroup: exclusive scan of the histogram from the last position
-// down (base[q] = tiles at positions after q); the total goes to *ntiles.
-__global__ __launch_bounds__(DA_SCAN_THREADS) void da_scan_kernel(const uint32_t* __restrict__ hist,
-                                                                  uint32_t* __restrict__ base, uint32_t n,
-                                                                  int32_t* __restrict__ ntiles) {
-    __shared__ uint32_t lds[DA_SCAN_THREADS / 64];
+// Exclusive prefix sum over the one workgroup of DA_SCAN_THREADS threads.
+__device__ __forceinline__ uint32_t da_block_scan(uint32_t v, uint32_t* lds, uint32_t& total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint32_t per = (n + DA_SCAN_THREADS - 1) / DA_SCAN_THREADS;
-    const uint32_t i0 = threadIdx.x * per;
-    uint32_t s = 0;
-    for (uint32_t i = i0; i < i0 + per && i < n; ++i) s += hist[n - 1 - i];
-    uint32_t x = s;
+    uint32_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t y = __shfl_up(x, o, 64);
@@ -102,12 +97,42 @@ __global__ __launch_bounds__(DA_SCAN_THREADS) void da_scan_kernel(const uint32_t
         off += i < w ? t : 0u;
         tot += t;
     }
-    uint32_t run = off + x - s;
+    __syncthreads();
+    total = tot;
+    return off + x - v;
+}
+
+// One workgroup.  hist[j] holds the batch-heads of segments with j + 1 tiles
+// per batch-head; position q then holds pos[q] = sum of hist[j] over j >= q
+// (a suffix sum), written over hist; base[q] = tiles at positions after q (a
+// suffix sum of pos excluding q); the total goes to *ntiles.  Each thread
+// owns a run of `per` consecutive entries counted from the end and touches
+// no other thread's entries.
+__global__ __launch_bounds__(DA_SCAN_THREADS) void da_scan_kernel(uint32_t* __restrict__ hist,
+                                                                  uint32_t* __restrict__ base, uint32_t n,
+                                                                  int32_t* __restrict__ ntiles) {
+    __shared__ uint32_t lds[DA_SCAN_THREADS / 64];
+    const uint32_t per = (n + DA_SCAN_THREADS - 1) / DA_SCAN_THREADS;
+    const uint32_t i0 = threadIdx.x * per;  // i counts from the end: entry n - 1 - i
+    uint32_t s = 0;
+    for (uint32_t i = i0; i < i0 + per && i < n; ++i) s += hist[n - 1 - i];
+    uint32_t tot;
+    const uint32_t run0 = da_block_scan(s, lds, tot);  // hist of the entries after this thread's run
+    uint32_t run = run0, psum = 0;
     for (uint32_t i = i0; i < i0 + per && i < n; ++i) {
-        base[n - 1 - i] = run;
         run += hist[n - 1 - i];
+        psum += run;
     }
-    if (threadIdx.x == 0) *ntiles = (int32_t)tot;
+    uint32_t ptot;
+    uint32_t prun = da_block_scan(psum, lds, ptot);
+    run = run0;
+    for (uint32_t i = i0; i < i0 + per && i < n; ++i) {
+        run += hist[n - 1 - i];
+        hist[n - 1 - i] = run;
+        base[n - 1 - i] = prun;
+        prun += run;
+    }
+    if (threadIdx.x == 0) *ntiles = (int32_t)ptot;
 }
 
 __global__ __launch_bounds__(DA_THREADS) void da_tile_kernel(const int64_t* __restrict__ counts,
@@ -160,8 +185,7 @@ hipError_t launch_dattn_tables(const DAttnArgs& a, const int64_t* splits, const 
                        a.nbucket, hist, cursor);
     hipLaunchKernelGGL(da_seg_kernel, dim3((nseg_blocks + DA_THREADS - 1) / DA_THREADS), dim3(DA_THREADS), 0, stream,
                        a, splits, rec, seg_off, counts, qbase, qn, kn, segs, tcnt, hist, seq32);
-    hipLaunchKernelGGL(da_scan_kernel, dim3(1), dim3(DA_SCAN_THREADS), 0, stream, (const uint32_t*)hist, base,
-                       a.nbucket, ntiles);
+    hipLaunchKernelGGL(da_scan_kernel, dim3(1), dim3(DA_SCAN_THREADS), 0, stream, hist, base, a.nbucket, ntiles);
     hipLaunchKernelGGL(da_tile_kernel, dim3(a.max_segs), dim3(DA_THREADS), 0, stream, counts, (const AttnSeg*)segs,
                        (const uint32_t*)tcnt, (const uint32_t*)base, cursor, tiles);
     hipLaunchKernelGGL(da_tuple_kernel, dim3((a.max_tuples + DA_THREADS - 1) / DA_THREADS), dim3(DA_THREADS), 0,
