@@ -4,10 +4,12 @@
 A step is one pass of the LLaMA-shaped block (batch 4, seq 2048, d 4096, 32
 heads of 128, ffn 11008, bf16) through libja: RMSNorm, the 2x2x2 QKV
 contraction join-agg, the tokens->heads repartition, causal attention with
-the online-softmax aggregation, heads->tokens, the output projection,
-residual add, RMSNorm, gate/up contractions, SwiGLU, down contraction and the
-second residual add.  Inputs are seeded synthetic tensors already resident
-in HBM in the blockings the operators need.
+the online-softmax aggregation, heads->tokens, the output projection with the
+residual add applied to its aggregated blocks, RMSNorm, the gate-and-up
+contraction with SwiGLU applied to its aggregated blocks, and the down
+contraction with the second residual add (`--workload block_unfused`: the
+adds and SwiGLU as launches of their own).  Inputs are seeded synthetic
+tensors already resident in HBM in the blockings the operators need.
 
 Prints one JSON line.  `value` is the block's join-agg throughput (all
 contraction and attention flops of a step / step time).  `roofline` is for
@@ -15,7 +17,7 @@ the dominant kernel (the bf16 MFMA contraction), timed with HIP events on
 the stream the steps run on.  `cpu_baseline` times the CPU oracle on a
 bounded token sample of the same block.
 
-    python bench.py [--steps K] [--warmup W] [--workload block|configs|ffn|attention|norm_swiglu|copy]
+    python bench.py [--steps K] [--warmup W] [--workload block|block_unfused|configs|ffn|attention|norm_swiglu|copy]
 
 The non-block workloads print per-operator diagnostics (and `copy` the HBM
 copy ceiling); only `block` prints the contract line.
@@ -104,10 +106,10 @@ def _mean_ms(pairs):
     return sum(s.elapsed_time(e) for s, e in pairs) / max(1, len(pairs))
 
 
-def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0):
+def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0, fused=True):
     """Time the oracle (as it stands) on the first n tokens of batch 0 of the
-    same block; n is grown (at most 16x per probe) until one run takes about
-    target_s seconds."""
+    same block (its fused or unfused rounding points); n is grown (at most
+    16x per probe) until one run takes about target_s seconds."""
     import numpy as np
 
     import oracle
@@ -125,7 +127,7 @@ def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0):
         toks = list(range(n))
         t0 = time.perf_counter()
         oracle.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
-                                  f["w_down"], batch, seq, heads, toks)
+                                  f["w_down"], batch, seq, heads, toks, fused=fused)
         dt = time.perf_counter() - t0
         if dt >= target_s * 0.7 or n >= seq:
             break
@@ -162,24 +164,30 @@ BLOCKS = {
     "block_gqa": dict(name="llama3_8b_shaped_block_gqa", batch=8, seq=1024, dm=4096, heads=32, kv_heads=8,
                       ffn=14336),
 }
+# each block also runs with the residual adds and SwiGLU as separate 1:1
+# join launches (every projection written) instead of fused into the
+# contractions that produce their inputs
+BLOCKS.update({k + "_unfused": dict(v, fused=False) for k, v in list(BLOCKS.items())})
 
 
 def bench_block(args):
     import torch
 
     from tensor_relational_join_amd import synth
-    from tensor_relational_join_amd.block import GEMMS, LlamaBlock
+    from tensor_relational_join_amd.block import LlamaBlock
     from tensor_relational_join_amd.device import alloc
 
     cfg = BLOCKS[args.workload]
     batch, seq, dm, heads, kv, ffn = (cfg[k] for k in ("batch", "seq", "dm", "heads", "kv_heads", "ffn"))
-    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv)
+    fused = cfg.get("fused", True)
+    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv, fused=fused)
+    GEMMS = blk.gemms
     inp = synth.llama_block_inputs(5, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols)
     x = blk.materialize(_bits_to_dev(inp["x"]), blk.x_rel)
     w = {k: blk.materialize(_bits_to_dev(inp[k]), rel) for k, rel in blk.w_rel.items()}
     w["g1"] = blk.materialize(_bits_to_dev(inp["g1"]), blk.g_rel)
     w["g2"] = blk.materialize(_bits_to_dev(inp["g2"]), blk.ops["norm2"].in_rels[1])
-    y = alloc(blk.ops["add2"].out_rel)
+    y = alloc(blk.y_rel)
     flops = blk.flops()
     total_flops = sum(flops.values())
 
@@ -226,12 +234,14 @@ def bench_block(args):
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": batch, "seq_len": seq, "d_model": dm,
-                   "heads": heads, "kv_heads": kv, "head_dim": 128, "ffn": ffn, "parallelism": "single GPU"},
+                   "heads": heads, "kv_heads": kv, "head_dim": 128, "ffn": ffn, "parallelism": "single GPU",
+                   "adds_and_swiglu": "fused into the contractions" if fused else "separate launches"},
         "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "block_gflop": round(total_flops / 1e9, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_ms": step_stats,
-        "roofline": {"kernel": "gemm_bf16_kernel (contraction join-agg, fused SUM)", "bound": "mfma",
+        "roofline": {"kernel": "gemm_bf16_dma_kernel (contraction join-agg, fused SUM%s)" %
+                               (" and 1:1-join epilogues" if fused else ""), "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": _gemm_traffic(),
                      "traffic_unit": "bytes per launch (L2 memory side, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
@@ -704,8 +714,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block",
-                    choices=["block", "block_gqa", "configs", "ffn", "attention", "norm_swiglu", "gqa", "copy",
-                             "join", "plans", "f16", "varlen", "ceilings"])
+                    choices=["block", "block_gqa", "block_unfused", "block_gqa_unfused", "configs", "ffn",
+                             "attention", "norm_swiglu", "gqa", "copy", "join", "plans", "f16", "varlen",
+                             "ceilings"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -735,8 +746,9 @@ def main():
         return
     out, inp = bench_block(args)
     out["device"] = _device_snapshot()
-    if args.workload == "block" and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_block(inp, 4, 2048, 4096, 32, 11008)
+    if args.workload in ("block", "block_unfused") and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(inp, 4, 2048, 4096, 32, 11008,
+                                                 fused=BLOCKS[args.workload].get("fused", True))
     print(json.dumps(out))
 
 

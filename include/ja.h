@@ -134,6 +134,21 @@ ja_status ja_relation_block(const ja_relation_desc* rel, const int64_t* key, int
  *                   block contraction; letters absent from the output are
  *                   aggregated with SUM (section 3.2, Examples 3.8, 3.9).
  *                   Every letter must appear in at least two of A, B, C.
+ *   The next two fuse a 1:1 join (how section 1 models elementwise
+ *   operators) into the contraction, applied to each aggregated block.
+ *   op "contract_add": "A,B,C->C" (e.g. "tm,mn,tn->tn"): the contraction
+ *                   with the residual relation R (third operand, the
+ *                   output's letters and blocking) joined 1:1 on the output
+ *                   key after the SUM: C = A B + R, rounded once.
+ *   op "contract_swiglu": "A,B->C" where B's last letter (absent from A and
+ *                   C, extent 2, one interval) indexes a (gate, up) pair
+ *                   (e.g. "td,dfc->tf", B[d][f][0] the gate weights and
+ *                   B[d][f][1] the up weights): the contraction's two
+ *                   members g, u of each pair are joined 1:1 after the SUM,
+ *                   C = g / (1 + exp(-g)) * u, rounded once.  Both fused
+ *                   forms take and write bf16 or f16 (JA_ERR_DTYPE
+ *                   otherwise) and have no unfused path (JA_ERR_UNSUPPORTED
+ *                   from ja_plan_partial_bytes, ja_kernel and ja_agg).
  *   op "attention": "Q,K,V->O" with Q = O = [batch..., group..., s, d] and
  *                   K = V = [batch..., t, d] (e.g. "bhsd,bhtd,bhtd->bhsd").
  *                   The optional group letters, which must not index K and
@@ -357,7 +372,8 @@ ja_status ja_graph_add_input(ja_graph* graph, int32_t rank, const int64_t* shape
 /* Operator `spec` (copied) on tensors inputs[0..n_inputs), whose dimensions
  * bind the spec's input letters in order; writes the output tensor's id.
  * JA_ERR_SHAPE when a letter gets two extents or a rank differs;
- * JA_ERR_UNSUPPORTED for packed-sequence attention. */
+ * JA_ERR_UNSUPPORTED for packed-sequence attention and for the contractions
+ * with an epilogue (contract_add, contract_swiglu). */
 ja_status ja_graph_add_op(ja_graph* graph, const ja_spec* spec, const int32_t* inputs, int32_t n_inputs,
                           int32_t* tensor);
 ja_status ja_graph_count(const ja_graph* graph, int32_t* n_ops, int32_t* n_tensors);

@@ -28,7 +28,13 @@ Einsummable", paperpeel full text):
   g*R .. g*R+R-1 share key-value head g), and ``attention`` /
   ``tuple_records`` take sequences packed end to end along the sequence index
   (section 3.3: attention never crosses a sequence boundary);
-* the LLaMA-shaped block as a chain of the above -- ``llama_block``.
+* a contraction followed by a 1:1 join on its output key, with nothing
+  rounded in between (elementwise operators as joins, section 1) --
+  ``contract_residual`` (A B + R) and ``contract_swiglu`` (silu(gate) * up
+  over a (gate, up) pair letter);
+* the LLaMA-shaped block as a chain of the above -- ``llama_block``, whose
+  ``fused`` form leaves unrounded the contraction results that such a join
+  consumes.
 
 Readings where the pages are silent (listed again in the design notes):
 intervals are half-open [lo, hi); near-equal intervals give the first
@@ -268,6 +274,24 @@ def add(a, b) -> np.ndarray:
     c = np.empty_like(a)
     _load().orc_add(_ptr(a, _f64p), _ptr(b, _f64p), a.size, _ptr(c, _f64p))
     return c
+
+
+def contract_residual(spec: str, A, B, R) -> np.ndarray:
+    """A contraction followed by a 1:1 join with a residual relation on the
+    output key (section 1: elementwise operators as joins): A B + R in
+    float64, with no rounding in between.  spec: 'A,B->C'; R has C's shape."""
+    return add(einsum(spec, A, B), R)
+
+
+def contract_swiglu(spec: str, A, B) -> np.ndarray:
+    """spec 'A,B->C' whose B ends with a letter (absent from A and C) of
+    extent 2 that indexes a (gate, up) pair: the contraction into C's letters
+    plus that letter, then the 1:1 join of the pair's members,
+    silu(gate) * up, in float64 with no rounding in between."""
+    lhs, out = spec.split("->")
+    a, b = lhs.split(",")
+    P = einsum("%s,%s->%s%s" % (a, b, out, b[-1]), A, B)
+    return swiglu(P[..., 0], P[..., 1])
 
 
 # --------------------------------------------------------------------------
@@ -614,30 +638,37 @@ def _qkv_heads(qkv, batch: int, seq: int, heads: int, kv_heads: int, hd: int):
 
 
 def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
-                eps: float = 1e-6, return_intermediates: bool = False, kv_heads: Optional[int] = None):
+                eps: float = 1e-6, return_intermediates: bool = False, kv_heads: Optional[int] = None,
+                fused: bool = False):
     """Float64 reference of one transformer block on bf16 inputs, with every
     materialised relation rounded to bf16.  x [batch*seq, d]; w_qkv is
     [d, (heads + 2 kv_heads) hd] = [W_q | W_k | W_v] with head h in columns
     [h*hd, (h+1)*hd) of each part; kv_heads < heads is grouped-query
     attention (query head h reads key-value head h // (heads // kv_heads),
     section 3.3), kv_heads = heads (the default) multi-head attention.
-    Token t = b*seq + s.  No rotary embedding and no biases."""
+    Token t = b*seq + s.  No rotary embedding and no biases.
+
+    fused: the block whose residual adds and SwiGLU are 1:1 joins applied
+    inside the producing contractions, so the output projection, the gate
+    and up projections and the down projection are never materialised and
+    are not rounded; every relation that is written still is."""
     T, Dm = x.shape
     hd = Dm // heads
     kv_heads = heads if kv_heads is None else kv_heads
     r = round_bf16
+    rc = (lambda v: v) if fused else r  # contraction outputs consumed by a 1:1 join
     h1 = r(rmsnorm(x, g1, eps))
     qkv = r(matmul(h1, w_qkv))
     Q, K, V = _qkv_heads(qkv, batch, seq, heads, kv_heads, hd)
     O = r(attention(Q, K, V, 1.0 / np.sqrt(hd), True))
     o = O.transpose(0, 2, 1, 3).reshape(T, Dm)
-    a = r(matmul(o, w_o))
+    a = rc(matmul(o, w_o))
     x2 = r(add(x, a))
     h2 = r(rmsnorm(x2, g2, eps))
-    gt = r(matmul(h2, w_gate))
-    up = r(matmul(h2, w_up))
+    gt = rc(matmul(h2, w_gate))
+    up = rc(matmul(h2, w_up))
     f = r(swiglu(gt, up))
-    d = r(matmul(f, w_down))
+    d = rc(matmul(f, w_down))
     y = r(add(x2, d))
     if return_intermediates:
         return y, dict(h1=h1, qkv=qkv, O=O, a=a, x2=x2, h2=h2, gate=gt, up=up, f=f, d=d)
@@ -645,7 +676,7 @@ def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: in
 
 
 def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
-                       tokens, eps: float = 1e-6, kv_heads: Optional[int] = None):
+                       tokens, eps: float = 1e-6, kv_heads: Optional[int] = None, fused: bool = False):
     """The same block as `llama_block`, evaluated only at the listed tokens
     (t = b*seq + s).  Keys and values are formed for every position up to the
     largest listed s of each batch, as causal attention needs them.  Every
@@ -656,6 +687,7 @@ def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, 
     hd = Dm // heads
     kv_heads = heads if kv_heads is None else kv_heads
     r = round_bf16
+    rc = (lambda v: v) if fused else r
     tokens = np.asarray(tokens, dtype=np.int64)
     y = np.empty((tokens.size, Dm))
     for b in sorted(set((tokens // seq).tolist())):
@@ -668,9 +700,9 @@ def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, 
         Q, K, V = _qkv_heads(qkv, 1, smax + 1, heads, kv_heads, hd)
         q_rows = np.array([(0, h, s) for s in ss for h in range(heads)], dtype=np.int64)
         O = r(attention_rows(Q, K, V, q_rows, 1.0 / np.sqrt(hd), True)).reshape(len(ss), heads * hd)
-        a = r(matmul(O, w_o))
+        a = rc(matmul(O, w_o))
         x2 = r(add(rows[ss], a))
         h2 = r(rmsnorm(x2, g2, eps))
-        f = r(swiglu(r(matmul(h2, w_gate)), r(matmul(h2, w_up))))
-        y[sel] = r(add(x2, r(matmul(f, w_down))))
+        f = r(swiglu(rc(matmul(h2, w_gate)), rc(matmul(h2, w_up))))
+        y[sel] = r(add(x2, rc(matmul(f, w_down))))
     return y

@@ -35,6 +35,18 @@ kv_heads), the shape of the pages' own LLaMA-3-8B-like blocks:
 
 With t unsplit, the three column blocks of the projection's output are
 three contiguous [t, *] arrays, each re-blocked on its own.
+
+With fused=True the two residual adds and SwiGLU are 1:1 joins applied by
+the producing contractions to each aggregated block before it is written,
+and the gate and up projections are one contraction whose weight pairs the
+two matrices column by column (W_gu[d, f, 0] = W_gate[d, f], W_gu[d, f, 1] =
+W_up[d, f]):
+
+    x2 = o @ W_o + x                  tm,mn,tn->tn  contract_add     t: 2  m: 2  n: 2
+    f = swiglu(h2 @ W_gu)             td,dfc->tf    contract_swiglu  t: 2  d: 2  f: 4  c: whole
+    y = f @ W_down + x2               tf,fn,tn->tn  contract_add     t: 2  f: 4  n: 2
+
+The projections a, gt, up and dn are then never written (nor rounded).
 """
 from __future__ import annotations
 
@@ -45,22 +57,25 @@ import torch
 from . import binding as B
 from .device import Op, Repart, alloc, equal_splits
 
-# (name, kind) of every step, in execution order
+# the steps in execution order, and the contractions among them
 STEPS = ["norm1", "qkv", "to_heads", "attn", "to_tokens", "oproj", "add1", "norm2", "gate", "up", "swiglu",
          "down", "add2"]
 GEMMS = ["qkv", "oproj", "gate", "up", "down"]
+FUSED_STEPS = ["norm1", "qkv", "to_heads", "attn", "to_tokens", "oproj_add", "norm2", "gate_up", "down_add"]
+FUSED_GEMMS = ["qkv", "oproj_add", "gate_up", "down_add"]
 
 
 class LlamaBlock:
     def __init__(self, batch: int = 4, seq: int = 2048, dm: int = 4096, heads: int = 32, ffn: int = 11008,
-                 eps: float = 1e-6, device="cuda", kv_heads: Optional[int] = None):
+                 eps: float = 1e-6, device="cuda", kv_heads: Optional[int] = None, fused: bool = False):
         if dm % heads or dm // heads != 128 or seq % 128:
             raise ValueError("the attention kernel needs head_dim 128 and 128-multiples of seq")
         kv = heads if kv_heads is None else kv_heads
         if kv <= 0 or heads % kv:
             raise ValueError("kv_heads must divide heads")
         self.batch, self.seq, self.dm, self.heads, self.ffn, self.eps = batch, seq, dm, heads, ffn, eps
-        self.kv_heads, self.gqa = kv, kv != heads
+        self.kv_heads, self.gqa, self.fused = kv, kv != heads, fused
+        self.steps, self.gemms = (FUSED_STEPS, FUSED_GEMMS) if fused else (STEPS, GEMMS)
         self.hd = dm // heads
         T = batch * seq
         self.T = T
@@ -86,14 +101,23 @@ class LlamaBlock:
             att_sp = {"b": equal_splits(batch, batch), "g": equal_splits(kv, kv), "r": [0, heads // kv],
                       "s": equal_splits(seq, nb), "t": equal_splits(seq, nb), "d": [0, self.hd]}
             self.ops["attn"] = Op("bgrsd,bgtd,bgtd->bgrsd", "attention", att_sp, "causal=s,t", device=device)
-        self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": d2, "n": d2}, device=device)
-        self.ops["add1"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
+        if not fused:
+            self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": d2, "n": d2}, device=device)
+            self.ops["add1"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
+        else:
+            self.ops["oproj_add"] = Op("tm,mn,tn->tn", "contract_add", {"t": t2, "m": d2, "n": d2}, device=device)
         self.ops["norm2"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
-        self.ops["gate"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
-        self.ops["up"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
-        self.ops["swiglu"] = Op("tf,tf->tf", "swiglu", {"t": t2, "f": f4}, device=device)
-        self.ops["down"] = Op("tf,fn->tn", "contract", {"t": t2, "f": f4, "n": d2}, device=device)
-        self.ops["add2"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
+        if not fused:
+            self.ops["gate"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
+            self.ops["up"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
+            self.ops["swiglu"] = Op("tf,tf->tf", "swiglu", {"t": t2, "f": f4}, device=device)
+            self.ops["down"] = Op("tf,fn->tn", "contract", {"t": t2, "f": f4, "n": d2}, device=device)
+            self.ops["add2"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
+        else:
+            self.ops["gate_up"] = Op("td,dfc->tf", "contract_swiglu", {"t": t2, "d": d2, "f": f4, "c": [0, 2]},
+                                     device=device)
+            self.ops["down_add"] = Op("tf,fn,tn->tn", "contract_add", {"t": t2, "f": f4, "n": d2}, device=device)
+        oproj = self.ops["oproj_add" if fused else "oproj"]
         # token-major <-> head-major re-blockings around attention
         self.rp: Dict[str, Repart] = {}
         if not self.gqa:
@@ -101,7 +125,7 @@ class LlamaBlock:
             self.rp["to_heads"] = Repart(self.ops["qkv"].out_rel, heads_rel,
                                          B.make_view((batch, seq, 3, heads, self.hd), (2, 0, 3, 1, 4)),
                                          device=device)
-            self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, self.ops["oproj"].in_rels[0],
+            self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, oproj.in_rels[0],
                                           B.make_view((batch, heads, seq, self.hd), (0, 2, 1, 3)), device=device)
             self.heads_rel = heads_rel
         else:
@@ -115,29 +139,38 @@ class LlamaBlock:
             for name, rel in (("k", k_rel), ("v", v_rel)):
                 self.rp["to_" + name] = Repart(self.part_rel[name], rel,
                                                B.make_view((batch, seq, kv, self.hd), (0, 2, 1, 3)), device=device)
-            self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, self.ops["oproj"].in_rels[0],
+            self.rp["to_tokens"] = Repart(self.ops["attn"].out_rel, oproj.in_rels[0],
                                           B.make_view((batch, kv, rep, seq, self.hd), (0, 3, 1, 2, 4)),
                                           device=device)
         # relations of the block's inputs (materialised straight into the blockings the ops need)
         self.x_rel = self.ops["norm1"].in_rels[0]
         self.g_rel = self.ops["norm1"].in_rels[1]
-        self.w_rel = {"w_qkv": self.ops["qkv"].in_rels[1], "w_o": self.ops["oproj"].in_rels[1],
-                      "w_gate": self.ops["gate"].in_rels[1], "w_up": self.ops["up"].in_rels[1],
-                      "w_down": self.ops["down"].in_rels[1]}
-        # intermediates
         o = self.ops
+        if not fused:
+            self.w_rel = {"w_qkv": o["qkv"].in_rels[1], "w_o": o["oproj"].in_rels[1], "w_gate": o["gate"].in_rels[1],
+                          "w_up": o["up"].in_rels[1], "w_down": o["down"].in_rels[1]}
+        else:
+            # w_gu [d, f, 2]: gate and up weights paired column by column
+            self.w_rel = {"w_qkv": o["qkv"].in_rels[1], "w_o": o["oproj_add"].in_rels[1],
+                          "w_gu": o["gate_up"].in_rels[1], "w_down": o["down_add"].in_rels[1]}
+        # the block's output relation
+        self.y_rel = o["down_add" if fused else "add2"].out_rel
+        # intermediates
         if not self.gqa:
             heads = {"heads": alloc(self.heads_rel, device)}
         else:
             heads = {n: alloc(r, device) for n, r in zip("qkv", o["attn"].in_rels)}
         self.buf = {
             "h1": alloc(o["norm1"].out_rel, device), "qkv": alloc(o["qkv"].out_rel, device),
-            **heads, "O": alloc(o["attn"].out_rel, device),
-            "o": alloc(o["oproj"].in_rels[0], device), "a": alloc(o["oproj"].out_rel, device),
-            "x2": alloc(o["add1"].out_rel, device), "h2": alloc(o["norm2"].out_rel, device),
-            "gt": alloc(o["gate"].out_rel, device), "up": alloc(o["up"].out_rel, device),
-            "f": alloc(o["swiglu"].out_rel, device), "dn": alloc(o["down"].out_rel, device),
+            **heads, "O": alloc(o["attn"].out_rel, device), "o": alloc(oproj.in_rels[0], device),
+            "x2": alloc(oproj.out_rel, device), "h2": alloc(o["norm2"].out_rel, device),
         }
+        if not fused:
+            self.buf.update({"a": alloc(o["oproj"].out_rel, device), "gt": alloc(o["gate"].out_rel, device),
+                             "up": alloc(o["up"].out_rel, device), "f": alloc(o["swiglu"].out_rel, device),
+                             "dn": alloc(o["down"].out_rel, device)})
+        else:
+            self.buf["f"] = alloc(o["gate_up"].out_rel, device)
 
     # ---------------------------------------------------------------- flops / bytes
     def flops(self) -> Dict[str, float]:
@@ -147,6 +180,10 @@ class LlamaBlock:
         nb = self.seq // 128
         kept = nb * (nb + 1) // 2  # kept (s-block, t-block) tuples per (b, h)
         f["attn"] = 2 * 2.0 * 128 * 128 * self.hd * kept * self.batch * self.heads
+        if self.fused:
+            f["oproj_add"] = f.pop("oproj")
+            f["gate_up"] = f.pop("gate") + f.pop("up")
+            f["down_add"] = f.pop("down")
         return f
 
     def step_bytes(self) -> Dict[str, float]:
@@ -154,9 +191,11 @@ class LlamaBlock:
         outputs written once)."""
         T, dm, ffn = self.T, self.dm, self.ffn
         e = 2.0
-        return {"norm1": e * (2 * T * dm + dm), "norm2": e * (2 * T * dm + dm), "add1": e * 3 * T * dm,
-                "add2": e * 3 * T * dm, "swiglu": e * 3 * T * ffn, "to_heads": e * 2 * T * self.qkv_cols,
-                "to_tokens": e * 2 * T * dm}
+        b = {"norm1": e * (2 * T * dm + dm), "norm2": e * (2 * T * dm + dm), "to_heads": e * 2 * T * self.qkv_cols,
+             "to_tokens": e * 2 * T * dm}
+        if not self.fused:
+            b.update({"add1": e * 3 * T * dm, "add2": e * 3 * T * dm, "swiglu": e * 3 * T * ffn})
+        return b
 
     # ---------------------------------------------------------------- execution
     def forward(self, x: torch.Tensor, w: Dict[str, torch.Tensor], y: torch.Tensor,
@@ -185,15 +224,25 @@ class LlamaBlock:
             ("to_heads", to_heads),
             ("attn", lambda: o["attn"].run([q, k, v], b["O"], stream)),
             ("to_tokens", lambda: self.rp["to_tokens"].run(b["O"], b["o"], stream)),
-            ("oproj", lambda: o["oproj"].run([b["o"], w["w_o"]], b["a"], stream)),
-            ("add1", lambda: o["add1"].run([x, b["a"]], b["x2"], stream)),
-            ("norm2", lambda: o["norm2"].run([b["x2"], w["g2"]], b["h2"], stream)),
-            ("gate", lambda: o["gate"].run([b["h2"], w["w_gate"]], b["gt"], stream)),
-            ("up", lambda: o["up"].run([b["h2"], w["w_up"]], b["up"], stream)),
-            ("swiglu", lambda: o["swiglu"].run([b["gt"], b["up"]], b["f"], stream)),
-            ("down", lambda: o["down"].run([b["f"], w["w_down"]], b["dn"], stream)),
-            ("add2", lambda: o["add2"].run([b["x2"], b["dn"]], y, stream)),
         ]
+        if not self.fused:
+            plan += [
+                ("oproj", lambda: o["oproj"].run([b["o"], w["w_o"]], b["a"], stream)),
+                ("add1", lambda: o["add1"].run([x, b["a"]], b["x2"], stream)),
+                ("norm2", lambda: o["norm2"].run([b["x2"], w["g2"]], b["h2"], stream)),
+                ("gate", lambda: o["gate"].run([b["h2"], w["w_gate"]], b["gt"], stream)),
+                ("up", lambda: o["up"].run([b["h2"], w["w_up"]], b["up"], stream)),
+                ("swiglu", lambda: o["swiglu"].run([b["gt"], b["up"]], b["f"], stream)),
+                ("down", lambda: o["down"].run([b["f"], w["w_down"]], b["dn"], stream)),
+                ("add2", lambda: o["add2"].run([b["x2"], b["dn"]], y, stream)),
+            ]
+        else:
+            plan += [
+                ("oproj_add", lambda: o["oproj_add"].run([b["o"], w["w_o"], x], b["x2"], stream)),
+                ("norm2", lambda: o["norm2"].run([b["x2"], w["g2"]], b["h2"], stream)),
+                ("gate_up", lambda: o["gate_up"].run([b["h2"], w["w_gu"]], b["f"], stream)),
+                ("down_add", lambda: o["down_add"].run([b["f"], w["w_down"], b["x2"]], y, stream)),
+            ]
         for name, fn in plan:
             if events is not None:
                 s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

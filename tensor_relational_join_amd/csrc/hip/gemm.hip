@@ -28,6 +28,71 @@
 
 namespace ja {
 
+// ---------------------------------------------------------------- epilogue
+// Write one lane's four adjacent outputs a[0..3]: columns col .. col + 3 of a
+// segment block N columns wide, `off` the element offset of column col in the
+// output as the contraction lays it out.  The epilogue `epi` is the 1:1 join
+// applied on the way out: JA_EPI_ADD adds the residual R at the same offset
+// (`r` holds its four elements when the store is vectorised, loaded earlier
+// by residual4); with JA_EPI_SWIGLU the columns are (gate, up) pairs (N even,
+// col a multiple of 4) and the pair at offset off writes silu(gate) * up to
+// element off / 2 of the real output.
+__device__ __forceinline__ bool vec_store(int64_t off, int col, int N) { return col + 4 <= N && (off & 3) == 0; }
+
+// The residual's four elements at off when the store there is vectorised
+// (all of a wavefront's loads are issued before its first store).
+__device__ __forceinline__ uint2 residual4(const uint16_t* __restrict__ R, int epi, int64_t off, int col, int N) {
+    if (epi == JA_EPI_ADD && vec_store(off, col, N)) return *reinterpret_cast<const uint2*>(R + off);
+    return make_uint2(0u, 0u);
+}
+
+template <bool IN_F16, bool OUT16>
+__device__ __forceinline__ void store_out4(void* __restrict__ C, const uint16_t* __restrict__ R, int epi, int64_t off,
+                                           int col, int N, f32x4_t a, uint2 r) {
+    if constexpr (OUT16) {
+        uint16_t* c = (uint16_t*)C;
+        if (epi == JA_EPI_SWIGLU) {
+            const int64_t o = off >> 1;
+            const float h0 = a[0] / (1.0f + __expf(-a[0])) * a[1];
+            const float h1 = a[2] / (1.0f + __expf(-a[2])) * a[3];
+            if (col + 4 <= N && (o & 1) == 0) {
+                *reinterpret_cast<uint32_t*>(c + o) = pack_h16x2<IN_F16>(h0, h1);
+            } else {
+                if (col + 2 <= N) c[o] = (uint16_t)f32_to_h16<IN_F16>(h0);
+                if (col + 4 <= N) c[o + 1] = (uint16_t)f32_to_h16<IN_F16>(h1);
+            }
+            return;
+        }
+        if (vec_store(off, col, N)) {
+            if (epi == JA_EPI_ADD) {
+                a[0] += h16lo_to_f32<IN_F16>(r.x);
+                a[1] += h16hi_to_f32<IN_F16>(r.x);
+                a[2] += h16lo_to_f32<IN_F16>(r.y);
+                a[3] += h16hi_to_f32<IN_F16>(r.y);
+            }
+            *reinterpret_cast<uint2*>(c + off) =
+                make_uint2(pack_h16x2<IN_F16>(a[0], a[1]), pack_h16x2<IN_F16>(a[2], a[3]));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (col + r < N) {
+                    float v = a[r];
+                    if (epi == JA_EPI_ADD) v += h16_to_f32<IN_F16>(R[off + r]);
+                    c[off + r] = (uint16_t)f32_to_h16<IN_F16>(v);
+                }
+        }
+    } else {
+        float* c = (float*)C;
+        if (col + 4 <= N && (off & 3) == 0) {
+            *reinterpret_cast<float4*>(c + off) = make_float4(a[0], a[1], a[2], a[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (col + r < N) c[off + r] = a[r];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- bf16 MFMA
 // LDS operand tiles are [rows][BK] bf16 with no padding.  The 16-byte chunk c
 // (8 consecutive k) of row r sits at chunk position c ^ swz(r), with
@@ -131,7 +196,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* 
                                                                 const GemmSeg* __restrict__ segs,
                                                                 const GemmTuple* __restrict__ tuples,
                                                                 const uint16_t* __restrict__ A,
-                                                                const uint16_t* __restrict__ B, void* __restrict__ C) {
+                                                                const uint16_t* __restrict__ B, void* __restrict__ C,
+                                                                const uint16_t* __restrict__ R, int epi) {
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -211,30 +277,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* 
 
     // epilogue: lane owns C[row][col .. col+3] of every fragment
     const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
+    static_assert(FM % 2 == 0, "the epilogue takes fragment rows in pairs");
+    // two rows of fragments at a time: their residual loads are all in
+    // flight before the first of their stores
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int row = m0 + wm * WTM + i * 16 + (lane & 15);
-        if (row >= sg.M) continue;
+    for (int i0 = 0; i0 < FM; i0 += 2) {
+        uint2 res[2][FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * WTN + j * 16 + 4 * kc;
-            const int64_t off = cbase + (int64_t)row * sg.ldc + col;
-            const f32x4_t a = acc[i][j];
-            if (col + 4 <= sg.N && (off & 3) == 0) {
-                if (OUT16)
-                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_h16x2<IN_F16>(a[0], a[1]),
-                                                                               pack_h16x2<IN_F16>(a[2], a[3]));
-                else
-                    *reinterpret_cast<float4*>((float*)C + off) = make_float4(a[0], a[1], a[2], a[3]);
-            } else {
+        for (int i = i0; i < i0 + 2; ++i) {
+            const int row = m0 + wm * WTM + i * 16 + (lane & 15);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (col + r < sg.N) {
-                        if (OUT16)
-                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_h16<IN_F16>(a[r]);
-                        else
-                            ((float*)C)[off + r] = a[r];
-                    }
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + wn * WTN + j * 16 + 4 * kc;
+                res[i - i0][j] = row < sg.M ? residual4(R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N)
+                                            : make_uint2(0u, 0u);
+            }
+        }
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i) {
+            const int row = m0 + wm * WTM + i * 16 + (lane & 15);
+            if (row >= sg.M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + wn * WTN + j * 16 + 4 * kc;
+                store_out4<IN_F16, OUT16>(C, R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N, acc[i][j],
+                                          res[i - i0][j]);
             }
         }
     }
@@ -373,7 +440,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
                                                                     const GemmTuple* __restrict__ tuples,
                                                                     const uint16_t* __restrict__ A,
                                                                     const uint16_t* __restrict__ B,
-                                                                    void* __restrict__ C) {
+                                                                    void* __restrict__ C,
+                                                                    const uint16_t* __restrict__ R, int epi) {
     constexpr int NT = WM * WN * 64;
     constexpr int BK = 32;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -507,30 +575,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     // epilogue: lane owns C[row][col .. col+3] of every fragment
     const int kc = lane >> 4;
     const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
+    static_assert(FM % 2 == 0, "the epilogue takes fragment rows in pairs");
+    // two rows of fragments at a time: their residual loads are all in
+    // flight before the first of their stores
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int row = m0 + arow + i * 16 + (lane & 15);
-        if (row >= sg.M) continue;
+    for (int i0 = 0; i0 < FM; i0 += 2) {
+        uint2 res[2][FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + brow + j * 16 + 4 * kc;
-            const int64_t off = cbase + (int64_t)row * sg.ldc + col;
-            const f32x4_t a = acc[i][j];
-            if (col + 4 <= sg.N && (off & 3) == 0) {
-                if (OUT16)
-                    *reinterpret_cast<uint2*>((uint16_t*)C + off) = make_uint2(pack_h16x2<IN_F16>(a[0], a[1]),
-                                                                               pack_h16x2<IN_F16>(a[2], a[3]));
-                else
-                    *reinterpret_cast<float4*>((float*)C + off) = make_float4(a[0], a[1], a[2], a[3]);
-            } else {
+        for (int i = i0; i < i0 + 2; ++i) {
+            const int row = m0 + arow + i * 16 + (lane & 15);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (col + r < sg.N) {
-                        if (OUT16)
-                            ((uint16_t*)C)[off + r] = (uint16_t)f32_to_h16<IN_F16>(a[r]);
-                        else
-                            ((float*)C)[off + r] = a[r];
-                    }
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + brow + j * 16 + 4 * kc;
+                res[i - i0][j] = row < sg.M ? residual4(R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N)
+                                            : make_uint2(0u, 0u);
+            }
+        }
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i) {
+            const int row = m0 + arow + i * 16 + (lane & 15);
+            if (row >= sg.M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + brow + j * 16 + 4 * kc;
+                store_out4<IN_F16, OUT16>(C, R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N, acc[i][j],
+                                          res[i - i0][j]);
             }
         }
     }
@@ -592,58 +661,60 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmTile* __restric
 // ---------------------------------------------------------------- dispatch
 template <int AL, int BL, bool F16, bool OUT16>
 static void launch_bf16(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples, const void* A,
-                        const void* B, void* C, hipStream_t s) {
+                        const void* B, void* C, const void* R, int epi, hipStream_t s) {
     constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, BK = GEMM_BF16_TK, WM = 2, WN = 4;
     constexpr unsigned lds = 2u * (BM + BN) * BK * sizeof(uint16_t);
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, AL, BL, F16, OUT16>), dim3(ntiles), dim3(WM * WN * 64),
-                       lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C);
+                       lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C,
+                       (const uint16_t*)R, epi);
 }
 
 template <int AL, int BL, bool F16, bool OUT16>
 static void launch_bf16_dma(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples,
-                            const void* A, const void* B, void* C, hipStream_t s) {
+                            const void* A, const void* B, void* C, const void* R, int epi, hipStream_t s) {
     constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, NS = GEMM_DMA_STAGES, WM = 2, WN = 4;
     constexpr unsigned lds = (unsigned)NS * (BM + BN) * 32 * sizeof(uint16_t);
     hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, F16, OUT16>), dim3(ntiles),
                        dim3(WM * WN * 64), lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A,
-                       (const uint16_t*)B, C);
+                       (const uint16_t*)B, C, (const uint16_t*)R, epi);
 }
 
 // 16-bit inputs (bf16 or, with F16, IEEE half) into fp32 accumulators;
 // out16 writes the output in the input's format, otherwise fp32.
 template <int AL, int BL, bool F16>
 static void launch_bf16_out(int out16, int dma, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
-                            const GemmTuple* tuples, const void* A, const void* B, void* C, hipStream_t s) {
+                            const GemmTuple* tuples, const void* A, const void* B, void* C, const void* R, int epi,
+                            hipStream_t s) {
     if (dma) {
         if (out16)
-            launch_bf16_dma<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16_dma<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
         else
-            launch_bf16_dma<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16_dma<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     } else {
         if (out16)
-            launch_bf16<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
         else
-            launch_bf16<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_bf16<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     }
 }
 
 template <bool F16>
 static void launch_h16(int a_layout, int b_layout, int out16, int dma, const GemmTile* tiles, int ntiles,
                        const GemmSeg* segs, const GemmTuple* tuples, const void* A, const void* B, void* C,
-                       hipStream_t s) {
+                       const void* R, int epi, hipStream_t s) {
     if (a_layout == JA_A_MK && b_layout == JA_B_KN)
-        launch_bf16_out<JA_A_MK, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+        launch_bf16_out<JA_A_MK, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     else if (a_layout == JA_A_MK && b_layout == JA_B_NK)
-        launch_bf16_out<JA_A_MK, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+        launch_bf16_out<JA_A_MK, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     else if (a_layout == JA_A_KM && b_layout == JA_B_KN)
-        launch_bf16_out<JA_A_KM, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+        launch_bf16_out<JA_A_KM, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     else
-        launch_bf16_out<JA_A_KM, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+        launch_bf16_out<JA_A_KM, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
 }
 
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
-                       const void* A, const void* B, void* C, int32_t in_dtype, int32_t out_dtype, int32_t a_layout,
-                       int32_t b_layout, int32_t dma, hipStream_t s) {
+                       const void* A, const void* B, void* C, const void* R, int32_t epi, int32_t in_dtype,
+                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, int32_t dma, hipStream_t s) {
     const uint8_t* t = (const uint8_t*)table;
     const GemmTile* tiles = (const GemmTile*)(t + tiles_off);
     const GemmSeg* segs = (const GemmSeg*)(t + segs_off);
@@ -651,9 +722,9 @@ hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int
     if (in_dtype == JA_BF16 || in_dtype == JA_F16) {
         const int out16 = out_dtype != JA_F32;
         if (in_dtype == JA_F16)
-            launch_h16<true>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_h16<true>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
         else
-            launch_h16<false>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, s);
+            launch_h16<false>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     } else {
 #define JA_F32_CASE(al, bl)                                                                                       \
     hipLaunchKernelGGL((gemm_f32_kernel<al, bl>), dim3(ntiles), dim3(256), 0, s, tiles, ntiles, segs, tuples,     \

@@ -203,10 +203,28 @@ static ja_status parse_spec(const char* einsum, const char* op, const char* para
     if (st) return st;
 
     std::string o(op);
-    if (o == "contract") {
+    if (o == "contract" || o == "contract_add" || o == "contract_swiglu") {
+        // contract_add: C = A B + R, the residual R joined 1:1 on the output
+        // key; contract_swiglu: B's last letter indexes a (gate, up) pair and
+        // C = silu(A B [gate]) * (A B [up]).  Both are applied to the
+        // aggregated block before it is written.
         s->kind = JA_OP_CONTRACT;
-        if (s->ins.size() != 2) return fail(JA_ERR_SPEC, "contract takes two operands");
+        s->epilogue = o == "contract_add" ? JA_EPI_ADD : o == "contract_swiglu" ? JA_EPI_SWIGLU : JA_EPI_NONE;
+        if (s->epilogue == JA_EPI_ADD) {
+            if (s->ins.size() != 3 || s->ins[2] != s->out)
+                return fail(JA_ERR_SPEC, "contract_add takes A, B and a residual with the output's letters");
+        } else if (s->ins.size() != 2) {
+            return fail(JA_ERR_SPEC, o + " takes two operands");
+        }
+        if (s->epilogue == JA_EPI_SWIGLU) {
+            const char c = s->ins[1].empty() ? 0 : s->ins[1].back();
+            if (!c || s->ins[0].find(c) != std::string::npos || s->out.find(c) != std::string::npos)
+                return fail(JA_ERR_SPEC, "contract_swiglu needs B's last letter to index the (gate, up) pair, "
+                                         "in neither A nor the output");
+            s->pair = c;
+        }
         for (char c : s->letters) {
+            if (c == s->pair) continue;
             int n = (s->ins[0].find(c) != std::string::npos) + (s->ins[1].find(c) != std::string::npos) +
                     (s->out.find(c) != std::string::npos);
             if (n < 2) return fail(JA_ERR_SPEC, std::string("letter ") + c + " must appear in two of A, B, C");

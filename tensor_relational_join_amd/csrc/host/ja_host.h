@@ -66,6 +66,8 @@ struct ja_spec {
     char causal_s = 0, causal_t = 0;
     std::vector<int64_t> packed;  // attention: ascending ends of sequences packed along the s and t letters
     bool packed_device = false;   // attention: the sequences end exactly at the cuts of the s and t letters
+    int32_t epilogue = 0;         // contract: JA_EPI_NONE, JA_EPI_ADD (third operand R) or JA_EPI_SWIGLU
+    char pair = 0;                // contract_swiglu: B's last letter, (gate, up) = (0, 1), absent from A and C
     double eps = 1e-6;
     int letter_index(char c) const {
         auto p = letters.find(c);
@@ -93,8 +95,8 @@ ja_status build_tuples(const ja_spec* spec, const ja_decomp* d, ja_tuples& t);
 // ---- kernel launchers (implemented in the .hip sources) --------------------
 namespace ja {
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
-                       const void* A, const void* B, void* C, int32_t in_dtype, int32_t out_dtype,
-                       int32_t a_layout, int32_t b_layout, int32_t dma, hipStream_t stream);
+                       const void* A, const void* B, void* C, const void* R, int32_t epi, int32_t in_dtype,
+                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, int32_t dma, hipStream_t stream);
 // seq_off / nseq: the packed sequences' int32 end positions in the table (nseq = 0: not packed)
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
                             int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,

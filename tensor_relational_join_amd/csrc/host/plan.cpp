@@ -257,7 +257,8 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
         case JA_OP_CONTRACT:
             if (p->ntiles == 0) return JA_OK;
             JA_TRY_HIP(launch_gemm(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
-                                   out_ptr, p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, p->gemm_dma, hs));
+                                   out_ptr, p->epilogue == JA_EPI_ADD ? in_ptrs[2] : nullptr, p->epilogue,
+                                   p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, p->gemm_dma, hs));
             break;
         case JA_OP_ATTENTION:
             if (p->ntiles == 0) return JA_OK;
@@ -281,6 +282,7 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
 ja_status ja_plan_partial_bytes(const ja_plan* p, size_t* bytes) {
     if (!p || !bytes) return fail(JA_ERR_ARG, "NULL argument");
     if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
     *bytes = (size_t)p->partial_elems * 4;
     return JA_OK;
 }
@@ -289,9 +291,11 @@ ja_status ja_kernel(const ja_plan* p, const void* const* in_ptrs, void* partials
     ja_status st = check_ptrs(p, in_ptrs, partials);
     if (st) return st;
     if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
     if (p->nutiles == 0) return JA_OK;
     JA_TRY_HIP(launch_gemm(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
-                           partials, p->in_dtype, JA_F32, p->a_layout, p->b_layout, p->gemm_dma, (hipStream_t)stream));
+                           partials, nullptr, JA_EPI_NONE, p->in_dtype, JA_F32, p->a_layout, p->b_layout, p->gemm_dma,
+                           (hipStream_t)stream));
     return JA_OK;
 }
 
@@ -299,6 +303,7 @@ ja_status ja_agg(const ja_plan* p, ja_agg_op op, const void* partials, void* out
     if (!p || !partials || !out_ptr) return fail(JA_ERR_ARG, "NULL argument");
     if (!p->dev) return fail(JA_ERR_STATE, "plan tables are not uploaded");
     if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
     if (op != JA_AGG_SUM && op != JA_AGG_MAX) return fail(JA_ERR_ARG, "unknown aggregation operator");
     if (((uintptr_t)partials & 15) || ((uintptr_t)out_ptr & 15)) return fail(JA_ERR_ARG, "buffers must be 16-byte aligned");
     if (p->natiles == 0) return JA_OK;

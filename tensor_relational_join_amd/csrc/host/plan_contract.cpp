@@ -38,10 +38,31 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
     Rel A, B, C;
     ja_status st;
     if ((st = rel_from_desc(in[0], A)) || (st = rel_from_desc(in[1], B)) || (st = rel_from_desc(out, C))) return st;
-    const std::string &sa = s->ins[0], &sb = s->ins[1], &sc = s->out;
+    const bool swig = s->epilogue == JA_EPI_SWIGLU;
+    // With the SwiGLU epilogue the kernel computes the contraction into the
+    // output's letters followed by the pair letter (whole, extent 2): element
+    // e of that layout is member e % 2 of the pair written to element e / 2
+    // of the real output, so its block offsets are twice the output's.
+    const std::string &sa = s->ins[0], &sb = s->ins[1];
+    const std::string sc = swig ? s->out + s->pair : s->out;
     if ((st = match_rel(A, sa, s, d, "operand A")) || (st = match_rel(B, sb, s, d, "operand B")) ||
-        (st = match_rel(C, sc, s, d, "output")))
+        (st = match_rel(C, s->out, s, d, "output")))
         return st;
+    if (swig) {
+        const int l = s->letter_index(s->pair);
+        if (d->ext[l] != 2 || d->sp[l].size() != 2)
+            return fail(JA_ERR_DECOMP, "the (gate, up) pair letter must have extent 2 and one interval");
+    }
+    if (s->epilogue != JA_EPI_NONE) {
+        if (A.dtype == JA_F32 || C.dtype != A.dtype)
+            return fail(JA_ERR_DTYPE, "a contraction with an epilogue takes and writes bf16 or f16");
+        if (s->epilogue == JA_EPI_ADD) {
+            Rel R;
+            if ((st = rel_from_desc(in[2], R)) || (st = match_rel(R, s->out, s, d, "residual"))) return st;
+            if (R.dtype != C.dtype) return fail(JA_ERR_DTYPE, "the residual must have the output's dtype");
+        }
+    }
+    p->epilogue = s->epilogue;
     if (A.dtype != B.dtype) return fail(JA_ERR_DTYPE, "contract operands must share a dtype");
     if (A.dtype == JA_F32) {
         if (C.dtype != JA_F32) return fail(JA_ERR_DTYPE, "f32 contraction writes f32");
@@ -122,7 +143,7 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         const int32_t* rec = &t.rec[t.seg[sg] * t.nl];
         int64_t nb = extent_of(d, s, rec, batch), m = extent_of(d, s, rec, Mo), n = extent_of(d, s, rec, No);
         GemmSeg& g = segs[sg];
-        g.c_off = C.blk_off[block_of(C, sc, s, rec)];
+        g.c_off = C.blk_off[block_of(C, s->out, s, rec)] * (swig ? 2 : 1);
         g.c_bstride = m * n;
         g.M = (int32_t)m;
         g.N = (int32_t)n;

@@ -313,7 +313,9 @@ ja_status ja_graph_add_input(ja_graph* g, int32_t rank, const int64_t* shape, in
 ja_status ja_graph_add_op(ja_graph* g, const ja_spec* spec, const int32_t* inputs, int32_t n_inputs, int32_t* tensor) {
     if (!g || !spec || !inputs || !tensor) return fail(JA_ERR_ARG, "NULL argument");
     if (n_inputs != (int32_t)spec->ins.size()) return fail(JA_ERR_ARG, "input count does not match the spec");
-    if (!spec->packed.empty()) return fail(JA_ERR_UNSUPPORTED, "planning packed-sequence attention");
+    if (!spec->packed.empty() || spec->packed_device)
+        return fail(JA_ERR_UNSUPPORTED, "planning packed-sequence attention");
+    if (spec->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "planning a contraction with an epilogue");
     GOp op;
     op.spec = *spec;
     op.ext.assign(spec->letters.size(), 0);

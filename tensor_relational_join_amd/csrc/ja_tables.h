@@ -45,6 +45,14 @@ enum : int32_t {
     JA_B_NK = 1,  // B[k][n] at n*ldb + k (k contiguous)
 };
 
+// What the contraction kernel does with an aggregated output tile on its way
+// out (a 1:1 join on the output key applied before the single write).
+enum : int32_t {
+    JA_EPI_NONE = 0,    // write the aggregated block
+    JA_EPI_ADD = 1,     // add the residual relation's element at the same offset
+    JA_EPI_SWIGLU = 2,  // columns come in (gate, up) pairs: write silu(gate) * up, one element per pair
+};
+
 // ---------------------------------------------------------------- attention
 struct AttnTile {
     int32_t seg;  // segment = one (batch-heads, query interval) output block

@@ -138,7 +138,8 @@ def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int, qkv_c
     """bf16 bit patterns of one block's inputs: x ~ N(0,1) [batch*seq, dm];
     gains ~ N(1, 0.1) [dm]; weights ~ N(0, 0.02): w_qkv [dm, qkv_cols] (= [W_q
     | W_k | W_v]; 3 dm columns unless given, fewer with grouped key-value
-    heads), w_o [dm, dm], w_gate and w_up [dm, ffn], w_down [ffn, dm].
+    heads), w_o [dm, dm], w_gate and w_up [dm, ffn], w_down [ffn, dm], and
+    w_gu [dm, ffn, 2], the gate and up weights paired column by column.
     Stream i of `seed` feeds the i-th tensor of LLAMA_BLOCK_STREAMS."""
     T = batch * seq
     shapes = {"x": (T, dm), "g1": (dm,), "w_qkv": (dm, qkv_cols or 3 * dm), "w_o": (dm, dm), "g2": (dm,),
@@ -152,4 +153,7 @@ def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int, qkv_c
         else:
             mean, std = 0.0, 0.02
         out[name] = normal_bf16(seed, i, shapes[name], mean=mean, std=std)
+    # the same weights laid out for a gate-and-up contraction: [dm, ffn, 2],
+    # the gate weight then the up weight of each column side by side
+    out["w_gu"] = np.ascontiguousarray(np.stack([out["w_gate"], out["w_up"]], axis=2))
     return out

@@ -14,7 +14,12 @@ of an ulp the downstream roundings decorrelate; each decorrelated rounding
 adds up to ~2^-8/sqrt(6) ~ 1.6e-3 relative noise, and with up to ~20
 such stages feeding forward the bound is sqrt(20) * 1.6e-3 ~ 7e-3, so the
 chain is held to CHAIN_TOL = 1e-2.  A wrong index, head mapping or dropped
-tuple gives errors of order 1."""
+tuple gives errors of order 1.
+
+Every test runs both forms of the block: the residual adds and SwiGLU as
+launches of their own, and fused into the contractions that produce their
+inputs (checked per step as contraction + residual and gate-and-up +
+SwiGLU, against the oracle's fused rounding points)."""
 import itertools
 
 import numpy as np
@@ -37,19 +42,19 @@ def _unpack(orc, rel, t, as_bits=False):
     return bits if as_bits else orc.bf16_to_f64(bits)
 
 
-def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None):
+def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False):
     import torch
 
     from tensor_relational_join_amd.block import LlamaBlock
     from tensor_relational_join_amd.device import alloc
 
-    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv_heads)
+    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv_heads, fused=fused)
     inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols)
     x = _pack(orc, blk.x_rel, inp["x"])
     w = {k: _pack(orc, rel, inp[k]) for k, rel in blk.w_rel.items()}
     w["g1"] = _pack(orc, blk.g_rel, inp["g1"])
     w["g2"] = _pack(orc, blk.ops["norm2"].in_rels[1], inp["g2"])
-    y = alloc(blk.ops["add2"].out_rel)
+    y = alloc(blk.y_rel)
     blk.forward(x, w, y)
     torch.cuda.synchronize()
     return blk, inp, x, y
@@ -64,18 +69,31 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
     rng = np.random.default_rng(2)
     errs = {}
 
-    def contract(name, a_rel, a_buf, w_name, out_rel, out_buf, N, blockN):
+    def contract(name, a_rel, a_buf, w_name, out_rel, out_buf, N, blockN, residual=None):
+        """out = A W (w_name "w_gu": silu(A W_gate) * (A W_up); residual: + R),
+        against the oracle on the GPU's A (and R)."""
         A = _unpack(orc, a_rel, a_buf)
-        W = f64(inp[w_name])
         got = _unpack(orc, out_rel, out_buf)
         if sampled:
             rows = sorted(set([0, 1, T // 2 - 1, T // 2, T - 1] + list(rng.integers(0, T, 24))))
             cols = sorted(set([0, 1, 127, 128, blockN - 1, blockN, N - 1] + list(rng.integers(0, N, 24))))
             pts = np.array(list(itertools.product(rows, cols)))
-            want = orc.round_bf16(orc.einsum_points("ij,jk->ik", A, W, pts))
-            errs[name] = rel_frobenius(got[pts[:, 0], pts[:, 1]], want)
+            prod = lambda W: orc.einsum_points("ij,jk->ik", A, W, pts)
+            if w_name == "w_gu":
+                want = orc.swiglu(prod(f64(inp["w_gate"])), prod(f64(inp["w_up"])))
+            else:
+                want = prod(f64(inp[w_name]))
+            if residual is not None:
+                want = orc.add(want, residual[pts[:, 0], pts[:, 1]])
+            errs[name] = rel_frobenius(got[pts[:, 0], pts[:, 1]], orc.round_bf16(want))
         else:
-            errs[name] = rel_frobenius(got, orc.round_bf16(orc.matmul(A, W)))
+            if w_name == "w_gu":
+                want = orc.contract_swiglu("td,dfc->tf", A, f64(inp["w_gu"]))
+            elif residual is not None:
+                want = orc.contract_residual("ij,jk->ik", A, f64(inp[w_name]), residual)
+            else:
+                want = orc.matmul(A, f64(inp[w_name]))
+            errs[name] = rel_frobenius(got, orc.round_bf16(want))
 
     xd = f64(inp["x"])
     h1 = _unpack(orc, o["norm1"].out_rel, b["h1"])
@@ -118,36 +136,51 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
         rows = np.array(list(itertools.product(range(batch), range(heads), range(seq))))
     want = orc.round_bf16(orc.attention_rows(Qd, Kd, Vd, rows, 1.0 / np.sqrt(128.0), True))
     errs["attn"] = rel_frobenius(Od[rows[:, 0], rows[:, 1], rows[:, 2]], want)
-    ar, orl = o["attn"].out_rel, o["oproj"].in_rels[0]
+    oproj = o["oproj_add" if blk.fused else "oproj"]
+    ar, orl = o["attn"].out_rel, oproj.in_rels[0]
     view = ((batch, kv, rep, seq, 128), (0, 3, 1, 2, 4)) if blk.gqa else ((batch, heads, seq, 128), (0, 2, 1, 3))
     want_o = orc.repartition(orc.Relation(ar.shape, ar.splits), bf16_bits(b["O"]),
                              orc.Relation(orl.shape, orl.splits), *view)
     errs["to_tokens"] = 0.0 if np.array_equal(bf16_bits(b["o"]), want_o) else 1.0
-    contract("oproj", orl, b["o"], "w_o", o["oproj"].out_rel, b["a"], dm, dm // 2)
-    x2 = _unpack(orc, o["add1"].out_rel, b["x2"])
-    errs["add1"] = rel_frobenius(x2, orc.round_bf16(xd + _unpack(orc, o["oproj"].out_rel, b["a"])))
+    if blk.fused:
+        contract("oproj_add", orl, b["o"], "w_o", oproj.out_rel, b["x2"], dm, dm // 2, residual=xd)
+        x2 = _unpack(orc, oproj.out_rel, b["x2"])
+    else:
+        contract("oproj", orl, b["o"], "w_o", o["oproj"].out_rel, b["a"], dm, dm // 2)
+        x2 = _unpack(orc, o["add1"].out_rel, b["x2"])
+        errs["add1"] = rel_frobenius(x2, orc.round_bf16(xd + _unpack(orc, o["oproj"].out_rel, b["a"])))
     h2 = _unpack(orc, o["norm2"].out_rel, b["h2"])
     errs["norm2"] = rel_frobenius(h2, orc.round_bf16(orc.rmsnorm(x2, f64(inp["g2"]), blk.eps)))
-    contract("gate", o["norm2"].out_rel, b["h2"], "w_gate", o["gate"].out_rel, b["gt"], ffn, ffn // 4)
-    contract("up", o["norm2"].out_rel, b["h2"], "w_up", o["up"].out_rel, b["up"], ffn, ffn // 4)
-    fa = _unpack(orc, o["swiglu"].out_rel, b["f"])
-    errs["swiglu"] = rel_frobenius(fa, orc.round_bf16(orc.swiglu(_unpack(orc, o["gate"].out_rel, b["gt"]),
-                                                                 _unpack(orc, o["up"].out_rel, b["up"]))))
-    contract("down", o["swiglu"].out_rel, b["f"], "w_down", o["down"].out_rel, b["dn"], dm, dm // 2)
-    yd = _unpack(orc, o["add2"].out_rel, y)
-    errs["add2"] = rel_frobenius(yd, orc.round_bf16(x2 + _unpack(orc, o["down"].out_rel, b["dn"])))
+    if blk.fused:
+        contract("gate_up", o["norm2"].out_rel, b["h2"], "w_gu", o["gate_up"].out_rel, b["f"], ffn, ffn // 4)
+        f_rel = o["gate_up"].out_rel
+    else:
+        contract("gate", o["norm2"].out_rel, b["h2"], "w_gate", o["gate"].out_rel, b["gt"], ffn, ffn // 4)
+        contract("up", o["norm2"].out_rel, b["h2"], "w_up", o["up"].out_rel, b["up"], ffn, ffn // 4)
+        fa = _unpack(orc, o["swiglu"].out_rel, b["f"])
+        errs["swiglu"] = rel_frobenius(fa, orc.round_bf16(orc.swiglu(_unpack(orc, o["gate"].out_rel, b["gt"]),
+                                                                     _unpack(orc, o["up"].out_rel, b["up"]))))
+        f_rel = o["swiglu"].out_rel
+    if blk.fused:
+        contract("down_add", f_rel, b["f"], "w_down", blk.y_rel, y, dm, dm // 2, residual=x2)
+        yd = _unpack(orc, blk.y_rel, y)
+    else:
+        contract("down", f_rel, b["f"], "w_down", o["down"].out_rel, b["dn"], dm, dm // 2)
+        yd = _unpack(orc, o["add2"].out_rel, y)
+        errs["add2"] = rel_frobenius(yd, orc.round_bf16(x2 + _unpack(orc, o["down"].out_rel, b["dn"])))
     assert np.isfinite(yd).all()
     return errs, yd
 
 
-def test_block_reduced_shapes(orc):
+@pytest.mark.parametrize("fused", [False, True])
+def test_block_reduced_shapes(orc, fused):
     batch, seq, dm, heads, ffn = 2, 256, 256, 2, 704
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=11)
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=11, fused=fused)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=False)
         f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
         want = orc.llama_block(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"],
-                               batch, seq, heads)
+                               batch, seq, heads, fused=fused)
         chain = rel_frobenius(yd, want)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
         for k, v in errs.items():
@@ -157,15 +190,16 @@ def test_block_reduced_shapes(orc):
         blk.close()
 
 
-def test_block_full_size(orc):
+@pytest.mark.parametrize("fused", [False, True])
+def test_block_full_size(orc, fused):
     batch, seq, dm, heads, ffn = 4, 2048, 4096, 32, 11008
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=5)
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=5, fused=fused)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
         toks = [bb * seq + s for bb in range(batch) for s in (0, 1, 63, 100)]
         f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
         want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
-                                        f["w_down"], batch, seq, heads, toks)
+                                        f["w_down"], batch, seq, heads, toks, fused=fused)
         chain = rel_frobenius(yd[toks], want_y)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
         for k, v in errs.items():
@@ -175,15 +209,16 @@ def test_block_full_size(orc):
         blk.close()
 
 
-def test_gqa_block_reduced_shapes(orc):
+@pytest.mark.parametrize("fused", [False, True])
+def test_gqa_block_reduced_shapes(orc, fused):
     """Grouped-query block: 8 query heads over 2 key-value heads."""
     batch, seq, dm, heads, kv, ffn = 2, 256, 1024, 8, 2, 768
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=13, kv_heads=kv)
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=13, kv_heads=kv, fused=fused)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=False)
         f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
         want = orc.llama_block(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"],
-                               batch, seq, heads, kv_heads=kv)
+                               batch, seq, heads, kv_heads=kv, fused=fused)
         chain = rel_frobenius(yd, want)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
         for k, v in errs.items():
@@ -193,17 +228,18 @@ def test_gqa_block_reduced_shapes(orc):
         blk.close()
 
 
-def test_gqa_block_llama3_8b_shape(orc):
+@pytest.mark.parametrize("fused", [False, True])
+def test_gqa_block_llama3_8b_shape(orc, fused):
     """The pages' LLaMA-3-8B-like block: d 4096, 32 query heads over 8
     key-value heads, FFN 14,336, 8 sequences of 1,024 tokens."""
     batch, seq, dm, heads, kv, ffn = 8, 1024, 4096, 32, 8, 14336
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=14, kv_heads=kv)
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=14, kv_heads=kv, fused=fused)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
         toks = [bb * seq + s for bb in (0, 5) for s in (0, 1, 63, 100)]
         f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
         want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
-                                        f["w_down"], batch, seq, heads, toks, kv_heads=kv)
+                                        f["w_down"], batch, seq, heads, toks, kv_heads=kv, fused=fused)
         chain = rel_frobenius(yd[toks], want_y)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
         for k, v in errs.items():

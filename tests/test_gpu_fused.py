@@ -1,0 +1,168 @@
+"""GPU parity of the contractions with a 1:1 join applied to each aggregated
+block on its way out (contract_add: + residual; contract_swiglu: silu(gate)
+* up over a (gate, up) pair letter), through the C ABI, against the oracle's
+contract_residual / contract_swiglu rounded once.
+
+Cases span several 256 x 256 output tiles with ragged tails, uneven
+intervals, all operand layouts the pair letter allows, a batch letter, both
+16-bit formats, the stores that are not 8-byte aligned, and run-to-run
+determinism.  Bar: relative Frobenius error <= 2e-3, and nearly every
+element equal to the correctly rounded value."""
+import itertools
+
+import numpy as np
+import pytest
+
+from gpu_helpers import bf16_bits, rel_frobenius, to_dev_bf16, to_dev_f16
+from tensor_relational_join_amd import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    assert torch.cuda.is_available()
+    from tensor_relational_join_amd import device
+
+    return device
+
+
+def _eq(n, q):
+    base, extra = divmod(n, q)
+    p = [0]
+    for i in range(q):
+        p.append(p[-1] + base + (i < extra))
+    return p
+
+
+def _run(dev, orc, einsum, op, splits, dense, f16=False, out=None):
+    """Pack the dense inputs into the decomposition's relations, run, unpack."""
+    import torch
+
+    from tensor_relational_join_amd.binding import JA_BF16, JA_F16
+
+    dt = JA_F16 if f16 else JA_BF16
+    lhs, o_letters = einsum.split("->")
+    ins = lhs.split(",")
+    o = dev.Op(einsum, op, splits, "", [dt] * len(ins), dt)
+    try:
+        to_dev = to_dev_f16 if f16 else to_dev_bf16
+        dev_ins = [to_dev(orc.Relation([splits[c][-1] for c in s], [splits[c] for c in s]).pack(x))
+                   for s, x in zip(ins, dense)]
+        out_t = dev.alloc(o.out_rel) if out is None else out
+        o.run(dev_ins, out_t)
+        torch.cuda.synchronize()
+        orel = orc.Relation([splits[c][-1] for c in o_letters], [splits[c] for c in o_letters])
+        bits = orel.unpack(bf16_bits(out_t))
+        res = orc.f16_to_f64(bits) if f16 else orc.bf16_to_f64(bits)
+        return res, o, dev_ins
+    except Exception:
+        o.close()
+        raise
+
+
+ADD_CASES = [
+    ("ij,jk,ik->ik", {"i": [0, 100, 300], "j": [0, 64, 256], "k": [0, 136, 264]}),
+    ("ij,kj,ik->ik", {"i": [0, 77, 200], "j": [0, 96, 320], "k": [0, 50, 130]}),     # rows of 50 and 80: unaligned stores
+    ("ji,jk,ik->ik", {"i": [0, 264, 520], "j": [0, 96, 328], "k": [0, 256, 264]}),
+    ("ji,kj,ik->ik", {"i": [0, 136], "j": [0, 64, 128], "k": [0, 40, 96]}),
+    ("bij,bjk,bik->bik", {"b": [0, 2, 3], "i": [0, 70, 130], "j": [0, 64, 192], "k": [0, 80, 160]}),
+    ("ij,jk,ik->ik", {"i": [0, 520], "j": [0, 200, 336, 432], "k": [0, 776]}),
+]
+
+
+@pytest.mark.parametrize("einsum,sp", ADD_CASES)
+@pytest.mark.parametrize("f16", [False, True])
+def test_contract_add(dev, orc, einsum, sp, f16):
+    lhs, out = einsum.split("->")
+    shapes = [tuple(sp[c][-1] for c in s) for s in lhs.split(",")]
+    draw = synth.normal_f16 if f16 else synth.normal_bf16
+    widen = orc.f16_to_f64 if f16 else orc.bf16_to_f64
+    rnd = orc.round_f16 if f16 else orc.round_bf16
+    X, W, R = draw(31, 0, shapes[0]), draw(31, 1, shapes[1], std=0.05), draw(31, 2, shapes[2])
+    got, o, _ = _run(dev, orc, einsum, "contract_add", sp, [X, W, R], f16=f16)
+    o.close()
+    plain = "%s,%s->%s" % (lhs.split(",")[0], lhs.split(",")[1], out)
+    want = rnd(orc.contract_residual(plain, widen(X), widen(W), widen(R)))
+    assert rel_frobenius(got, want) <= TOL
+    assert np.mean(got == want) > 0.95
+
+
+SWIGLU_CASES = [
+    ("td,dfc->tf", {"t": [0, 100, 300], "d": [0, 64, 256], "f": [0, 68, 132], "c": [0, 2]}),
+    ("td,dfc->tf", {"t": [0, 520], "d": [0, 200, 336, 432], "f": [0, 36, 100, 388], "c": [0, 2]}),
+    ("dt,dfc->tf", {"t": [0, 264, 520], "d": [0, 96, 328], "f": [0, 128, 264], "c": [0, 2]}),
+    ("btd,bdfc->btf", {"b": [0, 1, 3], "t": [0, 70, 130], "d": [0, 64, 192], "f": [0, 40, 80], "c": [0, 2]}),
+]
+
+
+@pytest.mark.parametrize("einsum,sp", SWIGLU_CASES)
+@pytest.mark.parametrize("f16", [False, True])
+def test_contract_swiglu(dev, orc, einsum, sp, f16):
+    lhs, out = einsum.split("->")
+    shapes = [tuple(sp[c][-1] for c in s) for s in lhs.split(",")]
+    draw = synth.normal_f16 if f16 else synth.normal_bf16
+    widen = orc.f16_to_f64 if f16 else orc.bf16_to_f64
+    rnd = orc.round_f16 if f16 else orc.round_bf16
+    X, W = draw(32, 0, shapes[0]), draw(32, 1, shapes[1], std=0.1)
+    got, o, _ = _run(dev, orc, einsum, "contract_swiglu", sp, [X, W], f16=f16)
+    o.close()
+    want = rnd(orc.contract_swiglu(einsum, widen(X), widen(W)))
+    assert rel_frobenius(got, want) <= TOL
+    assert np.mean(got == want) > 0.9
+
+
+def test_fused_forms_are_deterministic_and_match_the_separate_chain(dev, orc):
+    """Run to run bitwise.  The separate launches (gate and up written in
+    bf16, then SwiGLU) round twice more: each decorrelated bf16 rounding adds
+    at most ~2^-8/sqrt(6) ~ 1.6e-3 relative noise, and SwiGLU's sensitivity to
+    its gate can scale that by up to ~2, so the two forms agree to 1e-2 (an
+    indexing or pairing mistake gives order 1), and the fused form is the one
+    nearer the float64 value."""
+    import torch
+
+    sp = {"t": [0, 256, 512], "d": [0, 512, 1024], "f": [0, 384, 776], "c": [0, 2]}
+    X = synth.normal_bf16(33, 0, (512, 1024))
+    W = synth.normal_bf16(33, 1, (1024, 776, 2), std=0.03)
+    got, o, ins = _run(dev, orc, "td,dfc->tf", "contract_swiglu", sp, [X, W])
+    try:
+        a, b = dev.alloc(o.out_rel), dev.alloc(o.out_rel)
+        o.run(ins, a)
+        o.run(ins, b)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    finally:
+        o.close()
+    spl = {k: sp[k] for k in "tdf"}
+    g, og, _ = _run(dev, orc, "td,df->tf", "contract", spl, [X, np.ascontiguousarray(W[:, :, 0])])
+    og.close()
+    u, ou, _ = _run(dev, orc, "td,df->tf", "contract", spl, [X, np.ascontiguousarray(W[:, :, 1])])
+    ou.close()
+    sep = orc.round_bf16(orc.swiglu(g, u))
+    assert 0 < rel_frobenius(got, sep) <= 1e-2
+    exact = orc.contract_swiglu("td,dfc->tf", orc.bf16_to_f64(X), orc.bf16_to_f64(W))
+    assert rel_frobenius(got, exact) < rel_frobenius(sep, exact)
+
+
+def test_contract_add_full_size_sampled(dev, orc):
+    """The block's down projection with the second residual add: t 8,192 by
+    2, f 11,008 by 4, n 4,096 by 2 (16 tuples, 4 segments of 4), sampled
+    outputs across every block boundary."""
+    T, F, N = 8192, 11008, 4096
+    sp = {"t": _eq(T, 2), "f": _eq(F, 4), "n": _eq(N, 2)}
+    A = synth.normal_bf16(34, 0, (T, F))
+    W = synth.normal_bf16(34, 1, (F, N), std=0.02)
+    R = synth.normal_bf16(34, 2, (T, N))
+    got, o, _ = _run(dev, orc, "tf,fn,tn->tn", "contract_add", sp, [A, W, R])
+    o.close()
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 4095, 4096, T - 1] + list(rng.integers(0, T, 30))))
+    cols = sorted(set([0, 1, 255, 256, 2047, 2048, N - 1] + list(rng.integers(0, N, 30))))
+    pts = np.array(list(itertools.product(rows, cols)))
+    P = orc.einsum_points("tf,fn->tn", orc.bf16_to_f64(A), orc.bf16_to_f64(W), pts)
+    want = orc.round_bf16(orc.add(P, orc.bf16_to_f64(R)[pts[:, 0], pts[:, 1]]))
+    assert rel_frobenius(got[pts[:, 0], pts[:, 1]], want) <= TOL
+    assert np.isfinite(got).all()

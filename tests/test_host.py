@@ -187,6 +187,13 @@ def test_relation_layout_matches_oracle(B, orc):
     ("rbgsd,bgtd,bgtd->rbgsd", "attention", "", "JA_ERR_SPEC"),
     ("bgsd,bgrtd,bgrtd->bgsd", "attention", "", "JA_ERR_SPEC"),
     ("bgrsd,bgsd,bgsd->bgrsd", "attention", "", "JA_ERR_SPEC"),
+    # fused contractions: the residual has the output's letters; the pair letter is B's last, nowhere else
+    ("tm,mn->tn", "contract_add", "", "JA_ERR_SPEC"),
+    ("tm,mn,nt->tn", "contract_add", "", "JA_ERR_SPEC"),
+    ("td,dcf->tf", "contract_swiglu", "", "JA_ERR_SPEC"),
+    ("tdc,dfc->tf", "contract_swiglu", "", "JA_ERR_SPEC"),
+    ("td,dfc->tfc", "contract_swiglu", "", "JA_ERR_SPEC"),
+    ("td,dfc,tf->tf", "contract_swiglu", "", "JA_ERR_SPEC"),
 ])
 def test_spec_errors(B, einsum, op, params, code):
     with pytest.raises(B.JaError) as e:
@@ -251,6 +258,82 @@ def test_plan_validation_errors(B):
             B.ja_plan_create(s, d, [A16, B16], C16)
     finally:
         B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
+
+
+def test_fused_contraction_plans(B):
+    """contract_add and contract_swiglu: same tuples as the plain
+    contraction; 16-bit relations only; the pair letter whole with extent 2;
+    no unfused path; not planned by the logical optimizer."""
+    from tensor_relational_join_amd.device import relation_for
+
+    sp = {"t": [0, 64, 128], "m": [0, 64, 128], "n": [0, 32, 96]}
+    plain = _tuples(B, "tm,mn->tn", "contract", sp)
+    fused = _tuples(B, "tm,mn,tn->tn", "contract_add", sp)
+    assert plain[0] == "tmn" and fused[0] == "tmn"
+    assert np.array_equal(plain[1], fused[1]) and np.array_equal(plain[2], fused[2])
+    s = B.ja_spec_create("tm,mn,tn->tn", "contract_add")
+    d = B.ja_decomp_create(s, [128, 128, 96], [2, 2, 2], [sp["t"], sp["m"], sp["n"]])
+    try:
+        bf = [relation_for(x, sp, B.JA_BF16) for x in ("tm", "mn", "tn")]
+        p = B.ja_plan_create(s, d, bf, relation_for("tn", sp, B.JA_BF16))
+        for call in (lambda: B.ja_plan_partial_bytes(p), lambda: B.ja_kernel(p, [16, 32, 48], 64),
+                     lambda: B.ja_agg(p, B.JA_AGG_SUM, 16, 32)):
+            with pytest.raises(B.JaError) as e:
+                call()
+            assert e.value.name in ("JA_ERR_UNSUPPORTED", "JA_ERR_STATE")
+        with pytest.raises(B.JaError) as e:
+            B.ja_plan_partial_bytes(p)
+        assert e.value.name == "JA_ERR_UNSUPPORTED"
+        B.ja_plan_destroy(p)
+        for ins, out, code in (
+                (bf, relation_for("tn", sp, B.JA_F32), "JA_ERR_DTYPE"),                      # f32 output
+                ([relation_for(x, sp, B.JA_F32) for x in ("tm", "mn", "tn")],
+                 relation_for("tn", sp, B.JA_F32), "JA_ERR_DTYPE"),                           # f32 inputs
+                (bf[:2] + [relation_for("tn", sp, B.JA_F16)], relation_for("tn", sp, B.JA_BF16), "JA_ERR_DTYPE"),
+                (bf[:2] + [relation_for("tn", {**sp, "n": [0, 48, 96]}, B.JA_BF16)],
+                 relation_for("tn", sp, B.JA_BF16), "JA_ERR_SHAPE")):                         # residual blocked apart
+            with pytest.raises(B.JaError) as e:
+                B.ja_plan_create(s, d, ins, out)
+            assert e.value.name == code
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
+    sw = {"t": [0, 64, 128], "d": [0, 64], "f": [0, 48, 96], "c": [0, 2]}
+    plain = _tuples(B, "td,df->tf", "contract", {k: sw[k] for k in "tdf"})
+    fused = _tuples(B, "td,dfc->tf", "contract_swiglu", sw)
+    assert fused[0] == "tdfc" and np.array_equal(plain[1], fused[1][:, :3]) and np.array_equal(plain[2], fused[2])
+    s = B.ja_spec_create("td,dfc->tf", "contract_swiglu")
+    try:
+        d = B.ja_decomp_create(s, [128, 64, 96, 2], [2, 1, 2, 1], [sw["t"], sw["d"], sw["f"], sw["c"]])
+        try:
+            p = B.ja_plan_create(s, d, [relation_for("td", sw, B.JA_BF16), relation_for("dfc", sw, B.JA_BF16)],
+                                 relation_for("tf", sw, B.JA_BF16))
+            B.ja_plan_destroy(p)
+        finally:
+            B.ja_decomp_destroy(d)
+        for ext, iv, splits in (([128, 64, 96, 4], [2, 1, 2, 1], [sw["t"], sw["d"], sw["f"], [0, 4]]),
+                                ([128, 64, 96, 2], [2, 1, 2, 2], [sw["t"], sw["d"], sw["f"], [0, 1, 2]])):
+            d = B.ja_decomp_create(s, ext, iv, splits)
+            try:
+                c = {"c": splits[3]}
+                with pytest.raises(B.JaError) as e:
+                    B.ja_plan_create(s, d, [relation_for("td", sw, B.JA_BF16),
+                                            relation_for("dfc", {**sw, **c}, B.JA_BF16)],
+                                     relation_for("tf", sw, B.JA_BF16))
+                assert e.value.name == "JA_ERR_DECOMP"
+            finally:
+                B.ja_decomp_destroy(d)
+        g = B.ja_graph_create()
+        try:
+            x = B.ja_graph_add_input(g, [128, 64])
+            w = B.ja_graph_add_input(g, [64, 96, 2])
+            with pytest.raises(B.JaError) as e:
+                B.ja_graph_add_op(g, s, [x, w])
+            assert e.value.name == "JA_ERR_UNSUPPORTED"
+        finally:
+            B.ja_graph_destroy(g)
+    finally:
         B.ja_spec_destroy(s)
 
 

@@ -467,6 +467,69 @@ def test_block_tokens_match_full(orc):
     assert np.array_equal(yt, y[toks])
 
 
+def test_contract_residual_rounds_once(orc):
+    """A B + R with nothing rounded in between.  Small integers: the exact
+    brute-force value.  The tie case: A B = 2^-8 + 2^-16 needs nine
+    significant bits; rounded first to bf16 it becomes 2^-8 (a tie, to even)
+    and 1 + 2^-8 is again a tie that goes to 1, while the unrounded sum
+    1 + 2^-8 + 2^-16 rounds up to 1 + 2^-7."""
+    rng = np.random.default_rng(11)
+    A = rng.integers(-3, 4, (5, 7)).astype(np.float64)
+    Bm = rng.integers(-3, 4, (7, 6)).astype(np.float64)
+    R = rng.integers(-9, 10, (5, 6)).astype(np.float64)
+    assert np.array_equal(orc.contract_residual("ij,jk->ik", A, Bm, R),
+                          orc.brute_force_einsum("ij,jk->ik", A, Bm) + R)
+    A = np.array([[1.0, 1.0]])
+    Bm = np.array([[2.0 ** -8], [2.0 ** -16]])
+    R = np.array([[1.0]])
+    once = orc.round_bf16(orc.contract_residual("ij,jk->ik", A, Bm, R))
+    twice = orc.round_bf16(orc.add(orc.round_bf16(orc.einsum("ij,jk->ik", A, Bm)), R))
+    assert once[0, 0] == 1.0 + 2.0 ** -7 and twice[0, 0] == 1.0
+
+
+def test_contract_swiglu_pair_order(orc):
+    """Member 0 of the pair is the gate, member 1 the up projection.  With
+    the up weights reading a column of ones, the result is silu of the gate:
+    silu(ln 3) = ln 3 / (1 + 1/3) = 0.75 ln 3, silu(0) = 0; swapping the
+    members would give silu(1) * ln 3 instead."""
+    l3 = np.log(3.0)
+    A = np.array([[l3, 1.0], [0.0, 1.0]])            # rows: (x, 1)
+    W = np.zeros((2, 1, 2))
+    W[0, 0, 0] = 1.0                                 # gate = x
+    W[1, 0, 1] = 1.0                                 # up = 1
+    h = orc.contract_swiglu("td,dfc->tf", A, W)
+    assert abs(h[0, 0] - 0.75 * l3) < 1e-15 and h[1, 0] == 0.0
+    # a wider case equals silu(A Wg) * (A Wu) from the separate contractions
+    rng = np.random.default_rng(12)
+    A = rng.standard_normal((4, 6))
+    Wg, Wu = rng.standard_normal((6, 5)), rng.standard_normal((6, 5))
+    h = orc.contract_swiglu("td,dfc->tf", A, np.stack([Wg, Wu], axis=2))
+    assert np.array_equal(h, orc.swiglu(orc.matmul(A, Wg), orc.matmul(A, Wu)))
+
+
+def test_fused_block_rounding_points(orc):
+    """The fused block (adds and SwiGLU applied inside the contractions)
+    rounds fewer intermediates: with zero projections it is still the
+    identity, token rows still agree with the full block bit for bit, its
+    intermediates a, gate, up and d are the unrounded contraction results,
+    and it differs from the unfused block by no more than bf16 rounding."""
+    w, batch, seq, heads = _tiny_block(5)
+    w["x"] = orc.round_bf16(w["x"])
+    z = {k: (np.zeros_like(v) if k in ("w_o", "w_down") else v) for k, v in w.items()}
+    assert np.array_equal(orc.llama_block(**z, batch=batch, seq=seq, heads=heads, fused=True), w["x"])
+    y, mid = orc.llama_block(**w, batch=batch, seq=seq, heads=heads, fused=True, return_intermediates=True)
+    toks = [0, 2, seq - 1, seq + 1]
+    yt = orc.llama_block_tokens(**w, batch=batch, seq=seq, heads=heads, tokens=toks, fused=True)
+    assert np.array_equal(yt, y[toks])
+    for k in ("a", "gate", "up", "d"):
+        assert not np.array_equal(mid[k], orc.round_bf16(mid[k]))
+    for k in ("h1", "qkv", "O", "x2", "h2", "f"):
+        assert np.array_equal(mid[k], orc.round_bf16(mid[k]))
+    yu = orc.llama_block(**w, batch=batch, seq=seq, heads=heads)
+    assert not np.array_equal(y, yu)
+    assert np.linalg.norm(y - yu) <= 2.0 ** -7 * np.linalg.norm(yu)
+
+
 def test_gqa_block_equals_mha_block_on_expanded_weights(orc):
     """Grouped-query block (4 query heads over 2 key-value heads, section
     3.3): the same as the multi-head block whose W_k and W_v repeat each
