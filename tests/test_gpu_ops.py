@@ -111,6 +111,43 @@ def test_matmul_fp32_2x2x2(dev, orc):
         o.close()
 
 
+def test_one_cell_blocks_fp32(dev, orc):
+    """The degenerate decomposition: every interval one element long, so every
+    tuple joins two scalars and every segment sums j of them -- the scalar
+    relational join-agg of the paper's section 1, run on the GPU.  Small
+    integers keep every product and sum exact, so the result must equal the
+    brute-force join bit for bit, fused and unfused."""
+    import torch
+
+    from tensor_relational_join_amd.binding import JA_F32
+
+    rng = np.random.default_rng(7)
+    I, J, K = 5, 4, 3
+    A = rng.integers(-3, 4, (I, J)).astype(np.float64)
+    Bm = rng.integers(-3, 4, (J, K)).astype(np.float64)
+    sp = {"i": list(range(I + 1)), "j": list(range(J + 1)), "k": list(range(K + 1))}
+    got, o, ins = _run(dev, orc, "ij,jk->ik", "contract", sp, [A, Bm], in_dtypes=[JA_F32, JA_F32], out_dtype=JA_F32)
+    try:
+        rec, seg = o.tuples()
+        assert rec.shape[0] == I * J * K and len(seg) - 1 == I * K
+        want = orc.brute_force_einsum("ij,jk->ik", A, Bm)
+        assert np.array_equal(got, want)
+        part = o.partial_buffer()
+        o.kernel(ins, part)
+        out2 = torch.empty(I * K, dtype=torch.float32, device="cuda")
+        o.agg(part, out2)
+        torch.cuda.synchronize()
+        got2 = orc.Relation((I, K), [sp["i"], sp["k"]]).unpack(f32_host(out2)).astype(np.float64)
+        assert np.array_equal(got2, want)
+        # each one-element partial is the product of its tuple's two cells
+        p = f32_host(part)
+        for t, r in enumerate(rec.tolist()):
+            i, j, k = (r[o.letters.index(c)] for c in "ijk")
+            assert p[t] == A[i, j] * Bm[j, k]
+    finally:
+        o.close()
+
+
 def test_max_aggregation_fp32(dev, orc):
     import torch
 
