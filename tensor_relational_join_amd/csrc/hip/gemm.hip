@@ -4,12 +4,12 @@
 // A matrix multiply is a join of A blocks and B blocks on the contracted
 // index followed by a SUM over the contracted blocks ("Every Kernel Is a
 // Join", paperpeel full text, section 1 and section 3.2, Examples 3.8 and
-// 3.9).  Here one workgroup owns one output tile of one segment (all tuples
-// that write one output block).  It walks the segment's tuples in ascending
-// order and, inside each tuple, the contracted extent in BK-wide stages,
-// accumulating in fp32 registers across tuple boundaries; the aggregated tile
-// is written once.  So the SUM costs no extra memory traffic and needs no
-// atomics (eager aggregation pushed into the kernel).
+// 3.9).  Here a workgroup owns one output tile of one segment (all tuples
+// that write one output block) at a time.  It walks the segment's tuples in
+// ascending order and, inside each tuple, the contracted extent in BK-wide
+// stages, accumulating in fp32 registers across tuple boundaries; the
+// aggregated tile is written once.  So the SUM costs no extra memory traffic
+// and needs no atomics (eager aggregation pushed into the kernel).
 //
 // bf16 path: v_mfma_f32_16x16x32_bf16 on CDNA4.  A workgroup of 8 wavefronts
 // owns a 256 x 256 output tile (128 x 64 per wavefront), which keeps the
@@ -21,7 +21,10 @@
 // stage i+1 are in flight while stage i multiplies.  The host lists the tiles
 // of a segment in groups of GEMM_GROUP_M row tiles, and xcd_remap hands each
 // XCD a contiguous run of that list, so the tiles resident on one XCD share A
-// and B panels in its L2.
+// and B panels in its L2.  The direct-to-LDS kernel below is persistent: one
+// workgroup per compute unit walks its XCD's run, loading the next tile's
+// first stage while the current tile's results are stored.
+#include <atomic>
 #include <type_traits>
 
 #include "dev_common.h"
@@ -277,7 +280,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* 
 
     // epilogue: lane owns C[row][col .. col+3] of every fragment
     const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
-    static_assert(FM % 2 == 0, "the epilogue takes fragment rows in pairs");
     // two rows of fragments at a time: their residual loads are all in
     // flight before the first of their stores
 #pragma unroll
@@ -457,22 +459,26 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const GemmTile tl = tiles[xcd_remap(blockIdx.x, ntiles)];
-    const GemmSeg sg = segs[tl.seg];
-    const int m0 = tl.m0, n0 = tl.n0;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)gemm_lds;
-
-    int nst = 0;
-    for (int t = sg.t_begin; t < sg.t_end; ++t) nst += (tuples[t].K + BK - 1) / BK;
+    // The workgroup is persistent: it takes the tiles of the list at
+    // positions blockIdx.x, blockIdx.x + gridDim.x, ... (after xcd_remap, so
+    // every tile it takes is dealt to its own XCD, in the list's order).
+    int vt = blockIdx.x;
+    GemmTile tl = tiles[xcd_remap(vt, ntiles)];
+    GemmSeg sg = segs[tl.seg];
+    int m0 = tl.m0, n0 = tl.n0;
+    auto count_stages = [&]() {
+        int n = 0;
+        for (int t = sg.t_begin; t < sg.t_end; ++t) n += (tuples[t].K + BK - 1) / BK;
+        return n;
+    };
+    int nst = count_stages();
 
     f32x4_t acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // load cursor: tuple lt, contracted offset lk inside it; the per-lane
-    // offsets and buffer descriptors of tuple lt are cached
+    // offsets and buffer descriptors of tuple lt are cached (per tile: the
+    // offsets depend on the tile's rows and columns)
     int lt = sg.t_begin, lk = 0, cached = -1;
     TA ta;
     TB tb;
@@ -567,41 +573,75 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         wait_stage(0);
         read_frags(0, fa[0], fb[0]);
     }
-    for (int it = 0; it < nst; it += 2) {
-        step(it, fa[0], fb[0], fa[1], fb[1]);
-        if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
-    }
+    // epilogue of one tile: lane owns C[row][col .. col+3] of every fragment
+    auto epilogue = [&](int64_t cbase, int ldc, int eM, int eN, int em0, int en0) {
+        // The lane's row and column offsets are recomputed here from an
+        // opaque copy of the lane index: hoisted out of the tile loop they
+        // would stay live through the K loop and push it into spills.
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int kc = el >> 4;
+        // one row of fragments at a time: its residual loads are all in
+        // flight before the first of its stores
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = em0 + arow + i * 16 + (el & 15);
+            uint2 res[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = en0 + brow + j * 16 + 4 * kc;
+                res[j] = row < eM ? residual4(R, epi, cbase + (int64_t)row * ldc + col, col, eN) : make_uint2(0u, 0u);
+            }
+            if (row >= eM) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = en0 + brow + j * 16 + 4 * kc;
+                store_out4<IN_F16, OUT16>(C, R, epi, cbase + (int64_t)row * ldc + col, col, eN, acc[i][j], res[j]);
+            }
+        }
+    };
 
-    // epilogue: lane owns C[row][col .. col+3] of every fragment
-    const int kc = lane >> 4;
-    const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
-    static_assert(FM % 2 == 0, "the epilogue takes fragment rows in pairs");
-    // two rows of fragments at a time: their residual loads are all in
-    // flight before the first of their stores
+    while (true) {
 #pragma unroll
-    for (int i0 = 0; i0 < FM; i0 += 2) {
-        uint2 res[2][FN];
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int i = i0; i < i0 + 2; ++i) {
-            const int row = m0 + arow + i * 16 + (lane & 15);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + brow + j * 16 + 4 * kc;
-                res[i - i0][j] = row < sg.M ? residual4(R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N)
-                                            : make_uint2(0u, 0u);
-            }
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (nst > 0) {
+            wait_stage(0);
+            read_frags(0, fa[0], fb[0]);
         }
-#pragma unroll
-        for (int i = i0; i < i0 + 2; ++i) {
-            const int row = m0 + arow + i * 16 + (lane & 15);
-            if (row >= sg.M) continue;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + brow + j * 16 + 4 * kc;
-                store_out4<IN_F16, OUT16>(C, R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N, acc[i][j],
-                                          res[i - i0][j]);
-            }
+        for (int it = 0; it < nst; it += 2) {
+            step(it, fa[0], fb[0], fa[1], fb[1]);
+            if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
         }
+        // Next tile: its first stage is loaded while this tile's results
+        // leave, the rest after them (so that waiting for stage 0 does not
+        // wait for the later stages).  The barrier makes sure that every
+        // wavefront's last fragment reads are complete before LDS is refilled.
+        const int64_t ecbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
+        const int eldc = sg.ldc, eM = sg.M, eN = sg.N, em0 = m0, en0 = n0;
+        const int vnext = vt + (int)gridDim.x;
+        const bool more = vnext < ntiles;
+        if (more) {
+            vt = vnext;
+            tl = tiles[xcd_remap(vt, ntiles)];
+            sg = segs[tl.seg];
+            m0 = tl.m0;
+            n0 = tl.n0;
+            nst = count_stages();
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (more) {
+            lt = sg.t_begin;
+            lk = 0;
+            cached = -1;
+            if (nst > 0) issue(0);
+        }
+        epilogue(ecbase, eldc, eM, eN, em0, en0);
+        if (!more) break;
+#pragma unroll
+        for (int s = 1; s < NS; ++s)
+            if (s < nst) issue(s);
     }
 }
 
@@ -669,12 +709,29 @@ static void launch_bf16(const GemmTile* tiles, int ntiles, const GemmSeg* segs, 
                        (const uint16_t*)R, epi);
 }
 
+// Compute units of the current device (one persistent contraction workgroup
+// each); cached per device.
+static int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 0;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int AL, int BL, bool F16, bool OUT16>
 static void launch_bf16_dma(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples,
                             const void* A, const void* B, void* C, const void* R, int epi, hipStream_t s) {
     constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, NS = GEMM_DMA_STAGES, WM = 2, WN = 4;
     constexpr unsigned lds = (unsigned)NS * (BM + BN) * 32 * sizeof(uint16_t);
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, F16, OUT16>), dim3(ntiles),
+    // one workgroup per compute unit (128 KiB of LDS each), walking the tile list
+    const int cus = device_cus();
+    const int grid = cus > 0 && cus < ntiles ? cus : ntiles;
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, F16, OUT16>), dim3(grid),
                        dim3(WM * WN * 64), lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A,
                        (const uint16_t*)B, C, (const uint16_t*)R, epi);
 }
