@@ -25,9 +25,15 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 // on gfx950 so that every MFMA fragment read takes the minimum 4 LDS cycles:
 // K tile [key][d] bf16, 16-byte chunk c of row `key` at c ^ kswz(key);
 // V^T tile [d][key'] fp16 (key' = key with the middle quads of every 16 keys
-// swapped, see below), chunk c of row d at c ^ vswz(d).
+// swapped, see below), chunk c of row d at c ^ vswz(d).  A V^T row is 128
+// bytes, so rows of one parity share one half of the 64 banks.  An MFMA read
+// covers 32 consecutive rows, inside which the last term of vswz is constant;
+// the 8 rows of one parity that a staging write covers (rows 16 apart) get 8
+// distinct swizzles, which spreads them over all chunk positions of their half.
 __device__ __forceinline__ int kswz(int r) { return ((r & 1) << 1) ^ ((r >> 1) & 1) ^ (r & 4) ^ ((r >> 1) & 8); }
-__device__ __forceinline__ int vswz(int d) { return (d & 6) ^ (((d >> 3) & 1) * 3) ^ (((d >> 4) & 1) * 7); }
+__device__ __forceinline__ int vswz(int d) {
+    return (d & 6) ^ (((d >> 3) & 1) * 3) ^ (((d >> 4) & 1) * 7) ^ (((d >> 5) & 3) << 1);
+}
 __device__ __forceinline__ int at_koff(int key, int c) { return key * ATTN_D + ((c ^ kswz(key)) << 3); }
 __device__ __forceinline__ int at_voff(int d, int c) { return d * AT_KT + ((c ^ vswz(d)) << 3); }
 
@@ -219,36 +225,40 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     };
     // V^T[d][key'] <- vr, in fp16 (converted from bf16, moved as is from
     // fp16); key' swaps the middle quads of each 16 keys, matching the order
-    // P^T takes from the S^T accumulators
+    // P^T takes from the S^T accumulators.  Word w of a lane's 4 keys holds
+    // rows 8 dj + 2 w (low halves) and 8 dj + 2 w + 1 (high halves); lanes of
+    // odd dj write the odd row first, so that each write instruction covers
+    // rows of both parities (both halves of the banks).
     auto store_v = [&](int buf) {
         _Float16* vt = reinterpret_cast<_Float16*>(at_lds + buf * AT_STAGE + AT_KT * D);
         const int hgrp = kg >> 2, q = kg & 3;
         const int qpos = q == 1 ? 2 : (q == 2 ? 1 : q);
         const int c = 2 * hgrp + (qpos >> 1), half = qpos & 1;
+        const int par = dj & 1;
         const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vr[0]);
         const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vr[1]);
         const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vr[2]);
         const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vr[3]);  // words of the 4 keys' 8 d values
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int d = dj * 8 + 2 * w + e;
-                if constexpr (F16) {
-                    // already fp16: move the e-th half of word w of the 4 keys
-                    const uint32_t sh = 16 * e, mk = 0xffffu;
-                    *reinterpret_cast<uint2*>(vt + at_voff(d, c) + half * 4) =
-                        make_uint2(((r0[w] >> sh) & mk) | (((r1[w] >> sh) & mk) << 16),
-                                   ((r2[w] >> sh) & mk) | (((r3[w] >> sh) & mk) << 16));
-                } else {
-                    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-                    h4 hv = {(_Float16)(e ? bf16hi_to_f32(r0[w]) : bf16lo_to_f32(r0[w])),
-                             (_Float16)(e ? bf16hi_to_f32(r1[w]) : bf16lo_to_f32(r1[w])),
-                             (_Float16)(e ? bf16hi_to_f32(r2[w]) : bf16lo_to_f32(r2[w])),
-                             (_Float16)(e ? bf16hi_to_f32(r3[w]) : bf16lo_to_f32(r3[w]))};
-                    *reinterpret_cast<h4*>(vt + at_voff(d, c) + half * 4) = hv;
-                }
+        for (int w = 0; w < 4; ++w) {
+            uint2 lo, hi;  // the 4 keys' fp16 values of rows 8 dj + 2 w and 8 dj + 2 w + 1
+            if constexpr (F16) {
+                const uint32_t mk = 0xffffu;
+                lo = make_uint2((r0[w] & mk) | (r1[w] << 16), (r2[w] & mk) | (r3[w] << 16));
+                hi = make_uint2((r0[w] >> 16) | (r1[w] & 0xffff0000u), (r2[w] >> 16) | (r3[w] & 0xffff0000u));
+            } else {
+                typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                const h4 l4 = {(_Float16)bf16lo_to_f32(r0[w]), (_Float16)bf16lo_to_f32(r1[w]),
+                               (_Float16)bf16lo_to_f32(r2[w]), (_Float16)bf16lo_to_f32(r3[w])};
+                const h4 h4v = {(_Float16)bf16hi_to_f32(r0[w]), (_Float16)bf16hi_to_f32(r1[w]),
+                                (_Float16)bf16hi_to_f32(r2[w]), (_Float16)bf16hi_to_f32(r3[w])};
+                lo = __builtin_bit_cast(uint2, l4);
+                hi = __builtin_bit_cast(uint2, h4v);
             }
+            const int d0 = dj * 8 + 2 * w + par, d1 = dj * 8 + 2 * w + (par ^ 1);
+            *reinterpret_cast<uint2*>(vt + at_voff(d0, c) + half * 4) = par ? hi : lo;
+            *reinterpret_cast<uint2*>(vt + at_voff(d1, c) + half * 4) = par ? lo : hi;
+        }
     };
     auto sync_step = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
