@@ -463,10 +463,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     // The workgroup is persistent: it takes the tiles of the list at
     // positions blockIdx.x, blockIdx.x + gridDim.x, ... (after xcd_remap, so
     // every tile it takes is dealt to its own XCD, in the list's order).
+    // A kernel whose tile height is below the list's (BM < GEMM_BF16_TM) runs
+    // the tail of a list: virtual tile v is rows [BM (v % 2), BM (v % 2 + 1))
+    // of listed tile v / 2 (GEMM_BF16_TM = 2 BM), taken in list order.
+    constexpr bool HALF = BM < GEMM_BF16_TM;
+    static_assert(!HALF || 2 * BM == GEMM_BF16_TM, "a tail tile is half a listed tile");
+    auto tile_at = [&](int v) { return HALF ? tiles[v >> 1] : tiles[xcd_remap(v, ntiles)]; };
+    auto row0 = [&](int v, const GemmTile& t) { return HALF ? t.m0 + (v & 1) * BM : t.m0; };
     int vt = blockIdx.x;
-    GemmTile tl = tiles[xcd_remap(vt, ntiles)];
+    GemmTile tl = tile_at(vt);
     GemmSeg sg = segs[tl.seg];
-    int m0 = tl.m0, n0 = tl.n0;
+    int m0 = row0(vt, tl), n0 = tl.n0;
     auto count_stages = [&]() {
         int n = 0;
         for (int t = sg.t_begin; t < sg.t_end; ++t) n += (tuples[t].K + BK - 1) / BK;
@@ -624,9 +631,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         const bool more = vnext < ntiles;
         if (more) {
             vt = vnext;
-            tl = tiles[xcd_remap(vt, ntiles)];
+            tl = tile_at(vt);
             sg = segs[tl.seg];
-            m0 = tl.m0;
+            m0 = row0(vt, tl);
             n0 = tl.n0;
             nst = count_stages();
         }
@@ -730,10 +737,22 @@ static void launch_bf16_dma(const GemmTile* tiles, int ntiles, const GemmSeg* se
     constexpr unsigned lds = (unsigned)NS * (BM + BN) * 32 * sizeof(uint16_t);
     // one workgroup per compute unit (128 KiB of LDS each), walking the tile list
     const int cus = device_cus();
-    const int grid = cus > 0 && cus < ntiles ? cus : ntiles;
+    // A last round that would fill at most half the compute units runs as
+    // twice as many half-height tiles instead: 2r tiles of half the work each
+    // finish sooner than r full tiles on r units.
+    const int tail = cus > 0 && ntiles > cus && 2 * (ntiles % cus) <= cus ? ntiles % cus : 0;
+    const int nmain = ntiles - tail;
+    const int grid = cus > 0 && cus < nmain ? cus : nmain;
     hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, NS, WM, WN, AL, BL, F16, OUT16>), dim3(grid),
-                       dim3(WM * WN * 64), lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A,
+                       dim3(WM * WN * 64), lds, s, tiles, nmain, segs, tuples, (const uint16_t*)A,
                        (const uint16_t*)B, C, (const uint16_t*)R, epi);
+    if (tail > 0) {
+        constexpr int HM = BM / 2;
+        constexpr unsigned hlds = (unsigned)NS * (HM + BN) * 32 * sizeof(uint16_t);
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<HM, BN, NS, WM, WN, AL, BL, F16, OUT16>), dim3(2 * tail),
+                           dim3(WM * WN * 64), hlds, s, tiles + nmain, 2 * tail, segs, tuples, (const uint16_t*)A,
+                           (const uint16_t*)B, C, (const uint16_t*)R, epi);
+    }
 }
 
 // 16-bit inputs (bf16 or, with F16, IEEE half) into fp32 accumulators;

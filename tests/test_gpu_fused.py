@@ -91,6 +91,33 @@ def test_contract_add(dev, orc, einsum, sp, f16):
     assert np.mean(got == want) > 0.95
 
 
+# A tile list whose last round would fill at most half of the compute units
+# runs that round as twice as many half-height tiles (a second launch).  Each
+# case leaves such a tail on 256 compute units: 15 x 20 = 300 tiles of
+# 256 x 256 (tail 44; the last row tile is 156 rows, so its second half holds
+# 28), and 2 segments of 8 x 20 (tail 64, all in the second segment).
+TAIL_CASES = [
+    ("ij,jk->ik", "contract", {"i": [0, 3740], "j": [0, 40, 72], "k": [0, 5120]}),
+    ("ij,jk,ik->ik", "contract_add", {"i": [0, 3740], "j": [0, 40, 72], "k": [0, 5120]}),
+    ("ij,kj->ik", "contract", {"i": [0, 1870, 3740], "j": [0, 72], "k": [0, 5120]}),
+]
+
+
+@pytest.mark.parametrize("einsum,op,sp", TAIL_CASES)
+def test_contract_with_half_height_tail(dev, orc, einsum, op, sp):
+    lhs, out = einsum.split("->")
+    shapes = [tuple(sp[c][-1] for c in s) for s in lhs.split(",")]
+    dense = [synth.normal_bf16(37, i, shp, std=0.05 if i == 1 else 1.0) for i, shp in enumerate(shapes)]
+    got, o, _ = _run(dev, orc, einsum, op, sp, dense)
+    o.close()
+    plain = "%s,%s->%s" % (lhs.split(",")[0], lhs.split(",")[1], out)
+    w = [orc.bf16_to_f64(x) for x in dense]
+    want = orc.contract_residual(plain, *w) if op == "contract_add" else orc.einsum(plain, w[0], w[1])
+    want = orc.round_bf16(want)
+    assert rel_frobenius(got, want) <= TOL
+    assert np.mean(got == want) > 0.95
+
+
 SWIGLU_CASES = [
     ("td,dfc->tf", {"t": [0, 100, 300], "d": [0, 64, 256], "f": [0, 68, 132], "c": [0, 2]}),
     ("td,dfc->tf", {"t": [0, 520], "d": [0, 200, 336, 432], "f": [0, 36, 100, 388], "c": [0, 2]}),
