@@ -720,7 +720,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (every kernel runs on one "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (every kernel runs on one "
               "GPU's share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     _device_snapshot()  # before anything initialises the GPU in this process

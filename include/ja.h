@@ -66,7 +66,7 @@ typedef int32_t ja_status;
 #define JA_ERR_SHAPE (-4)       /* relation shape or blocking does not match the spec / decomposition */
 #define JA_ERR_DTYPE (-5)       /* unsupported or mismatched element type */
 #define JA_ERR_WORKSPACE (-6)   /* a caller buffer is smaller than the size query returned */
-#define JA_ERR_UNSUPPORTED (-7) /* valid request that this build has no kernel for */
+#define JA_ERR_UNSUPPORTED (-7) /* valid request that the library has no kernel for */
 #define JA_ERR_HIP (-8)         /* a HIP runtime call failed (message in ja_last_error) */
 #define JA_ERR_STATE (-9)       /* plan used before ja_plan_upload / ja_repart_upload */
 
