@@ -97,25 +97,36 @@ def test_contract_add(dev, orc, einsum, sp, f16):
 # 256 x 256 (tail 44; the last row tile is 156 rows, so its second half holds
 # 28), and 2 segments of 8 x 20 (tail 64, all in the second segment).
 TAIL_CASES = [
-    ("ij,jk->ik", "contract", {"i": [0, 3740], "j": [0, 40, 72], "k": [0, 5120]}),
-    ("ij,jk,ik->ik", "contract_add", {"i": [0, 3740], "j": [0, 40, 72], "k": [0, 5120]}),
-    ("ij,kj->ik", "contract", {"i": [0, 1870, 3740], "j": [0, 72], "k": [0, 5120]}),
+    ("ij,jk->ik", "contract", {"i": [0, 3740], "j": [0, 40, 72], "k": [0, 5120]}, False),
+    ("ij,jk,ik->ik", "contract_add", {"i": [0, 3740], "j": [0, 40, 72], "k": [0, 5120]}, False),
+    ("ij,kj->ik", "contract", {"i": [0, 1870, 3740], "j": [0, 72], "k": [0, 5120]}, False),
+    # SwiGLU over (gate, up) column pairs: 2 x 2560 columns, 20 column tiles
+    ("td,dfc->tf", "contract_swiglu", {"t": [0, 3740], "d": [0, 40, 72], "f": [0, 2560], "c": [0, 2]}, False),
+    ("ij,jk,ik->ik", "contract_add", {"i": [0, 3740], "j": [0, 40, 72], "k": [0, 5120]}, True),
 ]
 
 
-@pytest.mark.parametrize("einsum,op,sp", TAIL_CASES)
-def test_contract_with_half_height_tail(dev, orc, einsum, op, sp):
+@pytest.mark.parametrize("einsum,op,sp,f16", TAIL_CASES)
+def test_contract_with_half_height_tail(dev, orc, einsum, op, sp, f16):
     lhs, out = einsum.split("->")
     shapes = [tuple(sp[c][-1] for c in s) for s in lhs.split(",")]
-    dense = [synth.normal_bf16(37, i, shp, std=0.05 if i == 1 else 1.0) for i, shp in enumerate(shapes)]
-    got, o, _ = _run(dev, orc, einsum, op, sp, dense)
+    draw = synth.normal_f16 if f16 else synth.normal_bf16
+    widen = orc.f16_to_f64 if f16 else orc.bf16_to_f64
+    rnd = orc.round_f16 if f16 else orc.round_bf16
+    dense = [draw(37, i, shp, std=0.05 if i == 1 else 1.0) for i, shp in enumerate(shapes)]
+    got, o, _ = _run(dev, orc, einsum, op, sp, dense, f16=f16)
     o.close()
+    w = [widen(x) for x in dense]
     plain = "%s,%s->%s" % (lhs.split(",")[0], lhs.split(",")[1], out)
-    w = [orc.bf16_to_f64(x) for x in dense]
-    want = orc.contract_residual(plain, *w) if op == "contract_add" else orc.einsum(plain, w[0], w[1])
-    want = orc.round_bf16(want)
+    if op == "contract_swiglu":
+        want = orc.contract_swiglu(einsum, w[0], w[1])
+    elif op == "contract_add":
+        want = orc.contract_residual(plain, *w)
+    else:
+        want = orc.einsum(plain, w[0], w[1])
+    want = rnd(want)
     assert rel_frobenius(got, want) <= TOL
-    assert np.mean(got == want) > 0.95
+    assert np.mean(got == want) > (0.9 if op == "contract_swiglu" else 0.95)
 
 
 SWIGLU_CASES = [
