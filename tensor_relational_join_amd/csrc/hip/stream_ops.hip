@@ -356,7 +356,11 @@ hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, in
 // ---------------------------------------------------------------- aggregation
 // One workgroup per (segment, chunk of AGG_CHUNK output elements); each
 // thread folds its elements over the segment's tuples in ascending order and
-// writes them once.  No atomics: every output element has one owner.
+// writes them once.  No atomics: every output element has one owner.  A
+// thread owns PER consecutive elements: where every partial block of the
+// segment and the output block start on a 16-byte boundary they move as
+// 16-byte vectors (two loads per tuple, one store of 8 halves or two of 4
+// floats), otherwise, and for the last elements of a block, one by one.
 constexpr int AGG_THREADS = 256;
 
 template <int OUT>  // 0: f32, 1: bf16, 2: IEEE half
@@ -368,23 +372,46 @@ __global__ __launch_bounds__(AGG_THREADS) void agg_kernel(const AggTile* __restr
     const AggTile tl = tiles[blockIdx.x];
     const AggSeg sg = segs[tl.seg];
     constexpr int PER = AGG_CHUNK / AGG_THREADS;
+    static_assert(PER == 8, "a thread owns two 16-byte vectors of partials");
+    const bool mx = op == JA_AGG_MAX;
+    const int e0 = tl.e0 + threadIdx.x * PER;
     float acc[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = op == JA_AGG_MAX ? -INFINITY : 0.f;
+    for (int j = 0; j < PER; ++j) acc[j] = mx ? -INFINITY : 0.f;
+    bool vec = (sg.out_off & (OUT == 0 ? 3 : 7)) == 0;
+    for (int t = sg.t_begin; t < sg.t_end; ++t) vec = vec && (poff[t] & 3) == 0;
+    if (vec && e0 + PER <= sg.nelem) {
+#pragma unroll 4
+        for (int t = sg.t_begin; t < sg.t_end; ++t) {
+            const float4* p = reinterpret_cast<const float4*>(part + poff[t] + e0);
+            const float4 a = p[0], b = p[1];
+            const float v[PER] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < PER; ++j) acc[j] = mx ? fmaxf(acc[j], v[j]) : acc[j] + v[j];
+        }
+        if (OUT == 0) {
+            float4* o = reinterpret_cast<float4*>((float*)out + sg.out_off + e0);
+            o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        } else {
+            uint32_t w[PER / 2];
+#pragma unroll
+            for (int j = 0; j < PER / 2; ++j)
+                w[j] = OUT == 1 ? (f32_to_bf16(acc[2 * j]) | (f32_to_bf16(acc[2 * j + 1]) << 16))
+                                : (f32_to_f16(acc[2 * j]) | (f32_to_f16(acc[2 * j + 1]) << 16));
+            *reinterpret_cast<uint4*>((uint16_t*)out + sg.out_off + e0) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        return;
+    }
     for (int t = sg.t_begin; t < sg.t_end; ++t) {
         const float* p = part + poff[t];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            int e = tl.e0 + threadIdx.x + j * AGG_THREADS;
-            if (e < sg.nelem) {
-                float v = p[e];
-                acc[j] = op == JA_AGG_MAX ? fmaxf(acc[j], v) : acc[j] + v;
-            }
-        }
+        for (int j = 0; j < PER; ++j)
+            if (e0 + j < sg.nelem) acc[j] = mx ? fmaxf(acc[j], p[e0 + j]) : acc[j] + p[e0 + j];
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        int e = tl.e0 + threadIdx.x + j * AGG_THREADS;
+        const int e = e0 + j;
         if (e < sg.nelem) {
             if (OUT == 1)
                 ((uint16_t*)out)[sg.out_off + e] = (uint16_t)f32_to_bf16(acc[j]);

@@ -148,6 +148,67 @@ def test_one_cell_blocks_fp32(dev, orc):
         o.close()
 
 
+@pytest.mark.parametrize("case", ["f32_ragged", "bf16"])
+def test_aggregation_of_host_partials(dev, orc, case):
+    """ja_agg alone, on fp32 partial blocks drawn on the host and laid out as
+    the unfused path lays them out (one block per tuple, in tuple order).
+    The fp32 case has block sizes that are not multiples of 4, so some
+    segments fold element by element and others in 16-byte vectors; the bf16
+    case writes packed halves.  SUM against the fold written out in float64,
+    MAX exactly."""
+    import torch
+
+    from tensor_relational_join_amd.binding import JA_AGG_MAX, JA_AGG_SUM, JA_BF16, JA_F32
+
+    if case == "f32_ragged":
+        sp = {"i": [0, 37, 100, 1125], "j": [0, 40, 72, 136], "k": [0, 29, 90, 2137]}
+        dt = JA_F32
+    else:
+        sp = {"i": [0, 40, 104, 1128], "j": [0, 40, 72, 136], "k": [0, 32, 96, 2144]}
+        dt = JA_BF16
+    o = dev.Op("ij,jk->ik", "contract", sp, "", [dt, dt], dt)
+    try:
+        rec, seg = o.tuples()
+        li, lk = o.letters.index("i"), o.letters.index("k")
+        sizes = [(sp["i"][r[li] + 1] - sp["i"][r[li]]) * (sp["k"][r[lk] + 1] - sp["k"][r[lk]]) for r in rec.tolist()]
+        offs = np.concatenate([[0], np.cumsum(sizes)])
+        rng = np.random.default_rng(11)
+        part = rng.standard_normal(int(offs[-1])).astype(np.float32)
+        part_dev = torch.from_numpy(part).cuda()
+        orel = orc.Relation((sp["i"][-1], sp["k"][-1]), [sp["i"], sp["k"]])
+        for op in (JA_AGG_SUM, JA_AGG_MAX):
+            want = np.zeros((sp["i"][-1], sp["k"][-1]))
+            for sgi in range(len(seg) - 1):
+                ts = range(int(seg[sgi]), int(seg[sgi + 1]))
+                r = rec[ts[0]]
+                i0, i1 = sp["i"][r[li]], sp["i"][r[li] + 1]
+                k0, k1 = sp["k"][r[lk]], sp["k"][r[lk] + 1]
+                blocks = [part[offs[t]:offs[t + 1]].astype(np.float64).reshape(i1 - i0, k1 - k0) for t in ts]
+                fold = blocks[0].copy()
+                for b in blocks[1:]:
+                    fold = fold + b if op == JA_AGG_SUM else np.maximum(fold, b)
+                want[i0:i1, k0:k1] = fold
+            out = dev.alloc(o.out_rel)
+            o.agg(part_dev, out, op=op)
+            torch.cuda.synchronize()
+            if dt == JA_F32:
+                got = orel.unpack(f32_host(out)).astype(np.float64)
+                if op == JA_AGG_MAX:
+                    assert np.array_equal(got, want)
+                else:
+                    assert rel_inf(got, want) <= FP32_TOL
+            else:
+                got = orc.bf16_to_f64(orel.unpack(bf16_bits(out)))
+                want_b = orc.round_bf16(want)
+                if op == JA_AGG_MAX:
+                    assert np.array_equal(got, want_b)
+                else:
+                    assert rel_frobenius(got, want_b) <= BF16_TOL
+                    assert np.mean(got == want_b) > 0.99
+    finally:
+        o.close()
+
+
 def test_max_aggregation_fp32(dev, orc):
     import torch
 
