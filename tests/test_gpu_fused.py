@@ -114,8 +114,23 @@ def test_contract_with_half_height_tail(dev, orc, einsum, op, sp, f16):
     widen = orc.f16_to_f64 if f16 else orc.bf16_to_f64
     rnd = orc.round_f16 if f16 else orc.round_bf16
     dense = [draw(37, i, shp, std=0.05 if i == 1 else 1.0) for i, shp in enumerate(shapes)]
-    got, o, _ = _run(dev, orc, einsum, op, sp, dense, f16=f16)
-    o.close()
+    got, o, ins = _run(dev, orc, einsum, op, sp, dense, f16=f16)
+    unfused = None
+    try:
+        if op == "contract":
+            # per-tuple partials (their own tile list, with its own tail), then the SUM
+            import torch
+
+            part = o.partial_buffer()
+            o.kernel(ins, part)
+            out2 = dev.alloc(o.out_rel)
+            o.agg(part, out2)
+            torch.cuda.synchronize()
+            orel = orc.Relation([sp[c][-1] for c in out], [sp[c] for c in out])
+            bits = out2.view(torch.int16).cpu().numpy().view(np.uint16)
+            unfused = (orc.f16_to_f64 if f16 else orc.bf16_to_f64)(orel.unpack(bits))
+    finally:
+        o.close()
     w = [widen(x) for x in dense]
     plain = "%s,%s->%s" % (lhs.split(",")[0], lhs.split(",")[1], out)
     if op == "contract_swiglu":
@@ -127,6 +142,9 @@ def test_contract_with_half_height_tail(dev, orc, einsum, op, sp, f16):
     want = rnd(want)
     assert rel_frobenius(got, want) <= TOL
     assert np.mean(got == want) > (0.9 if op == "contract_swiglu" else 0.95)
+    if unfused is not None:
+        assert rel_frobenius(unfused, want) <= TOL
+        assert np.mean(unfused == want) > 0.95
 
 
 SWIGLU_CASES = [
