@@ -263,6 +263,7 @@ GEMM_CU_FLOPS = 1213e12 / CUS   # measured fused bf16 contraction, per CU
 ATTN_CU_FLOPS = 775e12 / CUS    # measured causal attention, per CU
 COPY_BPS = 5.0e12               # measured plain device copy
 LAUNCH_US = 4.0
+HALF_TILE = 0.66                # measured: a half-height contraction tile's time over a full tile's
 
 
 def makespan(times: Sequence[float], cus: int = CUS) -> float:
@@ -273,6 +274,18 @@ def makespan(times: Sequence[float], cus: int = CUS) -> float:
         k = min(range(cus), key=lambda c: loads[c])
         loads[k] += t
     return max(loads) if times else 0.0
+
+
+def contract_makespan(times: Sequence[float], cus: int = CUS) -> float:
+    """A contraction's tiles: a last round that would fill at most half the
+    CUs runs, after the full rounds, as a second launch of twice as many
+    half-height tiles; the shortest tiles form that round."""
+    n, r = len(times), len(times) % cus
+    if n <= cus or r == 0 or 2 * r > cus:
+        return makespan(times, cus)
+    ts = sorted(times, reverse=True)
+    half = [HALF_TILE * x for x in ts[n - r:] for _ in range(2)]
+    return makespan(ts[:n - r], cus) + LAUNCH_US + makespan(half, cus)
 
 
 def op_device_time(op: dict, counts: Dict[str, int]) -> float:
@@ -334,7 +347,7 @@ def op_device_time(op: dict, counts: Dict[str, int]) -> float:
                     hi = min(t_hi, last + 1) if op["causal"] is not None else t_hi
                     keys += max(0, hi - t_lo)
                 tiles += [4.0 * 128 * op["ext"][d] * keys / ATTN_CU_FLOPS * 1e6] * nbh
-    return LAUNCH_US + makespan(tiles)
+    return LAUNCH_US + (contract_makespan(tiles) if op["kind"] == "contract" else makespan(tiles))
 
 
 def plan_device_time(g: Graph, plan: Sequence[Dict[str, int]]) -> float:

@@ -162,6 +162,7 @@ constexpr double DEV_ATTN_CU_FLOPS = 775e12 / DEV_CUS;   // measured causal atte
 constexpr double DEV_COPY_BPS = 5.0e12;                  // measured plain device copy, bytes/s
 constexpr double DEV_LAUNCH_US = 4.0;                    // per kernel launch
 constexpr int DEV_GEMM_TILE = 256, DEV_ATTN_ROWS = 128;
+constexpr double DEV_HALF_TILE = 0.66;  // measured: a half-height contraction tile's time over a full tile's
 
 // Longest-processing-time-first placement of tile times on DEV_CUS CUs: the
 // finishing time of the last CU.
@@ -177,6 +178,22 @@ double makespan(std::vector<double> t) {
         end = std::max(end, l);
     }
     return end;
+}
+
+// A contraction's tiles: a last round that would fill at most half the CUs
+// runs, after the full rounds, as a second launch of twice as many
+// half-height tiles (the shortest tiles form that round).
+double contract_makespan(std::vector<double> t) {
+    const size_t n = t.size(), r = n % DEV_CUS;
+    if (n <= (size_t)DEV_CUS || r == 0 || 2 * r > (size_t)DEV_CUS) return makespan(t);
+    std::sort(t.begin(), t.end(), std::greater<double>());
+    std::vector<double> half;
+    for (size_t i = n - r; i < n; ++i) {
+        half.push_back(DEV_HALF_TILE * t[i]);
+        half.push_back(DEV_HALF_TILE * t[i]);
+    }
+    t.resize(n - r);
+    return makespan(t) + DEV_LAUNCH_US + makespan(half);
 }
 
 void device_time(const GOp& op, Cand& c) {
@@ -254,7 +271,7 @@ void device_time(const GOp& op, Cand& c) {
             }
         }
     }
-    c.dev_us = DEV_LAUNCH_US + makespan(tiles);
+    c.dev_us = DEV_LAUNCH_US + (s.kind == JA_OP_CONTRACT ? contract_makespan(tiles) : makespan(tiles));
 }
 
 // A repartition in the device-time model: one launch copying the tensor once.

@@ -291,7 +291,8 @@ def test_planner_errors(B):
 
 def test_device_model_closed_forms():
     """The model's arithmetic on cases whose answer is known: 256 equal tiles
-    fill the 256 CUs once, one tile more takes a second round; a 4,096^3
+    fill the 256 CUs once, one tile more takes a second round (a contraction
+    runs a last round of at most 128 tiles as half-height tiles); a 4,096^3
     product as one block is 16 x 16 tiles of K = 4,096; a copy-bound
     operator is its bytes over the copy rate."""
     assert P.makespan([1.0] * 256) == 1.0 and P.makespan([1.0] * 257) == 2.0
@@ -305,13 +306,36 @@ def test_device_model_closed_forms():
     assert P.op_device_time(g.ops[0], {"i": 1, "j": 2, "k": 1}) == pytest.approx(P.LAUNCH_US + tile)
     # i cut in 8 x 512-row blocks: 2 x 16 tiles per block, 256 tiles in all, one round
     assert P.op_device_time(g.ops[0], {"i": 8, "j": 1, "k": 1}) == pytest.approx(P.LAUNCH_US + tile)
-    # i cut in 3: 1,366 / 1,365-row blocks give 6 x 16 tiles each (288 > 256): two rounds
-    assert P.op_device_time(g.ops[0], {"i": 3, "j": 1, "k": 1}) == pytest.approx(P.LAUNCH_US + 2 * tile)
+    # i cut in 3: 1,366 / 1,365-row blocks give 6 x 16 tiles each (288 > 256): one full round, then the other
+    # 32 tiles as 64 half-height tiles in a second launch
+    assert P.op_device_time(g.ops[0], {"i": 3, "j": 1, "k": 1}) == pytest.approx(
+        2 * P.LAUNCH_US + tile + P.HALF_TILE * tile)
+    # i cut in 25: 163 / 164-row blocks of 1 x 16 tiles, 400 in all: the last round (144) would fill more than
+    # half the CUs, so it runs at full height: two rounds
+    assert P.op_device_time(g.ops[0], {"i": 25, "j": 1, "k": 1}) == pytest.approx(P.LAUNCH_US + 2 * tile)
+    assert P.contract_makespan([1.0] * 512) == 2.0  # whole rounds: no second launch
     g2 = P.Graph()
     x, y = g2.input((1024, 4096)), g2.input((1024, 4096))
     g2.op("rd,rd->rd", "add", [x, y])
     assert P.op_device_time(g2.ops[0], {"r": 2, "d": 4}) == pytest.approx(
         P.LAUNCH_US + 6.0 * 1024 * 4096 / P.COPY_BPS * 1e6)
+
+
+def test_device_model_tail_matches_oracle(B):
+    """Library and oracle agree where a contraction's last round runs as
+    half-height tiles (288 tiles), where it does not (400), and on whole
+    rounds (256)."""
+    inputs = [(4096, 4096), (4096, 4096)]
+    ops = [("ij,jk->ik", "contract", "", [0, 1])]
+    og = _oracle_graph(inputs, ops)
+    g, letters = _lib_graph(B, inputs, ops)
+    try:
+        for i in (3, 25, 8):
+            sp = {"i": i, "j": 1, "k": 1}
+            iv = [[sp[c] for c in letters[0]]]
+            assert B.ja_graph_device_time(g, iv) == pytest.approx(P.plan_device_time(og, [sp]), rel=1e-9)
+    finally:
+        B.ja_graph_destroy(g)
 
 
 @pytest.mark.parametrize("dims,p", CHAINS[:3])
