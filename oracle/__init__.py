@@ -23,7 +23,8 @@ Einsummable", paperpeel full text):
   and the repartition itself -- ``overlay_atoms``, ``repartition``;
 * attention as a blocked join-agg with the online-softmax aggregation
   (m, l, acc) -- ``attention_online_blocked`` (the aggregation operator need
-  not be addition, section 5.2); both attention forms take fewer key-value
+  not be addition, section 5.2), its per-tuple triples before aggregation
+  and their fold -- ``attention_triples``, ``softmax_fold``; both attention forms take fewer key-value
   heads than query heads (grouped-query attention, section 3.3: query heads
   g*R .. g*R+R-1 share key-value head g), and ``attention`` /
   ``tuple_records`` take sequences packed end to end along the sequence index
@@ -588,6 +589,79 @@ def attention_online_blocked(Q, K, V, s_splits, t_splits, scale: float, causal: 
                     m = mn
                 out[b, h, s0:s1] = acc / l[:, None]
     return out
+
+
+def attention_triples(Q, K, V, s_splits, t_splits, scale: float, causal: bool,
+                      seq_ends: Optional[Sequence[int]] = None):
+    """The per-tuple results of attention as a join-agg, before aggregation
+    (section 3.2, Definition 3.7, step 1 -- f applied to every joined tuple):
+    for every kept (b, h, s-block, t-block) tuple and each query row of the
+    s-block, the triple over the keys of the t-block that the row may see
+        m   = max of scale * q . k,
+        l   = sum of exp(scale * q . k - m),
+        acc = sum of exp(scale * q . k - m) * v
+    (a row that sees none of the block's keys gets the identity (-inf, 0, 0)).
+    Q [B,H,S,D], K/V [B,HK,T,D]; query head h reads key-value head
+    h // (H // HK).  A tuple is kept unless causal drops it (its key block
+    starts at or after the end of its query block) or, with seq_ends, its two
+    blocks share no sequence.  Returns a list of ((b, h, si, ti), m, l, acc)
+    in tuple order: grouped by (b, h, si), ti ascending."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    Bn, H, S, D = Q.shape
+    rep = H // K.shape[1]
+    ends = list(seq_ends) if seq_ends is not None else None
+    starts = [0] + ends[:-1] if ends else None
+
+    def seq_id(pos):
+        return np.searchsorted(np.asarray(ends), pos, side="right")
+
+    out = []
+    for b in range(Bn):
+        for h in range(H):
+            kh = h // rep
+            for si in range(len(s_splits) - 1):
+                s0, s1 = s_splits[si], s_splits[si + 1]
+                for ti in range(len(t_splits) - 1):
+                    t0, t1 = t_splits[ti], t_splits[ti + 1]
+                    if causal and t0 >= s1:
+                        continue
+                    if ends and not any(a < s1 and e > s0 and a < t1 and e > t0 for a, e in zip(starts, ends)):
+                        continue
+                    sc = scale * (Q[b, h, s0:s1] @ K[b, kh, t0:t1].T)
+                    qs = np.arange(s0, s1)[:, None]
+                    ks = np.arange(t0, t1)[None, :]
+                    vis = np.ones(sc.shape, dtype=bool)
+                    if causal:
+                        vis &= ks <= qs
+                    if ends:
+                        vis &= seq_id(ks) == seq_id(qs)
+                    sc = np.where(vis, sc, -np.inf)
+                    m = sc.max(axis=1)
+                    mref = np.where(np.isfinite(m), m, 0.0)
+                    p = np.where(vis, np.exp(sc - mref[:, None]), 0.0)
+                    out.append(((b, h, si, ti), m, p.sum(axis=1), p @ V[b, kh, t0:t1]))
+    return out
+
+
+def softmax_fold(triples):
+    """The aggregation of attention's per-tuple triples (section 5.2: the
+    aggregation operator need not be addition): fold (m, l, acc) pairs with
+        m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m),
+        acc = acc1 e^(m1-m) + acc2 e^(m2-m),
+    starting from the identity (-inf, 0, 0), in the order given.  Returns the
+    folded (m, l, acc)."""
+    m, l, acc = None, None, None
+    for m2, l2, acc2 in triples:
+        if m is None:
+            m, l, acc = np.full_like(m2, -np.inf), np.zeros_like(l2), np.zeros_like(acc2)
+        mn = np.maximum(m, m2)
+        mref = np.where(np.isfinite(mn), mn, 0.0)
+        a1 = np.where(np.isfinite(m), np.exp(m - mref), 0.0)
+        a2 = np.where(np.isfinite(m2), np.exp(m2 - mref), 0.0)
+        l = l * a1 + l2 * a2
+        acc = acc * a1[:, None] + acc2 * a2[:, None]
+        m = mn
+    return m, l, acc
 
 
 # --------------------------------------------------------------------------

@@ -344,6 +344,65 @@ def test_attention_online_blocked_equals_two_pass(orc):
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
 
 
+def test_attention_triples_pins(orc):
+    """Per-tuple triples (the join's output before aggregation) pinned three
+    ways: (1) each tuple's log-sum-exp m + ln l and normalised values acc / l
+    equal scipy's logsumexp and a softmax over that tuple's visible scores
+    (library routines, not this code); (2) their fold with the softmax
+    aggregation, in any order, gives textbook two-pass attention; (3) the
+    tuple list is the one the join keeps (causal drop, packed sequences)."""
+    from scipy.special import logsumexp, softmax
+
+    rng = np.random.default_rng(21)
+    S, D = 20, 4
+    Q = rng.standard_normal((1, 4, S, D))
+    K, V = (rng.standard_normal((1, 2, S, D)) for _ in range(2))  # two query heads per key-value head
+    s_sp, t_sp = [0, 6, 13, 20], [0, 4, 9, 16, 20]
+    for causal, ends in ((True, None), (False, None), (True, [7, 15, 20]), (False, [7, 15, 20])):
+        tri = orc.attention_triples(Q, K, V, s_sp, t_sp, 0.7, causal, ends)
+        keys = [k for k, *_ in tri]
+        recs, _ = orc.tuple_records("bhst", {"b": [0, 1], "h": [0, 1, 2, 3, 4], "s": s_sp, "t": t_sp}, "bhs",
+                                    causal=("s", "t") if causal else None,
+                                    packed=("s", "t", ends) if ends else None)
+        assert keys == [tuple(int(x) for x in r) for r in recs]
+        seq = np.searchsorted(ends, np.arange(S), side="right") if ends else np.zeros(S, dtype=int)
+        for (b, h, si, ti), m, l, acc in tri:
+            for r, s_ in enumerate(range(s_sp[si], s_sp[si + 1])):
+                ks = [t for t in range(t_sp[ti], t_sp[ti + 1]) if (not causal or t <= s_) and seq[t] == seq[s_]]
+                if not ks:
+                    assert m[r] == -np.inf and l[r] == 0 and not acc[r].any()
+                    continue
+                sc = 0.7 * K[b, h // 2, ks] @ Q[b, h, s_]
+                assert abs(m[r] + np.log(l[r]) - logsumexp(sc)) < 1e-12
+                np.testing.assert_allclose(acc[r] / l[r], softmax(sc) @ V[b, h // 2, ks], rtol=1e-12, atol=1e-13)
+        ref = orc.attention(Q, K, V, 0.7, causal, ends)
+        for order in (lambda x: x, lambda x: x[::-1], lambda x: x[1::2] + x[0::2]):
+            out = np.zeros_like(Q)
+            for b, h, si in {k[:3] for k in keys}:
+                group = order([(m, l, a) for k, m, l, a in tri if k[:3] == (b, h, si)])
+                m, l, acc = orc.softmax_fold(group)
+                out[b, h, s_sp[si]:s_sp[si + 1]] = acc / l[:, None]
+            np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_softmax_fold_identity_and_shift(orc):
+    """The identity (-inf, 0, 0) leaves a triple unchanged, and a triple is
+    the same element of the monoid under a change of reference maximum:
+    (m, l, acc) ~ (m', l e^(m - m'), acc e^(m - m'))."""
+    m, l, acc = np.array([0.5, -np.inf]), np.array([2.0, 0.0]), np.array([[1.0, -2.0], [0.0, 0.0]])
+    ident = (np.full(2, -np.inf), np.zeros(2), np.zeros((2, 2)))
+    for seq in ([(m, l, acc), ident], [ident, (m, l, acc)]):
+        fm, fl, fa = orc.softmax_fold(seq)
+        np.testing.assert_array_equal(fm, m)
+        np.testing.assert_array_equal(fl, l)
+        np.testing.assert_array_equal(fa, acc)
+    other = (np.array([1.0, 3.0]), np.array([1.5, 4.0]), np.array([[0.25, 0.5], [1.0, 2.0]]))
+    fm, fl, fa = orc.softmax_fold([(m, l, acc), other])
+    fm2, fl2, fa2 = orc.softmax_fold([(m - 3.0, l * np.exp(3.0), acc * np.exp(3.0)), other])
+    np.testing.assert_allclose(fa / fl[:, None], fa2 / fl2[:, None], rtol=1e-14)
+    np.testing.assert_allclose(fm + np.log(fl), fm2 + np.log(fl2), rtol=1e-14)
+
+
 # ---------------------------------------------------------------- rmsnorm / swiglu / add
 
 def test_rmsnorm_hand_values(orc):
