@@ -404,7 +404,11 @@ ja_status ja_graph_device_time(const ja_graph* graph, const int32_t* const* inte
  * f16 x f16 -> f16 / f32, accumulating in f32; attention, rmsnorm, swiglu,
  * add: every relation bf16, or every relation f16 -- JA_ERR_DTYPE
  * otherwise), run the join, and build the device tables.  16-bit outputs are
- * rounded to nearest even once from f32. */
+ * rounded to nearest even once from f32.  A 16-bit contraction needs block
+ * extents along every contiguous axis that are multiples of 8 and operand
+ * matrices (one batch entry of an operand block) of fewer than 2^30 elements,
+ * which its kernel addresses with 32-bit byte offsets (JA_ERR_UNSUPPORTED
+ * otherwise). */
 ja_status ja_plan_create(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
                          int32_t n_in, const ja_relation_desc* out, ja_plan** plan);
 /* table_bytes: device buffer size for ja_plan_upload; workspace_bytes: the

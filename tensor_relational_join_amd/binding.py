@@ -181,7 +181,10 @@ class Relation:
 
     @property
     def nbytes(self) -> int:
-        return ja_relation_bytes(self)
+        # a relation is immutable once described: ask the library once
+        if getattr(self, "_nbytes", None) is None:
+            self._nbytes = ja_relation_bytes(self)
+        return self._nbytes
 
 
 def _desc_array(rels):

@@ -11,19 +11,17 @@
 // aggregated tile is written once.  So the SUM costs no extra memory traffic
 // and needs no atomics (eager aggregation pushed into the kernel).
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16 on CDNA4.  A workgroup of 8 wavefronts
-// owns a 256 x 256 output tile (128 x 64 per wavefront), which keeps the
-// operand traffic from L2 at 64 KiB per 8.4 MFLOP stage.  Operand tiles are
-// staged through LDS as [row][k] (k contiguous) so that every MFMA operand
-// fragment is one 16-byte LDS read; an operand whose k is not contiguous in
-// memory is transposed in registers on its way to LDS (4 x 8 sub-blocks).
-// LDS is double buffered (128 KiB of the 160 KiB per CU); the global loads of
-// stage i+1 are in flight while stage i multiplies.  The host lists the tiles
-// of a segment in groups of GEMM_GROUP_M row tiles, and xcd_remap hands each
-// XCD a contiguous run of that list, so the tiles resident on one XCD share A
-// and B panels in its L2.  The direct-to-LDS kernel below is persistent: one
-// workgroup per compute unit walks its XCD's run, loading the next tile's
-// first stage while the current tile's results are stored.
+// bf16 / f16 path: v_mfma_f32_16x16x32_{bf16,f16} on CDNA4.  A workgroup of 8
+// wavefronts owns a 256 x 256 output tile (128 x 64 per wavefront).  Operand
+// tiles travel from global memory straight into LDS (buffer_load ... lds) in
+// 32-wide stages, four stages in flight (128 KiB of the 160 KiB of LDS per
+// CU).  The host lists the tiles of a segment in groups of GEMM_GROUP_M row
+// tiles, and xcd_remap hands each XCD a contiguous run of that list, so the
+// tiles resident on one XCD share A and B panels in its L2.  The kernel is
+// persistent: one workgroup per compute unit walks its XCD's run, loading
+// the next tile's first stage while the current tile's results are stored.
+// Operand matrices are addressed with 32-bit buffer offsets, so the planner
+// refuses an operand matrix of 2^30 elements or more.
 #include <atomic>
 #include <type_traits>
 
@@ -92,219 +90,6 @@ __device__ __forceinline__ void store_out4(void* __restrict__ C, const uint16_t*
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (col + r < N) c[off + r] = a[r];
-        }
-    }
-}
-
-// ---------------------------------------------------------------- bf16 MFMA
-// LDS operand tiles are [rows][BK] bf16 with no padding.  The 16-byte chunk c
-// (8 consecutive k) of row r sits at chunk position c ^ swz(r), with
-// swz(r) = (r ^ (r >> 3)) mod (BK / 8).  Both access patterns are then free
-// of bank conflicts: an MFMA fragment read (16 consecutive rows, one logical
-// chunk) touches 8 distinct chunk positions in every group of 8 rows, and the
-// transposing writes (rows 8 apart, one logical chunk) spread over all of
-// them as well.
-template <int BK>
-__device__ __forceinline__ int lds_chunk(int r, int c) {
-    return r * BK + ((c ^ ((r ^ (r >> 3)) & (BK / 8 - 1))) << 3);
-}
-
-// Operand whose k is contiguous in memory: element (r, k) at p[r*ld + k].
-// Each thread moves VPT 16-byte chunks; 8 consecutive lanes cover one row.
-template <int R, int BK, int NT>
-struct DirectStage {
-    static constexpr int CPR = BK / 8;
-    static constexpr int VPT = R * CPR / NT;
-    static_assert(R * CPR % NT == 0, "staging must divide evenly");
-    uint4 v[VPT];
-
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ p, int64_t ld, int r0, int rext, int k0,
-                                         int kext, int tid) {
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int vi = tid + j * NT, r = vi / CPR, c = vi % CPR;
-            const int gr = r0 + r, gk = k0 + c * 8;
-            v[j] = make_uint4(0, 0, 0, 0);
-            if (gr < rext && gk < kext) v[j] = *reinterpret_cast<const uint4*>(p + (int64_t)gr * ld + gk);
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int vi = tid + j * NT;
-            *reinterpret_cast<uint4*>(lds + lds_chunk<BK>(vi / CPR, vi % CPR)) = v[j];
-        }
-    }
-};
-
-// Operand whose rows are contiguous in memory: element (r, k) at p[k*ld + r].
-// Each thread loads sub-blocks of 4 k x 8 rows (four 16-byte loads along the
-// rows, 32 lanes cover 256 consecutive rows) and transposes them in
-// registers into eight 8-byte runs of 4 consecutive k.
-template <int R, int BK, int NT>
-struct TransStage {
-    static constexpr int RG = R / 8;
-    static constexpr int SPT = (BK / 4) * RG / NT;
-    static_assert((BK / 4) * RG % NT == 0, "staging must divide evenly");
-    uint4 v[SPT * 4];
-
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ p, int64_t ld, int r0, int rext, int k0,
-                                         int kext, int tid) {
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int si = tid + j * NT, kg = si / RG, rg = si % RG;
-            const int gr = r0 + rg * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int gk = k0 + kg * 4 + i;
-                v[j * 4 + i] = make_uint4(0, 0, 0, 0);
-                if (gr < rext && gk < kext) v[j * 4 + i] = *reinterpret_cast<const uint4*>(p + (int64_t)gk * ld + gr);
-            }
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int si = tid + j * NT, kg = si / RG, rg = si % RG;
-            const uint32_t* q0 = reinterpret_cast<const uint32_t*>(&v[j * 4 + 0]);
-            const uint32_t* q1 = reinterpret_cast<const uint32_t*>(&v[j * 4 + 1]);
-            const uint32_t* q2 = reinterpret_cast<const uint32_t*>(&v[j * 4 + 2]);
-            const uint32_t* q3 = reinterpret_cast<const uint32_t*>(&v[j * 4 + 3]);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // rows 8rg + 2w (low halves) and 8rg + 2w + 1 (high halves), k = 4kg .. 4kg+3
-                uint2 lo, hi;
-                lo.x = (q0[w] & 0xffffu) | (q1[w] << 16);
-                lo.y = (q2[w] & 0xffffu) | (q3[w] << 16);
-                hi.x = (q0[w] >> 16) | (q1[w] & 0xffff0000u);
-                hi.y = (q2[w] >> 16) | (q3[w] & 0xffff0000u);
-                const int r = rg * 8 + 2 * w;
-                *reinterpret_cast<uint2*>(lds + lds_chunk<BK>(r, kg >> 1) + (kg & 1) * 4) = lo;
-                *reinterpret_cast<uint2*>(lds + lds_chunk<BK>(r + 1, kg >> 1) + (kg & 1) * 4) = hi;
-            }
-        }
-    }
-};
-
-template <int R, int BK, int NT, bool TRANS>
-using Stage = typename std::conditional<TRANS, TransStage<R, BK, NT>, DirectStage<R, BK, NT>>::type;
-
-// One workgroup = one BM x BN output tile of one segment; WM x WN waves, each
-// owning a (BM/WM) x (BN/WN) sub-tile of 16x16 fragments.  The MFMA is issued
-// with the B fragment as its first operand, so each accumulator holds C^T:
-// lane l owns C[m = l % 16][n = 4 (l / 16) .. +3], four adjacent columns that
-// leave in one store.
-template <int BM, int BN, int BK, int WM, int WN, int AL, int BL, bool IN_F16, bool OUT16>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(const GemmTile* __restrict__ tiles, int ntiles,
-                                                                const GemmSeg* __restrict__ segs,
-                                                                const GemmTuple* __restrict__ tuples,
-                                                                const uint16_t* __restrict__ A,
-                                                                const uint16_t* __restrict__ B, void* __restrict__ C,
-                                                                const uint16_t* __restrict__ R, int epi) {
-    constexpr int NT = WM * WN * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 16, FN = WTN / 16;
-    using SA = Stage<BM, BK, NT, AL == JA_A_KM>;
-    using SB = Stage<BN, BK, NT, BL == JA_B_KN>;
-    extern __shared__ __attribute__((aligned(16))) uint16_t gemm_lds[];
-    // [A buffer 0][A buffer 1][B buffer 0][B buffer 1]
-    auto As = [&](int b) { return gemm_lds + b * (BM * BK); };
-    auto Bs = [&](int b) { return gemm_lds + 2 * BM * BK + b * (BN * BK); };
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const GemmTile tl = tiles[xcd_remap(blockIdx.x, ntiles)];
-    const GemmSeg sg = segs[tl.seg];
-    const int m0 = tl.m0, n0 = tl.n0;
-
-    f32x4_t acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    SA sa;
-    SB sb;
-    // stage cursor: tuple t, contracted offset k0 inside it
-    int t = sg.t_begin, k0 = 0;
-    auto load_stage = [&](int tt, int kk) {
-        const GemmTuple tp = tuples[tt];
-        const uint16_t* pa = A + tp.a_off + (int64_t)tl.batch * tp.a_bstride;
-        const uint16_t* pb = B + tp.b_off + (int64_t)tl.batch * tp.b_bstride;
-        sa.load(pa, tp.lda, m0, sg.M, kk, tp.K, tid);
-        sb.load(pb, tp.ldb, n0, sg.N, kk, tp.K, tid);
-    };
-    auto advance = [&]() {
-        k0 += BK;
-        if (k0 >= tuples[t].K) {
-            k0 = 0;
-            ++t;
-        }
-    };
-    if (t >= sg.t_end) return;  // a segment always has tuples; guard anyway
-    load_stage(t, k0);
-    sa.store(As(0), tid);
-    sb.store(Bs(0), tid);
-    advance();
-    __syncthreads();
-    int buf = 0;
-    const int arow = wm * WTM + (lane & 15), brow = wn * WTN + (lane & 15);
-    const int kc = lane >> 4;  // this lane's 8-k chunk inside a 32-k step
-    while (true) {
-        const bool more = t < sg.t_end;
-        if (more) load_stage(t, k0);
-        const uint16_t* as = As(buf);
-        const uint16_t* bs = Bs(buf);
-#pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(as + lds_chunk<BK>(arow + i * 16, ks / 8 + kc));
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t*>(bs + lds_chunk<BK>(brow + j * 16, ks / 8 + kc));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma16x16x32<IN_F16>(bfr[j], af[i], acc[i][j]);
-        }
-        if (!more) break;
-        sa.store(As(buf ^ 1), tid);
-        sb.store(Bs(buf ^ 1), tid);
-        advance();
-        __syncthreads();
-        buf ^= 1;
-    }
-
-    // epilogue: lane owns C[row][col .. col+3] of every fragment
-    const int64_t cbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
-    // two rows of fragments at a time: their residual loads are all in
-    // flight before the first of their stores
-#pragma unroll
-    for (int i0 = 0; i0 < FM; i0 += 2) {
-        uint2 res[2][FN];
-#pragma unroll
-        for (int i = i0; i < i0 + 2; ++i) {
-            const int row = m0 + wm * WTM + i * 16 + (lane & 15);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + wn * WTN + j * 16 + 4 * kc;
-                res[i - i0][j] = row < sg.M ? residual4(R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N)
-                                            : make_uint2(0u, 0u);
-            }
-        }
-#pragma unroll
-        for (int i = i0; i < i0 + 2; ++i) {
-            const int row = m0 + wm * WTM + i * 16 + (lane & 15);
-            if (row >= sg.M) continue;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + wn * WTN + j * 16 + 4 * kc;
-                store_out4<IN_F16, OUT16>(C, R, epi, cbase + (int64_t)row * sg.ldc + col, col, sg.N, acc[i][j],
-                                          res[i - i0][j]);
-            }
         }
     }
 }
@@ -706,16 +491,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmTile* __restric
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int AL, int BL, bool F16, bool OUT16>
-static void launch_bf16(const GemmTile* tiles, int ntiles, const GemmSeg* segs, const GemmTuple* tuples, const void* A,
-                        const void* B, void* C, const void* R, int epi, hipStream_t s) {
-    constexpr int BM = GEMM_BF16_TM, BN = GEMM_BF16_TN, BK = GEMM_BF16_TK, WM = 2, WN = 4;
-    constexpr unsigned lds = 2u * (BM + BN) * BK * sizeof(uint16_t);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, AL, BL, F16, OUT16>), dim3(ntiles), dim3(WM * WN * 64),
-                       lds, s, tiles, ntiles, segs, tuples, (const uint16_t*)A, (const uint16_t*)B, C,
-                       (const uint16_t*)R, epi);
-}
-
 // Compute units of the current device (one persistent contraction workgroup
 // each); cached per device.
 static int device_cus() {
@@ -758,39 +533,32 @@ static void launch_bf16_dma(const GemmTile* tiles, int ntiles, const GemmSeg* se
 // 16-bit inputs (bf16 or, with F16, IEEE half) into fp32 accumulators;
 // out16 writes the output in the input's format, otherwise fp32.
 template <int AL, int BL, bool F16>
-static void launch_bf16_out(int out16, int dma, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
+static void launch_bf16_out(int out16, const GemmTile* tiles, int ntiles, const GemmSeg* segs,
                             const GemmTuple* tuples, const void* A, const void* B, void* C, const void* R, int epi,
                             hipStream_t s) {
-    if (dma) {
-        if (out16)
-            launch_bf16_dma<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
-        else
-            launch_bf16_dma<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
-    } else {
-        if (out16)
-            launch_bf16<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
-        else
-            launch_bf16<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
-    }
+    if (out16)
+        launch_bf16_dma<AL, BL, F16, true>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
+    else
+        launch_bf16_dma<AL, BL, F16, false>(tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
 }
 
 template <bool F16>
-static void launch_h16(int a_layout, int b_layout, int out16, int dma, const GemmTile* tiles, int ntiles,
+static void launch_h16(int a_layout, int b_layout, int out16, const GemmTile* tiles, int ntiles,
                        const GemmSeg* segs, const GemmTuple* tuples, const void* A, const void* B, void* C,
                        const void* R, int epi, hipStream_t s) {
     if (a_layout == JA_A_MK && b_layout == JA_B_KN)
-        launch_bf16_out<JA_A_MK, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
+        launch_bf16_out<JA_A_MK, JA_B_KN, F16>(out16, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     else if (a_layout == JA_A_MK && b_layout == JA_B_NK)
-        launch_bf16_out<JA_A_MK, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
+        launch_bf16_out<JA_A_MK, JA_B_NK, F16>(out16, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     else if (a_layout == JA_A_KM && b_layout == JA_B_KN)
-        launch_bf16_out<JA_A_KM, JA_B_KN, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
+        launch_bf16_out<JA_A_KM, JA_B_KN, F16>(out16, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     else
-        launch_bf16_out<JA_A_KM, JA_B_NK, F16>(out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
+        launch_bf16_out<JA_A_KM, JA_B_NK, F16>(out16, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
 }
 
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
                        const void* A, const void* B, void* C, const void* R, int32_t epi, int32_t in_dtype,
-                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, int32_t dma, hipStream_t s) {
+                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, hipStream_t s) {
     const uint8_t* t = (const uint8_t*)table;
     const GemmTile* tiles = (const GemmTile*)(t + tiles_off);
     const GemmSeg* segs = (const GemmSeg*)(t + segs_off);
@@ -798,9 +566,9 @@ hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int
     if (in_dtype == JA_BF16 || in_dtype == JA_F16) {
         const int out16 = out_dtype != JA_F32;
         if (in_dtype == JA_F16)
-            launch_h16<true>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
+            launch_h16<true>(a_layout, b_layout, out16, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
         else
-            launch_h16<false>(a_layout, b_layout, out16, dma, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
+            launch_h16<false>(a_layout, b_layout, out16, tiles, ntiles, segs, tuples, A, B, C, R, epi, s);
     } else {
 #define JA_F32_CASE(al, bl)                                                                                       \
     hipLaunchKernelGGL((gemm_f32_kernel<al, bl>), dim3(ntiles), dim3(256), 0, s, tiles, ntiles, segs, tuples,     \

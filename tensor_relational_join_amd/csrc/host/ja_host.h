@@ -96,7 +96,7 @@ ja_status build_tuples(const ja_spec* spec, const ja_decomp* d, ja_tuples& t);
 namespace ja {
 hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t tuples_off,
                        const void* A, const void* B, void* C, const void* R, int32_t epi, int32_t in_dtype,
-                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, int32_t dma, hipStream_t stream);
+                       int32_t out_dtype, int32_t a_layout, int32_t b_layout, hipStream_t stream);
 // seq_off / nseq: the packed sequences' int32 end positions in the table (nseq = 0: not packed)
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
                             int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,

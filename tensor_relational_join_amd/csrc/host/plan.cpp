@@ -258,7 +258,7 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
             if (p->ntiles == 0) return JA_OK;
             JA_TRY_HIP(launch_gemm(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
                                    out_ptr, p->epilogue == JA_EPI_ADD ? in_ptrs[2] : nullptr, p->epilogue,
-                                   p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, p->gemm_dma, hs));
+                                   p->in_dtype, p->out_dtype, p->a_layout, p->b_layout, hs));
             break;
         case JA_OP_ATTENTION:
             if (p->ntiles == 0) return JA_OK;
@@ -294,7 +294,7 @@ ja_status ja_kernel(const ja_plan* p, const void* const* in_ptrs, void* partials
     if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
     if (p->nutiles == 0) return JA_OK;
     JA_TRY_HIP(launch_gemm(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
-                           partials, nullptr, JA_EPI_NONE, p->in_dtype, JA_F32, p->a_layout, p->b_layout, p->gemm_dma,
+                           partials, nullptr, JA_EPI_NONE, p->in_dtype, JA_F32, p->a_layout, p->b_layout,
                            (hipStream_t)stream));
     return JA_OK;
 }

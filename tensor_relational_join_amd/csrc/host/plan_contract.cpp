@@ -179,10 +179,10 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         for (const GemmSeg& g : segs)
             if ((!a_m_first && g.M % 8) || (b_k_first && g.N % 8))
                 return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction needs block extents that are multiples of 8");
-        // the direct-to-LDS kernel addresses each operand matrix with 32-bit byte offsets
-        bool dma = true;
-        for (const GemmTuple& g : tuples) dma = dma && g.a_bstride * 2 < lim && g.b_bstride * 2 < lim;
-        p->gemm_dma = dma ? 1 : 0;
+        // the MFMA kernel addresses each operand matrix with 32-bit buffer byte offsets
+        for (const GemmTuple& g : tuples)
+            if (g.a_bstride >= ((int64_t)1 << 30) || g.b_bstride >= ((int64_t)1 << 30))
+                return fail(JA_ERR_UNSUPPORTED, "a 16-bit contraction operand matrix must hold fewer than 2^30 elements");
     }
     p->partial_elems = part;
     p->tiles_off = put(p->table, tiles);

@@ -19,7 +19,6 @@ struct ja_plan {
     int64_t atiles_off = 0, asegs_off = 0, apoff_off = 0;
     int32_t natiles = 0;
     int32_t in_dtype = 0, out_dtype = 0, a_layout = 0, b_layout = 0;
-    int32_t gemm_dma = 0;  // bf16 operands reachable through 32-bit buffer offsets
     int32_t epilogue = 0;  // JA_EPI_*: the 1:1 join applied to the aggregated tile on its way out
     int64_t partial_elems = 0;
     // attention

@@ -1,13 +1,15 @@
 // repart.cpp -- re-blocking a relation between two decompositions.
 //
-// Section 5.3 of "Every Kernel Is a Join" (paperpeel full text) forms, per
-// dimension, the union of the block boundaries of the producer's blocks and
-// the consumer's blocks; the cells of that overlay grid are atoms, and every
-// existing and every required block is a disjoint union of atoms.  Decompose
-// kernels slice producer blocks into atoms and recompose kernels concatenate
-// atoms into the consumer's contiguous blocks.  On one GPU there is no
-// exchange in between, so each atom is copied once, straight from its source
-// block to its destination block (decompose and recompose fused).
+// "Every Kernel Is a Join" (paperpeel full text), section 5.3: take every cut
+// position of the source blocking and every cut position of the target
+// blocking, dimension by dimension, and cut the tensor at all of them.  The
+// resulting grid cells ("atoms") are small enough that each source block and
+// each target block is made of whole atoms with no overlap.  Moving data
+// between the two blockings then means slicing source blocks into atoms,
+// shipping the atoms, and gluing them into target blocks.  On one GPU nothing
+// is shipped, so the slicing and the gluing collapse into a single copy of
+// every atom from its place in the source buffer to its place in the target
+// buffer.
 //
 // A repartition may also re-index the tensor (read as another shape, permute
 // axes, read as the destination's shape), e.g. token-major projections to

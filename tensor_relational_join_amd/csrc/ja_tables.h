@@ -115,7 +115,6 @@ namespace ja {
 // Tile shapes shared by the planner (which enumerates tiles) and the kernels.
 constexpr int GEMM_BF16_TM = 256;  // output rows per workgroup tile, bf16 MFMA kernel
 constexpr int GEMM_BF16_TN = 256;  // output columns per workgroup tile
-constexpr int GEMM_BF16_TK = 64;   // contracted elements per LDS stage
 constexpr int GEMM_GROUP_M = 4;    // row tiles per group in the tile order (L2 reuse)
 constexpr int GEMM_DMA_STAGES = 4; // 32-wide stages in flight in the direct-to-LDS kernel
 constexpr int GEMM_F32_TM = 64;    // fp32 kernel tile

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 from typing import Dict, Optional, Sequence
 
+import numpy as np
 import torch
 
 from . import binding as B
@@ -29,6 +30,45 @@ def alloc(rel: Relation, device="cuda") -> torch.Tensor:
     256-byte aligned)."""
     n = rel.nbytes // B.DTYPE_SIZE[rel.dtype]
     return torch.empty(n, dtype=TORCH_DTYPE[rel.dtype], device=device)
+
+
+def _check_layout(t, nbytes: int, dtype: Optional[torch.dtype], what: str):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s: expected a torch tensor, got %s" % (what, type(t).__name__))
+    if not t.is_contiguous():
+        raise ValueError("%s: the tensor must be contiguous" % what)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s: dtype %s, expected %s" % (what, t.dtype, dtype))
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError("%s: %d bytes, the relation needs %d" % (what, have, nbytes))
+
+
+def check_buffers(bufs):
+    """Device addresses of the (tensor, nbytes, dtype, name) entries of
+    `bufs` after checking that a kernel may read or write `nbytes` bytes of
+    elements of `dtype` (None: any) in each: a contiguous tensor of that
+    dtype, at least that large, on a GPU.  The library checks only pointer
+    alignment, so a short or mistyped buffer would otherwise be read or
+    written out of bounds on the device.  Every buffer's layout is checked
+    before any buffer's device.  Raises ValueError."""
+    for t, n, dt, what in bufs:
+        _check_layout(t, n, dt, what)
+    for t, _, _, what in bufs:
+        if not t.is_cuda:
+            raise ValueError("%s: the tensor must be on the GPU (device %s)" % (what, t.device))
+    return [t.data_ptr() for t, _, _, _ in bufs]
+
+
+def check_buffer(t, nbytes: int, dtype: Optional[torch.dtype], what: str) -> int:
+    """check_buffers for one buffer."""
+    return check_buffers([(t, nbytes, dtype, what)])[0]
+
+
+def _rel_bufs(ts: Sequence[torch.Tensor], rels: Sequence[Relation], what: str):
+    if len(ts) != len(rels):
+        raise ValueError("%s: %d tensors for %d relations" % (what, len(ts), len(rels)))
+    return [(t, r.nbytes, TORCH_DTYPE[r.dtype], "%s %d" % (what, i)) for i, (t, r) in enumerate(zip(ts, rels))]
 
 
 def _table(nbytes: int, device) -> torch.Tensor:
@@ -89,17 +129,26 @@ class Op:
             B.ja_tuples_destroy(t)
 
     def run(self, ins: Sequence[torch.Tensor], out: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+        ptrs = check_buffers(_rel_bufs(ins, self.in_rels, "input") +
+                             [(out, self.out_rel.nbytes, TORCH_DTYPE[self.out_rel.dtype], "output")])
         ws = self.workspace.data_ptr() if self.workspace is not None else 0
-        B.ja_plan_run(self.plan, [t.data_ptr() for t in ins], out.data_ptr(), ws, stream_handle(stream))
+        B.ja_plan_run(self.plan, ptrs[:-1], ptrs[-1], ws, stream_handle(stream))
+
+    def partial_bytes(self) -> int:
+        return B.ja_plan_partial_bytes(self.plan)
 
     def partial_buffer(self) -> torch.Tensor:
-        return torch.empty(B.ja_plan_partial_bytes(self.plan) // 4, dtype=torch.float32, device=self.table.device)
+        return torch.empty(self.partial_bytes() // 4, dtype=torch.float32, device=self.table.device)
 
     def kernel(self, ins: Sequence[torch.Tensor], partials: torch.Tensor, stream=None):
-        B.ja_kernel(self.plan, [t.data_ptr() for t in ins], partials.data_ptr(), stream_handle(stream))
+        ptrs = check_buffers(_rel_bufs(ins, self.in_rels, "input") +
+                             [(partials, self.partial_bytes(), torch.float32, "partials")])
+        B.ja_kernel(self.plan, ptrs[:-1], ptrs[-1], stream_handle(stream))
 
     def agg(self, partials: torch.Tensor, out: torch.Tensor, op: int = B.JA_AGG_SUM, stream=None):
-        B.ja_agg(self.plan, op, partials.data_ptr(), out.data_ptr(), stream_handle(stream))
+        pptr, optr = check_buffers([(partials, self.partial_bytes(), torch.float32, "partials"),
+                                    (out, self.out_rel.nbytes, TORCH_DTYPE[self.out_rel.dtype], "output")])
+        B.ja_agg(self.plan, op, pptr, optr, stream_handle(stream))
 
     def close(self):
         if self.plan:
@@ -135,7 +184,9 @@ class Repart:
             raise
 
     def run(self, src: torch.Tensor, dst: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
-        B.ja_repart_run(self.rp, src.data_ptr(), dst.data_ptr(), stream_handle(stream))
+        sptr, dptr = check_buffers([(src, self.src.nbytes, TORCH_DTYPE[self.src.dtype], "source"),
+                                    (dst, self.dst.nbytes, TORCH_DTYPE[self.dst.dtype], "destination")])
+        B.ja_repart_run(self.rp, sptr, dptr, stream_handle(stream))
 
     def close(self):
         if self.rp:
@@ -226,6 +277,12 @@ class DeviceAttention:
             self.letters = B.ja_spec_letters(self.spec)
             self.da = B.ja_dattn_create(self.spec, [extents[c] for c in self.letters],
                                         [counts[c] for c in self.letters], dtype)
+            # Q, K, V, O hold every element of their letters' extents (their
+            # blocks tile them whatever the sequence ends)
+            esize = B.DTYPE_SIZE[dtype]
+            self._tdtype = TORCH_DTYPE[dtype]
+            lhs, out = einsum.split("->")
+            self._nbytes = [esize * int(np.prod([extents[c] for c in x])) for x in lhs.split(",") + [out]]
             tb, wb, self.n_splits = B.ja_dattn_device_bytes(self.da)
             self.table = torch.empty(max(tb, 256), dtype=torch.uint8, device=device)
             B.ja_dattn_upload(self.da, self.table.data_ptr(), self.table.numel(), stream_handle(stream))
@@ -239,8 +296,9 @@ class DeviceAttention:
             stream: Optional[torch.cuda.Stream] = None):
         if splits.dtype != torch.int64 or not splits.is_cuda or splits.numel() != self.n_splits:
             raise ValueError("splits: a device int64 tensor of %d split points" % self.n_splits)
-        B.ja_dattn_run(self.da, splits.data_ptr(), Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
-                       self.counts.data_ptr(), self.workspace.data_ptr(), stream_handle(stream))
+        q, k, v, o = check_buffers([(t, n, self._tdtype, w) for t, n, w in zip((Q, K, V, O), self._nbytes, "QKVO")])
+        B.ja_dattn_run(self.da, splits.data_ptr(), q, k, v, o, self.counts.data_ptr(), self.workspace.data_ptr(),
+                       stream_handle(stream))
 
     def close(self):
         if self.da:

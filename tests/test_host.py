@@ -353,6 +353,31 @@ def test_bf16_alignment_is_refused_not_miscomputed(B):
         B.ja_spec_destroy(s)
 
 
+def test_operand_matrix_beyond_32bit_offsets_is_refused(B):
+    """The MFMA contraction addresses every operand matrix with 32-bit buffer
+    byte offsets: an operand block of 2^30 elements or more is refused at
+    plan time (no kernel would address it), one just below is accepted."""
+    from tensor_relational_join_amd.device import relation_for
+
+    s = B.ja_spec_create("ij,jk->ik", "contract")
+    try:
+        for k, code in ((1 << 22, "JA_ERR_UNSUPPORTED"), ((1 << 22) - 8, None)):
+            sp = {"i": [0, 256], "j": [0, k], "k": [0, 64]}
+            d = B.ja_decomp_create(s, [256, k, 64], [1, 1, 1], [sp["i"], sp["j"], sp["k"]])
+            try:
+                ins = [relation_for("ij", sp, B.JA_BF16), relation_for("jk", sp, B.JA_BF16)]
+                if code is None:
+                    B.ja_plan_destroy(B.ja_plan_create(s, d, ins, relation_for("ik", sp, B.JA_BF16)))
+                else:
+                    with pytest.raises(B.JaError) as e:
+                        B.ja_plan_create(s, d, ins, relation_for("ik", sp, B.JA_BF16))
+                    assert e.value.name == code and "2^30" in str(e.value)
+            finally:
+                B.ja_decomp_destroy(d)
+    finally:
+        B.ja_spec_destroy(s)
+
+
 def test_section_5_3_overlay_atom_count(B):
     g = json.load(open(os.path.join(GOLDEN, "section_5_3_overlay_atoms.json")))
     src = B.Relation(g["shape"], splits=[g["producer_row_splits"], g["col_splits"]], dtype=B.JA_BF16)
