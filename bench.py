@@ -268,24 +268,28 @@ def bench_kernel(args):
     from tensor_relational_join_amd.device import Op, alloc
 
     if args.workload == "copy":
-        # a plain device copy of known size: the HBM ceiling, and the
-        # calibration point of the FETCH_SIZE / WRITE_SIZE counters
-        n = 1 << 29  # 1 GiB of bf16
-        src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+        # the library's own streaming copy of 1 GiB: the calibration point of
+        # the FETCH_SIZE / WRITE_SIZE counters (bytes known exactly)
+        from tensor_relational_join_amd import binding as B
+
+        n = 1 << 30
+        src = torch.empty(n // 2, dtype=torch.int16, device="cuda").random_()
         dst = torch.empty_like(src)
+        stream = torch.cuda.current_stream().cuda_stream
         for _ in range(args.warmup):
-            dst.copy_(src)
+            B.ja_calibrate_copy(src.data_ptr(), dst.data_ptr(), n, stream)
         torch.cuda.synchronize()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record()
         for _ in range(args.steps):
-            dst.copy_(src)
+            B.ja_calibrate_copy(src.data_ptr(), dst.data_ptr(), n, stream)
         s1.record()
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / args.steps
-        gbs = 2.0 * n * 2 / (ms / 1e3) / 1e9
-        return {"workload": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "steps": args.steps,
-                "ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
+        gbs = 2.0 * n / (ms / 1e3) / 1e9
+        return {"workload": "copy", "kernel": "ja::copy_kernel", "bytes_read": n, "bytes_written": n,
+                "steps": args.steps, "ms": round(ms, 4), "gbs": round(gbs, 1),
+                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
     runs = []  # (name, launch, flops, bytes, ops to close)
     want = ["tiny", "ffn", "ffn_unfused", "attention", "rmsnorm", "swiglu"] if args.workload == "configs" else \
         {"ffn": ["ffn"], "attention": ["attention"], "norm_swiglu": ["rmsnorm", "swiglu"],
@@ -443,20 +447,45 @@ def _cpu_configs():
     return {k: {"ms": round(v, 2), "cores": threads, "kind": "oracle"} for k, v in out.items()}
 
 
-def bench_ceilings(args):
-    """The two ceilings the kernels are compared against beside the published
-    peaks: a plain 1 GiB device copy (HBM) and a loop of nothing but bf16
-    MFMAs (matrix cores, no memory traffic), each timed per launch."""
+def _copy_ceiling(nbytes_moved, steps, cold=True):
+    """The library's own streaming copy (ja_calibrate_copy) moving
+    `nbytes_moved` bytes per launch (half read, half written), timed per
+    launch on the current stream; cold: each launch after a 512 MiB read that
+    evicts the 256 MB Infinity Cache."""
     import torch
 
     from tensor_relational_join_amd import binding as B
 
-    n = 1 << 29
-    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    n = nbytes_moved // 2 // 16 * 16
+    src = torch.empty(n // 2, dtype=torch.int16, device="cuda").random_()
     dst = torch.empty_like(src)
-    for _ in range(args.warmup):
-        dst.copy_(src)
-    copy = _stats(_timed(lambda: dst.copy_(src), args.steps))
+    stream = torch.cuda.current_stream().cuda_stream
+    launch = lambda: B.ja_calibrate_copy(src.data_ptr(), dst.data_ptr(), n, stream)  # noqa: E731
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    scratch = torch.ones(1 << 28, dtype=torch.int16, device="cuda") if cold else None
+    st = _stats(_timed(launch, steps, flush=(lambda: scratch.max()) if cold else None))
+    gbs = 2 * n / (st["median"] / 1e3) / 1e9
+    return {"bytes_moved": 2 * n, "ms": st, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
+
+
+def bench_ceilings(args):
+    """The two ceilings the kernels are compared against beside the published
+    peaks: the library's own streaming copy (HBM; at 2 GiB moved and at the
+    byte counts of the RMSNorm and SwiGLU configs, cold and warm) and a loop
+    of nothing but bf16 MFMAs (matrix cores, no memory traffic), each timed
+    per launch."""
+    import torch
+
+    from tensor_relational_join_amd import binding as B
+
+    copies = {}
+    for name, nb in (("2GiB", 1 << 31), ("rmsnorm_bytes", 2 * (2 * 8192 * 4096 + 4096)),
+                     ("swiglu_bytes", 2 * 3 * 8192 * 11008)):
+        copies[name + "_cold"] = _copy_ceiling(nb, max(args.steps, 30), cold=True)
+        copies[name + "_warm"] = _copy_ceiling(nb, max(args.steps, 30), cold=False)
     wgs, iters = 256 * 8, 4096
     sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -466,11 +495,41 @@ def bench_ceilings(args):
     mf = _stats(_timed(lambda: B.ja_calibrate_mfma(wgs, iters, sink.data_ptr(), stream), args.steps))
     mfma_tflops = fl / (mf["median"] / 1e3) / 1e12
     return {"workload": "ceilings", "steps": args.steps, "warmup": args.warmup, "device": _device_snapshot(),
-            "copy": {"bytes_moved": 4 * n, "ms": copy, "gbs": round(4 * n / (copy["median"] / 1e3) / 1e9, 1),
-                     "frac_hbm_peak": round(4 * n / (copy["median"] / 1e3) / 1e9 / PEAK_HBM_GBS, 3)},
+            "copy": copies,
             "mfma_loop": {"flops": fl, "ms": mf, "tflops": round(mfma_tflops, 1),
                           "frac_mfma_peak": round(mfma_tflops / PEAK_BF16_TFLOPS, 3),
                           "implied_clock_ghz": round(mfma_tflops / PEAK_BF16_TFLOPS * 2.4, 3)}}
+
+
+def configs_summary(args):
+    """The single-operator configurations measured in the default run, one
+    compact entry each: back-to-back, warm-median and cold-median ms, the rate
+    (TFLOP/s for the contractions and attention, GB/s for the memory-bound
+    operators) of the cold median and its fraction of the published peak, and
+    the float64 oracle's time on the host cores beside it."""
+    cfg = argparse.Namespace(workload="configs", steps=20, warmup=3, no_cpu_baseline=args.no_cpu_baseline)
+    res = bench_kernel(cfg)["results"]
+    names = {"tiny_fp32_2x2x2": "cfg1 ij,jk->ik 64^3 fp32 2x2x2",
+             "ffn_contract": "cfg2 bd,df->bf 2048x4096x11008 bf16 2x4x4",
+             "ffn_unfused_kernel_then_agg": "cfg2 unfused (ja_kernel fp32 partials, then ja_agg SUM)",
+             "attention": "cfg3 causal attention [4,32,2048,128] bf16, 128-blocks",
+             "rmsnorm": "cfg4a RMSNorm [8192,4096] bf16, d by 8",
+             "swiglu": "cfg4b SwiGLU [8192,11008] bf16, f by 8"}
+    out = {}
+    for k, d in res.items():
+        e = {"what": names.get(k, k), "ms": d["ms"], "warm_median_ms": d["warm"]["median"],
+             "cold_median_ms": d["cold"]["median"]}
+        if "cold_tflops" in d and k != "tiny_fp32_2x2x2":
+            e["cold_tflops"] = d["cold_tflops"]
+            e["cold_frac_mfma_peak"] = round(d["cold_tflops"] / PEAK_BF16_TFLOPS, 3)
+        elif "cold_gbs" in d and k != "tiny_fp32_2x2x2":
+            e["cold_gbs"] = d["cold_gbs"]
+            e["cold_frac_hbm_peak"] = round(d["cold_gbs"] / PEAK_HBM_GBS, 3)
+        if "cpu_oracle" in d:
+            e["cpu_oracle_ms"] = d["cpu_oracle"]["ms"]
+            e["cpu_oracle_cores"] = d["cpu_oracle"]["cores"]
+        out[k] = e
+    return out
 
 
 def bench_join(args):
@@ -746,6 +805,10 @@ def main():
         return
     out, inp = bench_block(args)
     out["device"] = _device_snapshot()
+    if args.workload == "block":
+        # the single-operator configurations and the copy ceiling, in the same run
+        out["configs"] = configs_summary(args)
+        out["copy_ceiling_cold"] = _copy_ceiling(1 << 31, 20, cold=True)["gbs"]
     if args.workload in ("block", "block_unfused") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_block(inp, 4, 2048, 4096, 32, 11008,
                                                  fused=BLOCKS[args.workload].get("fused", True))

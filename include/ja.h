@@ -72,8 +72,12 @@ typedef int32_t ja_status;
 
 typedef enum { JA_F32 = 0, JA_BF16 = 1, JA_F16 = 2 } ja_dtype;
 
-/* Aggregation operators for ja_agg (section 3.2 step 2; section 5.2). */
-typedef enum { JA_AGG_SUM = 0, JA_AGG_MAX = 1 } ja_agg_op;
+/* Aggregation operators for ja_agg (section 3.2 step 2; section 5.2: the
+ * aggregation need not be addition).  JA_AGG_SOFTMAX folds attention's
+ * per-tuple triples (m, l, acc) with m = max(m1, m2),
+ * l = l1 e^(m1-m) + l2 e^(m2-m), acc = acc1 e^(m1-m) + acc2 e^(m2-m) and
+ * writes acc / l. */
+typedef enum { JA_AGG_SUM = 0, JA_AGG_MAX = 1, JA_AGG_SOFTMAX = 2 } ja_agg_op;
 
 /* A blocked tensor relation.  For dimension d, the blocks' boundaries are
  * splits[d][0] = 0 < splits[d][1] < ... < splits[d][nblk[d]] = shape[d]
@@ -275,6 +279,11 @@ void ja_djoin_destroy(ja_djoin* join);
  * workgroups * 256 floats, written with the accumulators' sums.  *flops
  * (may be NULL) gets the flops enqueued; time the launch on `stream`. */
 ja_status ja_calibrate_mfma(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream);
+/* The HBM ceiling a plain streaming copy reaches: copy `bytes` bytes from
+ * src to dst (device buffers, 16-byte aligned, bytes a multiple of 16, not
+ * overlapping) with 16-byte vector loads and stores, four per thread in
+ * flight.  Asynchronous on `stream`; time the launch there. */
+ja_status ja_calibrate_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* ---- attention planned on the device (section 3.3; section 3.2 on the GPU) */
 
@@ -412,21 +421,44 @@ ja_status ja_graph_device_time(const ja_graph* graph, const int32_t* const* inte
 ja_status ja_plan_create(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
                          int32_t n_in, const ja_relation_desc* out, ja_plan** plan);
 /* table_bytes: device buffer size for ja_plan_upload; workspace_bytes: the
- * workspace ja_plan_run needs (may be 0). */
+ * workspace ja_plan_run needs (may be 0; bf16 attention: 16 bytes per query
+ * tile of 128 rows). */
 ja_status ja_plan_device_bytes(const ja_plan* plan, size_t* table_bytes, size_t* workspace_bytes);
 /* Copy the plan's tables to dev_buf (at least table_bytes) on `stream` and
  * wait for the copy.  The buffer must stay alive while the plan is run. */
 ja_status ja_plan_upload(ja_plan* plan, void* dev_buf, size_t bytes, void* stream);
 /* Run the whole join-agg: every tuple's kernel with the aggregation fused
  * into it, writing each output block exactly once (recompose in place).
- * in_ptrs[i] / out_ptr: device buffers of the relations given at create. */
+ * in_ptrs[i] / out_ptr: device buffers of the relations given at create;
+ * workspace: workspace_bytes of device scratch, 16-byte aligned (NULL while
+ * that is 0; JA_ERR_WORKSPACE when it is needed and NULL), overwritten by
+ * the run, so two runs that share it must not overlap.
+ * Attention rounds V to fp16 for its P V product; with bf16 relations a
+ * query tile whose accumulators show V outside fp16's range (a value that is
+ * not finite, or outputs averaging below 2^-12) is computed again, by a
+ * second launch, with V multiplied by a power of two chosen from the largest
+ * exponent among the V rows it reads and O divided by it, so every finite
+ * bf16 V is in range. */
 ja_status ja_plan_run(const ja_plan* plan, const void* const* in_ptrs, void* out_ptr, void* workspace,
                       void* stream);
-/* Unfused path (contract only): ja_kernel writes every tuple's partial
- * output block in float32 to `partials` (ja_plan_partial_bytes bytes; tuple
- * i's block starts after the blocks of tuples 0..i-1, dense row-major);
- * ja_agg folds each segment's partials in ascending tuple order with `op`
- * and writes the output relation. */
+/* Unfused path (section 3.2, Definition 3.7, with the join's per-tuple
+ * results materialised): ja_kernel writes every tuple's partial result in
+ * float32 to `partials` (ja_plan_partial_bytes bytes; tuple i's part starts
+ * after the parts of tuples 0..i-1); ja_agg folds each segment's partials in
+ * ascending tuple order with `op` and writes the output relation.
+ *   contract (no epilogue): a tuple's part is its dense row-major partial
+ *     output block; op JA_AGG_SUM (the contraction) or JA_AGG_MAX.
+ *   attention: a tuple's part holds, per query row of its query block (rows
+ *     in the O block's order: batch-heads, then s), 132 floats [m, l, -, -,
+ *     acc[128]]: over the keys of the tuple's key block the row may see,
+ *     m = max of scale q.k (or a value below it: the triple is only defined
+ *     up to the shift (m, l, acc) ~ (m', l e^(m-m'), acc e^(m-m'))),
+ *     l = sum of exp(scale q.k - m), acc = sum of exp(scale q.k - m) v; a
+ *     row that sees none of them gets (-inf, 0, 0).  op JA_AGG_SOFTMAX.
+ *     With bf16 relations ja_plan_partial_bytes also counts 16 bytes per
+ *     query tile of scratch after the parts (the range check of ja_plan_run).
+ * Other operators and contractions with an epilogue: JA_ERR_UNSUPPORTED;
+ * an op that does not match the operator: JA_ERR_UNSUPPORTED. */
 ja_status ja_plan_partial_bytes(const ja_plan* plan, size_t* bytes);
 ja_status ja_kernel(const ja_plan* plan, const void* const* in_ptrs, void* partials, void* stream);
 ja_status ja_agg(const ja_plan* plan, ja_agg_op op, const void* partials, void* out_ptr, void* stream);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libja.so")
 
 JA_MAX_RANK = 8
 JA_F32, JA_BF16, JA_F16 = 0, 1, 2
-JA_AGG_SUM, JA_AGG_MAX = 0, 1
+JA_AGG_SUM, JA_AGG_MAX, JA_AGG_SOFTMAX = 0, 1, 2
 STATUS = {0: "JA_OK", -1: "JA_ERR_ARG", -2: "JA_ERR_SPEC", -3: "JA_ERR_DECOMP", -4: "JA_ERR_SHAPE",
           -5: "JA_ERR_DTYPE", -6: "JA_ERR_WORKSPACE", -7: "JA_ERR_UNSUPPORTED", -8: "JA_ERR_HIP",
           -9: "JA_ERR_STATE"}
@@ -79,6 +79,7 @@ _SIGS = {
     "ja_djoin_run": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ja_djoin_destroy": (None, [_vp]),
     "ja_calibrate_mfma": (_st, [_i32, _i32, _vp, ctypes.POINTER(ctypes.c_double), _vp]),
+    "ja_calibrate_copy": (_st, [_vp, _vp, _sz, _vp]),
     "ja_dattn_create": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, ctypes.POINTER(_vp)]),
     "ja_dattn_device_bytes": (_st, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_i64)]),
     "ja_dattn_upload": (_st, [_vp, _vp, _sz, _vp]),
@@ -344,6 +345,10 @@ def ja_calibrate_mfma(workgroups: int, iters: int, sink: int, stream: int = 0) -
     f = ctypes.c_double()
     _check(_lib.ja_calibrate_mfma(workgroups, iters, _vp(sink), ctypes.byref(f), _vp(stream)))
     return f.value
+
+
+def ja_calibrate_copy(src: int, dst: int, nbytes: int, stream: int = 0):
+    _check(_lib.ja_calibrate_copy(_vp(src), _vp(dst), nbytes, _vp(stream)))
 
 
 def ja_dattn_create(spec: int, extents: Sequence[int], intervals: Sequence[int], dtype: int = JA_BF16) -> int:

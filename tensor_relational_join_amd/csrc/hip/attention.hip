@@ -74,7 +74,26 @@ __device__ __forceinline__ void at_dma16(at_i32x4_t rsrc, uint32_t lds_byte, uin
 // some query's running maximum moved.
 // With tables built on the device, the grid covers an upper bound of tiles and
 // the count is read from ntiles_dev (NULL: the grid is exact).
-template <bool PACKED, bool F16>
+//
+// bf16 relations: V is rounded to fp16 for the P V product, whose exponent
+// range is far narrower than bf16's.  Ordinary data passes as is; at the end
+// of a tile every wave records in `flags` whether its accumulators look out of
+// range -- a value that is not finite (V beyond fp16's range) or outputs
+// averaging below 2^-12 (V perhaps below fp16's normal range).  A second,
+// REDO launch over the same tiles returns at once except on flagged tiles,
+// which take the largest exponent among the V rows the tile reads; when that lies outside [-8, 14]
+// it computes the tile again with every staged V value multiplied by
+// 2^-shift (shift = exponent - 14, so the largest magnitude lands in
+// [2^14, 2^15)) and O multiplied by 2^shift on the way out.  Powers of two
+// are exact in both formats, so any finite bf16 V is computed in range; data
+// of ordinary magnitude pays a sum over the accumulators, a store per wave
+// and a REDO launch whose workgroups find no flag and return.
+//
+// PARTIAL: every segment is one tuple and the tile writes, instead of O, the
+// tuple's unnormalised triple per query row -- f32 [m, l, 0, 0, acc[128]]
+// (ATTN_PROW floats) at element o_off + (bh S + row) ATTN_PROW, with m in
+// units of the scaled scores (P = exp(scale q.k - m)) -- for ja_agg to fold.
+template <bool PACKED, bool F16, bool PARTIAL, bool REDO>
 __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile* __restrict__ tiles,
                                                                const int32_t* __restrict__ ntiles_dev,
                                                                const AttnSeg* __restrict__ segs,
@@ -82,17 +101,24 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                                                                const int32_t* __restrict__ seq_ends, int nseq,
                                                                const uint16_t* __restrict__ Q,
                                                                const uint16_t* __restrict__ K,
-                                                               const uint16_t* __restrict__ V,
-                                                               uint16_t* __restrict__ O, float scale_log2, int causal) {
+                                                               const uint16_t* __restrict__ V, void* __restrict__ O,
+                                                               uint32_t* __restrict__ flags, float scale_log2,
+                                                               int causal) {
     constexpr int D = ATTN_D;
-    if (ntiles_dev && (int)blockIdx.x >= *ntiles_dev) return;
+    const int vt = blockIdx.x;
+    if (ntiles_dev && vt >= *ntiles_dev) return;
+    if constexpr (REDO) {
+        // only the tiles a wave of the first launch flagged
+        const uint4 f = *reinterpret_cast<const uint4*>(flags + 4 * vt);
+        if ((f.x | f.y | f.z | f.w) == 0) return;
+    }
     extern __shared__ __attribute__((aligned(16))) uint16_t at_lds[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)at_lds;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lq = lane & 31;
-    const AttnTile tl = tiles[blockIdx.x];
+    const AttnTile tl = tiles[vt];
     const AttnSeg sg = segs[tl.seg];
     const int kvbh = tl.bh / sg.rep;  // key-value batch-head (query heads of a group share it)
     const int qrow = tl.s0 + wave * 32 + lq;  // query row inside the block
@@ -229,6 +255,11 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     // rows 8 dj + 2 w (low halves) and 8 dj + 2 w + 1 (high halves); lanes of
     // odd dj write the odd row first, so that each write instruction covers
     // rows of both parities (both halves of the banks).
+    int vshift = 0;  // REDO: V staged as V 2^-vshift, O written as O 2^vshift
+    auto cvt = [&](float x) -> _Float16 {
+        if constexpr (REDO) x = __builtin_amdgcn_ldexpf(x, -vshift);
+        return (_Float16)x;
+    };
     auto store_v = [&](int buf) {
         _Float16* vt = reinterpret_cast<_Float16*>(at_lds + buf * AT_STAGE + AT_KT * D);
         const int hgrp = kg >> 2, q = kg & 3;
@@ -248,10 +279,10 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                 hi = make_uint2((r0[w] >> 16) | (r1[w] & 0xffff0000u), (r2[w] >> 16) | (r3[w] & 0xffff0000u));
             } else {
                 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-                const h4 l4 = {(_Float16)bf16lo_to_f32(r0[w]), (_Float16)bf16lo_to_f32(r1[w]),
-                               (_Float16)bf16lo_to_f32(r2[w]), (_Float16)bf16lo_to_f32(r3[w])};
-                const h4 h4v = {(_Float16)bf16hi_to_f32(r0[w]), (_Float16)bf16hi_to_f32(r1[w]),
-                                (_Float16)bf16hi_to_f32(r2[w]), (_Float16)bf16hi_to_f32(r3[w])};
+                const h4 l4 = {cvt(bf16lo_to_f32(r0[w])), cvt(bf16lo_to_f32(r1[w])), cvt(bf16lo_to_f32(r2[w])),
+                               cvt(bf16lo_to_f32(r3[w]))};
+                const h4 h4v = {cvt(bf16hi_to_f32(r0[w])), cvt(bf16hi_to_f32(r1[w])), cvt(bf16hi_to_f32(r2[w])),
+                                cvt(bf16hi_to_f32(r3[w]))};
                 lo = __builtin_bit_cast(uint2, l4);
                 hi = __builtin_bit_cast(uint2, h4v);
             }
@@ -262,6 +293,36 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     };
     auto sync_step = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
+    if constexpr (REDO) {
+        // the largest exponent field among the V rows of the visible keys
+        // (a superset of what the steps read), over the workgroup
+        uint32_t em = 0;
+        for (int t = sg.t_begin; t < sg.t_end; ++t) {
+            const AttnTuple tp = tuples[t];
+            const int f = first_key(tp), e = end_key(tp);
+            if (e <= f) continue;
+            const uint4* vp =
+                reinterpret_cast<const uint4*>(V + tp.v_off + (int64_t)kvbh * tp.kv_bhstride + (int64_t)f * D);
+            for (int c = tid; c < (e - f) * (D / 8); c += AT_THREADS) {
+                const uint4 v = vp[c];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) em = max(em, max((w[k] >> 7) & 0xffu, (w[k] >> 23) & 0xffu));
+            }
+        }
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1) em = max(em, (uint32_t)__shfl_xor((int)em, k));
+        __shared__ uint32_t at_emax[AT_THREADS / 64];
+        if (lane == 0) at_emax[wave] = em;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        em = at_emax[0];
+#pragma unroll
+        for (int w = 1; w < AT_THREADS / 64; ++w) em = max(em, at_emax[w]);
+        const int e = (int)max(em, 1u) - 127;  // a field of 0 (zeros, subnormals) counts as 2^-126
+        vshift = __builtin_amdgcn_readfirstlane((e >= 15 || e < -8) ? e - 14 : 0);
+        // flagged by a false alarm: the first launch's result stands
+        if (vshift == 0) return;
+    }
     // compute cursor (same walk as the load cursor)
     int ct = sg.t_begin, ckt = 0;
     enter(ct, ckt);
@@ -391,48 +452,111 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    const float inv = 1.0f / l_tot;
-    if (qrow < sg.S) {
-        uint16_t* op = O + sg.o_off + (int64_t)tl.bh * sg.q_bhstride + (int64_t)qrow * D;
+    if constexpr (!F16 && !REDO) {
+        // this wave's verdict for the REDO launch: its accumulators are not
+        // finite (V beyond fp16's range), or its outputs average below 2^-12
+        // (V perhaps below fp16's normal range; rows that saw no key are left
+        // out)
+        float sabs = 0.f;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = dt * 32 + 8 * j + 4 * g;
-                uint2 w;
-                w.x = pack_h16x2<F16>(oacc[dt][4 * j + 0] * inv, oacc[dt][4 * j + 1] * inv);
-                w.y = pack_h16x2<F16>(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
-                *reinterpret_cast<uint2*>(op + d) = w;
-            }
+            for (int r = 0; r < 16; ++r) sabs += fabsf(oacc[dt][r]);
+        const bool odd = !(sabs < INFINITY) || (l_tot > 0.f && sabs < l_tot * 0x1p-6f);
+        const uint32_t any = __builtin_amdgcn_ballot_w64(odd) != 0;
+        if (lane == 0) flags[4 * vt + wave] = any;
     }
+    auto unscale = [&](float x) {
+        if constexpr (REDO) return __builtin_amdgcn_ldexpf(x, vshift);
+        return x;
+    };
+    if constexpr (PARTIAL) {
+        if (qrow < sg.S) {
+            float* pp = (float*)O + sg.o_off + ((int64_t)tl.bh * sg.S + qrow) * ATTN_PROW;
+            if (g == 0)
+                *reinterpret_cast<float4*>(pp) = make_float4(
+                    m_run == -INFINITY ? -INFINITY : m_run * (scale_log2 * 0.6931471805599453f), l_tot, 0.f, 0.f);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = dt * 32 + 8 * j + 4 * g;
+                    *reinterpret_cast<float4*>(pp + 4 + d) =
+                        make_float4(unscale(oacc[dt][4 * j + 0]), unscale(oacc[dt][4 * j + 1]),
+                                    unscale(oacc[dt][4 * j + 2]), unscale(oacc[dt][4 * j + 3]));
+                }
+        }
+    } else {
+        const float inv = 1.0f / l_tot;
+        if (qrow < sg.S) {
+            uint16_t* op = (uint16_t*)O + sg.o_off + (int64_t)tl.bh * sg.q_bhstride + (int64_t)qrow * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = dt * 32 + 8 * j + 4 * g;
+                    uint2 w;
+                    w.x = pack_h16x2<F16>(unscale(oacc[dt][4 * j + 0] * inv), unscale(oacc[dt][4 * j + 1] * inv));
+                    w.y = pack_h16x2<F16>(unscale(oacc[dt][4 * j + 2] * inv), unscale(oacc[dt][4 * j + 3] * inv));
+                    *reinterpret_cast<uint2*>(op + d) = w;
+                }
+        }
+    }
+}
+
+template <bool PACKED, bool F16, bool PARTIAL>
+static void launch_pair(const AttnTile* tiles, int ntiles, const int32_t* ntiles_dev, const AttnSeg* segs,
+                        const AttnTuple* tuples, const int32_t* seq_ends, int nseq, const void* Q, const void* K,
+                        const void* V, void* O, uint32_t* flags, float scale_log2, int causal, hipStream_t stream) {
+    const unsigned lds = 2u * AT_STAGE * sizeof(uint16_t);
+    hipLaunchKernelGGL((attention_kernel<PACKED, F16, PARTIAL, false>), dim3(ntiles), dim3(AT_THREADS), lds, stream,
+                       tiles, ntiles_dev, segs, tuples, seq_ends, nseq, (const uint16_t*)Q, (const uint16_t*)K,
+                       (const uint16_t*)V, O, flags, scale_log2, causal);
+    if constexpr (!F16)  // the flagged tiles again, V scaled (every other workgroup returns at once)
+        hipLaunchKernelGGL((attention_kernel<PACKED, F16, PARTIAL, true>), dim3(ntiles), dim3(AT_THREADS), lds, stream,
+                           tiles, ntiles_dev, segs, tuples, seq_ends, nseq, (const uint16_t*)Q, (const uint16_t*)K,
+                           (const uint16_t*)V, O, flags, scale_log2, causal);
 }
 
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
                             int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,
-                            const void* V, void* O, float scale, int32_t causal, int32_t f16, hipStream_t stream) {
+                            const void* V, void* O, uint32_t* flags, float scale, int32_t causal, int32_t f16,
+                            int32_t partial, hipStream_t stream) {
     const uint8_t* t = (const uint8_t*)table;
-    const float scale_log2 = scale * 1.4426950408889634f;
-    const unsigned lds = 2u * AT_STAGE * sizeof(uint16_t);
-    auto kernel = nseq ? (f16 ? attention_kernel<true, true> : attention_kernel<true, false>)
-                       : (f16 ? attention_kernel<false, true> : attention_kernel<false, false>);
-    hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(AT_THREADS), lds, stream,
-                       (const AttnTile*)(t + tiles_off), (const int32_t*)nullptr, (const AttnSeg*)(t + segs_off),
-                       (const AttnTuple*)(t + tuples_off), nseq ? (const int32_t*)(t + seq_off) : nullptr, nseq,
-                       (const uint16_t*)Q, (const uint16_t*)K,
-                       (const uint16_t*)V, (uint16_t*)O, scale_log2, causal);
+    const float sl2 = scale * 1.4426950408889634f;
+    const AttnTile* tl = (const AttnTile*)(t + tiles_off);
+    const AttnSeg* sg = (const AttnSeg*)(t + segs_off);
+    const AttnTuple* tp = (const AttnTuple*)(t + tuples_off);
+    const int32_t* se = nseq ? (const int32_t*)(t + seq_off) : nullptr;
+#define JA_ATT(P, H, R) launch_pair<P, H, R>(tl, ntiles, nullptr, sg, tp, se, nseq, Q, K, V, O, flags, sl2, causal, stream)
+    if (partial) {
+        if (nseq) {
+            if (f16) JA_ATT(true, true, true); else JA_ATT(true, false, true);
+        } else {
+            if (f16) JA_ATT(false, true, true); else JA_ATT(false, false, true);
+        }
+    } else {
+        if (nseq) {
+            if (f16) JA_ATT(true, true, false); else JA_ATT(true, false, false);
+        } else {
+            if (f16) JA_ATT(false, true, false); else JA_ATT(false, false, false);
+        }
+    }
+#undef JA_ATT
     return hipGetLastError();
 }
 
 hipError_t launch_attention_dev(const AttnTile* tiles, const int32_t* ntiles_dev, uint32_t max_tiles,
                                 const AttnSeg* segs, const AttnTuple* tuples, const int32_t* seq_ends, int32_t nseq,
-                                const void* Q, const void* K, const void* V, void* O, float scale, int32_t causal,
-                                int32_t f16, hipStream_t stream) {
-    const float scale_log2 = scale * 1.4426950408889634f;
-    const unsigned lds = 2u * AT_STAGE * sizeof(uint16_t);
-    auto kernel = f16 ? attention_kernel<true, true> : attention_kernel<true, false>;
-    hipLaunchKernelGGL(kernel, dim3(max_tiles), dim3(AT_THREADS), lds, stream, tiles, ntiles_dev, segs, tuples,
-                       seq_ends, nseq, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)O,
-                       scale_log2, causal);
+                                const void* Q, const void* K, const void* V, void* O, uint32_t* flags, float scale,
+                                int32_t causal, int32_t f16, hipStream_t stream) {
+    const float sl2 = scale * 1.4426950408889634f;
+    if (f16)
+        launch_pair<true, true, false>(tiles, (int)max_tiles, ntiles_dev, segs, tuples, seq_ends, nseq, Q, K, V, O,
+                                       flags, sl2, causal, stream);
+    else
+        launch_pair<true, false, false>(tiles, (int)max_tiles, ntiles_dev, segs, tuples, seq_ends, nseq, Q, K, V, O,
+                                        flags, sl2, causal, stream);
     return hipGetLastError();
 }
 

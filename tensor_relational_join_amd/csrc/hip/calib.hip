@@ -1,7 +1,7 @@
-// calib.hip -- a measurement aid: the matrix-core throughput this GPU
+// calib.hip -- measurement aids: the matrix-core throughput this GPU
 // sustains on a loop of nothing but bf16 MFMAs (no memory traffic, no LDS, no
-// barriers), the ceiling the contraction and attention kernels are compared
-// against beside the published peak.
+// barriers), and the HBM bandwidth a plain streaming copy reaches -- the
+// ceilings the kernels are compared against beside the published peaks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +42,43 @@ __global__ __launch_bounds__(CAL_THREADS) void mfma_loop_kernel(int32_t iters, f
 
 hipError_t launch_mfma_loop(int32_t workgroups, int32_t iters, float* sink, hipStream_t stream) {
     hipLaunchKernelGGL(mfma_loop_kernel, dim3(workgroups), dim3(CAL_THREADS), 0, stream, iters, sink);
+    return hipGetLastError();
+}
+
+// A streaming copy of n16 16-byte vectors: each thread moves COPY_UNROLL
+// vectors per round, all loaded before any is stored, rounds strided by the
+// whole grid.
+constexpr int COPY_UNROLL = 4;
+
+__global__ __launch_bounds__(CAL_THREADS) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * CAL_THREADS * COPY_UNROLL;
+    for (int64_t base = (int64_t)blockIdx.x * CAL_THREADS * COPY_UNROLL + threadIdx.x; base < n16; base += stride) {
+        uint4 v[COPY_UNROLL];
+#pragma unroll
+        for (int j = 0; j < COPY_UNROLL; ++j) {
+            const int64_t i = base + (int64_t)j * CAL_THREADS;
+            if (i < n16) v[j] = src[i];
+        }
+#pragma unroll
+        for (int j = 0; j < COPY_UNROLL; ++j) {
+            const int64_t i = base + (int64_t)j * CAL_THREADS;
+            if (i < n16) dst[i] = v[j];
+        }
+    }
+}
+
+hipError_t launch_copy(const void* src, void* dst, int64_t n16, hipStream_t stream) {
+    if (n16 <= 0) return hipSuccess;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus < 1)
+        cus = 256;
+    // enough workgroups to keep every compute unit's loads in flight, no more than the vectors need
+    const int64_t need = (n16 + CAL_THREADS * COPY_UNROLL - 1) / (CAL_THREADS * COPY_UNROLL);
+    const int64_t grid = need < (int64_t)cus * 16 ? need : (int64_t)cus * 16;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(CAL_THREADS), 0, stream, (const uint4*)src, (uint4*)dst,
+                       n16);
     return hipGetLastError();
 }
 

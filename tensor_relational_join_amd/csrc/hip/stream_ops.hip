@@ -438,4 +438,54 @@ hipError_t launch_agg(const void* table, int64_t tiles_off, int32_t ntiles, int6
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- softmax aggregation
+// The aggregation of attention's per-tuple triples (the operator need not be
+// addition, "Every Kernel Is a Join", paperpeel full text, section 5.2): each
+// query row's triples (m, l, acc) from the tuples of its segment, in tuple
+// order, folded with m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m),
+// acc = acc1 e^(m1-m) + acc2 e^(m2-m) from the identity (-inf, 0, 0); the
+// row's output is acc / l.  A workgroup owns SMAX_ROWS rows of one segment,
+// 32 lanes per row, 4 of the 128 values per lane; the partial row of tuple t
+// starts at poff[t] + row ATTN_PROW (f32 [m, l, -, -, acc[128]]), the output
+// row at out_off + row 128.  AggSeg.nelem counts the segment's rows.
+template <bool F16>
+__global__ __launch_bounds__(256) void smax_agg_kernel(const AggTile* __restrict__ tiles,
+                                                       const AggSeg* __restrict__ segs,
+                                                       const int64_t* __restrict__ poff,
+                                                       const float* __restrict__ part, uint16_t* __restrict__ out) {
+    static_assert(256 / 32 == SMAX_ROWS, "32 lanes per row");
+    const AggTile tl = tiles[blockIdx.x];
+    const AggSeg sg = segs[tl.seg];
+    const int row = tl.e0 + (int)(threadIdx.x >> 5), c = (threadIdx.x & 31) * 4;
+    if (row >= sg.nelem) return;
+    float m = -INFINITY, l = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t = sg.t_begin; t < sg.t_end; ++t) {
+        const float* pr = part + poff[t] + (int64_t)row * ATTN_PROW;
+        const float2 ml = *reinterpret_cast<const float2*>(pr);
+        const float4 a = *reinterpret_cast<const float4*>(pr + 4 + c);
+        const float mn = fmaxf(m, ml.x);
+        if (mn == -INFINITY) continue;  // identity folded with identity
+        const float s1 = __expf(m - mn), s2 = __expf(ml.x - mn);  // exp(-inf) = 0
+        l = l * s1 + ml.y * s2;
+        acc.x = acc.x * s1 + a.x * s2;
+        acc.y = acc.y * s1 + a.y * s2;
+        acc.z = acc.z * s1 + a.z * s2;
+        acc.w = acc.w * s1 + a.w * s2;
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+    *reinterpret_cast<uint2*>(out + sg.out_off + (int64_t)row * ATTN_D + c) =
+        make_uint2(pack_h16x2<F16>(acc.x * inv, acc.y * inv), pack_h16x2<F16>(acc.z * inv, acc.w * inv));
+}
+
+hipError_t launch_smax_agg(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t poff_off,
+                           const float* partials, void* out, int32_t f16, hipStream_t stream) {
+    const uint8_t* t = (const uint8_t*)table;
+    auto kernel = f16 ? smax_agg_kernel<true> : smax_agg_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(256), 0, stream, (const AggTile*)(t + tiles_off),
+                       (const AggSeg*)(t + segs_off), (const int64_t*)(t + poff_off), partials, (uint16_t*)out);
+    return hipGetLastError();
+}
+
 }  // namespace ja

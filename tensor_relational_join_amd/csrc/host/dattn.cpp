@@ -15,8 +15,8 @@ hipError_t launch_dattn_tables(const DAttnArgs& a, const int64_t* splits, const 
                                int32_t* seq32, hipStream_t stream);
 hipError_t launch_attention_dev(const AttnTile* tiles, const int32_t* ntiles_dev, uint32_t max_tiles,
                                 const AttnSeg* segs, const AttnTuple* tuples, const int32_t* seq_ends, int32_t nseq,
-                                const void* Q, const void* K, const void* V, void* O, float scale, int32_t causal,
-                                int32_t f16, hipStream_t stream);
+                                const void* Q, const void* K, const void* V, void* O, uint32_t* flags, float scale,
+                                int32_t causal, int32_t f16, hipStream_t stream);
 namespace {
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -56,7 +56,7 @@ struct ja_dattn {
     std::vector<int32_t> qn, kn;
     size_t dj_table = 0, off_qbase = 0, off_qn = 0, off_kbase = 0, off_kn = 0, table_bytes = 0;
     size_t dj_ws = 0, off_rec = 0, off_seg = 0, off_tcnt = 0, off_hist = 0, off_base = 0, off_cursor = 0,
-           off_ntiles = 0, off_segs = 0, off_tuples = 0, off_tiles = 0, off_seq = 0, ws_bytes = 0;
+           off_ntiles = 0, off_segs = 0, off_tuples = 0, off_tiles = 0, off_seq = 0, off_flags = 0, ws_bytes = 0;
     int64_t n_splits = 0, max_tuples = 0, max_segs = 0;
     int32_t f16 = 0, causal = 0;
     float scale = 0;
@@ -177,6 +177,9 @@ ja_status ja_dattn_create(const ja_spec* s, const int64_t* extents, const int32_
     o = al256(o + sizeof(AttnTile) * (size_t)max_tiles);
     d->off_seq = o;
     o = al256(o + 4 * (size_t)a.nseq);
+    // bf16: the attention tiles' range-check flags (4 words per tile)
+    d->off_flags = o;
+    if (!d->f16) o = al256(o + 16 * (size_t)max_tiles);
     d->ws_bytes = o;
     *out = d;
     return JA_OK;
@@ -233,7 +236,7 @@ ja_status ja_dattn_run(const ja_dattn* d, const int64_t* splits_dev, const void*
                                    (uint32_t*)(ws + d->off_tcnt), (uint32_t*)(ws + d->off_hist),
                                    (uint32_t*)(ws + d->off_base), (uint32_t*)(ws + d->off_cursor), ntiles, seq32, hs));
     JA_TRY_HIP(launch_attention_dev(tiles, ntiles, d->a.max_tiles, segs, tuples, seq32, d->a.nseq, Q, K, V, O,
-                                    d->scale, d->causal, d->f16, hs));
+                                    (uint32_t*)(ws + d->off_flags), d->scale, d->causal, d->f16, hs));
     return JA_OK;
 }
 

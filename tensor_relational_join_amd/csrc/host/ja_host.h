@@ -98,9 +98,14 @@ hipError_t launch_gemm(const void* table, int64_t tiles_off, int32_t ntiles, int
                        const void* A, const void* B, void* C, const void* R, int32_t epi, int32_t in_dtype,
                        int32_t out_dtype, int32_t a_layout, int32_t b_layout, hipStream_t stream);
 // seq_off / nseq: the packed sequences' int32 end positions in the table (nseq = 0: not packed)
+// partial: write the per-tuple softmax triples instead of O; flags: bf16, 4
+// words per tile for the range check (see attention.hip), unused for f16
 hipError_t launch_attention(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off,
                             int64_t tuples_off, int64_t seq_off, int32_t nseq, const void* Q, const void* K,
-                            const void* V, void* O, float scale, int32_t causal, int32_t f16, hipStream_t stream);
+                            const void* V, void* O, uint32_t* flags, float scale, int32_t causal, int32_t f16,
+                            int32_t partial, hipStream_t stream);
+hipError_t launch_smax_agg(const void* table, int64_t tiles_off, int32_t ntiles, int64_t segs_off, int64_t poff_off,
+                           const float* partials, void* out, int32_t f16, hipStream_t stream);
 hipError_t launch_rmsnorm(const void* table, int64_t rsplit_off, int32_t nrb, int64_t blocks_off, int32_t ndb,
                           int64_t rows, int32_t D, int32_t W, const void* x, const void* gain, void* y, float eps,
                           int32_t vec, int32_t f16, hipStream_t stream);

@@ -109,10 +109,52 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
     tiles.reserve(work.size());
     for (auto& w : work) tiles.push_back(w.tile);
     if ((int64_t)tiles.size() > lim) return fail(JA_ERR_UNSUPPORTED, "too many tiles");
+    // Unfused path (ja_kernel / ja_agg): every tuple is a segment of its own
+    // writing f32 triples [m, l, -, -, acc[D]] per query row of its block
+    // (ATTN_PROW floats, rows in the O block's [bh][s] order) into the
+    // partials; the softmax aggregation then folds each segment's tuples.
+    std::vector<AttnSeg> usegs(nt);
+    std::vector<AttnTile> utiles;
+    std::vector<int64_t> poff(nt);
+    std::vector<AggSeg> asegs(nseg);
+    std::vector<AggTile> atiles;
+    int64_t part = 0;
+    for (int64_t sg = 0; sg < nseg; ++sg) {
+        const AttnSeg& g = segs[sg];
+        const int64_t rows = (int64_t)g.S * extent_of(d, s, &t.rec[t.seg[sg] * t.nl], batch);
+        if (rows > lim) return fail(JA_ERR_UNSUPPORTED, "query block beyond 2^31 rows");
+        for (int32_t k = g.t_begin; k < g.t_end; ++k) {
+            AttnSeg u = g;
+            u.o_off = part;
+            u.t_begin = k;
+            u.t_end = k + 1;
+            usegs[k] = u;
+            poff[k] = part;
+            part += rows * ATTN_PROW;
+            for (int32_t bh = 0; bh < rows / g.S; ++bh)
+                for (int32_t s0 = 0; s0 < g.S; s0 += ATTN_TQ) utiles.push_back({k, bh, s0, 0});
+        }
+        AggSeg& a = asegs[sg];
+        a.out_off = g.o_off;
+        a.nelem = (int32_t)rows;
+        a.t_begin = g.t_begin;
+        a.t_end = g.t_end;
+        a.pad = 0;
+        for (int32_t r0 = 0; r0 < a.nelem; r0 += SMAX_ROWS) atiles.push_back({(int32_t)sg, r0});
+    }
+    if ((int64_t)utiles.size() > lim || (int64_t)atiles.size() > lim) return fail(JA_ERR_UNSUPPORTED, "too many tiles");
+    p->partial_elems = part;
     p->tiles_off = put(p->table, tiles);
     p->ntiles = (int32_t)tiles.size();
     p->segs_off = put(p->table, segs);
     p->tuples_off = put(p->table, tuples);
+    p->utiles_off = put(p->table, utiles);
+    p->nutiles = (int32_t)utiles.size();
+    p->usegs_off = put(p->table, usegs);
+    p->atiles_off = put(p->table, atiles);
+    p->natiles = (int32_t)atiles.size();
+    p->asegs_off = put(p->table, asegs);
+    p->apoff_off = put(p->table, poff);
     if (!ends.empty()) {
         std::vector<int32_t> e32(ends.begin(), ends.end());
         p->seq_off = put(p->table, e32);
@@ -186,6 +228,12 @@ ja_status plan_zip(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_re
 
 }  // namespace
 
+// bf16 attention: 4 words of range-check flags per tile (fused tiles for
+// ja_plan_run's workspace, per-tuple tiles after ja_kernel's partials)
+static size_t att_flag_bytes(const ja_plan* p, int32_t ntiles) {
+    return p->kind == JA_OP_ATTENTION && p->in_dtype == JA_BF16 ? (size_t)16 * (size_t)ntiles : 0;
+}
+
 extern "C" {
 
 ja_status ja_plan_create(const ja_spec* s, const ja_decomp* d, const ja_relation_desc* const* in, int32_t n_in,
@@ -221,7 +269,7 @@ ja_status ja_plan_create(const ja_spec* s, const ja_decomp* d, const ja_relation
 ja_status ja_plan_device_bytes(const ja_plan* p, size_t* table_bytes, size_t* workspace_bytes) {
     if (!p) return fail(JA_ERR_ARG, "plan is NULL");
     if (table_bytes) *table_bytes = p->table.size();
-    if (workspace_bytes) *workspace_bytes = 0;
+    if (workspace_bytes) *workspace_bytes = att_flag_bytes(p, p->ntiles);
     return JA_OK;
 }
 
@@ -249,7 +297,6 @@ static ja_status check_ptrs(const ja_plan* p, const void* const* in_ptrs, const 
 }
 
 ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_ptr, void* workspace, void* stream) {
-    (void)workspace;
     ja_status st = check_ptrs(p, in_ptrs, out_ptr);
     if (st) return st;
     hipStream_t hs = (hipStream_t)stream;
@@ -262,9 +309,12 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
             break;
         case JA_OP_ATTENTION:
             if (p->ntiles == 0) return JA_OK;
+            if (att_flag_bytes(p, p->ntiles) && !workspace)
+                return fail(JA_ERR_WORKSPACE, "bf16 attention needs the plan's workspace");
+            if ((uintptr_t)workspace & 15) return fail(JA_ERR_ARG, "workspace must be 16-byte aligned");
             JA_TRY_HIP(launch_attention(p->dev, p->tiles_off, p->ntiles, p->segs_off, p->tuples_off, p->seq_off,
-                                        p->nseq, in_ptrs[0], in_ptrs[1], in_ptrs[2], out_ptr, p->scale, p->causal,
-                                        p->in_dtype == JA_F16, hs));
+                                        p->nseq, in_ptrs[0], in_ptrs[1], in_ptrs[2], out_ptr, (uint32_t*)workspace,
+                                        p->scale, p->causal, p->in_dtype == JA_F16, 0, hs));
             break;
         case JA_OP_RMSNORM:
             JA_TRY_HIP(launch_rmsnorm(p->dev, p->rsplit_off, p->nrb, p->nblk_off, p->ndb, p->rows, p->D, p->norm_w,
@@ -281,32 +331,52 @@ ja_status ja_plan_run(const ja_plan* p, const void* const* in_ptrs, void* out_pt
 
 ja_status ja_plan_partial_bytes(const ja_plan* p, size_t* bytes) {
     if (!p || !bytes) return fail(JA_ERR_ARG, "NULL argument");
-    if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (p->kind != JA_OP_CONTRACT && p->kind != JA_OP_ATTENTION)
+        return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract and attention only");
     if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
-    *bytes = (size_t)p->partial_elems * 4;
+    // bf16 attention: the per-tuple tiles' range-check flags follow the partials
+    *bytes = (size_t)p->partial_elems * 4 + att_flag_bytes(p, p->nutiles);
     return JA_OK;
 }
 
 ja_status ja_kernel(const ja_plan* p, const void* const* in_ptrs, void* partials, void* stream) {
     ja_status st = check_ptrs(p, in_ptrs, partials);
     if (st) return st;
-    if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (p->kind != JA_OP_CONTRACT && p->kind != JA_OP_ATTENTION)
+        return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract and attention only");
     if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
     if (p->nutiles == 0) return JA_OK;
+    hipStream_t hs = (hipStream_t)stream;
+    if (p->kind == JA_OP_ATTENTION) {
+        uint32_t* flags = (uint32_t*)((uint8_t*)partials + (size_t)p->partial_elems * 4);
+        JA_TRY_HIP(launch_attention(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off, p->seq_off,
+                                    p->nseq, in_ptrs[0], in_ptrs[1], in_ptrs[2], partials, flags, p->scale,
+                                    p->causal, p->in_dtype == JA_F16, 1, hs));
+        return JA_OK;
+    }
     JA_TRY_HIP(launch_gemm(p->dev, p->utiles_off, p->nutiles, p->usegs_off, p->tuples_off, in_ptrs[0], in_ptrs[1],
-                           partials, nullptr, JA_EPI_NONE, p->in_dtype, JA_F32, p->a_layout, p->b_layout,
-                           (hipStream_t)stream));
+                           partials, nullptr, JA_EPI_NONE, p->in_dtype, JA_F32, p->a_layout, p->b_layout, hs));
     return JA_OK;
 }
 
 ja_status ja_agg(const ja_plan* p, ja_agg_op op, const void* partials, void* out_ptr, void* stream) {
     if (!p || !partials || !out_ptr) return fail(JA_ERR_ARG, "NULL argument");
     if (!p->dev) return fail(JA_ERR_STATE, "plan tables are not uploaded");
-    if (p->kind != JA_OP_CONTRACT) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract only");
+    if (p->kind != JA_OP_CONTRACT && p->kind != JA_OP_ATTENTION)
+        return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract and attention only");
     if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
-    if (op != JA_AGG_SUM && op != JA_AGG_MAX) return fail(JA_ERR_ARG, "unknown aggregation operator");
+    if (op != JA_AGG_SUM && op != JA_AGG_MAX && op != JA_AGG_SOFTMAX)
+        return fail(JA_ERR_ARG, "unknown aggregation operator");
+    if ((p->kind == JA_OP_ATTENTION) != (op == JA_AGG_SOFTMAX))
+        return fail(JA_ERR_UNSUPPORTED, "attention partials aggregate with JA_AGG_SOFTMAX, contraction partials with "
+                                        "JA_AGG_SUM or JA_AGG_MAX");
     if (((uintptr_t)partials & 15) || ((uintptr_t)out_ptr & 15)) return fail(JA_ERR_ARG, "buffers must be 16-byte aligned");
     if (p->natiles == 0) return JA_OK;
+    if (op == JA_AGG_SOFTMAX) {
+        JA_TRY_HIP(launch_smax_agg(p->dev, p->atiles_off, p->natiles, p->asegs_off, p->apoff_off,
+                                   (const float*)partials, out_ptr, p->in_dtype == JA_F16, (hipStream_t)stream));
+        return JA_OK;
+    }
     JA_TRY_HIP(launch_agg(p->dev, p->atiles_off, p->natiles, p->asegs_off, p->apoff_off, (const float*)partials,
                           out_ptr, p->out_dtype, (int32_t)op, (hipStream_t)stream));
     return JA_OK;

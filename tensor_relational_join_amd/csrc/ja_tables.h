@@ -121,6 +121,8 @@ constexpr int GEMM_F32_TM = 64;    // fp32 kernel tile
 constexpr int GEMM_F32_TN = 64;
 constexpr int ATTN_TQ = 128;       // query rows per attention workgroup
 constexpr int ATTN_D = 128;        // head dimension the attention kernel is built for
+constexpr int ATTN_PROW = 132;     // f32 per query row of an attention partial: m, l, 2 pad, acc[128]
+constexpr int SMAX_ROWS = 8;       // query rows per softmax-aggregation workgroup
 constexpr int AGG_CHUNK = 2048;    // output elements per aggregation workgroup
 constexpr int REP_CHUNK = 16384;   // max elements per repartition task
 constexpr int REP_VEC = 1;         // RepTask.flags bit: 16-byte vector copies are valid

@@ -184,8 +184,14 @@ class Repart:
             raise
 
     def run(self, src: torch.Tensor, dst: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
-        sptr, dptr = check_buffers([(src, self.src.nbytes, TORCH_DTYPE[self.src.dtype], "source"),
-                                    (dst, self.dst.nbytes, TORCH_DTYPE[self.dst.dtype], "destination")])
+        # a repartition copies bytes: any dtype of the relation's element size will do
+        esize = B.DTYPE_SIZE[self.src.dtype]
+        for t, what in ((src, "source"), (dst, "destination")):
+            if isinstance(t, torch.Tensor) and t.element_size() != esize:
+                raise ValueError("%s: %d-byte elements, the relation has %d-byte elements" %
+                                 (what, t.element_size(), esize))
+        sptr, dptr = check_buffers([(src, self.src.nbytes, None, "source"),
+                                    (dst, self.dst.nbytes, None, "destination")])
         B.ja_repart_run(self.rp, sptr, dptr, stream_handle(stream))
 
     def close(self):

@@ -1,5 +1,8 @@
 """Shared helpers of the GPU parity tests: metrics and host<->device moves.
 The metrics are the ones the parity bar is stated in."""
+import json
+import os
+
 import numpy as np
 
 
@@ -45,3 +48,17 @@ def to_dev_f16(bits):
 
     return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16).ravel()).view(
         torch.float16).cuda()
+
+
+def record(test: str, **values):
+    """Append one JSON line of measured parity figures to the file named by
+    JA_PARITY_RECORD (nothing when it is unset), so that a GPU run keeps the
+    errors it measured and not only whether they passed."""
+    path = os.environ.get("JA_PARITY_RECORD")
+    if not path:
+        return
+    d = os.path.dirname(path)
+    if d:
+        os.makedirs(d, exist_ok=True)
+    with open(path, "a") as f:
+        f.write(json.dumps(dict(test=test, **values), sort_keys=True) + "\n")

@@ -76,8 +76,10 @@ def test_repart_run_refuses_bad_buffers():
     rp.rp = None
     with pytest.raises(ValueError, match="source: .* bytes"):
         rp.run(_bf16(100), _bf16(64 * 64))
-    with pytest.raises(ValueError, match="destination: dtype"):
+    with pytest.raises(ValueError, match="destination: 4-byte elements"):
         rp.run(_bf16(64 * 64), torch.zeros(64 * 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU"):  # raw 16-bit views of the bytes are fine, but not on the host
+        rp.run(torch.zeros(64 * 64, dtype=torch.int16), _bf16(64 * 64))
 
 
 def test_device_attention_refuses_bad_buffers():

@@ -8,13 +8,15 @@ contractions and attention, bit-exact for the two repartitions -- at the
 bf16 tolerance (relative Frobenius <= 2e-3).
 
 End-to-end chain: the block output is also compared with the oracle's own
-chain from the block inputs.  Both sides round every one of the eleven
-materialised bf16 relations, so once an upstream value differs by a fraction
-of an ulp the downstream roundings decorrelate; each decorrelated rounding
-adds up to ~2^-8/sqrt(6) ~ 1.6e-3 relative noise, and with up to ~20
-such stages feeding forward the bound is sqrt(20) * 1.6e-3 ~ 7e-3, so the
-chain is held to CHAIN_TOL = 1e-2.  A wrong index, head mapping or dropped
-tuple gives errors of order 1.
+chain from the block inputs.  At the reduced shapes it is held to the same
+2e-3.  At full size it is held to CHAIN_TOL_FULL = 5e-3: attention rounds P
+to IEEE half for its P V product, which keeps attention itself within 2e-3
+but changes O enough to flip downstream bf16 roundings, and the FFN carries
+those to y.  The oracle alone shows it (tests/test_chain_tolerance.py): with
+only P rounded to half, its full-size chain moves by 3.4-3.8e-3; with P kept
+in float32, by nothing.  The measured errors are recorded through
+JA_PARITY_RECORD.  The full-size tokens span each sequence, so queries that
+read every off-diagonal key block feed the comparison.
 
 Every test runs both forms of the block: the residual adds and SwiGLU as
 launches of their own, and fused into the contractions that produce their
@@ -25,12 +27,13 @@ import itertools
 import numpy as np
 import pytest
 
-from gpu_helpers import bf16_bits, rel_frobenius, to_dev_bf16
+from gpu_helpers import bf16_bits, record, rel_frobenius, to_dev_bf16
 from tensor_relational_join_amd import synth
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
-CHAIN_TOL = 1e-2
+CHAIN_TOL = 2e-3
+CHAIN_TOL_FULL = 5e-3  # derived in tests/test_chain_tolerance.py
 
 
 def _pack(orc, rel, bits):
@@ -183,6 +186,7 @@ def test_block_reduced_shapes(orc, fused):
                                batch, seq, heads, fused=fused)
         chain = rel_frobenius(yd, want)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        record("block_reduced_shapes", fused=fused, steps=errs, chain=chain)
         for k, v in errs.items():
             assert v <= TOL, (k, v)
         assert chain <= CHAIN_TOL
@@ -196,15 +200,16 @@ def test_block_full_size(orc, fused):
     blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=5, fused=fused)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
-        toks = [bb * seq + s for bb in range(batch) for s in (0, 1, 63, 100)]
+        toks = [bb * seq + s for bb in range(batch) for s in (0, 1, 100, 500, 1000, 1500, seq - 1)]
         f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
         want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
                                         f["w_down"], batch, seq, heads, toks, fused=fused)
         chain = rel_frobenius(yd[toks], want_y)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        record("block_full_size", fused=fused, steps=errs, chain=chain, tokens=len(toks))
         for k, v in errs.items():
             assert v <= TOL, (k, v)
-        assert chain <= CHAIN_TOL
+        assert chain <= CHAIN_TOL_FULL
     finally:
         blk.close()
 
@@ -221,6 +226,7 @@ def test_gqa_block_reduced_shapes(orc, fused):
                                batch, seq, heads, kv_heads=kv, fused=fused)
         chain = rel_frobenius(yd, want)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        record("gqa_block_reduced_shapes", fused=fused, steps=errs, chain=chain)
         for k, v in errs.items():
             assert v <= TOL, (k, v)
         assert chain <= CHAIN_TOL
@@ -236,14 +242,15 @@ def test_gqa_block_llama3_8b_shape(orc, fused):
     blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=14, kv_heads=kv, fused=fused)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
-        toks = [bb * seq + s for bb in (0, 5) for s in (0, 1, 63, 100)]
+        toks = [bb * seq + s for bb in (0, 5) for s in (0, 1, 100, 511, 800, seq - 1)]
         f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
         want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
                                         f["w_down"], batch, seq, heads, toks, kv_heads=kv, fused=fused)
         chain = rel_frobenius(yd[toks], want_y)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
+        record("gqa_block_llama3_8b_shape", fused=fused, steps=errs, chain=chain, tokens=len(toks))
         for k, v in errs.items():
             assert v <= TOL, (k, v)
-        assert chain <= CHAIN_TOL
+        assert chain <= CHAIN_TOL_FULL
     finally:
         blk.close()

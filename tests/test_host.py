@@ -542,3 +542,8 @@ def test_calibration_argument_checks(B):
         with pytest.raises(B.JaError) as e:
             B.ja_calibrate_mfma(wgs, iters, sink)
         assert e.value.name == "JA_ERR_ARG"
+    # the copy ceiling: NULL buffers, misaligned pointers or sizes are refused before any launch
+    for src, dst, n in ((0, 256, 16), (256, 0, 16), (264, 256, 16), (256, 264, 16), (256, 512, 24)):
+        with pytest.raises(B.JaError) as e:
+            B.ja_calibrate_copy(src, dst, n)
+        assert e.value.name == "JA_ERR_ARG"
