@@ -474,6 +474,23 @@ ja_status ja_einsum(const ja_spec* spec, const ja_decomp* decomp, const ja_relat
                     const void* const* in_ptrs, int32_t n_in, const ja_relation_desc* out, void* out_ptr,
                     void* dev_ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ja_einsum
+ * with the plan tables and the run's scratch in a static device array of
+ * JA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends, instead of a caller workspace.  The caller passes inputs and
+ * outputs only.  JA_ERR_WORKSPACE (before any HIP call) when the plan needs
+ * more than the array holds -- ja_einsum_workspace_bytes gives the need --
+ * otherwise the errors of ja_einsum.  Blocks until the table upload is done;
+ * the run stays asynchronous on `stream`.  No device memory is allocated or
+ * freed.  Every call on a GPU shares that GPU's array: calls that overlap on
+ * one GPU (other streams, other host threads) race; calls in order on one
+ * stream do not. */
+#define JA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ja_status ja_einsum_noalloc(const ja_spec* spec, const ja_decomp* decomp, const ja_relation_desc* const* in,
+                            const void* const* in_ptrs, int32_t n_in, const ja_relation_desc* out, void* out_ptr,
+                            void* stream);
+
 /* ---- repartition (section 4.3 repartition cost; section 5.3 atoms) ----- */
 
 /* Plan the re-blocking of `src` into `dst`, optionally through `view` (NULL:

@@ -105,6 +105,7 @@ _SIGS = {
     "ja_plan_destroy": (None, [_vp]),
     "ja_einsum_workspace_bytes": (_st, [_vp, _vp, _descpp, _i32, _descp, ctypes.POINTER(_sz)]),
     "ja_einsum": (_st, [_vp, _vp, _descpp, ctypes.POINTER(_vp), _i32, _descp, _vp, _vp, _sz, _vp]),
+    "ja_einsum_noalloc": (_st, [_vp, _vp, _descpp, ctypes.POINTER(_vp), _i32, _descp, _vp, _vp]),
     "ja_repart_create": (_st, [_descp, _descp, _viewp, ctypes.POINTER(_vp)]),
     "ja_repart_count": (_st, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "ja_repart_device_bytes": (_st, [_vp, ctypes.POINTER(_sz)]),
@@ -495,6 +496,15 @@ def ja_einsum(spec: int, decomp: int, ins: Sequence[Relation], in_ptrs: Sequence
               out_ptr: int, dev_ws: int, ws_bytes: int, stream: int = 0):
     _check(_lib.ja_einsum(_vp(spec), _vp(decomp), _desc_array(ins), _ptr_array(in_ptrs), len(ins), out.ptr,
                           _vp(out_ptr), _vp(dev_ws), ws_bytes, _vp(stream)))
+
+
+def ja_einsum_noalloc(spec: int, decomp: int, ins: Sequence[Relation], in_ptrs: Sequence[int], out: Relation,
+                      out_ptr: int, stream: int = 0):
+    _check(_lib.ja_einsum_noalloc(_vp(spec), _vp(decomp), _desc_array(ins), _ptr_array(in_ptrs), len(ins), out.ptr,
+                                  _vp(out_ptr), _vp(stream)))
+
+
+JA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def _view_ptr(view: Optional[ja_view]):

@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libja.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HOST_SOURCES = ["host/core.cpp", "host/plan.cpp", "host/plan_contract.cpp", "host/repart.cpp", "host/djoin.cpp", "host/planner.cpp", "host/dattn.cpp", "host/calib.cpp"]
-HIP_SOURCES = ["hip/gemm.hip", "hip/attention.hip", "hip/stream_ops.hip", "hip/join.hip", "hip/dattn.hip", "hip/calib.hip"]
+HIP_SOURCES = ["hip/gemm.hip", "hip/attention.hip", "hip/stream_ops.hip", "hip/join.hip", "hip/dattn.hip", "hip/calib.hip", "hip/noalloc.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 # gfx950 only; packed-fp32 instructions are disabled in all device code.

@@ -547,3 +547,26 @@ def test_calibration_argument_checks(B):
         with pytest.raises(B.JaError) as e:
             B.ja_calibrate_copy(src, dst, n)
         assert e.value.name == "JA_ERR_ARG"
+
+
+def test_noalloc_einsum_refuses_a_plan_beyond_its_scratch(B):
+    """ja_einsum_noalloc's tables live in a static device array of
+    JA_NOALLOC_SCRATCH_BYTES: a plan that needs more is refused with
+    JA_ERR_WORKSPACE before any HIP call (so this runs without a GPU).  A
+    contraction cut into 100 x 100 x 100 blocks of 8 has 10^6 tuples of 40
+    bytes of table each."""
+    from tensor_relational_join_amd.device import relation_for
+
+    s = B.ja_spec_create("ij,jk->ik", "contract")
+    sp = {c: list(range(0, 801, 8)) for c in "ijk"}
+    d = B.ja_decomp_create(s, [800] * 3, [100] * 3, [sp["i"], sp["j"], sp["k"]])
+    try:
+        ins = [relation_for("ij", sp, B.JA_BF16), relation_for("jk", sp, B.JA_BF16)]
+        out = relation_for("ik", sp, B.JA_BF16)
+        assert B.ja_einsum_workspace_bytes(s, d, ins, out) > B.JA_NOALLOC_SCRATCH_BYTES
+        with pytest.raises(B.JaError) as e:
+            B.ja_einsum_noalloc(s, d, ins, [256, 256], out, 256)
+        assert e.value.name == "JA_ERR_WORKSPACE" and "static scratch" in str(e.value)
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
