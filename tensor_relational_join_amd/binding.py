@@ -15,7 +15,9 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libja.so")
+# JA_LIBJA names another build of the same library (the host-sanitizer build
+# of `python -m tensor_relational_join_amd.build --sanitize`)
+LIB_PATH = os.environ.get("JA_LIBJA") or os.path.join(_HERE, "libja.so")
 
 JA_MAX_RANK = 8
 JA_F32, JA_BF16, JA_F16 = 0, 1, 2
