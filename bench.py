@@ -118,8 +118,11 @@ def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0, fused=Tru
     hd = dm // heads
 
     def flops(n):
+        # the GPU value's convention: attention counted over the kept
+        # (query block, key block) tuples of 128-blocks, so token s is
+        # charged for the (s // 128 + 1) * 128 keys of its kept blocks
         per_tok = 2.0 * (dm * 3 * dm + dm * dm + 3 * dm * ffn)
-        att = sum(2 * 2.0 * (s + 1) * hd * heads for s in range(n))
+        att = sum(2 * 2.0 * (s // 128 + 1) * 128 * hd * heads for s in range(n))
         return n * per_tok + att
 
     n, dt = 8, 0.0
@@ -133,8 +136,19 @@ def cpu_baseline_block(inp, batch, seq, dm, heads, ffn, target_s=12.0, fused=Tru
             break
         n = min(seq, 16 * n, max(n * 2, int(n * target_s / max(dt, 1e-3))))
     return {"value": flops(n) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "float64 oracle block forward on tokens 0..%d of batch 0 (%.1f GFLOP, %.2f s)" %
-                      (n - 1, flops(n) / 1e9, dt)}
+            "cpu": _cpu_model(),
+            "sample": "float64 oracle block forward on tokens 0..%d of batch 0 (%.1f GFLOP counted as the GPU value "
+                      "counts them, over kept 128-block tuples; %.2f s)" % (n - 1, flops(n) / 1e9, dt)}
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _gemm_traffic():

@@ -63,13 +63,15 @@ _u16p = ctypes.POINTER(ctypes.c_uint16)
 
 
 def build(force: bool = False) -> str:
-    """Compile ja_oracle.c into libja_oracle.so with gcc + OpenMP."""
+    """Compile ja_oracle.c into libja_oracle.so with gcc -O3 + OpenMP (no
+    -ffast-math, so every float64 operation keeps its order and rounding; no
+    -march=native, since the library built here also runs on other hosts)."""
     import subprocess
 
     src = os.path.join(_HERE, "ja_oracle.c")
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", src, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", src, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
