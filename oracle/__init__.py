@@ -713,9 +713,18 @@ def _qkv_heads(qkv, batch: int, seq: int, heads: int, kv_heads: int, hd: int):
     return Q, K, V
 
 
+def _rounder(dtype: str):
+    """The rounding of a materialised relation: bf16 or IEEE half, nearest even."""
+    if dtype == "bf16":
+        return round_bf16
+    if dtype == "f16":
+        return round_f16
+    raise ValueError("dtype is 'bf16' or 'f16'")
+
+
 def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
                 eps: float = 1e-6, return_intermediates: bool = False, kv_heads: Optional[int] = None,
-                fused: bool = False):
+                fused: bool = False, dtype: str = "bf16"):
     """Float64 reference of one transformer block on bf16 inputs, with every
     materialised relation rounded to bf16.  x [batch*seq, d]; w_qkv is
     [d, (heads + 2 kv_heads) hd] = [W_q | W_k | W_v] with head h in columns
@@ -727,11 +736,14 @@ def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: in
     fused: the block whose residual adds and SwiGLU are 1:1 joins applied
     inside the producing contractions, so the output projection, the gate
     and up projections and the down projection are never materialised and
-    are not rounded; every relation that is written still is."""
+    are not rounded; every relation that is written still is.
+
+    dtype: the format every materialised relation is rounded to, "bf16" or
+    "f16" (IEEE half; the pages run their blocks in FP16, section 6.1)."""
     T, Dm = x.shape
     hd = Dm // heads
     kv_heads = heads if kv_heads is None else kv_heads
-    r = round_bf16
+    r = _rounder(dtype)
     rc = (lambda v: v) if fused else r  # contraction outputs consumed by a 1:1 join
     h1 = r(rmsnorm(x, g1, eps))
     qkv = r(matmul(h1, w_qkv))
@@ -752,7 +764,8 @@ def llama_block(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: in
 
 
 def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, seq: int, heads: int,
-                       tokens, eps: float = 1e-6, kv_heads: Optional[int] = None, fused: bool = False):
+                       tokens, eps: float = 1e-6, kv_heads: Optional[int] = None, fused: bool = False,
+                       dtype: str = "bf16"):
     """The same block as `llama_block`, evaluated only at the listed tokens
     (t = b*seq + s).  Keys and values are formed for every position up to the
     largest listed s of each batch, as causal attention needs them.  Every
@@ -762,7 +775,7 @@ def llama_block_tokens(x, g1, w_qkv, w_o, g2, w_gate, w_up, w_down, batch: int, 
     T, Dm = x.shape
     hd = Dm // heads
     kv_heads = heads if kv_heads is None else kv_heads
-    r = round_bf16
+    r = _rounder(dtype)
     rc = (lambda v: v) if fused else r
     tokens = np.asarray(tokens, dtype=np.int64)
     y = np.empty((tokens.size, Dm))

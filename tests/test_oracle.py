@@ -589,6 +589,34 @@ def test_fused_block_rounding_points(orc):
     assert np.linalg.norm(y - yu) <= 2.0 ** -7 * np.linalg.norm(yu)
 
 
+def test_block_in_ieee_half(orc):
+    """The block with every materialised relation rounded to IEEE half
+    instead of bf16.  Half keeps 11 significant bits to bf16's 8: against
+    the same chain with no rounding at all, the half block sits roughly 8
+    times closer than the bf16 block (a chain still rounding to bf16
+    somewhere would not), and both are within a few bf16 roundings of it;
+    every relation it writes is a half value.  Token rows agree with the
+    full form bit for bit."""
+    w, batch, seq, heads = _tiny_block(7, T=64, Dm=16, heads=2, F=12, batch=2)
+    yb = orc.llama_block(**w, batch=batch, seq=seq, heads=heads)
+    yh, mid = orc.llama_block(**w, batch=batch, seq=seq, heads=heads, dtype="f16", return_intermediates=True)
+    for k in ("h1", "qkv", "O", "x2", "h2", "f"):
+        assert np.array_equal(mid[k], orc.round_f16(mid[k]))
+    assert np.array_equal(yh, orc.round_f16(yh)) and not np.array_equal(yh, orc.round_bf16(yh))
+    # the chain with no rounding: the same formulas with the identity as rounding
+    saved = orc.round_bf16
+    try:
+        orc.round_bf16 = lambda v: np.asarray(v, dtype=np.float64)
+        y0 = orc.llama_block(**w, batch=batch, seq=seq, heads=heads)
+    finally:
+        orc.round_bf16 = saved
+    eb, eh = np.linalg.norm(yb - y0), np.linalg.norm(yh - y0)
+    assert 3.0 * eh < eb <= 2.0 ** -5 * np.linalg.norm(y0)
+    toks = [0, 5, seq - 1, seq + 3]
+    yt = orc.llama_block_tokens(**w, batch=batch, seq=seq, heads=heads, tokens=toks, dtype="f16")
+    assert np.array_equal(yt, yh[toks])
+
+
 def test_gqa_block_equals_mha_block_on_expanded_weights(orc):
     """Grouped-query block (4 query heads over 2 key-value heads, section
     3.3): the same as the multi-head block whose W_k and W_v repeat each
