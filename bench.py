@@ -46,11 +46,12 @@ def _eq(n, q):
     return p
 
 
-def _bits_to_dev(bits):
+def _bits_to_dev(bits, dtype: str = "bf16"):
     import numpy as np
     import torch
 
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).ravel()).view(torch.bfloat16).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).ravel())
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).cuda()
 
 
 def _stats(ms_list):
@@ -177,6 +178,16 @@ BLOCKS = {
     "block": dict(name="llama7b_shaped_block", batch=4, seq=2048, dm=4096, heads=32, kv_heads=32, ffn=11008),
     "block_gqa": dict(name="llama3_8b_shaped_block_gqa", batch=8, seq=1024, dm=4096, heads=32, kv_heads=8,
                       ffn=14336),
+    # the same blocks in IEEE half (the pages run their blocks in FP16), and the pages' single-sequence
+    # workloads of the LLaMA-3-8B-like block: 1,024 and 8,192 tokens
+    "block_f16": dict(name="llama7b_shaped_block_f16", batch=4, seq=2048, dm=4096, heads=32, kv_heads=32,
+                      ffn=11008, dtype="f16"),
+    "block_gqa_f16": dict(name="llama3_8b_shaped_block_gqa_f16", batch=8, seq=1024, dm=4096, heads=32, kv_heads=8,
+                          ffn=14336, dtype="f16"),
+    "block_gqa_1k_f16": dict(name="llama3_8b_shaped_block_gqa_1x1024_f16", batch=1, seq=1024, dm=4096, heads=32,
+                             kv_heads=8, ffn=14336, dtype="f16"),
+    "block_gqa_8k_f16": dict(name="llama3_8b_shaped_block_gqa_1x8192_f16", batch=1, seq=8192, dm=4096, heads=32,
+                             kv_heads=8, ffn=14336, dtype="f16"),
 }
 # each block also runs with the residual adds and SwiGLU as separate 1:1
 # join launches (every projection written) instead of fused into the
@@ -191,16 +202,19 @@ def bench_block(args):
     from tensor_relational_join_amd.block import LlamaBlock
     from tensor_relational_join_amd.device import alloc
 
+    from tensor_relational_join_amd.binding import JA_BF16, JA_F16
+
     cfg = BLOCKS[args.workload]
     batch, seq, dm, heads, kv, ffn = (cfg[k] for k in ("batch", "seq", "dm", "heads", "kv_heads", "ffn"))
     fused = cfg.get("fused", True)
-    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv, fused=fused)
+    dt = cfg.get("dtype", "bf16")
+    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv, fused=fused, dtype=JA_F16 if dt == "f16" else JA_BF16)
     GEMMS = blk.gemms
-    inp = synth.llama_block_inputs(5, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols)
-    x = blk.materialize(_bits_to_dev(inp["x"]), blk.x_rel)
-    w = {k: blk.materialize(_bits_to_dev(inp[k]), rel) for k, rel in blk.w_rel.items()}
-    w["g1"] = blk.materialize(_bits_to_dev(inp["g1"]), blk.g_rel)
-    w["g2"] = blk.materialize(_bits_to_dev(inp["g2"]), blk.ops["norm2"].in_rels[1])
+    inp = synth.llama_block_inputs(5, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols, dtype=dt)
+    x = blk.materialize(_bits_to_dev(inp["x"], dt), blk.x_rel)
+    w = {k: blk.materialize(_bits_to_dev(inp[k], dt), rel) for k, rel in blk.w_rel.items()}
+    w["g1"] = blk.materialize(_bits_to_dev(inp["g1"], dt), blk.g_rel)
+    w["g2"] = blk.materialize(_bits_to_dev(inp["g2"], dt), blk.ops["norm2"].in_rels[1])
     y = alloc(blk.y_rel)
     flops = blk.flops()
     total_flops = sum(flops.values())
@@ -246,7 +260,7 @@ def bench_block(args):
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": batch, "seq_len": seq, "d_model": dm,
                    "heads": heads, "kv_heads": kv, "head_dim": 128, "ffn": ffn, "parallelism": "single GPU",
                    "adds_and_swiglu": "fused into the contractions" if fused else "separate launches"},
@@ -787,7 +801,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block",
-                    choices=["block", "block_gqa", "block_unfused", "block_gqa_unfused", "configs", "ffn",
+                    choices=sorted(BLOCKS) + ["configs", "ffn",
                              "attention", "norm_swiglu", "gqa", "copy", "join", "plans", "f16", "varlen",
                              "ceilings"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -36,6 +36,9 @@ kv_heads), the shape of the pages' own LLaMA-3-8B-like blocks:
 With t unsplit, the three column blocks of the projection's output are
 three contiguous [t, *] arrays, each re-blocked on its own.
 
+Every relation is bf16, or IEEE half with dtype=JA_F16 (the pages run
+their blocks in FP16, section 6.1); the contractions accumulate in fp32.
+
 With fused=True the two residual adds and SwiGLU are 1:1 joins applied by
 the producing contractions to each aggregated block before it is written,
 and the gate and up projections are one contraction whose weight pairs the
@@ -55,7 +58,8 @@ from typing import Dict, List, Optional
 import torch
 
 from . import binding as B
-from .device import Op, Repart, alloc, equal_splits
+from .device import Op as _Op
+from .device import Repart, alloc, equal_splits
 
 # the steps in execution order, and the contractions among them
 STEPS = ["norm1", "qkv", "to_heads", "attn", "to_tokens", "oproj", "add1", "norm2", "gate", "up", "swiglu",
@@ -67,9 +71,13 @@ FUSED_GEMMS = ["qkv", "oproj_add", "gate_up", "down_add"]
 
 class LlamaBlock:
     def __init__(self, batch: int = 4, seq: int = 2048, dm: int = 4096, heads: int = 32, ffn: int = 11008,
-                 eps: float = 1e-6, device="cuda", kv_heads: Optional[int] = None, fused: bool = False):
+                 eps: float = 1e-6, device="cuda", kv_heads: Optional[int] = None, fused: bool = False,
+                 dtype: int = B.JA_BF16):
         if dm % heads or dm // heads != 128 or seq % 128:
             raise ValueError("the attention kernel needs head_dim 128 and 128-multiples of seq")
+        if dtype not in (B.JA_BF16, B.JA_F16):
+            raise ValueError("the block's relations are bf16 or IEEE half")
+        self.dtype = dtype
         kv = heads if kv_heads is None else kv_heads
         if kv <= 0 or heads % kv:
             raise ValueError("kv_heads must divide heads")
@@ -88,6 +96,11 @@ class LlamaBlock:
         ep = "eps=%r" % eps
         nb = seq // 128
         self.ops: Dict[str, Op] = {}
+
+        def Op(einsum, op, splits, params="", device="cuda"):  # noqa: N802 -- every relation in the block's dtype
+            n_in = len(einsum.split("->")[0].split(","))
+            return _Op(einsum, op, splits, params, [dtype] * n_in, dtype, device=device)
+
         self.ops["norm1"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
         if not self.gqa:
             self.ops["qkv"] = Op("td,dn->tn", "contract", {"t": t2, "d": d2, "n": equal_splits(3 * dm, 2)},
@@ -121,7 +134,7 @@ class LlamaBlock:
         # token-major <-> head-major re-blockings around attention
         self.rp: Dict[str, Repart] = {}
         if not self.gqa:
-            heads_rel = B.Relation((3, batch, heads, seq, self.hd), nblk=(3, batch, heads, nb, 1), dtype=B.JA_BF16)
+            heads_rel = B.Relation((3, batch, heads, seq, self.hd), nblk=(3, batch, heads, nb, 1), dtype=dtype)
             self.rp["to_heads"] = Repart(self.ops["qkv"].out_rel, heads_rel,
                                          B.make_view((batch, seq, 3, heads, self.hd), (2, 0, 3, 1, 4)),
                                          device=device)
@@ -131,9 +144,9 @@ class LlamaBlock:
         else:
             rep = heads // kv
             q_rel, k_rel, v_rel = self.ops["attn"].in_rels
-            self.part_rel = {"q": B.Relation((T, dm), nblk=(1, 1), dtype=B.JA_BF16),
-                             "k": B.Relation((T, kvd), nblk=(1, 1), dtype=B.JA_BF16),
-                             "v": B.Relation((T, kvd), nblk=(1, 1), dtype=B.JA_BF16)}
+            self.part_rel = {"q": B.Relation((T, dm), nblk=(1, 1), dtype=dtype),
+                             "k": B.Relation((T, kvd), nblk=(1, 1), dtype=dtype),
+                             "v": B.Relation((T, kvd), nblk=(1, 1), dtype=dtype)}
             self.rp["to_q"] = Repart(self.part_rel["q"], q_rel,
                                      B.make_view((batch, seq, kv, rep, self.hd), (0, 2, 3, 1, 4)), device=device)
             for name, rel in (("k", k_rel), ("v", v_rel)):
@@ -255,7 +268,7 @@ class LlamaBlock:
 
     # ---------------------------------------------------------------- inputs
     def materialize(self, dense: torch.Tensor, rel: B.Relation) -> torch.Tensor:
-        """Copy a dense row-major bf16 device tensor into `rel`'s blocking
+        """Copy a dense row-major device tensor (the block's dtype) into `rel`'s blocking
         with ja_repartition (a dense tensor is the relation with one block)."""
         src = B.Relation(rel.shape, nblk=[1] * len(rel.shape), dtype=rel.dtype)
         out = alloc(rel, dense.device)

@@ -134,8 +134,9 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
 LLAMA_BLOCK_STREAMS = ["x", "g1", "w_qkv", "w_o", "g2", "w_gate", "w_up", "w_down"]
 
 
-def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int, qkv_cols: Optional[int] = None) -> dict:
-    """bf16 bit patterns of one block's inputs: x ~ N(0,1) [batch*seq, dm];
+def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int, qkv_cols: Optional[int] = None,
+                       dtype: str = "bf16") -> dict:
+    """bf16 (dtype "f16": IEEE half) bit patterns of one block's inputs: x ~ N(0,1) [batch*seq, dm];
     gains ~ N(1, 0.1) [dm]; weights ~ N(0, 0.02): w_qkv [dm, qkv_cols] (= [W_q
     | W_k | W_v]; 3 dm columns unless given, fewer with grouped key-value
     heads), w_o [dm, dm], w_gate and w_up [dm, ffn], w_down [ffn, dm], and
@@ -152,7 +153,8 @@ def llama_block_inputs(seed: int, batch: int, seq: int, dm: int, ffn: int, qkv_c
             mean, std = 1.0, 0.1
         else:
             mean, std = 0.0, 0.02
-        out[name] = normal_bf16(seed, i, shapes[name], mean=mean, std=std)
+        draw = normal_f16 if dtype == "f16" else normal_bf16
+        out[name] = draw(seed, i, shapes[name], mean=mean, std=std)
     # the same weights laid out for a gate-and-up contraction: [dm, ffn, 2],
     # the gate weight then the up weight of each column side by side
     out["w_gu"] = np.ascontiguousarray(np.stack([out["w_gate"], out["w_up"]], axis=2))

@@ -27,7 +27,7 @@ import itertools
 import numpy as np
 import pytest
 
-from gpu_helpers import bf16_bits, record, rel_frobenius, to_dev_bf16
+from gpu_helpers import bf16_bits, record, rel_frobenius, to_dev_bf16, to_dev_f16
 from tensor_relational_join_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -36,39 +36,45 @@ CHAIN_TOL = 2e-3
 CHAIN_TOL_FULL = 5e-3  # derived in tests/test_chain_tolerance.py
 
 
-def _pack(orc, rel, bits):
-    return to_dev_bf16(orc.Relation(rel.shape, rel.splits).pack(bits))
+def _fmt(orc, dt):
+    """(decode, round, upload) of the block's 16-bit format: "bf16" or "f16"."""
+    if dt == "f16":
+        return orc.f16_to_f64, orc.round_f16, to_dev_f16
+    return orc.bf16_to_f64, orc.round_bf16, to_dev_bf16
 
 
-def _unpack(orc, rel, t, as_bits=False):
-    bits = orc.Relation(rel.shape, rel.splits).unpack(bf16_bits(t))
-    return bits if as_bits else orc.bf16_to_f64(bits)
-
-
-def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False):
+def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False, dt="bf16"):
     import torch
 
+    from tensor_relational_join_amd.binding import JA_BF16, JA_F16
     from tensor_relational_join_amd.block import LlamaBlock
     from tensor_relational_join_amd.device import alloc
 
-    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv_heads, fused=fused)
-    inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols)
-    x = _pack(orc, blk.x_rel, inp["x"])
-    w = {k: _pack(orc, rel, inp[k]) for k, rel in blk.w_rel.items()}
-    w["g1"] = _pack(orc, blk.g_rel, inp["g1"])
-    w["g2"] = _pack(orc, blk.ops["norm2"].in_rels[1], inp["g2"])
+    put = _fmt(orc, dt)[2]
+    pack = lambda rel, bits: put(orc.Relation(rel.shape, rel.splits).pack(bits))  # noqa: E731
+    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv_heads, fused=fused,
+                     dtype=JA_F16 if dt == "f16" else JA_BF16)
+    inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols, dtype=dt)
+    x = pack(blk.x_rel, inp["x"])
+    w = {k: pack(rel, inp[k]) for k, rel in blk.w_rel.items()}
+    w["g1"] = pack(blk.g_rel, inp["g1"])
+    w["g2"] = pack(blk.ops["norm2"].in_rels[1], inp["g2"])
     y = alloc(blk.y_rel)
     blk.forward(x, w, y)
     torch.cuda.synchronize()
     return blk, inp, x, y
 
 
-def _check_steps(orc, blk, inp, y, sampled: bool):
+def _check_steps(orc, blk, inp, y, sampled: bool, dt="bf16"):
     """Each step against the oracle on the GPU's inputs to that step.
     Returns {step: error}; repartitions report 0.0 when bit-exact."""
     o, b = blk.ops, blk.buf
     batch, seq, dm, heads, ffn, T = blk.batch, blk.seq, blk.dm, blk.heads, blk.ffn, blk.T
-    f64 = orc.bf16_to_f64
+    f64, rnd, _ = _fmt(orc, dt)
+
+    def _unpack(orc, rel, t):
+        return f64(orc.Relation(rel.shape, rel.splits).unpack(bf16_bits(t)))
+
     rng = np.random.default_rng(2)
     errs = {}
 
@@ -88,7 +94,7 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
                 want = prod(f64(inp[w_name]))
             if residual is not None:
                 want = orc.add(want, residual[pts[:, 0], pts[:, 1]])
-            errs[name] = rel_frobenius(got[pts[:, 0], pts[:, 1]], orc.round_bf16(want))
+            errs[name] = rel_frobenius(got[pts[:, 0], pts[:, 1]], rnd(want))
         else:
             if w_name == "w_gu":
                 want = orc.contract_swiglu("td,dfc->tf", A, f64(inp["w_gu"]))
@@ -96,11 +102,11 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
                 want = orc.contract_residual("ij,jk->ik", A, f64(inp[w_name]), residual)
             else:
                 want = orc.matmul(A, f64(inp[w_name]))
-            errs[name] = rel_frobenius(got, orc.round_bf16(want))
+            errs[name] = rel_frobenius(got, rnd(want))
 
     xd = f64(inp["x"])
     h1 = _unpack(orc, o["norm1"].out_rel, b["h1"])
-    errs["norm1"] = rel_frobenius(h1, orc.round_bf16(orc.rmsnorm(xd, f64(inp["g1"]), blk.eps)))
+    errs["norm1"] = rel_frobenius(h1, rnd(orc.rmsnorm(xd, f64(inp["g1"]), blk.eps)))
     N = blk.qkv_cols
     contract("qkv", o["norm1"].out_rel, b["h1"], "w_qkv", o["qkv"].out_rel, b["qkv"], N,
              dm if blk.gqa else N // 2)
@@ -137,7 +143,7 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
                          for s in ss])
     else:
         rows = np.array(list(itertools.product(range(batch), range(heads), range(seq))))
-    want = orc.round_bf16(orc.attention_rows(Qd, Kd, Vd, rows, 1.0 / np.sqrt(128.0), True))
+    want = rnd(orc.attention_rows(Qd, Kd, Vd, rows, 1.0 / np.sqrt(128.0), True))
     errs["attn"] = rel_frobenius(Od[rows[:, 0], rows[:, 1], rows[:, 2]], want)
     oproj = o["oproj_add" if blk.fused else "oproj"]
     ar, orl = o["attn"].out_rel, oproj.in_rels[0]
@@ -151,9 +157,9 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
     else:
         contract("oproj", orl, b["o"], "w_o", o["oproj"].out_rel, b["a"], dm, dm // 2)
         x2 = _unpack(orc, o["add1"].out_rel, b["x2"])
-        errs["add1"] = rel_frobenius(x2, orc.round_bf16(xd + _unpack(orc, o["oproj"].out_rel, b["a"])))
+        errs["add1"] = rel_frobenius(x2, rnd(xd + _unpack(orc, o["oproj"].out_rel, b["a"])))
     h2 = _unpack(orc, o["norm2"].out_rel, b["h2"])
-    errs["norm2"] = rel_frobenius(h2, orc.round_bf16(orc.rmsnorm(x2, f64(inp["g2"]), blk.eps)))
+    errs["norm2"] = rel_frobenius(h2, rnd(orc.rmsnorm(x2, f64(inp["g2"]), blk.eps)))
     if blk.fused:
         contract("gate_up", o["norm2"].out_rel, b["h2"], "w_gu", o["gate_up"].out_rel, b["f"], ffn, ffn // 4)
         f_rel = o["gate_up"].out_rel
@@ -161,7 +167,7 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
         contract("gate", o["norm2"].out_rel, b["h2"], "w_gate", o["gate"].out_rel, b["gt"], ffn, ffn // 4)
         contract("up", o["norm2"].out_rel, b["h2"], "w_up", o["up"].out_rel, b["up"], ffn, ffn // 4)
         fa = _unpack(orc, o["swiglu"].out_rel, b["f"])
-        errs["swiglu"] = rel_frobenius(fa, orc.round_bf16(orc.swiglu(_unpack(orc, o["gate"].out_rel, b["gt"]),
+        errs["swiglu"] = rel_frobenius(fa, rnd(orc.swiglu(_unpack(orc, o["gate"].out_rel, b["gt"]),
                                                                      _unpack(orc, o["up"].out_rel, b["up"]))))
         f_rel = o["swiglu"].out_rel
     if blk.fused:
@@ -170,23 +176,44 @@ def _check_steps(orc, blk, inp, y, sampled: bool):
     else:
         contract("down", f_rel, b["f"], "w_down", o["down"].out_rel, b["dn"], dm, dm // 2)
         yd = _unpack(orc, o["add2"].out_rel, y)
-        errs["add2"] = rel_frobenius(yd, orc.round_bf16(x2 + _unpack(orc, o["down"].out_rel, b["dn"])))
+        errs["add2"] = rel_frobenius(yd, rnd(x2 + _unpack(orc, o["down"].out_rel, b["dn"])))
     assert np.isfinite(yd).all()
     return errs, yd
 
 
+def _chain(orc, blk, inp, yd, toks, fused, dt):
+    """The oracle's own chain from the block inputs, at the listed tokens
+    (all of them when toks is None), against the GPU's block output."""
+    dec = _fmt(orc, dt)[0]
+    f = {k: dec(v) for k, v in inp.items()}
+    args = (f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"], blk.batch, blk.seq,
+            blk.heads)
+    kw = dict(kv_heads=blk.kv_heads, fused=fused, dtype=dt)
+    if toks is None:
+        return rel_frobenius(yd, orc.llama_block(*args, **kw))
+    return rel_frobenius(yd[toks], orc.llama_block_tokens(*args, toks, **kw))
+
+
+REDUCED = [  # (name, batch, seq, dm, heads, kv_heads, ffn, seed, dtype)
+    ("mha", 2, 256, 256, 2, 2, 704, 11, "bf16"),
+    ("mha_f16", 2, 256, 256, 2, 2, 704, 15, "f16"),
+    ("gqa", 2, 256, 1024, 8, 2, 768, 13, "bf16"),
+    ("gqa_f16", 1, 384, 1024, 8, 2, 768, 16, "f16"),
+]
+
+
 @pytest.mark.parametrize("fused", [False, True])
-def test_block_reduced_shapes(orc, fused):
-    batch, seq, dm, heads, ffn = 2, 256, 256, 2, 704
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=11, fused=fused)
+@pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
+def test_block_reduced_shapes(orc, case, fused):
+    """Every step and the whole chain compared in full (the chain at the
+    per-step bar)."""
+    name, batch, seq, dm, heads, kv, ffn, seed, dt = case
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=seed, kv_heads=kv, fused=fused, dt=dt)
     try:
-        errs, yd = _check_steps(orc, blk, inp, y, sampled=False)
-        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
-        want = orc.llama_block(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"],
-                               batch, seq, heads, fused=fused)
-        chain = rel_frobenius(yd, want)
+        errs, yd = _check_steps(orc, blk, inp, y, sampled=False, dt=dt)
+        chain = _chain(orc, blk, inp, yd, None, fused, dt)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
-        record("block_reduced_shapes", fused=fused, steps=errs, chain=chain)
+        record("block_reduced_shapes", case=name, fused=fused, steps=errs, chain=chain)
         for k, v in errs.items():
             assert v <= TOL, (k, v)
         assert chain <= CHAIN_TOL
@@ -194,61 +221,32 @@ def test_block_reduced_shapes(orc, fused):
         blk.close()
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_block_full_size(orc, fused):
-    batch, seq, dm, heads, ffn = 4, 2048, 4096, 32, 11008
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=5, fused=fused)
-    try:
-        errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
-        toks = [bb * seq + s for bb in range(batch) for s in (0, 1, 100, 500, 1000, 1500, seq - 1)]
-        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
-        want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
-                                        f["w_down"], batch, seq, heads, toks, fused=fused)
-        chain = rel_frobenius(yd[toks], want_y)
-        print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
-        record("block_full_size", fused=fused, steps=errs, chain=chain, tokens=len(toks))
-        for k, v in errs.items():
-            assert v <= TOL, (k, v)
-        assert chain <= CHAIN_TOL_FULL
-    finally:
-        blk.close()
+FULL = [  # (name, batch, seq, dm, heads, kv_heads, ffn, seed, dtype, sampled positions)
+    # the LLaMA-7B-shaped block the bench times
+    ("llama7b_4x2048", 4, 2048, 4096, 32, 32, 11008, 5, "bf16", (0, 1, 100, 500, 1000, 1500, 2047)),
+    # the pages' LLaMA-3-8B-like blocks (32 query over 8 key-value heads, FFN 14,336): 8 x 1,024 tokens in
+    # bf16 and in FP16 (the pages' precision), and single sequences of 1,024 and 8,192 tokens in FP16
+    ("llama3_8b_8x1024", 8, 1024, 4096, 32, 8, 14336, 14, "bf16", (0, 1, 100, 511, 800, 1023)),
+    ("llama3_8b_8x1024_f16", 8, 1024, 4096, 32, 8, 14336, 17, "f16", (0, 1, 100, 511, 800, 1023)),
+    ("llama3_8b_1x1024_f16", 1, 1024, 4096, 32, 8, 14336, 18, "f16", (0, 1, 100, 511, 800, 1023)),
+    ("llama3_8b_1x8192_f16", 1, 8192, 4096, 32, 8, 14336, 19, "f16", (0, 1, 129, 2047, 4000, 6500, 8191)),
+]
 
 
 @pytest.mark.parametrize("fused", [False, True])
-def test_gqa_block_reduced_shapes(orc, fused):
-    """Grouped-query block: 8 query heads over 2 key-value heads."""
-    batch, seq, dm, heads, kv, ffn = 2, 256, 1024, 8, 2, 768
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=13, kv_heads=kv, fused=fused)
+@pytest.mark.parametrize("case", FULL, ids=[c[0] for c in FULL])
+def test_block_full_size(orc, case, fused):
+    """Every step at full size (sampled outputs for the contractions and
+    attention, full tensors otherwise, repartitions bit-exact) and the chain
+    at tokens spanning each sequence."""
+    name, batch, seq, dm, heads, kv, ffn, seed, dt, pos = case
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=seed, kv_heads=kv, fused=fused, dt=dt)
     try:
-        errs, yd = _check_steps(orc, blk, inp, y, sampled=False)
-        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
-        want = orc.llama_block(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"],
-                               batch, seq, heads, kv_heads=kv, fused=fused)
-        chain = rel_frobenius(yd, want)
+        errs, yd = _check_steps(orc, blk, inp, y, sampled=True, dt=dt)
+        toks = [bb * seq + s for bb in sorted({0, batch // 2, batch - 1}) for s in pos]
+        chain = _chain(orc, blk, inp, yd, toks, fused, dt)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
-        record("gqa_block_reduced_shapes", fused=fused, steps=errs, chain=chain)
-        for k, v in errs.items():
-            assert v <= TOL, (k, v)
-        assert chain <= CHAIN_TOL
-    finally:
-        blk.close()
-
-
-@pytest.mark.parametrize("fused", [False, True])
-def test_gqa_block_llama3_8b_shape(orc, fused):
-    """The pages' LLaMA-3-8B-like block: d 4096, 32 query heads over 8
-    key-value heads, FFN 14,336, 8 sequences of 1,024 tokens."""
-    batch, seq, dm, heads, kv, ffn = 8, 1024, 4096, 32, 8, 14336
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=14, kv_heads=kv, fused=fused)
-    try:
-        errs, yd = _check_steps(orc, blk, inp, y, sampled=True)
-        toks = [bb * seq + s for bb in (0, 5) for s in (0, 1, 100, 511, 800, seq - 1)]
-        f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
-        want_y = orc.llama_block_tokens(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"],
-                                        f["w_down"], batch, seq, heads, toks, kv_heads=kv, fused=fused)
-        chain = rel_frobenius(yd[toks], want_y)
-        print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
-        record("gqa_block_llama3_8b_shape", fused=fused, steps=errs, chain=chain, tokens=len(toks))
+        record("block_full_size", case=name, fused=fused, steps=errs, chain=chain, tokens=len(toks))
         for k, v in errs.items():
             assert v <= TOL, (k, v)
         assert chain <= CHAIN_TOL_FULL
