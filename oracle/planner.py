@@ -14,6 +14,13 @@ Every function here enumerates: the candidate specs of an operator, the cells
 of its interval grid, and every joint choice of specs.  Nothing is shared with
 the library's planner.
 
+A view (a tensor re-indexed by a reshape and a permutation of axes, e.g.
+token-major projections read as head-major attention inputs) is realised by
+a repartition that moves every element into whatever blocking its consumer
+asks for: it is charged as a repartition on every edge out of it (all its
+elements; one copy launch in the device-time model) and leaves both its
+source's and its consumer's tilings free.
+
 Readings (also in the design notes): candidate specs cut the shardable
 indices into near-equal intervals whose counts multiply to p; a tiling is the
 interval count per dimension; the join sub-cost counts only cells that the
@@ -38,6 +45,7 @@ class Graph:
         self.shapes: List[Tuple[int, ...]] = []
         self.producer: List[Optional[int]] = []
         self.ops: List[dict] = []
+        self.view_of: Dict[int, int] = {}  # view tensor -> the tensor it re-indexes
 
     def input(self, shape) -> int:
         self.shapes.append(tuple(shape))
@@ -64,6 +72,18 @@ class Graph:
                              causal=causal))
         self.shapes.append(tuple(ext[c] for c in out))
         self.producer.append(len(self.ops) - 1)
+        return len(self.shapes) - 1
+
+    def view(self, t: int, shape) -> int:
+        """Tensor t read as `shape` (same element count) after a reshape and
+        a permutation of axes; which ones does not change any cost."""
+        n = 1
+        for e in shape:
+            n *= e
+        assert n == self.numel(t) and t not in self.view_of
+        self.shapes.append(tuple(shape))
+        self.producer.append(None)
+        self.view_of[len(self.shapes) - 1] = t
         return len(self.shapes) - 1
 
     def consumers(self, t: int) -> List[Tuple[int, int]]:
@@ -147,7 +167,9 @@ def plan_cost(g: Graph, plan: Sequence[Dict[str, int]]) -> Tuple[float, float, f
         agg += a
         for s, t in zip(op["ins"], op["inputs"]):
             q = g.producer[t]
-            if q is not None and tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q]):
+            if t in g.view_of:
+                rep += g.numel(t)
+            elif q is not None and tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q]):
                 rep += g.numel(t)
     return rep, join, agg
 
@@ -213,6 +235,9 @@ def piece_cost(g: Graph, plan: Sequence[Optional[Dict[str, int]]], root: int, op
             continue
         for s, t in zip(op["ins"], op["inputs"]):
             q = g.producer[t]
+            if t in g.view_of:
+                cost += g.numel(t)  # a view: one repartition whatever the tilings
+                continue
             if q is None or plan[q] is None:
                 continue  # a computation input, or charged when the producer's piece is planned
             if tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q]):
@@ -352,13 +377,14 @@ def op_device_time(op: dict, counts: Dict[str, int]) -> float:
 
 def plan_device_time(g: Graph, plan: Sequence[Dict[str, int]]) -> float:
     """Every operator's modelled time, plus one copy launch per edge whose
-    tilings differ (each element read and written once, 2 bytes each)."""
+    tilings differ or that leaves a view (each element read and written once,
+    2 bytes each)."""
     total = 0.0
     for i, op in enumerate(g.ops):
         total += op_device_time(op, plan[i])
         for s, t in zip(op["ins"], op["inputs"]):
             q = g.producer[t]
-            if q is not None and tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q]):
+            if t in g.view_of or (q is not None and tiling(s, plan[i]) != tiling(g.ops[q]["out"], plan[q])):
                 total += LAUNCH_US + 2 * 2 * g.numel(t) / COPY_BPS * 1e6
     return total
 

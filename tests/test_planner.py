@@ -107,6 +107,58 @@ def _ffn_desc(T=64, D=32, F=48):
     return inputs, ops
 
 
+def _view_desc():
+    """A projection whose output is read head-major (a view) by an attention
+    and then read back token-major (a view) by a second projection:
+    y = x W1 [T, H*D]; Q = K = V = view(y) [1, H, T, D]; O = attention;
+    o = view(O) [T, H*D]; z = o W2."""
+    T, H, D = 16, 2, 8
+    inputs = [(T, 12), (12, H * D), (H * D, 10)]
+    ops = [("td,dn->tn", "contract", "", [0, 1]),                                     # 3
+           ("VIEW", (1, H, T, D), "", [3]),                                           # 4 (a view)
+           ("bhsd,bhtd,bhtd->bhsd", "attention", "causal=s,t", [4, 4, 4]),            # 5
+           ("VIEW", (T, H * D), "", [5]),                                             # 6 (a view)
+           ("tm,mn->tn", "contract", "", [6, 2])]                                     # 7
+    return inputs, ops
+
+
+def _oracle_graph_v(inputs, ops):
+    g = P.Graph()
+    for s in inputs:
+        g.input(s)
+    for einsum, kind, params, ins in ops:
+        if einsum == "VIEW":
+            g.view(ins[0], kind)
+        else:
+            g.op(einsum, kind, ins, params)
+    return g
+
+
+def test_view_edges_cost_one_repartition_whatever_the_tilings():
+    """A view is realised by a repartition into the consumer's blocking: every
+    edge out of it costs all its elements (three for the attention reading
+    Q, K and V from one view), under every joint choice of specs, and it
+    decouples the operators around it, so the exhaustive optimum is each
+    operator's cheapest join + aggregation plus those fixed charges."""
+    inputs, ops = _view_desc()
+    og = _oracle_graph_v(inputs, ops)
+    views = 3 * 16 * 16 + 16 * 16  # three edges out of the head-major view, one out of the token-major one
+    for p in (2, 4):
+        cands = [P.candidate_specs(op, p) for op in og.ops]
+        for plan in itertools.islice(itertools.product(*cands), 0, None, 7):
+            rep, _, _ = P.plan_cost(og, plan)
+            assert rep == views
+        best, _ = P.brute_force(og, p)
+        assert best == pytest.approx(views + sum(min(sum(P.spec_subcosts(op, c)) for c in cs)
+                                                 for op, cs in zip(og.ops, cands)), rel=1e-12)
+        assert P.piecewise_plan(og, p)[0] == pytest.approx(best, rel=1e-12)
+        # the device model charges one copy launch per view edge on top of the operators
+        plan = [cs[0] for cs in cands]
+        ops_us = sum(P.op_device_time(op, c) for op, c in zip(og.ops, plan))
+        assert P.plan_device_time(og, plan) == pytest.approx(
+            ops_us + 4 * P.LAUNCH_US + 2 * 2 * views / P.COPY_BPS * 1e6, rel=1e-12)
+
+
 def _ffn_graph_oracle():
     inputs, ops = _ffn_desc()
     return _oracle_graph(inputs, ops)
