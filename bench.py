@@ -642,8 +642,11 @@ def bench_plans(args):
     Graphs: the pages' matrix chains B, (M1 M2)((M3 M4) M5) with dimensions
     9,216 / 20,480 / 5,120 / 20,480 / 5,120 / 9,216, and C, M1 (M2 M3) with
     10,240 x 12,288 x 32,768 x 2,048; and the LLaMA-7B-shaped pre-norm FFN
-    with its residual (8,192 tokens, d 4,096, FFN 11,008).  bf16, N(0, 1)
-    inputs scaled by 1/sqrt(fan-in)."""
+    with its residual (8,192 tokens, d 4,096, FFN 11,008); and the whole
+    LLaMA-7B-shaped block (batch 4 x 2,048 tokens, 32 heads of 128, FFN
+    11,008) with its head views, for which the LlamaBlock class's hand
+    decompositions are timed too (under "hand").  bf16, N(0, 1) inputs scaled
+    by 1/sqrt(fan-in) (the block's weights N(0, 0.02^2))."""
     import torch
 
     from tensor_relational_join_amd.binding import JA_PLAN_DEVICE, JA_PLAN_GREEDY, JA_PLAN_OPTIMAL, JA_PLAN_RANDOM
@@ -678,31 +681,49 @@ def bench_plans(args):
         g.op("rd,rd->rd", "add", [dn, x])
         return g
 
+    def block():
+        # the LLaMA-7B-shaped block (batch 4 x 2048, d 4096, 32 heads, FFN 11008) with views around attention
+        from tensor_relational_join_amd.graph import llama_block_graph
+
+        g, _ = llama_block_graph(4, 2048, 4096, 32, 11008)
+        return g
+
     p, nrand = 8, 20
     res = {}
-    for name, make in (("chain_b", chain_b), ("chain_c", chain_c), ("ffn_llama7b", ffn)):
+    for name, make in (("chain_b", chain_b), ("chain_c", chain_c), ("ffn_llama7b", ffn), ("llama7b_block", block)):
         g = make()
         torch.manual_seed(11)
         dense = {}
         for t, shape in enumerate(g.shapes):
-            if g.producer[t] is not None:
+            if g.producer[t] is not None or t in g.views:
                 continue
             x = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
             if len(shape) == 1:  # the RMSNorm gain
                 x.normal_(1.0, 0.1)
-            elif name == "ffn_llama7b" and t == 0:  # the FFN's activations
+            elif name in ("ffn_llama7b", "llama7b_block") and t == 0:  # the activations
                 x.normal_()
+            elif name == "llama7b_block":  # the block's weights
+                x.normal_(0.0, 0.02)
             else:  # a matrix of a chain or a weight: N(0, 1 / fan-in)
                 x.normal_(0.0, float(shape[0]) ** -0.5)
             dense[t] = x
         plans = [("optimal", JA_PLAN_OPTIMAL, 0), ("greedy", JA_PLAN_GREEDY, 0), ("device", JA_PLAN_DEVICE, 0)] + \
                 [("random", JA_PLAN_RANDOM, s) for s in range(nrand)]
+        if name == "llama7b_block":  # the LlamaBlock class's hand decompositions (unfused), beside the selectors
+            plans.append(("hand", None, 0))
         rows = []
         for label, mode, seed in plans:
-            _, plan = g.plan(p, mode, seed)
+            splits = None
+            if label == "hand":
+                from tensor_relational_join_amd.graph import llama_block_hand_splits
+
+                splits = llama_block_hand_splits(g, 4, 2048)
+                plan = [{c: len(v) - 1 for c, v in sp.items()} for sp in splits]
+            else:
+                _, plan = g.plan(p, mode, seed)
             cost = sum(g.cost(plan))
             model_us = g.device_time(plan)
-            run = PlannedRun(g, plan)
+            run = PlannedRun(g, plan, splits=splits)
             try:
                 run.load(dense)
                 for _ in range(args.warmup):
@@ -722,6 +743,10 @@ def bench_plans(args):
             finally:
                 run.close()
         rnd = [r for r in rows if r["plan"] == "random"]
+        hand = [r for r in rows if r["plan"] == "hand"]
+        if hand:
+            res.setdefault("hand", {})[name] = hand[0]
+        rows = [r for r in rows if r["plan"] != "hand"]
         res[name] = {"p": p, "optimal": rows[0], "greedy": rows[1], "device": rows[2],
                      "random_ms_median": float(sorted(r["ms"] for r in rnd)[len(rnd) // 2]),
                      "random_ms_best": min(r["ms"] for r in rnd),

@@ -385,6 +385,17 @@ ja_status ja_graph_add_input(ja_graph* graph, int32_t rank, const int64_t* shape
  * with an epilogue (contract_add, contract_swiglu). */
 ja_status ja_graph_add_op(ja_graph* graph, const ja_spec* spec, const int32_t* inputs, int32_t n_inputs,
                           int32_t* tensor);
+/* A view of `tensor` (a computation input or an operator output, not itself
+ * a view): the tensor re-indexed by `view` (ja_repartition's reshape and
+ * permutation) and read as shape[0..rank), with the same element count
+ * (JA_ERR_SHAPE otherwise); writes its tensor id.  It is realised by a
+ * repartition through the view into whatever blocking each consumer's spec
+ * asks for, so it constrains neither its source's nor its consumers' tilings,
+ * and every edge out of it is charged as one repartition: all its elements
+ * in the proxy, one copy launch in the device model.  (A view is how
+ * token-major projections feed head-major attention, and back.) */
+ja_status ja_graph_add_view(ja_graph* graph, int32_t tensor, const ja_view* view, int32_t rank, const int64_t* shape,
+                            int32_t* out);
 ja_status ja_graph_count(const ja_graph* graph, int32_t* n_ops, int32_t* n_tensors);
 /* Choose a spec for every operator (mode above); *cost (may be NULL) gets
  * the chosen plan's total proxy cost (JA_PLAN_DEVICE: its modelled time in

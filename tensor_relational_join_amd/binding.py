@@ -91,6 +91,7 @@ _SIGS = {
     "ja_graph_destroy": (None, [_vp]),
     "ja_graph_add_input": (_st, [_vp, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
     "ja_graph_add_op": (_st, [_vp, _vp, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
+    "ja_graph_add_view": (_st, [_vp, _i32, ctypes.POINTER(ja_view), _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
     "ja_graph_count": (_st, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "ja_graph_plan": (_st, [_vp, _i32, _i32, ctypes.c_uint64, ctypes.POINTER(ctypes.c_double)]),
     "ja_graph_plan_intervals": (_st, [_vp, _i32, ctypes.POINTER(_i32), _i32]),
@@ -405,6 +406,13 @@ def ja_graph_add_op(graph: int, spec: int, inputs: Sequence[int]) -> int:
     t = _i32()
     _check(_lib.ja_graph_add_op(_vp(graph), _vp(spec), (_i32 * len(inputs))(*inputs), len(inputs), ctypes.byref(t)))
     return t.value
+
+
+def ja_graph_add_view(graph: int, tensor: int, view: ja_view, shape: Sequence[int]) -> int:
+    out = _i32()
+    n = len(shape)
+    _check(_lib.ja_graph_add_view(_vp(graph), tensor, ctypes.byref(view), n, (_i64 * n)(*shape), ctypes.byref(out)))
+    return out.value
 
 
 def ja_graph_count(graph: int):

@@ -3,6 +3,11 @@
 // to minimize the communication-cost proxy of section 4.3, with the dynamic
 // program over output tilings of section 4.2 and the graph cuts of section 4.5.
 //
+// A view (ja_graph_add_view) re-indexes a tensor by a reshape and a
+// permutation of axes; it is realised by a repartition into whatever blocking
+// each consumer asks for, so it frees the tilings on both sides and every
+// edge out of it costs one full repartition.
+//
 // Candidate specs of an operator cut its shardable indices into near-equal
 // intervals whose counts multiply to the processor count p (section 3.3 asks
 // for one function spec per combination of intervals; section 4.3 for
@@ -22,7 +27,8 @@ namespace {
 
 struct GTensor {
     std::vector<int64_t> shape;
-    int producer = -1;                          // operator, or -1 for a computation input
+    int producer = -1;                          // operator, or -1 for a computation input or a view
+    int view_of = -1;                           // a view: the tensor it re-indexes
     std::vector<std::pair<int, int>> consumers;  // (operator, input slot)
     double numel() const {
         double n = 1;
@@ -293,10 +299,20 @@ double rep_cost(const ja_graph* g, int op, int slot, const std::vector<int32_t>&
     return cons_tiling == prod_tiling ? 0.0 : g->t[g->ops[op].inputs[slot]].numel();
 }
 
+double copy_time(double numel) { return DEV_LAUNCH_US + 2.0 * 2.0 * numel / DEV_COPY_BPS * 1e6; }
+
 double rep_time(const ja_graph* g, int op, int slot, const std::vector<int32_t>& cons_tiling,
                 const std::vector<int32_t>& prod_tiling) {
     if (cons_tiling == prod_tiling) return 0.0;
-    return DEV_LAUNCH_US + 2.0 * 2.0 * g->t[g->ops[op].inputs[slot]].numel() / DEV_COPY_BPS * 1e6;
+    return copy_time(g->t[g->ops[op].inputs[slot]].numel());
+}
+
+// An edge out of a view: the re-indexing is a repartition into whatever
+// blocking the consumer asks for, so it costs all the view's elements (one
+// copy launch in the device model) whatever the tilings on either side.
+double view_edge(const ja_graph* g, int op, int slot, bool dev) {
+    const double n = g->t[g->ops[op].inputs[slot]].numel();
+    return dev ? copy_time(n) : n;
 }
 
 }  // namespace
@@ -359,6 +375,35 @@ ja_status ja_graph_add_op(ja_graph* g, const ja_spec* spec, const int32_t* input
     g->ops[id].out = (int)g->t.size() - 1;
     for (int k = 0; k < n_inputs; ++k) g->t[inputs[k]].consumers.push_back({id, k});
     *tensor = (int32_t)g->t.size() - 1;
+    return JA_OK;
+}
+
+ja_status ja_graph_add_view(ja_graph* g, int32_t tensor, const ja_view* view, int32_t rank, const int64_t* shape,
+                            int32_t* out) {
+    if (!g || !view || !shape || !out) return fail(JA_ERR_ARG, "NULL argument");
+    if (tensor < 0 || tensor >= (int32_t)g->t.size()) return fail(JA_ERR_ARG, "unknown tensor");
+    if (g->t[tensor].view_of >= 0) return fail(JA_ERR_UNSUPPORTED, "a view of a view");
+    if (rank < 1 || rank > JA_MAX_RANK || view->rank < 1 || view->rank > JA_MAX_RANK)
+        return fail(JA_ERR_ARG, "rank must be 1..8");
+    double nv = 1, no = 1;
+    std::vector<bool> seen(view->rank, false);
+    for (int i = 0; i < view->rank; ++i) {
+        if (view->shape[i] < 1) return fail(JA_ERR_SHAPE, "view extents must be positive");
+        nv *= (double)view->shape[i];
+        const int pm = view->perm[i];
+        if (pm < 0 || pm >= view->rank || seen[pm]) return fail(JA_ERR_ARG, "view perm is not a permutation");
+        seen[pm] = true;
+    }
+    GTensor o;
+    for (int i = 0; i < rank; ++i) {
+        if (shape[i] < 1) return fail(JA_ERR_SHAPE, "extents must be positive");
+        no *= (double)shape[i];
+        o.shape.push_back(shape[i]);
+    }
+    if (nv != g->t[tensor].numel() || no != nv) return fail(JA_ERR_SHAPE, "a view keeps the element count");
+    o.view_of = tensor;
+    g->t.push_back(o);
+    *out = (int32_t)g->t.size() - 1;
     return JA_OK;
 }
 
@@ -447,6 +492,10 @@ ja_status ja_graph_plan(ja_graph* g, int32_t p, int32_t mode, uint64_t seed, dou
                     pk[ci].assign(op.inputs.size(), {});
                     for (size_t k = 0; k < op.inputs.size(); ++k) {
                         const int tin = op.inputs[k], q = g->t[tin].producer;
+                        if (g->t[tin].view_of >= 0) {  // a view: one repartition, any tiling
+                            if (with_rep) b += view_edge(g, i, (int)k, dev);
+                            continue;
+                        }
                         if (q < 0) continue;  // a computation input: materialised in the blocks asked for
                         if (cut(tin)) {
                             // charged here if its producer is already fixed, else when it is planned
@@ -566,7 +615,10 @@ ja_status ja_graph_cost(const ja_graph* g, const int32_t* const* intervals, doub
         a += pl[i].agg;
         for (size_t k = 0; k < op.inputs.size(); ++k) {
             const int q = g->t[op.inputs[k]].producer;
-            if (q >= 0) r += rep_cost(g, i, (int)k, pl[i].in[k], pl[q].out);
+            if (g->t[op.inputs[k]].view_of >= 0)
+                r += view_edge(g, i, (int)k, false);
+            else if (q >= 0)
+                r += rep_cost(g, i, (int)k, pl[i].in[k], pl[q].out);
         }
     }
     if (repart) *repart = r;
@@ -586,7 +638,10 @@ ja_status ja_graph_device_time(const ja_graph* g, const int32_t* const* interval
         t += pl[i].dev_us;
         for (size_t k = 0; k < op.inputs.size(); ++k) {
             const int q = g->t[op.inputs[k]].producer;
-            if (q >= 0) t += rep_time(g, (int)i, (int)k, pl[i].in[k], pl[q].out);
+            if (g->t[op.inputs[k]].view_of >= 0)
+                t += view_edge(g, (int)i, (int)k, true);
+            else if (q >= 0)
+                t += rep_time(g, (int)i, (int)k, pl[i].in[k], pl[q].out);
         }
     }
     *us = t;

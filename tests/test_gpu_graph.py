@@ -105,3 +105,45 @@ def test_residual_ffn_plans(G, orc):
         for mode, seed in [(JA_PLAN_OPTIMAL, 0), (JA_PLAN_RANDOM, 1), (JA_PLAN_RANDOM, 2)]:
             _, plan = g.plan(p, mode, seed)
             _check_plan(G, orc, g, plan, inputs)
+
+
+def test_llama_block_graph_plans(G, orc):
+    """The LLaMA-shaped block as a graph of the pages' operators with views
+    between the token-major projections and the head-major attention
+    (graph.llama_block_graph), planned on p = 8 by the optimizer, the greedy
+    selector, the device-time model and a random choice, and under the
+    LlamaBlock class's hand decompositions: every plan's block output
+    against the oracle's own block (Q, K and V as the column groups of one
+    fused projection: the same values, rounded at the same points) end to
+    end, at reduced shapes."""
+    import torch
+
+    from tensor_relational_join_amd import synth
+    from tensor_relational_join_amd.binding import JA_PLAN_DEVICE, JA_PLAN_GREEDY, JA_PLAN_OPTIMAL, JA_PLAN_RANDOM
+
+    batch, seq, dm, heads, ffn = 2, 256, 256, 2, 704
+    g, t = G.llama_block_graph(batch, seq, dm, heads, ffn)
+    inp = synth.llama_block_inputs(21, batch, seq, dm, ffn)
+    w = dict(inp)
+    for i, n in enumerate("qkv"):
+        w["w_" + n] = np.ascontiguousarray(inp["w_qkv"][:, i * dm:(i + 1) * dm])
+    dev = {t[n]: torch.from_numpy(np.ascontiguousarray(w[n]).view(np.int16)).view(torch.bfloat16).cuda()
+           for n in ("x", "g1", "w_q", "w_k", "w_v", "w_o", "g2", "w_gate", "w_up", "w_down")}
+    f = {k: orc.bf16_to_f64(v) for k, v in inp.items()}
+    want = orc.llama_block(f["x"], f["g1"], f["w_qkv"], f["w_o"], f["g2"], f["w_gate"], f["w_up"], f["w_down"],
+                           batch, seq, heads)
+    y_op = g.producer[t["y"]]
+    runs = [(mode, seed, None) for mode, seed in ((JA_PLAN_OPTIMAL, 0), (JA_PLAN_GREEDY, 0), (JA_PLAN_DEVICE, 0),
+                                                  (JA_PLAN_RANDOM, 3))]
+    runs.append((None, 0, G.llama_block_hand_splits(g, batch, seq)))
+    for mode, seed, splits in runs:
+        plan = g.plan(8, mode, seed)[1] if splits is None else None
+        run = G.PlannedRun(g, plan, splits=splits)
+        try:
+            run.load(dev)
+            run.run()
+            torch.cuda.synchronize()
+            got = orc.bf16_to_f64(_dense_bits(run.dense_output(y_op)))
+        finally:
+            run.close()
+        assert rel_frobenius(got, want) <= BF16_TOL, (mode, seed, splits is not None)

@@ -115,9 +115,9 @@ def _view_desc():
     T, H, D = 16, 2, 8
     inputs = [(T, 12), (12, H * D), (H * D, 10)]
     ops = [("td,dn->tn", "contract", "", [0, 1]),                                     # 3
-           ("VIEW", (1, H, T, D), "", [3]),                                           # 4 (a view)
+           ("VIEW", (1, H, T, D), ((T, H, D), (1, 0, 2)), [3]),                       # 4 (a view)
            ("bhsd,bhtd,bhtd->bhsd", "attention", "causal=s,t", [4, 4, 4]),            # 5
-           ("VIEW", (T, H * D), "", [5]),                                             # 6 (a view)
+           ("VIEW", (T, H * D), ((H, T, D), (1, 0, 2)), [5]),                         # 6 (a view)
            ("tm,mn->tn", "contract", "", [6, 2])]                                     # 7
     return inputs, ops
 
@@ -157,6 +157,47 @@ def test_view_edges_cost_one_repartition_whatever_the_tilings():
         ops_us = sum(P.op_device_time(op, c) for op, c in zip(og.ops, plan))
         assert P.plan_device_time(og, plan) == pytest.approx(
             ops_us + 4 * P.LAUNCH_US + 2 * 2 * views / P.COPY_BPS * 1e6, rel=1e-12)
+
+
+def test_library_plans_graphs_with_views(B):
+    """The library's planner on the graph with views: its plans (optimal,
+    greedy, device) cost what the oracle says they cost, the optimum is the
+    exhaustive one, and the device model agrees with the oracle's."""
+    inputs, ops = _view_desc()
+    og = _oracle_graph_v(inputs, ops)
+    g = B.ja_graph_create()
+    try:
+        for sh in inputs:
+            B.ja_graph_add_input(g, list(sh))
+        letters = []
+        for einsum, kind, params, ins in ops:
+            if einsum == "VIEW":
+                vshape, perm = params
+                B.ja_graph_add_view(g, ins[0], B.make_view(vshape, perm), list(kind))
+            else:
+                sp = B.ja_spec_create(einsum, kind, params)
+                letters.append(B.ja_spec_letters(sp))
+                B.ja_graph_add_op(g, sp, ins)
+                B.ja_spec_destroy(sp)
+        assert B.ja_graph_count(g) == (3, 8)
+        for p in (2, 4):
+            cost = B.ja_graph_plan(g, p, B.JA_PLAN_OPTIMAL)
+            plan = _lib_plan(B, g, letters)
+            assert cost == pytest.approx(sum(P.plan_cost(og, plan)), rel=1e-12)
+            assert cost == pytest.approx(P.brute_force(og, p)[0], rel=1e-12)
+            B.ja_graph_plan(g, p, B.JA_PLAN_GREEDY)
+            assert B.ja_graph_cost(g) == pytest.approx(P.plan_cost(og, _lib_plan(B, g, letters)), rel=1e-12)
+            us = B.ja_graph_plan(g, p, B.JA_PLAN_DEVICE)
+            assert us == pytest.approx(P.plan_device_time(og, _lib_plan(B, g, letters)), rel=1e-9)
+        # a view must keep the element count and may not re-index another view
+        with pytest.raises(B.JaError) as e:
+            B.ja_graph_add_view(g, 3, B.make_view((16, 2, 8), (1, 0, 2)), [1, 2, 16, 4])
+        assert e.value.name == "JA_ERR_SHAPE"
+        with pytest.raises(B.JaError) as e:
+            B.ja_graph_add_view(g, 4, B.make_view((2, 16, 8), (0, 1, 2)), [32, 8])
+        assert e.value.name == "JA_ERR_UNSUPPORTED"
+    finally:
+        B.ja_graph_destroy(g)
 
 
 def _ffn_graph_oracle():
