@@ -281,6 +281,13 @@ def piecewise_plan(g: Graph, p: int, with_repartition: bool = True) -> Tuple[flo
 # --------------------------------------------------------------------------
 # the device-time model of one MI355X running this library's kernels (the
 # computation awareness the pages leave as future work, section 8)
+#
+# PARITY UNPINNED as a model of the hardware.  The pages define no such
+# model: this one is written out from the library's own kernel design (tile
+# shapes, the half-height last round) with rates measured on those kernels,
+# and it changes with them.  Its closed-form tests pin only its arithmetic
+# (rounds, placement, cuts), so it checks that the library's dynamic program
+# finds the plan this model ranks best, not that the model predicts the GPU.
 # --------------------------------------------------------------------------
 
 CUS = 256

@@ -9,7 +9,8 @@ bf16 tolerance (relative Frobenius <= 2e-3).
 
 End-to-end chain: the block output is also compared with the oracle's own
 chain from the block inputs.  At the reduced shapes it is held to the same
-2e-3.  At full size it is held to CHAIN_TOL_FULL = 5e-3: attention rounds P
+2e-3, and so are the all-half blocks at full size.  The full-size bf16
+blocks are held to CHAIN_TOL_FULL = 5e-3: attention rounds P
 to IEEE half for its P V product, which keeps attention itself within 2e-3
 but changes O enough to flip downstream bf16 roundings, and the FFN carries
 those to y.  The oracle alone shows it (tests/test_chain_tolerance.py): with
@@ -249,6 +250,7 @@ def test_block_full_size(orc, case, fused):
         record("block_full_size", case=name, fused=fused, steps=errs, chain=chain, tokens=len(toks))
         for k, v in errs.items():
             assert v <= TOL, (k, v)
-        assert chain <= CHAIN_TOL_FULL
+        # fp16 P costs the bf16 chain up to 5e-3 at full size; an all-half block keeps the 2e-3 bar
+        assert chain <= (CHAIN_TOL if dt == "f16" else CHAIN_TOL_FULL)
     finally:
         blk.close()
