@@ -251,46 +251,55 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     };
     // V^T[d][key'] <- vr, in fp16 (converted from bf16, moved as is from
     // fp16); key' swaps the middle quads of each 16 keys, matching the order
-    // P^T takes from the S^T accumulators.  Word w of a lane's 4 keys holds
-    // rows 8 dj + 2 w (low halves) and 8 dj + 2 w + 1 (high halves); lanes of
-    // odd dj write the odd row first, so that each write instruction covers
-    // rows of both parities (both halves of the banks).
+    // P^T takes from the S^T accumulators.  Word w of a key's 8 d values holds
+    // rows 8 dj + 2 w (low half) and 8 dj + 2 w + 1 (high half); each write
+    // instruction covers rows of both parities (both halves of the banks), so
+    // lanes of odd dj write the odd row first.  Byte selectors (v_perm_b32)
+    // pick each lane's first and second row out of the words directly.
     int vshift = 0;  // REDO: V staged as V 2^-vshift, O written as O 2^vshift
     auto cvt = [&](float x) -> _Float16 {
         if constexpr (REDO) x = __builtin_amdgcn_ldexpf(x, -vshift);
         return (_Float16)x;
     };
+    const int par = dj & 1;
+    // bf16 half of a word -> its float bits (the half in the top two bytes)
+    const uint32_t sel_f1 = par ? 0x03020c0cu : 0x01000c0cu, sel_f2 = par ? 0x01000c0cu : 0x03020c0cu;
+    // fp16: the same half of two words side by side (first word low)
+    const uint32_t sel_h1 = par ? 0x07060302u : 0x05040100u, sel_h2 = par ? 0x05040100u : 0x07060302u;
     auto store_v = [&](int buf) {
         _Float16* vt = reinterpret_cast<_Float16*>(at_lds + buf * AT_STAGE + AT_KT * D);
         const int hgrp = kg >> 2, q = kg & 3;
         const int qpos = q == 1 ? 2 : (q == 2 ? 1 : q);
         const int c = 2 * hgrp + (qpos >> 1), half = qpos & 1;
-        const int par = dj & 1;
         const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vr[0]);
         const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vr[1]);
         const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vr[2]);
         const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vr[3]);  // words of the 4 keys' 8 d values
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            uint2 lo, hi;  // the 4 keys' fp16 values of rows 8 dj + 2 w and 8 dj + 2 w + 1
+            uint2 first, second;  // the 4 keys' fp16 values of rows 8 dj + 2 w + par and 8 dj + 2 w + (1 - par)
             if constexpr (F16) {
-                const uint32_t mk = 0xffffu;
-                lo = make_uint2((r0[w] & mk) | (r1[w] << 16), (r2[w] & mk) | (r3[w] << 16));
-                hi = make_uint2((r0[w] >> 16) | (r1[w] & 0xffff0000u), (r2[w] >> 16) | (r3[w] & 0xffff0000u));
+                first = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], sel_h1), __builtin_amdgcn_perm(r3[w], r2[w], sel_h1));
+                second = make_uint2(__builtin_amdgcn_perm(r1[w], r0[w], sel_h2), __builtin_amdgcn_perm(r3[w], r2[w], sel_h2));
             } else {
                 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-                const h4 l4 = {cvt(bf16lo_to_f32(r0[w])), cvt(bf16lo_to_f32(r1[w])), cvt(bf16lo_to_f32(r2[w])),
-                               cvt(bf16lo_to_f32(r3[w]))};
-                const h4 h4v = {cvt(bf16hi_to_f32(r0[w])), cvt(bf16hi_to_f32(r1[w])), cvt(bf16hi_to_f32(r2[w])),
-                                cvt(bf16hi_to_f32(r3[w]))};
-                lo = __builtin_bit_cast(uint2, l4);
-                hi = __builtin_bit_cast(uint2, h4v);
+                auto f = [](uint32_t x, uint32_t sel) { return __uint_as_float(__builtin_amdgcn_perm(x, x, sel)); };
+                const h4 a = {cvt(f(r0[w], sel_f1)), cvt(f(r1[w], sel_f1)), cvt(f(r2[w], sel_f1)), cvt(f(r3[w], sel_f1))};
+                const h4 b = {cvt(f(r0[w], sel_f2)), cvt(f(r1[w], sel_f2)), cvt(f(r2[w], sel_f2)), cvt(f(r3[w], sel_f2))};
+                first = __builtin_bit_cast(uint2, a);
+                second = __builtin_bit_cast(uint2, b);
             }
             const int d0 = dj * 8 + 2 * w + par, d1 = dj * 8 + 2 * w + (par ^ 1);
-            *reinterpret_cast<uint2*>(vt + at_voff(d0, c) + half * 4) = par ? hi : lo;
-            *reinterpret_cast<uint2*>(vt + at_voff(d1, c) + half * 4) = par ? lo : hi;
+            *reinterpret_cast<uint2*>(vt + at_voff(d0, c) + half * 4) = first;
+            *reinterpret_cast<uint2*>(vt + at_voff(d1, c) + half * 4) = second;
         }
     };
+    // V^T fragment reads: row 32 dt + lq, chunk (2 kq + g) ^ vswz(32 dt + lq)
+    // = (g ^ vswz(lq)) ^ 2 (kq ^ dt), so four per-lane byte offsets (one per
+    // kq ^ dt) and an immediate per dt address all sixteen reads of a step
+    uint32_t vrd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vrd[e] = (uint32_t)(lq * AT_KT * 2 + ((((g ^ vswz(lq)) ^ (2 * e)) & 7) << 4));
     auto sync_step = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
     if constexpr (REDO) {
@@ -436,7 +445,8 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
                 h8_t vf[D / 32];
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-                    vf[dt] = *reinterpret_cast<const h8_t*>(vt + at_voff(dt * 32 + lq, 2 * kq + g));
+                    vf[dt] = *reinterpret_cast<const h8_t*>(reinterpret_cast<const char*>(vt) + vrd[kq ^ dt] +
+                                                            dt * 32 * AT_KT * 2);
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
                     oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[dt], pf[kq], oacc[dt], 0, 0, 0);

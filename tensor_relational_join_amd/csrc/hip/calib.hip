@@ -2,8 +2,7 @@
 // sustains on a loop of nothing but bf16 MFMAs (no memory traffic, no LDS, no
 // barriers), and the HBM bandwidth a plain streaming copy reaches -- the
 // ceilings the kernels are compared against beside the published peaks.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "dev_common.h"
 
 namespace ja {
 
@@ -46,37 +45,32 @@ hipError_t launch_mfma_loop(int32_t workgroups, int32_t iters, float* sink, hipS
 }
 
 // A streaming copy of n16 16-byte vectors: each thread moves COPY_UNROLL
-// vectors per round, all loaded before any is stored, rounds strided by the
-// whole grid.
+// vectors, all loaded before any is stored, loads and stores non-temporal,
+// one pass with no grid-stride loop (the fastest plain copy among those
+// tried on MI355X: unroll 2 to 8, grids of 4 to 32 workgroups per compute
+// unit, with and without the hint).
 constexpr int COPY_UNROLL = 4;
 
 __global__ __launch_bounds__(CAL_THREADS) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                            int64_t n16) {
-    const int64_t stride = (int64_t)gridDim.x * CAL_THREADS * COPY_UNROLL;
-    for (int64_t base = (int64_t)blockIdx.x * CAL_THREADS * COPY_UNROLL + threadIdx.x; base < n16; base += stride) {
-        uint4 v[COPY_UNROLL];
+    const int64_t base = (int64_t)blockIdx.x * CAL_THREADS * COPY_UNROLL + threadIdx.x;
+    uint4 v[COPY_UNROLL];
 #pragma unroll
-        for (int j = 0; j < COPY_UNROLL; ++j) {
-            const int64_t i = base + (int64_t)j * CAL_THREADS;
-            if (i < n16) v[j] = src[i];
-        }
+    for (int j = 0; j < COPY_UNROLL; ++j) {
+        const int64_t i = base + (int64_t)j * CAL_THREADS;
+        if (i < n16) v[j] = ld_nt(src + i);
+    }
 #pragma unroll
-        for (int j = 0; j < COPY_UNROLL; ++j) {
-            const int64_t i = base + (int64_t)j * CAL_THREADS;
-            if (i < n16) dst[i] = v[j];
-        }
+    for (int j = 0; j < COPY_UNROLL; ++j) {
+        const int64_t i = base + (int64_t)j * CAL_THREADS;
+        if (i < n16) st_nt(dst + i, v[j]);
     }
 }
 
 hipError_t launch_copy(const void* src, void* dst, int64_t n16, hipStream_t stream) {
     if (n16 <= 0) return hipSuccess;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus < 1)
-        cus = 256;
-    // enough workgroups to keep every compute unit's loads in flight, no more than the vectors need
-    const int64_t need = (n16 + CAL_THREADS * COPY_UNROLL - 1) / (CAL_THREADS * COPY_UNROLL);
-    const int64_t grid = need < (int64_t)cus * 16 ? need : (int64_t)cus * 16;
+    const int64_t grid = (n16 + CAL_THREADS * COPY_UNROLL - 1) / (CAL_THREADS * COPY_UNROLL);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(CAL_THREADS), 0, stream, (const uint4*)src, (uint4*)dst,
                        n16);
     return hipGetLastError();

@@ -18,24 +18,28 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bfloat16 bits, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// float -> bfloat16 bits, round to nearest, ties to even; NaN stays NaN
+// (the hardware conversion, v_cvt_pk_bf16_f32, two values per instruction).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Two floats -> two bfloat16 packed in one dword (lo = a).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
 
 // IEEE half bits <-> float: exact widening; narrowing rounds to nearest even
-// (the default rounding mode of v_cvt_f16_f32).
+// (the default rounding mode of v_cvt_f16_f32 and v_cvt_pk_f16_f32).
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 __device__ __forceinline__ uint32_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) { return f32_to_f16(a) | (f32_to_f16(b) << 16); }
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    const f16x2_t v = {(_Float16)a, (_Float16)b};  // v_cvt_pk_f16_f32
+    return __builtin_bit_cast(uint32_t, v);
+}
 
 // The 16-bit element formats the kernels read and write: F16 selects IEEE
 // half, otherwise bfloat16.
@@ -55,7 +59,10 @@ __device__ __forceinline__ uint32_t f32_to_h16(float f) {
 }
 template <bool F16>
 __device__ __forceinline__ uint32_t pack_h16x2(float a, float b) {
-    return f32_to_h16<F16>(a) | (f32_to_h16<F16>(b) << 16);
+    if constexpr (F16)
+        return pack_f16x2(a, b);
+    else
+        return pack_bf16x2(a, b);
 }
 // low / high 16-bit element of a dword, widened to float
 template <bool F16>
@@ -75,6 +82,24 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
                                                       c, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Streaming 16-byte accesses with the non-temporal hint, for data a kernel
+// touches once.  On MI355X a plain cold copy of 2 x 67 MB rises from about
+// 4.0 to 5.4 TB/s with both hinted and a 1:1 join over 2 x 180 MB in, 180 MB
+// out from 5.9 to 6.2 TB/s with its loads hinted.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(void* p, uint4 v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ float4 ld_nt_f4(const float* p) {
+    const uint4 v = ld_nt(p);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
 // Workgroup index -> work-item index such that each XCD (workgroups are

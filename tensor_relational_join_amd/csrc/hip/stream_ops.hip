@@ -3,7 +3,10 @@
 // segmented aggregation.
 //
 // All of them stream: coalesced 16-byte loads issued back to back before any
-// use, arithmetic in fp32, one pass over the data.
+// use, arithmetic in fp32, one pass over the data.  Loads of data read once
+// carry the non-temporal hint; stores do not, since the next operator reads
+// them and finds them in the caches (non-temporal stores measured no faster
+// alone and slowed the consumers down inside the block).
 #include "dev_common.h"
 
 namespace ja {
@@ -44,7 +47,7 @@ __device__ __forceinline__ void rep_vec_pass(const RepTask& t, const uint8_t* __
         }
         // issued as asm so the compiler cannot sink each load to its store
         // and wait for it there; one explicit wait covers them all
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v[j]) : "v"(src + so * esize) : "memory");
+        asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(v[j]) : "v"(src + so * esize) : "memory");
         doff[j] = dof;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -119,8 +122,8 @@ __global__ __launch_bounds__(ZIP_THREADS) void zip_kernel(const uint4* __restric
     for (int j = 0; j < ZIP_V; ++j) {
         int64_t i = base + j * ZIP_THREADS;
         if (i < nvec) {
-            va[j] = a[i];
-            vb[j] = b[i];
+            va[j] = ld_nt(a + i);
+            vb[j] = ld_nt(b + i);
         }
     }
 #pragma unroll
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_kernel(const int64_t*
         const uint16_t* src = x + b.off + rr * b.width;
         if (vec) {
             for (int e = lane * 8; e < b.width; e += 512) {
-                uint4 v = *reinterpret_cast<const uint4*>(src + e);
+                uint4 v = ld_nt(src + e);
                 *reinterpret_cast<uint4*>(row + b.d_lo + e) = v;
                 uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(NORM_WAVES * 64) void rmsnorm_rows_kernel(const int
     for (int k = 0; k < NV; ++k) {
         const int db = (k * 512) / W;
         off[k] = bl[db].off + rr * W + (k * 512 - db * W) + lane * 8;
-        v[k] = *reinterpret_cast<const uint4*>(x + off[k]);
+        v[k] = ld_nt(x + off[k]);
     }
     float ss = 0.f;
 #pragma unroll
@@ -383,8 +386,8 @@ __global__ __launch_bounds__(AGG_THREADS) void agg_kernel(const AggTile* __restr
     if (vec && e0 + PER <= sg.nelem) {
 #pragma unroll 4
         for (int t = sg.t_begin; t < sg.t_end; ++t) {
-            const float4* p = reinterpret_cast<const float4*>(part + poff[t] + e0);
-            const float4 a = p[0], b = p[1];
+            const float* p = part + poff[t] + e0;
+            const float4 a = ld_nt_f4(p), b = ld_nt_f4(p + 4);
             const float v[PER] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
             for (int j = 0; j < PER; ++j) acc[j] = mx ? fmaxf(acc[j], v[j]) : acc[j] + v[j];
@@ -397,8 +400,7 @@ __global__ __launch_bounds__(AGG_THREADS) void agg_kernel(const AggTile* __restr
             uint32_t w[PER / 2];
 #pragma unroll
             for (int j = 0; j < PER / 2; ++j)
-                w[j] = OUT == 1 ? (f32_to_bf16(acc[2 * j]) | (f32_to_bf16(acc[2 * j + 1]) << 16))
-                                : (f32_to_f16(acc[2 * j]) | (f32_to_f16(acc[2 * j + 1]) << 16));
+                w[j] = OUT == 1 ? pack_bf16x2(acc[2 * j], acc[2 * j + 1]) : pack_f16x2(acc[2 * j], acc[2 * j + 1]);
             *reinterpret_cast<uint4*>((uint16_t*)out + sg.out_off + e0) = make_uint4(w[0], w[1], w[2], w[3]);
         }
         return;
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(256) void smax_agg_kernel(const AggTile* __restrict
     for (int t = sg.t_begin; t < sg.t_end; ++t) {
         const float* pr = part + poff[t] + (int64_t)row * ATTN_PROW;
         const float2 ml = *reinterpret_cast<const float2*>(pr);
-        const float4 a = *reinterpret_cast<const float4*>(pr + 4 + c);
+        const float4 a = ld_nt_f4(pr + 4 + c);
         const float mn = fmaxf(m, ml.x);
         if (mn == -INFINITY) continue;  // identity folded with identity
         const float s1 = __expf(m - mn), s2 = __expf(ml.x - mn);  // exp(-inf) = 0
