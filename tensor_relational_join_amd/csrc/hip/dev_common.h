@@ -102,6 +102,13 @@ __device__ __forceinline__ float4 ld_nt_f4(const float* p) {
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
+// silu(g) u = g u / (1 + e^-g), with the hardware reciprocal (v_rcp_f32,
+// within 1 ulp in fp32) instead of an IEEE division: the result is rounded
+// to a 16-bit format next, whose unit roundoff is 2^16 times larger.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // Workgroup index -> work-item index such that each XCD (workgroups are
 // dealt to the 8 XCDs round-robin) receives a contiguous range of the work
 // list, keeping neighbouring tiles in one L2.

@@ -54,8 +54,8 @@ __device__ __forceinline__ void store_out4(void* __restrict__ C, const uint16_t*
         uint16_t* c = (uint16_t*)C;
         if (epi == JA_EPI_SWIGLU) {
             const int64_t o = off >> 1;
-            const float h0 = a[0] / (1.0f + __expf(-a[0])) * a[1];
-            const float h1 = a[2] / (1.0f + __expf(-a[2])) * a[3];
+            const float h0 = silu_mul(a[0], a[1]);
+            const float h1 = silu_mul(a[2], a[3]);
             if (col + 4 <= N && (o & 1) == 0) {
                 *reinterpret_cast<uint32_t*>(c + o) = pack_h16x2<IN_F16>(h0, h1);
             } else {

@@ -139,8 +139,8 @@ __global__ __launch_bounds__(ZIP_THREADS) void zip_kernel(const uint4* __restric
             float y0 = h16lo_to_f32<F16>(y[k]), y1 = h16hi_to_f32<F16>(y[k]);
             float r0, r1;
             if (OP == 0) {
-                r0 = x0 / (1.0f + __expf(-x0)) * y0;
-                r1 = x1 / (1.0f + __expf(-x1)) * y1;
+                r0 = silu_mul(x0, y0);
+                r1 = silu_mul(x1, y1);
             } else {
                 r0 = x0 + y0;
                 r1 = x1 + y1;
@@ -156,7 +156,7 @@ __global__ void zip_tail_kernel(const uint16_t* a, const uint16_t* b, uint16_t* 
     int64_t i = first + threadIdx.x;
     if (i >= n) return;
     float x = h16_to_f32<F16>(a[i]), y = h16_to_f32<F16>(b[i]);
-    float r = OP == 0 ? x / (1.0f + __expf(-x)) * y : x + y;
+    float r = OP == 0 ? silu_mul(x, y) : x + y;
     c[i] = (uint16_t)f32_to_h16<F16>(r);
 }
 
