@@ -373,6 +373,51 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         int el = lane;
         asm volatile("" : "+v"(el));
         const int kc = el >> 4;
+        // A whole tile inside its block with 4-element aligned rows (the
+        // usual case): every store is a vector store, so the bounds and
+        // alignment checks and the choice of epilogue are made once per tile.
+        if (OUT16 && em0 + BM <= eM && en0 + BN <= eN && ((cbase | (int64_t)ldc) & 3) == 0) {
+            uint16_t* c = (uint16_t*)C;
+            const int64_t lbase = cbase + (int64_t)(em0 + arow + (el & 15)) * ldc + en0 + brow + 4 * kc;
+            if (epi == JA_EPI_SWIGLU) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int64_t o = (lbase + (int64_t)i * 16 * ldc + j * 16) >> 1;
+                        const f32x4_t a = acc[i][j];
+                        *reinterpret_cast<uint32_t*>(c + o) =
+                            pack_h16x2<IN_F16>(silu_mul(a[0], a[1]), silu_mul(a[2], a[3]));
+                    }
+            } else if (epi == JA_EPI_ADD) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    uint2 res[FN];
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        res[j] = *reinterpret_cast<const uint2*>(R + lbase + (int64_t)i * 16 * ldc + j * 16);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const f32x4_t a = acc[i][j];
+                        *reinterpret_cast<uint2*>(c + lbase + (int64_t)i * 16 * ldc + j * 16) =
+                            make_uint2(pack_h16x2<IN_F16>(a[0] + h16lo_to_f32<IN_F16>(res[j].x),
+                                                          a[1] + h16hi_to_f32<IN_F16>(res[j].x)),
+                                       pack_h16x2<IN_F16>(a[2] + h16lo_to_f32<IN_F16>(res[j].y),
+                                                          a[3] + h16hi_to_f32<IN_F16>(res[j].y)));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const f32x4_t a = acc[i][j];
+                        *reinterpret_cast<uint2*>(c + lbase + (int64_t)i * 16 * ldc + j * 16) =
+                            make_uint2(pack_h16x2<IN_F16>(a[0], a[1]), pack_h16x2<IN_F16>(a[2], a[3]));
+                    }
+            }
+            return;
+        }
         // one row of fragments at a time: its residual loads are all in
         // flight before the first of its stores
 #pragma unroll
