@@ -486,14 +486,15 @@ ja_status ja_einsum(const ja_spec* spec, const ja_decomp* decomp, const ja_relat
                     void* dev_ws, size_t ws_bytes, void* stream);
 
 /* For callers that cannot allocate device memory (code under stream
- * capture, tight serving loops, harnesses that forbid hipMalloc): ja_einsum
+ * loops, harnesses that forbid hipMalloc): ja_einsum
  * with the plan tables and the run's scratch in a static device array of
  * JA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
  * process ends, instead of a caller workspace.  The caller passes inputs and
  * outputs only.  JA_ERR_WORKSPACE (before any HIP call) when the plan needs
  * more than the array holds -- ja_einsum_workspace_bytes gives the need --
  * otherwise the errors of ja_einsum.  Blocks until the table upload is done;
- * the run stays asynchronous on `stream`.  No device memory is allocated or
+ * the run stays asynchronous on `stream` (the upload synchronises the stream, so a
+ * call cannot be recorded into a stream capture).  No device memory is allocated or
  * freed.  Every call on a GPU shares that GPU's array: calls that overlap on
  * one GPU (other streams, other host threads) race; calls in order on one
  * stream do not. */

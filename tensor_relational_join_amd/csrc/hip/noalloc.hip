@@ -1,6 +1,7 @@
 // noalloc.hip -- the one-shot join-agg for callers that cannot allocate device
-// memory (code under stream capture, serving loops, harnesses that forbid
-// hipMalloc).
+// memory (serving loops, harnesses that forbid hipMalloc).  The plan tables
+// are still copied in with a synchronous host-to-device copy, so a call
+// cannot be recorded into a stream capture.
 //
 // ja_einsum takes a caller-owned workspace for the plan's device tables and
 // the run's scratch.  ja_einsum_noalloc puts both in `scratch`, a static
