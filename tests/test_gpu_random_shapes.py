@@ -7,7 +7,7 @@ for every letter; every operand layout of a contraction (with a batch letter
 too) in bf16, fp16 and fp32; causal and non-causal attention with multi-head
 and grouped-query specs in bf16 and fp16; packed sequences with random ends,
 cut at a random subset of them; RMSNorm and the 1:1 joins over random
-blockings.  The draws are fixed by the case number, so a failing case is
+blockings; repartitions through random reshape-and-permute views (bit-exact).  The draws are fixed by the case number, so a failing case is
 rerun by its id.  Bars as everywhere: fp32 contractions infinity-norm
 relative <= 1e-5; 16-bit relations (fp32 accumulation) relative Frobenius
 <= 2e-3 against the oracle rounded to the output format, and for the
@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from gpu_helpers import record, rel_frobenius, rel_inf
-from test_gpu_ops import _run
+from test_gpu_ops import _repart_case, _run
 from tensor_relational_join_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -191,3 +191,31 @@ def test_random_one_to_one_joins(dev, orc, case):
     record("random_one_to_one_joins", case=case, op=op, rel_frobenius=err, equal_fraction=eq)
     assert err <= TOL16, (case, err)
     assert eq > 0.99, (case, eq)
+
+
+def _group(rng, factors):
+    """Consecutive factors merged into dimensions at random."""
+    dims, cur = [], 1
+    for i, f in enumerate(factors):
+        cur *= f
+        if i == len(factors) - 1 or rng.random() < 0.5:
+            dims.append(cur)
+            cur = 1
+    return tuple(dims)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_view_repartition(dev, orc, case):
+    """A tensor re-indexed through a view: its shape and the destination's
+    are random groupings of the same factors, the view permutes the factors,
+    and both sides are blocked at random; every element bit for bit."""
+    rng = np.random.default_rng(10000 + case)
+    factors = [int(x) for x in rng.integers(1, 25 if case % 4 else 9, int(rng.integers(2, 5)))]
+    perm = [int(x) for x in rng.permutation(len(factors))]
+    src = _group(rng, factors)
+    dst = _group(rng, [factors[p] for p in perm])
+    src_sp = [_cuts(rng, n, 3, 1) for n in src]
+    dst_sp = [_cuts(rng, n, 3, 1) for n in dst]
+    print("case", case, "factors", factors, "perm", perm, "src", src, src_sp, "dst", dst, dst_sp, flush=True)
+    _repart_case(dev, orc, src, src_sp, dst, dst_sp, vshape=tuple(factors), perm=perm,
+                 dtype="bf16" if case % 2 else "f32", seed=case)
