@@ -58,10 +58,21 @@ SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=unde
 ASAN_OUT = os.path.join(PKG, "libja_asan.so")
 
 
+def _generate(build_dir: str) -> str:
+    """Write the generated sources (the contraction's assembly K loop) into build_dir/gen."""
+    gen = os.path.join(build_dir, "gen")
+    os.makedirs(gen, exist_ok=True)
+    cmd = [sys.executable, os.path.join(CSRC, "hip", "gen_gemm_asm.py"), os.path.join(gen, "gemm_asm.inc")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("generation failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    return gen
+
+
 def build(debug: bool = False, verbose: bool = False, sanitize: bool = False) -> str:
     build_dir = os.path.join(BUILD, "asan") if sanitize else BUILD
     os.makedirs(build_dir, exist_ok=True)
-    extra = ["-g"] if debug else []
+    extra = (["-g"] if debug else []) + ["-I" + _generate(build_dir)]
     srcs = HOST_SOURCES + HIP_SOURCES
 
     def one(src):

@@ -107,6 +107,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_p;
 typedef __attribute__((address_space(3))) bf16x8_t* lds_bf16x8_p;
 
+// GemmAsm<FM, KN, F16>::run / drain: the K loop in assembly (generated by gen_gemm_asm.py)
+#include "gemm_asm.inc"
+
 constexpr uint32_t DMA_OOB = 0x80000000u;  // a buffer offset past any valid extent: reads as zero
 
 // Raw buffer descriptor over [base, base + bytes).
@@ -156,7 +159,6 @@ struct DmaTile {
     static constexpr int PER_WAVE = SLOTS / 64 / WAVES;  // load instructions per wavefront per stage
     static_assert(SLOTS % (64 * WAVES) == 0, "tile must split evenly over the wavefronts");
     uint32_t off[PER_WAVE];  // byte offset of this lane's slot at k0 = 0
-    int kin[PER_WAVE];       // k of the slot's first element inside the stage
 
     // the slot's logical (row, k) inside the tile
     __device__ static void slot(int s, int& r, int& k) {
@@ -174,14 +176,19 @@ struct DmaTile {
             int r, k;
             slot((wave * PER_WAVE + j) * 64 + lane, r, k);
             const int gr = r0 + r;
-            kin[j] = k;
             off[j] = gr < rext ? (uint32_t)((MN ? (int64_t)k * ld + gr : (int64_t)gr * ld + k) * 2) : DMA_OOB;
         }
     }
     // uniform byte offset of contracted position k0
     __device__ static uint32_t koffset(int ld, int k0) { return (uint32_t)((MN ? (int64_t)k0 * ld : (int64_t)k0) * 2); }
 
-    __device__ void issue(uint32_t lds_byte, i32x4_t rsrc, int ld, int k0, int kext, int wave) const {
+    // k of load instruction j's first element inside the stage (for ragged stages only)
+    __device__ static int kin(int j, int wave, int lane) {
+        int r, k;
+        slot((wave * PER_WAVE + j) * 64 + lane, r, k);
+        return k;
+    }
+    __device__ void issue(uint32_t lds_byte, i32x4_t rsrc, int ld, int k0, int kext, int wave, int lane) const {
         const uint32_t soff = koffset(ld, k0);
         if (k0 + 32 <= kext) {
 #pragma unroll
@@ -190,7 +197,7 @@ struct DmaTile {
 #pragma unroll
             for (int j = 0; j < PER_WAVE; ++j)
                 dma16(rsrc, lds_byte + (wave * PER_WAVE + j) * 1024,
-                      (k0 + kin[j] < kext && off[j] != DMA_OOB) ? off[j] + soff : DMA_OOB, 0u);
+                      (k0 + kin(j, wave, lane) < kext && off[j] != DMA_OOB) ? off[j] + soff : DMA_OOB, 0u);
         }
     }
 
@@ -236,7 +243,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     using TA = DmaTile<BM, NT, AL == JA_A_KM>;
     using TB = DmaTile<BN, NT, BL == JA_B_KN>;
     constexpr int PER_STAGE = TA::PER_WAVE + TB::PER_WAVE;
-    constexpr int STAGE = (BM + BN) * BK;  // elements per stage
+    // LDS: the A tiles of the NS stages, then their B tiles (so that every
+    // fragment read of a stage is a base register plus a 16-bit offset)
+    constexpr uint32_t A_STAGE = BM * BK * 2, B_STAGE = BN * BK * 2, B_REGION = NS * A_STAGE;
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
     static_assert((NS - 1) * PER_STAGE <= 63, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) uint16_t gemm_lds[];
@@ -276,7 +285,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     TB tb;
     i32x4_t rsa, rsb;
     int lda = 0, ldb = 0, kext = 0;
-    auto issue = [&](int buf) {
+    auto use_tuple = [&]() {
         if (cached != lt) {
             const GemmTuple tp = tuples[lt];
             const uint16_t* pa = A + tp.a_off + (int64_t)tl.batch * tp.a_bstride;
@@ -286,13 +295,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
             lda = tp.lda;
             ldb = tp.ldb;
             kext = tp.K;
-            ta.setup(lda, m0, sg.M, wave, lane);
-            tb.setup(ldb, n0, sg.N, wave, lane);
+            // from an opaque copy of the lane index, so that the slot
+            // arithmetic is not hoisted out of the tile loop and kept live
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            ta.setup(lda, m0, sg.M, wave, el);
+            tb.setup(ldb, n0, sg.N, wave, el);
             cached = lt;
         }
-        const uint32_t st = lds0 + (uint32_t)(buf * STAGE * 2);
-        ta.issue(st, rsa, lda, lk, kext, wave);
-        tb.issue(st + BM * BK * 2, rsb, ldb, lk, kext, wave);
+    };
+    auto issue = [&](int buf) {
+        use_tuple();
+        ta.issue(lds0 + buf * A_STAGE, rsa, lda, lk, kext, wave, lane);
+        tb.issue(lds0 + B_REGION + buf * B_STAGE, rsb, ldb, lk, kext, wave, lane);
         lk += BK;
         if (lk >= kext) {
             lk = 0;
@@ -310,8 +325,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     const int arow = wm * WTM, brow = wn * WTN;
     bf16x8_t fa[2][FM], fb[2][FN];
     auto read_frags = [&](int buf, bf16x8_t* a, bf16x8_t* b) {
-        const uint16_t* as = gemm_lds + buf * STAGE;
-        const uint16_t* bs = as + BM * BK;
+        const uint16_t* as = gemm_lds + buf * (A_STAGE / 2);
+        const uint16_t* bs = gemm_lds + (B_REGION + buf * B_STAGE) / 2;
 #pragma unroll
         for (int i = 0; i < FM; ++i) a[i] = TA::frag(as, arow + i * 16, lane);
 #pragma unroll
@@ -361,11 +376,113 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         __builtin_amdgcn_sched_barrier(0);
         mfma_rows(FM / 2, FM, ca, cb);
     };
-    if (nst > 0) {
+    // Row-major A in the 8-wavefront kernels: the K loop is inline assembly
+    // (GemmAsm, written out by gen_gemm_asm.py) that threads the next stage's
+    // fragment reads and the refill loads between the MFMAs one at a time.
+    // The C++ side walks a tile's steps in runs: steps whose refills are full
+    // stages of one tuple, a single step whose refill is a ragged stage, and
+    // the last steps, which refill nothing.  Each run starts from stage buffer
+    // it % NS with the lane's fragment addresses offset to it.
+    constexpr bool ASM = AL == JA_A_MK && NT == 512 && NS == 4 && BK == 32 && BN == 256 && (BM == 256 || BM == 128);
+    using GA = GemmAsm<FM, BL == JA_B_KN, IN_F16>;
+    static_assert(!ASM || (GA::PA == TA::PER_WAVE && GA::PB == TB::PER_WAVE && FN == 4), "asm instance");
+    // Between statements the compiler has only the registers the statement
+    // leaves it (its fragments take 96 VGPRs, the accumulators 128 AGPRs), so
+    // every per-lane value a statement needs is recomputed before it from an
+    // opaque copy of the lane index instead of being kept across the loop.
+    int scached = -1;
+    auto k_loop_asm = [&]() {
+        int it = 0;
+        scached = -1;
+        while (it < nst) {
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            const uint32_t ph = (uint32_t)(it % NS);
+            // the lane's fragment addresses in stage buffer ph (as TA::frag and TB::frag compute them)
+            const uint32_t ra = lds0 + ph * A_STAGE + 2 * koff(arow + (el & 15), el >> 4);
+            uint32_t rb[GA::NRB];
+            if constexpr (BL == JA_B_KN) {
+                const int jl = el & 15, k = 8 * (el >> 4) + (jl >> 2);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = brow + j * 16 + 4 * (jl & 3);
+                    rb[2 * j] = lds0 + B_REGION + ph * B_STAGE + 2 * moff<BN>(k, n);
+                    rb[2 * j + 1] = lds0 + B_REGION + ph * B_STAGE + 2 * moff<BN>(k + 4, n);
+                }
+            } else {
+                rb[0] = lds0 + B_REGION + ph * B_STAGE + 2 * koff(brow + (el & 15), el >> 4);
+            }
+            // n1 steps refilling a stage each (the refill of step it is stage
+            // it + NS, at the load cursor), then n2 steps refilling nothing
+            uint32_t va[GA::PA], vb[GA::PB], sa = 0, sb = 0, ia = 0, ib = 0;
+            int n1 = 0;
+            if (it + NS < nst) {
+                if (scached != lt) {  // the tuple's scalars only: per-lane offsets are recomputed below
+                    const GemmTuple tp = tuples[lt];
+                    rsa = buffer_rsrc(A + tp.a_off + (int64_t)tl.batch * tp.a_bstride, (uint32_t)(tp.a_bstride * 2));
+                    rsb = buffer_rsrc(B + tp.b_off + (int64_t)tl.batch * tp.b_bstride, (uint32_t)(tp.b_bstride * 2));
+                    lda = tp.lda;
+                    ldb = tp.ldb;
+                    kext = tp.K;
+                    scached = lt;
+                    cached = -1;
+                }
+                // this run's load offsets, from the lane index (not kept from the tuple's set-up)
+                TA xa_t;
+                TB xb_t;
+                xa_t.setup(lda, m0, sg.M, wave, el);
+                xb_t.setup(ldb, n0, sg.N, wave, el);
+                ia = TA::koffset(lda, BK);
+                ib = TB::koffset(ldb, BK);
+                n1 = 1;
+                if (lk + BK <= kext) {
+                    n1 = min((kext - lk) / BK, nst - NS - it);
+#pragma unroll
+                    for (int j = 0; j < GA::PA; ++j) va[j] = xa_t.off[j];
+#pragma unroll
+                    for (int j = 0; j < GA::PB; ++j) vb[j] = xb_t.off[j];
+                    sa = TA::koffset(lda, lk);
+                    sb = TB::koffset(ldb, lk);
+                } else {  // ragged stage: slots past the contracted extent read zeros
+                    const uint32_t xa = TA::koffset(lda, lk), xb = TB::koffset(ldb, lk);
+#pragma unroll
+                    for (int j = 0; j < GA::PA; ++j)
+                        va[j] = (lk + TA::kin(j, wave, el) < kext && xa_t.off[j] != DMA_OOB) ? xa_t.off[j] + xa : DMA_OOB;
+#pragma unroll
+                    for (int j = 0; j < GA::PB; ++j)
+                        vb[j] = (lk + TB::kin(j, wave, el) < kext && xb_t.off[j] != DMA_OOB) ? xb_t.off[j] + xb : DMA_OOB;
+                }
+                lk += n1 * BK;
+                if (lk >= kext) {
+                    lk = 0;
+                    ++lt;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < GA::PA; ++j) va[j] = DMA_OOB;
+#pragma unroll
+                for (int j = 0; j < GA::PB; ++j) vb[j] = DMA_OOB;
+            }
+            const int n2 = it + n1 + NS >= nst ? nst - it - n1 : 0;
+            const uint32_t ma = lds0 + ph * A_STAGE + wave * TA::PER_WAVE * 1024;
+            const uint32_t mb = lds0 + B_REGION + ph * B_STAGE + wave * TB::PER_WAVE * 1024;
+            GA::steps(acc, (uint32_t)n1, (uint32_t)n2, ph, ra, rb, rsa, rsb, va, vb, sa, sb, ia, ib, ma, mb);
+            it += n1 + n2;
+        }
+    };
+    if (!ASM && nst > 0) {
         wait_stage(0);
         read_frags(0, fa[0], fb[0]);
     }
     // epilogue of one tile: lane owns C[row][col .. col+3] of every fragment
+    // An accumulator fragment moved into VGPRs where it is used: with the
+    // accumulators in AGPRs the compiler would otherwise copy them all out at
+    // the start of the epilogue and spill what does not fit.
+    auto accv = [&](int i, int j) {
+        f32x4_t a = acc[i][j];
+        if constexpr (ASM) asm volatile("" : "+v"(a));
+        return a;
+    };
     auto epilogue = [&](int64_t cbase, int ldc, int eM, int eN, int em0, int en0) {
         // The lane's row and column offsets are recomputed here from an
         // opaque copy of the lane index: hoisted out of the tile loop they
@@ -385,7 +502,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         const int64_t o = (lbase + (int64_t)i * 16 * ldc + j * 16) >> 1;
-                        const f32x4_t a = acc[i][j];
+                        const f32x4_t a = accv(i, j);
                         *reinterpret_cast<uint32_t*>(c + o) =
                             pack_h16x2<IN_F16>(silu_mul(a[0], a[1]), silu_mul(a[2], a[3]));
                     }
@@ -398,7 +515,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
                         res[j] = *reinterpret_cast<const uint2*>(R + lbase + (int64_t)i * 16 * ldc + j * 16);
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const f32x4_t a = acc[i][j];
+                        const f32x4_t a = accv(i, j);
                         *reinterpret_cast<uint2*>(c + lbase + (int64_t)i * 16 * ldc + j * 16) =
                             make_uint2(pack_h16x2<IN_F16>(a[0] + h16lo_to_f32<IN_F16>(res[j].x),
                                                           a[1] + h16hi_to_f32<IN_F16>(res[j].x)),
@@ -411,7 +528,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const f32x4_t a = acc[i][j];
+                        const f32x4_t a = accv(i, j);
                         *reinterpret_cast<uint2*>(c + lbase + (int64_t)i * 16 * ldc + j * 16) =
                             make_uint2(pack_h16x2<IN_F16>(a[0], a[1]), pack_h16x2<IN_F16>(a[2], a[3]));
                     }
@@ -433,7 +550,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int col = en0 + brow + j * 16 + 4 * kc;
-                store_out4<IN_F16, OUT16>(C, R, epi, cbase + (int64_t)row * ldc + col, col, eN, acc[i][j], res[j]);
+                store_out4<IN_F16, OUT16>(C, R, epi, cbase + (int64_t)row * ldc + col, col, eN, accv(i, j), res[j]);
             }
         }
     };
@@ -443,13 +560,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (nst > 0) {
-            wait_stage(0);
-            read_frags(0, fa[0], fb[0]);
-        }
-        for (int it = 0; it < nst; it += 2) {
-            step(it, fa[0], fb[0], fa[1], fb[1]);
-            if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
+        if constexpr (ASM) {
+            if (nst > 0) wait_stage(0);
+            k_loop_asm();
+        } else {
+            if (nst > 0) {
+                wait_stage(0);
+                read_frags(0, fa[0], fb[0]);
+            }
+            for (int it = 0; it < nst; it += 2) {
+                step(it, fa[0], fb[0], fa[1], fb[1]);
+                if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
+            }
         }
         // Next tile: its first stage is loaded while this tile's results
         // leave, the rest after them (so that waiting for stage 0 does not
