@@ -573,9 +573,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
                 if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
             }
         }
-        // Next tile: its first stage is loaded while this tile's results
-        // leave, the rest after them (so that waiting for stage 0 does not
-        // wait for the later stages).  The barrier makes sure that every
+        // Next tile: its first stages are loaded while this tile's results
+        // leave (all of them, unless the epilogue loads a residual: that load
+        // would wait behind them, so then only the first stage goes early and
+        // the rest after the stores).  The barrier makes sure that every
         // wavefront's last fragment reads are complete before LDS is refilled.
         const int64_t ecbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
         const int eldc = sg.ldc, eM = sg.M, eN = sg.N, em0 = m0, en0 = n0;
@@ -590,17 +591,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
             nst = count_stages();
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // an epilogue that loads the residual would wait behind every stage
+        // issued before it, so then only the first goes out early
+        const int early = epi == JA_EPI_ADD ? 1 : NS;
         if (more) {
             lt = sg.t_begin;
             lk = 0;
             cached = -1;
-            if (nst > 0) issue(0);
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                if (s < early && s < nst) issue(s);
         }
         epilogue(ecbase, eldc, eM, eN, em0, en0);
         if (!more) break;
 #pragma unroll
         for (int s = 1; s < NS; ++s)
-            if (s < nst) issue(s);
+            if (s >= early && s < nst) issue(s);
     }
 }
 
