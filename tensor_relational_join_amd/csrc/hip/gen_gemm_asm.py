@@ -74,7 +74,8 @@ def _advance(nrb, sa_stage, sb_stage, refill):
     def sel(cmp):
         return [cmp, "s_mov_b32 %%[t0], %d" % sa_stage, "s_cmov_b32 %%[t0], 0x%x" % neg_a,
                 "s_mov_b32 %%[t1], %d" % sb_stage, "s_cmov_b32 %%[t1], 0x%x" % neg_b]
-    out = ["s_add_u32 %[ph], %[ph], 1", "s_and_b32 %%[ph], %%[ph], %d" % (NS - 1)] + sel("s_cmp_eq_u32 %[ph], 0")
+    out = ["s_add_u32 %[ph], %[ph], 1", "s_cmp_eq_u32 %%[ph], %d" % NS, "s_cselect_b32 %[ph], 0, %[ph]"]
+    out += sel("s_cmp_eq_u32 %[ph], 0")
     out += ["v_add_u32 %[ra], %[t0], %[ra]"]
     out += ["v_add_u32 %%[rb%d], %%[t1], %%[rb%d]" % (k, k) for k in range(nrb)]
     if refill:
@@ -84,9 +85,12 @@ def _advance(nrb, sa_stage, sb_stage, refill):
     return out
 
 
-def _step(fm, fn, b_tr, f16, cur, nxt, pa, pb, refill):
+def _step(fm, fn, b_tr, f16, cur, nxt, pa, pb, refill, vm=None):
+    """One step; vm = stages that may stay in flight past the one read next."""
     ps = pa + pb
-    out = ["s_waitcnt vmcnt(%d)" % (2 * ps if refill else 0), "s_waitcnt lgkmcnt(0)", "s_barrier"]
+    if vm is None:
+        vm = NS - 2 if refill else 0
+    out = ["s_waitcnt vmcnt(%d)" % (vm * ps), "s_waitcnt lgkmcnt(0)", "s_barrier"]
     mf = _mfmas(fm, fn, f16, cur)
     reads = _read_ops(fm, fn, b_tr, nxt)
     dmas = _dmas(pa, pb) if refill else []
@@ -120,18 +124,31 @@ def statement(fm, fn, b_tr, f16, bm, bn):
     body += ["s_sub_u32 %[n1], %[n1], 1", "s_cmp_eq_u32 %[n1], 0", "s_cbranch_scc1 4f"]
     body += _step(fm, fn, b_tr, f16, s, 0, pa, pb, True) + _advance(nrb, sa_stage, sb_stage, True)
     body += ["s_sub_u32 %[n1], %[n1], 1", "s_cmp_eq_u32 %[n1], 0", "s_cbranch_scc0 1b"]
-    # drain steps starting from set 0
-    body += ["3:", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc1 6f"]
-    body += ["2:"] + _step(fm, fn, b_tr, f16, 0, s, pa, pb, False) + _advance(nrb, sa_stage, sb_stage, False)
-    body += ["s_sub_u32 %[n2], %[n2], 1", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc1 6f"]
-    body += _step(fm, fn, b_tr, f16, s, 0, pa, pb, False) + _advance(nrb, sa_stage, sb_stage, False)
-    body += ["s_sub_u32 %[n2], %[n2], 1", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc0 2b", "s_branch 6f"]
-    # drain steps starting from set 1
-    body += ["4:", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc1 6f"]
-    body += ["5:"] + _step(fm, fn, b_tr, f16, s, 0, pa, pb, False) + _advance(nrb, sa_stage, sb_stage, False)
-    body += ["s_sub_u32 %[n2], %[n2], 1", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc1 6f"]
-    body += _step(fm, fn, b_tr, f16, 0, s, pa, pb, False) + _advance(nrb, sa_stage, sb_stage, False)
-    body += ["s_sub_u32 %[n2], %[n2], 1", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc0 5b"]
+    # The last NS steps of a tile (n2 == NS after a run that reaches the end):
+    # step k may leave the NS - 2 - k stages loaded after the one it reads in
+    # flight.  Any other n2 (a tile of fewer than NS stages) waits for all.
+    def drain_exact(first):
+        out = []
+        for k in range(NS):
+            cur = first if k % 2 == 0 else s - first
+            out += _step(fm, fn, b_tr, f16, cur, s - cur, pa, pb, False, max(0, NS - 2 - k))
+            out += _advance(nrb, sa_stage, sb_stage, False)
+        return out
+    def drain_loop(first, lab):
+        other = s - first
+        out = ["%d:" % lab] + _step(fm, fn, b_tr, f16, first, other, pa, pb, False) + _advance(nrb, sa_stage, sb_stage, False)
+        out += ["s_sub_u32 %[n2], %[n2], 1", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc1 6f"]
+        out += _step(fm, fn, b_tr, f16, other, first, pa, pb, False) + _advance(nrb, sa_stage, sb_stage, False)
+        out += ["s_sub_u32 %[n2], %[n2], 1", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc0 %db" % lab, "s_branch 6f"]
+        return out
+    # drain starting from set 0
+    body += ["3:", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc1 6f", "s_cmp_eq_u32 %%[n2], %d" % NS, "s_cbranch_scc0 2f"]
+    body += drain_exact(0) + ["s_branch 6f"]
+    body += drain_loop(0, 2)
+    # drain starting from set 1
+    body += ["4:", "s_cmp_eq_u32 %[n2], 0", "s_cbranch_scc1 6f", "s_cmp_eq_u32 %%[n2], %d" % NS, "s_cbranch_scc0 5f"]
+    body += drain_exact(s) + ["s_branch 6f"]
+    body += drain_loop(s, 5)
     body += ["6:", "s_waitcnt lgkmcnt(0)", "s_nop 7", "s_nop 7", "s_nop 4"]
     outs = ['[c%d_%d] "+a"(acc[%d][%d])' % (i, j, i, j) for i in range(fm) for j in range(fn)]
     outs += ['[n1] "+s"(n1)', '[n2] "+s"(n2)', '[ph] "+s"(ph)', '[ra] "+v"(ra)']
