@@ -306,8 +306,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     };
     auto issue = [&](int buf) {
         use_tuple();
-        ta.issue(lds0 + buf * A_STAGE, rsa, lda, lk, kext, wave, lane);
-        tb.issue(lds0 + B_REGION + buf * B_STAGE, rsb, ldb, lk, kext, wave, lane);
+        int el = lane;  // opaque, as in use_tuple
+        asm volatile("" : "+v"(el));
+        ta.issue(lds0 + buf * A_STAGE, rsa, lda, lk, kext, wave, el);
+        tb.issue(lds0 + B_REGION + buf * B_STAGE, rsb, ldb, lk, kext, wave, el);
         lk += BK;
         if (lk >= kext) {
             lk = 0;
@@ -604,6 +606,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         }
         epilogue(ecbase, eldc, eM, eN, em0, en0);
         if (!more) break;
+        cached = -1;  // the load offsets are recomputed rather than kept through the epilogue
 #pragma unroll
         for (int s = 1; s < NS; ++s)
             if (s >= early && s < nst) issue(s);
