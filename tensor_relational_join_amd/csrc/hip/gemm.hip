@@ -378,14 +378,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         __builtin_amdgcn_sched_barrier(0);
         mfma_rows(FM / 2, FM, ca, cb);
     };
-    // Row-major A in the 8-wavefront kernels: the K loop is inline assembly
+    // Row-major A and 16-bit outputs in the 8-wavefront kernels: the K loop is inline assembly
     // (GemmAsm, written out by gen_gemm_asm.py) that threads the next stage's
     // fragment reads and the refill loads between the MFMAs one at a time.
     // The C++ side walks a tile's steps in runs: steps whose refills are full
     // stages of one tuple, a single step whose refill is a ragged stage, and
     // the last steps, which refill nothing.  Each run starts from stage buffer
     // it % NS with the lane's fragment addresses offset to it.
-    constexpr bool ASM = AL == JA_A_MK && NT == 512 && NS == 4 && BK == 32 && BN == 256 && (BM == 256 || BM == 128);
+    // (fp32 outputs, the unfused form's per-tuple partials, keep the compiler's
+    // loop: their four-byte stores from AGPR accumulators measured 10% slower)
+    constexpr bool ASM = OUT16 && AL == JA_A_MK && NT == 512 && NS == 4 && BK == 32 && BN == 256 &&
+                         (BM == 256 || BM == 128);
     using GA = GemmAsm<FM, BL == JA_B_KN, IN_F16>;
     static_assert(!ASM || (GA::PA == TA::PER_WAVE && GA::PB == TB::PER_WAVE && FN == 4), "asm instance");
     // Between statements the compiler has only the registers the statement
