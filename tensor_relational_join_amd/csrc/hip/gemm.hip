@@ -498,6 +498,66 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         // A whole tile inside its block with 4-element aligned rows (the
         // usual case): every store is a vector store, so the bounds and
         // alignment checks and the choice of epilogue are made once per tile.
+        // Full tiles whose rows are 8-element aligned, in fragment pairs: one
+        // v_permlane16_swap per accumulator register gives each lane eight
+        // adjacent columns (lanes 0-15 and 32-47 columns 0-7 and 8-15 of the
+        // first fragment, lanes 16-31 and 48-63 those of the second), so each
+        // store writes 16 bytes per lane and 64 contiguous bytes per row:
+        // half the store instructions of the plain layout and no 32-byte
+        // pieces, which matters because every compute unit writes its tile at
+        // the same moment.
+        if (OUT16 && FN % 2 == 0 && em0 + BM <= eM && en0 + BN <= eN && ((cbase | (int64_t)ldc) & 7) == 0) {
+            uint16_t* c = (uint16_t*)C;
+            const int64_t lbase =
+                cbase + (int64_t)(em0 + arow + (el & 15)) * ldc + en0 + brow + (kc & 1) * 16 + (kc >> 1) * 8;
+            // the lane's eight columns of fragment pair (i, 2 p), in order
+            auto pair = [&](int i, int p, float* v) {
+                const f32x4_t x = accv(i, 2 * p), y = accv(i, 2 * p + 1);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r]), __float_as_uint(y[r]), false,
+                                                                     false);
+                    v[r] = __uint_as_float(sw[0]);
+                    v[4 + r] = __uint_as_float(sw[1]);
+                }
+            };
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int64_t rbase = lbase + (int64_t)i * 16 * ldc;
+                if (epi == JA_EPI_ADD) {
+                    uint4 res[FN / 2];
+#pragma unroll
+                    for (int p = 0; p < FN / 2; ++p) res[p] = *reinterpret_cast<const uint4*>(R + rbase + 32 * p);
+#pragma unroll
+                    for (int p = 0; p < FN / 2; ++p) {
+                        float v[8];
+                        pair(i, p, v);
+                        const uint32_t w[4] = {res[p].x, res[p].y, res[p].z, res[p].w};
+                        uint32_t o[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            o[q] = pack_h16x2<IN_F16>(v[2 * q] + h16lo_to_f32<IN_F16>(w[q]),
+                                                      v[2 * q + 1] + h16hi_to_f32<IN_F16>(w[q]));
+                        *reinterpret_cast<uint4*>(c + rbase + 32 * p) = make_uint4(o[0], o[1], o[2], o[3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int p = 0; p < FN / 2; ++p) {
+                        float v[8];
+                        pair(i, p, v);
+                        if (epi == JA_EPI_SWIGLU)  // four (gate, up) pairs -> four adjacent outputs
+                            *reinterpret_cast<uint2*>(c + ((rbase + 32 * p) >> 1)) =
+                                make_uint2(pack_h16x2<IN_F16>(silu_mul(v[0], v[1]), silu_mul(v[2], v[3])),
+                                           pack_h16x2<IN_F16>(silu_mul(v[4], v[5]), silu_mul(v[6], v[7])));
+                        else
+                            *reinterpret_cast<uint4*>(c + rbase + 32 * p) =
+                                make_uint4(pack_h16x2<IN_F16>(v[0], v[1]), pack_h16x2<IN_F16>(v[2], v[3]),
+                                           pack_h16x2<IN_F16>(v[4], v[5]), pack_h16x2<IN_F16>(v[6], v[7]));
+                    }
+                }
+            }
+            return;
+        }
         if (OUT16 && em0 + BM <= eM && en0 + BN <= eN && ((cbase | (int64_t)ldc) & 3) == 0) {
             uint16_t* c = (uint16_t*)C;
             const int64_t lbase = cbase + (int64_t)(em0 + arow + (el & 15)) * ldc + en0 + brow + 4 * kc;
