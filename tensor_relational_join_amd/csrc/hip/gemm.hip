@@ -237,7 +237,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
                                                                     void* __restrict__ C,
                                                                     const uint16_t* __restrict__ R, int epi) {
     constexpr int NT = WM * WN * 64;
-    constexpr int BK = 32;
+    constexpr int BK = GEMM_DMA_BK;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 16, FN = WTN / 16;
     using TA = DmaTile<BM, NT, AL == JA_A_KM>;
@@ -268,11 +268,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     GemmTile tl = tile_at(vt);
     GemmSeg sg = segs[tl.seg];
     int m0 = row0(vt, tl), n0 = tl.n0;
-    auto count_stages = [&]() {
-        int n = 0;
-        for (int t = sg.t_begin; t < sg.t_end; ++t) n += (tuples[t].K + BK - 1) / BK;
-        return n;
-    };
+    auto count_stages = [&]() { return sg.nst; };  // planned on the host
     int nst = count_stages();
 
     f32x4_t acc[FM][FN];

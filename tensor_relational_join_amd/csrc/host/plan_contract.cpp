@@ -132,7 +132,7 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         u.ldc = (int32_t)n;
         u.t_begin = (int32_t)i;
         u.t_end = (int32_t)i + 1;
-        u.pad = 0;
+        u.nst = (int32_t)((k + GEMM_DMA_BK - 1) / GEMM_DMA_BK);
         poff[i] = part;
         part += nb * m * n;
         for (int32_t b = 0; b < nb; ++b)
@@ -150,7 +150,10 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         g.ldc = (int32_t)n;
         g.t_begin = (int32_t)t.seg[sg];
         g.t_end = (int32_t)t.seg[sg + 1];
-        g.pad = 0;
+        int64_t nst = 0;
+        for (int32_t i = g.t_begin; i < g.t_end; ++i) nst += (tuples[i].K + GEMM_DMA_BK - 1) / GEMM_DMA_BK;
+        if (nst > lim) return fail(JA_ERR_UNSUPPORTED, "contracted extent beyond 2^31 stages");
+        g.nst = (int32_t)nst;
         // grouped order: GEMM_GROUP_M row tiles, then every column tile, so a
         // contiguous run of the list forms a compact block of output tiles
         const int32_t mt = (int32_t)((m + TM - 1) / TM), ntl = (int32_t)((n + TN - 1) / TN);

@@ -25,7 +25,7 @@ struct GemmSeg {
     int64_t c_bstride;  // output batch stride
     int32_t M, N, ldc;  // block rows, block columns, row pitch
     int32_t t_begin, t_end;  // tuple range [t_begin, t_end)
-    int32_t pad;
+    int32_t nst;             // contracted stages of the tuples: the sum of ceil(K / GEMM_DMA_BK)
 };
 
 // One joined tuple: the A block and the B block it multiplies.
@@ -117,6 +117,7 @@ constexpr int GEMM_BF16_TM = 256;  // output rows per workgroup tile, bf16 MFMA 
 constexpr int GEMM_BF16_TN = 256;  // output columns per workgroup tile
 constexpr int GEMM_GROUP_M = 4;    // row tiles per group in the tile order (L2 reuse)
 constexpr int GEMM_DMA_STAGES = 4; // 32-wide stages in flight in the direct-to-LDS kernel
+constexpr int GEMM_DMA_BK = 32;     // contracted elements per stage of the 16-bit kernels
 constexpr int GEMM_F32_TM = 64;    // fp32 kernel tile
 constexpr int GEMM_F32_TN = 64;
 constexpr int ATTN_TQ = 128;       // query rows per attention workgroup
