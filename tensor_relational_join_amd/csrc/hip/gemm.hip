@@ -281,8 +281,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     TB tb;
     i32x4_t rsa, rsb;
     int lda = 0, ldb = 0, kext = 0;
+    // (kernels with the assembly K loop issue here only between tiles, and
+    // recompute the offsets each time rather than keep them live: kept, they
+    // would be spilled, and a spill reload's wait also waits for the stage
+    // loads in flight)
+    constexpr bool RECOMPUTE = OUT16 && AL == JA_A_MK && NT == 512 && NS == 4 && BK == 32 && BN == 256 &&
+                               (BM == 256 || BM == 128);
     auto use_tuple = [&]() {
-        if (cached != lt) {
+        if (RECOMPUTE || cached != lt) {
             const GemmTuple tp = tuples[lt];
             const uint16_t* pa = A + tp.a_off + (int64_t)tl.batch * tp.a_bstride;
             const uint16_t* pb = B + tp.b_off + (int64_t)tl.batch * tp.b_bstride;
@@ -383,22 +389,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     // it % NS with the lane's fragment addresses offset to it.
     // (fp32 outputs, the unfused form's per-tuple partials, keep the compiler's
     // loop: their four-byte stores from AGPR accumulators measured 10% slower)
-    constexpr bool ASM = OUT16 && AL == JA_A_MK && NT == 512 && NS == 4 && BK == 32 && BN == 256 &&
-                         (BM == 256 || BM == 128);
+    constexpr bool ASM = RECOMPUTE;
     using GA = GemmAsm<FM, BL == JA_B_KN, IN_F16>;
     static_assert(!ASM || (GA::PA == TA::PER_WAVE && GA::PB == TB::PER_WAVE && FN == 4), "asm instance");
     // Between statements the compiler has only the registers the statement
     // leaves it (its fragments take 96 VGPRs, the accumulators 128 AGPRs), so
     // every per-lane value a statement needs is recomputed before it from an
     // opaque copy of the lane index instead of being kept across the loop.
+    // head: 0, or the memory operations per fragment pair and lane (1: a
+    // store, 2: a residual load and a store) of the previous tile's full-tile
+    // epilogue, issued after this tile's first NS stages, which its first
+    // steps need not wait for.  pbase: the stage buffer holding the tile's
+    // stage 0.  pf: the tile's last NS steps refill the stage buffers with
+    // the first NS stages of the workgroup's next tile (full stages of its
+    // first tuple), so those load while this tile drains and stores.
     int scached = -1;
-    auto k_loop_asm = [&]() {
+    auto k_loop_asm = [&](uint32_t head, int pbase, bool pf) {
         int it = 0;
         scached = -1;
         while (it < nst) {
             int el = lane;
             asm volatile("" : "+v"(el));
-            const uint32_t ph = (uint32_t)(it % NS);
+            const uint32_t ph = (uint32_t)((it + pbase) % NS);
             // the lane's fragment addresses in stage buffer ph (as TA::frag and TB::frag compute them)
             const uint32_t ra = lds0 + ph * A_STAGE + 2 * koff(arow + (el & 15), el >> 4);
             uint32_t rb[GA::NRB];
@@ -458,16 +470,42 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
                     lk = 0;
                     ++lt;
                 }
+            } else if (pf) {  // it == nst - NS: refill with the next tile's stages 0 .. NS - 1
+                const int vn = vt + (int)gridDim.x;
+                const GemmTile tn = tile_at(vn);
+                const GemmSeg sn = segs[tn.seg];
+                const GemmTuple tp = tuples[sn.t_begin];
+                rsa = buffer_rsrc(A + tp.a_off + (int64_t)tn.batch * tp.a_bstride, (uint32_t)(tp.a_bstride * 2));
+                rsb = buffer_rsrc(B + tp.b_off + (int64_t)tn.batch * tp.b_bstride, (uint32_t)(tp.b_bstride * 2));
+                scached = -1;
+                cached = -1;
+                TA xa_t;
+                TB xb_t;
+                xa_t.setup(tp.lda, row0(vn, tn), sn.M, wave, el);
+                xb_t.setup(tp.ldb, tn.n0, sn.N, wave, el);
+                ia = TA::koffset(tp.lda, BK);
+                ib = TB::koffset(tp.ldb, BK);
+#pragma unroll
+                for (int j = 0; j < GA::PA; ++j) va[j] = xa_t.off[j];
+#pragma unroll
+                for (int j = 0; j < GA::PB; ++j) vb[j] = xb_t.off[j];
+                n1 = NS;
             } else {
 #pragma unroll
                 for (int j = 0; j < GA::PA; ++j) va[j] = DMA_OOB;
 #pragma unroll
                 for (int j = 0; j < GA::PB; ++j) vb[j] = DMA_OOB;
             }
-            const int n2 = it + n1 + NS >= nst ? nst - it - n1 : 0;
+            const int n2 = !pf && it + n1 + NS >= nst ? nst - it - n1 : 0;
+            const uint32_t nh = __builtin_amdgcn_readfirstlane(it == 0 && n1 >= NS - 1 ? head : 0u);
             const uint32_t ma = lds0 + ph * A_STAGE + wave * TA::PER_WAVE * 1024;
             const uint32_t mb = lds0 + B_REGION + ph * B_STAGE + wave * TB::PER_WAVE * 1024;
-            GA::steps(acc, (uint32_t)n1, (uint32_t)n2, ph, ra, rb, rsa, rsb, va, vb, sa, sb, ia, ib, ma, mb);
+            // (uniform values; read from lane 0 so that they stay scalar operands)
+            sa = __builtin_amdgcn_readfirstlane(sa);
+            sb = __builtin_amdgcn_readfirstlane(sb);
+            ia = __builtin_amdgcn_readfirstlane(ia);
+            ib = __builtin_amdgcn_readfirstlane(ib);
+            GA::steps(acc, (uint32_t)n1, (uint32_t)n2, ph, ra, rb, rsa, rsb, va, vb, sa, sb, ia, ib, ma, mb, nh);
             it += n1 + n2;
         }
     };
@@ -483,6 +521,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         f32x4_t a = acc[i][j];
         if constexpr (ASM) asm volatile("" : "+v"(a));
         return a;
+    };
+    // a whole tile inside its block with 8-element aligned rows: the epilogue
+    // stores it in fragment pairs, FM * FN / 2 stores per lane
+    auto paired = [&](int64_t cbase, int ldc, int eM, int eN, int em0, int en0) {
+        return OUT16 && FN % 2 == 0 && em0 + BM <= eM && en0 + BN <= eN && ((cbase | (int64_t)ldc) & 7) == 0;
     };
     auto epilogue = [&](int64_t cbase, int ldc, int eM, int eN, int em0, int en0) {
         // The lane's row and column offsets are recomputed here from an
@@ -502,7 +545,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         // half the store instructions of the plain layout and no 32-byte
         // pieces, which matters because every compute unit writes its tile at
         // the same moment.
-        if (OUT16 && FN % 2 == 0 && em0 + BM <= eM && en0 + BN <= eN && ((cbase | (int64_t)ldc) & 7) == 0) {
+        if (paired(cbase, ldc, eM, eN, em0, en0)) {
             uint16_t* c = (uint16_t*)C;
             const int64_t lbase =
                 cbase + (int64_t)(em0 + arow + (el & 15)) * ldc + en0 + brow + (kc & 1) * 16 + (kc >> 1) * 8;
@@ -616,14 +659,37 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         }
     };
 
+    // the previous tile's epilogue, if it stored in fragment pairs after this
+    // tile's first NS stages had been issued: its memory operations per
+    // fragment pair and lane (0: not so)
+    uint32_t stored_after = 0;
+    int pbase = 0;  // stage buffer of the tile's stage 0 (ASM)
+    bool pf = false;
     while (true) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if constexpr (ASM) {
-            if (nst > 0) wait_stage(0);
-            k_loop_asm();
+            // Stage 0 is followed in issue order by stages 1 .. NS - 1 and
+            // then the stores; vector memory operations complete in issue
+            // order, so waiting for stage 0 leaves both in flight.
+            const uint32_t head = nst >= NS ? stored_after : 0u;
+            if (head == 2)
+                wait_loads_barrier<(NS - 1) * PER_STAGE + 2 * GA::STORES>();
+            else if (head == 1)
+                wait_loads_barrier<(NS - 1) * PER_STAGE + GA::STORES>();
+            else if (nst > 0)
+                wait_stage(0);
+            // prefetch the next tile's first stages if this tile has a full
+            // drain and the next one starts with NS full stages of one tuple
+            pf = false;
+            if (nst >= NS && vt + (int)gridDim.x < ntiles) {
+                const GemmTile tn = tile_at(vt + (int)gridDim.x);
+                const GemmSeg sn = segs[tn.seg];
+                pf = sn.nst >= NS && tuples[sn.t_begin].K >= NS * BK;
+            }
+            k_loop_asm(head, pbase, pf);
         } else {
             if (nst > 0) {
                 wait_stage(0);
@@ -643,6 +709,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
         const int eldc = sg.ldc, eM = sg.M, eN = sg.N, em0 = m0, en0 = n0;
         const int vnext = vt + (int)gridDim.x;
         const bool more = vnext < ntiles;
+        const int nst_done = nst;
         if (more) {
             vt = vnext;
             tl = tile_at(vt);
@@ -659,16 +726,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
             lt = sg.t_begin;
             lk = 0;
             cached = -1;
+            if (pf) {  // stages 0 .. NS - 1 are in flight, in the buffers after this tile's last
+                pbase = (pbase + nst_done) % NS;
+                lk = NS * BK;
+                if (lk >= tuples[lt].K) {
+                    lk = 0;
+                    ++lt;
+                }
+            } else {
+                pbase = 0;
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                if (s < early && s < nst) issue(s);
+                for (int s = 0; s < NS; ++s)
+                    if (s < early && s < nst) issue(s);
+            }
         }
+        stored_after = more && (pf || early == NS) && paired(ecbase, eldc, eM, eN, em0, en0)
+                           ? (epi == JA_EPI_ADD ? 2u : 1u)
+                           : 0u;
         epilogue(ecbase, eldc, eM, eN, em0, en0);
         if (!more) break;
         cached = -1;  // the load offsets are recomputed rather than kept through the epilogue
+        if (!pf) {
 #pragma unroll
-        for (int s = 1; s < NS; ++s)
-            if (s >= early && s < nst) issue(s);
+            for (int s = 1; s < NS; ++s)
+                if (s >= early && s < nst) issue(s);
+        }
     }
 }
 

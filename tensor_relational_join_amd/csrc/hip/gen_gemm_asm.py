@@ -11,14 +11,17 @@ AGPRs, fragments live in fixed VGPRs v0 .. v(2 S - 1) that the statement
 clobbers (S = 4 (FM + FN) per set), and the schedule is exactly the
 instruction order below.
 
-Two statements per instance (fragment rows FM, columns FN, B layout, dtype):
-  run   -- n >= 1 steps that each refill one stage: wait for the stage read
+One statement per instance (fragment rows FM, columns FN, B layout, dtype)
+runs the steps of one run of a tile:
+  head  -- optionally, the tile's first three steps, which may also leave the
+           previous tile's output stores in flight (see statement());
+  run   -- n1 steps that each refill one stage: wait for the stage read
            next (vmcnt: two later stages may stay in flight), barrier, MFMAs
            with the reads and loads between them, then advance the LDS read
            addresses, the refill's LDS bases and global offsets;
-  drain -- n steps with no refill (the last stages of a tile), waiting for
-           every load.
-Each statement first re-reads the current stage's fragments (the compiler
+  drain -- n2 steps with no refill (the last stages of a tile), each waiting
+           for no more than its own stage.
+The statement first re-reads the current stage's fragments (the compiler
 owns the fixed VGPRs between statements) and ends with enough wait states for
 a VALU read of the accumulators.  Run as a script (build.py does) it writes
 the file given as its argument.
@@ -85,12 +88,14 @@ def _advance(nrb, sa_stage, sb_stage, refill):
     return out
 
 
-def _step(fm, fn, b_tr, f16, cur, nxt, pa, pb, refill, vm=None):
-    """One step; vm = stages that may stay in flight past the one read next."""
+def _step(fm, fn, b_tr, f16, cur, nxt, pa, pb, refill, vm=None, extra=0):
+    """One step; vm = stages that may stay in flight past the one read next,
+    extra = further memory operations issued after that stage (a previous
+    tile's output stores) that may stay in flight too."""
     ps = pa + pb
     if vm is None:
         vm = NS - 2 if refill else 0
-    out = ["s_waitcnt vmcnt(%d)" % (vm * ps), "s_waitcnt lgkmcnt(0)", "s_barrier"]
+    out = ["s_waitcnt vmcnt(%d)" % (vm * ps + extra), "s_waitcnt lgkmcnt(0)", "s_barrier"]
     mf = _mfmas(fm, fn, f16, cur)
     reads = _read_ops(fm, fn, b_tr, nxt)
     dmas = _dmas(pa, pb) if refill else []
@@ -109,8 +114,17 @@ def _step(fm, fn, b_tr, f16, cur, nxt, pa, pb, refill, vm=None):
 
 
 def statement(fm, fn, b_tr, f16, bm, bn):
-    """n1 steps that refill a stage each, then n2 steps that refill nothing."""
+    """n1 steps that refill a stage each, then n2 steps that refill nothing.
+
+    With nh != 0 (the caller guarantees n1 >= NS - 1) the first NS - 1 steps
+    are head steps: the tile's first NS stages were loaded before the
+    previous tile's full-tile epilogue, which issued nh memory operations
+    per fragment pair and lane (a store; or a residual load and a store), so
+    the stage a head step reads is followed in issue order by those
+    nh * fm * fn / 2 operations as well as the usual NS - 2 stages, and the
+    head steps do not wait for the epilogue's stores to complete."""
     s = 4 * (fm + fn)
+    stores = fm * fn // 2
     pa = bm * 32 // 8 // 64 // 8
     pb = bn * 32 // 8 // 64 // 8
     nrb = 2 * fn if b_tr else 1
@@ -118,11 +132,23 @@ def statement(fm, fn, b_tr, f16, bm, bn):
     body = ["s_nop 4"]  # the compiler may have just written the accumulators
     body += _read_ops(fm, fn, b_tr, 0)
     body += _advance(nrb, sa_stage, sb_stage, False)
-    body += ["s_cmp_eq_u32 %[n1], 0", "s_cbranch_scc1 3f"]
+    body += ["s_cmp_eq_u32 %[n1], 0", "s_cbranch_scc1 3f", "s_cmp_eq_u32 %[nh], 0", "s_cbranch_scc1 1f",
+             "s_cmp_eq_u32 %[nh], 1", "s_cbranch_scc0 7f"]
+    # head steps (NS - 1 = 3 of them: fragment sets 0, 1, 0), then the refill
+    # loop's second half (current set 1) or the drain from set 1
+    assert NS - 1 == 3
+    for kind in (1, 2):
+        if kind == 2:
+            body += ["7:"]
+        for k in range(NS - 1):
+            cur = 0 if k % 2 == 0 else s
+            body += _step(fm, fn, b_tr, f16, cur, s - cur, pa, pb, True, extra=kind * stores)
+            body += _advance(nrb, sa_stage, sb_stage, True) + ["s_sub_u32 %[n1], %[n1], 1"]
+        body += ["s_cmp_eq_u32 %[n1], 0", "s_cbranch_scc1 4f", "s_branch 8f"]
     # refill steps, current fragments in set 0 then set 1
     body += ["1:"] + _step(fm, fn, b_tr, f16, 0, s, pa, pb, True) + _advance(nrb, sa_stage, sb_stage, True)
     body += ["s_sub_u32 %[n1], %[n1], 1", "s_cmp_eq_u32 %[n1], 0", "s_cbranch_scc1 4f"]
-    body += _step(fm, fn, b_tr, f16, s, 0, pa, pb, True) + _advance(nrb, sa_stage, sb_stage, True)
+    body += ["8:"] + _step(fm, fn, b_tr, f16, s, 0, pa, pb, True) + _advance(nrb, sa_stage, sb_stage, True)
     body += ["s_sub_u32 %[n1], %[n1], 1", "s_cmp_eq_u32 %[n1], 0", "s_cbranch_scc0 1b"]
     # The last NS steps of a tile (n2 == NS after a run that reaches the end):
     # step k may leave the NS - 2 - k stages loaded after the one it reads in
@@ -155,7 +181,7 @@ def statement(fm, fn, b_tr, f16, bm, bn):
     outs += ['[rb%d] "+v"(rb[%d])' % (k, k) for k in range(nrb)]
     outs += ['[t0] "=&s"(t0)', '[t1] "=&s"(t1)']
     outs += ['[sa] "+s"(sa)', '[sb] "+s"(sb)', '[ma] "+s"(ma)', '[mb] "+s"(mb)']
-    ins = ['[rsa] "s"(rsa)', '[rsb] "s"(rsb)', '[ia] "s"(ia)', '[ib] "s"(ib)']
+    ins = ['[rsa] "s"(rsa)', '[rsb] "s"(rsb)', '[ia] "s"(ia)', '[ib] "s"(ib)', '[nh] "s"(nh)']
     ins += ['[va%d] "v"(va[%d])' % (j, j) for j in range(pa)]
     ins += ['[vb%d] "v"(vb[%d])' % (j, j) for j in range(pb)]
     clob = ['"v%d"' % r for r in range(2 * s)] + ['"m0"', '"scc"', '"memory"']
@@ -176,11 +202,11 @@ def emit():
                 pb = bn * 32 // 8 // 64 // 8
                 out.append("template <>")
                 out.append("struct GemmAsm<%d, %s, %s> {" % (fm, "true" if b_tr else "false", "true" if f16 else "false"))
-                out.append("    static constexpr int PA = %d, PB = %d, NRB = %d;" % (pa, pb, nrb))
+                out.append("    static constexpr int PA = %d, PB = %d, NRB = %d, STORES = %d;" % (pa, pb, nrb, fm * fn // 2))
                 out.append("    __device__ __forceinline__ static void steps(f32x4_t (&acc)[%d][%d], uint32_t n1, uint32_t n2, "
                            "uint32_t ph, uint32_t ra, uint32_t (&rb)[%d], i32x4_t rsa, i32x4_t rsb, const uint32_t (&va)[%d], "
                            "const uint32_t (&vb)[%d], uint32_t sa, uint32_t sb, uint32_t ia, uint32_t ib, uint32_t ma, "
-                           "uint32_t mb) {" % (fm, fn, nrb, pa, pb))
+                           "uint32_t mb, uint32_t nh) {" % (fm, fn, nrb, pa, pb))
                 out.append("    uint32_t t0, t1;")
                 out.append(statement(fm, fn, b_tr, f16, bm, bn) + "    }")
                 out.append("};")
