@@ -193,6 +193,9 @@ BLOCKS = {
 # join launches (every projection written) instead of fused into the
 # contractions that produce their inputs
 BLOCKS.update({k + "_unfused": dict(v, fused=False) for k, v in list(BLOCKS.items())})
+# the LLaMA-7B-shaped block with attention on head-major relations: the two
+# re-indexing repartitions (tokens -> heads, heads -> tokens) around it
+BLOCKS["block_heads"] = dict(BLOCKS["block"], name="llama7b_shaped_block_head_major", layout="heads")
 
 
 def bench_block(args):
@@ -208,7 +211,8 @@ def bench_block(args):
     batch, seq, dm, heads, kv, ffn = (cfg[k] for k in ("batch", "seq", "dm", "heads", "kv_heads", "ffn"))
     fused = cfg.get("fused", True)
     dt = cfg.get("dtype", "bf16")
-    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv, fused=fused, dtype=JA_F16 if dt == "f16" else JA_BF16)
+    blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv, fused=fused, dtype=JA_F16 if dt == "f16" else JA_BF16,
+                     layout=cfg.get("layout", "tokens"))
     GEMMS = blk.gemms
     inp = synth.llama_block_inputs(5, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols, dtype=dt)
     x = blk.materialize(_bits_to_dev(inp["x"], dt), blk.x_rel)
@@ -263,7 +267,9 @@ def bench_block(args):
         "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": batch, "seq_len": seq, "d_model": dm,
                    "heads": heads, "kv_heads": kv, "head_dim": 128, "ffn": ffn, "parallelism": "single GPU",
-                   "adds_and_swiglu": "fused into the contractions" if fused else "separate launches"},
+                   "adds_and_swiglu": "fused into the contractions" if fused else "separate launches",
+                   "attention_layout": ("token-major (no repartition)" if blk.layout == "tokens"
+                                        else "head-major (repartitions around attention)")},
         "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "block_gflop": round(total_flops / 1e9, 1),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),

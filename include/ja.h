@@ -160,7 +160,14 @@ ja_status ja_relation_block(const ja_relation_desc* rel, const int64_t* key, int
  *                   (grouped-query attention, section 3.3: with
  *                   "bgrsd,bgtd,bgtd->bgrsd", query head 4g + r of a
  *                   4-per-group layout reads key-value head g, and splitting
- *                   g splits the query heads with it).
+ *                   g splits the query heads with it).  The batch and group
+ *                   letters may also follow the position letter, as in the
+ *                   token-major relations a projection writes: Q = O =
+ *                   [batch..., s, batch..., group..., d], K = V = [batch...,
+ *                   t, batch..., d] with the same letters before s and t
+ *                   (e.g. "bshd,bthd,bthd->bshd" or "bsgrd,btgd,btgd->bsgrd");
+ *                   Q's second-to-last letter is read as s whenever it is
+ *                   absent from K and t is K's second to last.
  *                   Scores Q K^T * scale joined on d; aggregation over t with
  *                   the online-softmax triple (max, sum of exponentials,
  *                   weighted sum of values); then O = weighted sum / sum.
@@ -459,7 +466,8 @@ ja_status ja_plan_run(const ja_plan* plan, const void* const* in_ptrs, void* out
  * ascending tuple order with `op` and writes the output relation.
  *   contract (no epilogue): a tuple's part is its dense row-major partial
  *     output block; op JA_AGG_SUM (the contraction) or JA_AGG_MAX.
- *   attention: a tuple's part holds, per query row of its query block (rows
+ *   attention (every batch and group letter before s; JA_ERR_UNSUPPORTED
+ *     otherwise): a tuple's part holds, per query row of its query block (rows
  *     in the O block's order: batch-heads, then s), 132 floats [m, l, -, -,
  *     acc[128]]: over the keys of the tuple's key block the row may see,
  *     m = max of scale q.k (or a value below it: the triple is only defined

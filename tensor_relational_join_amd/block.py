@@ -20,7 +20,23 @@ Only the QKV decomposition is fixed by the workload; the others are chosen
 so that every producer's output blocking is its consumer's input blocking
 (the repartition sub-cost of the pages' cost model, section 4.3, is then
 zero for them), which leaves exactly the two re-indexing repartitions around
-attention (tokens <-> heads).
+attention (tokens <-> heads).  That is the layout="heads" form above.
+
+The default, layout="tokens", needs no repartition at all: attention's
+relations keep the projections' token-major layout, the heads inside a row
+(a block (b, s-interval) is 128 whole token rows of every head):
+
+    h1 = rmsnorm(x, g1)               rd,d->rd      r: 1  d: 2
+    qkv = h1 @ W_qkv                  td,dn->tn     t: 1  d: 2  n: cut at the Q | K | V column boundaries
+    O = attention(Q, K, V)            bshd,bthd,bthd->bshd   b unit intervals, s and t 128-blocks, h whole
+                                      (bsgrd,btgd,btgd->bsgrd with grouped key-value heads)
+    a = O @ W_o                       tm,mn->tn     t: 1  m: 1  n: 2
+    (every other op as above, with the tokens in one block)
+
+The projection's Q, K and V column blocks are three contiguous [t, *]
+arrays, exactly the relations Q [b, s, h, d], K and V [b, t, h, d] blocked
+by (b, 128-interval of s or t), and attention's output O [b, s, h, d] is the
+output projection's A [t, dm] as one block.
 
 With kv_heads < heads the block uses grouped-query attention (the pages'
 section 3.3: query heads g*R .. g*R+R-1 read key-value head g, R = heads /
@@ -61,29 +77,35 @@ from . import binding as B
 from .device import Op as _Op
 from .device import Repart, alloc, equal_splits
 
-# the steps in execution order, and the contractions among them
+# the steps in execution order (head-major layout), and the contractions among them
 STEPS = ["norm1", "qkv", "to_heads", "attn", "to_tokens", "oproj", "add1", "norm2", "gate", "up", "swiglu",
          "down", "add2"]
 GEMMS = ["qkv", "oproj", "gate", "up", "down"]
 FUSED_STEPS = ["norm1", "qkv", "to_heads", "attn", "to_tokens", "oproj_add", "norm2", "gate_up", "down_add"]
 FUSED_GEMMS = ["qkv", "oproj_add", "gate_up", "down_add"]
+LAYOUTS = ("tokens", "heads")
 
 
 class LlamaBlock:
     def __init__(self, batch: int = 4, seq: int = 2048, dm: int = 4096, heads: int = 32, ffn: int = 11008,
                  eps: float = 1e-6, device="cuda", kv_heads: Optional[int] = None, fused: bool = False,
-                 dtype: int = B.JA_BF16):
+                 dtype: int = B.JA_BF16, layout: str = "tokens"):
         if dm % heads or dm // heads != 128 or seq % 128:
             raise ValueError("the attention kernel needs head_dim 128 and 128-multiples of seq")
         if dtype not in (B.JA_BF16, B.JA_F16):
             raise ValueError("the block's relations are bf16 or IEEE half")
-        self.dtype = dtype
+        if layout not in LAYOUTS:
+            raise ValueError("layout is 'tokens' (attention on the projections' token-major relations) or 'heads'")
+        self.dtype, self.layout = dtype, layout
+        tok = layout == "tokens"
         kv = heads if kv_heads is None else kv_heads
         if kv <= 0 or heads % kv:
             raise ValueError("kv_heads must divide heads")
         self.batch, self.seq, self.dm, self.heads, self.ffn, self.eps = batch, seq, dm, heads, ffn, eps
         self.kv_heads, self.gqa, self.fused = kv, kv != heads, fused
         self.steps, self.gemms = (FUSED_STEPS, FUSED_GEMMS) if fused else (STEPS, GEMMS)
+        if tok:
+            self.steps = [n for n in self.steps if n not in ("to_heads", "to_tokens")]
         self.hd = dm // heads
         T = batch * seq
         self.T = T
@@ -91,7 +113,7 @@ class LlamaBlock:
         self.qkv_cols = dm + 2 * kvd
         # tokens in two blocks; one block with grouped key-value heads, where the
         # projection's output must keep its Q, K, V parts contiguous
-        t2, d2 = (equal_splits(T, 2) if not self.gqa else [0, T]), equal_splits(dm, 2)
+        t2, d2 = (equal_splits(T, 2) if not (self.gqa or tok) else [0, T]), equal_splits(dm, 2)
         f4 = equal_splits(ffn, 4)
         ep = "eps=%r" % eps
         nb = seq // 128
@@ -102,7 +124,21 @@ class LlamaBlock:
             return _Op(einsum, op, splits, params, [dtype] * n_in, dtype, device=device)
 
         self.ops["norm1"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
-        if not self.gqa:
+        if tok:
+            # the projection's Q, K, V parts are three contiguous token-major
+            # arrays, which are attention's relations as they are: a block
+            # (b, s-interval) holds whole rows of every head
+            self.ops["qkv"] = Op("td,dn->tn", "contract",
+                                 {"t": t2, "d": d2, "n": [0, dm, dm + kvd, dm + 2 * kvd]}, device=device)
+            bs = {"b": equal_splits(batch, batch), "s": equal_splits(seq, nb), "t": equal_splits(seq, nb),
+                  "d": [0, self.hd]}
+            if not self.gqa:
+                self.ops["attn"] = Op("bshd,bthd,bthd->bshd", "attention", {**bs, "h": [0, heads]}, "causal=s,t",
+                                      device=device)
+            else:
+                self.ops["attn"] = Op("bsgrd,btgd,btgd->bsgrd", "attention",
+                                      {**bs, "g": [0, kv], "r": [0, heads // kv]}, "causal=s,t", device=device)
+        elif not self.gqa:
             self.ops["qkv"] = Op("td,dn->tn", "contract", {"t": t2, "d": d2, "n": equal_splits(3 * dm, 2)},
                                  device=device)
             att_sp = {"b": equal_splits(batch, batch), "h": equal_splits(heads, heads), "s": equal_splits(seq, nb),
@@ -114,11 +150,13 @@ class LlamaBlock:
             att_sp = {"b": equal_splits(batch, batch), "g": equal_splits(kv, kv), "r": [0, heads // kv],
                       "s": equal_splits(seq, nb), "t": equal_splits(seq, nb), "d": [0, self.hd]}
             self.ops["attn"] = Op("bgrsd,bgtd,bgtd->bgrsd", "attention", att_sp, "causal=s,t", device=device)
+        # attention's token-major output is the projection's A as it is (m whole)
+        m2 = [0, dm] if tok else d2
         if not fused:
-            self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": d2, "n": d2}, device=device)
+            self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": m2, "n": d2}, device=device)
             self.ops["add1"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
         else:
-            self.ops["oproj_add"] = Op("tm,mn,tn->tn", "contract_add", {"t": t2, "m": d2, "n": d2}, device=device)
+            self.ops["oproj_add"] = Op("tm,mn,tn->tn", "contract_add", {"t": t2, "m": m2, "n": d2}, device=device)
         self.ops["norm2"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
         if not fused:
             self.ops["gate"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
@@ -133,7 +171,9 @@ class LlamaBlock:
         oproj = self.ops["oproj_add" if fused else "oproj"]
         # token-major <-> head-major re-blockings around attention
         self.rp: Dict[str, Repart] = {}
-        if not self.gqa:
+        if tok:
+            pass
+        elif not self.gqa:
             heads_rel = B.Relation((3, batch, heads, seq, self.hd), nblk=(3, batch, heads, nb, 1), dtype=dtype)
             self.rp["to_heads"] = Repart(self.ops["qkv"].out_rel, heads_rel,
                                          B.make_view((batch, seq, 3, heads, self.hd), (2, 0, 3, 1, 4)),
@@ -169,15 +209,19 @@ class LlamaBlock:
         # the block's output relation
         self.y_rel = o["down_add" if fused else "add2"].out_rel
         # intermediates
-        if not self.gqa:
+        if tok:
+            heads = {}
+        elif not self.gqa:
             heads = {"heads": alloc(self.heads_rel, device)}
         else:
             heads = {n: alloc(r, device) for n, r in zip("qkv", o["attn"].in_rels)}
         self.buf = {
             "h1": alloc(o["norm1"].out_rel, device), "qkv": alloc(o["qkv"].out_rel, device),
-            **heads, "O": alloc(o["attn"].out_rel, device), "o": alloc(oproj.in_rels[0], device),
+            **heads, "O": alloc(o["attn"].out_rel, device),
             "x2": alloc(oproj.out_rel, device), "h2": alloc(o["norm2"].out_rel, device),
         }
+        # the projection's input: attention's output itself in the token-major layout
+        self.buf["o"] = self.buf["O"] if tok else alloc(oproj.in_rels[0], device)
         if not fused:
             self.buf.update({"a": alloc(o["oproj"].out_rel, device), "gt": alloc(o["gate"].out_rel, device),
                              "up": alloc(o["up"].out_rel, device), "f": alloc(o["swiglu"].out_rel, device),
@@ -204,8 +248,9 @@ class LlamaBlock:
         outputs written once)."""
         T, dm, ffn = self.T, self.dm, self.ffn
         e = 2.0
-        b = {"norm1": e * (2 * T * dm + dm), "norm2": e * (2 * T * dm + dm), "to_heads": e * 2 * T * self.qkv_cols,
-             "to_tokens": e * 2 * T * dm}
+        b = {"norm1": e * (2 * T * dm + dm), "norm2": e * (2 * T * dm + dm)}
+        if self.layout == "heads":
+            b.update({"to_heads": e * 2 * T * self.qkv_cols, "to_tokens": e * 2 * T * dm})
         if not self.fused:
             b.update({"add1": e * 3 * T * dm, "add2": e * 3 * T * dm, "swiglu": e * 3 * T * ffn})
         return b
@@ -217,7 +262,12 @@ class LlamaBlock:
         the relations' layouts (x_rel, w_rel, g_rel).  If `events` is given,
         a (start, end) torch event pair is recorded around every step."""
         o, b = self.ops, self.buf
-        if not self.gqa:
+        tok = self.layout == "tokens"
+        if tok:
+            nq, nk = self.T * self.dm, self.T * self.kv_heads * self.hd
+            q, k, v = b["qkv"][:nq], b["qkv"][nq:nq + nk], b["qkv"][nq + nk:]
+            to_heads = None
+        elif not self.gqa:
             n = self.T * self.heads * self.hd  # elements of each of Q, K, V
             q, k, v = b["heads"][:n], b["heads"][n:2 * n], b["heads"][2 * n:]
 
@@ -238,6 +288,8 @@ class LlamaBlock:
             ("attn", lambda: o["attn"].run([q, k, v], b["O"], stream)),
             ("to_tokens", lambda: self.rp["to_tokens"].run(b["O"], b["o"], stream)),
         ]
+        if tok:
+            plan = [st for st in plan if st[0] not in ("to_heads", "to_tokens")]
         if not self.fused:
             plan += [
                 ("oproj", lambda: o["oproj"].run([b["o"], w["w_o"]], b["a"], stream)),

@@ -121,6 +121,11 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     const AttnTile tl = tiles[vt];
     const AttnSeg sg = segs[tl.seg];
     const int kvbh = tl.bh / sg.rep;  // key-value batch-head (query heads of a group share it)
+    // element offsets of this batch-head's first row and the row strides
+    // (inner batch-heads sit inside a row: token-major relations)
+    const int64_t qbh = (int64_t)(tl.bh / sg.q_hin) * sg.q_bstride + (int64_t)(tl.bh % sg.q_hin) * D;
+    const int32_t qrs = sg.q_hin * D, kvrs = sg.kv_hin * D;
+    const int kvo = kvbh / sg.kv_hin, kvi = kvbh % sg.kv_hin;
     const int qrow = tl.s0 + wave * 32 + lq;  // query row inside the block
     const int qglob = sg.s_lo + qrow;         // global query index (causal mask)
     const int wave_qmin = sg.s_lo + tl.s0 + wave * 32;
@@ -169,8 +174,8 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     // Q^T fragments (B operand): lane holds Q[query lq][d = 16 st + 8 g .. +7]
     bf16x8_t qf[D / 16];
     {
-        const at_i32x4_t rq = at_rsrc(Q + sg.q_off + (int64_t)tl.bh * sg.q_bhstride, (uint32_t)(sg.q_bhstride * 2));
-        const int32_t qo = qrow < sg.S ? (qrow * D + 8 * g) * 2 : (int32_t)0x80000000;
+        const at_i32x4_t rq = at_rsrc(Q + sg.q_off + qbh, (uint32_t)((sg.q_bstride - qbh % sg.q_bstride) * 2));
+        const int32_t qo = qrow < sg.S ? (qrow * qrs + 8 * g) * 2 : (int32_t)0x80000000;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st)
             qf[st] = __builtin_bit_cast(bf16x8_t, at_buffer_load_x4(rq, qo + (qrow < sg.S ? 32 * st : 0), 0, 0));
@@ -211,11 +216,11 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
         const int s = (wave * 4 + j) * 64 + lane;  // 16-byte slot of the 16 KiB tile
         const int key = s >> 4, c = (s & 15) ^ kswz(key);
         kkey[j] = key;
-        koffb[j] = (uint32_t)((key * D + c * 8) * 2);
+        koffb[j] = (uint32_t)((key * kvrs + c * 8) * 2);
     }
     // V staging: keys 4 kg .. 4 kg + 3 of the step, d = 8 dj .. 8 dj + 7
     const int kg = tid >> 4, dj = tid & 15;
-    const int32_t vlane = ((kg * 4) * D + dj * 8) * 2;  // byte offset of this lane's first V row at key 0
+    const int32_t vlane = ((kg * 4) * kvrs + dj * 8) * 2;  // byte offset of this lane's first V row at key 0
     at_i32x4_t vr[4];
 
     // load cursor
@@ -223,16 +228,19 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     enter(lt, lkt);
     auto load_step = [&](int buf) {
         const AttnTuple tp = tuples[lt];
-        const uint16_t* kb = K + tp.k_off + (int64_t)kvbh * tp.kv_bhstride;
-        const at_i32x4_t rs = at_rsrc(kb, (uint32_t)(tp.kv_bhstride * 2));
+        // the buffers' extents end at the block's end (within an outer slab)
+        const int64_t kvb = (int64_t)kvo * tp.kv_bstride + (int64_t)kvi * D;
+        const uint32_t ext = (uint32_t)((tp.kv_bstride - (int64_t)kvi * D) * 2);
+        const uint16_t* kb = K + tp.k_off + kvb;
+        const at_i32x4_t rs = at_rsrc(kb, ext);
         const uint32_t st = lds0 + (uint32_t)(buf * AT_STAGE * 2);
-        const uint32_t soff = (uint32_t)(lkt * D * 2);
-        const at_i32x4_t rv = at_rsrc(V + tp.v_off + (int64_t)kvbh * tp.kv_bhstride, (uint32_t)(tp.kv_bhstride * 2));
+        const uint32_t soff = (uint32_t)(lkt * kvrs * 2);
+        const at_i32x4_t rv = at_rsrc(V + tp.v_off + kvb, ext);
         if (lkt + AT_KT <= tp.T) {  // every key of the step is in the block
 #pragma unroll
             for (int j = 0; j < 4; ++j) at_dma16(rs, st + (wave * 4 + j) * 1024, koffb[j], soff);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vr[i] = at_buffer_load_x4(rv, vlane + i * D * 2, (int32_t)soff, 0);
+            for (int i = 0; i < 4; ++i) vr[i] = at_buffer_load_x4(rv, vlane + i * kvrs * 2, (int32_t)soff, 0);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = lkt + kg * 4 + i;
-                vr[i] = at_buffer_load_x4(rv, key < tp.T ? (key * D + dj * 8) * 2 : (int32_t)0x80000000, 0, 0);
+                vr[i] = at_buffer_load_x4(rv, key < tp.T ? (key * kvrs + dj * 8) * 2 : (int32_t)0x80000000, 0, 0);
             }
         }
         advance(lt, lkt, tp);  // to the next visible step
@@ -310,10 +318,9 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
             const AttnTuple tp = tuples[t];
             const int f = first_key(tp), e = end_key(tp);
             if (e <= f) continue;
-            const uint4* vp =
-                reinterpret_cast<const uint4*>(V + tp.v_off + (int64_t)kvbh * tp.kv_bhstride + (int64_t)f * D);
+            const uint16_t* vb = V + tp.v_off + (int64_t)kvo * tp.kv_bstride + (int64_t)kvi * D;
             for (int c = tid; c < (e - f) * (D / 8); c += AT_THREADS) {
-                const uint4 v = vp[c];
+                const uint4 v = *reinterpret_cast<const uint4*>(vb + (int64_t)(f + c / (D / 8)) * kvrs + (c % (D / 8)) * 8);
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) em = max(em, max((w[k] >> 7) & 0xffu, (w[k] >> 23) & 0xffu));
@@ -499,7 +506,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attention_kernel(const AttnTile
     } else {
         const float inv = 1.0f / l_tot;
         if (qrow < sg.S) {
-            uint16_t* op = (uint16_t*)O + sg.o_off + (int64_t)tl.bh * sg.q_bhstride + (int64_t)qrow * D;
+            uint16_t* op = (uint16_t*)O + sg.o_off + qbh + (int64_t)qrow * qrs;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll

@@ -67,12 +67,14 @@ __global__ __launch_bounds__(DA_THREADS) void da_seg_kernel(DAttnArgs a, const i
     AttnSeg g;
     g.q_off = qbase[qi] + s_lo * a.D;
     g.o_off = g.q_off;
-    g.q_bhstride = a.S * a.D;
+    g.q_bstride = a.S * a.D;
     g.S = (int32_t)(s_hi - s_lo);
     g.s_lo = (int32_t)s_lo;
     g.t_begin = (int32_t)t0;
     g.t_end = (int32_t)t1;
     g.rep = qn[qi] / kn[ki];
+    g.q_hin = 1;  // head-major blocks: every batch-head letter before the position letter
+    g.kv_hin = 1;
     g.pad = 0;
     segs[k] = g;
     const int32_t ntq = (g.S + ATTN_TQ - 1) / ATTN_TQ;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(DA_THREADS) void da_tuple_kernel(DAttnArgs a, const
     AttnTuple t;
     t.k_off = kbase[ki] + t_lo * a.D;
     t.v_off = t.k_off;
-    t.kv_bhstride = a.S * a.D;
+    t.kv_bstride = a.S * a.D;
     t.T = (int32_t)(t_hi - t_lo);
     t.t_lo = (int32_t)t_lo;
     tuples[i] = t;

@@ -235,19 +235,50 @@ static ja_status parse_spec(const char* einsum, const char* op, const char* para
         if (s->ins.size() != 3) return fail(JA_ERR_SPEC, "attention takes Q, K, V");
         // Q = O = [batch..., group..., s, d], K = V = [batch..., t, d]: the
         // optional group letters index the query heads that share one
-        // key-value head (grouped-query attention)
+        // key-value head (grouped-query attention).  Batch-head letters may
+        // also follow the position letter (token-major relations, e.g.
+        // bshd,bthd,bthd->bshd): with the position and head-dimension letters
+        // removed, Q's letters must be K's followed by the group letters.
         const std::string &q = s->ins[0], &k = s->ins[1], &v = s->ins[2];
         if (q != s->out || k != v || k.size() < 2 || q.size() < k.size())
             return fail(JA_ERR_SPEC,
                         "attention needs Q = O = [batch..., group..., s, d] and K = V = [batch..., t, d]");
         const size_t r = q.size(), rk = k.size();
-        if (q[r - 1] != k[rk - 1] || q[r - 2] == k[rk - 2] || q.substr(0, rk - 2) != k.substr(0, rk - 2) ||
-            q.find(k[rk - 2]) != std::string::npos)
-            return fail(JA_ERR_SPEC, "attention letters must be [batch..., group..., s, d] and [batch..., t, d]");
-        for (size_t i = rk - 2; i < r - 2; ++i)
-            if (k.find(q[i]) != std::string::npos)
+        if (q[r - 1] != k[rk - 1])
+            return fail(JA_ERR_SPEC, "attention: Q and K must end in the same head-dimension letter");
+        // the key position letter: the one letter of K that Q lacks
+        char ct = 0;
+        for (size_t i = 0; i + 1 < rk; ++i)
+            if (q.find(k[i]) == std::string::npos) {
+                if (ct) return fail(JA_ERR_SPEC, "attention: K has more than one letter that Q lacks");
+                ct = k[i];
+            }
+        if (!ct) return fail(JA_ERR_SPEC, "attention: K needs a key position letter absent from Q");
+        // the query position letter: Q's second to last when that letter is
+        // absent from K and K's position letter is K's second to last (the
+        // head-major form, so "bgsrd,bgtd" has position letter r and group
+        // letter s), else the letter at the key position letter's place in K
+        // (the letters before both the same: token-major)
+        const size_t pt = k.find(ct);
+        char cs = 0;
+        if (k.find(q[r - 2]) == std::string::npos && k[rk - 2] == ct)
+            cs = q[r - 2];
+        else if (pt < r - 1 && q.substr(0, pt) == k.substr(0, pt) && k.find(q[pt]) == std::string::npos)
+            cs = q[pt];
+        if (!cs) return fail(JA_ERR_SPEC, "attention letters must be [batch..., s, batch..., d] and [batch..., t, batch..., d]");
+        std::string lq, lk;  // batch-head letters in storage order
+        for (char c : q.substr(0, r - 1))
+            if (c != cs) lq += c;
+        for (char c : k.substr(0, rk - 1))
+            if (c != ct) lk += c;
+        if (lq.compare(0, lk.size(), lk) != 0)
+            return fail(JA_ERR_SPEC, "attention: Q's batch-head letters must be K's followed by the group letters");
+        for (size_t i = lk.size(); i < lq.size(); ++i)
+            if (k.find(lq[i]) != std::string::npos)
                 return fail(JA_ERR_SPEC, "attention group letters must not index K and V");
-        if (s->causal && (s->causal_s != q[r - 2] || s->causal_t != k[rk - 2]))
+        s->att_s = cs;
+        s->att_t = ct;
+        if (s->causal && (s->causal_s != cs || s->causal_t != ct))
             return fail(JA_ERR_SPEC, "causal pair must name the query and key position letters");
         s->group_by = s->out;
     } else if (o == "rmsnorm") {
@@ -294,9 +325,8 @@ ja_status build_tuples(const ja_spec* s, const ja_decomp* d, ja_tuples& t) {
     }
     int ps = -1, pt = -1;  // packed sequences: the query and key position letters
     if (!s->packed.empty() || s->packed_device) {
-        const std::string &q = s->ins[0], &k = s->ins[1];
-        ps = s->letter_index(q[q.size() - 2]);
-        pt = s->letter_index(k[k.size() - 2]);
+        ps = s->letter_index(s->att_s);
+        pt = s->letter_index(s->att_t);
     }
     t.nl = nl;
     t.rec.clear();
@@ -451,7 +481,7 @@ ja_status ja_decomp_create(const ja_spec* s, const int64_t* extents, const int32
         if (s->packed_device) {
             // sequence ends given by the cuts themselves: both sequence letters cut alike
             const std::string &q = s->ins[0], &k = s->ins[1];
-            if (d->sp[s->letter_index(q[q.size() - 2])] != d->sp[s->letter_index(k[k.size() - 2])]) {
+            if (d->sp[s->letter_index(s->att_s)] != d->sp[s->letter_index(s->att_t)]) {
                 delete d;
                 return fail(JA_ERR_DECOMP, "attention: packed=device needs the same cuts on both sequence letters");
             }
@@ -460,7 +490,7 @@ ja_status ja_decomp_create(const ja_spec* s, const int64_t* extents, const int32
             // packed sequences: the sequence letters span every sequence and may be
             // split only at sequence ends (section 3.3)
             const std::string &q = s->ins[0], &k = s->ins[1];
-            for (char c : {q[q.size() - 2], k[k.size() - 2]}) {
+            for (char c : {s->att_s, s->att_t}) {
                 const std::vector<int64_t>& sp = d->sp[s->letter_index(c)];
                 bool ok = sp.back() == s->packed.back();
                 for (size_t i = 1; ok && i + 1 < sp.size(); ++i)

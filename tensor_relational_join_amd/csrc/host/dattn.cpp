@@ -82,7 +82,9 @@ ja_status ja_dattn_create(const ja_spec* s, const int64_t* extents, const int32_
         return fail(JA_ERR_SPEC, "the device planner takes attention with packed=device");
     if (dtype != JA_BF16 && dtype != JA_F16) return fail(JA_ERR_DTYPE, "attention relations are bf16 or f16");
     const std::string &q = s->ins[0], &k = s->ins[1];
-    const int ls = s->letter_index(q[q.size() - 2]), lt = s->letter_index(k[k.size() - 2]);
+    if (q[q.size() - 2] != s->att_s || k[k.size() - 2] != s->att_t)
+        return fail(JA_ERR_UNSUPPORTED, "the device planner takes head-major relations (position letter second to last)");
+    const int ls = s->letter_index(s->att_s), lt = s->letter_index(s->att_t);
     const int ld = s->letter_index(q.back());
     if (extents[ld] != ATTN_D) return fail(JA_ERR_UNSUPPORTED, "attention kernel is built for head dimension 128");
     if (extents[ls] > ((int64_t)1 << 31) - 1) return fail(JA_ERR_UNSUPPORTED, "sequence index beyond 2^31");

@@ -55,12 +55,12 @@ ja_status ja_djoin_create(const ja_spec* s, const int64_t* extents, const int32_
         if (intervals[s->letter_index(q.back())] != 1)
             return fail(JA_ERR_DECOMP, "attention: the head-dimension letter cannot be split");
         if (s->packed_device) {
-            const int ls = s->letter_index(q[q.size() - 2]), lt = s->letter_index(k[k.size() - 2]);
+            const int ls = s->letter_index(s->att_s), lt = s->letter_index(s->att_t);
             if (extents[ls] != extents[lt] || intervals[ls] != intervals[lt])
                 return fail(JA_ERR_DECOMP, "attention: packed=device needs the same cuts on both sequence letters");
         }
         if (!s->packed.empty())
-            for (char c : {q[q.size() - 2], k[k.size() - 2]}) {
+            for (char c : {s->att_s, s->att_t}) {
                 const int l = s->letter_index(c);
                 if (extents[l] != s->packed.back() || intervals[l] > (int64_t)s->packed.size())
                     return fail(JA_ERR_DECOMP, std::string("attention: letter ") + c +
@@ -108,9 +108,8 @@ ja_status ja_djoin_create(const ja_spec* s, const int64_t* extents, const int32_
         a.it = s->letter_index(s->causal_t);
     }
     if (!s->packed.empty() || s->packed_device) {
-        const std::string &q = s->ins[0], &k = s->ins[1];
-        a.ps = s->letter_index(q[q.size() - 2]);
-        a.pt = s->letter_index(k[k.size() - 2]);
+        a.ps = s->letter_index(s->att_s);
+        a.pt = s->letter_index(s->att_t);
         j->ends = s->packed;
         a.nends = s->packed_device ? -1 : (int32_t)s->packed.size();
     }

@@ -64,6 +64,11 @@ struct ja_spec {
     bool has_scale = false;
     bool causal = false;
     char causal_s = 0, causal_t = 0;
+    // attention: the query and key position letters.  Q = O = [outer..., s,
+    // inner..., d] and K = V = [outer..., t, inner..., d]: the letters other
+    // than s (t) and d index batch-heads, those after s (t) stored inside a
+    // row (token-major relations), those before it outside
+    char att_s = 0, att_t = 0;
     std::vector<int64_t> packed;  // attention: ascending ends of sequences packed along the s and t letters
     bool packed_device = false;   // attention: the sequences end exactly at the cuts of the s and t letters
     int32_t epilogue = 0;         // contract: JA_EPI_NONE, JA_EPI_ADD (third operand R) or JA_EPI_SWIGLU

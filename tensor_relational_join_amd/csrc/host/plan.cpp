@@ -20,6 +20,10 @@ using namespace ja;
 
 namespace {
 
+// the softmax aggregation writes O rows in [batch-head][query] order
+const char* const INNER_UNFUSED =
+    "the unfused attention path takes Q, K, V and O with every batch-head letter before the position letter";
+
 ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const ja_tuples& t,
                          const ja_relation_desc* const* in, const ja_relation_desc* out) {
     Rel Q, K, V, O;
@@ -34,9 +38,17 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
         return fail(JA_ERR_DTYPE, "attention takes and writes bf16 or f16 (one format for Q, K, V and O)");
     p->in_dtype = Q.dtype;
     const std::string& q = s->ins[0];
-    const size_t r = q.size(), rk = s->ins[1].size();
-    const std::string batch = q.substr(0, r - 2), kbatch = s->ins[1].substr(0, rk - 2);
-    const char cs = q[r - 2], ct = s->ins[1][rk - 2], cd = q[r - 1];
+    const std::string& k = s->ins[1];
+    const char cs = s->att_s, ct = s->att_t, cd = q.back();
+    // batch-head letters in storage order (all of them, and those stored
+    // inside a row: after the position letter)
+    std::string batch, kbatch, qin, kin;
+    for (size_t i = 0; i + 1 < q.size(); ++i)
+        if (q[i] != cs) (i > q.find(cs) ? qin : batch) += q[i];
+    batch += qin;
+    for (size_t i = 0; i + 1 < k.size(); ++i)
+        if (k[i] != ct) (i > k.find(ct) ? kin : kbatch) += k[i];
+    kbatch += kin;
     const int64_t D = d->ext[s->letter_index(cd)];
     if (D != ATTN_D) return fail(JA_ERR_UNSUPPORTED, "attention kernel is built for head dimension 128");
     p->scale = (float)(s->has_scale ? s->scale : 1.0 / std::sqrt((double)D));
@@ -56,7 +68,8 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
         AttnTuple& a = tuples[i];
         a.k_off = K.blk_off[block_of(K, s->ins[1], s, rec)];
         a.v_off = V.blk_off[block_of(V, s->ins[2], s, rec)];
-        a.kv_bhstride = T * D;
+        a.kv_bstride = T * extent_of(d, s, rec, kin) * D;
+        if (a.kv_bstride > lim) return fail(JA_ERR_UNSUPPORTED, "key block rows beyond 2^31 elements");
         a.T = (int32_t)T;
         a.t_lo = (int32_t)d->sp[lt][rec[lt]];
     }
@@ -74,10 +87,14 @@ ja_status plan_attention(ja_plan* p, const ja_spec* s, const ja_decomp* d, const
         // the group letters trail the batch letters, so query batch-head bh
         // of the block reads key-value batch-head bh / rep
         g.rep = (int32_t)(nbh / nkv);
+        g.q_hin = (int32_t)extent_of(d, s, rec, qin);
+        g.kv_hin = (int32_t)extent_of(d, s, rec, kin);
         g.pad = 0;
+        if (g.q_hin > 1 || g.kv_hin > 1) p->att_inner = 1;
+        if (S * g.q_hin * D > lim) return fail(JA_ERR_UNSUPPORTED, "query block rows beyond 2^31 elements");
         g.q_off = Q.blk_off[block_of(Q, q, s, rec)];
         g.o_off = O.blk_off[block_of(O, s->out, s, rec)];
-        g.q_bhstride = S * D;
+        g.q_bstride = S * g.q_hin * D;
         g.S = (int32_t)S;
         g.s_lo = (int32_t)d->sp[ls][rec[ls]];
         g.t_begin = (int32_t)t.seg[sg];
@@ -334,6 +351,7 @@ ja_status ja_plan_partial_bytes(const ja_plan* p, size_t* bytes) {
     if (p->kind != JA_OP_CONTRACT && p->kind != JA_OP_ATTENTION)
         return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract and attention only");
     if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
+    if (p->att_inner) return fail(JA_ERR_UNSUPPORTED, INNER_UNFUSED);
     // bf16 attention: the per-tuple tiles' range-check flags follow the partials
     *bytes = (size_t)p->partial_elems * 4 + att_flag_bytes(p, p->nutiles);
     return JA_OK;
@@ -345,6 +363,7 @@ ja_status ja_kernel(const ja_plan* p, const void* const* in_ptrs, void* partials
     if (p->kind != JA_OP_CONTRACT && p->kind != JA_OP_ATTENTION)
         return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract and attention only");
     if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
+    if (p->att_inner) return fail(JA_ERR_UNSUPPORTED, INNER_UNFUSED);
     if (p->nutiles == 0) return JA_OK;
     hipStream_t hs = (hipStream_t)stream;
     if (p->kind == JA_OP_ATTENTION) {
@@ -365,6 +384,7 @@ ja_status ja_agg(const ja_plan* p, ja_agg_op op, const void* partials, void* out
     if (p->kind != JA_OP_CONTRACT && p->kind != JA_OP_ATTENTION)
         return fail(JA_ERR_UNSUPPORTED, "unfused path exists for contract and attention only");
     if (p->epilogue != JA_EPI_NONE) return fail(JA_ERR_UNSUPPORTED, "unfused path exists for plain contractions only");
+    if (p->att_inner) return fail(JA_ERR_UNSUPPORTED, INNER_UNFUSED);
     if (op != JA_AGG_SUM && op != JA_AGG_MAX && op != JA_AGG_SOFTMAX)
         return fail(JA_ERR_ARG, "unknown aggregation operator");
     if ((p->kind == JA_OP_ATTENTION) != (op == JA_AGG_SOFTMAX))

@@ -24,6 +24,7 @@ struct ja_plan {
     // attention
     float scale = 0.f;
     int32_t causal = 0;
+    int32_t att_inner = 0;  // some block stores batch-heads inside a row (token-major)
     int64_t seq_off = 0;  // packed sequences: int32 sequence ends in the table
     int32_t nseq = 0;
     // rmsnorm

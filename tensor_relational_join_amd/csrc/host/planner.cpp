@@ -76,7 +76,7 @@ std::vector<bool> shardable(const ja_spec& s) {
         const std::string &q = s.ins[0], &k = s.ins[1];
         for (size_t i = 0; i < s.letters.size(); ++i) {
             const char c = s.letters[i];
-            sh[i] = k.find(c) != std::string::npos || c == q[q.size() - 2];
+            sh[i] = k.find(c) != std::string::npos || c == s.att_s;
         }
         sh[s.letter_index(q.back())] = false;
     }
@@ -257,8 +257,8 @@ void device_time(const GOp& op, Cand& c) {
         }
     } else {  // attention
         const std::string& q = s.ins[0];
-        const int ls = s.letter_index(q[q.size() - 2]), ld = s.letter_index(q.back());
-        const int lt = s.letter_index(s.ins[1][s.ins[1].size() - 2]);
+        const int ls = s.letter_index(s.att_s), ld = s.letter_index(q.back());
+        const int lt = s.letter_index(s.att_t);
         const double D = (double)op.ext[ld];
         for (auto& kv : seg) {
             const std::vector<int64_t>& first = kv.second[0];

@@ -61,21 +61,28 @@ struct AttnTile {
     int32_t pad;
 };
 
+// A Q, K, V or O block is [outer batch-heads][rows][inner batch-heads][D]:
+// the batch-head letters before the position letter index whole [rows][inner]
+// [D] slabs, those after it (token-major relations) sit inside a row.  With
+// hin inner batch-heads, batch-head bh's row r starts at element
+//   (bh / hin) * bstride + (bh % hin) * D + r * hin * D.
 struct AttnSeg {
-    int64_t q_off, o_off;  // Q block and O block offsets
-    int64_t q_bhstride;    // S * D
+    int64_t q_off, o_off;  // Q block and O block offsets (O has Q's letters)
+    int64_t q_bstride;     // S * q_hin * D
     int32_t S;             // query rows in the block
     int32_t s_lo;          // global query index of the block's first row
     int32_t t_begin, t_end;
     int32_t rep;           // query batch-heads per key-value batch-head: K/V index = bh / rep
+    int32_t q_hin;         // inner batch-heads of the Q and O blocks
+    int32_t kv_hin;        // inner batch-heads of the segment's K and V blocks
     int32_t pad;
 };
 
 struct AttnTuple {
     int64_t k_off, v_off;
-    int64_t kv_bhstride;  // T * D
-    int32_t T;            // keys in the block
-    int32_t t_lo;         // global key index of the block's first key
+    int64_t kv_bstride;  // T * kv_hin * D
+    int32_t T;           // keys in the block
+    int32_t t_lo;        // global key index of the block's first key
 };
 
 // ---------------------------------------------------------------- rmsnorm

@@ -44,7 +44,7 @@ def _fmt(orc, dt):
     return orc.bf16_to_f64, orc.round_bf16, to_dev_bf16
 
 
-def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False, dt="bf16"):
+def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False, dt="bf16", layout="tokens"):
     import torch
 
     from tensor_relational_join_amd.binding import JA_BF16, JA_F16
@@ -54,7 +54,7 @@ def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False
     put = _fmt(orc, dt)[2]
     pack = lambda rel, bits: put(orc.Relation(rel.shape, rel.splits).pack(bits))  # noqa: E731
     blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv_heads, fused=fused,
-                     dtype=JA_F16 if dt == "f16" else JA_BF16)
+                     dtype=JA_F16 if dt == "f16" else JA_BF16, layout=layout)
     inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols, dtype=dt)
     x = pack(blk.x_rel, inp["x"])
     w = {k: pack(rel, inp[k]) for k, rel in blk.w_rel.items()}
@@ -109,11 +109,19 @@ def _check_steps(orc, blk, inp, y, sampled: bool, dt="bf16"):
     h1 = _unpack(orc, o["norm1"].out_rel, b["h1"])
     errs["norm1"] = rel_frobenius(h1, rnd(orc.rmsnorm(xd, f64(inp["g1"]), blk.eps)))
     N = blk.qkv_cols
+    tok = blk.layout == "tokens"
     contract("qkv", o["norm1"].out_rel, b["h1"], "w_qkv", o["qkv"].out_rel, b["qkv"], N,
-             dm if blk.gqa else N // 2)
+             dm if blk.gqa or tok else N // 2)
     qr = o["qkv"].out_rel
     kv, rep = blk.kv_heads, heads // blk.kv_heads
-    if not blk.gqa:
+    if tok:
+        # attention reads the projection's three contiguous token-major parts as they are
+        flat = f64(bf16_bits(b["qkv"]))
+        nq, nk = T * dm, T * kv * 128
+        Qd = flat[:nq].reshape(batch, seq, heads, 128).transpose(0, 2, 1, 3)
+        Kd = flat[nq:nq + nk].reshape(batch, seq, kv, 128).transpose(0, 2, 1, 3)
+        Vd = flat[nq + nk:].reshape(batch, seq, kv, 128).transpose(0, 2, 1, 3)
+    elif not blk.gqa:
         hr = blk.heads_rel
         want_heads = orc.repartition(orc.Relation(qr.shape, qr.splits), bf16_bits(b["qkv"]),
                                      orc.Relation(hr.shape, hr.splits), (batch, seq, 3, heads, 128), (2, 0, 3, 1, 4))
@@ -137,7 +145,8 @@ def _check_steps(orc, blk, inp, y, sampled: bool, dt="bf16"):
             dense[name] = f64(orc.Relation(rel.shape, rel.splits).unpack(got_p))
         errs["to_heads"] = 0.0 if ok else 1.0
         Qd, Kd, Vd = dense["q"].reshape(batch, heads, seq, 128), dense["k"], dense["v"]
-    Od = _unpack(orc, o["attn"].out_rel, b["O"]).reshape(batch, heads, seq, 128)
+    Od = _unpack(orc, o["attn"].out_rel, b["O"])
+    Od = Od.reshape(batch, seq, heads, 128).transpose(0, 2, 1, 3) if tok else Od.reshape(batch, heads, seq, 128)
     if sampled:
         ss = [0, 1, 127, 128, 1000, seq - 1]
         rows = np.array([(bb, hh, s) for bb, hh in [(0, 0), (batch // 2, heads // 2), (batch - 1, heads - 1)]
@@ -148,10 +157,13 @@ def _check_steps(orc, blk, inp, y, sampled: bool, dt="bf16"):
     errs["attn"] = rel_frobenius(Od[rows[:, 0], rows[:, 1], rows[:, 2]], want)
     oproj = o["oproj_add" if blk.fused else "oproj"]
     ar, orl = o["attn"].out_rel, oproj.in_rels[0]
-    view = ((batch, kv, rep, seq, 128), (0, 3, 1, 2, 4)) if blk.gqa else ((batch, heads, seq, 128), (0, 2, 1, 3))
-    want_o = orc.repartition(orc.Relation(ar.shape, ar.splits), bf16_bits(b["O"]),
-                             orc.Relation(orl.shape, orl.splits), *view)
-    errs["to_tokens"] = 0.0 if np.array_equal(bf16_bits(b["o"]), want_o) else 1.0
+    if not tok:
+        view = ((batch, kv, rep, seq, 128), (0, 3, 1, 2, 4)) if blk.gqa else ((batch, heads, seq, 128), (0, 2, 1, 3))
+        want_o = orc.repartition(orc.Relation(ar.shape, ar.splits), bf16_bits(b["O"]),
+                                 orc.Relation(orl.shape, orl.splits), *view)
+        errs["to_tokens"] = 0.0 if np.array_equal(bf16_bits(b["o"]), want_o) else 1.0
+    else:
+        assert b["o"].data_ptr() == b["O"].data_ptr()
     if blk.fused:
         contract("oproj_add", orl, b["o"], "w_o", oproj.out_rel, b["x2"], dm, dm // 2, residual=xd)
         x2 = _unpack(orc, oproj.out_rel, b["x2"])
@@ -203,18 +215,21 @@ REDUCED = [  # (name, batch, seq, dm, heads, kv_heads, ffn, seed, dtype)
 ]
 
 
+@pytest.mark.parametrize("layout", ["tokens", "heads"])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
-def test_block_reduced_shapes(orc, case, fused):
+def test_block_reduced_shapes(orc, case, fused, layout):
     """Every step and the whole chain compared in full (the chain at the
-    per-step bar)."""
+    per-step bar), with attention on the projections' token-major relations
+    and on head-major ones (repartitions around it)."""
     name, batch, seq, dm, heads, kv, ffn, seed, dt = case
-    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=seed, kv_heads=kv, fused=fused, dt=dt)
+    blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=seed, kv_heads=kv, fused=fused, dt=dt,
+                                layout=layout)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=False, dt=dt)
         chain = _chain(orc, blk, inp, yd, None, fused, dt)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
-        record("block_reduced_shapes", case=name, fused=fused, steps=errs, chain=chain)
+        record("block_reduced_shapes", case=name, fused=fused, layout=layout, steps=errs, chain=chain)
         for k, v in errs.items():
             assert v <= TOL, (k, v)
         assert chain <= CHAIN_TOL

@@ -400,6 +400,51 @@ def test_attention_bf16_values_beyond_the_fp16_range(dev, orc):
         assert max(errs) <= BF16_TOL, errs
 
 
+# ------------------------------------------------------------------ token-major attention
+
+TOKEN_MAJOR_CASES = [
+    # (einsum, Q shape, K shape, splits, causal): batch-head letters after the position letter, so a
+    # block holds whole token rows of several heads
+    ("bshd,bthd,bthd->bshd", (2, 384, 4, 128), (2, 384, 4, 128),
+     {"b": [0, 1, 2], "s": _eq(384, 3), "t": _eq(384, 3), "h": [0, 4], "d": [0, 128]}, True),
+    ("bshd,bthd,bthd->bshd", (1, 300, 3, 128), (1, 300, 3, 128),                  # heads cut 1 + 2, ragged tiles
+     {"b": [0, 1], "s": [0, 100, 300], "t": [0, 200, 300], "h": [0, 1, 3], "d": [0, 128]}, True),
+    ("bshd,bthd,bthd->bshd", (1, 256, 2, 128), (1, 384, 2, 128),                  # non-causal, S != T
+     {"b": [0, 1], "s": [0, 128, 256], "t": [0, 64, 384], "h": [0, 2], "d": [0, 128]}, False),
+    ("bsgrd,btgd,btgd->bsgrd", (1, 384, 2, 3, 128), (1, 384, 2, 128),             # grouped-query, r cut 1 + 2
+     {"b": [0, 1], "s": _eq(384, 3), "t": _eq(384, 3), "g": [0, 2], "r": [0, 1, 3], "d": [0, 128]}, True),
+]
+
+
+def _heads_first(x):
+    """[b, pos, heads..., d] -> [b, prod(heads), pos, d]"""
+    x = np.moveaxis(x, 1, -2)
+    return x.reshape(x.shape[0], -1, x.shape[-2], x.shape[-1])
+
+
+@pytest.mark.parametrize("einsum,qshape,kshape,sp,causal", TOKEN_MAJOR_CASES)
+def test_attention_token_major(dev, orc, einsum, qshape, kshape, sp, causal):
+    """Q, K, V and O token-major (the projections' own layout): against the
+    oracle's attention on the same values head-major, and bit for bit against
+    the kernel on the head-major relations of the same values."""
+    Q = synth.normal_bf16(23, 0, qshape)
+    K = synth.normal_bf16(23, 1, kshape)
+    V = synth.normal_bf16(23, 2, kshape)
+    params = "causal=s,t" if causal else ""
+    got, o, _ = _run(dev, orc, einsum, "attention", sp, [Q, K, V], params=params)
+    o.close()
+    f = orc.bf16_to_f64
+    want_hm = orc.attention(f(_heads_first(Q)), f(_heads_first(K)), f(_heads_first(V)), 1.0 / np.sqrt(128.0), causal)
+    want = np.moveaxis(want_hm.reshape(qshape[:1] + qshape[2:-1] + (qshape[1], 128)), -2, 1)
+    assert rel_frobenius(got, orc.round_bf16(want)) <= BF16_TOL
+    if einsum.startswith("bshd"):
+        hm = {"b": sp["b"], "h": sp["h"], "s": sp["s"], "t": sp["t"], "d": sp["d"]}
+        ref, o, _ = _run(dev, orc, "bhsd,bhtd,bhtd->bhsd", "attention", hm,
+                         [np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in (Q, K, V)], params=params)
+        o.close()
+        assert np.array_equal(got, ref.transpose(0, 2, 1, 3))
+
+
 # ------------------------------------------------------------------ grouped-query attention
 
 GQA_CASES = [

@@ -187,6 +187,12 @@ def test_relation_layout_matches_oracle(B, orc):
     ("rbgsd,bgtd,bgtd->rbgsd", "attention", "", "JA_ERR_SPEC"),
     ("bgsd,bgrtd,bgrtd->bgsd", "attention", "", "JA_ERR_SPEC"),
     ("bgrsd,bgsd,bgsd->bgrsd", "attention", "", "JA_ERR_SPEC"),
+    # token-major relations: the letters before both position letters agree, and with the position and
+    # head-dimension letters removed Q's letters are K's followed by the group letters
+    ("bshd,bhtd,bhtd->bshd", "attention", "", "JA_ERR_SPEC"),
+    ("bshd,bthd,bthd->bhsd", "attention", "", "JA_ERR_SPEC"),
+    ("bsrgd,btgd,btgd->bsrgd", "attention", "", "JA_ERR_SPEC"),
+    ("bshd,bthd,bthd->bshd", "attention", "causal=h,t", "JA_ERR_SPEC"),
     # fused contractions: the residual has the output's letters; the pair letter is B's last, nowhere else
     ("tm,mn->tn", "contract_add", "", "JA_ERR_SPEC"),
     ("tm,mn,nt->tn", "contract_add", "", "JA_ERR_SPEC"),
@@ -200,6 +206,43 @@ def test_spec_errors(B, einsum, op, params, code):
         B.ja_spec_create(einsum, op, params)
     assert e.value.name == code
     assert B.ja_last_error()
+
+
+@pytest.mark.parametrize("einsum", ["bshd,bthd,bthd->bshd", "bsgrd,btgd,btgd->bsgrd", "bhsd,bhtd,bhtd->bhsd",
+                                    "bgrsd,bgtd,bgtd->bgrsd"])
+def test_attention_spec_forms(B, orc, einsum):
+    """Head-major and token-major attention specs (batch-head letters before
+    or after the position letter) are accepted, and their causal tuple lists
+    are the oracle's: the join does not depend on where the letters sit."""
+    lq = einsum.split(",")[0]
+    sp = {c: [0, 2] for c in einsum if c.isalpha()}
+    sp.update({"s": [0, 128, 256, 300], "t": [0, 100, 300], "d": [0, 128], "r": [0, 1, 3]})
+    letters, rec, seg = _tuples(B, einsum, "attention", sp, "causal=s,t")
+    o_rec, o_seg = orc.tuple_records(list(letters), sp, group_by=list(lq), causal=("s", "t"))
+    assert np.array_equal(rec, o_rec) and np.array_equal(seg, o_seg)
+
+
+def test_token_major_attention_has_no_unfused_path(B):
+    """Blocks with batch-heads inside a row have the fused kernel only: the
+    softmax aggregation writes rows in [batch-head][query] order."""
+    from tensor_relational_join_amd.device import relation_for
+
+    sp = {"b": [0, 1], "s": [0, 128, 256], "h": [0, 4], "t": [0, 128, 256], "d": [0, 128]}
+    s = B.ja_spec_create("bshd,bthd,bthd->bshd", "attention", "causal=s,t")
+    ls = B.ja_spec_letters(s)
+    d = B.ja_decomp_create(s, [sp[c][-1] for c in ls], [len(sp[c]) - 1 for c in ls], [sp[c] for c in ls])
+    try:
+        ins = [relation_for(x, sp, B.JA_BF16) for x in ("bshd", "bthd", "bthd")]
+        p = B.ja_plan_create(s, d, ins, relation_for("bshd", sp, B.JA_BF16))
+        try:
+            with pytest.raises(B.JaError) as e:
+                B.ja_plan_partial_bytes(p)
+            assert e.value.name == "JA_ERR_UNSUPPORTED"
+        finally:
+            B.ja_plan_destroy(p)
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
 
 
 def test_decomposition_errors(B):
