@@ -559,6 +559,28 @@ def test_packed_attention(dev, orc, H, HK, S, ends, cuts, causal):
     assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("H,HK,S,ends,cuts,causal", [PACKED_CASES[0], PACKED_CASES[3]])
+def test_packed_attention_token_major(dev, orc, H, HK, S, ends, cuts, causal):
+    """Packed sequences on token-major relations (the heads inside a row): bit
+    for bit the head-major result on the same values."""
+    R = H // HK
+    sp = {"b": [0, 1], "g": [0, HK], "r": [0, R], "s": cuts, "t": cuts, "d": [0, 128]}
+    Q = synth.normal_bf16(25, 0, (1, HK, R, S, 128))
+    K = synth.normal_bf16(25, 1, (1, HK, S, 128))
+    V = synth.normal_bf16(25, 2, (1, HK, S, 128))
+    params = "packed=" + ",".join(map(str, ends)) + (";causal=s,t" if causal else "")
+    hm, o, _ = _run(dev, orc, "bgrsd,bgtd,bgtd->bgrsd", "attention", sp, [Q, K, V], params=params)
+    o.close()
+    tm, o, _ = _run(dev, orc, "bsgrd,btgd,btgd->bsgrd", "attention", sp,
+                    [np.ascontiguousarray(Q.transpose(0, 3, 1, 2, 4))] +
+                    [np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in (K, V)], params=params)
+    o.close()
+    assert np.array_equal(tm, hm.transpose(0, 3, 1, 2, 4))
+    want = orc.attention(orc.bf16_to_f64(Q).reshape(1, H, S, 128), orc.bf16_to_f64(K), orc.bf16_to_f64(V),
+                         1.0 / np.sqrt(128.0), causal, seq_ends=ends)
+    assert rel_frobenius(hm.reshape(1, H, S, 128), orc.round_bf16(want)) <= BF16_TOL
+
+
 # ------------------------------------------------------------------ fp16 relations
 
 F16_CONTRACT_CASES = [
