@@ -325,7 +325,7 @@ def bench_kernel(args):
                 "steps": args.steps, "ms": round(ms, 4), "gbs": round(gbs, 1),
                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
     runs = []  # (name, launch, flops, bytes, ops to close)
-    want = ["tiny", "ffn", "ffn_unfused", "attention", "rmsnorm", "swiglu"] if args.workload == "configs" else \
+    want = ["tiny", "ffn", "ffn_unfused", "attention", "rmsnorm", "swiglu", "repart"] if args.workload == "configs" else \
         {"ffn": ["ffn"], "attention": ["attention"], "norm_swiglu": ["rmsnorm", "swiglu"],
          "gqa": ["gqa_8k", "gqa_8x1k", "gqa_128k"], "f16": ["ffn_f16", "attention_f16"]}[args.workload]
 
@@ -407,6 +407,24 @@ def bench_kernel(args):
         ins, out = tensors(op, 4, [(0.0, 1.0)] * 2)
         runs.append(("swiglu", lambda op=op, ins=ins, out=out: op.run(ins, out), None, 2.0 * 3 * 8192 * 11008,
                      [op]))
+    if "repart" in want:
+        # the LLaMA-7B-shaped block's re-indexing repartitions around head-major attention: the QKV projection's
+        # output [8192, 12288] in 2 x 2 blocks viewed as [3, 4, 32, 2048, 128] in 128-row head blocks (402.7 MB
+        # moved), and attention's output back to [8192, 4096] in 2 x 2 blocks (134.2 MB)
+        from tensor_relational_join_amd import binding as B
+        from tensor_relational_join_amd.device import Repart
+
+        for name, src, dst, view in (
+                ("repart_to_heads", B.Relation((8192, 12288), nblk=(2, 2), dtype=B.JA_BF16),
+                 B.Relation((3, 4, 32, 2048, 128), nblk=(3, 4, 32, 16, 1), dtype=B.JA_BF16),
+                 B.make_view((4, 2048, 3, 32, 128), (2, 0, 3, 1, 4))),
+                ("repart_to_tokens", B.Relation((4, 32, 2048, 128), nblk=(4, 32, 16, 1), dtype=B.JA_BF16),
+                 B.Relation((8192, 4096), nblk=(2, 2), dtype=B.JA_BF16),
+                 B.make_view((4, 32, 2048, 128), (0, 2, 1, 3)))):
+            rp = Repart(src, dst, view)
+            torch.manual_seed(6)
+            a, b = alloc(src).normal_(0.0, 1.0), alloc(dst)
+            runs.append((name, lambda rp=rp, a=a, b=b: rp.run(a, b), None, 2.0 * 2 * a.numel(), [rp]))
     res = {}
     # cold runs: reading 512 MiB between iterations evicts the 256 MB Infinity
     # Cache (a read leaves clean lines, so the timed kernel writes nothing back)
@@ -548,7 +566,9 @@ def configs_summary(args):
              "ffn_unfused_kernel_then_agg": "cfg2 unfused (ja_kernel fp32 partials, then ja_agg SUM)",
              "attention": "cfg3 causal attention [4,32,2048,128] bf16, 128-blocks",
              "rmsnorm": "cfg4a RMSNorm [8192,4096] bf16, d by 8",
-             "swiglu": "cfg4b SwiGLU [8192,11008] bf16, f by 8"}
+             "swiglu": "cfg4b SwiGLU [8192,11008] bf16, f by 8",
+             "repart_to_heads": "repartition [8192,12288] 2x2 -> [3,4,32,2048,128] head blocks (tokens to heads view)",
+             "repart_to_tokens": "repartition [4,32,2048,128] head blocks -> [8192,4096] 2x2 (heads to tokens view)"}
     out = {}
     for k, d in res.items():
         e = {"what": names.get(k, k), "ms": d["ms"], "warm_median_ms": d["warm"]["median"],
