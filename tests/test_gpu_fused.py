@@ -13,7 +13,7 @@ import itertools
 import numpy as np
 import pytest
 
-from gpu_helpers import bf16_bits, rel_frobenius, to_dev_bf16, to_dev_f16
+from gpu_helpers import bf16_bits, record, rel_frobenius, to_dev_bf16, to_dev_f16
 from tensor_relational_join_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -145,6 +145,45 @@ def test_contract_with_half_height_tail(dev, orc, einsum, op, sp, f16):
     if unfused is not None:
         assert rel_frobenius(unfused, want) <= TOL
         assert np.mean(unfused == want) > 0.95
+
+
+# Two tiles per workgroup with the next tile's first four stages loaded
+# during the current tile's last four steps (its first tuple holds at least
+# four 32-wide stages): 24 x 22 = 528 tiles of 256 x 256, ragged in both
+# directions, so transitions go from full tiles (whose stores the next tile's
+# first steps need not wait for) and from ragged ones (which they do); the
+# last 16 tiles run half-height.  K = 136 + 64 puts a ragged stage right
+# after the prefetched ones; the residual form's epilogue also loads.
+PREFETCH_CASES = [
+    ("ij,jk->ik", "contract", {"i": [0, 5896], "j": [0, 136, 200], "k": [0, 5496]}, False),
+    ("ij,jk,ik->ik", "contract_add", {"i": [0, 5896], "j": [0, 256], "k": [0, 5496]}, False),
+    ("td,dfc->tf", "contract_swiglu", {"t": [0, 5896], "d": [0, 136, 200], "f": [0, 2748], "c": [0, 2]}, False),
+    ("ij,jk,ik->ik", "contract_add", {"i": [0, 5896], "j": [0, 256], "k": [0, 5496]}, True),
+]
+
+
+@pytest.mark.parametrize("einsum,op,sp,f16", PREFETCH_CASES)
+def test_contract_tile_walk_with_stage_prefetch(dev, orc, einsum, op, sp, f16):
+    lhs, out = einsum.split("->")
+    shapes = [tuple(sp[c][-1] for c in s) for s in lhs.split(",")]
+    draw = synth.normal_f16 if f16 else synth.normal_bf16
+    widen = orc.f16_to_f64 if f16 else orc.bf16_to_f64
+    rnd = orc.round_f16 if f16 else orc.round_bf16
+    dense = [draw(41, i, shp, std=0.05 if i == 1 else 1.0) for i, shp in enumerate(shapes)]
+    got, o, _ = _run(dev, orc, einsum, op, sp, dense, f16=f16)
+    o.close()
+    w = [widen(x) for x in dense]
+    plain = "%s,%s->%s" % (lhs.split(",")[0], lhs.split(",")[1], out)
+    if op == "contract_swiglu":
+        want = rnd(orc.contract_swiglu(einsum, w[0], w[1]))
+    elif op == "contract_add":
+        want = rnd(orc.contract_residual(plain, *w))
+    else:
+        want = rnd(orc.einsum(plain, w[0], w[1]))
+    err, eq = rel_frobenius(got, want), float(np.mean(got == want))
+    record("contract_tile_walk_with_stage_prefetch", op=op, f16=f16, rel_frobenius=err, equal_fraction=eq)
+    assert err <= TOL
+    assert eq > 0.95
 
 
 SWIGLU_CASES = [
