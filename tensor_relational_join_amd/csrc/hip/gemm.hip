@@ -672,8 +672,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if constexpr (ASM) {
             // Stage 0 is followed in issue order by stages 1 .. NS - 1 and
-            // then the stores; vector memory operations complete in issue
-            // order, so waiting for stage 0 leaves both in flight.
+            // then the previous tile's epilogue (its stores, and with head 2
+            // a residual load before each); vector memory operations
+            // complete in issue order, so waiting for stage 0 leaves both in
+            // flight.
             const uint32_t head = nst >= NS ? stored_after : 0u;
             if (head == 2)
                 wait_loads_barrier<(NS - 1) * PER_STAGE + 2 * GA::STORES>();
@@ -700,11 +702,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
                 if (it + 1 < nst) step(it + 1, fa[1], fb[1], fa[0], fb[0]);
             }
         }
-        // Next tile: its first stages are loaded while this tile's results
-        // leave (all of them, unless the epilogue loads a residual: that load
-        // would wait behind them, so then only the first stage goes early and
-        // the rest after the stores).  The barrier makes sure that every
-        // wavefront's last fragment reads are complete before LDS is refilled.
+        // Next tile: with pf its first NS stages were loaded during this
+        // tile's last NS steps.  Otherwise they are loaded now, while this
+        // tile's results leave (all of them, unless the epilogue loads a
+        // residual: that load would wait behind them, so then only the first
+        // stage goes early and the rest after the stores).  The barrier makes
+        // sure that every wavefront's last fragment reads are complete before
+        // LDS is refilled.
         const int64_t ecbase = sg.c_off + (int64_t)tl.batch * sg.c_bstride;
         const int eldc = sg.ldc, eM = sg.M, eN = sg.N, em0 = m0, en0 = n0;
         const int vnext = vt + (int)gridDim.x;
