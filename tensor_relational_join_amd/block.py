@@ -84,12 +84,34 @@ GEMMS = ["qkv", "oproj", "gate", "up", "down"]
 FUSED_STEPS = ["norm1", "qkv", "to_heads", "attn", "to_tokens", "oproj_add", "norm2", "gate_up", "down_add"]
 FUSED_GEMMS = ["qkv", "oproj_add", "gate_up", "down_add"]
 LAYOUTS = ("tokens", "heads")
+SPLIT_TILES = 128
+
+
+def _out_tiles(op) -> int:
+    """256 x 256 output tiles of a contraction over its output blocks."""
+    lhs, out = op.einsum.split("->")
+    n = 1
+    for c in out[-2:]:
+        sp = op.splits[c]
+        n *= sum(-(-(hi - lo) // 256) for lo, hi in zip(sp[:-1], sp[1:]))
+    for c in out[:-2]:
+        n *= op.splits[c][-1] - op.splits[c][0]
+    return n
+
+
+def _k_tuples(op) -> int:
+    """Tuples per segment: the intervals of the contracted letters."""
+    lhs, out = op.einsum.split("->")
+    n = 1
+    for c in set(lhs.replace(",", "")) - set(out):
+        n *= len(op.splits[c]) - 1
+    return n
 
 
 class LlamaBlock:
     def __init__(self, batch: int = 4, seq: int = 2048, dm: int = 4096, heads: int = 32, ffn: int = 11008,
                  eps: float = 1e-6, device="cuda", kv_heads: Optional[int] = None, fused: bool = False,
-                 dtype: int = B.JA_BF16, layout: str = "tokens"):
+                 dtype: int = B.JA_BF16, layout: str = "tokens", split_small: bool = True):
         if dm % heads or dm // heads != 128 or seq % 128:
             raise ValueError("the attention kernel needs head_dim 128 and 128-multiples of seq")
         if dtype not in (B.JA_BF16, B.JA_F16):
@@ -228,6 +250,34 @@ class LlamaBlock:
                              "dn": alloc(o["down"].out_rel, device)})
         else:
             self.buf["f"] = alloc(o["gate_up"].out_rel, device)
+        # Contractions with few output tiles (at most SPLIT_TILES 256 x 256
+        # tiles, under half of the 256 compute units) and at least two tuples
+        # per segment run unfused: every tuple's partial block in parallel
+        # (ja_kernel), then the atomic-free SUM of each segment's partials in
+        # tuple order (ja_agg), so that the K tuples occupy compute units the
+        # output tiles alone would leave idle.  A residual add fused into such
+        # a contraction becomes a 1:1 join of its own after the SUM.
+        self.split: Dict[str, str] = {}
+        if split_small:
+            for name in ("qkv", "oproj", "oproj_add", "down", "down_add"):
+                op = self.ops.get(name)
+                if op is not None and _out_tiles(op) <= SPLIT_TILES and _k_tuples(op) >= 2:
+                    self.split[name] = name
+        if "down_add" in self.split:
+            sp = self.ops["down_add"].splits
+            self.ops["down_split"] = Op("tf,fn->tn", "contract", {c: sp[c] for c in "tfn"}, device=device)
+            self.ops["add2_split"] = Op("td,td->td", "add", {"t": sp["t"], "d": sp["n"]}, device=device)
+            self.split["down_add"] = "down_split"
+            self.buf["dn"] = alloc(self.ops["down_split"].out_rel, device)
+        if "oproj_add" in self.split:
+            sp = self.ops["oproj_add"].splits
+            self.ops["oproj_split"] = Op("tm,mn->tn", "contract", {c: sp[c] for c in "tmn"}, device=device)
+            self.ops["add1_split"] = Op("td,td->td", "add", {"t": sp["t"], "d": sp["n"]}, device=device)
+            self.split["oproj_add"] = "oproj_split"
+            self.buf["a"] = alloc(self.ops["oproj_split"].out_rel, device)
+        if self.split:
+            self.partials = torch.empty(max(self.ops[v].partial_bytes() for v in self.split.values()) // 4,
+                                        dtype=torch.float32, device=device)
 
     # ---------------------------------------------------------------- flops / bytes
     def flops(self) -> Dict[str, float]:
@@ -281,9 +331,26 @@ class LlamaBlock:
                 self.rp["to_q"].run(b["qkv"][:nq], q, stream)
                 self.rp["to_k"].run(b["qkv"][nq:nq + nk], k, stream)
                 self.rp["to_v"].run(b["qkv"][nq + nk:], v, stream)
+        def contract(name, ins, out):
+            """op `name`, fused, or split into per-tuple partials and their SUM
+            (the residual, if any, added after it as a 1:1 join)"""
+            if name not in self.split:
+                o[name].run(ins, out, stream)
+                return
+            sop = o[self.split[name]]
+            sop.kernel(ins[:2], self.partials, stream)
+            if name == "down_add":
+                sop.agg(self.partials, b["dn"], stream=stream)
+                o["add2_split"].run([ins[2], b["dn"]], out, stream)
+            elif name == "oproj_add":
+                sop.agg(self.partials, b["a"], stream=stream)
+                o["add1_split"].run([ins[2], b["a"]], out, stream)
+            else:
+                sop.agg(self.partials, out, stream=stream)
+
         plan = [
             ("norm1", lambda: o["norm1"].run([x, w["g1"]], b["h1"], stream)),
-            ("qkv", lambda: o["qkv"].run([b["h1"], w["w_qkv"]], b["qkv"], stream)),
+            ("qkv", lambda: contract("qkv", [b["h1"], w["w_qkv"]], b["qkv"])),
             ("to_heads", to_heads),
             ("attn", lambda: o["attn"].run([q, k, v], b["O"], stream)),
             ("to_tokens", lambda: self.rp["to_tokens"].run(b["O"], b["o"], stream)),
@@ -292,21 +359,21 @@ class LlamaBlock:
             plan = [st for st in plan if st[0] not in ("to_heads", "to_tokens")]
         if not self.fused:
             plan += [
-                ("oproj", lambda: o["oproj"].run([b["o"], w["w_o"]], b["a"], stream)),
+                ("oproj", lambda: contract("oproj", [b["o"], w["w_o"]], b["a"])),
                 ("add1", lambda: o["add1"].run([x, b["a"]], b["x2"], stream)),
                 ("norm2", lambda: o["norm2"].run([b["x2"], w["g2"]], b["h2"], stream)),
                 ("gate", lambda: o["gate"].run([b["h2"], w["w_gate"]], b["gt"], stream)),
                 ("up", lambda: o["up"].run([b["h2"], w["w_up"]], b["up"], stream)),
                 ("swiglu", lambda: o["swiglu"].run([b["gt"], b["up"]], b["f"], stream)),
-                ("down", lambda: o["down"].run([b["f"], w["w_down"]], b["dn"], stream)),
+                ("down", lambda: contract("down", [b["f"], w["w_down"]], b["dn"])),
                 ("add2", lambda: o["add2"].run([b["x2"], b["dn"]], y, stream)),
             ]
         else:
             plan += [
-                ("oproj_add", lambda: o["oproj_add"].run([b["o"], w["w_o"], x], b["x2"], stream)),
+                ("oproj_add", lambda: contract("oproj_add", [b["o"], w["w_o"], x], b["x2"])),
                 ("norm2", lambda: o["norm2"].run([b["x2"], w["g2"]], b["h2"], stream)),
                 ("gate_up", lambda: o["gate_up"].run([b["h2"], w["w_gu"]], b["f"], stream)),
-                ("down_add", lambda: o["down_add"].run([b["f"], w["w_down"], b["x2"]], y, stream)),
+                ("down_add", lambda: contract("down_add", [b["f"], w["w_down"], b["x2"]], y)),
             ]
         for name, fn in plan:
             if events is not None:

@@ -99,6 +99,7 @@ class Op:
                  in_dtypes: Optional[Sequence[int]] = None, out_dtype: int = JA_BF16, device="cuda",
                  stream: Optional[torch.cuda.Stream] = None):
         self.einsum, self.op = einsum, op
+        self.splits = {c: list(v) for c, v in splits.items()}
         self.spec = B.ja_spec_create(einsum, op, params)
         self.decomp = None
         self.plan = None

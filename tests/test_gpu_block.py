@@ -44,7 +44,8 @@ def _fmt(orc, dt):
     return orc.bf16_to_f64, orc.round_bf16, to_dev_bf16
 
 
-def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False, dt="bf16", layout="tokens"):
+def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False, dt="bf16", layout="tokens",
+               split_small=True):
     import torch
 
     from tensor_relational_join_amd.binding import JA_BF16, JA_F16
@@ -54,7 +55,7 @@ def _run_block(orc, batch, seq, dm, heads, ffn, seed, kv_heads=None, fused=False
     put = _fmt(orc, dt)[2]
     pack = lambda rel, bits: put(orc.Relation(rel.shape, rel.splits).pack(bits))  # noqa: E731
     blk = LlamaBlock(batch, seq, dm, heads, ffn, kv_heads=kv_heads, fused=fused,
-                     dtype=JA_F16 if dt == "f16" else JA_BF16, layout=layout)
+                     dtype=JA_F16 if dt == "f16" else JA_BF16, layout=layout, split_small=split_small)
     inp = synth.llama_block_inputs(seed, batch, seq, dm, ffn, qkv_cols=blk.qkv_cols, dtype=dt)
     x = pack(blk.x_rel, inp["x"])
     w = {k: pack(rel, inp[k]) for k, rel in blk.w_rel.items()}
@@ -215,21 +216,24 @@ REDUCED = [  # (name, batch, seq, dm, heads, kv_heads, ffn, seed, dtype)
 ]
 
 
-@pytest.mark.parametrize("layout", ["tokens", "heads"])
+@pytest.mark.parametrize("layout,split", [("tokens", True), ("heads", True), ("tokens", False)])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
-def test_block_reduced_shapes(orc, case, fused, layout):
+def test_block_reduced_shapes(orc, case, fused, layout, split):
     """Every step and the whole chain compared in full (the chain at the
     per-step bar), with attention on the projections' token-major relations
-    and on head-major ones (repartitions around it)."""
+    and on head-major ones (repartitions around it); at these sizes every
+    contraction with two or more K tuples runs split into per-tuple partials
+    and their SUM (split=True), or fused."""
     name, batch, seq, dm, heads, kv, ffn, seed, dt = case
     blk, inp, x, y = _run_block(orc, batch, seq, dm, heads, ffn, seed=seed, kv_heads=kv, fused=fused, dt=dt,
-                                layout=layout)
+                                layout=layout, split_small=split)
     try:
         errs, yd = _check_steps(orc, blk, inp, y, sampled=False, dt=dt)
         chain = _chain(orc, blk, inp, yd, None, fused, dt)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
-        record("block_reduced_shapes", case=name, fused=fused, layout=layout, steps=errs, chain=chain)
+        record("block_reduced_shapes", case=name, fused=fused, layout=layout, split=sorted(blk.split), steps=errs,
+               chain=chain)
         for k, v in errs.items():
             assert v <= TOL, (k, v)
         assert chain <= CHAIN_TOL
@@ -262,7 +266,8 @@ def test_block_full_size(orc, case, fused):
         toks = [bb * seq + s for bb in sorted({0, batch // 2, batch - 1}) for s in pos]
         chain = _chain(orc, blk, inp, yd, toks, fused, dt)
         print("per-step errors:", {k: "%.2e" % v for k, v in errs.items()}, "chain: %.2e" % chain)
-        record("block_full_size", case=name, fused=fused, steps=errs, chain=chain, tokens=len(toks))
+        record("block_full_size", case=name, fused=fused, split=sorted(blk.split), steps=errs, chain=chain,
+               tokens=len(toks))
         for k, v in errs.items():
             assert v <= TOL, (k, v)
         # fp16 P costs the bf16 chain up to 5e-3 at full size; an all-half block keeps the 2e-3 bar
