@@ -45,9 +45,7 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
     // of the real output, so its block offsets are twice the output's.
     const std::string &sa = s->ins[0], &sb = s->ins[1];
     const std::string sc = swig ? s->out + s->pair : s->out;
-    if ((st = match_rel(A, sa, s, d, "operand A")) || (st = match_rel(B, sb, s, d, "operand B")) ||
-        (st = match_rel(C, s->out, s, d, "output")))
-        return st;
+    if ((st = match_rel(C, s->out, s, d, "output"))) return st;
     if (swig) {
         const int l = s->letter_index(s->pair);
         if (d->ext[l] != 2 || d->sp[l].size() != 2)
@@ -93,6 +91,26 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
     if (sc != batch + Mo + No || !runs(sa, batch, Mo, K, a_m_first) || !runs(sb, batch, K, No, b_k_first))
         return fail(JA_ERR_UNSUPPORTED,
                     "contract needs operands laid out as [batch][rows][cols] runs with matching letter orders");
+    // An operand of two letters (no batch letter) may be blocked coarser than
+    // the decomposition: a tuple then reads its sub-box of the block in place
+    // (offset inside the block, the block's row length as leading dimension),
+    // so a refinement of an operand's blocking needs no repartition.
+    const bool a_sub = batch.empty() && sa.size() == 2, b_sub = batch.empty() && sb.size() == 2;
+    if ((st = a_sub ? match_rel_coarse(A, sa, s, d, "operand A") : match_rel(A, sa, s, d, "operand A")) ||
+        (st = b_sub ? match_rel_coarse(B, sb, s, d, "operand B") : match_rel(B, sb, s, d, "operand B")))
+        return st;
+    // a tuple's sub-box of a two-letter operand: element offset, leading
+    // dimension (the block's inner extent) and the sub-box's span (outer
+    // interval extent times the leading dimension)
+    auto sub_box = [&](const Rel& X, const std::string& xs, const int32_t* rec, int64_t& off, int64_t& ld,
+                       int64_t& span) {
+        const int l0 = s->letter_index(xs[0]), l1 = s->letter_index(xs[1]);
+        const int64_t lo0 = d->sp[l0][rec[l0]], lo1 = d->sp[l1][rec[l1]];
+        int64_t key[2] = {X.find(0, lo0), X.find(1, lo1)};
+        ld = X.ext(1, key[1]);
+        off = X.blk_off[X.block_index(key)] + (lo0 - X.sp[0][key[0]]) * ld + (lo1 - X.sp[1][key[1]]);
+        span = (d->sp[l0][rec[l0] + 1] - lo0) * ld;
+    };
     p->a_layout = a_m_first ? JA_A_MK : JA_A_KM;
     p->b_layout = b_k_first ? JA_B_KN : JA_B_NK;
     p->in_dtype = A.dtype;
@@ -122,6 +140,20 @@ ja_status plan_contract(ja_plan* p, const ja_spec* s, const ja_decomp* d, const 
         g.K = (int32_t)k;
         g.lda = (int32_t)(a_m_first ? k : m);
         g.ldb = (int32_t)(b_k_first ? n : k);
+        if (a_sub) {  // (with the decomposition's own blocking this gives the values above)
+            int64_t ld, span;
+            sub_box(A, sa, rec, g.a_off, ld, span);
+            if (ld > lim) return fail(JA_ERR_UNSUPPORTED, "block extent beyond 2^31");
+            g.lda = (int32_t)ld;
+            g.a_bstride = span;
+        }
+        if (b_sub) {
+            int64_t ld, span;
+            sub_box(B, sb, rec, g.b_off, ld, span);
+            if (ld > lim) return fail(JA_ERR_UNSUPPORTED, "block extent beyond 2^31");
+            g.ldb = (int32_t)ld;
+            g.b_bstride = span;
+        }
         g.pad = 0;
         // unfused: every tuple is its own segment writing an f32 partial block
         GemmSeg& u = usegs[i];

@@ -2,6 +2,7 @@
 // planners of libja (plan.cpp: attention, RMSNorm, 1:1 joins and the ABI;
 // plan_contract.cpp: contractions).
 #pragma once
+#include <algorithm>
 #include <cstring>
 
 #include "ja_host.h"
@@ -60,6 +61,25 @@ inline ja_status match_rel(const Rel& r, const std::string& s, const ja_spec* sp
         if (r.sp[k] != d->sp[l])
             return fail(JA_ERR_SHAPE, std::string(what) + ": blocking of letter " + s[k] +
                                           " differs from the decomposition (repartition it first)");
+    }
+    return JA_OK;
+}
+
+// The same check for a relation that may be blocked coarser than the
+// decomposition: each of its split points is one of the decomposition's, so
+// every interval of the decomposition lies inside one of its blocks.
+inline ja_status match_rel_coarse(const Rel& r, const std::string& s, const ja_spec* sp, const ja_decomp* d,
+                                  const char* what) {
+    if (r.rank != (int)s.size())
+        return fail(JA_ERR_SHAPE, std::string(what) + ": rank differs from its letters '" + s + "'");
+    for (int k = 0; k < r.rank; ++k) {
+        int l = sp->letter_index(s[k]);
+        if (r.shape[k] != d->ext[l])
+            return fail(JA_ERR_SHAPE, std::string(what) + ": extent of letter " + s[k] + " differs from the decomposition");
+        for (int64_t x : r.sp[k])
+            if (!std::binary_search(d->sp[l].begin(), d->sp[l].end(), x))
+                return fail(JA_ERR_SHAPE, std::string(what) + ": blocking of letter " + s[k] +
+                                              " is neither the decomposition's nor coarser (repartition it first)");
     }
     return JA_OK;
 }

@@ -97,7 +97,11 @@ class Op:
 
     def __init__(self, einsum: str, op: str, splits: Dict[str, Sequence[int]], params: str = "",
                  in_dtypes: Optional[Sequence[int]] = None, out_dtype: int = JA_BF16, device="cuda",
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None,
+                 in_splits: Optional[Sequence[Optional[Dict[str, Sequence[int]]]]] = None):
+        """in_splits: per input, an optional blocking of its own letters (a
+        contraction operand of two letters may be blocked coarser than the
+        decomposition; its tuples then read sub-boxes of its blocks)."""
         self.einsum, self.op = einsum, op
         self.splits = {c: list(v) for c, v in splits.items()}
         self.spec = B.ja_spec_create(einsum, op, params)
@@ -111,7 +115,9 @@ class Op:
             lhs, out = einsum.split("->")
             ins = lhs.split(",")
             in_dtypes = in_dtypes or [JA_BF16] * len(ins)
-            self.in_rels = [relation_for(s, splits, dt) for s, dt in zip(ins, in_dtypes)]
+            in_splits = list(in_splits or []) + [None] * len(ins)
+            self.in_rels = [relation_for(s, {**splits, **(own or {})}, dt)
+                            for s, dt, own in zip(ins, in_dtypes, in_splits)]
             self.out_rel = relation_for(out, splits, out_dtype)
             self.plan = B.ja_plan_create(self.spec, self.decomp, self.in_rels, self.out_rel)
             tb, wb = B.ja_plan_device_bytes(self.plan)

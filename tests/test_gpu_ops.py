@@ -326,6 +326,58 @@ def test_contraction_persistent_multi_tile_walk(dev, orc):
     assert eq > 0.95
 
 
+# Contraction operands blocked coarser than the decomposition: each tuple reads
+# a sub-box of its operand block in place (the block's row length as leading
+# dimension), fused and through per-tuple partials and their SUM.
+COARSE_CASES = [
+    # (einsum, op, decomposition, the inputs' own blockings)
+    ("ij,jk->ik", "contract", {"i": [0, 256, 520], "j": [0, 64, 136, 200, 256], "k": [0, 264, 520]},
+     [{"j": [0, 136, 256]}, {"j": [0, 256], "k": [0, 520]}]),
+    ("ji,kj->ik", "contract", {"i": [0, 136, 264], "j": [0, 96, 160, 256], "k": [0, 128, 392]},
+     [{"j": [0, 256], "i": [0, 264]}, {"j": [0, 160, 256]}]),
+    ("ij,jk,ik->ik", "contract_add", {"i": [0, 256, 520], "j": [0, 64, 136, 200, 256], "k": [0, 264, 520]},
+     [{"j": [0, 256]}, None, None]),
+]
+
+
+@pytest.mark.parametrize("einsum,op,sp,own", COARSE_CASES)
+def test_contraction_operands_blocked_coarser(dev, orc, einsum, op, sp, own):
+    import torch
+
+    from tensor_relational_join_amd.binding import JA_BF16
+
+    lhs, out = einsum.split("->")
+    ins = lhs.split(",")
+    shapes = [tuple(sp[c][-1] for c in x) for x in ins]
+    dense = [synth.normal_bf16(43, i, shp, std=0.05 if i == 1 else 1.0) for i, shp in enumerate(shapes)]
+    o = dev.Op(einsum, op, sp, "", [JA_BF16] * len(ins), JA_BF16, in_splits=own)
+    try:
+        dev_ins = [to_dev_bf16(orc.Relation([sp[c][-1] for c in x], [(blk or {}).get(c, sp[c]) for c in x]).pack(v))
+                   for x, v, blk in zip(ins, dense, own)]
+        orel = orc.Relation([sp[c][-1] for c in out], [sp[c] for c in out])
+        out_t = dev.alloc(o.out_rel)
+        o.run(dev_ins, out_t)
+        torch.cuda.synchronize()
+        got = orc.bf16_to_f64(orel.unpack(bf16_bits(out_t)))
+        unfused = None
+        if op == "contract":  # per-tuple partials over the same sub-boxes, then the SUM
+            part = o.partial_buffer()
+            o.kernel(dev_ins, part)
+            out2 = dev.alloc(o.out_rel)
+            o.agg(part, out2)
+            torch.cuda.synchronize()
+            unfused = orc.bf16_to_f64(orel.unpack(bf16_bits(out2)))
+    finally:
+        o.close()
+    w = [orc.bf16_to_f64(x) for x in dense]
+    plain = "%s,%s->%s" % (ins[0], ins[1], out)
+    want = orc.round_bf16(orc.contract_residual(plain, *w) if op == "contract_add" else orc.einsum(plain, w[0], w[1]))
+    assert rel_frobenius(got, want) <= BF16_TOL
+    assert np.mean(got == want) > 0.95
+    if unfused is not None:
+        assert rel_frobenius(unfused, want) <= BF16_TOL
+
+
 # ------------------------------------------------------------------ attention
 
 ATT_CASES = [

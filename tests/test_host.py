@@ -285,7 +285,8 @@ def test_plan_validation_errors(B):
             B.ja_plan_run(p, [16, 32], 48)
         assert e.value.name == "JA_ERR_STATE"
         B.ja_plan_destroy(p)
-        bad = B.Relation((64, 64), nblk=(1, 2), dtype=B.JA_F32)   # A not blocked as the decomposition asks
+        # A blocked finer than the decomposition (a coarser blocking is read in sub-boxes)
+        bad = B.Relation((64, 64), nblk=(4, 2), dtype=B.JA_F32)
         with pytest.raises(B.JaError) as e:
             B.ja_plan_create(s, d, [bad, Bm], C)
         assert e.value.name == "JA_ERR_SHAPE"
@@ -299,6 +300,47 @@ def test_plan_validation_errors(B):
         A16, B16 = relation_for("ij", sp, B.JA_BF16), relation_for("jk", {**sp, "k": [0, 30, 64]}, B.JA_BF16)
         with pytest.raises(B.JaError):
             B.ja_plan_create(s, d, [A16, B16], C16)
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
+
+
+def test_contraction_operands_blocked_coarser(B):
+    """A two-letter contraction operand may be blocked coarser than the
+    decomposition (each of its split points one of the decomposition's): its
+    tuples read sub-boxes of its blocks in place.  A blocking with a split
+    point the decomposition lacks, or a batched operand blocked apart, is
+    refused."""
+    from tensor_relational_join_amd.device import relation_for
+
+    sp = {"i": [0, 64, 128], "j": [0, 32, 64, 96, 128], "k": [0, 64, 128]}
+    s = B.ja_spec_create("ij,jk->ik", "contract")
+    d = B.ja_decomp_create(s, [128, 128, 128], [2, 4, 2], [sp["i"], sp["j"], sp["k"]])
+    try:
+        out = relation_for("ik", sp, B.JA_BF16)
+        for aj, bj in (([0, 64, 128], [0, 128]), ([0, 128], [0, 32, 128]), (sp["j"], sp["j"])):
+            a = relation_for("ij", {**sp, "j": aj}, B.JA_BF16)
+            b = relation_for("jk", {**sp, "j": bj, "k": [0, 128]}, B.JA_BF16)
+            B.ja_plan_destroy(B.ja_plan_create(s, d, [a, b], out))
+        bad = relation_for("ij", {**sp, "j": [0, 48, 128]}, B.JA_BF16)
+        with pytest.raises(B.JaError) as e:
+            B.ja_plan_create(s, d, [bad, relation_for("jk", sp, B.JA_BF16)], out)
+        assert e.value.name == "JA_ERR_SHAPE"
+        with pytest.raises(B.JaError) as e:  # the output stays blocked as the decomposition
+            B.ja_plan_create(s, d, [relation_for("ij", sp, B.JA_BF16), relation_for("jk", sp, B.JA_BF16)],
+                             relation_for("ik", {**sp, "k": [0, 128]}, B.JA_BF16))
+        assert e.value.name == "JA_ERR_SHAPE"
+    finally:
+        B.ja_decomp_destroy(d)
+        B.ja_spec_destroy(s)
+    bsp = {"b": [0, 1, 2], "i": [0, 64], "j": [0, 32, 64], "k": [0, 64]}
+    s = B.ja_spec_create("bij,bjk->bik", "contract")
+    d = B.ja_decomp_create(s, [2, 64, 64, 64], [2, 1, 2, 1], [bsp["b"], bsp["i"], bsp["j"], bsp["k"]])
+    try:
+        with pytest.raises(B.JaError) as e:
+            B.ja_plan_create(s, d, [relation_for("bij", {**bsp, "j": [0, 64]}, B.JA_BF16),
+                                    relation_for("bjk", bsp, B.JA_BF16)], relation_for("bik", bsp, B.JA_BF16))
+        assert e.value.name == "JA_ERR_SHAPE"
     finally:
         B.ja_decomp_destroy(d)
         B.ja_spec_destroy(s)
