@@ -141,9 +141,9 @@ class LlamaBlock:
         nb = seq // 128
         self.ops: Dict[str, Op] = {}
 
-        def Op(einsum, op, splits, params="", device="cuda"):  # noqa: N802 -- every relation in the block's dtype
+        def Op(einsum, op, splits, params="", device="cuda", in_splits=None):  # noqa: N802 -- the block's dtype
             n_in = len(einsum.split("->")[0].split(","))
-            return _Op(einsum, op, splits, params, [dtype] * n_in, dtype, device=device)
+            return _Op(einsum, op, splits, params, [dtype] * n_in, dtype, device=device, in_splits=in_splits)
 
         self.ops["norm1"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
         if tok:
@@ -174,11 +174,20 @@ class LlamaBlock:
             self.ops["attn"] = Op("bgrsd,bgtd,bgtd->bgrsd", "attention", att_sp, "causal=s,t", device=device)
         # attention's token-major output is the projection's A as it is (m whole)
         m2 = [0, dm] if tok else d2
+        # With few output tiles the projection's m is cut in four anyway (so
+        # that it can run split into K tuples, below) while its A stays one
+        # block: each tuple reads a sub-box of attention's token-major output.
+        self._o_in = None
+        if tok and split_small and -(-T // 256) * sum(-(-(b - a) // 256) for a, b in zip(d2[:-1], d2[1:])) \
+                <= SPLIT_TILES:
+            m2, self._o_in = equal_splits(dm, 4), [{"m": [0, dm]}]
         if not fused:
-            self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": m2, "n": d2}, device=device)
+            self.ops["oproj"] = Op("tm,mn->tn", "contract", {"t": t2, "m": m2, "n": d2}, device=device,
+                                   in_splits=self._o_in)
             self.ops["add1"] = Op("td,td->td", "add", {"t": t2, "d": d2}, device=device)
         else:
-            self.ops["oproj_add"] = Op("tm,mn,tn->tn", "contract_add", {"t": t2, "m": m2, "n": d2}, device=device)
+            self.ops["oproj_add"] = Op("tm,mn,tn->tn", "contract_add", {"t": t2, "m": m2, "n": d2}, device=device,
+                                       in_splits=self._o_in)
         self.ops["norm2"] = Op("rd,d->rd", "rmsnorm", {"r": t2, "d": d2}, ep, device=device)
         if not fused:
             self.ops["gate"] = Op("td,df->tf", "contract", {"t": t2, "d": d2, "f": f4}, device=device)
@@ -271,7 +280,8 @@ class LlamaBlock:
             self.buf["dn"] = alloc(self.ops["down_split"].out_rel, device)
         if "oproj_add" in self.split:
             sp = self.ops["oproj_add"].splits
-            self.ops["oproj_split"] = Op("tm,mn->tn", "contract", {c: sp[c] for c in "tmn"}, device=device)
+            self.ops["oproj_split"] = Op("tm,mn->tn", "contract", {c: sp[c] for c in "tmn"}, device=device,
+                                         in_splits=self._o_in)
             self.ops["add1_split"] = Op("td,td->td", "add", {"t": sp["t"], "d": sp["n"]}, device=device)
             self.split["oproj_add"] = "oproj_split"
             self.buf["a"] = alloc(self.ops["oproj_split"].out_rel, device)
