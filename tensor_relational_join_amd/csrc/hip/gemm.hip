@@ -258,12 +258,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_dma_kernel(const GemmTi
     // positions blockIdx.x, blockIdx.x + gridDim.x, ... (after xcd_remap, so
     // every tile it takes is dealt to its own XCD, in the list's order).
     // A kernel whose tile height is below the list's (BM < GEMM_BF16_TM) runs
-    // the tail of a list: virtual tile v is rows [BM (v % 2), BM (v % 2 + 1))
-    // of listed tile v / 2 (GEMM_BF16_TM = 2 BM), taken in list order.
+    // the tail of a list: virtual tile u = xcd_remap(v) is rows
+    // [BM (u % 2), BM (u % 2 + 1)) of listed tile u / 2 (GEMM_BF16_TM = 2 BM).
     constexpr bool HALF = BM < GEMM_BF16_TM;
     static_assert(!HALF || 2 * BM == GEMM_BF16_TM, "a tail tile is half a listed tile");
-    auto tile_at = [&](int v) { return HALF ? tiles[v >> 1] : tiles[xcd_remap(v, ntiles)]; };
-    auto row0 = [&](int v, const GemmTile& t) { return HALF ? t.m0 + (v & 1) * BM : t.m0; };
+    // (the virtual tiles of a tail launch are dealt through xcd_remap too, so
+    // the two halves of a listed tile and its neighbours share one L2)
+    auto tile_at = [&](int v) { return HALF ? tiles[xcd_remap(v, ntiles) >> 1] : tiles[xcd_remap(v, ntiles)]; };
+    auto row0 = [&](int v, const GemmTile& t) { return HALF ? t.m0 + (xcd_remap(v, ntiles) & 1) * BM : t.m0; };
     int vt = blockIdx.x;
     GemmTile tl = tile_at(vt);
     GemmSeg sg = segs[tl.seg];
