@@ -730,6 +730,10 @@ def test_norm_and_elementwise_f16(dev, orc, op):
     (300, 2048, [0, 100, 300], _eq(2048, 2)),
     (10, 3072, [0, 3, 10], _eq(3072, 3)),
     (5, 1024, [0, 5], [0, 1024]),
+    # more rows than resident wavefronts, so each walks several rows and
+    # prefetches the next, across row blocks; 16 vectors per lane
+    (5000, 1024, [0, 1999, 5000], _eq(1024, 2)),
+    (2500, 8192, [0, 1300, 2500], [0, 8192]),
 ])
 def test_rmsnorm(dev, orc, R, D, rsp, dsp):
     x = synth.normal_bf16(4, 0, (R, D))
